@@ -1,0 +1,15 @@
+"""CPU oracle of the tensor-parallel block shard (fp64 NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package entry point's smoke check and by
+the benchmark's CPU-baseline leg, never by the product path. It shares no code with the HIP
+library or its binding.
+
+Parity unpinned: the absolute values of a whole block's output. The pages print no numeric
+example of a block; the output is pinned only through the pins of its parts (sharded equals
+unsharded, library cross-checks of every sublayer, brute force on tiny shapes, closed forms).
+"""
+from .block import (  # noqa: F401
+    ACTIVATIONS, attend, bf16_bits_to_f64, block_sharded, block_unsharded, caches_f64,
+    dequant_q8_0, f16_bits_to_f64, gelu_tanh, params_f64, rank_caches, rms_norm, rope,
+    rope_cos_sin, run_block, shard_slices, shard_weights, silu, to_f64,
+)

@@ -1,0 +1,480 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* closed forms and hand-written fixtures (tests/golden/),
+* library routines (torch fp64: rms_norm, linear, scaled_dot_product_attention with grouped KV
+  heads, silu, gelu-tanh, complex multiplication for the rotary embedding),
+* brute force in scalar pure-Python loops on tiny shapes,
+* the block-matrix identity the tensor-parallel split rests on (sharded == unsharded),
+* shard-map invariants (row-parallel slices concatenate back bit-exactly, fused column rows form
+  the same multiset, every rank holds exactly 1/N of the sharded bytes),
+* planted mistakes in the oracle, each of which must trip at least one pin.
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import oracle.block as ob
+from tensor_transformer_block_amd.inputs import (
+    CONFIGS, BlockShape, f32_to_bf16_bits, make_inputs, q8_0_encode, weight_shapes)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def nrel(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+TINY = BlockShape(name="tiny-brute", index=101, d_model=8, n_heads=4, n_kv_heads=2, head_dim=4,
+                  ffn_dim=12, tp=2, w_dtype="f32", act_dtype="f32", ffn_act="silu",
+                  mode="decode", kv_lens=(3,), n_tokens=1)
+SMALL_SHAPES = [
+    TINY,
+    TINY.with_(name="tiny-n1", index=102, tp=1),
+    TINY.with_(name="tiny-gelu-bf16", index=103, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="gelu_tanh"),
+    TINY.with_(name="tiny-prefill", index=104, mode="prefill", kv_lens=(7,), n_tokens=4),
+    TINY.with_(name="tiny-batch", index=105, kv_lens=(3, 1, 5), n_tokens=3, tp=2),
+    BlockShape(name="small-q8", index=106, d_model=64, n_heads=4, n_kv_heads=2, head_dim=16,
+               ffn_dim=128, tp=2, w_dtype="q8_0", act_dtype="bf16", ffn_act="gelu_tanh",
+               mode="decode", kv_lens=(20, 9), n_tokens=2),
+    BlockShape(name="small-prefill-n4", index=107, d_model=64, n_heads=8, n_kv_heads=4,
+               head_dim=8, ffn_dim=96, tp=4, w_dtype="bf16", act_dtype="bf16", ffn_act="silu",
+               mode="prefill", kv_lens=(40,), n_tokens=33),
+    CONFIGS["tiny-llama-fp32"],
+]
+
+
+# ----------------------------------------------------------------------------- independent references
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a))
+
+
+def torch_decode_storage(a, dtype, shape=None):
+    """Storage -> float64 torch tensor through torch's own dtype views (not the oracle's)."""
+    if dtype == "f32":
+        return _t(np.asarray(a, np.float32)).double()
+    if dtype == "bf16":
+        return _t(np.asarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).double()
+    if dtype == "q8_0":
+        rows, cols = shape
+        raw = _t(np.asarray(a, np.uint8).reshape(rows, cols // 32, 34))
+        d = raw[..., 0:2].contiguous().view(torch.float16).double()          # [rows, nb, 1]
+        q = raw[..., 2:].contiguous().view(torch.int8).double()              # [rows, nb, 32]
+        return (d * q).reshape(rows, cols)
+    raise ValueError(dtype)
+
+
+def torch_rope(x, pos, base):
+    """Rotate-half rotary embedding as a complex product: (a + ib) * exp(i * pos * theta)."""
+    hd = x.shape[-1]
+    theta = base ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    z = torch.complex(x[..., : hd // 2], x[..., hd // 2:])
+    z = z * torch.polar(torch.ones_like(theta), pos * theta)
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+def torch_block(inp):
+    """The unsharded block written with torch library routines in float64."""
+    s = inp.shape
+    shp = weight_shapes(s)
+    W = {k: torch_decode_storage(inp.weights[k], s.w_dtype, shp[k]) for k in shp}
+    g1 = torch_decode_storage(inp.gamma1, s.act_dtype)
+    g2 = torch_decode_storage(inp.gamma2, s.act_dtype)
+    x = torch_decode_storage(inp.x, s.act_dtype)
+    T, hd, Hq, Hkv = x.shape[0], s.head_dim, s.n_heads, s.n_kv_heads
+    xn = F.rms_norm(x, (s.d_model,), g1, eps=s.rms_eps)
+    q = F.linear(xn, W["wq"]).view(T, Hq, hd)
+    k = F.linear(xn, W["wk"]).view(T, Hkv, hd)
+    v = F.linear(xn, W["wv"]).view(T, Hkv, hd)
+    pos = torch.from_numpy(inp.positions.astype(np.int64))
+    qr = torch.stack([torch_rope(q[t], float(pos[t]), s.rope_base) for t in range(T)])
+    kr = torch.stack([torch_rope(k[t], float(pos[t]), s.rope_base) for t in range(T)])
+    attn = torch.zeros(T, Hq, hd, dtype=torch.float64)
+    for b in range(s.n_seqs):
+        L = int(inp.seq_lens[b])
+        K = torch.zeros(Hkv, L, hd, dtype=torch.float64)
+        V = torch.zeros(Hkv, L, hd, dtype=torch.float64)
+        kp = torch_decode_storage(inp.k_prior[b], s.act_dtype)
+        vp = torch_decode_storage(inp.v_prior[b], s.act_dtype)
+        K[:, : kp.shape[1]] = kp
+        V[:, : vp.shape[1]] = vp
+        toks = [t for t in range(T) if int(inp.token_seq[t]) == b]
+        for t in toks:
+            K[:, int(pos[t])] = kr[t]
+            V[:, int(pos[t])] = v[t]
+        qs = qr[toks].transpose(0, 1).unsqueeze(0)                            # [1, Hq, n, hd]
+        mask = torch.arange(L)[None, :] <= pos[toks][:, None]                 # [n, L]
+        o = F.scaled_dot_product_attention(qs, K.unsqueeze(0), V.unsqueeze(0), attn_mask=mask,
+                                           enable_gqa=True)
+        attn[toks] = o[0].transpose(0, 1)
+    attn = attn.reshape(T, Hq * hd)
+    h1 = x + F.linear(attn, W["wo"])
+    xn2 = F.rms_norm(h1, (s.d_model,), g2, eps=s.rms_eps)
+    gate, up = F.linear(xn2, W["wg"]), F.linear(xn2, W["wu"])
+    act = F.silu(gate) if s.ffn_act == "silu" else F.gelu(gate, approximate="tanh")
+    out = h1 + F.linear(act * up, W["wd"])
+    return dict(xn=xn, q=qr, k_new=kr, attn=attn, h1=h1, xn2=xn2, m=act * up, out=out)
+
+
+def brute_block(inp):
+    """The unsharded block in scalar pure-Python loops (tiny shapes only)."""
+    s = inp.shape
+    shp = weight_shapes(s)
+    W = {k: torch_decode_storage(inp.weights[k], s.w_dtype, shp[k]).tolist() for k in shp}
+    g1 = torch_decode_storage(inp.gamma1, s.act_dtype).tolist()
+    g2 = torch_decode_storage(inp.gamma2, s.act_dtype).tolist()
+    X = torch_decode_storage(inp.x, s.act_dtype).tolist()
+    d, hd, Hq, Hkv, Fd = s.d_model, s.head_dim, s.n_heads, s.n_kv_heads, s.ffn_dim
+    half = hd // 2
+
+    def norm(vec, g):
+        ms = sum(e * e for e in vec) / len(vec)
+        inv = 1.0 / math.sqrt(ms + s.rms_eps)
+        return [g[i] * vec[i] * inv for i in range(len(vec))]
+
+    def matvec(Wm, vec):
+        return [sum(Wm[o][i] * vec[i] for i in range(len(vec))) for o in range(len(Wm))]
+
+    def rot(vec, p):
+        out = [0.0] * hd
+        for i in range(half):
+            z = complex(vec[i], vec[i + half]) * cmath.exp(1j * p * s.rope_base ** (-2.0 * i / hd))
+            out[i], out[i + half] = z.real, z.imag
+        return out
+
+    caches = []
+    for b in range(s.n_seqs):
+        kp = torch_decode_storage(inp.k_prior[b], s.act_dtype).tolist()
+        vp = torch_decode_storage(inp.v_prior[b], s.act_dtype).tolist()
+        caches.append(({(g, j): kp[g][j] for g in range(Hkv) for j in range(len(kp[g]))},
+                       {(g, j): vp[g][j] for g in range(Hkv) for j in range(len(vp[g]))}))
+    T = len(X)
+    xns = [norm(X[t], g1) for t in range(T)]
+    for t in range(T):
+        b, p = int(inp.token_seq[t]), int(inp.positions[t])
+        kk, vv = matvec(W["wk"], xns[t]), matvec(W["wv"], xns[t])
+        for g in range(Hkv):
+            caches[b][0][(g, p)] = rot(kk[g * hd:(g + 1) * hd], p)
+            caches[b][1][(g, p)] = vv[g * hd:(g + 1) * hd]
+    outs = []
+    for t in range(T):
+        b, p = int(inp.token_seq[t]), int(inp.positions[t])
+        qq = matvec(W["wq"], xns[t])
+        a = []
+        for h in range(Hq):
+            g = h * Hkv // Hq
+            qh = rot(qq[h * hd:(h + 1) * hd], p)
+            sc = [sum(qh[i] * caches[b][0][(g, j)][i] for i in range(hd)) / math.sqrt(hd)
+                  for j in range(p + 1)]
+            mx = max(sc)
+            e = [math.exp(z - mx) for z in sc]
+            tot = sum(e)
+            a += [sum(e[j] / tot * caches[b][1][(g, j)][i] for j in range(p + 1)) for i in range(hd)]
+        h1 = [X[t][i] + v for i, v in enumerate(matvec(W["wo"], a))]
+        xn2 = norm(h1, g2)
+        gt, up = matvec(W["wg"], xn2), matvec(W["wu"], xn2)
+        if s.ffn_act == "silu":
+            m = [gt[j] / (1.0 + math.exp(-gt[j])) * up[j] for j in range(Fd)]
+        else:
+            m = [0.5 * gt[j] * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt[j] + 0.044715 * gt[j] ** 3)))
+                 * up[j] for j in range(Fd)]
+        outs.append([h1[i] + v for i, v in enumerate(matvec(W["wd"], m))])
+    return np.array(outs)
+
+
+# ----------------------------------------------------------------------------- block-level pins
+
+@pytest.mark.parametrize("s", SMALL_SHAPES, ids=lambda s: s.name)
+def test_sharded_equals_unsharded(s):
+    """Row-parallel partial sums add up to the unsharded projections (block-matrix identity)."""
+    inp = make_inputs(s, seed=3)
+    a = oracle.run_block(inp, sharded=True)
+    b = oracle.run_block(inp, sharded=False)
+    for key in ("xn", "h1", "xn2", "out"):
+        assert nrel(a[key], b[key]) <= 1e-12, key
+    assert nrel(a["attn_sum"], b["attn_proj"]) <= 1e-12
+    assert nrel(a["ffn_sum"], b["ffn_proj"]) <= 1e-12
+    hq, hd = s.n_heads // s.tp, s.head_dim
+    fr = s.ffn_dim // s.tp
+    for r, rk in enumerate(a["ranks"]):
+        assert nrel(rk["a"], b["attn"][:, r * hq * hd:(r + 1) * hq * hd]) <= 1e-12
+        assert nrel(rk["m"], b["m"][:, r * fr:(r + 1) * fr]) <= 1e-12
+
+
+@pytest.mark.parametrize("s", SMALL_SHAPES, ids=lambda s: s.name)
+def test_oracle_matches_torch_library_block(s):
+    inp = make_inputs(s, seed=5)
+    ref = torch_block(inp)
+    for sharded in (False, True):
+        res = oracle.run_block(inp, sharded=sharded)
+        for key in ("xn", "h1", "xn2", "out"):
+            assert nrel(res[key], ref[key].numpy()) <= 1e-12, (sharded, key)
+    res = oracle.run_block(inp, sharded=False)
+    assert nrel(res["attn"], ref["attn"].numpy()) <= 1e-12
+    assert nrel(res["q"], ref["q"].numpy()) <= 1e-12
+    assert nrel(res["m"], ref["m"].numpy()) <= 1e-12
+
+
+@pytest.mark.parametrize("s", [x for x in SMALL_SHAPES if x.d_model <= 8], ids=lambda s: s.name)
+def test_oracle_matches_scalar_brute_force(s):
+    inp = make_inputs(s, seed=7)
+    ref = brute_block(inp)
+    for sharded in (False, True):
+        res = oracle.run_block(inp, sharded=sharded)
+        assert nrel(res["out"], ref) <= 1e-12, sharded
+
+
+def test_n1_reduces_sharded_to_unsharded():
+    s = TINY.with_(tp=1, index=110)
+    inp = make_inputs(s, seed=1)
+    a, b = oracle.run_block(inp, True), oracle.run_block(inp, False)
+    assert nrel(a["out"], b["out"]) <= 1e-14
+    assert nrel(a["ranks"][0]["a"], b["attn"]) <= 1e-14
+
+
+def test_replicated_state_is_rank_independent():
+    """Every rank sees the same xn/xn2; the rank loop order of the reduction is fixed."""
+    s = CONFIGS["tiny-llama-fp32"]
+    inp = make_inputs(s)
+    res = oracle.run_block(inp, True)
+    ps = [rk["p_attn"] for rk in res["ranks"]]
+    manual = ps[0] + ps[1]
+    assert np.array_equal(manual, res["attn_sum"])
+
+
+# ----------------------------------------------------------------------------- sublayer pins
+
+def test_rms_norm_closed_form_and_library():
+    c, eps, d = 3.5, 1e-5, 16
+    g = np.linspace(0.5, 1.5, d)
+    y = oracle.rms_norm(np.full(d, c), g, eps)
+    assert np.allclose(y, g * c / math.sqrt(c * c + eps), rtol=1e-15, atol=0)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, d))
+    ref = F.rms_norm(_t(x), (d,), _t(g), eps=eps).numpy()
+    assert nrel(oracle.rms_norm(x, g, eps), ref) <= 1e-14
+    # scale invariance as eps -> 0
+    assert nrel(oracle.rms_norm(7.0 * x, g, 0.0), oracle.rms_norm(x, g, 0.0)) <= 1e-14
+
+
+def test_rope_golden_hd4():
+    doc = json.load(open(os.path.join(GOLDEN, "rope_hd4.json")))
+    for c in doc["cases"]:
+        y = oracle.rope(np.array(c["x"], dtype=np.float64), c["position"], doc["base"])
+        assert np.allclose(y, c["y"], rtol=0, atol=1e-15), c
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(1)
+    hd, base = 128, 10000.0
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    assert np.array_equal(oracle.rope(q, 0, base), q)
+    y = oracle.rope(q, 4095, base)
+    assert np.allclose(q[:64] ** 2 + q[64:] ** 2, y[:64] ** 2 + y[64:] ** 2, rtol=1e-12)
+    for p, pp, dl in [(3, 10, 7), (100, 5, 4000), (0, 0, 123)]:
+        lhs = oracle.rope(q, p + dl, base) @ oracle.rope(k, pp + dl, base)
+        rhs = oracle.rope(q, p, base) @ oracle.rope(k, pp, base)
+        assert abs(lhs - rhs) <= 1e-10 * (1 + abs(rhs))
+    # hd = 2: a plain rotation by the position (theta_0 = 1)
+    y2 = oracle.rope(np.array([0.3, -0.7]), 5, base)
+    z = complex(0.3, -0.7) * cmath.exp(5j)
+    assert np.allclose(y2, [z.real, z.imag], rtol=0, atol=1e-15)
+    ref = torch_rope(_t(q), 77.0, base).numpy()
+    assert nrel(oracle.rope(q, 77, base), ref) <= 1e-13
+
+
+def test_attention_special_cases_and_library():
+    rng = np.random.default_rng(2)
+    hd = 8
+    q, k, v = rng.standard_normal(hd), rng.standard_normal((1, hd)), rng.standard_normal((1, hd))
+    assert np.allclose(oracle.attend(q, k, v), v[0], rtol=1e-15)
+    kk = np.repeat(rng.standard_normal((1, hd)), 6, axis=0)
+    vv = rng.standard_normal((6, hd))
+    assert np.allclose(oracle.attend(q, kk, vv), vv.mean(axis=0), rtol=1e-13)
+    K, V = rng.standard_normal((9, hd)), rng.standard_normal((9, hd))
+    ref = F.scaled_dot_product_attention(_t(q)[None, None, None], _t(K)[None, None],
+                                         _t(V)[None, None])[0, 0, 0].numpy()
+    assert nrel(oracle.attend(q, K, V), ref) <= 1e-14
+
+
+def test_activations_library():
+    z = np.linspace(-9, 9, 1001)
+    assert nrel(oracle.silu(z), F.silu(_t(z)).numpy()) <= 1e-15
+    assert nrel(oracle.gelu_tanh(z), F.gelu(_t(z), approximate="tanh").numpy()) <= 1e-15
+    assert oracle.silu(np.array(0.0)) == 0.0 and oracle.gelu_tanh(np.array(0.0)) == 0.0
+
+
+# ----------------------------------------------------------------------------- storage pins
+
+def test_q8_0_golden_blocks():
+    doc = json.load(open(os.path.join(GOLDEN, "q8_0_blocks.json")))
+    raw, vals = [], []
+    for blk in doc["blocks"]:
+        bits = int(blk["scale_bits"], 16)
+        raw += [bits & 0xFF, bits >> 8] + [q & 0xFF for q in blk["q"]]
+        vals += [blk["scale"] * q for q in blk["q"]]
+    got = oracle.dequant_q8_0(np.array(raw, dtype=np.uint8), doc["rows"], doc["cols"])
+    assert np.array_equal(got.reshape(-1), np.array(vals))
+
+
+def test_q8_0_encoder_bounds():
+    rng = np.random.default_rng(4)
+    w = (0.02 * rng.standard_normal((16, 256))).astype(np.float32)
+    w[3, 32:64] = 0.0
+    blocks = q8_0_encode(w)
+    deq = oracle.dequant_q8_0(blocks, 16, 256)
+    raw = blocks.reshape(16, 8, 34)
+    d16 = raw[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    q = raw[..., 2:].copy().view(np.int8).astype(np.int32)
+    wb = w.reshape(16, 8, 32).astype(np.float64)
+    amax = np.abs(wb).max(axis=2)
+    d32 = amax / 127.0
+    err = np.abs(deq.reshape(16, 8, 32) - wb)
+    # half a quantisation step plus the fp16 rounding of the scale (at most 127 * |d16 - d32|)
+    bound = d32 / 2 + 127 * np.abs(d16 - d32) + 1e-12
+    assert np.all(err <= bound[..., None])
+    nz = amax > 0
+    imax = np.abs(wb).argmax(axis=2)
+    qmax = np.take_along_axis(q, imax[..., None], axis=2)[..., 0]
+    assert np.all(np.abs(qmax[nz]) == 127)
+    assert np.all(d16[~nz] == 0) and np.all(q[~nz] == 0)
+    # fp16 scale x int8 code is exact in fp32
+    f32 = (d16[..., None].astype(np.float32) * q.astype(np.float32)).astype(np.float64)
+    assert np.array_equal(f32, d16[..., None] * q)
+
+
+def test_bf16_encoder_round_to_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1e-3, 3.0e38], dtype=np.float32)
+    bits = f32_to_bf16_bits(vals)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(100000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f32_to_bf16_bits(x), ref)
+    assert nrel(oracle.bf16_bits_to_f64(ref), torch.from_numpy(x).to(torch.bfloat16).double().numpy()) == 0
+
+
+# ----------------------------------------------------------------------------- shard-map pins
+
+@pytest.mark.parametrize("name", ["tiny-llama-fp32", "small-q8", "small-prefill-n4"])
+def test_shard_maps_and_bytes(name):
+    s = {x.name: x for x in SMALL_SHAPES}[name]
+    inp = make_inputs(s)
+    p = oracle.params_f64(inp)
+    parts = [oracle.shard_weights(s, p, r) for r in range(s.tp)]
+    assert np.array_equal(np.concatenate([w["wo"] for w in parts], axis=1), p["wo"])
+    assert np.array_equal(np.concatenate([w["wd"] for w in parts], axis=1), p["wd"])
+    for key_full, keys in (("qkv", ("wq", "wk", "wv")), ("gu", ("wg", "wu"))):
+        full = np.concatenate([p[k] for k in keys], axis=0)
+        fused = np.concatenate([np.concatenate([w[k] for k in keys], axis=0) for w in parts])
+        a = sorted(map(tuple, full.tolist()))
+        b = sorted(map(tuple, fused.tolist()))
+        assert a == b, key_full
+    counts = [sum(w[k].size for k in w) for w in parts]
+    total = sum(p[k].size for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"))
+    assert all(c * s.tp == total for c in counts)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _rope_wrong_sign(vec, position, base):
+    hd = vec.shape[-1]
+    c, s = ob.rope_cos_sin(position, hd, base)
+    a, b = vec[..., : hd // 2], vec[..., hd // 2:]
+    return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)
+
+
+def _rope_interleaved(vec, position, base):
+    hd = vec.shape[-1]
+    c, s = ob.rope_cos_sin(position, hd, base)
+    a, b = vec[..., 0::2], vec[..., 1::2]
+    out = np.empty_like(vec)
+    out[..., 0::2], out[..., 1::2] = a * c - b * s, b * c + a * s
+    return out
+
+
+def _norm_no_eps(x, gamma, eps):
+    return gamma * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+
+
+def _attend_no_scale(q, keys, values):
+    s = keys @ q
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ values
+
+
+def _attend_no_max(q, keys, values):
+    s = keys @ q / np.sqrt(q.shape[-1])
+    w = np.exp(s)
+    return (w / (w.sum() + 1e-3)) @ values
+
+
+PLANTS = {
+    "rope_sign": ("rope", _rope_wrong_sign),
+    "rope_interleaved": ("rope", _rope_interleaved),
+    "norm_no_eps": ("rms_norm", _norm_no_eps),
+    "attn_no_scale": ("attend", _attend_no_scale),
+    "attn_bad_normaliser": ("attend", _attend_no_max),
+    "silu_for_gelu": ("gelu_tanh", lambda z: z / (1 + np.exp(-z))),
+}
+
+
+@pytest.mark.parametrize("plant", sorted(PLANTS))
+def test_planted_mistake_is_caught(plant, monkeypatch):
+    fn_name, bad = PLANTS[plant]
+    s = {x.name: x for x in SMALL_SHAPES}["small-q8"]
+    inp = make_inputs(s, seed=9)
+    ref = torch_block(inp)
+    monkeypatch.setattr(ob, fn_name, bad)
+    if fn_name == "gelu_tanh":
+        monkeypatch.setitem(ob.ACTIVATIONS, "gelu_tanh", bad)
+    caught = False
+    for sharded in (False, True):
+        res = oracle.run_block(inp, sharded=sharded)
+        caught |= any(nrel(res[k], ref[k].numpy()) > 1e-9 for k in ("xn", "h1", "xn2", "out"))
+    assert caught, plant
+
+
+def test_planted_gqa_mapping_is_caught(monkeypatch):
+    """A wrong query-head to KV-head mapping (heads of different groups swapped) must be caught."""
+    s = {x.name: x for x in SMALL_SHAPES}["small-prefill-n4"]
+    inp = make_inputs(s, seed=2)
+    ref = torch_block(inp)
+    real = ob.block_unsharded
+
+    def bad_unsharded(s_, p, x, kc, vc, positions, token_seq, rows=None):
+        s2 = s_.with_(n_heads=s_.n_heads)
+        perm = np.arange(s_.n_heads).reshape(s_.n_kv_heads, -1).T.reshape(-1)
+        p2 = dict(p)
+        hd = s_.head_dim
+        p2["wq"] = p["wq"].reshape(s_.n_heads, hd, -1)[perm].reshape(p["wq"].shape)
+        p2["wo"] = p["wo"].reshape(p["wo"].shape[0], s_.n_heads, hd)[:, perm].reshape(p["wo"].shape)
+        return real(s2, p2, x, kc, vc, positions, token_seq, rows)
+
+    ok = oracle.run_block(inp, sharded=False)
+    assert nrel(ok["out"], ref["out"].numpy()) <= 1e-12
+    monkeypatch.setattr(ob, "block_unsharded", bad_unsharded)
+    res = ob.run_block(inp, sharded=False)
+    assert nrel(res["attn"], ref["attn"].numpy()) > 1e-6
+
+
+def test_planted_transposed_wo_is_caught():
+    s = CONFIGS["tiny-llama-fp32"]          # d == Hq * hd, so a transposed Wo still fits
+    inp = make_inputs(s, seed=4)
+    ref = torch_block(inp)
+    p = oracle.params_f64(inp)
+    p["wo"] = p["wo"].T.copy()
+    x = oracle.to_f64(inp.x, s.act_dtype)
+    kc, vc = oracle.caches_f64(inp)
+    res = oracle.block_unsharded(s, p, x, kc, vc, inp.positions, inp.token_seq)
+    assert nrel(res["h1"], ref["h1"].numpy()) > 1e-6
