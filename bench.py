@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of one emulated N-rank tensor-parallel block step on one MI355X.
+
+A step is the whole path: the replicated RMSNorm, N ranks' attention halves (QKV projection,
+rotary embedding + paged KV append, owned-head attention, o_proj partial), the local N-way
+reduce + residual + RMSNorm, N ranks' FFN halves (gate/up + activation, down partial) and the
+final reduce + residual, for one batch of synthetic inputs already resident in HBM.
+
+Default workload: the Llama-3-8B-shaped block at tensor-parallel degree 2, bf16, decode of one
+token against a 4096-token KV cache. Timing: every step is captured as a HIP graph; `copies`
+independent sets of shards and KV caches (>= 1 GB in total) rotate so repeats cannot be served
+from the 256 MB last-level cache. One JSON line on stdout; progress on stderr.
+
+Roofline: the dominant kernel is the gate/up projection (the largest weight stream of a rank).
+Its average duration is measured live with HIP events recorded by the library immediately around
+its launch, on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes(s):
+    from tensor_transformer_block_amd.inputs import weight_shapes
+    per = {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[s.w_dtype]
+    return int(sum(o * i for o, i in weight_shapes(s).values()) * per)
+
+
+def step_bytes(s):
+    """Algorithmic HBM bytes of one block step, all N ranks: every shard's weights once, the KV
+    read of every attended key (new one included) for all heads, the N partials written and read
+    at the activation dtype per half, and the residual read and written per half."""
+    act = 4 if s.act_dtype == "f32" else 2
+    kv = sum(s.kv_lens) * s.n_kv_heads * s.head_dim * act * 2
+    if s.mode == "prefill":
+        kv = s.n_tokens * s.n_kv_heads * s.head_dim * act * 2
+    a = 4 * s.tp * s.n_tokens * s.d_model * act + 4 * s.n_tokens * s.d_model * act
+    return weight_bytes(s) + kv + a
+
+
+def step_flops(s):
+    """Projection FLOPs 2*T*params plus causal attention 4*hd per attended (query, key) pair."""
+    params = sum(o * i for o, i in __import__(
+        "tensor_transformer_block_amd.inputs", fromlist=["weight_shapes"]).weight_shapes(s).values())
+    pairs = 0
+    if s.mode == "prefill":
+        L = s.kv_lens[0]
+        pairs = sum(p + 1 for p in range(L - s.n_tokens, L))
+    else:
+        pairs = sum(s.kv_lens)
+    return 2.0 * s.n_tokens * params + 4.0 * s.head_dim * s.n_heads * pairs
+
+
+def gate_up_unit(s):
+    """Algorithmic bytes and FLOPs of one gate/up launch (one rank): the weight slice once, the
+    normed input read and the activation output written."""
+    act = 4 if s.act_dtype == "f32" else 2
+    per = {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[s.w_dtype]
+    fr = s.ffn_dim // s.tp
+    wb = 2 * fr * s.d_model * per
+    return int(wb + s.n_tokens * s.d_model * act + s.n_tokens * fr * act), \
+        2.0 * s.n_tokens * 2 * fr * s.d_model
+
+
+def cpu_baseline(inp, seconds):
+    """The oracle's explicit N-rank block, fp64 NumPy, on the host cores, for a bounded sample."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    s = inp.shape
+    p = oracle.params_f64(inp)
+    x = oracle.to_f64(inp.x, s.act_dtype)
+    kc, vc = oracle.caches_f64(inp)
+    kr, vr = oracle.rank_caches(s, kc, vc)
+    rows = None
+    if s.mode == "prefill":
+        rows = np.array([s.n_tokens - 1])          # the last row attends to every key
+    ntok = s.n_tokens if rows is None else len(rows)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.block_sharded(s, p, x, kr, vr, inp.positions, inp.token_seq, rows)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (s.mode == "prefill" and n >= 1):
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    sample = (f"{n} full block steps (all {s.tp} ranks) of the same workload" if rows is None else
+              f"{n} step(s) of the same workload with the oracle producing {len(rows)} output "
+              f"row(s) (K/V and QKV for all {s.n_tokens} tokens)")
+    return {"value": round(n * ntok / el, 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample + f"; {el:.1f} s wall, fp64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="llama3-8b-decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-bytes", type=float, default=1.0e9,
+                    help="rotate at least this many bytes of distinct shards + KV caches")
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the N tensor-parallel ranks are emulated in sequence "
+              "on a single MI355X; runs on more than one GPU are not part of this build "
+              f"(got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import DeviceBlock
+    from tensor_transformer_block_amd.inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fails loudly if the HIP library is missing
+    s = CONFIGS[args.workload]
+    log(f"workload {s.name}: generating inputs (seed {args.seed})")
+    inp = make_inputs(s, seed=args.seed)
+    sb = step_bytes(s)
+    resident = weight_bytes(s) + sum(s.kv_lens) * s.n_kv_heads * s.head_dim * (
+        4 if s.act_dtype == "f32" else 2) * 2
+    copies = max(1, math.ceil(args.cold_bytes / resident))
+    log(f"building device block: {copies} cold cop{'y' if copies == 1 else 'ies'} "
+        f"x {resident / 1e6:.1f} MB")
+    blk = DeviceBlock(inp, copies=copies)
+    torch.cuda.synchronize()
+
+    for c in range(copies):
+        blk.step(c)
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                blk.step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                blk.step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            blk.step(i % copies)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok_s = s.n_tokens / (ms / 1e3)
+
+    # Dominant kernel: the gate/up projection, bracketed by events the library records on the
+    # launch stream. A backlog of graph replays keeps the stream busy so no host launch latency
+    # lands between the events.
+    log(f"timing the gate/up projection ({args.kernel_iters} launches)")
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.kernel_iters)]
+    for i in range(min(64, args.steps)):
+        run(i)
+    for i, (eb, ee) in enumerate(pairs):
+        c, r = i % copies, (i // copies) % s.tp
+        B.tp_block_shard_forward_timed(blk.desc, r, B.TP_HALF_FFN, blk.shards[c][r], blk.batch,
+                                       blk.xn2, None, blk.partials[r], blk.workspace, eb, ee,
+                                       blk.ws_bytes)
+    torch.cuda.synchronize()
+    kdur = [eb.elapsed_time(ee) * 1e-3 for eb, ee in pairs]
+    kavg = float(np.mean(kdur))
+    ub, uf = gate_up_unit(s)
+    if s.mode == "prefill":
+        roof = {"bound": "mfma", "achieved": round(uf / kavg / 1e12, 3),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(ub / kavg / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "gate/up projection (one rank)"
+    roof["avg_us"] = round(kavg * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    step_gbs = sb / (ms / 1e3) / 1e9
+    line = {
+        "metric": "shard decode tokens/s + achieved HBM GB/s (% of peak); prefill MFMA % peak",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": s.act_dtype, "data": "synthetic",
+        "config": {"workload": s.name, "d_model": s.d_model, "n_heads": s.n_heads,
+                   "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "ffn_dim": s.ffn_dim,
+                   "tp_degree_emulated": s.tp, "weights": s.w_dtype, "mode": s.mode,
+                   "tokens": s.n_tokens, "kv_len": max(s.kv_lens), "page_size": s.page_size,
+                   "cold_copies": copies, "graph": not args.no_graph},
+        "step_algorithmic_bytes": sb,
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_tflops": round(step_flops(s) / (ms / 1e3) / 1e12, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * tp_block.h - one rank's share of a Megatron-style tensor-parallel transformer block on one
+ * AMD Instinct MI355X (gfx950), with the N-way partial-sum reduce done locally.
+ *
+ * The operations follow these passages of the source pages:
+ *   [TS-HOW]   TensorSharp "Multi-GPU & Multi-Node", section "How tensor parallelism works":
+ *              column-parallel QKV and gate/up split the output dim (heads, FFN columns); attention
+ *              and the activation run per rank over the owned heads against that rank's own KV
+ *              cache; row-parallel o_proj and down split the input dim and emit partial sums; one
+ *              all-reduce per block half leaves every rank with the identical hidden state; norms
+ *              are replicated.
+ *   [TS-REQ]   same page, section "Requirements & constraints": head counts, KV-head counts and
+ *              the FFN width must divide by the degree; a block-quantised row-parallel split needs
+ *              its input dim divisible by degree x block size.
+ *   [ML-PROB]  mlxcel issue #488, section "Problem": the one-device runtime builds every rank's
+ *              shard from the full weights, runs the ranks in sequence and sums the partials
+ *              locally (reduce_sum).
+ *   [ML-ACC]   same issue, section "Acceptance criteria": running tp>1 on one device is legitimate
+ *              if it is explicit, and must never give silently wrong results.
+ *   [NN-CHG]   nnsight PR #677, section "Change": row-parallel layers split the input dim, the
+ *              others the output dim; fused weights keep their rows grouped by rank.
+ *
+ * Conventions for every call:
+ *   - All tensors are caller-owned device memory unless stated. The library allocates nothing,
+ *     keeps no state between calls and never synchronises the host, except tp_rope_table_init.
+ *   - `stream` is a hipStream_t (NULL = the default stream); every launch is asynchronous on it.
+ *   - Weights are [out, in] row-major (y = x * W^T). Activations are [tokens, features] row-major.
+ *   - Every argument is validated on the host before any launch; a failed call launches nothing
+ *     and returns a non-zero tp_status, with details in tp_last_error() (per calling thread).
+ *     Unsupported combinations are refused, never silently approximated [ML-ACC].
+ *   - Device-side indices (positions, block tables, page ids) are trusted; out-of-range values are
+ *     clamped into the buffers they index, so they cannot fault, but give unspecified results.
+ */
+#ifndef TP_BLOCK_H
+#define TP_BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tp_status;
+enum {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1,      /* null pointer, bad enum, non-positive size                    */
+  TP_ERR_RANK = 2,             /* rank outside [0, tp_degree)                                  */
+  TP_ERR_NOT_DIVISIBLE = 3,    /* heads / kv heads / ffn not divisible by the degree [TS-REQ]  */
+  TP_ERR_QUANT_ALIGN = 4,      /* Q8_0 split not on a 32-weight block boundary [TS-REQ]        */
+  TP_ERR_BUFFER_TOO_SMALL = 5, /* a caller buffer is smaller than the size query reports       */
+  TP_ERR_UNSUPPORTED = 6,      /* a dtype / shape / mode combination this build does not run   */
+  TP_ERR_HIP = 7               /* a HIP runtime or launch error                                */
+};
+
+enum { TP_DTYPE_F32 = 0, TP_DTYPE_BF16 = 1, TP_DTYPE_Q8_0 = 2 };
+enum { TP_ACT_SILU = 0, TP_ACT_GELU_TANH = 1 };
+enum { TP_HALF_ATTN = 0, TP_HALF_FFN = 1 };
+enum { TP_MODE_DECODE = 0, TP_MODE_PREFILL = 1 };
+
+/* Block shape and numeric formats. Plain data, no pointers.
+ * Supported (w_dtype, act_dtype): (F32, F32), (BF16, BF16), (Q8_0, BF16). The KV cache uses the
+ * activation dtype. partial_dtype: F32 (default) or BF16. head_dim: 64, 128 or 256.
+ * n_heads / n_kv_heads: 1, 2, 4 or 8. rms_eps is added inside the square root; rope_base is the
+ * rotary base. max_position bounds every position (size of the rotary table). */
+typedef struct {
+  int32_t d_model, n_heads, n_kv_heads, head_dim, ffn_dim, tp_degree, page_size, max_position;
+  float rms_eps, rope_base;
+  int32_t w_dtype, act_dtype, partial_dtype, ffn_act;
+} tp_block_desc;
+
+typedef struct {
+  uint64_t offset, bytes;
+} tp_region;
+
+/* Where rank r's slices live inside its packed shard buffer (offsets 256-byte aligned).
+ *   qkv     [(Hq/N + 2 Hkv/N) * hd, d]: Wq rows of the owned query heads, then Wk rows, then Wv
+ *           rows of the owned KV heads (column-parallel, rows grouped by rank [NN-CHG]).
+ *   o       [d, Hq/N * hd]: the Wo columns of the owned query heads (row-parallel).
+ *   gate_up [2 F/N, d]: the Wg rows of the owned FFN columns, then the Wu rows.
+ *   down    [d, F/N]: the Wd columns of the owned FFN columns (row-parallel).
+ * For Q8_0 these regions hold the int8 codes ([out, in], one byte per weight) and the *_scale
+ * regions the fp16 block scales ([out, in/32]); for other dtypes *_scale.bytes is 0.
+ * payload_bytes is exactly 1/N of the full block's weight bytes; alloc_bytes adds alignment. */
+typedef struct {
+  tp_region qkv, o, gate_up, down;
+  tp_region qkv_scale, o_scale, gate_up_scale, down_scale;
+  uint64_t payload_bytes, alloc_bytes;
+} tp_shard_layout;
+
+/* Full (unsharded) weights, device pointers, [out, in] row-major:
+ * wq [Hq*hd, d], wk and wv [Hkv*hd, d], wo [d, Hq*hd], wg and wu [F, d], wd [d, F].
+ * F32 / BF16: plain elements. Q8_0: per row, in/32 blocks of 34 bytes (fp16 scale, 32 int8). */
+typedef struct {
+  const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+} tp_full_weights;
+
+/* One step's token batch. Device arrays: positions [n_tokens]; seq_lens [n_seqs] (keys attended by
+ * the sequence's last token, new tokens included); block_table [n_seqs, max_pages] (physical page
+ * of every page_size-token page). rope_table: the table tp_rope_table_init filled.
+ * DECODE: one new token per sequence, token b belongs to sequence b (n_tokens == n_seqs).
+ * PREFILL: n_seqs == 1; all tokens belong to sequence 0.
+ * Token t attends the keys at positions 0..positions[t] of its sequence (causal).
+ * max_seq_len (host value): an upper bound of positions[t] + 1 over the batch, at most
+ * max_pages * page_size and max_position; it sizes the split-KV grid. */
+typedef struct {
+  int32_t mode, n_tokens, n_seqs, max_pages, max_seq_len;
+  const int32_t* positions;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const float* rope_table;
+} tp_batch;
+
+/* Rank r's paged KV cache: k_pages and v_pages are [n_pages][Hkv/N][page_size][hd] in the
+ * activation dtype, holding only the KV heads rank r owns [TS-HOW]. K is stored after the rotary
+ * embedding. */
+typedef struct {
+  void* k_pages;
+  void* v_pages;
+  int32_t n_pages;
+} tp_kv_cache;
+
+/* Fill `out` with rank r's packed-shard layout. Host only; runs the full shape validation
+ * ([TS-REQ] divisibility and Q8_0 block alignment). */
+tp_status tp_shard_weights_size(const tp_block_desc* desc, int32_t rank, tp_shard_layout* out);
+
+/* Build rank r's shard from the full weights (the from_full_weights step of [ML-PROB]): copy its
+ * slices [TS-HOW] into `dst` (device, dst_bytes >= alloc_bytes) in the layout above. Q8_0 blocks
+ * are split into codes and scales. Norm weights are not sharded: callers pass the replicated
+ * gamma directly to tp_partial_reduce. */
+tp_status tp_shard_weights(const tp_block_desc* desc, int32_t rank, const tp_full_weights* src,
+                           void* dst, uint64_t dst_bytes, void* stream);
+
+/* Bytes of workspace tp_block_shard_forward needs for this batch (either half). */
+tp_status tp_workspace_size(const tp_block_desc* desc, const tp_batch* batch, uint64_t* bytes);
+
+/* Bytes of the rotary table: max_position * head_dim/2 pairs of fp32 (cos, sin). */
+tp_status tp_rope_table_bytes(const tp_block_desc* desc, uint64_t* bytes);
+
+/* Fill the rotary table: entry [p][i] = (cos, sin)(p * rope_base^(-2i/head_dim)), computed on the
+ * host in fp64, rounded to fp32 and copied to `dev_table`. Synchronises `stream`. */
+tp_status tp_rope_table_init(const tp_block_desc* desc, void* dev_table, uint64_t table_bytes,
+                             void* stream);
+
+/* One rank's share of one block half [TS-HOW], given the replicated normed input xn [T, d]
+ * (activation dtype):
+ *   ATTN: qkv_r = xn W_qkv,r^T; rotary embedding of q and k at the token positions; K and V of the
+ *         new tokens written into rank r's cache `kv`; causal attention of every owned query head
+ *         over its KV head (group = head / (Hq/Hkv)); partial_out = a_r W_o,r^T.
+ *   FFN:  [g ; u] = xn W_gu,r^T; m_r = act(g) * u; partial_out = m_r W_down,r^T.
+ * partial_out is [T, d] in partial_dtype; only it, the workspace and (ATTN) `kv` are written.
+ * workspace: device, at least tp_workspace_size bytes. n_tokens == 0 is a no-op. */
+tp_status tp_block_shard_forward(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                 const void* shard, const tp_batch* batch, const void* xn,
+                                 const tp_kv_cache* kv, void* partial_out, void* workspace,
+                                 uint64_t workspace_bytes, void* stream);
+
+/* Measurement variant of tp_block_shard_forward: the same work, plus hipEventRecord(ev_begin)
+ * on `stream` immediately before, and hipEventRecord(ev_end) immediately after, the launch of the
+ * half's dominant weight stream (ATTN: the QKV projection; FFN: the gate/up projection). The
+ * events are caller-created hipEvent_t handles; NULL skips that record. Not for graph capture. */
+tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                       const void* shard, const tp_batch* batch, const void* xn,
+                                       const tp_kv_cache* kv, void* partial_out, void* workspace,
+                                       uint64_t workspace_bytes, void* stream, void* ev_begin,
+                                       void* ev_end);
+
+/* The local copy-and-reduce step [ML-PROB] that stands in for the all-reduce [TS-HOW]:
+ *   residual_out[t] = residual_in[t] + (((P_0[t] + P_1[t]) + ...) + P_{n-1}[t])
+ * summed in fp32 in rank order (the partials first, then the residual) and rounded once to the
+ * activation dtype; then, if gamma is not NULL, normed_out = RMSNorm(residual_out) * gamma over
+ * d_model (fp32 math on the stored, rounded values).
+ * partials: [n_partials, n_tokens, d] in partial_dtype. residual_in/out, gamma, normed_out:
+ * activation dtype, [n_tokens, d] ([d] for gamma). residual_out may alias residual_in.
+ * n_partials == 0 gives a pure RMSNorm of residual_in (partials and residual_out may be NULL).
+ * n_tokens == 0 is a no-op. */
+tp_status tp_partial_reduce(const tp_block_desc* desc, int32_t n_tokens, const void* partials,
+                            int32_t n_partials, const void* residual_in, void* residual_out,
+                            const void* gamma, void* normed_out, void* stream);
+
+const char* tp_status_str(tp_status status);
+/* Detail of the calling thread's last failure ("" if none). */
+const char* tp_last_error(void);
+
+/* ---- test helpers: they run the same device index and dequant code as the hot path ---- */
+
+/* Scatter rank r's packed shard back to full-size logical matrices (device, same formats as
+ * tp_shard_weights' input); every element outside rank r's slices is left untouched. */
+tp_status tp_shard_unpack(const tp_block_desc* desc, int32_t rank, const void* shard,
+                          const tp_full_weights* dst, void* stream);
+
+/* Dequantise n_blocks Q8_0 blocks held as codes [n_blocks*32] int8 and scales [n_blocks] fp16
+ * into out [n_blocks*32] fp32: out = float(scale) * code. */
+tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uint64_t n_blocks,
+                          void* stream);
+
+/* Byte offsets, inside the workspace, of the intermediates of the last forward call with this
+ * desc/batch: post-rotary q [T, Hq/N*hd], attention output a_r [T, Hq/N*hd] (activation dtype),
+ * and the FFN activation m_r [T, F/N] (activation dtype). */
+tp_status tp_workspace_offsets(const tp_block_desc* desc, const tp_batch* batch,
+                               uint64_t* q_offset, uint64_t* attn_offset, uint64_t* ffn_offset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_BLOCK_H */

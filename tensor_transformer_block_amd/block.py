@@ -1,0 +1,170 @@
+"""Device buffers and the C-ABI call sequence of one emulated N-rank block step on one GPU.
+
+A block step (mlxcel issue #488, "Problem": every rank runs in sequence on one device and the
+partials are summed locally; TensorSharp "How tensor parallelism works": one reduce per half):
+
+    xn  = RMSNorm(x) * gamma1                               tp_partial_reduce (no partials)
+    for r in 0..N-1: P[r] = rank r's attention half          tp_block_shard_forward(ATTN, r)
+    h1  = x + sum_r P[r];  xn2 = RMSNorm(h1) * gamma2        tp_partial_reduce
+    for r in 0..N-1: P[r] = rank r's FFN half                tp_block_shard_forward(FFN, r)
+    out = h1 + sum_r P[r]                                     tp_partial_reduce
+
+Everything runs on the current HIP stream; this module only allocates torch tensors and passes
+their addresses. ``copies`` > 1 keeps that many independent sets of shards and KV caches so a
+timing loop can rotate through more bytes than the last-level cache holds.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .inputs import BlockInputs, paged_prior_cache
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Storage array (fp32 / bf16 bit patterns / Q8_0 bytes) -> torch tensor on `device`."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16))
+        return t.to(device).view(torch.bfloat16)
+    if dtype == "q8_0":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+    raise ValueError(dtype)
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Device tensor -> storage array (inverse of ``to_device``)."""
+    if dtype == "bf16":
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    if dtype == "f32":
+        return t.contiguous().cpu().numpy().astype(np.float32)
+    return t.contiguous().cpu().numpy()
+
+
+def act_torch_dtype(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+class DeviceBlock:
+    """One block's shards, caches and buffers on the GPU, for all N emulated ranks."""
+
+    def __init__(self, inp: BlockInputs, device="cuda", partial_dtype: str = "f32",
+                 copies: int = 1, keep_full: bool = False):
+        s = inp.shape
+        self.inp, self.shape, self.device = inp, s, device
+        self.N, self.T = s.tp, s.n_tokens
+        self.desc = B.make_desc(s, partial_dtype)
+        self.partial_dtype = partial_dtype
+        adt = act_torch_dtype(s.act_dtype)
+
+        full = {k: to_device(v, s.w_dtype, device) for k, v in inp.weights.items()}
+        self.full = full if keep_full else None
+        fw = B.full_weights(full)
+        self.layouts = [B.tp_shard_weights_size(self.desc, r) for r in range(self.N)]
+        self.shards = []          # [copy][rank]
+        for _ in range(copies):
+            row = []
+            for r in range(self.N):
+                buf = torch.empty(self.layouts[r].alloc_bytes, dtype=torch.uint8, device=device)
+                B.tp_shard_weights(self.desc, r, fw, buf)
+                row.append(buf)
+            self.shards.append(row)
+        torch.cuda.synchronize()
+        del fw
+        if not keep_full:
+            del full
+
+        self.gamma1 = to_device(inp.gamma1, s.act_dtype, device)
+        self.gamma2 = to_device(inp.gamma2, s.act_dtype, device)
+        self.x = to_device(inp.x, s.act_dtype, device)
+        self.positions = torch.from_numpy(inp.positions).to(device)
+        self.seq_lens = torch.from_numpy(inp.seq_lens).to(device)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(inp.block_table)).to(device)
+        self.rope = torch.empty(B.tp_rope_table_bytes(self.desc) // 4, dtype=torch.float32,
+                                device=device)
+        B.tp_rope_table_init(self.desc, self.rope)
+
+        self.max_pages = int(inp.block_table.shape[1])
+        self.max_seq_len = int(max(inp.seq_lens))
+        self.batch = B.make_batch(s.mode, self.T, s.n_seqs, self.max_pages, self.max_seq_len,
+                                  self.positions, self.seq_lens, self.block_table, self.rope)
+
+        # Per copy, per rank: paged K/V pools holding the owned KV heads' prior keys/values.
+        self.kv_host = [paged_prior_cache(inp, r) for r in range(self.N)]
+        self.k_pages, self.v_pages, self.kv = [], [], []
+        for _ in range(copies):
+            kr, vr, cr = [], [], []
+            for r in range(self.N):
+                kp = to_device(self.kv_host[r][0], s.act_dtype, device)
+                vp = to_device(self.kv_host[r][1], s.act_dtype, device)
+                kr.append(kp)
+                vr.append(vp)
+                cr.append(B.tp_kv_cache(k_pages=kp.data_ptr(), v_pages=vp.data_ptr(),
+                                        n_pages=inp.n_pages))
+            self.k_pages.append(kr)
+            self.v_pages.append(vr)
+            self.kv.append(cr)
+
+        pdt = torch.float32 if partial_dtype == "f32" else torch.bfloat16
+        self.partials = torch.empty((self.N, self.T, s.d_model), dtype=pdt, device=device)
+        self.xn = torch.empty((self.T, s.d_model), dtype=adt, device=device)
+        self.xn2 = torch.empty_like(self.xn)
+        self.h1 = torch.empty_like(self.xn)
+        self.out = torch.empty_like(self.xn)
+        self.ws_bytes = B.tp_workspace_size(self.desc, self.batch)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.copies = copies
+
+    # --------------------------------------------------------------------------- the step
+    def attn_half(self, rank: int, copy: int = 0, partial=None):
+        B.tp_block_shard_forward(self.desc, rank, B.TP_HALF_ATTN, self.shards[copy][rank],
+                                 self.batch, self.xn, self.kv[copy][rank],
+                                 self.partials[rank] if partial is None else partial,
+                                 self.workspace, self.ws_bytes)
+
+    def ffn_half(self, rank: int, copy: int = 0, partial=None):
+        B.tp_block_shard_forward(self.desc, rank, B.TP_HALF_FFN, self.shards[copy][rank],
+                                 self.batch, self.xn2, None,
+                                 self.partials[rank] if partial is None else partial,
+                                 self.workspace, self.ws_bytes)
+
+    def step(self, copy: int = 0):
+        """One full block step on the current stream; the result lands in ``self.out``."""
+        d, T, N = self.desc, self.T, self.N
+        B.tp_partial_reduce(d, T, None, 0, self.x, None, self.gamma1, self.xn)
+        for r in range(N):
+            self.attn_half(r, copy)
+        B.tp_partial_reduce(d, T, self.partials, N, self.x, self.h1, self.gamma2, self.xn2)
+        for r in range(N):
+            self.ffn_half(r, copy)
+        B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, None, None)
+
+    # --------------------------------------------------------------------------- readback
+    def workspace_views(self):
+        """Views of the last forward's intermediates: q [T, Hq/N*hd], a_r [T, Hq/N*hd], m_r."""
+        s = self.shape
+        qo, ao, fo = B.tp_workspace_offsets(self.desc, self.batch)
+        adt = act_torch_dtype(s.act_dtype)
+        es = 4 if s.act_dtype == "f32" else 2
+        qd = s.n_heads // s.tp * s.head_dim
+        fr = s.ffn_dim // s.tp
+
+        def view(off, cols):
+            return self.workspace[off: off + self.T * cols * es].view(adt).view(self.T, cols)
+        return view(qo, qd), view(ao, qd), view(fo, fr)
+
+    def cache_new_entries(self, rank: int, copy: int = 0):
+        """The K and V the last ATTN call of ``rank`` wrote, as [T, Hkv/N, hd] storage arrays."""
+        s = self.shape
+        kp = to_host(self.k_pages[copy][rank], s.act_dtype)
+        vp = to_host(self.v_pages[copy][rank], s.act_dtype)
+        ks, vs = [], []
+        for t in range(self.T):
+            b = int(self.inp.token_seq[t])
+            p = int(self.inp.positions[t])
+            phys = self.inp.block_table[b, p // s.page_size]
+            ks.append(kp[phys, :, p % s.page_size])
+            vs.append(vp[phys, :, p % s.page_size])
+        return np.stack(ks), np.stack(vs)

@@ -1,0 +1,162 @@
+// K4: bf16 projections for many tokens (batched decode, prefill) on the CDNA4 matrix cores.
+//
+// C[m, n] = sum_k A[m, k] B[n, k]: A = activations [M, K], B = weights [N, K], both K-contiguous,
+// so both MFMA operands are plain 16-byte loads of 8 consecutive k. Workgroup tile 64 x 64 x 64,
+// four waves in a 2 x 2 grid, each wave 32 x 32 = 2 x 2 tiles of v_mfma_f32_16x16x32_bf16.
+// A and B tiles are staged through LDS (double-buffered, rows padded by 16 bytes against bank
+// conflicts); the next tile's global loads are issued before the current tile's MFMAs.
+//
+// MFMA 16x16x32 operand layout (gfx950): lane l supplies row (l % 16) of A and column (l % 16) of
+// B, each as 8 consecutive k starting at 8 * (l / 16); the 16 x 16 fp32 result lands with lane l
+// holding rows 4 * (l / 16) + r, r = 0..3, of column l % 16. A and B use the same k assignment, so
+// the contraction over k does not depend on how the hardware orders k within the instruction.
+//
+// Epilogues as in the GEMV: activation-dtype store (QKV), fp32 / bf16 partial store (row-parallel
+// o_proj and down), and the fused gate/up pair: B2 holds the up rows, act(g) * u is stored.
+#include "tp_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+constexpr int GB_M = 64, GB_N = 64, GB_K = 64;
+constexpr int G_LDS_LD = GB_K + 8;  // bf16 elements per LDS row
+
+template <int EPI, int ACTF>
+__global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ A,
+                                                   const uint16_t* __restrict__ B,
+                                                   const uint16_t* __restrict__ B2, int M, int N,
+                                                   int K, void* __restrict__ C, int ldc) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int NB = DUAL ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][GB_M * G_LDS_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][NB][GB_N * G_LDS_LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * GB_M, n0 = blockIdx.x * GB_N;
+
+  // Global -> register staging: each thread moves 2 chunks of 8 bf16 per operand tile.
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  uint4 ra[2], rb[NB][2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 32 * h, k = k0 + lc;
+      const bool kin = k < K;
+      ra[h] = (m0 + r < M && kin) ? *(const uint4*)(A + (size_t)(m0 + r) * K + k)
+                                  : make_uint4(0, 0, 0, 0);
+      const bool nin = (n0 + r < N) && kin;
+      rb[0][h] = nin ? *(const uint4*)(B + (size_t)(n0 + r) * K + k) : make_uint4(0, 0, 0, 0);
+      if constexpr (DUAL)
+        rb[NB - 1][h] = nin ? *(const uint4*)(B2 + (size_t)(n0 + r) * K + k)
+                            : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 32 * h;
+      *(uint4*)(&sA[buf][r * G_LDS_LD + lc]) = ra[h];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *(uint4*)(&sB[buf][b][r * G_LDS_LD + lc]) = rb[b][h];
+    }
+  };
+
+  floatx4 acc[NB][2][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[b][i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + GB_K - 1) / GB_K;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * GB_K);
+#pragma unroll
+    for (int kk = 0; kk < GB_K; kk += 32) {
+      bf16x8 af[2], bfr[NB][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *(const bf16x8*)(&sA[cur][(wm * 32 + i * 16 + fr) * G_LDS_LD + kk + fk]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[b][j] = *(const bf16x8*)(&sB[cur][b][(wn * 32 + j * 16 + fr) * G_LDS_LD + kk + fk]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[b][i][j] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      sstore(cur ^ 1);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds C[row0 + r][col] for r = 0..3.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 32 + j * 16 + (lane & 15);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+        if (row >= M) continue;
+        const size_t o = (size_t)row * ldc + col;
+        const float v = acc[0][i][j][r];
+        if constexpr (EPI == EPI_GATED) {
+          ((uint16_t*)C)[o] = f32_to_bf16(gated<ACTF>(v, acc[NB - 1][i][j][r]));
+        } else if constexpr (EPI == EPI_F32) {
+          ((float*)C)[o] = v;
+        } else {
+          ((uint16_t*)C)[o] = f32_to_bf16(v);  // EPI_ACT (bf16 activations) and EPI_BF16
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
+                            const void* B2, void* C, int ldc, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  dim3 g((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M), b(256);
+  const uint16_t *a = (const uint16_t*)A, *bb = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
+  switch (epi) {
+    case EPI_ACT:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_ACT, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      break;
+    case EPI_F32:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_F32, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((k_gemm_bf16<EPI_BF16, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      break;
+    case EPI_GATED:
+      if (actf == 0)
+        hipLaunchKernelGGL((k_gemm_bf16<EPI_GATED, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      else
+        hipLaunchKernelGGL((k_gemm_bf16<EPI_GATED, 1>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -1,0 +1,518 @@
+// libtpblock C ABI: validation, shard and workspace layouts, and the launch sequences of one rank's
+// block half and of the local partial-sum reduce. See include/tp_block.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/tp_block.h"
+#include "tp_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+tp_status hip_fail(hipError_t e, const char* where) {
+  return fail(TP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Dims {
+  int d, Hq, Hkv, hd, F, N, ps, maxpos;
+  int hq, hk, fr, qdim, qkv_rows;
+  int wt, at, pt, actf;
+  float eps, base;
+  int wb;  // bytes per weight element (Q8_0: one code byte; scales are separate)
+  int ab;  // bytes per activation element
+};
+
+tp_status check_desc(const tp_block_desc* desc, Dims* o) {
+  if (!desc) return fail(TP_ERR_INVALID_ARG, "desc is NULL");
+  const tp_block_desc& D = *desc;
+  if (D.d_model <= 0 || D.n_heads <= 0 || D.n_kv_heads <= 0 || D.head_dim <= 0 ||
+      D.ffn_dim <= 0 || D.tp_degree <= 0 || D.page_size <= 0 || D.max_position <= 0)
+    return fail(TP_ERR_INVALID_ARG,
+                "dimensions must be positive (d_model=%d n_heads=%d n_kv_heads=%d head_dim=%d "
+                "ffn_dim=%d tp_degree=%d page_size=%d max_position=%d)",
+                D.d_model, D.n_heads, D.n_kv_heads, D.head_dim, D.ffn_dim, D.tp_degree,
+                D.page_size, D.max_position);
+  if (!(D.rms_eps >= 0.f) || !std::isfinite(D.rms_eps))
+    return fail(TP_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(D.rope_base > 0.f) || !std::isfinite(D.rope_base))
+    return fail(TP_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (D.w_dtype < TP_DTYPE_F32 || D.w_dtype > TP_DTYPE_Q8_0)
+    return fail(TP_ERR_INVALID_ARG, "unknown w_dtype %d", D.w_dtype);
+  if (D.act_dtype != TP_DTYPE_F32 && D.act_dtype != TP_DTYPE_BF16)
+    return fail(TP_ERR_INVALID_ARG, "act_dtype must be F32 or BF16 (got %d)", D.act_dtype);
+  if (D.partial_dtype != TP_DTYPE_F32 && D.partial_dtype != TP_DTYPE_BF16)
+    return fail(TP_ERR_INVALID_ARG, "partial_dtype must be F32 or BF16 (got %d)", D.partial_dtype);
+  if (D.ffn_act != TP_ACT_SILU && D.ffn_act != TP_ACT_GELU_TANH)
+    return fail(TP_ERR_INVALID_ARG, "unknown ffn_act %d", D.ffn_act);
+  const bool combo_ok = (D.w_dtype == TP_DTYPE_F32 && D.act_dtype == TP_DTYPE_F32) ||
+                        (D.w_dtype == TP_DTYPE_BF16 && D.act_dtype == TP_DTYPE_BF16) ||
+                        (D.w_dtype == TP_DTYPE_Q8_0 && D.act_dtype == TP_DTYPE_BF16);
+  if (!combo_ok)
+    return fail(TP_ERR_UNSUPPORTED,
+                "weight/activation dtypes (%d, %d) are not built; supported: (F32, F32), "
+                "(BF16, BF16), (Q8_0, BF16)",
+                D.w_dtype, D.act_dtype);
+  const int N = D.tp_degree;
+  if (D.n_heads % N || D.n_kv_heads % N || D.ffn_dim % N)
+    return fail(TP_ERR_NOT_DIVISIBLE,
+                "n_heads=%d, n_kv_heads=%d and ffn_dim=%d must all divide by tp_degree=%d",
+                D.n_heads, D.n_kv_heads, D.ffn_dim, N);
+  if (D.n_heads % D.n_kv_heads)
+    return fail(TP_ERR_NOT_DIVISIBLE, "n_heads=%d must be a multiple of n_kv_heads=%d", D.n_heads,
+                D.n_kv_heads);
+  if (D.w_dtype == TP_DTYPE_Q8_0) {
+    if (D.d_model % 32)
+      return fail(TP_ERR_QUANT_ALIGN, "Q8_0 needs d_model %% 32 == 0 (d_model=%d)", D.d_model);
+    if ((D.n_heads * D.head_dim) % (N * 32))
+      return fail(TP_ERR_QUANT_ALIGN,
+                  "Q8_0 row-parallel o_proj split needs n_heads*head_dim=%d divisible by "
+                  "tp_degree*32=%d",
+                  D.n_heads * D.head_dim, N * 32);
+    if (D.ffn_dim % (N * 32))
+      return fail(TP_ERR_QUANT_ALIGN,
+                  "Q8_0 row-parallel down split needs ffn_dim=%d divisible by tp_degree*32=%d",
+                  D.ffn_dim, N * 32);
+  }
+  const int G = D.n_heads / D.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(TP_ERR_UNSUPPORTED, "n_heads/n_kv_heads=%d: built for 1, 2, 4 or 8", G);
+  if (D.head_dim != 64 && D.head_dim != 128 && D.head_dim != 256)
+    return fail(TP_ERR_UNSUPPORTED, "head_dim=%d: built for 64, 128 or 256", D.head_dim);
+  if (D.page_size % 16)
+    return fail(TP_ERR_UNSUPPORTED, "page_size=%d: must be a multiple of 16", D.page_size);
+  const int fr = D.ffn_dim / N;
+  if (D.d_model % 8 || fr % 8)
+    return fail(TP_ERR_UNSUPPORTED,
+                "d_model=%d and ffn_dim/tp_degree=%d must be multiples of 8 (16-byte vectors)",
+                D.d_model, fr);
+  if (D.d_model > 16384)
+    return fail(TP_ERR_UNSUPPORTED, "d_model=%d: built for at most 16384", D.d_model);
+  Dims& x = *o;
+  x.d = D.d_model; x.Hq = D.n_heads; x.Hkv = D.n_kv_heads; x.hd = D.head_dim; x.F = D.ffn_dim;
+  x.N = N; x.ps = D.page_size; x.maxpos = D.max_position;
+  x.hq = D.n_heads / N; x.hk = D.n_kv_heads / N; x.fr = fr;
+  x.qdim = x.hq * x.hd; x.qkv_rows = (x.hq + 2 * x.hk) * x.hd;
+  x.wt = D.w_dtype; x.at = D.act_dtype; x.pt = D.partial_dtype; x.actf = D.ffn_act;
+  x.eps = D.rms_eps; x.base = D.rope_base;
+  x.wb = D.w_dtype == TP_DTYPE_F32 ? 4 : (D.w_dtype == TP_DTYPE_BF16 ? 2 : 1);
+  x.ab = D.act_dtype == TP_DTYPE_F32 ? 4 : 2;
+  return TP_OK;
+}
+
+void make_layout(const Dims& x, tp_shard_layout* L) {
+  *L = tp_shard_layout{};
+  uint64_t off = 0, payload = 0;
+  auto put = [&](tp_region& r, uint64_t rows, uint64_t cols, tp_region& sc) {
+    r.offset = off;
+    r.bytes = rows * cols * (uint64_t)x.wb;
+    off = align_up(off + r.bytes);
+    payload += r.bytes;
+    if (x.wt == TP_DTYPE_Q8_0) {
+      sc.offset = off;
+      sc.bytes = rows * (cols / 32) * 2;
+      off = align_up(off + sc.bytes);
+      payload += sc.bytes;
+    }
+  };
+  put(L->qkv, x.qkv_rows, x.d, L->qkv_scale);
+  put(L->o, x.d, x.qdim, L->o_scale);
+  put(L->gate_up, 2 * (uint64_t)x.fr, x.d, L->gate_up_scale);
+  put(L->down, x.d, x.fr, L->down_scale);
+  L->payload_bytes = payload;
+  L->alloc_bytes = off;
+}
+
+struct WsLayout {
+  uint64_t qkv, q, attn, part_o, part_ml, ffn, total;
+  int n_split, chunk, pos_limit;
+};
+
+tp_status check_batch(const Dims& x, const tp_batch* b, bool need_attn) {
+  if (!b) return fail(TP_ERR_INVALID_ARG, "batch is NULL");
+  if (b->mode != TP_MODE_DECODE && b->mode != TP_MODE_PREFILL)
+    return fail(TP_ERR_INVALID_ARG, "unknown batch mode %d", b->mode);
+  if (b->n_tokens < 0 || b->n_seqs < 0)
+    return fail(TP_ERR_INVALID_ARG, "n_tokens=%d and n_seqs=%d must be >= 0", b->n_tokens,
+                b->n_seqs);
+  if (b->mode == TP_MODE_DECODE && b->n_seqs != b->n_tokens)
+    return fail(TP_ERR_INVALID_ARG, "decode batches carry one token per sequence (n_tokens=%d, "
+                "n_seqs=%d)", b->n_tokens, b->n_seqs);
+  if (b->mode == TP_MODE_PREFILL && b->n_tokens > 0 && b->n_seqs != 1)
+    return fail(TP_ERR_INVALID_ARG, "prefill batches carry one sequence (n_seqs=%d)", b->n_seqs);
+  if (b->max_pages <= 0) return fail(TP_ERR_INVALID_ARG, "max_pages=%d must be > 0", b->max_pages);
+  const int64_t cap = (int64_t)b->max_pages * x.ps;
+  if (b->max_seq_len < 0 || b->max_seq_len > cap || b->max_seq_len > x.maxpos)
+    return fail(TP_ERR_INVALID_ARG,
+                "max_seq_len=%d must be in [0, min(max_pages*page_size=%lld, max_position=%d)]",
+                b->max_seq_len, (long long)cap, x.maxpos);
+  if (need_attn && b->n_tokens > 0 && (!b->positions || !b->block_table || !b->rope_table))
+    return fail(TP_ERR_INVALID_ARG, "positions, block_table and rope_table must be non-NULL");
+  return TP_OK;
+}
+
+WsLayout ws_layout(const Dims& x, const tp_batch& b) {
+  WsLayout w{};
+  const uint64_t T = (uint64_t)b.n_tokens;
+  int L = b.max_seq_len > 0 ? b.max_seq_len : b.max_pages * x.ps;
+  if (L > x.maxpos) L = x.maxpos;
+  if (L < 1) L = 1;
+  w.pos_limit = L;
+  const int pages = (L + x.ps - 1) / x.ps;
+  const int per_split = x.hk * (int)(T > 0 ? T : 1);
+  const int want = (1024 + per_split - 1) / per_split;
+  int chunk_pages = (pages + want - 1) / want;
+  if (chunk_pages < 4) chunk_pages = 4;
+  w.chunk = chunk_pages * x.ps;
+  w.n_split = (L + w.chunk - 1) / w.chunk;
+  uint64_t off = 0;
+  auto put = [&](uint64_t& o, uint64_t bytes) {
+    o = off;
+    off = align_up(off + bytes);
+  };
+  put(w.qkv, T * x.qkv_rows * x.ab);
+  put(w.q, T * x.qdim * x.ab);
+  put(w.attn, T * x.qdim * x.ab);
+  put(w.part_o, T * x.hq * (uint64_t)w.n_split * x.hd * 4);
+  put(w.part_ml, T * x.hq * (uint64_t)w.n_split * 2 * 4);
+  put(w.ffn, T * x.fr * x.ab);
+  w.total = off > 0 ? off : kAlign;
+  return w;
+}
+
+// One projection of T tokens: bf16 weights with more tokens than the GEMV holds go to the MFMA
+// GEMM; everything else streams through the GEMV (in groups of up to 4 tokens).
+hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
+                   int gate_off, const void* X, void* Y, int ldy, hipStream_t st) {
+  if (x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K)) {
+    const char* B2 = (epi == tpk::EPI_GATED) ? W + (size_t)gate_off * K * 2 : nullptr;
+    return tpk::launch_gemm_bf16(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, st);
+  }
+  const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
+  return tpk::launch_gemv(wt, x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16, epi, x.actf, T,
+                          W, S, K, n_out, gate_off, X, Y, ldy, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_str(tp_status s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID_ARG: return "TP_ERR_INVALID_ARG";
+    case TP_ERR_RANK: return "TP_ERR_RANK";
+    case TP_ERR_NOT_DIVISIBLE: return "TP_ERR_NOT_DIVISIBLE";
+    case TP_ERR_QUANT_ALIGN: return "TP_ERR_QUANT_ALIGN";
+    case TP_ERR_BUFFER_TOO_SMALL: return "TP_ERR_BUFFER_TOO_SMALL";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+const char* tp_last_error(void) { return g_err.c_str(); }
+
+tp_status tp_shard_weights_size(const tp_block_desc* desc, int32_t rank, tp_shard_layout* out) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (!out) return fail(TP_ERR_INVALID_ARG, "out is NULL");
+  make_layout(x, out);
+  g_err.clear();
+  return TP_OK;
+}
+
+static tp_status check_full(const tp_full_weights* w) {
+  if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->wg || !w->wu || !w->wd)
+    return fail(TP_ERR_INVALID_ARG, "full weights: every pointer must be non-NULL");
+  return TP_OK;
+}
+
+// Pack (to_shard = true) or unpack rank r's slices. The slice geometry is the same both ways.
+static tp_status shard_copy(const Dims& x, int r, const tp_full_weights* full, char* shard,
+                            bool to_shard, hipStream_t st) {
+  tp_shard_layout L;
+  make_layout(x, &L);
+  struct Piece {
+    const void* full;
+    int64_t row0, rows;      // rows taken from the full matrix
+    int64_t col0, cols;      // columns taken (elements)
+    int64_t full_cols;       // row length of the full matrix (elements)
+    uint64_t dst_row0;       // first row inside the packed region
+    const tp_region* reg;
+    const tp_region* sreg;
+    int64_t reg_cols;        // row length inside the packed region (elements)
+  };
+  const int64_t hd = x.hd, d = x.d;
+  const std::vector<Piece> pieces = {
+      {full->wq, r * x.hq * hd, x.hq * hd, 0, d, d, 0, &L.qkv, &L.qkv_scale, d},
+      {full->wk, r * x.hk * hd, x.hk * hd, 0, d, d, (uint64_t)(x.hq * hd), &L.qkv, &L.qkv_scale, d},
+      {full->wv, r * x.hk * hd, x.hk * hd, 0, d, d, (uint64_t)((x.hq + x.hk) * hd), &L.qkv,
+       &L.qkv_scale, d},
+      {full->wo, 0, d, (int64_t)r * x.qdim, x.qdim, (int64_t)x.Hq * hd, 0, &L.o, &L.o_scale, x.qdim},
+      {full->wg, (int64_t)r * x.fr, x.fr, 0, d, d, 0, &L.gate_up, &L.gate_up_scale, d},
+      {full->wu, (int64_t)r * x.fr, x.fr, 0, d, d, (uint64_t)x.fr, &L.gate_up, &L.gate_up_scale, d},
+      {full->wd, 0, d, (int64_t)r * x.fr, x.fr, (int64_t)x.F, 0, &L.down, &L.down_scale, x.fr},
+  };
+  for (const Piece& p : pieces) {
+    hipError_t e;
+    if (x.wt == TP_DTYPE_Q8_0) {
+      const size_t full_ld = (size_t)(p.full_cols / 32) * 34;
+      char* src = (char*)p.full + (size_t)p.row0 * full_ld + (size_t)(p.col0 / 32) * 34;
+      char* codes = shard + p.reg->offset + p.dst_row0 * (uint64_t)p.reg_cols;
+      char* scales = shard + p.sreg->offset + p.dst_row0 * (uint64_t)(p.reg_cols / 32) * 2;
+      e = to_shard ? tpk::q8_split(src, full_ld, p.rows, p.cols / 32, codes, scales, st)
+                   : tpk::q8_join(src, full_ld, p.rows, p.cols / 32, codes, scales, st);
+    } else {
+      const size_t full_ld = (size_t)p.full_cols * x.wb;
+      char* fptr = (char*)p.full + (size_t)p.row0 * full_ld + (size_t)p.col0 * x.wb;
+      char* sptr = shard + p.reg->offset + p.dst_row0 * (uint64_t)p.reg_cols * x.wb;
+      const size_t sld = (size_t)p.reg_cols * x.wb, row_bytes = (size_t)p.cols * x.wb;
+      e = to_shard ? tpk::copy2d(sptr, sld, fptr, full_ld, p.rows, row_bytes, st)
+                   : tpk::copy2d(fptr, full_ld, sptr, sld, p.rows, row_bytes, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, to_shard ? "tp_shard_weights" : "tp_shard_unpack");
+  }
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_shard_weights(const tp_block_desc* desc, int32_t rank, const tp_full_weights* src,
+                           void* dst, uint64_t dst_bytes, void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (tp_status s = check_full(src)) return s;
+  if (!dst) return fail(TP_ERR_INVALID_ARG, "dst is NULL");
+  tp_shard_layout L;
+  make_layout(x, &L);
+  if (dst_bytes < L.alloc_bytes)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "dst_bytes=%llu < alloc_bytes=%llu",
+                (unsigned long long)dst_bytes, (unsigned long long)L.alloc_bytes);
+  return shard_copy(x, rank, src, (char*)dst, true, (hipStream_t)stream);
+}
+
+tp_status tp_shard_unpack(const tp_block_desc* desc, int32_t rank, const void* shard,
+                          const tp_full_weights* dst, void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (tp_status s = check_full(dst)) return s;
+  if (!shard) return fail(TP_ERR_INVALID_ARG, "shard is NULL");
+  return shard_copy(x, rank, dst, (char*)shard, false, (hipStream_t)stream);
+}
+
+tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uint64_t n_blocks,
+                          void* stream) {
+  if (n_blocks == 0) return TP_OK;
+  if (!codes || !scales || !out)
+    return fail(TP_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
+  hipError_t e = tpk::q8_dequant_buf(codes, scales, out, (int64_t)n_blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tp_dequant_q8_0");
+  return TP_OK;
+}
+
+tp_status tp_workspace_size(const tp_block_desc* desc, const tp_batch* batch, uint64_t* bytes) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (tp_status s = check_batch(x, batch, false)) return s;
+  if (!bytes) return fail(TP_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(x, *batch).total;
+  return TP_OK;
+}
+
+tp_status tp_workspace_offsets(const tp_block_desc* desc, const tp_batch* batch,
+                               uint64_t* q_offset, uint64_t* attn_offset, uint64_t* ffn_offset) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (tp_status s = check_batch(x, batch, false)) return s;
+  if (!q_offset || !attn_offset || !ffn_offset)
+    return fail(TP_ERR_INVALID_ARG, "offset outputs must be non-NULL");
+  const WsLayout w = ws_layout(x, *batch);
+  *q_offset = w.q;
+  *attn_offset = w.attn;
+  *ffn_offset = w.ffn;
+  return TP_OK;
+}
+
+tp_status tp_rope_table_bytes(const tp_block_desc* desc, uint64_t* bytes) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (!bytes) return fail(TP_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = (uint64_t)x.maxpos * (x.hd / 2) * 2 * sizeof(float);
+  return TP_OK;
+}
+
+tp_status tp_rope_table_init(const tp_block_desc* desc, void* dev_table, uint64_t table_bytes,
+                             void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (!dev_table) return fail(TP_ERR_INVALID_ARG, "dev_table is NULL");
+  const uint64_t need = (uint64_t)x.maxpos * (x.hd / 2) * 2 * sizeof(float);
+  if (table_bytes < need)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "table_bytes=%llu < %llu", (unsigned long long)table_bytes,
+                (unsigned long long)need);
+  const int half = x.hd / 2;
+  std::vector<float> host((size_t)x.maxpos * half * 2);
+  for (int i = 0; i < half; ++i) {
+    const double theta = std::pow((double)x.base, -2.0 * i / x.hd);
+    for (int p = 0; p < x.maxpos; ++p) {
+      const double a = (double)p * theta;
+      host[((size_t)p * half + i) * 2] = (float)std::cos(a);
+      host[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(dev_table, host.data(), need, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "tp_rope_table_init");
+  return TP_OK;
+}
+
+static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t half,
+                              const void* shard, const tp_batch* batch, const void* xn,
+                              const tp_kv_cache* kv, void* partial_out, void* workspace,
+                              uint64_t workspace_bytes, void* stream, hipEvent_t evb,
+                              hipEvent_t eve) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (half != TP_HALF_ATTN && half != TP_HALF_FFN)
+    return fail(TP_ERR_INVALID_ARG, "unknown half %d", half);
+  const bool attn = half == TP_HALF_ATTN;
+  if (tp_status s = check_batch(x, batch, attn)) return s;
+  const int T = batch->n_tokens;
+  if (T == 0) {
+    g_err.clear();
+    return TP_OK;
+  }
+  if (!shard || !xn || !partial_out || !workspace)
+    return fail(TP_ERR_INVALID_ARG, "shard, xn, partial_out and workspace must be non-NULL");
+  if (!aligned16(shard) || !aligned16(xn) || !aligned16(partial_out) || !aligned16(workspace))
+    return fail(TP_ERR_INVALID_ARG, "shard, xn, partial_out and workspace must be 16-byte aligned");
+  if (attn) {
+    if (!kv || !kv->k_pages || !kv->v_pages || kv->n_pages <= 0)
+      return fail(TP_ERR_INVALID_ARG, "ATTN needs a KV cache with non-NULL pages and n_pages > 0");
+    if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
+      return fail(TP_ERR_INVALID_ARG, "KV pages must be 16-byte aligned");
+  }
+  const WsLayout w = ws_layout(x, *batch);
+  if (workspace_bytes < w.total)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu",
+                (unsigned long long)workspace_bytes, (unsigned long long)w.total);
+  const bool gemm = x.wt == TP_DTYPE_BF16;
+  const int kmax = attn ? (x.d > x.qdim ? x.d : x.qdim) : (x.d > x.fr ? x.d : x.fr);
+  if (tpk::gemv_max_tokens(kmax) < 1 && !(gemm && T > 4))
+    return fail(TP_ERR_UNSUPPORTED, "decode projection with K=%d exceeds the GEMV's 16384", kmax);
+
+  tp_shard_layout L;
+  make_layout(x, &L);
+  hipStream_t st = (hipStream_t)stream;
+  const char* sh = (const char*)shard;
+  char* ws = (char*)workspace;
+  const int epi_part = x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16;
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  hipError_t e;
+  if (attn) {
+    void* qkv = ws + w.qkv;
+    if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
+    e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d, x.qkv_rows, 0,
+                xn, qkv, x.qkv_rows, st);
+    if (e != hipSuccess) return hip_fail(e, "qkv projection");
+    if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
+    e = tpk::launch_rope_append(at, qkv, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
+                                batch->mode, batch->block_table, batch->max_pages, x.ps,
+                                kv->n_pages, w.pos_limit, kv->k_pages, kv->v_pages,
+                                batch->rope_table, st);
+    if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
+    e = tpk::launch_attn_decode(at, x.hd, x.Hq / x.Hkv, T, x.hk, ws + w.q, kv->k_pages,
+                                kv->v_pages, batch->positions, batch->mode, batch->block_table,
+                                batch->max_pages, x.ps, kv->n_pages, w.chunk, w.n_split,
+                                w.pos_limit, (float*)(ws + w.part_o), (float*)(ws + w.part_ml),
+                                ws + w.attn, st);
+    if (e != hipSuccess) return hip_fail(e, "attention");
+    e = project(x, epi_part, T, sh + L.o.offset, sh + L.o_scale.offset, x.qdim, x.d, 0,
+                ws + w.attn, partial_out, x.d, st);
+    if (e != hipSuccess) return hip_fail(e, "o projection");
+  } else {
+    if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
+    e = project(x, tpk::EPI_GATED, T, sh + L.gate_up.offset, sh + L.gate_up_scale.offset, x.d,
+                x.fr, x.fr, xn, ws + w.ffn, x.fr, st);
+    if (e != hipSuccess) return hip_fail(e, "gate/up projection");
+    if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
+    e = project(x, epi_part, T, sh + L.down.offset, sh + L.down_scale.offset, x.fr, x.d, 0,
+                ws + w.ffn, partial_out, x.d, st);
+    if (e != hipSuccess) return hip_fail(e, "down projection");
+  }
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_block_shard_forward(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                 const void* shard, const tp_batch* batch, const void* xn,
+                                 const tp_kv_cache* kv, void* partial_out, void* workspace,
+                                 uint64_t workspace_bytes, void* stream) {
+  return forward_impl(desc, rank, half, shard, batch, xn, kv, partial_out, workspace,
+                      workspace_bytes, stream, nullptr, nullptr);
+}
+
+tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                       const void* shard, const tp_batch* batch, const void* xn,
+                                       const tp_kv_cache* kv, void* partial_out, void* workspace,
+                                       uint64_t workspace_bytes, void* stream, void* ev_begin,
+                                       void* ev_end) {
+  return forward_impl(desc, rank, half, shard, batch, xn, kv, partial_out, workspace,
+                      workspace_bytes, stream, (hipEvent_t)ev_begin, (hipEvent_t)ev_end);
+}
+
+tp_status tp_partial_reduce(const tp_block_desc* desc, int32_t n_tokens, const void* partials,
+                            int32_t n_partials, const void* residual_in, void* residual_out,
+                            const void* gamma, void* normed_out, void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (n_tokens < 0 || n_partials < 0)
+    return fail(TP_ERR_INVALID_ARG, "n_tokens=%d and n_partials=%d must be >= 0", n_tokens,
+                n_partials);
+  if (n_tokens == 0) return TP_OK;
+  if (!residual_in) return fail(TP_ERR_INVALID_ARG, "residual_in is NULL");
+  if (n_partials > 0 && (!partials || !residual_out))
+    return fail(TP_ERR_INVALID_ARG, "n_partials=%d needs non-NULL partials and residual_out",
+                n_partials);
+  if (gamma && !normed_out) return fail(TP_ERR_INVALID_ARG, "gamma given but normed_out is NULL");
+  if (!gamma && n_partials == 0)
+    return fail(TP_ERR_INVALID_ARG, "nothing to do: no partials and no gamma");
+  if (!aligned16(residual_in) || (residual_out && !aligned16(residual_out)) ||
+      (partials && !aligned16(partials)) || (gamma && !aligned16(gamma)) ||
+      (normed_out && !aligned16(normed_out)))
+    return fail(TP_ERR_INVALID_ARG, "reduce buffers must be 16-byte aligned");
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  const int pt = x.pt == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  hipError_t e = tpk::launch_partial_reduce(at, pt, n_tokens, x.d, partials, n_partials,
+                                            residual_in, residual_out, gamma, normed_out, x.eps,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tp_partial_reduce");
+  g_err.clear();
+  return TP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device-side helpers shared by the kernels of libtpblock (gfx950 / CDNA4, 64-wide wavefronts).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tp_kernels.h"
+
+namespace tpk {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: data read once, keep it out of the way in cache).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Q8_0 dequantisation of one weight: fp16 scale times the signed code. The product of an 11-bit
+// significand and an 8-bit integer is exact in fp32.
+__device__ __forceinline__ float q8_dequant(float scale, int32_t code) {
+  return scale * (float)code;
+}
+
+template <int AT>
+__device__ __forceinline__ float ld_act(const void* p, size_t i) {
+  if constexpr (AT == ACT_F32) return ((const float*)p)[i];
+  else return bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int AT>
+__device__ __forceinline__ void st_act(void* p, size_t i, float v) {
+  if constexpr (AT == ACT_F32) ((float*)p)[i] = v;
+  else ((uint16_t*)p)[i] = f32_to_bf16(v);
+}
+
+// 16-byte vector of activations widened to fp32: 4 (fp32) or 8 (bf16) values.
+template <int AT> struct Vec16;
+template <> struct Vec16<ACT_F32> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const void* p, float* out) {
+    float4 v = *(const float4*)p;
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+template <> struct Vec16<ACT_BF16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const void* p, float* out) {
+    uint4 v = *(const uint4*)p;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// SiLU(z) = z / (1 + e^-z)  and  GELU-tanh(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float act_silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float act_gelu_tanh(float z) {
+  const float k = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = k * (z + 0.044715f * z * z * z);
+  // tanh(u) = 1 - 2 / (e^{2u} + 1), saturating correctly for large |u|.
+  float t = 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  return 0.5f * z * (1.0f + t);
+}
+
+template <int ACTF>
+__device__ __forceinline__ float gated(float g, float u) {
+  if constexpr (ACTF == 0) return act_silu(g) * u;
+  else return act_gelu_tanh(g) * u;
+}
+
+}  // namespace tpk

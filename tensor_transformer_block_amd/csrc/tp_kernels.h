@@ -1,0 +1,49 @@
+// Host-side launchers of the libtpblock kernels. Each enqueues on `st` and returns the launch
+// status; shapes are validated by the caller (tp_api.hip) before any of these run.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
+enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3 };
+
+// k_pack.hip
+hipError_t copy2d(void* dst, size_t dst_ld, const void* src, size_t src_ld, int64_t rows,
+                  size_t row_bytes, hipStream_t st);
+hipError_t q8_split(const void* aos, size_t aos_ld, int64_t rows, int64_t nblk, void* codes,
+                    void* scales, hipStream_t st);
+hipError_t q8_join(void* aos, size_t aos_ld, int64_t rows, int64_t nblk, const void* codes,
+                   const void* scales, hipStream_t st);
+hipError_t q8_dequant_buf(const void* codes, const void* scales, float* out, int64_t n_blocks,
+                          hipStream_t st);
+
+// k_reduce.hip
+hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,
+                                 const void* res_in, void* res_out, const void* gamma,
+                                 void* normed, float eps, hipStream_t st);
+
+// k_gemv.hip
+int gemv_max_tokens(int K);
+hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, const void* S,
+                       int K, int n_out, int gate_off, const void* X, void* Y, int ldy,
+                       hipStream_t st);
+
+// k_gemm.hip
+hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
+                            const void* B2, void* C, int ldc, hipStream_t st);
+
+// k_attn.hip
+hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, int hd, void* q_out,
+                              const int* positions, int mode, const int* block_table,
+                              int max_pages, int ps, int n_pages, int pos_limit, void* kp,
+                              void* vp, const float* rope, hipStream_t st);
+hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* q, const void* kp,
+                              const void* vp, const int* positions, int mode, const int* bt,
+                              int max_pages, int ps, int n_pages, int chunk, int n_split,
+                              int pos_limit, float* part_o, float* part_ml, void* out,
+                              hipStream_t st);
+
+}  // namespace tpk
