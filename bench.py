@@ -74,6 +74,35 @@ def gate_up_unit(s):
         2.0 * s.n_tokens * 2 * fr * s.d_model
 
 
+class HipEvents:
+    """Timing events created with the HIP runtime (hipEvent_t handles the library can record)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed_s(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e-3
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
 def cpu_baseline(inp, seconds):
     """The oracle's explicit N-rank block, fp64 NumPy, on the host cores, for a bounded sample."""
     import numpy as np
@@ -193,17 +222,17 @@ def main():
     # launch stream. A backlog of graph replays keeps the stream busy so no host launch latency
     # lands between the events.
     log(f"timing the gate/up projection ({args.kernel_iters} launches)")
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.kernel_iters)]
+    hev = HipEvents(2 * args.kernel_iters)
     for i in range(min(64, args.steps)):
         run(i)
-    for i, (eb, ee) in enumerate(pairs):
+    for i in range(args.kernel_iters):
         c, r = i % copies, (i // copies) % s.tp
         B.tp_block_shard_forward_timed(blk.desc, r, B.TP_HALF_FFN, blk.shards[c][r], blk.batch,
-                                       blk.xn2, None, blk.partials[r], blk.workspace, eb, ee,
-                                       blk.ws_bytes)
+                                       blk.xn2, None, blk.partials[r], blk.workspace,
+                                       hev.ev[2 * i], hev.ev[2 * i + 1], blk.ws_bytes)
     torch.cuda.synchronize()
-    kdur = [eb.elapsed_time(ee) * 1e-3 for eb, ee in pairs]
+    kdur = [hev.elapsed_s(2 * i, 2 * i + 1) for i in range(args.kernel_iters)]
+    hev.close()
     kavg = float(np.mean(kdur))
     ub, uf = gate_up_unit(s)
     if s.mode == "prefill":

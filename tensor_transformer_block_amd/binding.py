@@ -216,14 +216,13 @@ def tp_block_shard_forward(desc, rank, half, shard, batch: tp_batch, xn, kv: tp_
 def tp_block_shard_forward_timed(desc, rank, half, shard, batch: tp_batch, xn,
                                  kv: tp_kv_cache | None, partial_out, workspace, ev_begin, ev_end,
                                  workspace_bytes=None, stream=None) -> None:
-    """ev_begin / ev_end: torch.cuda.Event objects (or raw hipEvent_t addresses, or None)."""
+    """ev_begin / ev_end: raw hipEvent_t handles (ints from hipEventCreate) or None."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    ev = lambda e: None if e is None else (e if isinstance(e, int) else e.cuda_event)
     _check(lib().tp_block_shard_forward_timed(
         ctypes.byref(desc), rank, half, ptr(shard), ctypes.byref(batch), ptr(xn),
         ctypes.byref(kv) if kv is not None else None, ptr(partial_out), ptr(workspace),
-        workspace_bytes, _stream(stream), ev(ev_begin), ev(ev_end)))
+        workspace_bytes, _stream(stream), ev_begin, ev_end))
 
 
 def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residual_out, gamma,
