@@ -111,9 +111,10 @@ typedef struct {
   const float* rope_table;
 } tp_batch;
 
-/* Rank r's paged KV cache: k_pages and v_pages are [n_pages][Hkv/N][page_size][hd] in the
- * activation dtype, holding only the KV heads rank r owns [TS-HOW]. K is stored after the rotary
- * embedding. */
+/* Rank r's paged KV cache, holding only the KV heads rank r owns [TS-HOW], activation dtype:
+ * k_pages [n_pages][Hkv/N][page_size][hd] (after the rotary embedding) and v_pages stored
+ * transposed, [n_pages][Hkv/N][hd][page_size], so that 8 consecutive keys of one hd column are
+ * contiguous (the B operand layout of the P.V matrix-core step). */
 typedef struct {
   void* k_pages;
   void* v_pages;

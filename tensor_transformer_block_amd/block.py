@@ -166,5 +166,5 @@ class DeviceBlock:
             p = int(self.inp.positions[t])
             phys = self.inp.block_table[b, p // s.page_size]
             ks.append(kp[phys, :, p % s.page_size])
-            vs.append(vp[phys, :, p % s.page_size])
+            vs.append(vp[phys, :, :, p % s.page_size])
         return np.stack(ks), np.stack(vs)

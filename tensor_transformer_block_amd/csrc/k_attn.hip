@@ -56,10 +56,11 @@ __global__ void k_rope_append(const void* __restrict__ qkv, int T, int hq, int h
     st_act<AT>(kp, dk + e, a * cs.x - b * cs.y);
     st_act<AT>(kp, dk + e + half, b * cs.x + a * cs.y);
   } else {
+    // V pages are stored transposed: [page][kv head][hd][slot].
     const int g = head - hq - hk;
-    const size_t dv = (((size_t)page * hk + g) * ps + slot) * hd;
-    st_act<AT>(vp, dv + e, a);
-    st_act<AT>(vp, dv + e + half, b);
+    const size_t dv = ((size_t)page * hk + g) * hd;
+    st_act<AT>(vp, (dv + e) * ps + slot, a);
+    st_act<AT>(vp, (dv + e + half) * ps + slot, b);
   }
 }
 
@@ -85,18 +86,31 @@ hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, in
 // Split-KV attention. Lane layout inside a wavefront: a key's HD elements are spread over
 // LPK = HD / E lanes (E = elements per 16-byte load), so one wave-wide load covers KPP = 64 / LPK
 // keys. Lanes with the same key form a "subgroup"; dot products reduce across its LPK lanes.
-// The four waves of a workgroup take pages round-robin and merge through LDS at the end.
+// A wave walks its pages in 16-key tiles with the next tile's K and V loads in flight while the
+// current tile is scored; the physical page ids of all its pages are fetched up front, in
+// parallel with q. The four waves of a workgroup merge through LDS; with one split the result is
+// final, otherwise k_attn_combine merges the splits.
+constexpr int kMaxSplit = 1024;
+
+template <int AT, int HD>
+struct AttnTile {
+  static constexpr int E = Vec16<AT>::N;
+  static constexpr int LPK = HD / E;
+  static constexpr int KPP = 64 / LPK;
+  static constexpr int NP = 16 / KPP;  // passes per 16-key tile
+};
+
 template <int AT, int HD, int G>
 __global__ __launch_bounds__(256) void k_attn_split(
     const void* __restrict__ q, const void* __restrict__ kpages, const void* __restrict__ vpages,
     const int* __restrict__ positions, int mode, const int* __restrict__ block_table,
     int max_pages, int ps, int n_pages, int hk, int chunk, int n_split, int pos_limit,
-    float* __restrict__ part_o, float* __restrict__ part_ml, float scale_log2) {
-  constexpr int E = Vec16<AT>::N;
-  constexpr int LPK = HD / E;
-  constexpr int KPP = 64 / LPK;
+    float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
+    float scale_log2) {
+  using TL = AttnTile<AT, HD>;
+  constexpr int E = TL::E, LPK = TL::LPK, KPP = TL::KPP, NP = TL::NP;
   constexpr int EB = (AT == ACT_F32) ? 4 : 2;
-  static_assert(LPK <= 64 && KPP >= 1, "head_dim too large for one wavefront");
+  static_assert(LPK <= 64 && KPP >= 1 && NP >= 1, "head_dim too large for one wavefront");
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ float s_o[4][G][HD];
 
@@ -109,6 +123,17 @@ __global__ __launch_bounds__(256) void k_attn_split(
   const int k0 = split * chunk;
   const int k1 = min(n_keys, k0 + chunk);
   const int seq = (mode == 0) ? t : 0;
+
+  // This wave's 16-key tiles: tile j covers keys k0 + (wave + 4 j) * 16 + [0, 16).
+  const int tiles = (k1 > k0) ? (k1 - k0 + 15) / 16 : 0;
+  const int ntw = tiles > wave ? (tiles - wave + 3) / 4 : 0;
+  // Physical page of tile j, fetched by lane j % 64 (for j < 64; later blocks refetch).
+  auto fetch_page = [&](int j) -> int {
+    const int key = k0 + (wave + 4 * j) * 16;
+    const int pg = min(key / ps, max_pages - 1);
+    return clampi(block_table[(size_t)seq * max_pages + pg], 0, n_pages - 1);
+  };
+  int pid_reg = (lane < ntw) ? fetch_page(lane) : 0;
 
   float qv[G][E];
 #pragma unroll
@@ -127,72 +152,92 @@ __global__ __launch_bounds__(256) void k_attn_split(
     for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
   }
 
-  // Passes over one page, handled in groups of at most PG passes.
-  const int passes = ps / KPP;
-  constexpr int PG = 4;
-  if (k0 < k1) {
-    for (int pg = k0 / ps + wave; pg * ps < k1; pg += 4) {
-      const int phys = clampi(block_table[(size_t)seq * max_pages + pg], 0, n_pages - 1);
-      const char* kb = (const char*)kpages + (((size_t)phys * hk + g) * ps) * HD * EB;
-      const char* vb = (const char*)vpages + (((size_t)phys * hk + g) * ps) * HD * EB;
-      for (int p0 = 0; p0 < passes; p0 += PG) {
-        float kf[PG][E], vf[PG][E];
-        int key[PG];
+  auto tile_base = [&](int j, int pid) -> size_t {
+    const int key = k0 + (wave + 4 * j) * 16;
+    return (((size_t)pid * hk + g) * ps + (key % ps)) * HD;  // key % ps is a multiple of 16
+  };
+  auto load_tile = [&](int j, uint4 (&kbuf)[NP], uint4 (&vbuf)[NP]) {
+    if (j >= 64 && (j & 63) == 0) pid_reg = (lane < ntw - j) ? fetch_page(j + lane) : 0;
+    const int pid = __shfl(pid_reg, j & 63, 64);
+    const size_t base = tile_base(j, pid);
+    const size_t vbase = ((size_t)pid * hk + g) * HD;  // V^T: [page][head][hd][slot]
+    const int slot0 = (k0 + (wave + 4 * j) * 16) % ps;
 #pragma unroll
-        for (int j = 0; j < PG; ++j) {
-          const int kin = (p0 + j) * KPP + sub;
-          key[j] = pg * ps + kin;
-          if (p0 + j < passes) {
-            Vec16<AT>::load(kb + ((size_t)kin * HD + e0) * EB, kf[j]);
-            Vec16<AT>::load(vb + ((size_t)kin * HD + e0) * EB, vf[j]);
-          } else {
-            key[j] = k1;  // no such pass: masked below
+    for (int p = 0; p < NP; ++p) {
+      const size_t off = (base + (size_t)(p * KPP + sub) * HD + e0) * EB;
+      kbuf[p] = *(const uint4*)((const char*)kpages + off);
+      const int slot = slot0 + p * KPP + sub;
+      uint32_t w[4];
+      if constexpr (AT == ACT_F32) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) kf[j][e] = vf[j][e] = 0.f;
-          }
-        }
-        float s[PG][G];
+        for (int i = 0; i < 4; ++i)
+          w[i] = ((const uint32_t*)vpages)[(vbase + e0 + i) * ps + slot];
+      } else {
 #pragma unroll
-        for (int j = 0; j < PG; ++j) {
+        for (int i = 0; i < 4; ++i)
+          w[i] = (uint32_t)((const uint16_t*)vpages)[(vbase + e0 + 2 * i) * ps + slot] |
+                 ((uint32_t)((const uint16_t*)vpages)[(vbase + e0 + 2 * i + 1) * ps + slot] << 16);
+      }
+      vbuf[p] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+  auto score_tile = [&](int j, const uint4 (&kbuf)[NP], const uint4 (&vbuf)[NP]) {
+    const int kbase = k0 + (wave + 4 * j) * 16;
+    float s[NP][G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float d = 0.f;
+    for (int p = 0; p < NP; ++p) {
+      float kf[E];
+      unpack16<AT>(kbuf[p], kf);
+      const bool valid = kbase + p * KPP + sub < k1;
 #pragma unroll
-            for (int e = 0; e < E; ++e) d = fmaf(qv[h][e], kf[j][e], d);
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
 #pragma unroll
-            for (int o = LPK / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
-            s[j][h] = (key[j] >= k0 && key[j] < k1) ? d : -INFINITY;
-          }
-          // Slots past the sequence may hold anything (even NaN); keep them out of p * v.
-          if (!(key[j] >= k0 && key[j] < k1)) {
+        for (int e = 0; e < E; ++e) d = fmaf(qv[h][e], kf[e], d);
 #pragma unroll
-            for (int e = 0; e < E; ++e) vf[j][e] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float mx = s[0][h];
-#pragma unroll
-          for (int j = 1; j < PG; ++j) mx = fmaxf(mx, s[j][h]);
-#pragma unroll
-          for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-          const float mn = fmaxf(m[h], mx);
-          if (mn == -INFINITY) continue;  // nothing valid seen yet by this wave
-          const float alpha = exp2f(m[h] - mn);
-          m[h] = mn;
-          l[h] *= alpha;
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-#pragma unroll
-          for (int j = 0; j < PG; ++j) {
-            const float p = exp2f(s[j][h] - mn);
-            l[h] += p;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, vf[j][e], acc[h][e]);
-          }
-        }
+        for (int o = LPK / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+        s[p][h] = valid ? d : -INFINITY;
       }
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) mx = fmaxf(mx, s[p][h]);
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mn = fmaxf(m[h], mx);  // finite: key kbase < k1 is always valid
+      const float alpha = exp2f(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      float vf[E];
+      unpack16<AT>(vbuf[p], vf);
+      if (!(kbase + p * KPP + sub < k1)) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = 0.f;  // slots past the sequence may hold anything
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pr = exp2f(s[p][h] - m[h]);
+        l[h] += pr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
+      }
+    }
+  };
+  // Two named register buffers: tile j + 1 loads while tile j is scored.
+  uint4 ka[NP], va[NP], kc[NP], vc[NP];
+  if (ntw > 0) load_tile(0, ka, va);
+  for (int j = 0; j < ntw; j += 2) {
+    if (j + 1 < ntw) load_tile(j + 1, kc, vc);
+    score_tile(j, ka, va);
+    if (j + 2 < ntw) load_tile(j + 2, ka, va);
+    if (j + 1 < ntw) score_tile(j + 1, kc, vc);
   }
   // Sum the subgroups' partial l and o (they share m).
 #pragma unroll
@@ -218,9 +263,10 @@ __global__ __launch_bounds__(256) void k_attn_split(
     }
   }
   __syncthreads();
+  const size_t tg = (size_t)t * hq + (size_t)g * G;  // first query head row of this group
   for (int idx = tid; idx < G * HD; idx += 256) {
     const int h = idx / HD, e = idx % HD;
-    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
@@ -230,43 +276,359 @@ __global__ __launch_bounds__(256) void k_attn_split(
         O += s_o[w][h][e] * f;
       }
     }
-    const size_t row = ((size_t)t * hq + g * G + h) * n_split + split;
-    part_o[row * HD + e] = O;
-    if (e == 0) {
-      part_ml[row * 2] = M;
-      part_ml[row * 2 + 1] = L;
+    if (n_split == 1) {
+      st_act<AT>(out, (tg + h) * HD + e, O / L);
+    } else {
+      const size_t row = (tg + h) * n_split + split;
+      part_o[row * HD + e] = O;
+      if (e == 0) {
+        part_ml[row * 2] = M;
+        part_ml[row * 2 + 1] = L;
+      }
     }
   }
 }
 
-template <int AT>
-__global__ void k_attn_combine(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                               int n_split, int hd, int hq, void* __restrict__ out) {
-  const int t = blockIdx.x, h = blockIdx.y;
-  const size_t row0 = ((size_t)t * hq + h) * n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[(row0 + s) * 2]);
-  for (int e = threadIdx.x; e < hd; e += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float mv = part_ml[(row0 + s) * 2];
-      if (mv == -INFINITY) continue;
-      const float f = exp2f(mv - M);
-      L += part_ml[(row0 + s) * 2 + 1] * f;
-      O += part_o[(row0 + s) * hd + e] * f;
+// bf16 attention on the matrix cores, for decode (split over keys) and prefill (causal).
+//
+// A wavefront owns 16 query rows. Decode: the G query heads of one token's KV group (rows G..15
+// idle), and the four waves of a workgroup split the key range, then merge through LDS. Prefill:
+// 16 consecutive tokens of one query head, each wave its own rows, keys up to the rows' causal
+// limit. Per 32-key tile (two 16-key n-tiles, each inside one page):
+//   S = Q K^T   v_mfma_f32_16x16x32_bf16, A = q rows (16 B of hd per lane), B = K rows (16 B);
+//   online softmax on the 16 x 32 tile in registers (rows live in the same lanes as O's rows);
+//   O += P V    P goes through LDS (bf16) into the A layout; B = 8 consecutive keys of one hd
+//               column, a contiguous 16 B because V pages are stored transposed, [hd][slot].
+// The next tile's K loads are issued once the scores are done and its V loads once P V is done.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_a;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_a;
+
+constexpr int kPLd = 40;  // bf16 per LDS row of P (32 keys + padding)
+
+template <int HD, bool PREFILL>
+__global__ __launch_bounds__(256) void k_attn_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpages,
+    const uint16_t* __restrict__ vpages, const int* __restrict__ positions, int mode,
+    const int* __restrict__ block_table, int max_pages, int ps, int n_pages, int hk, int G,
+    int T, int chunk, int n_split, int pos_limit, float* __restrict__ part_o,
+    float* __restrict__ part_ml, uint16_t* __restrict__ out, float scale_log2) {
+  constexpr int KS = HD / 32;  // MFMA k-steps over hd in Q K^T
+  constexpr int NO = HD / 16;  // 16-wide hd n-tiles of O
+  __shared__ __attribute__((aligned(16))) uint16_t s_pb[4][16 * kPLd];
+  __shared__ float s_m[4][8], s_l[4][8];
+  __shared__ float s_o[PREFILL ? 1 : 4][PREFILL ? 1 : 8][HD];
+
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int hq = hk * G;
+
+  // ---- rows of this wave and the key range
+  int tok_fr, head_fr;   // the row this lane feeds into the A operand (row fr)
+  bool row_ok_fr;
+  int lim[4];            // per S/O row 4 fq + r: keys < lim are attended
+  int kstart, kend, tstep, toff, seq, split = 0;
+  if constexpr (PREFILL) {
+    const int ntt = (T + 15) / 16;
+    const int gi = blockIdx.x * 4 + wave;                // group: (token tile, head in group)
+    const bool gok = gi < ntt * G;
+    const int tt = gok ? (ntt - 1) - gi / G : 0;         // latest tokens first
+    const int hh = gok ? gi % G : 0;
+    tok_fr = tt * 16 + fr;
+    row_ok_fr = gok && tok_fr < T;
+    head_fr = g * G + hh;
+    int kmax = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = tt * 16 + 4 * fq + r;
+      const bool ok = gok && tk < T;
+      lim[r] = ok ? clampi(positions[tk], 0, pos_limit - 1) + 1 : pos_limit;
     }
-    st_act<AT>(out, ((size_t)t * hq + h) * hd + e, O / L);
+    for (int r = 0; r < 16; ++r) {
+      const int tk = tt * 16 + r;
+      if (gok && tk < T) kmax = max(kmax, clampi(positions[tk], 0, pos_limit - 1) + 1);
+    }
+    kstart = 0;
+    kend = kmax;
+    tstep = 1;
+    toff = 0;
+    seq = 0;
+  } else {
+    split = blockIdx.x;
+    const int t = blockIdx.z;
+    tok_fr = t;
+    row_ok_fr = fr < G;
+    head_fr = g * G + (fr < G ? fr : 0);
+    const int nk = clampi(positions[t], 0, pos_limit - 1) + 1;
+    kstart = split * chunk;
+    kend = min(nk, kstart + chunk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lim[r] = kend;
+    tstep = 4;
+    toff = wave;
+    seq = (mode == 0) ? t : 0;
   }
+  const int tiles = (kend > kstart) ? (kend - kstart + 31) / 32 : 0;
+  const int ntw = tiles > toff ? (tiles - toff + tstep - 1) / tstep : 0;
+
+  // Page ids: lane i of pid_reg holds the page of n-tile 64 * block + i of this wave.
+  auto tile_key = [&](int j) { return kstart + (toff + tstep * j) * 32; };
+  auto fetch_page = [&](int nt) -> int {
+    const int key = tile_key(nt >> 1) + 16 * (nt & 1);
+    const int pg = min(key / ps, max_pages - 1);
+    return clampi(block_table[(size_t)seq * max_pages + pg], 0, n_pages - 1);
+  };
+  int pid_reg = (lane < 2 * ntw) ? fetch_page(lane) : 0;
+  auto page_of = [&](int j, int h) -> int { return __shfl(pid_reg, (2 * j + h) & 63, 64); };
+
+  bf16x8_a qf[KS];
+  {
+    const uint16_t* qrow = q + ((size_t)(row_ok_fr ? tok_fr : 0) * hq + head_fr) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = row_ok_fr ? *(const uint4*)(qrow + ks * 32 + fq * 8) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8_a, v);
+    }
+  }
+  float m[4], lsum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    lsum[r] = 0.f;
+  }
+  floatx4_a o[NO];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) o[n] = floatx4_a{0.f, 0.f, 0.f, 0.f};
+
+  uint4 kf[2][KS], vf[NO];
+  auto load_k = [&](int j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pid = page_of(j, h);
+      const int key = tile_key(j) + 16 * h + fr;
+      const uint16_t* base = kpages + (((size_t)pid * hk + g) * ps + (key % ps)) * HD + fq * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[h][ks] = *(const uint4*)(base + ks * 32);
+    }
+  };
+  auto load_v = [&](int j) {
+    // lane: hd column n * 16 + fr, keys 8 fq .. 8 fq + 7 of the tile (n-tile fq / 2)
+    const int pid = page_of(j, fq >> 1);
+    const int slot = (tile_key(j) + 16 * (fq >> 1)) % ps + 8 * (fq & 1);
+    const uint16_t* base = vpages + (((size_t)pid * hk + g) * HD + fr) * ps + slot;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) vf[n] = *(const uint4*)(base + (size_t)n * 16 * ps);
+  };
+  auto refresh_pages = [&](int j) {
+    if ((j & 31) == 0) {
+      const int nt = 2 * j + lane;
+      pid_reg = (nt < 2 * ntw) ? fetch_page(nt) : 0;
+    }
+  };
+  uint16_t* pb = s_pb[wave];
+  if (ntw > 0) {
+    load_k(0);
+    load_v(0);
+  }
+  for (int j = 0; j < ntw; ++j) {
+    const int kb0 = tile_key(j);
+    floatx4_a sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = floatx4_a{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], __builtin_bit_cast(bf16x8_a, kf[h][ks]),
+                                                        sc[h], 0, 0, 0);
+    }
+    if (j + 1 < ntw) {
+      refresh_pages(j + 1);
+      load_k(j + 1);
+    }
+    // Lane holds S[row 4 fq + r][key kb0 + 16 h + fr].
+    float tmax[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = kb0 + 16 * h + fr;
+        sc[h][r] = (key < lim[r] && key < kend) ? sc[h][r] * scale_log2 : -INFINITY;
+      }
+      tmax[r] = fmaxf(sc[0][r], sc[1][r]);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax[r] = fmaxf(tmax[r], __shfl_xor(tmax[r], off, 64));
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // Every row has a valid key in its first tile, so mn is finite from there on.
+      const float mn = fmaxf(m[r], tmax[r]);
+      alpha[r] = exp2f(m[r] - mn);
+      m[r] = mn;
+      const float p0 = exp2f(sc[0][r] - mn), p1 = exp2f(sc[1][r] - mn);
+      lsum[r] = lsum[r] * alpha[r] + p0 + p1;
+      const int row = 4 * fq + r;
+      pb[row * kPLd + fr] = f32_to_bf16(p0);
+      pb[row * kPLd + 16 + fr] = f32_to_bf16(p1);
+    }
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
+    // The wave's own P writes must land before its lanes read them back in the A layout.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    const bf16x8_a pa = *(const bf16x8_a*)(pb + fr * kPLd + fq * 8);
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_a, vf[n]), o[n],
+                                                     0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (j + 1 < ntw) load_v(j + 1);
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lsum[r] += __shfl_xor(lsum[r], off, 64);
+
+  if constexpr (PREFILL) {
+    // Lane holds O[row 4 fq + r][hd n * 16 + fr]; write the finished rows.
+    const int ntt = (T + 15) / 16;
+    const int gi = blockIdx.x * 4 + wave;
+    if (gi >= ntt * G) return;
+    const int tt = (ntt - 1) - gi / G, hh = gi % G;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = tt * 16 + 4 * fq + r;
+      if (tk >= T) continue;
+      const float inv = 1.0f / lsum[r];
+      uint16_t* orow = out + ((size_t)tk * hq + g * G + hh) * HD;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) orow[n * 16 + fr] = f32_to_bf16(o[n][r] * inv);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * fq + r;
+      if (row < G) {
+        if (fr == 0) {
+          s_m[wave][row] = m[r];
+          s_l[wave][row] = lsum[r];
+        }
+#pragma unroll
+        for (int n = 0; n < NO; ++n) s_o[wave][row][n * 16 + fr] = o[n][r];
+      }
+    }
+    __syncthreads();
+    const int t = blockIdx.z;
+    const size_t tg = (size_t)t * hq + (size_t)g * G;
+    for (int idx = tid; idx < G * HD; idx += 256) {
+      const int h = idx / HD, e = idx % HD;
+      const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f = exp2f(s_m[w][h] - M);
+          L += s_l[w][h] * f;
+          O += s_o[w][h][e] * f;
+        }
+      }
+      if (n_split == 1) {
+        out[(tg + h) * HD + e] = f32_to_bf16(O / L);
+      } else {
+        const size_t row = (tg + h) * n_split + split;
+        part_o[row * HD + e] = O;
+        if (e == 0) {
+          part_ml[row * 2] = M;
+          part_ml[row * 2 + 1] = L;
+        }
+      }
+    }
+  }
+}
+
+// Merge of the key splits: workgroup (token, query head, 64-element slice of hd). Every split's
+// (m, l) is loaded in parallel, the weights 2^(m_s - M) go through LDS, four threads per element
+// each sum a quarter of the splits with independent loads, and the quarters are added in order.
+template <int AT>
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      int n_split, int hd, int hq,
+                                                      void* __restrict__ out) {
+  __shared__ float s_w[kMaxSplit];
+  __shared__ float s_red[2][4];
+  __shared__ float s_acc[4][64];
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int e = blockIdx.z * 64 + (tid & 63), part = tid >> 6;
+  const size_t row0 = ((size_t)t * hq + h) * n_split;
+  float mx = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += 256) {
+    const float m = part_ml[(row0 + sp) * 2];
+    s_w[sp] = m;
+    mx = fmaxf(mx, m);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[0][tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  float lsum = 0.f;
+  for (int sp = tid; sp < n_split; sp += 256) {
+    const float m = s_w[sp];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    s_w[sp] = w;
+    lsum += part_ml[(row0 + sp) * 2 + 1] * w;
+  }
+  lsum = wave_sum(lsum);
+  if ((tid & 63) == 0) s_red[1][tid >> 6] = lsum;
+  __syncthreads();
+  const float L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  float acc = 0.f;
+  if (e < hd) {
+#pragma unroll 8
+    for (int sp = part; sp < n_split; sp += 4) acc += part_o[(row0 + sp) * hd + e] * s_w[sp];
+  }
+  s_acc[part][tid & 63] = acc;
+  __syncthreads();
+  if (part == 0 && e < hd) {
+    const float o = ((s_acc[0][tid] + s_acc[1][tid]) + s_acc[2][tid]) + s_acc[3][tid];
+    st_act<AT>(out, ((size_t)t * hq + h) * hd + e, o / L);
+  }
+}
+
+template <int HD>
+static hipError_t attn_mfma_g(bool prefill, int G, int T, int hk, hipStream_t st, const void* q,
+                              const void* kp, const void* vp, const int* positions, int mode,
+                              const int* bt, int max_pages, int ps, int n_pages, int chunk,
+                              int n_split, int pos_limit, float* po, float* pml, void* out,
+                              float sl2) {
+  if (G > 8) return hipErrorInvalidValue;
+  if (prefill) {
+    const int groups = (T + 15) / 16 * G;
+    dim3 grid((groups + 3) / 4, hk, 1);
+    hipLaunchKernelGGL((k_attn_mfma<HD, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt, max_pages,
+                       ps, n_pages, hk, G, T, chunk, 1, pos_limit, po, pml, (uint16_t*)out, sl2);
+  } else {
+    dim3 grid(n_split, hk, T);
+    hipLaunchKernelGGL((k_attn_mfma<HD, false>), grid, dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt, max_pages,
+                       ps, n_pages, hk, G, T, chunk, n_split, pos_limit, po, pml, (uint16_t*)out,
+                       sl2);
+  }
+  return hipGetLastError();
 }
 
 template <int AT, int HD>
 static hipError_t attn_g(int G, dim3 grid, hipStream_t st, const void* q, const void* kp,
                          const void* vp, const int* positions, int mode, const int* bt,
                          int max_pages, int ps, int n_pages, int hk, int chunk, int n_split,
-                         int pos_limit, float* po, float* pml, float sl2) {
+                         int pos_limit, float* po, float* pml, void* out, float sl2) {
 #define TPK_ATT(GV)                                                                           \
   hipLaunchKernelGGL((k_attn_split<AT, HD, GV>), grid, dim3(256), 0, st, q, kp, vp, positions, \
-                     mode, bt, max_pages, ps, n_pages, hk, chunk, n_split, pos_limit, po, pml, sl2)
+                     mode, bt, max_pages, ps, n_pages, hk, chunk, n_split, pos_limit, po, pml,   \
+                     out, sl2)
   switch (G) {
     case 1: TPK_ATT(1); break;
     case 2: TPK_ATT(2); break;
@@ -284,27 +646,35 @@ hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* 
                               int pos_limit, float* part_o, float* part_ml, void* out,
                               hipStream_t st) {
   if (T == 0) return hipSuccess;
+  if (n_split > kMaxSplit || chunk % 16 || ps % 16) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
   dim3 grid(n_split, hk, T);
   hipError_t e;
 #define TPK_HD(ATV, HDV)                                                                        \
   e = attn_g<ATV, HDV>(G, grid, st, q, kp, vp, positions, mode, bt, max_pages, ps, n_pages, hk, \
-                       chunk, n_split, pos_limit, part_o, part_ml, sl2)
+                       chunk, n_split, pos_limit, part_o, part_ml, out, sl2)
   if (at == ACT_F32) {
     if (hd == 64) TPK_HD(ACT_F32, 64);
     else if (hd == 128) TPK_HD(ACT_F32, 128);
     else if (hd == 256) TPK_HD(ACT_F32, 256);
     else return hipErrorInvalidValue;
   } else {
-    if (hd == 64) TPK_HD(ACT_BF16, 64);
-    else if (hd == 128) TPK_HD(ACT_BF16, 128);
-    else if (hd == 256) TPK_HD(ACT_BF16, 256);
+    if (chunk % 32) return hipErrorInvalidValue;
+    const bool prefill = (mode == 1);
+#define TPK_HDM(HDV)                                                                          \
+  e = attn_mfma_g<HDV>(prefill, G, T, hk, st, q, kp, vp, positions, mode, bt, max_pages, ps, \
+                       n_pages, chunk, n_split, pos_limit, part_o, part_ml, out, sl2)
+    if (hd == 64) TPK_HDM(64);
+    else if (hd == 128) TPK_HDM(128);
+    else if (hd == 256) TPK_HDM(256);
     else return hipErrorInvalidValue;
+#undef TPK_HDM
+    if (prefill) return e;
   }
 #undef TPK_HD
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || n_split == 1) return e;
   const int hq = hk * G;
-  dim3 cg(T, hq), cb(hd < 256 ? hd : 256);
+  dim3 cg(T, hq, (hd + 63) / 64), cb(256);
   if (at == ACT_F32)
     hipLaunchKernelGGL(k_attn_combine<ACT_F32>, cg, cb, 0, st, part_o, part_ml, n_split, hd, hq, out);
   else

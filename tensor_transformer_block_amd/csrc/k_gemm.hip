@@ -132,11 +132,138 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
   }
 }
 
+// Skinny variant for batched decode (M <= 64 tokens): the weight stream dominates, so a
+// workgroup owns only 16 output columns (16 weight rows) for all M tokens and its four waves
+// split K four ways; each wave keeps MT (<= 4) 16 x 16 tiles in registers, loads both operands
+// straight from global memory (the small activation matrix is served by L2), and the four
+// partial tiles are added in LDS in wave order before the epilogue.
+constexpr int SK_U = 4;  // k-steps of 32 in flight per wave
+
+template <int EPI, int ACTF, int MT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ A,
+                                                     const uint16_t* __restrict__ B,
+                                                     const uint16_t* __restrict__ B2, int M,
+                                                     int N, int K, void* __restrict__ C,
+                                                     int ldc) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int NB = DUAL ? 2 : 1;
+  __shared__ floatx4 s_acc[4][NB][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const int ksteps = (K + 31) / 32;
+  const int per = (ksteps + 3) / 4;
+  const int ks0 = wave * per, ks1 = min(ksteps, ks0 + per);
+  const bool nin = n0 + fr < N;
+  const uint16_t* brow = B + (size_t)(nin ? n0 + fr : 0) * K;
+  const uint16_t* brow2 = DUAL ? B2 + (size_t)(nin ? n0 + fr : 0) * K : nullptr;
+
+  floatx4 acc[NB][MT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[b][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks = ks0; ks < ks1; ks += SK_U) {
+    bf16x8 af[SK_U][MT], bfr[SK_U][NB];
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+      const int k = (ks + u) * 32 + fk;
+      const bool kin = (ks + u < ks1) && (k < K);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int row = i * 16 + fr;
+        uint4 v = (kin && row < M) ? *(const uint4*)(A + (size_t)row * K + k) : make_uint4(0, 0, 0, 0);
+        af[u][i] = __builtin_bit_cast(bf16x8, v);
+      }
+      uint4 w = (kin && nin) ? ld_stream16(brow + k) : make_uint4(0, 0, 0, 0);
+      bfr[u][0] = __builtin_bit_cast(bf16x8, w);
+      if constexpr (DUAL) {
+        uint4 w2 = (kin && nin) ? ld_stream16(brow2 + k) : make_uint4(0, 0, 0, 0);
+        bfr[u][NB - 1] = __builtin_bit_cast(bf16x8, w2);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          acc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][i], bfr[u][b], acc[b][i], 0, 0, 0);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) s_acc[wave][b][i][lane] = acc[b][i];
+  __syncthreads();
+  if (wave != 0) return;
+  const int col = n0 + (lane & 15);
+  if (col >= N) return;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    floatx4 tot[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      tot[b] = s_acc[0][b][i][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) tot[b] += s_acc[w][b][i][lane];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = i * 16 + (lane >> 4) * 4 + r;
+      if (row >= M) continue;
+      const size_t o = (size_t)row * ldc + col;
+      if constexpr (EPI == EPI_GATED) {
+        ((uint16_t*)C)[o] = f32_to_bf16(gated<ACTF>(tot[0][r], tot[NB - 1][r]));
+      } else if constexpr (EPI == EPI_F32) {
+        ((float*)C)[o] = tot[0][r];
+      } else {
+        ((uint16_t*)C)[o] = f32_to_bf16(tot[0][r]);
+      }
+    }
+  }
+}
+
+template <int MT>
+static hipError_t skinny_mt(int epi, int actf, int M, int N, int K, const uint16_t* a,
+                            const uint16_t* b, const uint16_t* b2, void* C, int ldc,
+                            hipStream_t st) {
+  dim3 g((N + 15) / 16), blk(256);
+  switch (epi) {
+    case EPI_ACT:
+      hipLaunchKernelGGL((k_gemm_skinny<EPI_ACT, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      break;
+    case EPI_F32:
+      hipLaunchKernelGGL((k_gemm_skinny<EPI_F32, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((k_gemm_skinny<EPI_BF16, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      break;
+    case EPI_GATED:
+      if (actf == 0)
+        hipLaunchKernelGGL((k_gemm_skinny<EPI_GATED, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      else
+        hipLaunchKernelGGL((k_gemm_skinny<EPI_GATED, 1, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  dim3 g((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M), b(256);
   const uint16_t *a = (const uint16_t*)A, *bb = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
+  if (M <= 64) {
+    switch ((M + 15) / 16) {
+      case 1: return skinny_mt<1>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+      case 2: return skinny_mt<2>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+      case 3: return skinny_mt<3>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+      default: return skinny_mt<4>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+    }
+  }
+  dim3 g((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M), b(256);
   switch (epi) {
     case EPI_ACT:
       hipLaunchKernelGGL((k_gemm_bf16<EPI_ACT, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);

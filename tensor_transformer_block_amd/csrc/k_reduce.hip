@@ -44,6 +44,10 @@ __device__ __forceinline__ float round_to(float v) {
   else return bf16_to_f32(f32_to_bf16(v));
 }
 
+// Up to kPre partials per chunk are loaded before any is added, so their latencies overlap;
+// the sum is still taken strictly in rank order.
+constexpr int kPre = 8;
+
 template <int AT, int PT, int MAXC>
 __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __restrict__ partials,
                                                         int n_part, size_t part_stride,
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
   const int t = blockIdx.x, tid = threadIdx.x;
   const int nchunk = d >> 3;
   const size_t row = (size_t)t * d;
-  float v[MAXC][8];
+  float v[MAXC][8], gm[MAXC][8];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
@@ -63,16 +67,29 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
       const size_t idx = row + (size_t)ci * 8;
       float r[8];
       load8<AT>(res_in, idx, r);
+      if (gamma != nullptr) load8<AT>(gamma, (size_t)ci * 8, gm[c]);
       if (n_part > 0) {
-        float s[8], p[8];
-        load8<PT>(partials, idx, s);
-        for (int k = 1; k < n_part; ++k) {
-          load8<PT>(partials, (size_t)k * part_stride + idx, p);
+        float p[kPre][8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[e] += p[e];
+        for (int k = 0; k < kPre; ++k)
+          if (k < n_part) load8<PT>(partials, (size_t)k * part_stride + idx, p[k]);
+        float sum[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = p[0][e];
+#pragma unroll
+        for (int k = 1; k < kPre; ++k)
+          if (k < n_part) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[e] += p[k][e];
+          }
+        for (int k = kPre; k < n_part; ++k) {
+          float q[8];
+          load8<PT>(partials, (size_t)k * part_stride + idx, q);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] += q[e];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = round_to<AT>(r[e] + s[e]);
+        for (int e = 0; e < 8; ++e) r[e] = round_to<AT>(r[e] + sum[e]);
         store8<AT>(res_out, idx, r);
       }
 #pragma unroll
@@ -86,16 +103,15 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
     const int ci = tid + c * 256;
     if (ci < nchunk) {
-      float g[8], o[8];
-      load8<AT>(gamma, (size_t)ci * 8, g);
+      float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = g[e] * (v[c][e] * inv);
+      for (int e = 0; e < 8; ++e) o[e] = gm[c][e] * (v[c][e] * inv);
       store8<AT>(normed, row + (size_t)ci * 8, o);
     }
   }

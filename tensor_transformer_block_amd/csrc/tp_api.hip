@@ -177,13 +177,15 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   if (L > x.maxpos) L = x.maxpos;
   if (L < 1) L = 1;
   w.pos_limit = L;
-  const int pages = (L + x.ps - 1) / x.ps;
+  // Key splits of the attention: about 256 workgroups in total, each at least one 32-key tile
+  // per wave (128 keys), in multiples of 32 keys.
   const int per_split = x.hk * (int)(T > 0 ? T : 1);
-  const int want = (1024 + per_split - 1) / per_split;
-  int chunk_pages = (pages + want - 1) / want;
-  if (chunk_pages < 4) chunk_pages = 4;
-  w.chunk = chunk_pages * x.ps;
-  w.n_split = (L + w.chunk - 1) / w.chunk;
+  const int want = (256 + per_split - 1) / per_split;
+  int chunk = (L + want - 1) / want;
+  chunk = (chunk + 31) / 32 * 32;
+  if (chunk < 128) chunk = 128;
+  w.chunk = chunk;
+  w.n_split = (L + chunk - 1) / chunk;
   uint64_t off = 0;
   auto put = [&](uint64_t& o, uint64_t bytes) {
     o = off;
@@ -201,15 +203,20 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
 
 // One projection of T tokens: bf16 weights with more tokens than the GEMV holds go to the MFMA
 // GEMM; everything else streams through the GEMV (in groups of up to 4 tokens).
+bool use_gemm(const Dims& x, int T, int K) {
+  return x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K);
+}
+
 hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
-                   int gate_off, const void* X, void* Y, int ldy, hipStream_t st) {
-  if (x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K)) {
+                   int gate_off, const void* X, void* Y, int ldy, hipStream_t st,
+                   const tpk::RopeEpi* rope = nullptr) {
+  if (use_gemm(x, T, K)) {
     const char* B2 = (epi == tpk::EPI_GATED) ? W + (size_t)gate_off * K * 2 : nullptr;
     return tpk::launch_gemm_bf16(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, st);
   }
   const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
   return tpk::launch_gemv(wt, x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16, epi, x.actf, T,
-                          W, S, K, n_out, gate_off, X, Y, ldy, st);
+                          W, S, K, n_out, gate_off, X, Y, ldy, rope, st);
 }
 
 }  // namespace
@@ -436,15 +443,39 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   if (attn) {
     void* qkv = ws + w.qkv;
     if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
-    e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d, x.qkv_rows, 0,
-                xn, qkv, x.qkv_rows, st);
-    if (e != hipSuccess) return hip_fail(e, "qkv projection");
-    if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
-    e = tpk::launch_rope_append(at, qkv, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
-                                batch->mode, batch->block_table, batch->max_pages, x.ps,
-                                kv->n_pages, w.pos_limit, kv->k_pages, kv->v_pages,
-                                batch->rope_table, st);
-    if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
+    if (use_gemm(x, T, x.d)) {
+      // Multi-token MFMA path: projection, then rotary embedding + KV append.
+      e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
+                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st);
+      if (e != hipSuccess) return hip_fail(e, "qkv projection");
+      if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
+      e = tpk::launch_rope_append(at, qkv, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
+                                  batch->mode, batch->block_table, batch->max_pages, x.ps,
+                                  kv->n_pages, w.pos_limit, kv->k_pages, kv->v_pages,
+                                  batch->rope_table, st);
+      if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
+    } else {
+      // Decode path: the GEMV applies the rotary embedding and appends K/V in its epilogue.
+      tpk::RopeEpi re{};
+      re.positions = batch->positions;
+      re.block_table = batch->block_table;
+      re.rope = batch->rope_table;
+      re.q_out = ws + w.q;
+      re.k_pages = kv->k_pages;
+      re.v_pages = kv->v_pages;
+      re.mode = batch->mode;
+      re.max_pages = batch->max_pages;
+      re.ps = x.ps;
+      re.n_pages = kv->n_pages;
+      re.pos_limit = w.pos_limit;
+      re.hq = x.hq;
+      re.hk = x.hk;
+      re.hd = x.hd;
+      e = project(x, tpk::EPI_ROPE, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
+                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, &re);
+      if (e != hipSuccess) return hip_fail(e, "qkv projection");
+      if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
+    }
     e = tpk::launch_attn_decode(at, x.hd, x.Hq / x.Hkv, T, x.hk, ws + w.q, kv->k_pages,
                                 kv->v_pages, batch->positions, batch->mode, batch->block_table,
                                 batch->max_pages, x.ps, kv->n_pages, w.chunk, w.n_split,

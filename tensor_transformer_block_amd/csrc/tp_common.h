@@ -71,6 +71,22 @@ template <> struct Vec16<ACT_BF16> {
   }
 };
 
+// Widen a 16-byte register vector of activations to fp32 (4 fp32 or 8 bf16 values).
+template <int AT>
+__device__ __forceinline__ void unpack16(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (AT == ACT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -8,7 +8,19 @@ namespace tpk {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
-enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3 };
+enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3, EPI_ROPE = 4 };
+
+// Arguments of the fused QKV epilogue (rotary embedding + paged KV append), passed by value.
+struct RopeEpi {
+  const int* positions;
+  const int* block_table;
+  const float* rope;  // [pos_limit or more][hd/2] (cos, sin) pairs
+  void* q_out;        // [T][hq * hd]
+  void* k_pages;
+  void* v_pages;
+  int t0;             // first token of this launch's token group
+  int mode, max_pages, ps, n_pages, pos_limit, hq, hk, hd;
+};
 
 // k_pack.hip
 hipError_t copy2d(void* dst, size_t dst_ld, const void* src, size_t src_ld, int64_t rows,
@@ -29,7 +41,7 @@ hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* pa
 int gemv_max_tokens(int K);
 hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, const void* S,
                        int K, int n_out, int gate_off, const void* X, void* Y, int ldy,
-                       hipStream_t st);
+                       const RopeEpi* rope, hipStream_t st);
 
 // k_gemm.hip
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,

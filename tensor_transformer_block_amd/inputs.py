@@ -233,15 +233,16 @@ def make_inputs(s: BlockShape, seed: int = 0) -> BlockInputs:
 def paged_prior_cache(inp: BlockInputs, rank: int):
     """Rank ``rank``'s K and V page pools holding its owned KV heads' prior keys/values.
 
-    Layout [n_pages][n_kv_heads / tp][page_size][head_dim] in the activation storage dtype.
-    Slots that hold no prior key are zero.
+    K: [n_pages][n_kv_heads / tp][page_size][head_dim]; V is stored transposed,
+    [n_pages][n_kv_heads / tp][head_dim][page_size]; activation storage dtype. Slots that hold no
+    prior key are zero.
     """
     s = inp.shape
     hk = s.n_kv_heads // s.tp
     g0 = rank * hk
     dt = np.float32 if s.act_dtype == "f32" else np.uint16
     kp = np.zeros((inp.n_pages, hk, s.page_size, s.head_dim), dtype=dt)
-    vp = np.zeros_like(kp)
+    vp = np.zeros((inp.n_pages, hk, s.head_dim, s.page_size), dtype=dt)
     for b in range(s.n_seqs):
         kb, vb = inp.k_prior[b][g0:g0 + hk], inp.v_prior[b][g0:g0 + hk]
         plen = kb.shape[1]
@@ -249,5 +250,5 @@ def paged_prior_cache(inp: BlockInputs, rank: int):
             j0, j1 = pg * s.page_size, min(plen, (pg + 1) * s.page_size)
             phys = inp.block_table[b, pg]
             kp[phys, :, 0:j1 - j0] = kb[:, j0:j1]
-            vp[phys, :, 0:j1 - j0] = vb[:, j0:j1]
+            vp[phys, :, :, 0:j1 - j0] = np.swapaxes(vb[:, j0:j1], 1, 2)
     return kp, vp

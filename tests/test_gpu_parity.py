@@ -27,6 +27,9 @@ SHAPES = [
     MED.with_(name="med-bf16-batched-gemm", index=203,
               kv_lens=tuple(int(v) for v in np.random.default_rng(7).integers(1, 300, 21)),
               n_tokens=21),
+    MED.with_(name="med-bf16-batched-5", index=211, kv_lens=(3, 64, 17, 250, 33), n_tokens=5),
+    MED.with_(name="med-bf16-batched-64", index=212, tp=4, n_heads=8, n_kv_heads=4,
+              ffn_dim=1408, kv_lens=tuple(range(40, 40 + 64 * 3, 3)), n_tokens=64),
     MED.with_(name="med-bf16-prefill", index=204, mode="prefill", kv_lens=(137,), n_tokens=100),
     MED.with_(name="med-bf16-prefill-from-empty", index=205, mode="prefill", kv_lens=(70,),
               n_tokens=70, tp=4, n_heads=8, n_kv_heads=4, ffn_dim=1408),
