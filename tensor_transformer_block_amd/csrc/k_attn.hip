@@ -457,9 +457,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       tmax[r] = fmaxf(sc[0][r], sc[1][r]);
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tmax[r] = fmaxf(tmax[r], __shfl_xor(tmax[r], off, 64));
+    for (int r = 0; r < 4; ++r) tmax[r] = row16_max(tmax[r]);
     float alpha[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -488,9 +486,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     if (j + 1 < ntw) load_v(j + 1);
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] += __shfl_xor(lsum[r], off, 64);
+  for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(lsum[r]);
 
   if constexpr (PREFILL) {
     // Lane holds O[row 4 fq + r][hd n * 16 + fr]; write the finished rows.

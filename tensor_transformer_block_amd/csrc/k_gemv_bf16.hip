@@ -1,0 +1,12 @@
+// Decode projections for one weight format; the kernel template is in k_gemv_impl.h.
+#include "k_gemv_impl.h"
+
+namespace tpk {
+
+hipError_t gemv_bf16(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
+                   int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                   hipStream_t st) {
+  return gemv_format<W_BF16, ACT_BF16>(epi, actf, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+}
+
+}  // namespace tpk

@@ -1,0 +1,309 @@
+// K2 / K3: decode projections, y[t, o] = sum_k x[t, k] W[o, k], for a handful of tokens.
+//
+// Decode reads every byte of a rank's 1/N weight slice once per step and does ~1 FLOP per byte,
+// so these kernels are HBM-streaming GEMVs, not GEMMs. A wavefront owns R weight rows and streams
+// them with 16-byte loads, U per row and lane in flight (R * U = 16 loads per lane), R chosen by
+// row length so short rows (o_proj, Q8_0) still keep enough bytes in flight. The first batch of
+// loads is issued before the token vectors are staged in LDS (as fp32), so the two latencies
+// overlap. Dot products finish with DPP row reductions.
+//
+// Weight formats: fp32, bf16, and Q8_0 split into an int8 code plane [out, in] plus an fp16 scale
+// plane [out, in/32] (dequantised in registers, exactly, by q8_dequant).
+// Epilogues:
+//   EPI_F32 / EPI_BF16   store a partial sum (row-parallel o_proj and down, TensorSharp "How
+//             tensor parallelism works", step 3);
+//   EPI_GATED act(g) * u of the column-parallel gate/up pair (row slots 2k, 2k + 1 hold rows p
+//             and p + gate_off);
+//   EPI_ROPE  the fused QKV epilogue: slots 2k, 2k + 1 hold rows i and i + hd/2 of one head, so
+//             the rotary embedding of q and k is applied in registers, q is stored and k and v are
+//             appended to the rank's paged cache (step 2 of the same section: its own KV cache).
+#pragma once
+#include "tp_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+
+template <int WT> struct WFmt;
+template <> struct WFmt<W_F32> { static constexpr int VE = 4, WB = 4; };
+template <> struct WFmt<W_BF16> { static constexpr int VE = 8, WB = 2; };
+template <> struct WFmt<W_Q8> { static constexpr int VE = 16, WB = 1; };
+
+// Decode one 16-byte weight chunk into VE fp32 values.
+template <int WT>
+__device__ __forceinline__ void decode_chunk(const uint4& raw, float scale, float* w) {
+  const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+  if constexpr (WT == W_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __uint_as_float(r[i]);
+  } else if constexpr (WT == W_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = __uint_as_float(r[i] << 16);
+      w[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int32_t code = (int32_t)(int8_t)((r[i] >> (8 * b)) & 0xffu);
+        w[4 * i + b] = q8_dequant(scale, code);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int clampi_g(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Rows per wave by the number of 16-byte chunks per row.
+inline int gemv_rows_per_wave(int nch, bool paired) {
+  int r = nch > 512 ? 1 : (nch > 256 ? 2 : (nch > 128 ? 4 : 8));
+  return (paired && r < 2) ? 2 : r;
+}
+
+template <int WT, int AT, int EPI, int NT, int ACTF, int R>
+__global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
+                                              const uint16_t* __restrict__ S, int K, int n_out,
+                                              int gate_off, const void* __restrict__ X,
+                                              void* __restrict__ Y, int ldy, RopeEpi re) {
+  extern __shared__ float xs[];  // [NT][K]
+  constexpr int VE = WFmt<WT>::VE;
+  constexpr int WB = WFmt<WT>::WB;
+  constexpr int AV = Vec16<AT>::N;
+  constexpr int U = 16 / R;
+  constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
+  static_assert(!PAIRED || R % 2 == 0, "paired epilogues need an even number of rows");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int w = blockIdx.x * 4 + wave;
+
+  // Rows of this wavefront's slots.
+  int row[R];
+  bool ok[R];
+  const int half = re.hd >> 1;
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    if constexpr (EPI == EPI_GATED) {
+      const int p = w * (R / 2) + s / 2;
+      ok[s] = p < n_out;
+      row[s] = (s & 1) ? p + gate_off : p;
+    } else if constexpr (EPI == EPI_ROPE) {
+      const int p = w * (R / 2) + s / 2;
+      ok[s] = p < (n_out >> 1);
+      row[s] = (p / half) * re.hd + (p % half) + ((s & 1) ? half : 0);
+    } else {
+      row[s] = w * R + s;
+      ok[s] = row[s] < n_out;
+    }
+    if (!ok[s]) row[s] = 0;  // loads stay in bounds; results are dropped
+  }
+  const bool active = ok[0];
+  const int nch = K / VE;
+
+  const char* wp[R];
+  const uint16_t* sp[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    wp[s] = (const char*)W + (size_t)row[s] * K * WB;
+    sp[s] = S + (size_t)row[s] * (K / 32);
+  }
+  uint4 b[R][U];
+  float sc[R][U];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) {
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          b[s][u] = ld_stream16(wp[s] + (size_t)c * 16);
+          if constexpr (WT == W_Q8) sc[s][u] = f16_to_f32(sp[s][c >> 1]);
+          else sc[s][u] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          b[s][u] = make_uint4(0, 0, 0, 0);
+          sc[s][u] = 0.f;
+        }
+      }
+    }
+  };
+  load_batch(0);  // in flight while the token vectors are staged
+
+  for (int i = tid * AV; i < NT * K; i += 256 * AV)
+    Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
+  __syncthreads();
+  if (!active) return;
+
+  float acc[R][NT];
+#pragma unroll
+  for (int s = 0; s < R; ++s)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[s][t] = 0.f;
+
+  for (int c0 = 0; c0 < nch; c0 += 64 * U) {
+    if (c0 > 0) load_batch(c0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) {
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          float f[VE];
+          decode_chunk<WT>(b[s][u], sc[s][u], f);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const float* xp = xs + t * K + c * VE;
+#pragma unroll
+            for (int e = 0; e < VE; e += 4) {
+              const float4 xv = *(const float4*)(xp + e);
+              acc[s][t] = fmaf(f[e], xv.x, acc[s][t]);
+              acc[s][t] = fmaf(f[e + 1], xv.y, acc[s][t]);
+              acc[s][t] = fmaf(f[e + 2], xv.z, acc[s][t]);
+              acc[s][t] = fmaf(f[e + 3], xv.w, acc[s][t]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < R; ++s)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[s][t] = wave_sum(acc[s][t]);
+
+  // Lane t stores token t's results.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (lane != t) continue;
+    const size_t yo = (size_t)t * ldy;
+    if constexpr (EPI == EPI_GATED) {
+#pragma unroll
+      for (int s = 0; s < R; s += 2)
+        if (ok[s]) st_act<AT>(Y, yo + row[s], gated<ACTF>(acc[s][t], acc[s + 1][t]));
+    } else if constexpr (EPI == EPI_F32) {
+#pragma unroll
+      for (int s = 0; s < R; ++s)
+        if (ok[s]) ((float*)Y)[yo + row[s]] = acc[s][t];
+    } else if constexpr (EPI == EPI_BF16 || EPI == EPI_ACT) {
+#pragma unroll
+      for (int s = 0; s < R; ++s)
+        if (ok[s]) st_act<EPI == EPI_BF16 ? ACT_BF16 : AT>(Y, yo + row[s], acc[s][t]);
+    } else {  // EPI_ROPE
+      const int tok = re.t0 + t;
+      const int pos = clampi_g(re.positions[tok], 0, re.pos_limit - 1);
+#pragma unroll
+      for (int s = 0; s < R; s += 2) {
+        if (!ok[s]) continue;
+        const int p = w * (R / 2) + s / 2;
+        const int head = p / half, i = p % half;
+        const float a = acc[s][t], bv = acc[s + 1][t];
+        if (head < re.hq + re.hk) {
+          const float2 cs = ((const float2*)re.rope)[(size_t)pos * half + i];
+          const float ra = a * cs.x - bv * cs.y, rb = bv * cs.x + a * cs.y;
+          if (head < re.hq) {
+            const size_t dq = (size_t)tok * re.hq * re.hd + (size_t)head * re.hd + i;
+            st_act<AT>(re.q_out, dq, ra);
+            st_act<AT>(re.q_out, dq + half, rb);
+          } else {
+            const int seq = (re.mode == 0) ? tok : 0;
+            const int page = clampi_g(re.block_table[(size_t)seq * re.max_pages + pos / re.ps], 0,
+                                      re.n_pages - 1);
+            const size_t dk =
+                (((size_t)page * re.hk + (head - re.hq)) * re.ps + pos % re.ps) * re.hd + i;
+            st_act<AT>(re.k_pages, dk, ra);
+            st_act<AT>(re.k_pages, dk + half, rb);
+          }
+        } else {
+          const int seq = (re.mode == 0) ? tok : 0;
+          const int page = clampi_g(re.block_table[(size_t)seq * re.max_pages + pos / re.ps], 0,
+                                    re.n_pages - 1);
+          // V pages are stored transposed: [page][kv head][hd][slot].
+          const size_t dv = ((size_t)page * re.hk + (head - re.hq - re.hk)) * re.hd + i;
+          const int slot = pos % re.ps;
+          st_act<AT>(re.v_pages, dv * re.ps + slot, a);
+          st_act<AT>(re.v_pages, (dv + half) * re.ps + slot, bv);
+        }
+      }
+    }
+  }
+}
+
+template <int WT, int AT, int EPI, int ACTF, int R>
+static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n_out, int gate_off,
+                          const void* X, void* Y, int ldy, const RopeEpi& re, hipStream_t st) {
+  int waves;
+  if constexpr (EPI == EPI_GATED) waves = (n_out + R / 2 - 1) / (R / 2);
+  else if constexpr (EPI == EPI_ROPE) waves = (n_out / 2 + R / 2 - 1) / (R / 2);
+  else waves = (n_out + R - 1) / R;
+  dim3 g((waves + 3) / 4), b(256);
+  const size_t lds = (size_t)nt * K * sizeof(float);
+#define TPK_GEMV(NTV)                                                                       \
+  hipLaunchKernelGGL((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out,   \
+                     gate_off, X, Y, ldy, re)
+  switch (nt) {
+    case 1: TPK_GEMV(1); break;
+    case 2: TPK_GEMV(2); break;
+    case 3: TPK_GEMV(3); break;
+    case 4: TPK_GEMV(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef TPK_GEMV
+  return hipGetLastError();
+}
+
+template <int WT, int AT, int EPI, int ACTF>
+static hipError_t gemv_r(int r, int nt, const void* W, const uint16_t* S, int K, int n_out,
+                         int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                         hipStream_t st) {
+  constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
+  switch (r) {
+    case 1:
+      if constexpr (!PAIRED)
+        return gemv_nt<WT, AT, EPI, ACTF, 1>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return hipErrorInvalidValue;
+    case 2: return gemv_nt<WT, AT, EPI, ACTF, 2>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case 4: return gemv_nt<WT, AT, EPI, ACTF, 4>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case 8: return gemv_nt<WT, AT, EPI, ACTF, 8>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// All epilogues for one weight / activation format (one translation unit per format).
+template <int WT, int AT>
+hipError_t gemv_format(int epi, int actf, int nt, const void* W, const uint16_t* S, int K,
+                       int n_out, int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                       hipStream_t st) {
+  const int nch = K / WFmt<WT>::VE;
+  const bool paired = (epi == EPI_GATED || epi == EPI_ROPE);
+  const int r = gemv_rows_per_wave(nch, paired);
+  switch (epi) {
+    case EPI_F32:
+      return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case EPI_BF16:
+      return gemv_r<WT, AT, EPI_BF16, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case EPI_ACT:
+      return gemv_r<WT, AT, EPI_ACT, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case EPI_ROPE:
+      return gemv_r<WT, AT, EPI_ROPE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case EPI_GATED:
+      if (actf == 0)
+        return gemv_r<WT, AT, EPI_GATED, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return gemv_r<WT, AT, EPI_GATED, 1>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemv_f32(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
+                    int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                    hipStream_t st);
+hipError_t gemv_bf16(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
+                     int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                     hipStream_t st);
+hipError_t gemv_q8(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
+                   int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                   hipStream_t st);
+
+}  // namespace tpk

@@ -87,15 +87,45 @@ __device__ __forceinline__ void unpack16(const uint4& v, float* out) {
   }
 }
 
+// Cross-lane reductions. Inside a row of 16 lanes they use DPP lane swizzles (quad_perm, then
+// row_half_mirror, then row_mirror): after the four steps every lane of the row holds the row
+// total. Rows are combined with two lane permutes through the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kQuadXor1>(v);
+  v += dpp_f<kQuadXor2>(v);
+  v += dpp_f<kRowHalfMirror>(v);
+  v += dpp_f<kRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kRowMirror>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
   return v;
 }
 

@@ -31,6 +31,8 @@ SHAPES = [
     MED.with_(name="med-bf16-batched-64", index=212, tp=4, n_heads=8, n_kv_heads=4,
               ffn_dim=1408, kv_lens=tuple(range(40, 40 + 64 * 3, 3)), n_tokens=64),
     MED.with_(name="med-bf16-prefill", index=204, mode="prefill", kv_lens=(137,), n_tokens=100),
+    MED.with_(name="med-bf16-prefill-300", index=213, mode="prefill", kv_lens=(333,),
+              n_tokens=300),
     MED.with_(name="med-bf16-prefill-from-empty", index=205, mode="prefill", kv_lens=(70,),
               n_tokens=70, tp=4, n_heads=8, n_kv_heads=4, ffn_dim=1408),
     BlockShape(name="med-fp32-g2", index=206, d_model=384, n_heads=4, n_kv_heads=2, head_dim=128,
