@@ -103,6 +103,29 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None when there is no
+    summary for this workload or the kernel source changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"traffic_gate_up_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        srcs = fields["sources"].split()
+        h = hashlib.sha256(b"".join(open(os.path.join(root, p), "rb").read() for p in srcs))
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, seconds):
     """The oracle's explicit N-rank block, fp64 NumPy, on the host cores, for a bounded sample."""
     import numpy as np
@@ -145,6 +168,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a dispatch of known "
+                         "size for scaling hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +201,15 @@ def main():
         f"x {resident / 1e6:.1f} MB")
     blk = DeviceBlock(inp, copies=copies)
     torch.cuda.synchronize()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
 
     for c in range(copies):
         blk.step(c)
@@ -242,7 +277,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ub / kavg / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(s.name)
     roof["kernel"] = "gate/up projection (one rank)"
     roof["avg_us"] = round(kavg * 1e6, 2)
 
