@@ -312,6 +312,373 @@ static hipError_t big_bm(int epi, int actf, int M, int N, int K, const uint16_t*
   return hipGetLastError();
 }
 
+// Split-K variant for batched decode (M <= 64 tokens). A workgroup owns 64 output columns
+// (dual: 64 gate and the matching 64 up columns) for all M tokens and one K range; its four waves
+// take 16 columns each and share the activation tile through LDS (double-buffered, 128-wide K
+// stages), so the activations are read once per 64 columns instead of once per 16. The weight
+// stream of each wave goes straight to registers, one stage ahead. Each split writes its fp32
+// partial tile to workspace; k_splitk_epilogue adds the splits in split order (deterministic)
+// and applies the epilogue.
+constexpr int SP_BK = 128, SP_LD = SP_BK + 8;
+
+template <int MT, bool DUAL>
+__global__ __launch_bounds__(256) void k_gemm_splitk(const uint16_t* __restrict__ A,
+                                                     const uint16_t* __restrict__ B,
+                                                     const uint16_t* __restrict__ B2, int M,
+                                                     int N, int K, int kchunk,
+                                                     float* __restrict__ part) {
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int AR = MT * 16;                  // activation rows staged
+  constexpr int ACH = AR * SP_BK / 8 / 256;    // 16-byte A chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][AR * SP_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const int n0 = blockIdx.x * 64, sidx = blockIdx.y;
+  const int k0 = sidx * kchunk, k1 = min(K, k0 + kchunk);
+  const int col = n0 + wave * 16 + fr;
+  const bool cin = col < N;
+  const uint16_t* brow = B + (size_t)(cin ? col : 0) * K;
+  const uint16_t* brow2 = DUAL ? B2 + (size_t)(cin ? col : 0) * K : nullptr;
+
+  uint4 ra[ACH > 0 ? ACH : 1];
+  uint4 rb[SP_BK / 32][NB];
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + i * 256, r = c / (SP_BK / 8), k = ks + (c % (SP_BK / 8)) * 8;
+      ra[i] = (r < M && k < k1) ? *(const uint4*)(A + (size_t)r * K + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < SP_BK / 32; ++u) {
+      const int k = ks + u * 32 + fk;
+      const bool ok = cin && k < k1;
+      rb[u][0] = ok ? ld_stream16(brow + k) : make_uint4(0, 0, 0, 0);
+      if constexpr (DUAL) rb[u][NB - 1] = ok ? ld_stream16(brow2 + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + i * 256, r = c / (SP_BK / 8), kc = (c % (SP_BK / 8)) * 8;
+      *(uint4*)(&sA[buf][r * SP_LD + kc]) = ra[i];
+    }
+  };
+
+  floatx4 acc[NB][MT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[b][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = (k1 > k0) ? (k1 - k0 + SP_BK - 1) / SP_BK : 0;
+  if (nst > 0) {
+    gload(k0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    uint4 bcur[SP_BK / 32][NB];
+#pragma unroll
+    for (int u = 0; u < SP_BK / 32; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bcur[u][b] = rb[u][b];
+    if (st + 1 < nst) gload(k0 + (st + 1) * SP_BK);
+#pragma unroll
+    for (int u = 0; u < SP_BK / 32; ++u) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const bf16x8 af = *(const bf16x8*)(&sA[cur][(i * 16 + fr) * SP_LD + u * 32 + fk]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af, __builtin_bit_cast(bf16x8, bcur[u][b]), acc[b][i], 0, 0, 0);
+      }
+    }
+    if (st + 1 < nst) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  // Partial tile: part[sidx][row][col] (dual: gate at col, up at N + col).
+  const int ncols = DUAL ? 2 * N : N;
+  if (!cin) return;
+  float* pbase = part + (size_t)sidx * M * ncols;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = i * 16 + (lane >> 4) * 4 + r;
+      if (row >= M) continue;
+      pbase[(size_t)row * ncols + col] = acc[0][i][r];
+      if constexpr (DUAL) pbase[(size_t)row * ncols + N + col] = acc[NB - 1][i][r];
+    }
+}
+
+template <int EPI, int ACTF>
+__global__ void k_splitk_epilogue(const float* __restrict__ part, int S, int M, int N,
+                                  void* __restrict__ C, int ldc) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  const int ncols = DUAL ? 2 * N : N;
+  const size_t total = (size_t)M * N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(i / N), col = (int)(i % N);
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float* p = part + ((size_t)s * M + row) * ncols;
+      g += p[col];
+      if constexpr (DUAL) u += p[N + col];
+    }
+    const size_t o = (size_t)row * ldc + col;
+    if constexpr (EPI == EPI_GATED) ((uint16_t*)C)[o] = f32_to_bf16(gated<ACTF>(g, u));
+    else if constexpr (EPI == EPI_F32) ((float*)C)[o] = g;
+    else ((uint16_t*)C)[o] = f32_to_bf16(g);
+  }
+}
+
+// Split count for the split-K variant: enough workgroups to cover the chip, K ranges a multiple
+// of the 128-wide stage and at least 256 long.
+void splitk_plan(int N, int K, bool dual, int* S, int* kchunk) {
+  const int tiles = (N + 63) / 64;
+  int s = (256 + tiles - 1) / tiles;
+  const int smax = (K + 255) / 256;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  int kc = (K + s - 1) / s;
+  kc = (kc + SP_BK - 1) / SP_BK * SP_BK;
+  *kchunk = kc;
+  *S = (K + kc - 1) / kc;
+  (void)dual;
+}
+
+size_t splitk_workspace_bytes(int M, int N, int K, bool dual) {
+  int S, kc;
+  splitk_plan(N, K, dual, &S, &kc);
+  return (size_t)S * M * (dual ? 2 * N : N) * sizeof(float);
+}
+
+hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
+                              const void* B, const void* B2, void* C, int ldc, float* part,
+                              hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M > 64) return hipErrorInvalidValue;
+  const bool dual = (epi == EPI_GATED);
+  int S, kc;
+  splitk_plan(N, K, dual, &S, &kc);
+  dim3 g((N + 63) / 64, S), blk(256);
+  const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
+  const int mt = (M + 15) / 16;
+#define TPK_SK(MTV)                                                                              \
+  if (dual) hipLaunchKernelGGL((k_gemm_splitk<MTV, true>), g, blk, 0, st, a, b, b2, M, N, K, kc, part); \
+  else hipLaunchKernelGGL((k_gemm_splitk<MTV, false>), g, blk, 0, st, a, b, b2, M, N, K, kc, part)
+  switch (mt) {
+    case 1: TPK_SK(1); break;
+    case 2: TPK_SK(2); break;
+    case 3: TPK_SK(3); break;
+    default: TPK_SK(4); break;
+  }
+#undef TPK_SK
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t total = (size_t)M * N;
+  dim3 eg((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)), eb(256);
+  switch (epi) {
+    case EPI_ACT: hipLaunchKernelGGL((k_splitk_epilogue<EPI_ACT, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_F32: hipLaunchKernelGGL((k_splitk_epilogue<EPI_F32, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_BF16: hipLaunchKernelGGL((k_splitk_epilogue<EPI_BF16, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_GATED:
+      if (actf == 0) hipLaunchKernelGGL((k_splitk_epilogue<EPI_GATED, 0>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      else hipLaunchKernelGGL((k_splitk_epilogue<EPI_GATED, 1>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Prefill GEMM with a three-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4,
+// gfx950): a wave-wide load drops 64 x 16 bytes straight into LDS, so no registers hold staged
+// data and two K-tiles stay in flight while the third is multiplied. Rows of 64 bf16 are stored
+// with their eight 16-byte chunks XOR-swizzled by (row & 7): the DMA writes stay contiguous and
+// the MFMA operand reads (16 rows, one chunk each) hit distinct banks. Tiles and epilogues as in
+// k_gemm_big. Needs K % 64 == 0; rows and columns past M and N load clamped (valid) addresses and
+// their results are never stored.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int LG_BK = 64, LG_ST = 3;
+
+template <int N_OUT>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N_OUT (6-bit, split field), expcnt and lgkmcnt left at "no wait".
+  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | (7 << 4) | (15 << 8) | ((N_OUT >> 4) << 14));
+}
+
+template <int EPI, int ACTF, int BM>
+__global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A,
+                                                  const uint16_t* __restrict__ B,
+                                                  const uint16_t* __restrict__ B2, int M, int N,
+                                                  int K, void* __restrict__ C, int ldc,
+                                                  int tiles_m, int tiles_n) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int WM = BM / 2, TM = WM / 16, TN = 4;
+  constexpr int A_LOADS = BM / 8 / 4;   // 1 KB wave-loads of A per wave per stage
+  constexpr int B_LOADS = 128 / 8 / 4;  // ... of B
+  constexpr int LPS = A_LOADS + B_LOADS;
+  constexpr int STAGE = (BM + 128) * LG_BK;  // bf16 elements per stage
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int full = nblk / 8 * 8;
+  const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
+  const int tm = lt / tiles_n, tn = lt % tiles_n;
+  const int m0 = tm * BM;
+  const int n0 = DUAL ? tn * 64 : tn * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Per-lane source pointers of this wave's wave-loads (k offset added per stage).
+  const uint16_t* asrc[A_LOADS];
+  const uint16_t* bsrc[B_LOADS];
+  const int lrow = lane >> 3, lpc = lane & 7;
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int row = (wave * A_LOADS + i) * 8 + lrow;
+    const int kc = lpc ^ (row & 7);
+    const int gr = min(m0 + row, M - 1);
+    asrc[i] = A + (size_t)gr * K + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int row = (wave * B_LOADS + i) * 8 + lrow;  // 0..127
+    const int kc = lpc ^ (row & 7);
+    const uint16_t* src;
+    int col;
+    if constexpr (DUAL) {
+      src = (row < 64) ? B : B2;
+      col = n0 + (row & 63);
+    } else {
+      src = B;
+      col = n0 + row;
+    }
+    bsrc[i] = src + (size_t)min(col, N - 1) * K + kc * 8;
+  }
+  auto issue = [&](int stage_slot, int k0) {
+    uint16_t* st = smem + stage_slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[i] + k0),
+                                       (lds_void_t*)(st + (wave * A_LOADS + i) * 8 * LG_BK), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc[i] + k0),
+                                       (lds_void_t*)(st + BM * LG_BK + (wave * B_LOADS + i) * 8 * LG_BK),
+                                       16, 0, 0);
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto brow = [&](int j) -> int {
+    if constexpr (DUAL) return (j < 2 ? 0 : 64) + wn * 32 + (j & 1) * 16;
+    else return wn * 64 + j * 16;
+  };
+  const int fr = lane & 15, fq = lane >> 4;
+  const int nk = K / LG_BK;
+  issue(0, 0);
+  if (nk > 1) issue(1, LG_BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    // This wave's loads of stage kt are done once at most LPS (stage kt + 1) remain; after the
+    // barrier every wave's are, while the next stage's loads stay in flight.
+    if (kt + 1 < nk) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    // Bare barrier: the memory clobber keeps the compiler from moving LDS accesses across it.
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 < nk) issue((kt + 2) % LG_ST, (kt + 2) * LG_BK);
+    const uint16_t* a_s = smem + (kt % LG_ST) * STAGE;
+    const uint16_t* b_s = a_s + BM * LG_BK;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kc = kk * 4 + fq;  // logical 16-byte chunk of this lane's 8 k values
+      bf16x8 bf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = brow(j) + fr;
+        bf[j] = *(const bf16x8*)(b_s + r * LG_BK + 8 * (kc ^ (r & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 16 + fr;
+        const bf16x8 af = *(const bf16x8*)(a_s + r * LG_BK + 8 * (kc ^ (r & 7)));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * WM + i * 16 + fq * 4 + r;
+      if (row >= M) continue;
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wn * 32 + j * 16 + fr;
+          if (col < N)
+            ((uint16_t*)C)[(size_t)row * ldc + col] =
+                f32_to_bf16(gated<ACTF>(acc[i][j][r], acc[i][j + 2][r]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * 64 + j * 16 + fr;
+          if (col >= N) continue;
+          const size_t o = (size_t)row * ldc + col;
+          if constexpr (EPI == EPI_F32) ((float*)C)[o] = acc[i][j][r];
+          else ((uint16_t*)C)[o] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+template <int BM>
+static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t* a,
+                         const uint16_t* b, const uint16_t* b2, void* C, int ldc, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128;
+  dim3 g(tiles_m * tiles_n), blk(256);
+  const size_t lds = (size_t)LG_ST * (BM + 128) * LG_BK * sizeof(uint16_t);
+#define TPK_LDS(E, AF)                                                                          \
+  do {                                                                                          \
+    static bool attr_set = false;                                                               \
+    if (!attr_set) {                                                                            \
+      hipFuncSetAttribute((const void*)k_gemm_lds<E, AF, BM>,                                   \
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
+      attr_set = true;                                                                          \
+    }                                                                                           \
+    hipLaunchKernelGGL((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
+                       tiles_m, tiles_n);                                                       \
+  } while (0)
+  switch (epi) {
+    case EPI_ACT: TPK_LDS(EPI_ACT, 0); break;
+    case EPI_F32: TPK_LDS(EPI_F32, 0); break;
+    case EPI_BF16: TPK_LDS(EPI_BF16, 0); break;
+    case EPI_GATED:
+      if (actf == 0) TPK_LDS(EPI_GATED, 0);
+      else TPK_LDS(EPI_GATED, 1);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef TPK_LDS
+  return hipGetLastError();
+}
+
 // Skinny variant for batched decode (M <= 64 tokens): the weight stream dominates, so a
 // workgroup owns only 16 output columns (16 weight rows) for all M tokens and its four waves
 // split K four ways; each wave keeps MT (<= 4) 16 x 16 tiles in registers, loads both operands
@@ -455,6 +822,10 @@ hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* 
   if (M >= 256) {
     // Enough row bands for 256-row tiles to fill the chip, else 128-row tiles.
     const long t256 = (long)((M + 255) / 256) * ((epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128);
+    if (K % LG_BK == 0) {
+      if (t256 >= 256) return lds_bm<256>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+      return lds_bm<128>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
+    }
     if (t256 >= 256) return big_bm<256>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
     return big_bm<128>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
   }

@@ -143,7 +143,7 @@ void make_layout(const Dims& x, tp_shard_layout* L) {
 }
 
 struct WsLayout {
-  uint64_t qkv, q, attn, part_o, part_ml, ffn, total;
+  uint64_t qkv, q, attn, part_o, part_ml, ffn, gemm, total;
   int n_split, chunk, pos_limit;
 };
 
@@ -197,6 +197,17 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   put(w.part_o, T * x.hq * (uint64_t)w.n_split * x.hd * 4);
   put(w.part_ml, T * x.hq * (uint64_t)w.n_split * 2 * 4);
   put(w.ffn, T * x.fr * x.ab);
+  // fp32 split-K partial tiles of the batched-decode projections (bf16 weights, 4 < T <= 64).
+  uint64_t gemm = 0;
+  if (x.wt == TP_DTYPE_BF16 && T > 0 && T <= 64) {
+    const uint64_t cand[4] = {
+        tpk::splitk_workspace_bytes((int)T, x.qkv_rows, x.d, false),
+        tpk::splitk_workspace_bytes((int)T, x.d, x.qdim, false),
+        tpk::splitk_workspace_bytes((int)T, x.fr, x.d, true),
+        tpk::splitk_workspace_bytes((int)T, x.d, x.fr, false)};
+    for (uint64_t c : cand) gemm = c > gemm ? c : gemm;
+  }
+  put(w.gemm, gemm);
   w.total = off > 0 ? off : kAlign;
   return w;
 }
@@ -209,9 +220,11 @@ bool use_gemm(const Dims& x, int T, int K) {
 
 hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, hipStream_t st,
-                   const tpk::RopeEpi* rope = nullptr) {
+                   const tpk::RopeEpi* rope = nullptr, float* splitk_ws = nullptr) {
   if (use_gemm(x, T, K)) {
     const char* B2 = (epi == tpk::EPI_GATED) ? W + (size_t)gate_off * K * 2 : nullptr;
+    if (T <= 64 && splitk_ws)
+      return tpk::launch_gemm_splitk(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, splitk_ws, st);
     return tpk::launch_gemm_bf16(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, st);
   }
   const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
@@ -439,6 +452,7 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   char* ws = (char*)workspace;
   const int epi_part = x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16;
   const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  float* skw = w.gemm != w.total && x.wt == TP_DTYPE_BF16 && T <= 64 ? (float*)(ws + w.gemm) : nullptr;
   hipError_t e;
   if (attn) {
     void* qkv = ws + w.qkv;
@@ -446,7 +460,7 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
     if (use_gemm(x, T, x.d)) {
       // Multi-token MFMA path: projection, then rotary embedding + KV append.
       e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
-                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st);
+                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, nullptr, skw);
       if (e != hipSuccess) return hip_fail(e, "qkv projection");
       if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
       e = tpk::launch_rope_append(at, qkv, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
@@ -483,16 +497,16 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
                                 ws + w.attn, st);
     if (e != hipSuccess) return hip_fail(e, "attention");
     e = project(x, epi_part, T, sh + L.o.offset, sh + L.o_scale.offset, x.qdim, x.d, 0,
-                ws + w.attn, partial_out, x.d, st);
+                ws + w.attn, partial_out, x.d, st, nullptr, skw);
     if (e != hipSuccess) return hip_fail(e, "o projection");
   } else {
     if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
     e = project(x, tpk::EPI_GATED, T, sh + L.gate_up.offset, sh + L.gate_up_scale.offset, x.d,
-                x.fr, x.fr, xn, ws + w.ffn, x.fr, st);
+                x.fr, x.fr, xn, ws + w.ffn, x.fr, st, nullptr, skw);
     if (e != hipSuccess) return hip_fail(e, "gate/up projection");
     if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
     e = project(x, epi_part, T, sh + L.down.offset, sh + L.down_scale.offset, x.fr, x.d, 0,
-                ws + w.ffn, partial_out, x.d, st);
+                ws + w.ffn, partial_out, x.d, st, nullptr, skw);
     if (e != hipSuccess) return hip_fail(e, "down projection");
   }
   g_err.clear();

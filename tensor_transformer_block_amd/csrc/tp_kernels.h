@@ -44,6 +44,10 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
                        const RopeEpi* rope, hipStream_t st);
 
 // k_gemm.hip
+size_t splitk_workspace_bytes(int M, int N, int K, bool dual);
+hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
+                              const void* B, const void* B2, void* C, int ldc, float* part,
+                              hipStream_t st);
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
 
