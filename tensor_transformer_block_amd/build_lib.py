@@ -21,7 +21,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_*_f32) for this target.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # Keep MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register
+                # allocator copies them around every MFMA of a software-pipelined k-loop.
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
 

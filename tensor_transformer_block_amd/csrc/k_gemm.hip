@@ -513,7 +513,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int EPI, int ACTF, int BM>
-__global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 1 : 2))) void k_gemm_lds(const uint16_t* __restrict__ A,
                                                   const uint16_t* __restrict__ B,
                                                   const uint16_t* __restrict__ B2, int M, int N,
                                                   int K, void* __restrict__ C, int ldc,
@@ -530,49 +530,43 @@ __global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A
   const int full = nblk / 8 * 8;
   const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
   const int tm = lt / tiles_n, tn = lt % tiles_n;
-  const int m0 = tm * BM;
-  const int n0 = DUAL ? tn * 64 : tn * 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The last tile in M (and in N) is shifted back to end at the matrix edge, so every load is in
+  // bounds without per-row clamps; rows and columns before ms0 / ns0 belong to the previous tile
+  // and are not stored twice. The launcher guarantees M >= BM and N >= the tile width.
+  constexpr int NW = DUAL ? 64 : 128;
+  const int ms0 = tm * BM, ns0 = tn * NW;
+  const int m0 = min(ms0, M - BM), n0 = min(ns0, N - NW);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Per-lane source pointers of this wave's wave-loads (k offset added per stage).
-  const uint16_t* asrc[A_LOADS];
-  const uint16_t* bsrc[B_LOADS];
+  // Wave-load i of A covers tile rows (wave * A_LOADS + i) * 8 + lane / 8, 16 bytes each; since
+  // those row groups start at multiples of 8, the swizzled chunk (lane % 8) ^ (row % 8) and thus
+  // the lane's byte offset inside a group is the same for every load, A and B alike. Bases stay
+  // wave-uniform (scalar registers); only that one 32-bit offset lives in a vector register.
   const int lrow = lane >> 3, lpc = lane & 7;
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int row = (wave * A_LOADS + i) * 8 + lrow;
-    const int kc = lpc ^ (row & 7);
-    const int gr = min(m0 + row, M - 1);
-    asrc[i] = A + (size_t)gr * K + kc * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int row = (wave * B_LOADS + i) * 8 + lrow;  // 0..127
-    const int kc = lpc ^ (row & 7);
-    const uint16_t* src;
-    int col;
-    if constexpr (DUAL) {
-      src = (row < 64) ? B : B2;
-      col = n0 + (row & 63);
-    } else {
-      src = B;
-      col = n0 + row;
-    }
-    bsrc[i] = src + (size_t)min(col, N - 1) * K + kc * 8;
-  }
+  const uint32_t lane_off = (uint32_t)((lrow * K + ((lpc ^ lrow) << 3)) * 2);
+  const char* a_base = (const char*)(A + (size_t)(m0 + wave * A_LOADS * 8) * K);
+  const size_t grp_stride = (size_t)8 * K * 2;  // bytes between consecutive 8-row groups
   auto issue = [&](int stage_slot, int k0) {
     uint16_t* st = smem + stage_slot * STAGE;
+    const size_t kb = (size_t)k0 * 2;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[i] + k0),
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp_stride + kb + lane_off),
                                        (lds_void_t*)(st + (wave * A_LOADS + i) * 8 * LG_BK), 16,
                                        0, 0);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(bsrc[i] + k0),
-                                       (lds_void_t*)(st + BM * LG_BK + (wave * B_LOADS + i) * 8 * LG_BK),
-                                       16, 0, 0);
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int g = wave * B_LOADS + i;  // 8-row group of the 128 staged B rows
+      const char* src;
+      if constexpr (DUAL)
+        src = (const char*)((g < 8 ? B : B2) + (size_t)(n0 + (g & 7) * 8) * K);
+      else
+        src = (const char*)(B + (size_t)(n0 + g * 8) * K);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + kb + lane_off),
+                                       (lds_void_t*)(st + BM * LG_BK + g * 8 * LG_BK), 16, 0, 0);
+    }
   };
 
   floatx4 acc[TM][TN];
@@ -586,36 +580,97 @@ __global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A
   };
   const int fr = lane & 15, fq = lane >> 4;
   const int nk = K / LG_BK;
+  // Operand fragments of one 32-deep k-step: TN of B, TM of A, read from a swizzled stage.
+  struct Frag {
+    bf16x8 a[TM], b[TN];
+  };
+  auto load_frag = [&](Frag& f, int slot, int kk) {
+    const uint16_t* a_s = smem + slot * STAGE;
+    const uint16_t* b_s = a_s + BM * LG_BK;
+    const int kc = kk * 4 + fq;  // logical 16-byte chunk of this lane's 8 k values
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = brow(j) + fr;
+      f.b[j] = *(const bf16x8*)(b_s + r * LG_BK + 8 * (kc ^ (r & 7)));
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + i * 16 + fr;
+      f.a[i] = *(const bf16x8*)(a_s + r * LG_BK + 8 * (kc ^ (r & 7)));
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Schedule per K-tile kt (BK = 64, two k-steps): the second k-step's fragments are read while
+  // the first k-step's MFMAs run; the barrier that publishes tile kt + 1 sits between the two
+  // halves, and the next tile's first fragments are read while the second half's MFMAs run. So
+  // LDS read latency and the barrier wait overlap matrix work instead of adding to it.
   issue(0, 0);
   if (nk > 1) issue(1, LG_BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads of stage kt are done once at most LPS (stage kt + 1) remain; after the
-    // barrier every wave's are, while the next stage's loads stay in flight.
-    if (kt + 1 < nk) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-    // Bare barrier: the memory clobber keeps the compiler from moving LDS accesses across it.
-    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 2 < nk) issue((kt + 2) % LG_ST, (kt + 2) * LG_BK);
-    const uint16_t* a_s = smem + (kt % LG_ST) * STAGE;
-    const uint16_t* b_s = a_s + BM * LG_BK;
+  if (nk > 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+  // Bare barrier: the memory clobber keeps the compiler from moving LDS accesses across it.
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (nk > 2) issue(2, 2 * LG_BK);
+  Frag cur, nxt;
+  load_frag(cur, 0, 0);
+  int kt = 0;
+  // Steady state, free of branches between the two MFMA halves (a branch there makes the register
+  // allocator copy accumulators around): tiles kt + 1 and kt + 2 are in flight, kt + 3 is issued.
+  constexpr int NF = TM + TN, NMMA = TM * TN;
+  static_assert(NMMA >= 2 * NF && NMMA >= LPS + NF, "MFMA count must cover the interleaved reads");
+  for (; kt + 3 < nk; ++kt) {
+    const int slot = kt % LG_ST;
+    load_frag(nxt, slot, 1);
+    mma(cur);
+    // Scheduling hints: two MFMAs, then one fragment read, so the reads hide under matrix work.
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kc = kk * 4 + fq;  // logical 16-byte chunk of this lane's 8 k values
-      bf16x8 bf[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = brow(j) + fr;
-        bf[j] = *(const bf16x8*)(b_s + r * LG_BK + 8 * (kc ^ (r & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 16 + fr;
-        const bf16x8 af = *(const bf16x8*)(a_s + r * LG_BK + 8 * (kc ^ (r & 7)));
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-      }
+    for (int g = 0; g < NF; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
+    if constexpr (NMMA > 2 * NF) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - 2 * NF, 0);
+    // Nothing crosses the wait + barrier below (MFMAs touch no memory, so the asm alone would not
+    // stop the scheduler from moving them over it).
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<LPS>();
+    // After this barrier every wave has finished reading tile kt (its reads completed before
+    // the barrier), so tile kt + 3 may overwrite that slot.
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(slot, (kt + 3) * LG_BK);
+    load_frag(cur, (kt + 1) % LG_ST, 0);
+    mma(nxt);
+    // Hint: the global->LDS loads, then the next tile's first reads, each after one MFMA.
+#pragma unroll
+    for (int g = 0; g < LPS; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (direct-to-LDS load)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < NF; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if constexpr (NMMA > LPS + NF) __builtin_amdgcn_sched_group_barrier(0x008, NMMA - LPS - NF, 0);
+  }
+  // The last (at most three) tiles: nothing more to issue.
+  for (; kt < nk; ++kt) {
+    load_frag(nxt, kt % LG_ST, 1);
+    mma(cur);
+    if (kt + 1 < nk) {
+      if (kt + 2 < nk) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_frag(cur, (kt + 1) % LG_ST, 0);
+    }
+    mma(nxt);
   }
 
 #pragma unroll
@@ -623,12 +678,12 @@ __global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + wm * WM + i * 16 + fq * 4 + r;
-      if (row >= M) continue;
+      if (row < ms0) continue;  // stored by the previous tile
       if constexpr (DUAL) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + wn * 32 + j * 16 + fr;
-          if (col < N)
+          if (col >= ns0)
             ((uint16_t*)C)[(size_t)row * ldc + col] =
                 f32_to_bf16(gated<ACTF>(acc[i][j][r], acc[i][j + 2][r]));
         }
@@ -636,7 +691,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(const uint16_t* __restrict__ A
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col = n0 + wn * 64 + j * 16 + fr;
-          if (col >= N) continue;
+          if (col < ns0) continue;
           const size_t o = (size_t)row * ldc + col;
           if constexpr (EPI == EPI_F32) ((float*)C)[o] = acc[i][j][r];
           else ((uint16_t*)C)[o] = f32_to_bf16(acc[i][j][r]);
@@ -651,6 +706,7 @@ static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t*
                          const uint16_t* b, const uint16_t* b2, void* C, int ldc, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128;
+  if (M < BM || N < ((epi == EPI_GATED) ? 64 : 128) || K % LG_BK != 0) return hipErrorInvalidValue;
   dim3 g(tiles_m * tiles_n), blk(256);
   const size_t lds = (size_t)LG_ST * (BM + 128) * LG_BK * sizeof(uint16_t);
 #define TPK_LDS(E, AF)                                                                          \
@@ -822,7 +878,8 @@ hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* 
   if (M >= 256) {
     // Enough row bands for 256-row tiles to fill the chip, else 128-row tiles.
     const long t256 = (long)((M + 255) / 256) * ((epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128);
-    if (K % LG_BK == 0) {
+    // The direct-to-LDS kernel needs whole K-tiles and at least one full tile in N.
+    if (K % LG_BK == 0 && N >= ((epi == EPI_GATED) ? 64 : 128)) {
       if (t256 >= 256) return lds_bm<256>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
       return lds_bm<128>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);
     }
