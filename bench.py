@@ -253,9 +253,10 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     tok_s = s.n_tokens / (ms / 1e3)
 
-    # Dominant kernel: the gate/up projection, bracketed by events the library records on the
-    # launch stream. A backlog of graph replays keeps the stream busy so no host launch latency
-    # lands between the events.
+    # Dominant kernel: the gate/up projection. The library launches its kernels through
+    # hipExtLaunchKernel with these events, so each pair spans that projection's kernel execution
+    # on the launch stream (what a profiler's kernel trace reports). A backlog of graph replays
+    # first brings the GPU to the same steady state as the timed steps.
     log(f"timing the gate/up projection ({args.kernel_iters} launches)")
     hev = HipEvents(2 * args.kernel_iters)
     for i in range(min(64, args.steps)):

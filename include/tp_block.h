@@ -156,10 +156,13 @@ tp_status tp_block_shard_forward(const tp_block_desc* desc, int32_t rank, int32_
                                  const tp_kv_cache* kv, void* partial_out, void* workspace,
                                  uint64_t workspace_bytes, void* stream);
 
-/* Measurement variant of tp_block_shard_forward: the same work, plus hipEventRecord(ev_begin)
- * on `stream` immediately before, and hipEventRecord(ev_end) immediately after, the launch of the
- * half's dominant weight stream (ATTN: the QKV projection; FFN: the gate/up projection). The
- * events are caller-created hipEvent_t handles; NULL skips that record. Not for graph capture. */
+/* Measurement variant of tp_block_shard_forward: the same work, with the kernels of the half's
+ * dominant weight stream (ATTN: the QKV projection; FFN: the gate/up projection) launched through
+ * hipExtLaunchKernel so that ev_begin is recorded when the first of them starts executing and
+ * ev_end when the last of them finishes: hipEventElapsedTime(ev_begin, ev_end) is that
+ * projection's kernel time, as a profiler's kernel trace would report it, without the stream's
+ * dispatch gaps. The events are caller-created hipEvent_t handles (ev_end NULL: no timing).
+ * Not for graph capture. */
 tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, int32_t half,
                                        const void* shard, const tp_batch* batch, const void* xn,
                                        const tp_kv_cache* kv, void* partial_out, void* workspace,

@@ -294,7 +294,7 @@ static hipError_t big_bm(int epi, int actf, int M, int N, int K, const uint16_t*
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
       attr_set = true;                                                                          \
     }                                                                                           \
-    hipLaunchKernelGGL((k_gemm_big<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
+    launch((k_gemm_big<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
                        tiles_m, tiles_n);                                                       \
   } while (0)
   switch (epi) {
@@ -468,8 +468,8 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   const int mt = (M + 15) / 16;
 #define TPK_SK(MTV)                                                                              \
-  if (dual) hipLaunchKernelGGL((k_gemm_splitk<MTV, true>), g, blk, 0, st, a, b, b2, M, N, K, kc, part); \
-  else hipLaunchKernelGGL((k_gemm_splitk<MTV, false>), g, blk, 0, st, a, b, b2, M, N, K, kc, part)
+  if (dual) launch((k_gemm_splitk<MTV, true>), g, blk, 0, st, a, b, b2, M, N, K, kc, part); \
+  else launch((k_gemm_splitk<MTV, false>), g, blk, 0, st, a, b, b2, M, N, K, kc, part)
   switch (mt) {
     case 1: TPK_SK(1); break;
     case 2: TPK_SK(2); break;
@@ -482,12 +482,12 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
   const size_t total = (size_t)M * N;
   dim3 eg((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)), eb(256);
   switch (epi) {
-    case EPI_ACT: hipLaunchKernelGGL((k_splitk_epilogue<EPI_ACT, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_F32: hipLaunchKernelGGL((k_splitk_epilogue<EPI_F32, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_BF16: hipLaunchKernelGGL((k_splitk_epilogue<EPI_BF16, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_ACT: launch((k_splitk_epilogue<EPI_ACT, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_F32: launch((k_splitk_epilogue<EPI_F32, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_BF16: launch((k_splitk_epilogue<EPI_BF16, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
     case EPI_GATED:
-      if (actf == 0) hipLaunchKernelGGL((k_splitk_epilogue<EPI_GATED, 0>), eg, eb, 0, st, part, S, M, N, C, ldc);
-      else hipLaunchKernelGGL((k_splitk_epilogue<EPI_GATED, 1>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      if (actf == 0) launch((k_splitk_epilogue<EPI_GATED, 0>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      else launch((k_splitk_epilogue<EPI_GATED, 1>), eg, eb, 0, st, part, S, M, N, C, ldc);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -717,7 +717,7 @@ static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t*
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
       attr_set = true;                                                                          \
     }                                                                                           \
-    hipLaunchKernelGGL((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
+    launch((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
                        tiles_m, tiles_n);                                                       \
   } while (0)
   switch (epi) {
@@ -843,19 +843,19 @@ static hipError_t skinny_mt(int epi, int actf, int M, int N, int K, const uint16
   dim3 g((N + 15) / 16), blk(256);
   switch (epi) {
     case EPI_ACT:
-      hipLaunchKernelGGL((k_gemm_skinny<EPI_ACT, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      launch((k_gemm_skinny<EPI_ACT, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
       break;
     case EPI_F32:
-      hipLaunchKernelGGL((k_gemm_skinny<EPI_F32, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      launch((k_gemm_skinny<EPI_F32, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((k_gemm_skinny<EPI_BF16, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+      launch((k_gemm_skinny<EPI_BF16, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
       break;
     case EPI_GATED:
       if (actf == 0)
-        hipLaunchKernelGGL((k_gemm_skinny<EPI_GATED, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+        launch((k_gemm_skinny<EPI_GATED, 0, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
       else
-        hipLaunchKernelGGL((k_gemm_skinny<EPI_GATED, 1, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
+        launch((k_gemm_skinny<EPI_GATED, 1, MT>), g, blk, 0, st, a, b, b2, M, N, K, C, ldc);
       break;
     default:
       return hipErrorInvalidValue;
@@ -889,19 +889,19 @@ hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* 
   dim3 g((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M), b(256);
   switch (epi) {
     case EPI_ACT:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_ACT, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      launch((k_gemm_bf16<EPI_ACT, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
       break;
     case EPI_F32:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_F32, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      launch((k_gemm_bf16<EPI_F32, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((k_gemm_bf16<EPI_BF16, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+      launch((k_gemm_bf16<EPI_BF16, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
       break;
     case EPI_GATED:
       if (actf == 0)
-        hipLaunchKernelGGL((k_gemm_bf16<EPI_GATED, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+        launch((k_gemm_bf16<EPI_GATED, 0>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
       else
-        hipLaunchKernelGGL((k_gemm_bf16<EPI_GATED, 1>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
+        launch((k_gemm_bf16<EPI_GATED, 1>), g, b, 0, st, a, bb, b2, M, N, K, C, ldc);
       break;
     default:
       return hipErrorInvalidValue;

@@ -241,7 +241,7 @@ static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n
   dim3 g((waves + 3) / 4), b(256);
   const size_t lds = (size_t)nt * K * sizeof(float);
 #define TPK_GEMV(NTV)                                                                       \
-  hipLaunchKernelGGL((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out,   \
+  launch((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out,   \
                      gate_off, X, Y, ldy, re)
   switch (nt) {
     case 1: TPK_GEMV(1); break;

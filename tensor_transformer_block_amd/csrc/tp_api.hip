@@ -11,6 +11,10 @@
 #include "../../include/tp_block.h"
 #include "tp_kernels.h"
 
+namespace tpk {
+thread_local LaunchTiming g_timing;
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -217,6 +221,12 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
 bool use_gemm(const Dims& x, int T, int K) {
   return x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K);
 }
+
+// Kernel-execution timing of one projection (see tpk::LaunchTiming); cleared on every exit path.
+struct TimedScope {
+  TimedScope(hipEvent_t b, hipEvent_t e) { tpk::g_timing = {b, e}; }
+  ~TimedScope() { tpk::g_timing = {}; }
+};
 
 hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, hipStream_t st,
@@ -456,13 +466,14 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   hipError_t e;
   if (attn) {
     void* qkv = ws + w.qkv;
-    if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
     if (use_gemm(x, T, x.d)) {
       // Multi-token MFMA path: projection, then rotary embedding + KV append.
-      e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
-                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, nullptr, skw);
+      {
+        TimedScope ts(evb, eve);
+        e = project(x, tpk::EPI_ACT, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
+                    x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, nullptr, skw);
+      }
       if (e != hipSuccess) return hip_fail(e, "qkv projection");
-      if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
       e = tpk::launch_rope_append(at, qkv, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
                                   batch->mode, batch->block_table, batch->max_pages, x.ps,
                                   kv->n_pages, w.pos_limit, kv->k_pages, kv->v_pages,
@@ -485,10 +496,12 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
       re.hq = x.hq;
       re.hk = x.hk;
       re.hd = x.hd;
-      e = project(x, tpk::EPI_ROPE, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
-                  x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, &re);
+      {
+        TimedScope ts(evb, eve);
+        e = project(x, tpk::EPI_ROPE, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
+                    x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, &re);
+      }
       if (e != hipSuccess) return hip_fail(e, "qkv projection");
-      if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
     }
     e = tpk::launch_attn_decode(at, x.hd, x.Hq / x.Hkv, T, x.hk, ws + w.q, kv->k_pages,
                                 kv->v_pages, batch->positions, batch->mode, batch->block_table,
@@ -500,11 +513,12 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
                 ws + w.attn, partial_out, x.d, st, nullptr, skw);
     if (e != hipSuccess) return hip_fail(e, "o projection");
   } else {
-    if (evb && (e = hipEventRecord(evb, st)) != hipSuccess) return hip_fail(e, "event record");
-    e = project(x, tpk::EPI_GATED, T, sh + L.gate_up.offset, sh + L.gate_up_scale.offset, x.d,
-                x.fr, x.fr, xn, ws + w.ffn, x.fr, st, nullptr, skw);
+    {
+      TimedScope ts(evb, eve);
+      e = project(x, tpk::EPI_GATED, T, sh + L.gate_up.offset, sh + L.gate_up_scale.offset, x.d,
+                  x.fr, x.fr, xn, ws + w.ffn, x.fr, st, nullptr, skw);
+    }
     if (e != hipSuccess) return hip_fail(e, "gate/up projection");
-    if (eve && (e = hipEventRecord(eve, st)) != hipSuccess) return hip_fail(e, "event record");
     e = project(x, epi_part, T, sh + L.down.offset, sh + L.down_scale.offset, x.fr, x.d, 0,
                 ws + w.ffn, partial_out, x.d, st, nullptr, skw);
     if (e != hipSuccess) return hip_fail(e, "down projection");

@@ -1,6 +1,7 @@
 // Host-side launchers of the libtpblock kernels. Each enqueues on `st` and returns the launch
 // status; shapes are validated by the caller (tp_api.hip) before any of these run.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,6 +10,27 @@ namespace tpk {
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
 enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3, EPI_ROPE = 4 };
+
+// Optional timing of one projection by kernel execution (not by stream events): while `stop` is
+// set, every launch below goes through hipExtLaunchKernelGGL, the first one also recording
+// `start` when it begins and each one recording `stop` when it ends, so the pair spans exactly the
+// projection's kernels. Per calling thread; the API sets it around the timed projection only.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming g_timing;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, const dim3& grid, const dim3& block, uint32_t lds, hipStream_t st,
+                   Args... args) {
+  if (g_timing.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, g_timing.start, g_timing.stop, 0u,
+                          args...);
+    g_timing.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 // Arguments of the fused QKV epilogue (rotary embedding + paged KV append), passed by value.
 struct RopeEpi {
