@@ -21,17 +21,20 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_*_f32) for this target.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # Keep MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register
-                # allocator copies them around every MFMA of a software-pipelined k-loop.
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Keep MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register allocator copies
+# them around every MFMA of a software-pipelined k-loop. Not for the wide-tile GEMM, whose 256
+# accumulators per lane only fit in AGPRs (its loop compiles without copies).
+VGPR_ACC = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_ACC_SOURCES = {"k_gemm_wide.hip"}
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    acc = [] if os.path.basename(src) in AGPR_ACC_SOURCES else VGPR_ACC
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *acc, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -13,13 +13,10 @@
 //
 // Epilogues as in the GEMV: activation-dtype store (QKV), fp32 / bf16 partial store (row-parallel
 // o_proj and down), and the fused gate/up pair: B2 holds the up rows, act(g) * u is stored.
-#include "tp_common.h"
+#include "k_gemm_common.h"
 #include "tp_kernels.h"
 
 namespace tpk {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 constexpr int GB_M = 64, GB_N = 64, GB_K = 64;
 constexpr int G_LDS_LD = GB_K + 8;  // bf16 elements per LDS row
@@ -158,14 +155,8 @@ __global__ __launch_bounds__(256) void k_gemm_big(const uint16_t* __restrict__ A
   uint16_t* sA = smem;                          // [2][BM * BG_LD]
   uint16_t* sB = smem + 2 * BM * BG_LD;         // [2][BG_N * BG_LD]
 
-  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous run of tiles.
-  // The first 8 * floor(n / 8) blocks are remapped (a bijection on that range); the rest keep
-  // their index.
-  const int nblk = gridDim.x;
-  const int b = blockIdx.x;
-  const int full = nblk / 8 * 8;
-  const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
-  const int tm = lt / tiles_n, tn = lt % tiles_n;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM;
   // Columns of B this block stages: plain: n0 .. n0+127; dual: 64 output columns n0 .. n0+63 of
   // both the gate (B) and up (B2) matrices.
@@ -501,16 +492,8 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
 // the MFMA operand reads (16 rows, one chunk each) hit distinct banks. Tiles and epilogues as in
 // k_gemm_big. Needs K % 64 == 0; rows and columns past M and N load clamped (valid) addresses and
 // their results are never stored.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int LG_BK = 64, LG_ST = 3;
-
-template <int N_OUT>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt with vmcnt = N_OUT (6-bit, split field), expcnt and lgkmcnt left at "no wait".
-  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | (7 << 4) | (15 << 8) | ((N_OUT >> 4) << 14));
-}
 
 template <int EPI, int ACTF, int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 1 : 2))) void k_gemm_lds(const uint16_t* __restrict__ A,
@@ -526,10 +509,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 25
   constexpr int STAGE = (BM + 128) * LG_BK;  // bf16 elements per stage
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int full = nblk / 8 * 8;
-  const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
-  const int tm = lt / tiles_n, tn = lt % tiles_n;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   // The last tile in M (and in N) is shifted back to end at the matrix edge, so every load is in
   // bounds without per-row clamps; rows and columns before ms0 / ns0 belong to the previous tile
   // and are not stored twice. The launcher guarantees M >= BM and N >= the tile width.
@@ -878,6 +859,9 @@ hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* 
   if (M >= 256) {
     // Enough row bands for 256-row tiles to fill the chip, else 128-row tiles.
     const long t256 = (long)((M + 255) / 256) * ((epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128);
+    // Wide tiles when they alone nearly fill the chip (LDS traffic per MFMA is lowest there).
+    if (K % LG_BK == 0 && gemm_wide_tiles(epi, M, N) >= 192)
+      return launch_gemm_wide(epi, actf, M, N, K, A, B, B2, C, ldc, st);
     // The direct-to-LDS kernel needs whole K-tiles and at least one full tile in N.
     if (K % LG_BK == 0 && N >= ((epi == EPI_GATED) ? 64 : 128)) {
       if (t256 >= 256) return lds_bm<256>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);

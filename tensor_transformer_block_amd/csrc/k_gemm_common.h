@@ -1,0 +1,18 @@
+// Types and helpers shared by the MFMA GEMM kernels (k_gemm.hip, k_gemm_wide.hip).
+#pragma once
+#include "tp_common.h"
+
+namespace tpk {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int N_OUT>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N_OUT (6-bit, split field), expcnt and lgkmcnt left at "no wait".
+  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | (7 << 4) | (15 << 8) | ((N_OUT >> 4) << 14));
+}
+
+}  // namespace tpk

@@ -1,0 +1,220 @@
+// Prefill GEMM, wide tile: 256 x 256 per workgroup, 128 x 128 per wave, for projections with
+// enough rows and columns to fill the chip with such tiles (the 70B shard's gate/up, o_proj and
+// down). Same operand layout and epilogues as the 256 x 128 kernel in k_gemm.hip; what changes is
+// the LDS traffic per MFMA, the limit measured for that kernel on this chip: a 128 x 128 wave tile
+// reads 16 fragments per 64 MFMAs (0.25 per MFMA instead of 0.375), and a 256 x 256 tile takes
+// 128 bytes of direct-to-LDS writes per MFMA instead of 192.
+//
+// Two 64 KB LDS slots, each a 64-deep K-tile of A (256 rows) and B (256 rows; gated: 128 gate rows
+// then 128 up rows), filled by global_load_lds_dwordx4 with 16-byte chunks XOR-swizzled by
+// row % 8. Each K-tile is two 32-deep k-steps: the second step's fragments are read while the
+// first step's MFMAs issue, the barrier that publishes the next K-tile sits between the steps, and
+// the next tile's first fragments are read while the second step's MFMAs issue. The 256 fp32
+// accumulators per lane live in AGPRs (this file is built without the VGPR-accumulator option:
+// the fragment double buffer needs the VGPRs).
+#include <type_traits>
+
+#include "k_gemm_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+
+constexpr int WD_BK = 64;                 // k per LDS slot
+constexpr int WD_STAGE = 512 * WD_BK;     // bf16 elements per slot (256 A rows + 256 B rows)
+
+template <int EPI, int ACTF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_wide(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
+    int tiles_m, int tiles_n) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int TM = 8, TN = 8;            // 16 x 16 blocks per wave
+  constexpr int LOADS = 256 / 8 / 4;       // 1 KB wave-loads per wave per slot, for A and for B
+  constexpr int NW = DUAL ? 128 : 256;     // output columns per tile
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  // Edge tiles shift back inside the matrix (the launcher guarantees M >= 256 and N >= NW); what
+  // the previous tile already covers is not stored again.
+  const int ms0 = tm * 256, ns0 = tn * NW;
+  const int m0 = min(ms0, M - 256), n0 = min(ns0, N - NW);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Wave-load i covers 8 rows; the lane's swizzled chunk (lane % 8) ^ (row % 8) is the same for
+  // every load, so addresses are a wave-uniform base plus one 32-bit lane offset.
+  const int lrow = lane >> 3, lpc = lane & 7;
+  const uint32_t lane_off = (uint32_t)((lrow * K + ((lpc ^ lrow) << 3)) * 2);
+  const char* a_base = (const char*)(A + (size_t)(m0 + wave * LOADS * 8) * K);
+  const size_t grp = (size_t)8 * K * 2;
+  auto issue = [&](int slot, int kt) {
+    uint16_t* st = smem + slot * WD_STAGE;
+    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp + off),
+                                       (lds_void_t*)(st + (wave * LOADS + i) * 8 * WD_BK), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int g = wave * LOADS + i;  // 8-row group of the 256 staged B rows
+      const char* src;
+      if constexpr (DUAL)
+        src = (const char*)((g < 16 ? B : B2) + (size_t)(n0 + (g & 15) * 8) * K);
+      else
+        src = (const char*)(B + (size_t)(n0 + g * 8) * K);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
+                                       (lds_void_t*)(st + 256 * WD_BK + g * 8 * WD_BK), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Staged B row of block j: gated tiles keep gate rows in 0..127 and the matching up rows 128
+  // further on, so block j and block j + 4 of a wave are the same output columns.
+  auto brow = [&](int j) -> int {
+    if constexpr (DUAL) return (j < 4 ? 0 : 128) + wn * 64 + (j & 3) * 16;
+    else return wn * 128 + j * 16;
+  };
+  const int fr = lane & 15, fq = lane >> 4;
+  struct Frag {
+    bf16x8 a[TM], b[TN];
+  };
+  auto load = [&](Frag& f, int slot, int kk) {
+    const uint16_t* a_s = smem + slot * WD_STAGE;
+    const uint16_t* b_s = a_s + 256 * WD_BK;
+    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // Scheduling hints for one region: its global loads first, four MFMAs (the wait before them
+  // only covers reads issued a whole region earlier), then one fragment read per two MFMAs.
+  auto hints = [&](auto nvmem) {
+    if constexpr (decltype(nvmem)::value > 0)
+      __builtin_amdgcn_sched_group_barrier(0x010, decltype(nvmem)::value, 0);  // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                          // MFMA
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 4 - 2 * (TM + TN), 0);
+  };
+
+  const int nk = K / WD_BK;
+  Frag x, y;
+  issue(0, 0);
+  wait_vmcnt<0>();
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  issue(1, min(1, nk - 1));
+  load(x, 0, 0);
+  int kt = 0;
+  // Steady state, branch-free so the hints see whole regions. The tile issued two ahead is
+  // clamped to the last one (in bounds; its slot is never read again).
+  for (; kt + 1 < nk; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(y, kt & 1, 1);
+    mma(x);
+    hints(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // Tile kt + 1 has landed for this wave; after the barrier for every wave, and every wave is
+    // done reading slot kt & 1 (its reads completed before the barrier), which then refills.
+    wait_vmcnt<0>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt & 1, min(kt + 2, nk - 1));
+    load(x, (kt + 1) & 1, 0);
+    mma(y);
+    hints(std::integral_constant<int, 2 * LOADS>{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load(y, kt & 1, 1);
+  mma(x);
+  mma(y);
+  // The clamped loads may still be in flight; they must land before the LDS is released.
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 128 + i * 16 + fq * 4 + r;
+      if (row < ms0) continue;  // stored by the previous tile
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn * 64 + j * 16 + fr;
+          if (col >= ns0)
+            ((uint16_t*)C)[(size_t)row * ldc + col] =
+                f32_to_bf16(gated<ACTF>(acc[i][j][r], acc[i][j + 4][r]));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * 128 + j * 16 + fr;
+          if (col < ns0) continue;
+          const size_t o = (size_t)row * ldc + col;
+          if constexpr (EPI == EPI_F32) ((float*)C)[o] = acc[i][j][r];
+          else ((uint16_t*)C)[o] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+long gemm_wide_tiles(int epi, int M, int N) {
+  const int nw = (epi == EPI_GATED) ? 128 : 256;
+  if (M < 256 || N < nw) return 0;
+  return (long)((M + 255) / 256) * ((N + nw - 1) / nw);
+}
+
+hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
+                            const void* B2, void* C, int ldc, hipStream_t st) {
+  const int nw = (epi == EPI_GATED) ? 128 : 256;
+  if (M < 256 || N < nw || K % WD_BK != 0) return hipErrorInvalidValue;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + nw - 1) / nw;
+  dim3 g(tiles_m * tiles_n), blk(256);
+  const size_t lds = (size_t)2 * WD_STAGE * sizeof(uint16_t);
+  const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
+#define TPK_WIDE(E, AF)                                                                         \
+  do {                                                                                          \
+    static bool attr_set = false;                                                               \
+    if (!attr_set) {                                                                            \
+      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF>,                      \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (ea != hipSuccess) return ea;                                                          \
+      attr_set = true;                                                                          \
+    }                                                                                           \
+    launch((k_gemm_wide<E, AF>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m, tiles_n); \
+  } while (0)
+  switch (epi) {
+    case EPI_ACT: TPK_WIDE(EPI_ACT, 0); break;
+    case EPI_F32: TPK_WIDE(EPI_F32, 0); break;
+    case EPI_BF16: TPK_WIDE(EPI_BF16, 0); break;
+    case EPI_GATED:
+      if (actf == 0) TPK_WIDE(EPI_GATED, 0);
+      else TPK_WIDE(EPI_GATED, 1);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef TPK_WIDE
+  return hipGetLastError();
+}
+
+}  // namespace tpk

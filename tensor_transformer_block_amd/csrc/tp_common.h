@@ -145,4 +145,19 @@ __device__ __forceinline__ float gated(float g, float u) {
   else return act_gelu_tanh(g) * u;
 }
 
+// Workgroup -> output tile for the GEMMs. Workgroups are dealt round-robin to the 8 XCDs, so
+// the first 8 * floor(n / 8) of them are renumbered to make each XCD's share a contiguous run of
+// tile indices; a run then walks GM m-bands down before stepping across n, so the tiles one XCD
+// holds at a time form a GM x k block and both operands are reused in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int b, int nblk, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  constexpr int GM = 4;
+  const int full = nblk / 8 * 8;
+  const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
+  const int g = lt / (GM * tiles_n), r = lt % (GM * tiles_n);
+  const int gm = min(GM, tiles_m - g * GM);
+  tm = g * GM + r % gm;
+  tn = r / gm;
+}
+
 }  // namespace tpk

@@ -35,6 +35,14 @@ SHAPES = [
               n_tokens=300),
     MED.with_(name="med-bf16-prefill-from-empty", index=205, mode="prefill", kv_lens=(70,),
               n_tokens=70, tp=4, n_heads=8, n_kv_heads=4, ffn_dim=1408),
+    # Prefill shapes large enough for the 256 x 256 GEMM tiles, with ragged edges: gated
+    # gate/up with 600 rows and 8224 columns; o_proj and down with 2000 rows and 6200 columns.
+    MED.with_(name="med-bf16-prefill-wide-gated", index=214, mode="prefill", kv_lens=(650,),
+              n_tokens=600, ffn_dim=16448),
+    BlockShape(name="med-bf16-prefill-wide-rows", index=215, d_model=6200, n_heads=8,
+               n_kv_heads=2, head_dim=128, ffn_dim=2176, tp=2, w_dtype="bf16",
+               act_dtype="bf16", ffn_act="silu", mode="prefill", kv_lens=(2000,),
+               n_tokens=2000),
     BlockShape(name="med-fp32-g2", index=206, d_model=384, n_heads=4, n_kv_heads=2, head_dim=128,
                ffn_dim=688, tp=2, w_dtype="f32", act_dtype="f32", ffn_act="silu", mode="decode",
                kv_lens=(50, 3), n_tokens=2),
