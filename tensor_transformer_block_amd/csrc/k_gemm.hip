@@ -404,6 +404,121 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(const uint16_t* __restrict_
     }
 }
 
+// The same split-K GEMM with both operands fed through a six-slot LDS ring by direct-to-LDS
+// loads (used when K % 64 == 0). The weight tile of a stage is read as 8 rows x 128 bytes per
+// wave instruction (the register-fed form above reads 16 rows x 64 bytes, which the HBM serves at
+// well under half the rate of longer row segments), and five stages stay in flight per
+// workgroup, so a few hundred workgroups keep enough bytes outstanding to stream the weights at
+// HBM rate. Stage layout: the activation rows (AR = 16 MT) then the weight rows (64, gated: 64
+// gate then 64 up), 64 bf16 each, 16-byte chunks XOR-swizzled by row % 8.
+constexpr int SD_BK = 64, SD_ST = 6;
+
+template <int MT, bool DUAL>
+__global__ __launch_bounds__(256) void k_gemm_splitk_dma(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ B,
+                                                         const uint16_t* __restrict__ B2, int M,
+                                                         int N, int K, int kchunk,
+                                                         float* __restrict__ part) {
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int AR = MT * 16;                       // activation rows staged
+  constexpr int BR = 64 * NB;                       // weight rows staged
+  constexpr int STAGE = (AR + BR) * SD_BK;          // bf16 elements per slot
+  constexpr int A_WL = AR / 8;                      // 1 KB wave-loads of A per stage
+  constexpr int A_PW = (A_WL + 3) / 4;              // per wave (surplus loads repeat one)
+  constexpr int B_PW = BR / 8 / 4;                  // per wave
+  constexpr int LPW = A_PW + B_PW;                  // loads per wave per stage
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 64, sidx = blockIdx.y;
+  const int k0 = sidx * kchunk, k1 = min(K, k0 + kchunk);
+  const int nst = (k1 - k0) / SD_BK;  // K % 64 == 0 and kchunk % 64 == 0: whole stages
+
+  // Lane l of a wave-load covers row l / 8 of an 8-row group and stores its 16 bytes at chunk
+  // l % 8 of that row in LDS, so it loads global chunk (l % 8) ^ (row % 8). Rows past M or N load
+  // a clamped (valid) row and are never stored.
+  const int lrow = lane >> 3, lpc = lane & 7;
+  const int lchunk = (lpc ^ lrow) << 4;
+  auto issue = [&](int slot, int stg) {
+    uint16_t* st = smem + slot * STAGE;
+    const uint32_t kb = (uint32_t)(k0 + min(stg, nst - 1) * SD_BK) * 2;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int g = (wave * A_PW + i) % A_WL;  // a repeated group writes identical bytes
+      const int row = min(g * 8 + lrow, M - 1);
+      const char* src = (const char*)(A + (size_t)row * K) + kb + lchunk;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(st + g * 8 * SD_BK), 16,
+                                       0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const int g = wave * B_PW + i;  // 8-row group of the staged weight rows
+      const uint16_t* base;
+      int col;
+      if constexpr (DUAL) {
+        base = (g < 8) ? B : B2;
+        col = n0 + (g & 7) * 8 + lrow;
+      } else {
+        base = B;
+        col = n0 + g * 8 + lrow;
+      }
+      const char* src = (const char*)(base + (size_t)min(col, N - 1) * K) + kb + lchunk;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)src,
+                                       (lds_void_t*)(st + (AR + g * 8) * SD_BK), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[NB][MT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[b][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fq = lane >> 4;
+
+#pragma unroll
+  for (int s = 0; s < SD_ST - 1; ++s) issue(s, s);
+  for (int stg = 0; stg < nst; ++stg) {
+    // Stage stg has landed for this wave once only the SD_ST - 2 newer stages remain in flight;
+    // after the barrier for every wave, and every wave is done reading slot (stg - 1) % SD_ST.
+    wait_vmcnt<(SD_ST - 2) * LPW>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue((stg + SD_ST - 1) % SD_ST, stg + SD_ST - 1);
+    const uint16_t* a_s = smem + (stg % SD_ST) * STAGE;
+    const uint16_t* b_s = a_s + AR * SD_BK;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
+      bf16x8 bf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        bf[b] = *(const bf16x8*)(b_s + (b * 64 + wave * 16 + fr) * SD_BK + sw);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const bf16x8 af = *(const bf16x8*)(a_s + (i * 16 + fr) * SD_BK + sw);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[b], acc[b][i], 0, 0, 0);
+      }
+    }
+  }
+  // The clamped loads past the last stage may still be in flight.
+  wait_vmcnt<0>();
+  const int col = n0 + wave * 16 + fr;
+  if (col >= N) return;
+  const int ncols = DUAL ? 2 * N : N;
+  float* pbase = part + (size_t)sidx * M * ncols;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = i * 16 + fq * 4 + r;
+      if (row >= M) continue;
+      pbase[(size_t)row * ncols + col] = acc[0][i][r];
+      if constexpr (DUAL) pbase[(size_t)row * ncols + N + col] = acc[NB - 1][i][r];
+    }
+}
+
 template <int EPI, int ACTF>
 __global__ void k_splitk_epilogue(const float* __restrict__ part, int S, int M, int N,
                                   void* __restrict__ C, int ldc) {
@@ -426,11 +541,12 @@ __global__ void k_splitk_epilogue(const float* __restrict__ part, int S, int M, 
   }
 }
 
-// Split count for the split-K variant: enough workgroups to cover the chip, K ranges a multiple
-// of the 128-wide stage and at least 256 long.
+// Split count for the split-K variants: enough workgroups to cover the chip, K ranges a multiple
+// of the 128-wide stage and at least 256 long. The direct-to-LDS form (K % 64 == 0) holds one
+// workgroup per CU (its ring takes most of the LDS), so it stays within one round of 256.
 void splitk_plan(int N, int K, bool dual, int* S, int* kchunk) {
   const int tiles = (N + 63) / 64;
-  int s = (256 + tiles - 1) / tiles;
+  int s = (K % SD_BK == 0) ? 256 / tiles : (256 + tiles - 1) / tiles;
   const int smax = (K + 255) / 256;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -458,16 +574,42 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
   dim3 g((N + 63) / 64, S), blk(256);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   const int mt = (M + 15) / 16;
+  if (K % SD_BK == 0) {
+    // Direct-to-LDS form; the dynamic LDS of a six-slot ring exceeds the default 64 KB.
+#define TPK_SD(MTV, DV)                                                                          \
+  do {                                                                                           \
+    constexpr size_t lds = (size_t)SD_ST * (MTV * 16 + 64 * (DV ? 2 : 1)) * SD_BK * 2;          \
+    static bool attr_set = false;                                                                \
+    if (!attr_set) {                                                                             \
+      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_splitk_dma<MTV, DV>,               \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (ea != hipSuccess) return ea;                                                           \
+      attr_set = true;                                                                           \
+    }                                                                                            \
+    launch((k_gemm_splitk_dma<MTV, DV>), g, blk, lds, st, a, b, b2, M, N, K, kc, part);         \
+  } while (0)
+#define TPK_SDM(MTV) \
+  if (dual) TPK_SD(MTV, true); else TPK_SD(MTV, false)
+    switch (mt) {
+      case 1: TPK_SDM(1); break;
+      case 2: TPK_SDM(2); break;
+      case 3: TPK_SDM(3); break;
+      default: TPK_SDM(4); break;
+    }
+#undef TPK_SDM
+#undef TPK_SD
+  } else {
 #define TPK_SK(MTV)                                                                              \
   if (dual) launch((k_gemm_splitk<MTV, true>), g, blk, 0, st, a, b, b2, M, N, K, kc, part); \
   else launch((k_gemm_splitk<MTV, false>), g, blk, 0, st, a, b, b2, M, N, K, kc, part)
-  switch (mt) {
-    case 1: TPK_SK(1); break;
-    case 2: TPK_SK(2); break;
-    case 3: TPK_SK(3); break;
-    default: TPK_SK(4); break;
-  }
+    switch (mt) {
+      case 1: TPK_SK(1); break;
+      case 2: TPK_SK(2); break;
+      case 3: TPK_SK(3); break;
+      default: TPK_SK(4); break;
+    }
 #undef TPK_SK
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)M * N;

@@ -195,6 +195,7 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
     o = off;
     off = align_up(off + bytes);
   };
+  const bool splitk = x.wt == TP_DTYPE_BF16 && T > 0 && T <= 64;
   put(w.qkv, T * x.qkv_rows * x.ab);
   put(w.q, T * x.qdim * x.ab);
   put(w.attn, T * x.qdim * x.ab);
@@ -203,7 +204,7 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   put(w.ffn, T * x.fr * x.ab);
   // fp32 split-K partial tiles of the batched-decode projections (bf16 weights, 4 < T <= 64).
   uint64_t gemm = 0;
-  if (x.wt == TP_DTYPE_BF16 && T > 0 && T <= 64) {
+  if (splitk) {
     const uint64_t cand[4] = {
         tpk::splitk_workspace_bytes((int)T, x.qkv_rows, x.d, false),
         tpk::splitk_workspace_bytes((int)T, x.d, x.qdim, false),

@@ -66,6 +66,8 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
                        const RopeEpi* rope, hipStream_t st);
 
 // k_gemm.hip
+// Split-K projection of M <= 64 tokens; `part` holds the fp32 split tiles
+// (splitk_workspace_bytes), summed in split order by a small epilogue kernel.
 size_t splitk_workspace_bytes(int M, int N, int K, bool dual);
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
                               const void* B, const void* B2, void* C, int ldc, float* part,
