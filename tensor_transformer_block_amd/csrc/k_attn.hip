@@ -657,6 +657,9 @@ hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* 
   } else {
     if (chunk % 32) return hipErrorInvalidValue;
     const bool prefill = (mode == 1);
+    if (prefill && attn_prefill_supported(hd, G, ps))
+      return launch_attn_prefill(hd, G, T, hk, q, kp, vp, positions, bt, max_pages, n_pages,
+                                 pos_limit, out, st);
 #define TPK_HDM(HDV)                                                                          \
   e = attn_mfma_g<HDV>(prefill, G, T, hk, st, q, kp, vp, positions, mode, bt, max_pages, ps, \
                        n_pages, chunk, n_split, pos_limit, part_o, part_ml, out, sl2)

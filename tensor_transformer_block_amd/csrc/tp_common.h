@@ -19,12 +19,9 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even (the gfx950 conversion instruction); NaN stays a NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {

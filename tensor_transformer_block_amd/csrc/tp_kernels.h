@@ -86,6 +86,12 @@ hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, in
                               const int* positions, int mode, const int* block_table,
                               int max_pages, int ps, int n_pages, int pos_limit, void* kp,
                               void* vp, const float* rope, hipStream_t st);
+// k_attn_prefill.hip: bf16 causal prefill of one sequence, KV tiles shared by a GQA group.
+bool attn_prefill_supported(int hd, int G, int ps);
+hipError_t launch_attn_prefill(int hd, int G, int T, int hk, const void* q, const void* kp,
+                               const void* vp, const int* positions, const int* bt,
+                               int max_pages, int n_pages, int pos_limit, void* out,
+                               hipStream_t st);
 hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* q, const void* kp,
                               const void* vp, const int* positions, int mode, const int* bt,
                               int max_pages, int ps, int n_pages, int chunk, int n_split,
