@@ -43,6 +43,17 @@ SHAPES = [
                n_kv_heads=2, head_dim=128, ffn_dim=2176, tp=2, w_dtype="bf16",
                act_dtype="bf16", ffn_act="silu", mode="prefill", kv_lens=(2000,),
                n_tokens=2000),
+    # Prefill attention over the other GQA group sizes and head dims: one query head per KV
+    # head (hd 64 and 128) and eight (hd 64), with a cached prefix and ragged token counts.
+    BlockShape(name="med-bf16-prefill-g1-hd64", index=216, d_model=256, n_heads=4, n_kv_heads=4,
+               head_dim=64, ffn_dim=512, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="silu", mode="prefill", kv_lens=(211,), n_tokens=170),
+    BlockShape(name="med-bf16-prefill-g1-hd128", index=217, d_model=256, n_heads=4,
+               n_kv_heads=4, head_dim=128, ffn_dim=512, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="silu", mode="prefill", kv_lens=(300,), n_tokens=300),
+    BlockShape(name="med-bf16-prefill-g8-hd64", index=218, d_model=256, n_heads=16,
+               n_kv_heads=2, head_dim=64, ffn_dim=512, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="gelu_tanh", mode="prefill", kv_lens=(530,), n_tokens=389),
     BlockShape(name="med-fp32-g2", index=206, d_model=384, n_heads=4, n_kv_heads=2, head_dim=128,
                ffn_dim=688, tp=2, w_dtype="f32", act_dtype="f32", ffn_act="silu", mode="decode",
                kv_lens=(50, 3), n_tokens=2),
