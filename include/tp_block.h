@@ -114,7 +114,10 @@ typedef struct {
 /* Rank r's paged KV cache, holding only the KV heads rank r owns [TS-HOW], activation dtype:
  * k_pages [n_pages][Hkv/N][page_size][hd] (after the rotary embedding) and v_pages stored
  * transposed, [n_pages][Hkv/N][hd][page_size], so that 8 consecutive keys of one hd column are
- * contiguous (the B operand layout of the P.V matrix-core step). */
+ * contiguous (the B operand layout of the P.V matrix-core step). Slots no key has been written to
+ * yet (past a sequence's last position in its last page) are never attended, but the matrix-core
+ * steps multiply them by zero weights, so they must hold finite values: allocate the pools
+ * zero-filled. */
 typedef struct {
   void* k_pages;
   void* v_pages;

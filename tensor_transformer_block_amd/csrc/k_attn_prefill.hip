@@ -5,21 +5,23 @@
 // A workgroup takes four 16-row blocks of one KV head (16 tokens of four query heads, or more
 // tokens of fewer heads when the group is smaller) and splits their keys over four key groups of
 // two waves: super-tile j (128 keys, eight 16-token pages) gives group kg the 32 keys 128 j + 32 kg,
-// so the long causal rows are spread over all eight waves (two per SIMD, one hiding the other's
-// softmax) and the groups' partial softmax states are merged through LDS at the end. Each wave
-// computes two of the row blocks against its keys with the same K and V fragments, which halves
-// the LDS reads per MFMA. The super-tiles come into a double-buffered LDS ring by direct-to-LDS
-// loads (K rows with their 16-byte chunks XOR-swizzled by key, V as stored: transposed per page),
-// so the K/V bytes leave L2 once per workgroup. Scores and output are computed transposed,
-// S^T = K Q^T and O^T += V^T P^T (16x16x32 MFMA): each lane then owns one query row of each of
-// its two row blocks, a row's online softmax (exp2 domain, causal mask on edge tiles only) needs
-// two cross-lane steps, and P goes from the score registers straight into the next MFMA.
+// so the long causal rows are spread over all eight waves (two per SIMD) and the groups' partial
+// softmax states are merged through LDS at the end. Each wave computes two of the row blocks
+// against its keys with the same K and V fragments, which halves the LDS reads per MFMA.
+//
+// Scores and output are computed transposed, S^T = K Q^T and O^T += V^T P^T (16x16x32 MFMA):
+// each lane then owns one query row of each of its two row blocks, a row's online softmax needs
+// two cross-lane steps, and P goes from the score registers straight into the next MFMA. The
+// MFMA rows of K are permuted so that a lane's eight scores are eight consecutive keys, which
+// makes its V^T operand one 16-byte LDS read of the page as stored. The scores of the group's
+// next sub-tile are computed while the softmax of the current one runs (the matrix cores and
+// the vector ALUs work side by side), so K and V live one super-tile apart in two rings: K of
+// super-tiles j + 1 and j + 2, V of j and j + 1, each loaded by direct-to-LDS transfers with its
+// 16-byte chunks XOR-swizzled against LDS bank conflicts.
 #include "k_gemm_common.h"
 #include "tp_kernels.h"
 
 namespace tpk {
-
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 constexpr int AP_SUB = 32;  // keys per key group per step (two 16-token pages)
 constexpr int AP_KG = 4;    // key groups per workgroup (two waves each)
@@ -44,6 +46,14 @@ __device__ __forceinline__ float ap_rowsum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// K row swizzle: the 16-byte chunk c of sub-tile key `key` sits at chunk c ^ ap_kswz(key). The
+// eight keys one 16-lane K fragment read takes per bank window (keys 8 a + 4 kb + b, b < 4, two
+// consecutive a) then hit eight different chunk positions.
+template <int CH>
+__device__ __forceinline__ int ap_kswz(int key) {
+  return ((key & 3) | ((key >> 1) & 12)) & (CH - 1);
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__(512) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpages,
@@ -56,10 +66,10 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   constexpr int TB = 4 / NHW;               // 16-token blocks per workgroup
   constexpr int CH = HD / 8;                // 16-byte chunks per key row of K
   constexpr int SUBE = AP_SUB * HD;         // bf16 elements of a group's K (or V) sub-tile
-  constexpr int SLOT = AP_KG * 2 * SUBE;    // bf16 elements of one super-tile (K and V)
   constexpr int KPL = 1024 / (HD * 2);      // keys per K wave-load (1 KB)
   constexpr int PWL = HD * 32 / 1024;       // wave-loads per 16-key page of K (and of V)
   constexpr int NPG = NO / AP_KG;           // hd blocks of O each key group writes out
+  constexpr float TAU = 8.f;                // lazy running max: scores reach at most 2^TAU
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   __shared__ float2 s_ml[AP_KG][2][2][64];  // merge: (m, l) per key group, wave, row block, lane
   __shared__ int s_kmax;
@@ -81,9 +91,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   const int nsup = (s_kmax + 4 * AP_SUB - 1) / (4 * AP_SUB);
 
   // The wave's row blocks rb = 2 wp + h (h = 0, 1): token block rb / NHW, head rb % NHW of the
-  // workgroup's heads. Lane l works on row (token) l % 16 of both throughout: S and O are kept
-  // transposed (keys or hd along the MFMA rows), so the softmax of a row lives in the four lanes
-  // l % 16 + 16 i and P feeds the P V product straight from registers.
+  // workgroup's heads. Lane l works on row (token) l % 16 of both throughout.
   int tk[2], head[2], lim[2];
   bf16x8 qf[2][KS];  // Q^T operands: lane row fr, hd chunk fq of each 32-wide step
   int wmin = 0x7fffffff, wmax = 0;
@@ -108,32 +116,64 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
     wmax = max(wmax, __shfl_xor(wmax, off, 64));
   }
 
-  // Super-tile j in LDS slot j % 2: group kg's K sub-tile [32 keys][HD] at (2 kg) SUBE, its V
-  // sub-tile [2 pages][HD][16] at (2 kg + 1) SUBE. Wave wp of group kg loads page 2 kg + wp of
-  // the super-tile (K rows 16 wp .. 16 wp + 15 and V page wp of the group's sub-tile). The page
-  // ids of the next super-tile are read a step ahead into a register (lane i: page 8 j + i % 8).
-  auto page_ids = [&](int j) {
-    return block_table[min(8 * j + (lane & 7), max_pages - 1)];
-  };
-  auto issue = [&](int slot, int ptab) {
+  // LDS: K ring [2][AP_KG][32 keys][HD] (swizzled rows), V ring [2][AP_KG][2 pages][HD][16].
+  // Wave wp of group kg loads page 2 kg + wp of a super-tile: K keys 16 wp .. 16 wp + 15 and V
+  // page wp of the group's sub-tile. Page ids are read ahead into a register (lane i: page
+  // 8 j + i % 8 of super-tile j) and picked out with a lane read.
+  uint16_t* const kring = smem;
+  uint16_t* const vring = smem + 2 * AP_KG * SUBE;
+  auto page_ids = [&](int j) { return block_table[min(8 * j + (lane & 7), max_pages - 1)]; };
+  auto page_of = [&](int ptab) {
     const int pid = ap_clamp(__builtin_amdgcn_readlane(ptab, 2 * kg + wp), 0, n_pages - 1);
-    uint16_t* ks_ = smem + slot * SLOT + 2 * kg * SUBE + 16 * wp * HD;
-    uint16_t* vs_ = smem + slot * SLOT + (2 * kg + 1) * SUBE + wp * HD * 16;
-    const uint16_t* kpg = kpages + ((size_t)pid * hk + g) * 16 * HD;
-    const uint16_t* vpg = vpages + ((size_t)pid * hk + g) * HD * 16;
+    return (size_t)pid * hk + g;
+  };
+  auto issue_k = [&](int slot, int ptab) {
+    const uint16_t* kpg = kpages + page_of(ptab) * 16 * HD;
+    uint16_t* dst = kring + (slot * AP_KG + kg) * SUBE + 16 * wp * HD;
 #pragma unroll
     for (int i = 0; i < PWL; ++i) {
-      // K: keys KPL i .. of the page; lane -> key KPL i + l / CH, LDS chunk l % CH holding
-      // global chunk (l % CH) ^ (key % CH).
-      const int key = KPL * i + lane / CH, pos = lane % CH;
+      const int key = KPL * i + lane / CH, pos = lane % CH;  // key of the page; LDS chunk pos
       __builtin_amdgcn_global_load_lds(
-          (glb_void_t*)(kpg + key * HD + ((pos ^ ((16 * wp + key) & (CH - 1))) << 3)),
-          (lds_void_t*)(ks_ + i * 512), 16, 0, 0);
-      // V: 32 hd rows of the page per wave-load, as stored ([hd][16 keys]).
-      __builtin_amdgcn_global_load_lds(
-          (glb_void_t*)(vpg + (i * 32 + lane / 2) * 16 + (lane & 1) * 8),
-          (lds_void_t*)(vs_ + i * 512), 16, 0, 0);
+          (glb_void_t*)(kpg + key * HD + ((pos ^ ap_kswz<CH>(16 * wp + key)) << 3)),
+          (lds_void_t*)(dst + i * 512), 16, 0, 0);
     }
+  };
+  auto issue_v = [&](int slot, int ptab) {
+    const uint16_t* vpg = vpages + page_of(ptab) * HD * 16;
+    uint16_t* dst = vring + (slot * AP_KG + kg) * SUBE + wp * HD * 16;
+#pragma unroll
+    for (int i = 0; i < PWL; ++i) {
+      // 32 hd rows as stored ([hd][16 keys]); the two 16-byte halves of a row swap places on
+      // rows with bit 2 set.
+      const int row = i * 32 + lane / 2, half = (lane & 1) ^ ((row >> 2) & 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(vpg + row * 16 + half * 8),
+                                       (lds_void_t*)(dst + i * 512), 16, 0, 0);
+    }
+  };
+  // S^T = K Q^T of the sub-tile in K slot `slot`, per 16-key block kb and row block h. MFMA row
+  // 4 a + b of block kb takes key 8 a + 4 kb + b, so lane (fr, fq) ends up holding
+  // S[row fr][key 8 fq + 4 kb + r].
+  auto scores = [&](int slot, floatx4 (&sc)[2][2]) {
+    const uint16_t* ks_ = kring + (slot * AP_KG + kg) * SUBE;
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = 8 * (fr >> 2) + 4 * kb + (fr & 3);
+#pragma unroll
+      for (int kc = 0; kc < KS; ++kc)
+        kf[kb][kc] = *(const bf16x8*)(ks_ + key * HD + (((kc * 4 + fq) ^ ap_kswz<CH>(key)) << 3));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[h][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KS; ++kc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sc[h][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][kc], qf[h][kc], sc[h][kb], 0, 0, 0);
   };
 
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
@@ -142,92 +182,26 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int n = 0; n < NO; ++n) o[h][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  int ptab = 0;
-  if (nsup > 0) {
-    issue(0, page_ids(0));
-    ptab = page_ids(1);
-  }
-  for (int j = 0; j < nsup; ++j) {
-    // Super-tile j has landed for every wave, and every wave is done with super-tile j - 1,
-    // whose slot then takes super-tile j + 1.
-    wait_vmcnt<0>();
-    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (j + 1 < nsup) {
-      issue((j + 1) & 1, ptab);
-      ptab = page_ids(j + 2);
-    }
-    const int kb0 = (4 * j + kg) * AP_SUB;  // first key of this group's sub-tile
-    if (kb0 >= wmax) continue;
-    const uint16_t* ks_ = smem + (j & 1) * SLOT + 2 * kg * SUBE;
-    const uint16_t* vs_ = ks_ + SUBE;
-
-    // S^T = K Q^T per 16-key block kb and row block h: lane holds S[row fr][key 16 kb + 4 fq + r].
-    bf16x8 kf[2][KS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = 16 * kb + fr;
-#pragma unroll
-      for (int kc = 0; kc < KS; ++kc)
-        kf[kb][kc] = *(const bf16x8*)(ks_ + key * HD + (((kc * 4 + fq) ^ (key & (CH - 1))) << 3));
-    }
-    floatx4 s[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[h][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < KS; ++kc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[h][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][kc], qf[h][kc], s[h][kb], 0, 0, 0);
-    // V^T fragments, read now so the softmax below hides their latency: lane supplies V^T[hd
-    // 16 n + fr] at keys 4 fq + r and 16 + 4 fq + r (slots 4 fq .. 4 fq + 3 of the two pages),
-    // the key order of P^T below.
-    bf16x8 vf[NO];
-#pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      // Read as bf16 vectors: typed this way the compiler does not order these reads behind
-      // the tile loads still in flight (the explicit wait and barrier above already do).
-      const bf16x4 lo = *(const bf16x4*)(vs_ + (16 * n + fr) * 16 + 4 * fq);
-      const bf16x4 hi = *(const bf16x4*)(vs_ + (HD + 16 * n + fr) * 16 + 4 * fq);
-      vf[n] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    // Causal mask (edge sub-tiles only: a wave-uniform branch), online softmax in the exp2
-    // domain with the hardware exp2 (its flush of results below 2^-126 to zero is immaterial
-    // here). A row whose keys so far are all masked keeps m = -inf and contributes nothing.
-    const bool edge = kb0 + AP_SUB > wmin;
-    bf16x8 pf[2];
+  float mref[2];
+  bf16x8 pf[2];
+  // Online softmax of one sub-tile's scores in the exp2 domain, in two phases so that the rare
+  // O rescale (a branch) sits between them and the exponentials share one basic block with the
+  // MFMAs. The running max only moves when a tile's max exceeds it by more than TAU; a row whose
+  // keys so far are all masked keeps m = -inf and contributes nothing.
+  auto new_max = [&](floatx4 (&sc)[2][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (edge) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb0 + 16 * kb + 4 * fq + r >= lim[h]) s[h][kb][r] = -INFINITY;
-      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[h][kb][r]);
-      const float mn = fmaxf(m[h], ap_rowmax(mx) * scale_log2);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - mref);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[h][kb][r]);
+      mx = ap_rowmax(mx) * scale_log2;
+      const float mn = mx > m[h] + TAU ? mx : m[h];
+      mref[h] = mn == -INFINITY ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mref[h]);
       m[h] = mn;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][kb][r], scale_log2, -mref));
-          ps += p;
-          pf[h][4 * kb + r] = (__bf16)p;
-        }
-      lsum[h] = lsum[h] * alpha + ps;
+      lsum[h] *= alpha;
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int n = 0; n < NO; ++n)
@@ -235,23 +209,109 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
           for (int r = 0; r < 4; ++r) o[h][n][r] *= alpha;
       }
     }
-    // O^T += V^T P^T.
+  };
+  // P = exp2(s scale - m) with the hardware exp2 (its flush of results below 2^-126 to zero is
+  // immaterial here), packed to bf16 as the B operand of the P V step.
+  auto exps = [&](floatx4 (&sc)[2][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][kb][r], scale_log2, -mref[h]));
+          ps += p;
+          pf[h][4 * kb + r] = (__bf16)p;
+        }
+      lsum[h] += ps;
+    }
+  };
+  // V^T of the sub-tile in V slot `slot` (lane: hd row 16 n + fr, keys 8 fq .. 8 fq + 7, one
+  // 16-byte read), then O^T += V^T P^T.
+  auto accumulate = [&](int slot) {
+    const uint16_t* vs_ = vring + (slot * AP_KG + kg) * SUBE + (fq >> 1) * HD * 16;
+    bf16x8 vf[NO];
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+      vf[n] = *(const bf16x8*)(vs_ + (16 * n + fr) * 16 + (((fq & 1) ^ ((fr >> 2) & 1)) << 3));
 #pragma unroll
     for (int n = 0; n < NO; ++n)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         o[h][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n], pf[h], o[h][n], 0, 0, 0);
+  };
+  // Causal mask of the scores of the sub-tile starting at key kb0 (edge sub-tiles only).
+  auto mask = [&](floatx4 (&sc)[2][2], int kb0) {
+    if (kb0 + AP_SUB > wmin) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb0 + 8 * fq + 4 * kb + r >= lim[h]) sc[h][kb][r] = -INFINITY;
+    }
+  };
+
+  floatx4 scur[2][2], snxt[2][2];
+  int pb = 0, pc = 0;  // page ids of super-tiles j + 1 and j + 2
+  if (nsup > 0) {
+    const int pa = page_ids(0);
+    issue_k(0, pa);
+    issue_v(0, pa);
+    pb = page_ids(1);
+    if (nsup > 1) issue_k(1, pb);
+    pc = page_ids(2);
+    wait_vmcnt<0>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    scores(0, scur);
+  }
+  for (int j = 0; j < nsup; ++j) {
+    // K of super-tile j + 1 and V of j have landed for every wave, and every wave is done with
+    // K of j and V of j - 1, whose slots then take K of j + 2 and V of j + 1.
+    wait_vmcnt<0>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 2 < nsup) issue_k(j & 1, pc);
+    if (j + 1 < nsup) issue_v((j + 1) & 1, pb);
+    pb = pc;
+    pc = page_ids(j + 3);
+    const int kb0 = (4 * j + kg) * AP_SUB;  // first key of this group's current sub-tile
+    if (kb0 >= wmax) continue;
+    mask(scur, kb0);
+    new_max(scur);
+    if (j + 1 < nsup && kb0 + 4 * AP_SUB < wmax) {
+      // Scores of the next sub-tile on the matrix cores while the exponentials run on the VALUs.
+      scores((j + 1) & 1, snxt);
+      exps(scur);
+      accumulate(j & 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) scur[h][kb] = snxt[h][kb];
+      // Scheduling hints: the K reads, then each score MFMA followed by a few VALU operations
+      // of the exponentials, then the V reads and the P V MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, NO, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NO, 0);
+    } else {
+      exps(scur);
+      accumulate(j & 1);
+    }
   }
 
   // Merge the four key groups' states (m, l, O) of each row: every group publishes its state,
   // then group kg combines hd blocks NPG kg .. NPG kg + NPG - 1 of all four and writes them out.
-  // The tile ring is free once every wave has passed the barrier (nothing is in flight).
+  // The rings are free once every wave has passed the barrier (nothing is in flight).
   wait_vmcnt<0>();
   float* mo = (float*)smem;  // [kg][wp][h][n][lane][4]
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    lsum[h] = ap_rowsum(lsum[h]);
-  }
+  for (int h = 0; h < 2; ++h) lsum[h] = ap_rowsum(lsum[h]);
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
