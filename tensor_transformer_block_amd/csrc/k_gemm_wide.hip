@@ -5,9 +5,11 @@
 // reads 16 fragments per 64 MFMAs (0.25 per MFMA instead of 0.375), and a 256 x 256 tile takes
 // 128 bytes of direct-to-LDS writes per MFMA instead of 192.
 //
-// Two 64 KB LDS slots, each a 64-deep K-tile of A (256 rows) and B (256 rows; gated: 128 gate rows
-// then 128 up rows), filled by global_load_lds_dwordx4 with 16-byte chunks XOR-swizzled by
-// row % 8. Each K-tile is two 32-deep k-steps: the second step's fragments are read while the
+// Two LDS slots, each a 64-deep K-tile of A (256 rows) and B (256 rows; gated: 224 rows, 8 gate
+// rows then the 8 matching up rows, 14 times), filled by global_load_lds_dwordx4 with 16-byte
+// chunks XOR-swizzled by row % 8. A gated tile has 112 output columns, so that the 70B shard's
+// 3584 FFN columns make 32 tile columns and 256 tiles, one per CU; each 16-column MFMA block holds
+// 8 gate and the 8 matching up columns, which meet in one lane through a DPP row rotation. Each K-tile is two 32-deep k-steps: the second step's fragments are read while the
 // first step's MFMAs issue, the barrier that publishes the next K-tile sits between the steps, and
 // the next tile's first fragments are read while the second step's MFMAs issue. The 256 fp32
 // accumulators per lane live in AGPRs (this file is built without the VGPR-accumulator option:
@@ -20,7 +22,10 @@
 namespace tpk {
 
 constexpr int WD_BK = 64;                 // k per LDS slot
-constexpr int WD_STAGE = 512 * WD_BK;     // bf16 elements per slot (256 A rows + 256 B rows)
+
+// Staged B rows and output columns per tile.
+constexpr int wd_brows(int epi) { return epi == EPI_GATED ? 224 : 256; }
+constexpr int wd_ncols(int epi) { return epi == EPI_GATED ? 112 : 256; }
 
 template <int EPI, int ACTF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_wide(
@@ -28,9 +33,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
     int tiles_m, int tiles_n) {
   constexpr bool DUAL = (EPI == EPI_GATED);
-  constexpr int TM = 8, TN = 8;            // 16 x 16 blocks per wave
-  constexpr int LOADS = 256 / 8 / 4;       // 1 KB wave-loads per wave per slot, for A and for B
-  constexpr int NW = DUAL ? 128 : 256;     // output columns per tile
+  constexpr int NBR = wd_brows(EPI);       // staged B rows
+  constexpr int NW = wd_ncols(EPI);        // output columns per tile
+  constexpr int STAGE = (256 + NBR) * WD_BK;  // bf16 elements per slot
+  constexpr int TM = 8, TN = NBR / 32;     // 16 x 16 blocks per wave (2 x 2 waves)
+  constexpr int LOADS = 256 / 8 / 4;       // 1 KB wave-loads of A per wave per slot
+  constexpr int LOADS_B = NBR / 8 / 4;     // and of B
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   int tm, tn;
@@ -49,25 +57,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t lane_off = (uint32_t)((lrow * K + ((lpc ^ lrow) << 3)) * 2);
   const char* a_base = (const char*)(A + (size_t)(m0 + wave * LOADS * 8) * K);
   const size_t grp = (size_t)8 * K * 2;
-  auto issue = [&](int slot, int kt) {
-    uint16_t* st = smem + slot * WD_STAGE;
+  auto issue_a = [&](int slot, int kt) {
+    uint16_t* st = smem + slot * STAGE;
     const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp + off),
                                        (lds_void_t*)(st + (wave * LOADS + i) * 8 * WD_BK), 16, 0,
                                        0);
+  };
+  auto issue_b = [&](int slot, int kt) {
+    uint16_t* st = smem + slot * STAGE;
+    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int g = wave * LOADS + i;  // 8-row group of the 256 staged B rows
+    for (int i = 0; i < LOADS_B; ++i) {
+      const int g = wave * LOADS_B + i;  // 8-row group of the staged B rows
       const char* src;
       if constexpr (DUAL)
-        src = (const char*)((g < 16 ? B : B2) + (size_t)(n0 + (g & 15) * 8) * K);
+        src = (const char*)(((g & 1) ? B2 : B) + (size_t)(n0 + (g >> 1) * 8) * K);
       else
         src = (const char*)(B + (size_t)(n0 + g * 8) * K);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
                                        (lds_void_t*)(st + 256 * WD_BK + g * 8 * WD_BK), 16, 0, 0);
     }
+  };
+  auto issue = [&](int slot, int kt) {
+    issue_a(slot, kt);
+    issue_b(slot, kt);
   };
 
   floatx4 acc[TM][TN];
@@ -75,18 +91,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // Staged B row of block j: gated tiles keep gate rows in 0..127 and the matching up rows 128
-  // further on, so block j and block j + 4 of a wave are the same output columns.
-  auto brow = [&](int j) -> int {
-    if constexpr (DUAL) return (j < 4 ? 0 : 128) + wn * 64 + (j & 3) * 16;
-    else return wn * 128 + j * 16;
-  };
+  // Staged B row of block j (gated: output columns 8 of them, gate in lanes fr < 8, up above).
+  auto brow = [&](int j) -> int { return wn * (NBR / 2) + j * 16; };
   const int fr = lane & 15, fq = lane >> 4;
   struct Frag {
     bf16x8 a[TM], b[TN];
   };
+  auto load_b = [&](Frag& f, int slot, int kk) {
+    const uint16_t* b_s = smem + slot * STAGE + 256 * WD_BK;
+    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
+  };
+  auto load_a = [&](Frag& f, int slot, int kk) {
+    const uint16_t* a_s = smem + slot * STAGE;
+    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
+  };
   auto load = [&](Frag& f, int slot, int kk) {
-    const uint16_t* a_s = smem + slot * WD_STAGE;
+    const uint16_t* a_s = smem + slot * STAGE;
     const uint16_t* b_s = a_s + 256 * WD_BK;
     const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
 #pragma unroll
@@ -94,6 +119,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
+  };
+  auto mma_rows = [&](const Frag& f, auto i0) {
+#pragma unroll
+    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -115,8 +147,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 4 - 2 * (TM + TN), 0);
   };
+  // Half-region variant: rows [I0, I0 + TM / 2) of the MFMAs, NR fragment reads, NV loads.
+  auto hints_half = [&](auto nvmem, auto nreads) {
+    constexpr int NV = decltype(nvmem)::value, NR = decltype(nreads)::value;
+    constexpr int NM = TM * TN / 2;
+    if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x010, NV, 0);   // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 - 2 * NR, 0);
+  };
 
   const int nk = K / WD_BK;
+  constexpr int NVM = LOADS + LOADS_B;
   Frag x, y;
   issue(0, 0);
   wait_vmcnt<0>();
@@ -137,10 +183,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vmcnt<0>();
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(kt & 1, min(kt + 2, nk - 1));
-    load(x, (kt + 1) & 1, 0);
-    mma(y);
-    hints(std::integral_constant<int, 2 * LOADS>{});
+    // The refill is spread over the region in two halves (one burst of all of them right after
+    // the barrier, from every wave at once, holds up the fragment reads).
+    issue_a(kt & 1, min(kt + 2, nk - 1));
+    load_b(x, (kt + 1) & 1, 0);
+    mma_rows(y, std::integral_constant<int, 0>{});
+    hints_half(std::integral_constant<int, LOADS>{}, std::integral_constant<int, TN>{});
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt & 1, min(kt + 2, nk - 1));
+    load_a(x, (kt + 1) & 1, 0);
+    mma_rows(y, std::integral_constant<int, TM / 2>{});
+    hints_half(std::integral_constant<int, LOADS_B>{}, std::integral_constant<int, TM>{});
   }
   __builtin_amdgcn_sched_barrier(0);
   load(y, kt & 1, 1);
@@ -157,11 +210,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (row < ms0) continue;  // stored by the previous tile
       if constexpr (DUAL) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + fr;
-          if (col >= ns0)
-            ((uint16_t*)C)[(size_t)row * ldc + col] =
-                f32_to_bf16(gated<ACTF>(acc[i][j][r], acc[i][j + 4][r]));
+        for (int j = 0; j < TN; ++j) {
+          // Lanes fr and fr ^ 8 swap values (rotation by 8 within each row of 16 lanes).
+          const float v = acc[i][j][r];
+          const float w = __int_as_float(
+              __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+          const int col = n0 + wn * (NW / 2) + j * 8 + fr;
+          if (fr < 8 && col >= ns0)
+            ((uint16_t*)C)[(size_t)row * ldc + col] = f32_to_bf16(gated<ACTF>(v, w));
         }
       } else {
 #pragma unroll
@@ -178,18 +234,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 long gemm_wide_tiles(int epi, int M, int N) {
-  const int nw = (epi == EPI_GATED) ? 128 : 256;
+  const int nw = wd_ncols(epi);
   if (M < 256 || N < nw) return 0;
   return (long)((M + 255) / 256) * ((N + nw - 1) / nw);
 }
 
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st) {
-  const int nw = (epi == EPI_GATED) ? 128 : 256;
+  const int nw = wd_ncols(epi);
   if (M < 256 || N < nw || K % WD_BK != 0) return hipErrorInvalidValue;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + nw - 1) / nw;
   dim3 g(tiles_m * tiles_n), blk(256);
-  const size_t lds = (size_t)2 * WD_STAGE * sizeof(uint16_t);
+  const size_t lds = (size_t)2 * (256 + wd_brows(epi)) * WD_BK * sizeof(uint16_t);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
 #define TPK_WIDE(E, AF)                                                                         \
   do {                                                                                          \
