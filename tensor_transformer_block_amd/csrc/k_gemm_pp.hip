@@ -1,0 +1,234 @@
+// Prefill GEMM, wide tile with two waves per SIMD: the 256 x 256 (gated: 256 x 112) tile of
+// k_gemm_wide.hip split over eight waves of 64 x 128 (gated 64 x 112) instead of four of
+// 128 x 128. Each SIMD then holds two waves of the same tile, so while one waits (at the barrier
+// that publishes a K-tile, on a burst of direct-to-LDS loads, on a fragment read) the other keeps
+// the matrix core busy. The price is more LDS fragment reads per MFMA (4 + 8 fragments per 32
+// MFMAs instead of 8 + 8 per 64), which the LDS bandwidth still covers.
+//
+// Same LDS layout as k_gemm_wide.hip: two slots, each a 64-deep K-tile of A (256 rows) and B
+// (256 rows; gated: 224 rows, 8 gate rows then the 8 matching up rows, 14 times), 16-byte chunks
+// XOR-swizzled by row % 8, filled by global_load_lds_dwordx4. Each K-tile is two 32-deep k-steps
+// whose fragment reads are double-buffered in registers; the barrier sits between the steps.
+// Accumulators live in VGPRs (112 or 128 per lane).
+#include <type_traits>
+
+#include "k_gemm_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+
+constexpr int PP_BK = 64;  // k per LDS slot
+
+constexpr int pp_brows(int epi) { return epi == EPI_GATED ? 224 : 256; }
+constexpr int pp_ncols(int epi) { return epi == EPI_GATED ? 112 : 256; }
+
+template <int EPI, int ACTF>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_pp(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
+    int tiles_m, int tiles_n) {
+  constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int NBR = pp_brows(EPI);          // staged B rows
+  constexpr int NW = pp_ncols(EPI);           // output columns per tile
+  constexpr int STAGE = (256 + NBR) * PP_BK;  // bf16 elements per slot
+  constexpr int TM = 4, TN = NBR / 32;        // 16 x 16 blocks per wave (4 x 2 waves)
+  constexpr int LA = 4;                       // 1 KB wave-loads of A per wave per slot
+  constexpr int NGB = NBR / 8;                // 8-row groups of B per slot
+  constexpr int LB = (NGB + 7) / 8;           // B wave-loads per wave
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  // Edge tiles shift back inside the matrix (the launcher guarantees M >= 256 and N >= NW); what
+  // the previous tile already covers is not stored again.
+  const int ms0 = tm * 256, ns0 = tn * NW;
+  const int m0 = min(ms0, M - 256), n0 = min(ns0, N - NW);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < 8);
+  // Waves w and w + 4 share a SIMD: same 64-row band, the two column halves.
+  const int wm = wave & 3, wn = wave >> 2;
+
+  // Wave-load i covers 8 rows; the lane's swizzled chunk (lane % 8) ^ (row % 8) is the same for
+  // every load, so addresses are a wave-uniform base plus one 32-bit lane offset.
+  const int lrow = lane >> 3, lpc = lane & 7;
+  const uint32_t lane_off = (uint32_t)((lrow * K + ((lpc ^ lrow) << 3)) * 2);
+  const char* a_base = (const char*)(A + (size_t)(m0 + wave * LA * 8) * K);
+  const size_t grp = (size_t)8 * K * 2;
+  auto issue_a = [&](int slot, int kt) {
+    uint16_t* st = smem + slot * STAGE;
+    const uint32_t off = lane_off + (uint32_t)kt * (PP_BK * 2);
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp + off),
+                                       (lds_void_t*)(st + (wave * LA + i) * 8 * PP_BK), 16, 0, 0);
+  };
+  auto issue_b = [&](int slot, int kt) {
+    uint16_t* st = smem + slot * STAGE + 256 * PP_BK;
+    const uint32_t off = lane_off + (uint32_t)kt * (PP_BK * 2);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      // 8-row group of the staged B rows (wave-uniform). Where NGB is not a multiple of 8 the
+      // spare waves repeat the last group: the same bytes to the same LDS place, branch-free.
+      const int g = min(wave + 8 * i, NGB - 1);
+      const char* src;
+      if constexpr (DUAL)
+        src = (const char*)(((g & 1) ? B2 : B) + (size_t)(n0 + (g >> 1) * 8) * K);
+      else
+        src = (const char*)(B + (size_t)(n0 + g * 8) * K);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
+                                       (lds_void_t*)(st + g * 8 * PP_BK), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Staged B row of block j (gated: 8 output columns, gate in lanes fr < 8, up above).
+  auto brow = [&](int j) -> int { return wn * (NBR / 2) + j * 16; };
+  const int fr = lane & 15, fq = lane >> 4;
+  struct Frag {
+    bf16x8 a[TM], b[TN];
+  };
+  auto load = [&](Frag& f, int slot, int kk) {
+    const uint16_t* a_s = smem + slot * STAGE;
+    const uint16_t* b_s = a_s + 256 * PP_BK;
+    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * PP_BK + sw);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      f.a[i] = *(const bf16x8*)(a_s + (wm * 64 + i * 16 + fr) * PP_BK + sw);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // Scheduling hints for one region: its global loads first, two MFMAs, then one fragment read
+  // per two MFMAs.
+  auto hints = [&](auto nvmem) {
+    if constexpr (decltype(nvmem)::value > 0)
+      __builtin_amdgcn_sched_group_barrier(0x010, decltype(nvmem)::value, 0);  // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 - 2 * (TM + TN), 0);
+  };
+
+  const int nk = K / PP_BK;
+  constexpr int NVM = LA + LB;
+  Frag x, y;
+  issue_a(0, 0);
+  issue_b(0, 0);
+  wait_vmcnt<0>();
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  issue_a(1, min(1, nk - 1));
+  issue_b(1, min(1, nk - 1));
+  load(x, 0, 0);
+  int kt = 0;
+  // Steady state, branch-free so the hints see whole regions. The tile issued two ahead is
+  // clamped to the last one (in bounds; its slot is never read again).
+  for (; kt + 1 < nk; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(y, kt & 1, 1);
+    mma(x);
+    hints(std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // Tile kt + 1 has landed for this wave; after the barrier for every wave, and every wave is
+    // done reading slot kt & 1 (its reads completed before the barrier), which then refills.
+    wait_vmcnt<0>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(kt & 1, min(kt + 2, nk - 1));
+    issue_b(kt & 1, min(kt + 2, nk - 1));
+    load(x, (kt + 1) & 1, 0);
+    mma(y);
+    hints(std::integral_constant<int, NVM>{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load(y, kt & 1, 1);
+  mma(x);
+  mma(y);
+  // The clamped loads may still be in flight; they must land before the LDS is released.
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 64 + i * 16 + fq * 4 + r;
+      if (row < ms0) continue;  // stored by the previous tile
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          // Lanes fr and fr ^ 8 swap values (rotation by 8 within each row of 16 lanes).
+          const float v = acc[i][j][r];
+          const float w = __int_as_float(
+              __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+          const int col = n0 + wn * (NW / 2) + j * 8 + fr;
+          if (fr < 8 && col >= ns0)
+            ((uint16_t*)C)[(size_t)row * ldc + col] = f32_to_bf16(gated<ACTF>(v, w));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * 128 + j * 16 + fr;
+          if (col < ns0) continue;
+          const size_t o = (size_t)row * ldc + col;
+          if constexpr (EPI == EPI_F32) ((float*)C)[o] = acc[i][j][r];
+          else ((uint16_t*)C)[o] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+long gemm_pp_tiles(int epi, int M, int N) {
+  const int nw = pp_ncols(epi);
+  if (M < 256 || N < nw) return 0;
+  return (long)((M + 255) / 256) * ((N + nw - 1) / nw);
+}
+
+hipError_t launch_gemm_pp(int epi, int actf, int M, int N, int K, const void* A, const void* B,
+                          const void* B2, void* C, int ldc, hipStream_t st) {
+  const int nw = pp_ncols(epi);
+  if (M < 256 || N < nw || K % PP_BK != 0) return hipErrorInvalidValue;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + nw - 1) / nw;
+  dim3 g(tiles_m * tiles_n), blk(512);
+  const size_t lds = (size_t)2 * (256 + pp_brows(epi)) * PP_BK * sizeof(uint16_t);
+  const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
+#define TPK_PP(E, AF)                                                                           \
+  do {                                                                                          \
+    static bool attr_set = false;                                                               \
+    if (!attr_set) {                                                                            \
+      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_pp<E, AF>,                        \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (ea != hipSuccess) return ea;                                                          \
+      attr_set = true;                                                                          \
+    }                                                                                           \
+    launch((k_gemm_pp<E, AF>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m, tiles_n);   \
+  } while (0)
+  switch (epi) {
+    case EPI_ACT: TPK_PP(EPI_ACT, 0); break;
+    case EPI_F32: TPK_PP(EPI_F32, 0); break;
+    case EPI_BF16: TPK_PP(EPI_BF16, 0); break;
+    case EPI_GATED:
+      if (actf == 0) TPK_PP(EPI_GATED, 0);
+      else TPK_PP(EPI_GATED, 1);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef TPK_PP
+  return hipGetLastError();
+}
+
+}  // namespace tpk

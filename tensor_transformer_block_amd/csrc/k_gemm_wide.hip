@@ -85,6 +85,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     issue_a(slot, kt);
     issue_b(slot, kt);
   };
+  // Loads [L0, L1) of the combined list (A loads, then B loads).
+  auto issue_range = [&](int slot, int kt, auto l0, auto l1) {
+    uint16_t* st = smem + slot * STAGE;
+    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
+#pragma unroll
+    for (int l = decltype(l0)::value; l < decltype(l1)::value; ++l) {
+      if (l < LOADS) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + l * grp + off),
+                                         (lds_void_t*)(st + (wave * LOADS + l) * 8 * WD_BK), 16,
+                                         0, 0);
+      } else {
+        const int g = wave * LOADS_B + (l - LOADS);
+        const char* src;
+        if constexpr (DUAL)
+          src = (const char*)(((g & 1) ? B2 : B) + (size_t)(n0 + (g >> 1) * 8) * K);
+        else
+          src = (const char*)(B + (size_t)(n0 + g * 8) * K);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
+                                         (lds_void_t*)(st + 256 * WD_BK + g * 8 * WD_BK), 16, 0,
+                                         0);
+      }
+    }
+  };
 
   floatx4 acc[TM][TN];
 #pragma unroll
@@ -97,17 +120,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   struct Frag {
     bf16x8 a[TM], b[TN];
   };
-  auto load_b = [&](Frag& f, int slot, int kk) {
+  auto load_b = [&](Frag& f, int slot, int kk, auto j0, auto j1) {
     const uint16_t* b_s = smem + slot * STAGE + 256 * WD_BK;
     const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
+    for (int j = decltype(j0)::value; j < decltype(j1)::value; ++j)
+      f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
   };
-  auto load_a = [&](Frag& f, int slot, int kk) {
+  auto load_a = [&](Frag& f, int slot, int kk, auto i0, auto i1) {
     const uint16_t* a_s = smem + slot * STAGE;
     const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i)
       f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
   };
   auto load = [&](Frag& f, int slot, int kk) {
@@ -122,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto mma_rows = [&](const Frag& f, auto i0) {
 #pragma unroll
-    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 2; ++i)
+    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 4; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
@@ -147,10 +171,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 4 - 2 * (TM + TN), 0);
   };
-  // Half-region variant: rows [I0, I0 + TM / 2) of the MFMAs, NR fragment reads, NV loads.
-  auto hints_half = [&](auto nvmem, auto nreads) {
+  // Quarter-region variant: TM / 4 rows of MFMAs, NR fragment reads, NV loads.
+  auto hints_q = [&](auto nvmem, auto nreads) {
     constexpr int NV = decltype(nvmem)::value, NR = decltype(nreads)::value;
-    constexpr int NM = TM * TN / 2;
+    constexpr int NM = TM * TN / 4;
     if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x010, NV, 0);   // VMEM
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
 #pragma unroll
@@ -183,17 +207,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vmcnt<0>();
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // The refill is spread over the region in two halves (one burst of all of them right after
+    // The refill is spread over the region in four parts (one burst of all of them right after
     // the barrier, from every wave at once, holds up the fragment reads).
-    issue_a(kt & 1, min(kt + 2, nk - 1));
-    load_b(x, (kt + 1) & 1, 0);
-    mma_rows(y, std::integral_constant<int, 0>{});
-    hints_half(std::integral_constant<int, LOADS>{}, std::integral_constant<int, TN>{});
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt & 1, min(kt + 2, nk - 1));
-    load_a(x, (kt + 1) & 1, 0);
-    mma_rows(y, std::integral_constant<int, TM / 2>{});
-    hints_half(std::integral_constant<int, LOADS_B>{}, std::integral_constant<int, TM>{});
+    {
+      using std::integral_constant;
+      constexpr int Q1 = NVM / 4, Q2 = NVM / 2, Q3 = 3 * NVM / 4;
+      const int kn = min(kt + 2, nk - 1), rs = (kt + 1) & 1;
+      issue_range(kt & 1, kn, integral_constant<int, 0>{}, integral_constant<int, Q1>{});
+      load_b(x, rs, 0, integral_constant<int, 0>{}, integral_constant<int, TN / 2>{});
+      mma_rows(y, integral_constant<int, 0>{});
+      hints_q(integral_constant<int, Q1>{}, integral_constant<int, TN / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_range(kt & 1, kn, integral_constant<int, Q1>{}, integral_constant<int, Q2>{});
+      load_b(x, rs, 0, integral_constant<int, TN / 2>{}, integral_constant<int, TN>{});
+      mma_rows(y, integral_constant<int, TM / 4>{});
+      hints_q(integral_constant<int, Q2 - Q1>{}, integral_constant<int, TN - TN / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_range(kt & 1, kn, integral_constant<int, Q2>{}, integral_constant<int, Q3>{});
+      load_a(x, rs, 0, integral_constant<int, 0>{}, integral_constant<int, TM / 2>{});
+      mma_rows(y, integral_constant<int, TM / 2>{});
+      hints_q(integral_constant<int, Q3 - Q2>{}, integral_constant<int, TM / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue_range(kt & 1, kn, integral_constant<int, Q3>{}, integral_constant<int, NVM>{});
+      load_a(x, rs, 0, integral_constant<int, TM / 2>{}, integral_constant<int, TM>{});
+      mma_rows(y, integral_constant<int, 3 * TM / 4>{});
+      hints_q(integral_constant<int, NVM - Q3>{}, integral_constant<int, TM / 2>{});
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   load(y, kt & 1, 1);
