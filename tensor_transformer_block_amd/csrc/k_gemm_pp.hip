@@ -102,6 +102,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < TM; ++i)
       f.a[i] = *(const bf16x8*)(a_s + (wm * 64 + i * 16 + fr) * PP_BK + sw);
   };
+  // MFMAs of block rows [I0, I0 + TM / 2).
+  auto mma_rows = [&](const Frag& f, auto i0) {
+#pragma unroll
+    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -124,7 +132,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   const int nk = K / PP_BK;
-  constexpr int NVM = LA + LB;
   Frag x, y;
   issue_a(0, 0);
   issue_b(0, 0);
@@ -147,11 +154,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wait_vmcnt<0>();
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    // The refill goes out in two halves, A with the first half of the MFMAs and the fragment
+    // reads, B with the second half (one burst of all loads from every wave at once right after
+    // the barrier holds up the fragment reads).
     issue_a(kt & 1, min(kt + 2, nk - 1));
-    issue_b(kt & 1, min(kt + 2, nk - 1));
     load(x, (kt + 1) & 1, 0);
-    mma(y);
-    hints(std::integral_constant<int, NVM>{});
+    mma_rows(y, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_group_barrier(0x010, LA, 0);                          // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                           // MFMA
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt & 1, min(kt + 2, nk - 1));
+    mma_rows(y, std::integral_constant<int, TM / 2>{});
+    __builtin_amdgcn_sched_group_barrier(0x010, LB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   load(y, kt & 1, 1);
