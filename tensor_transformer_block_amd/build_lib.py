@@ -23,10 +23,9 @@ ARCH = "gfx950"
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_*_f32) for this target.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Keep MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register allocator copies
-# them around every MFMA of a software-pipelined k-loop. Not for the wide-tile GEMM, whose 256
-# accumulators per lane only fit in AGPRs (its loop compiles without copies).
+# them around every MFMA of a software-pipelined k-loop.
 VGPR_ACC = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-AGPR_ACC_SOURCES = {"k_gemm_wide.hip"}
+AGPR_ACC_SOURCES: set = set()
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include")]
 

@@ -1002,8 +1002,8 @@ hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* 
     // Enough row bands for 256-row tiles to fill the chip, else 128-row tiles.
     const long t256 = (long)((M + 255) / 256) * ((epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128);
     // Wide tiles when they alone nearly fill the chip (LDS traffic per MFMA is lowest there).
-    if (K % LG_BK == 0 && gemm_pp_tiles(epi, M, N) >= 192)
-      return launch_gemm_pp(epi, actf, M, N, K, A, B, B2, C, ldc, st);
+    if (K % LG_BK == 0 && gemm_wide_tiles(epi, M, N) >= 192)
+      return launch_gemm_wide(epi, actf, M, N, K, A, B, B2, C, ldc, st);
     // The direct-to-LDS kernel needs whole K-tiles and at least one full tile in N.
     if (K % LG_BK == 0 && N >= ((epi == EPI_GATED) ? 64 : 128)) {
       if (t256 >= 256) return lds_bm<256>(epi, actf, M, N, K, a, bb, b2, C, ldc, st);

@@ -1,4 +1,4 @@
-// Types and helpers shared by the MFMA GEMM kernels (k_gemm.hip, k_gemm_wide.hip).
+// Types and helpers shared by the MFMA GEMM kernels (k_gemm.hip, k_gemm_wide.hip, k_attn_prefill.hip).
 #pragma once
 #include "tp_common.h"
 

@@ -1,19 +1,19 @@
-// Prefill GEMM, wide tile: 256 x 256 per workgroup, 128 x 128 per wave, for projections with
-// enough rows and columns to fill the chip with such tiles (the 70B shard's gate/up, o_proj and
-// down). Same operand layout and epilogues as the 256 x 128 kernel in k_gemm.hip; what changes is
-// the LDS traffic per MFMA, the limit measured for that kernel on this chip: a 128 x 128 wave tile
-// reads 16 fragments per 64 MFMAs (0.25 per MFMA instead of 0.375), and a 256 x 256 tile takes
-// 128 bytes of direct-to-LDS writes per MFMA instead of 192.
+// Prefill GEMM, wide tile: 256 x 256 per workgroup (gated: 256 rows x 112 output columns), for
+// projections with enough rows and columns to fill the chip with such tiles (the 70B shard's
+// gate/up, o_proj and down). Same operand layout and epilogues as the 256 x 128 kernel in
+// k_gemm.hip. Eight waves of 64 x 128 (gated 64 x 112), two per SIMD: while one waits (at the
+// barrier that publishes a K-tile, on a burst of direct-to-LDS loads, on a fragment read) the
+// other keeps the matrix core busy. A wave reads 4 + 8 fragments per 32 MFMAs; the big tile keeps
+// the direct-to-LDS writes at 128 bytes per MFMA.
 //
 // Two LDS slots, each a 64-deep K-tile of A (256 rows) and B (256 rows; gated: 224 rows, 8 gate
-// rows then the 8 matching up rows, 14 times), filled by global_load_lds_dwordx4 with 16-byte
-// chunks XOR-swizzled by row % 8. A gated tile has 112 output columns, so that the 70B shard's
-// 3584 FFN columns make 32 tile columns and 256 tiles, one per CU; each 16-column MFMA block holds
-// 8 gate and the 8 matching up columns, which meet in one lane through a DPP row rotation. Each K-tile is two 32-deep k-steps: the second step's fragments are read while the
-// first step's MFMAs issue, the barrier that publishes the next K-tile sits between the steps, and
-// the next tile's first fragments are read while the second step's MFMAs issue. The 256 fp32
-// accumulators per lane live in AGPRs (this file is built without the VGPR-accumulator option:
-// the fragment double buffer needs the VGPRs).
+// rows then the 8 matching up rows, 14 times), 16-byte chunks XOR-swizzled by row % 8, filled by
+// global_load_lds_dwordx4. A gated tile has 112 output columns, so that the 70B shard's 3584 FFN
+// columns make 32 tile columns and 256 tiles, one per CU; each 16-column MFMA block holds 8 gate
+// and the 8 matching up columns, which meet in one lane through a DPP row rotation. Each K-tile
+// is two 32-deep k-steps whose fragment reads are double-buffered in registers; the barrier that
+// publishes the next K-tile sits between the steps. Accumulators live in VGPRs (112 or 128 per
+// lane).
 #include <type_traits>
 
 #include "k_gemm_common.h"
@@ -21,24 +21,24 @@
 
 namespace tpk {
 
-constexpr int WD_BK = 64;                 // k per LDS slot
+constexpr int WD_BK = 64;  // k per LDS slot
 
-// Staged B rows and output columns per tile.
 constexpr int wd_brows(int epi) { return epi == EPI_GATED ? 224 : 256; }
 constexpr int wd_ncols(int epi) { return epi == EPI_GATED ? 112 : 256; }
 
 template <int EPI, int ACTF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_wide(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_wide(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
     int tiles_m, int tiles_n) {
   constexpr bool DUAL = (EPI == EPI_GATED);
-  constexpr int NBR = wd_brows(EPI);       // staged B rows
-  constexpr int NW = wd_ncols(EPI);        // output columns per tile
+  constexpr int NBR = wd_brows(EPI);          // staged B rows
+  constexpr int NW = wd_ncols(EPI);           // output columns per tile
   constexpr int STAGE = (256 + NBR) * WD_BK;  // bf16 elements per slot
-  constexpr int TM = 8, TN = NBR / 32;     // 16 x 16 blocks per wave (2 x 2 waves)
-  constexpr int LOADS = 256 / 8 / 4;       // 1 KB wave-loads of A per wave per slot
-  constexpr int LOADS_B = NBR / 8 / 4;     // and of B
+  constexpr int TM = 4, TN = NBR / 32;        // 16 x 16 blocks per wave (4 x 2 waves)
+  constexpr int LA = 4;                       // 1 KB wave-loads of A per wave per slot
+  constexpr int NGB = NBR / 8;                // 8-row groups of B per slot
+  constexpr int LB = (NGB + 7) / 8;           // B wave-loads per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   int tm, tn;
@@ -49,63 +49,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m0 = min(ms0, M - 256), n0 = min(ns0, N - NW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  __builtin_assume(wave >= 0 && wave < 8);
+  // Waves w and w + 4 share a SIMD: same 64-row band, the two column halves.
+  const int wm = wave & 3, wn = wave >> 2;
 
   // Wave-load i covers 8 rows; the lane's swizzled chunk (lane % 8) ^ (row % 8) is the same for
   // every load, so addresses are a wave-uniform base plus one 32-bit lane offset.
   const int lrow = lane >> 3, lpc = lane & 7;
   const uint32_t lane_off = (uint32_t)((lrow * K + ((lpc ^ lrow) << 3)) * 2);
-  const char* a_base = (const char*)(A + (size_t)(m0 + wave * LOADS * 8) * K);
+  const char* a_base = (const char*)(A + (size_t)(m0 + wave * LA * 8) * K);
   const size_t grp = (size_t)8 * K * 2;
   auto issue_a = [&](int slot, int kt) {
     uint16_t* st = smem + slot * STAGE;
     const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
+    for (int i = 0; i < LA; ++i)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp + off),
-                                       (lds_void_t*)(st + (wave * LOADS + i) * 8 * WD_BK), 16, 0,
-                                       0);
+                                       (lds_void_t*)(st + (wave * LA + i) * 8 * WD_BK), 16, 0, 0);
   };
   auto issue_b = [&](int slot, int kt) {
-    uint16_t* st = smem + slot * STAGE;
+    uint16_t* st = smem + slot * STAGE + 256 * WD_BK;
     const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
 #pragma unroll
-    for (int i = 0; i < LOADS_B; ++i) {
-      const int g = wave * LOADS_B + i;  // 8-row group of the staged B rows
+    for (int i = 0; i < LB; ++i) {
+      // 8-row group of the staged B rows (wave-uniform). Where NGB is not a multiple of 8 the
+      // spare waves repeat the last group: the same bytes to the same LDS place, branch-free.
+      const int g = min(wave + 8 * i, NGB - 1);
       const char* src;
       if constexpr (DUAL)
         src = (const char*)(((g & 1) ? B2 : B) + (size_t)(n0 + (g >> 1) * 8) * K);
       else
         src = (const char*)(B + (size_t)(n0 + g * 8) * K);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
-                                       (lds_void_t*)(st + 256 * WD_BK + g * 8 * WD_BK), 16, 0, 0);
-    }
-  };
-  auto issue = [&](int slot, int kt) {
-    issue_a(slot, kt);
-    issue_b(slot, kt);
-  };
-  // Loads [L0, L1) of the combined list (A loads, then B loads).
-  auto issue_range = [&](int slot, int kt, auto l0, auto l1) {
-    uint16_t* st = smem + slot * STAGE;
-    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
-#pragma unroll
-    for (int l = decltype(l0)::value; l < decltype(l1)::value; ++l) {
-      if (l < LOADS) {
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + l * grp + off),
-                                         (lds_void_t*)(st + (wave * LOADS + l) * 8 * WD_BK), 16,
-                                         0, 0);
-      } else {
-        const int g = wave * LOADS_B + (l - LOADS);
-        const char* src;
-        if constexpr (DUAL)
-          src = (const char*)(((g & 1) ? B2 : B) + (size_t)(n0 + (g >> 1) * 8) * K);
-        else
-          src = (const char*)(B + (size_t)(n0 + g * 8) * K);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off),
-                                         (lds_void_t*)(st + 256 * WD_BK + g * 8 * WD_BK), 16, 0,
-                                         0);
-      }
+                                       (lds_void_t*)(st + g * 8 * WD_BK), 16, 0, 0);
     }
   };
 
@@ -114,25 +90,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // Staged B row of block j (gated: output columns 8 of them, gate in lanes fr < 8, up above).
+  // Staged B row of block j (gated: 8 output columns, gate in lanes fr < 8, up above).
   auto brow = [&](int j) -> int { return wn * (NBR / 2) + j * 16; };
   const int fr = lane & 15, fq = lane >> 4;
   struct Frag {
     bf16x8 a[TM], b[TN];
-  };
-  auto load_b = [&](Frag& f, int slot, int kk, auto j0, auto j1) {
-    const uint16_t* b_s = smem + slot * STAGE + 256 * WD_BK;
-    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
-#pragma unroll
-    for (int j = decltype(j0)::value; j < decltype(j1)::value; ++j)
-      f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
-  };
-  auto load_a = [&](Frag& f, int slot, int kk, auto i0, auto i1) {
-    const uint16_t* a_s = smem + slot * STAGE;
-    const int sw = 8 * ((kk * 4 + fq) ^ (fr & 7));
-#pragma unroll
-    for (int i = decltype(i0)::value; i < decltype(i1)::value; ++i)
-      f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
   };
   auto load = [&](Frag& f, int slot, int kk) {
     const uint16_t* a_s = smem + slot * STAGE;
@@ -142,11 +104,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int j = 0; j < TN; ++j) f.b[j] = *(const bf16x8*)(b_s + (brow(j) + fr) * WD_BK + sw);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      f.a[i] = *(const bf16x8*)(a_s + (wm * 128 + i * 16 + fr) * WD_BK + sw);
+      f.a[i] = *(const bf16x8*)(a_s + (wm * 64 + i * 16 + fr) * WD_BK + sw);
   };
+  // MFMAs of block rows [I0, I0 + TM / 2).
   auto mma_rows = [&](const Frag& f, auto i0) {
 #pragma unroll
-    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 4; ++i)
+    for (int i = decltype(i0)::value; i < decltype(i0)::value + TM / 2; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
@@ -158,40 +121,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
-  // Scheduling hints for one region: its global loads first, four MFMAs (the wait before them
-  // only covers reads issued a whole region earlier), then one fragment read per two MFMAs.
+  // Scheduling hints for one region: its global loads first, two MFMAs, then one fragment read
+  // per two MFMAs.
   auto hints = [&](auto nvmem) {
     if constexpr (decltype(nvmem)::value > 0)
       __builtin_amdgcn_sched_group_barrier(0x010, decltype(nvmem)::value, 0);  // VMEM
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                          // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
 #pragma unroll
     for (int g = 0; g < TM + TN; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 4 - 2 * (TM + TN), 0);
-  };
-  // Quarter-region variant: TM / 4 rows of MFMAs, NR fragment reads, NV loads.
-  auto hints_q = [&](auto nvmem, auto nreads) {
-    constexpr int NV = decltype(nvmem)::value, NR = decltype(nreads)::value;
-    constexpr int NM = TM * TN / 4;
-    if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x010, NV, 0);   // VMEM
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                          // MFMA
-#pragma unroll
-    for (int g = 0; g < NR; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 - 2 * NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 - 2 * (TM + TN), 0);
   };
 
   const int nk = K / WD_BK;
-  constexpr int NVM = LOADS + LOADS_B;
   Frag x, y;
-  issue(0, 0);
+  issue_a(0, 0);
+  issue_b(0, 0);
   wait_vmcnt<0>();
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  issue(1, min(1, nk - 1));
+  issue_a(1, min(1, nk - 1));
+  issue_b(1, min(1, nk - 1));
   load(x, 0, 0);
   int kt = 0;
   // Steady state, branch-free so the hints see whole regions. The tile issued two ahead is
@@ -207,32 +158,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vmcnt<0>();
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // The refill is spread over the region in four parts (one burst of all of them right after
-    // the barrier, from every wave at once, holds up the fragment reads).
-    {
-      using std::integral_constant;
-      constexpr int Q1 = NVM / 4, Q2 = NVM / 2, Q3 = 3 * NVM / 4;
-      const int kn = min(kt + 2, nk - 1), rs = (kt + 1) & 1;
-      issue_range(kt & 1, kn, integral_constant<int, 0>{}, integral_constant<int, Q1>{});
-      load_b(x, rs, 0, integral_constant<int, 0>{}, integral_constant<int, TN / 2>{});
-      mma_rows(y, integral_constant<int, 0>{});
-      hints_q(integral_constant<int, Q1>{}, integral_constant<int, TN / 2>{});
-      __builtin_amdgcn_sched_barrier(0);
-      issue_range(kt & 1, kn, integral_constant<int, Q1>{}, integral_constant<int, Q2>{});
-      load_b(x, rs, 0, integral_constant<int, TN / 2>{}, integral_constant<int, TN>{});
-      mma_rows(y, integral_constant<int, TM / 4>{});
-      hints_q(integral_constant<int, Q2 - Q1>{}, integral_constant<int, TN - TN / 2>{});
-      __builtin_amdgcn_sched_barrier(0);
-      issue_range(kt & 1, kn, integral_constant<int, Q2>{}, integral_constant<int, Q3>{});
-      load_a(x, rs, 0, integral_constant<int, 0>{}, integral_constant<int, TM / 2>{});
-      mma_rows(y, integral_constant<int, TM / 2>{});
-      hints_q(integral_constant<int, Q3 - Q2>{}, integral_constant<int, TM / 2>{});
-      __builtin_amdgcn_sched_barrier(0);
-      issue_range(kt & 1, kn, integral_constant<int, Q3>{}, integral_constant<int, NVM>{});
-      load_a(x, rs, 0, integral_constant<int, TM / 2>{}, integral_constant<int, TM>{});
-      mma_rows(y, integral_constant<int, 3 * TM / 4>{});
-      hints_q(integral_constant<int, NVM - Q3>{}, integral_constant<int, TM / 2>{});
+    // The refill goes out in two halves, A with the first half of the MFMAs and the fragment
+    // reads, B with the second half (one burst of all loads from every wave at once right after
+    // the barrier holds up the fragment reads).
+    issue_a(kt & 1, min(kt + 2, nk - 1));
+    load(x, (kt + 1) & 1, 0);
+    mma_rows(y, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_group_barrier(0x010, LA, 0);                          // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                           // MFMA
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt & 1, min(kt + 2, nk - 1));
+    mma_rows(y, std::integral_constant<int, TM / 2>{});
+    __builtin_amdgcn_sched_group_barrier(0x010, LB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   load(y, kt & 1, 1);
@@ -245,7 +188,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 128 + i * 16 + fq * 4 + r;
+      const int row = m0 + wm * 64 + i * 16 + fq * 4 + r;
       if (row < ms0) continue;  // stored by the previous tile
       if constexpr (DUAL) {
 #pragma unroll
@@ -279,23 +222,23 @@ long gemm_wide_tiles(int epi, int M, int N) {
 }
 
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                            const void* B2, void* C, int ldc, hipStream_t st) {
+                          const void* B2, void* C, int ldc, hipStream_t st) {
   const int nw = wd_ncols(epi);
   if (M < 256 || N < nw || K % WD_BK != 0) return hipErrorInvalidValue;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + nw - 1) / nw;
-  dim3 g(tiles_m * tiles_n), blk(256);
+  dim3 g(tiles_m * tiles_n), blk(512);
   const size_t lds = (size_t)2 * (256 + wd_brows(epi)) * WD_BK * sizeof(uint16_t);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
-#define TPK_WIDE(E, AF)                                                                         \
+#define TPK_WIDE(E, AF)                                                                           \
   do {                                                                                          \
     static bool attr_set = false;                                                               \
     if (!attr_set) {                                                                            \
-      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF>,                      \
+      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF>,                        \
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (ea != hipSuccess) return ea;                                                          \
       attr_set = true;                                                                          \
     }                                                                                           \
-    launch((k_gemm_wide<E, AF>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m, tiles_n); \
+    launch((k_gemm_wide<E, AF>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m, tiles_n);   \
   } while (0)
   switch (epi) {
     case EPI_ACT: TPK_WIDE(EPI_ACT, 0); break;

@@ -75,13 +75,10 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
 
-// k_gemm_wide.hip: 256 x 256 tiles (gated: 112 output columns); M >= 256, N >= the tile width,
-// K % 64 == 0. gemm_wide_tiles returns the tile count, 0 when the shape does not fit.
+// k_gemm_wide.hip: 256 x 256 tiles over eight waves (gated: 112 output columns); M >= 256,
+// N >= the tile width, K % 64 == 0. gemm_wide_tiles returns the tile count, 0 when the shape
+// does not fit.
 long gemm_wide_tiles(int epi, int M, int N);
-// k_gemm_pp.hip: the same tiles over eight waves (two per SIMD); same shape rules.
-long gemm_pp_tiles(int epi, int M, int N);
-hipError_t launch_gemm_pp(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                          const void* B2, void* C, int ldc, hipStream_t st);
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
 
