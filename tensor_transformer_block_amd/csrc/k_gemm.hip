@@ -642,7 +642,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 25
                                                   const uint16_t* __restrict__ B,
                                                   const uint16_t* __restrict__ B2, int M, int N,
                                                   int K, void* __restrict__ C, int ldc,
-                                                  int tiles_m, int tiles_n) {
+                                                  int tiles_m, int tiles_n, RopeEpi re) {
   constexpr bool DUAL = (EPI == EPI_GATED);
   constexpr int WM = BM / 2, TM = WM / 16, TN = 4;
   constexpr int A_LOADS = BM / 8 / 4;   // 1 KB wave-loads of A per wave per stage
@@ -662,6 +662,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 25
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // Rotary epilogue: lane k of wave w holds the position and KV page of tile row w + 4 k, loaded
+  // now so that the epilogue's loads do not wait on them.
+  int pos_l = 0, page_l = 0;
+  if constexpr (EPI == EPI_ROPE) {
+    if (lane < BM / 4) {
+      const int t = m0 + wave + 4 * lane;
+      pos_l = min(max(re.positions[t], 0), re.pos_limit - 1);
+      const int seq = (re.mode == 0) ? t : 0;
+      page_l = min(max(re.block_table[(size_t)seq * re.max_pages + pos_l / re.ps], 0),
+                   re.n_pages - 1);
+    }
+  }
 
   // Wave-load i of A covers tile rows (wave * A_LOADS + i) * 8 + lane / 8, 16 bytes each; since
   // those row groups start at multiples of 8, the swizzled chunk (lane % 8) ^ (row % 8) and thus
@@ -796,6 +808,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 25
     mma(nxt);
   }
 
+  if constexpr (EPI == EPI_ROPE) {
+    // Fused rotary embedding + KV append (launcher: N % 128 == 0 and hd of 64 or 128, so the
+    // tile's 128 columns are whole heads and never shifted). The tile, rounded to bf16 as the
+    // plain QKV output would be, goes through LDS (free once every wave is past its last reads)
+    // with each row's position and KV page; rows are padded to 130 elements so that 16 rows of
+    // one column sit in distinct banks.
+    constexpr int TS = 130;
+    __syncthreads();
+    uint16_t* tile = smem;                           // [BM][TS] bf16
+    int* s_pp = (int*)(smem + ((BM * TS + 7) & ~7));  // [BM][2]: position, page
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          tile[(wm * WM + i * 16 + fq * 4 + r) * TS + wn * 64 + j * 16 + fr] =
+              f32_to_bf16(acc[i][j][r]);
+    if (lane < BM / 4) {
+      s_pp[2 * (wave + 4 * lane)] = pos_l;
+      s_pp[2 * (wave + 4 * lane) + 1] = page_l;
+    }
+    __syncthreads();
+    const int hd = re.hd, half = hd >> 1;
+    const float2* rope = (const float2*)re.rope;
+    // q and k heads: thread (wave w, lane p) owns rotation pair p of the tile's 64 (head hh,
+    // element e) and rows w, w + 4, ...; a row's position and page are lane reads of the
+    // registers loaded at the start, so the unrolled rows' loads are independent.
+    {
+      const int p = lane;
+      const int hh = p / half, e = p - hh * half;
+      const int head = (n0 + hh * hd) / hd;
+      const int col = hh * hd + e;
+      if (head < re.hq + re.hk) {
+#pragma unroll
+        for (int k = 0; k < BM / 4; ++k) {
+          const int rl = wave + 4 * k;
+          const int t = m0 + rl;
+          if (t < ms0) continue;  // stored by the previous tile
+          const int pos = __builtin_amdgcn_readlane(pos_l, k);
+          const int page = __builtin_amdgcn_readlane(page_l, k);
+          const float a = bf16_to_f32(tile[rl * TS + col]), b = bf16_to_f32(tile[rl * TS + col + half]);
+          const float2 cs = rope[(size_t)pos * half + e];
+          const uint16_t ra = f32_to_bf16(a * cs.x - b * cs.y), rb = f32_to_bf16(b * cs.x + a * cs.y);
+          uint16_t* d = head < re.hq
+              ? (uint16_t*)re.q_out + ((size_t)t * re.hq + head) * hd
+              : (uint16_t*)re.k_pages + (((size_t)page * re.hk + (head - re.hq)) * re.ps + pos % re.ps) * hd;
+          d[e] = ra;
+          d[e + half] = rb;
+        }
+      }
+    }
+    // v heads, into the transposed pages ([page][kv head][hd][slot]): lanes take 16 consecutive
+    // rows of one hd element, so consecutive positions land in one 32-byte page row.
+    for (int hh = 0; hh < 128 / hd; ++hh) {
+      const int head = (n0 + hh * hd) / hd;
+      if (head < re.hq + re.hk) continue;  // uniform
+      const int g = head - re.hq - re.hk;
+      const int rs = tid & 15, e0 = tid >> 4;
+#pragma unroll 2
+      for (int rb = 0; rb < BM / 16; ++rb) {
+        const int rl = 16 * rb + rs;
+        if (m0 + rl < ms0) continue;
+        const int pos = s_pp[2 * rl], page = s_pp[2 * rl + 1];
+        uint16_t* dv = (uint16_t*)re.v_pages + ((size_t)page * re.hk + g) * hd * re.ps + pos % re.ps;
+#pragma unroll
+        for (int e = e0; e < 128; e += 16)
+          if (e < hd) dv[(size_t)e * re.ps] = tile[rl * TS + hh * hd + e];
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -826,7 +911,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM == 25
 
 template <int BM>
 static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t* a,
-                         const uint16_t* b, const uint16_t* b2, void* C, int ldc, hipStream_t st) {
+                         const uint16_t* b, const uint16_t* b2, void* C, int ldc, hipStream_t st,
+                         const RopeEpi* re = nullptr) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (epi == EPI_GATED) ? (N + 63) / 64 : (N + 127) / 128;
   if (M < BM || N < ((epi == EPI_GATED) ? 64 : 128) || K % LG_BK != 0) return hipErrorInvalidValue;
@@ -840,9 +926,11 @@ static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t*
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
       attr_set = true;                                                                          \
     }                                                                                           \
-    launch((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
-                       tiles_m, tiles_n);                                                       \
+    launch((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m,        \
+           tiles_n, rope_arg);                                                                  \
   } while (0)
+  RopeEpi rope_arg{};
+  if (re) rope_arg = *re;
   switch (epi) {
     case EPI_ACT: TPK_LDS(EPI_ACT, 0); break;
     case EPI_F32: TPK_LDS(EPI_F32, 0); break;
@@ -850,6 +938,10 @@ static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t*
     case EPI_GATED:
       if (actf == 0) TPK_LDS(EPI_GATED, 0);
       else TPK_LDS(EPI_GATED, 1);
+      break;
+    case EPI_ROPE:
+      if (!re) return hipErrorInvalidValue;
+      TPK_LDS(EPI_ROPE, 0);
       break;
     default:
       return hipErrorInvalidValue;
@@ -984,6 +1076,21 @@ static hipError_t skinny_mt(int epi, int actf, int M, int N, int K, const uint16
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+bool gemm_rope_supported(int M, int N, int K, int hd) {
+  return M >= 128 && N >= 128 && N % 128 == 0 && K % LG_BK == 0 && (hd == 64 || hd == 128) &&
+         gemm_wide_tiles(EPI_ACT, M, N) < 192;
+}
+
+hipError_t launch_gemm_qkv_rope(int M, int N, int K, const void* A, const void* B,
+                                const RopeEpi& re, hipStream_t st) {
+  if (!gemm_rope_supported(M, N, K, re.hd) || re.hd * (re.hq + 2 * re.hk) != N)
+    return hipErrorInvalidValue;
+  const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B;
+  const long t256 = (long)((M + 255) / 256) * ((N + 127) / 128);
+  if (M >= 256 && t256 >= 256) return lds_bm<256>(EPI_ROPE, 0, M, N, K, a, b, nullptr, nullptr, 0, st, &re);
+  return lds_bm<128>(EPI_ROPE, 0, M, N, K, a, b, nullptr, nullptr, 0, st, &re);
 }
 
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,

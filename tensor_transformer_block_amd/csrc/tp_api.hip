@@ -467,7 +467,30 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   hipError_t e;
   if (attn) {
     void* qkv = ws + w.qkv;
-    if (use_gemm(x, T, x.d)) {
+    tpk::RopeEpi re{};
+    re.positions = batch->positions;
+    re.block_table = batch->block_table;
+    re.rope = batch->rope_table;
+    re.q_out = ws + w.q;
+    re.k_pages = kv->k_pages;
+    re.v_pages = kv->v_pages;
+    re.mode = batch->mode;
+    re.max_pages = batch->max_pages;
+    re.ps = x.ps;
+    re.n_pages = kv->n_pages;
+    re.pos_limit = w.pos_limit;
+    re.hq = x.hq;
+    re.hk = x.hk;
+    re.hd = x.hd;
+    if (use_gemm(x, T, x.d) && !skw && at == tpk::ACT_BF16 &&
+        tpk::gemm_rope_supported(T, x.qkv_rows, x.d, x.hd)) {
+      // Multi-token MFMA path with the rotary embedding and the KV append in the GEMM epilogue.
+      {
+        TimedScope ts(evb, eve);
+        e = tpk::launch_gemm_qkv_rope(T, x.qkv_rows, x.d, xn, sh + L.qkv.offset, re, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "qkv projection");
+    } else if (use_gemm(x, T, x.d)) {
       // Multi-token MFMA path: projection, then rotary embedding + KV append.
       {
         TimedScope ts(evb, eve);
@@ -482,21 +505,6 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
       if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
     } else {
       // Decode path: the GEMV applies the rotary embedding and appends K/V in its epilogue.
-      tpk::RopeEpi re{};
-      re.positions = batch->positions;
-      re.block_table = batch->block_table;
-      re.rope = batch->rope_table;
-      re.q_out = ws + w.q;
-      re.k_pages = kv->k_pages;
-      re.v_pages = kv->v_pages;
-      re.mode = batch->mode;
-      re.max_pages = batch->max_pages;
-      re.ps = x.ps;
-      re.n_pages = kv->n_pages;
-      re.pos_limit = w.pos_limit;
-      re.hq = x.hq;
-      re.hk = x.hk;
-      re.hd = x.hd;
       {
         TimedScope ts(evb, eve);
         e = project(x, tpk::EPI_ROPE, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,

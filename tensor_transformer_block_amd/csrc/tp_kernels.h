@@ -74,6 +74,13 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
                               hipStream_t st);
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
+// The bf16 QKV projection of M tokens with the rotary embedding and the KV append in its epilogue
+// (the 128 or 256-row direct-to-LDS tiles; q goes to re.q_out, k and v into the pages). Supported
+// when N % 128 == 0, hd is 64 or 128, K % 64 == 0, M >= 128 and the shape is not one for the
+// wide-tile kernel; otherwise the caller projects and then runs launch_rope_append.
+bool gemm_rope_supported(int M, int N, int K, int hd);
+hipError_t launch_gemm_qkv_rope(int M, int N, int K, const void* A, const void* B,
+                                const RopeEpi& re, hipStream_t st);
 
 // k_gemm_wide.hip: 256 x 256 tiles over eight waves (gated: 112 output columns); M >= 256,
 // N >= the tile width, K % 64 == 0. gemm_wide_tiles returns the tile count, 0 when the shape
