@@ -64,6 +64,85 @@ __global__ void k_rope_append(const void* __restrict__ qkv, int T, int hq, int h
   }
 }
 
+// The same rotary embedding + KV append from NP fp32 partial products of the QKV projection
+// (a split-K GEMM's K ranges, [NP][T][heads * hd]): the partials are summed in range order and
+// rounded once to bf16, the value the unsplit projection would have stored, then rotated.
+template <int NP>
+__global__ void k_rope_append_parts(const float* __restrict__ parts, int T, int hq, int hk, int hd,
+                                    uint16_t* __restrict__ q_out,
+                                    const int* __restrict__ positions, int mode,
+                                    const int* __restrict__ block_table, int max_pages, int ps,
+                                    int n_pages, int pos_limit, uint16_t* __restrict__ kp,
+                                    uint16_t* __restrict__ vp, const float2* __restrict__ rope) {
+  const int half = hd >> 1;
+  const int heads = hq + 2 * hk;
+  const int64_t total = (int64_t)T * heads * half;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int e = (int)(i % half);
+  const int head = (int)((i / half) % heads);
+  const int t = (int)(i / ((int64_t)half * heads));
+  const int pos = clampi(positions[t], 0, pos_limit - 1);
+  const size_t src = (size_t)t * heads * hd + (size_t)head * hd;
+  const size_t pstride = (size_t)T * heads * hd;
+  float sa = parts[src + e], sb = parts[src + e + half];
+#pragma unroll
+  for (int p = 1; p < NP; ++p) {
+    sa += parts[p * pstride + src + e];
+    sb += parts[p * pstride + src + e + half];
+  }
+  const uint16_t ua = f32_to_bf16(sa), ub = f32_to_bf16(sb);
+  const float a = bf16_to_f32(ua), b = bf16_to_f32(ub);
+  if (head < hq + hk) {
+    const float2 cs = rope[(size_t)pos * half + e];
+    const uint16_t ra = f32_to_bf16(a * cs.x - b * cs.y), rb = f32_to_bf16(b * cs.x + a * cs.y);
+    if (head < hq) {
+      const size_t dq = (size_t)t * hq * hd + (size_t)head * hd;
+      q_out[dq + e] = ra;
+      q_out[dq + e + half] = rb;
+      return;
+    }
+    const int seq = (mode == 0) ? t : 0;
+    const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
+    const size_t dk = (((size_t)page * hk + (head - hq)) * ps + pos % ps) * hd;
+    kp[dk + e] = ra;
+    kp[dk + e + half] = rb;
+  } else {
+    const int seq = (mode == 0) ? t : 0;
+    const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
+    // V pages are stored transposed: [page][kv head][hd][slot].
+    const size_t dv = ((size_t)page * hk + (head - hq - hk)) * hd;
+    vp[(dv + e) * ps + pos % ps] = ua;
+    vp[(dv + e + half) * ps + pos % ps] = ub;
+  }
+}
+
+hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, int hk, int hd,
+                                    void* q_out, const int* positions, int mode,
+                                    const int* block_table, int max_pages, int ps, int n_pages,
+                                    int pos_limit, void* kp, void* vp, const float* rope,
+                                    hipStream_t st) {
+  const int64_t total = (int64_t)T * (hq + 2 * hk) * (hd / 2);
+  if (total == 0) return hipSuccess;
+  dim3 g((unsigned)((total + 255) / 256)), b(256);
+#define TPK_RAP(NPV)                                                                            \
+  hipLaunchKernelGGL(k_rope_append_parts<NPV>, g, b, 0, st, parts, T, hq, hk, hd,               \
+                     (uint16_t*)q_out, positions, mode, block_table, max_pages, ps, n_pages,    \
+                     pos_limit, (uint16_t*)kp, (uint16_t*)vp, (const float2*)rope)
+  switch (np) {
+    case 2: TPK_RAP(2); break;
+    case 3: TPK_RAP(3); break;
+    case 4: TPK_RAP(4); break;
+    case 5: TPK_RAP(5); break;
+    case 6: TPK_RAP(6); break;
+    case 7: TPK_RAP(7); break;
+    case 8: TPK_RAP(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef TPK_RAP
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, int hd, void* q_out,
                               const int* positions, int mode, const int* block_table,
                               int max_pages, int ps, int n_pages, int pos_limit, void* kp,

@@ -23,17 +23,24 @@ namespace tpk {
 
 constexpr int WD_BK = 64;  // k per LDS slot
 
-constexpr int wd_brows(int epi) { return epi == EPI_GATED ? 224 : 256; }
-constexpr int wd_ncols(int epi) { return epi == EPI_GATED ? 112 : 256; }
+// Staged B rows and output columns per tile (BR: a narrower non-gated tile, 160 columns).
+constexpr int wd_brows(int epi, int br = 0) { return br ? br : (epi == EPI_GATED ? 224 : 256); }
+constexpr int wd_ncols(int epi, int br = 0) {
+  return epi == EPI_GATED ? wd_brows(epi, br) / 2 : wd_brows(epi, br);
+}
 
-template <int EPI, int ACTF>
+// Grid: tiles_m * tiles_n tiles times ksplit K ranges. Block b is renumbered so each XCD's share
+// is a contiguous run (K range major, then tiles); inside a K range a run walks GM = 4 m-bands
+// down before stepping across n, so the tiles one XCD holds at a time reuse both operands in its
+// L2. With ksplit > 1 each K range writes its own fp32 partial product, C + range * M * ldc.
+template <int EPI, int ACTF, int BR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_wide(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, int ksplit) {
   constexpr bool DUAL = (EPI == EPI_GATED);
-  constexpr int NBR = wd_brows(EPI);          // staged B rows
-  constexpr int NW = wd_ncols(EPI);           // output columns per tile
+  constexpr int NBR = wd_brows(EPI, BR);      // staged B rows
+  constexpr int NW = wd_ncols(EPI, BR);       // output columns per tile
   constexpr int STAGE = (256 + NBR) * WD_BK;  // bf16 elements per slot
   constexpr int TM = 4, TN = NBR / 32;        // 16 x 16 blocks per wave (4 x 2 waves)
   constexpr int LA = 4;                       // 1 KB wave-loads of A per wave per slot
@@ -41,8 +48,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int LB = (NGB + 7) / 8;           // B wave-loads per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  {
+    constexpr int GM = 4;
+    const int b = blockIdx.x, nblk = gridDim.x, tiles = tiles_m * tiles_n;
+    const int full = nblk / 8 * 8;
+    const int lt = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
+    split = lt / tiles;
+    const int t = lt % tiles;
+    const int g = t / (GM * tiles_n), r = t % (GM * tiles_n);
+    const int gm = min(GM, tiles_m - g * GM);
+    tm = g * GM + r % gm;
+    tn = r / gm;
+  }
+  // This block's K range, in 64-deep K-tiles.
+  const int nk_all = K / WD_BK, kbase = nk_all / ksplit, krem = nk_all % ksplit;
+  const int kt0 = split * kbase + min(split, krem);
+  const int nk = kbase + (split < krem ? 1 : 0);
   // Edge tiles shift back inside the matrix (the launcher guarantees M >= 256 and N >= NW); what
   // the previous tile already covers is not stored again.
   const int ms0 = tm * 256, ns0 = tn * NW;
@@ -61,7 +83,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const size_t grp = (size_t)8 * K * 2;
   auto issue_a = [&](int slot, int kt) {
     uint16_t* st = smem + slot * STAGE;
-    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
+    const uint32_t off = lane_off + (uint32_t)(kt0 + kt) * (WD_BK * 2);
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + i * grp + off),
@@ -69,7 +91,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto issue_b = [&](int slot, int kt) {
     uint16_t* st = smem + slot * STAGE + 256 * WD_BK;
-    const uint32_t off = lane_off + (uint32_t)kt * (WD_BK * 2);
+    const uint32_t off = lane_off + (uint32_t)(kt0 + kt) * (WD_BK * 2);
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       // 8-row group of the staged B rows (wave-uniform). Where NGB is not a multiple of 8 the
@@ -135,7 +157,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 - 2 * (TM + TN), 0);
   };
 
-  const int nk = K / WD_BK;
   Frag x, y;
   issue_a(0, 0);
   issue_b(0, 0);
@@ -204,10 +225,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * 128 + j * 16 + fr;
+          const int col = n0 + wn * (NW / 2) + j * 16 + fr;
           if (col < ns0) continue;
           const size_t o = (size_t)row * ldc + col;
-          if constexpr (EPI == EPI_F32) ((float*)C)[o] = acc[i][j][r];
+          if constexpr (EPI == EPI_F32) ((float*)C + (size_t)split * M * ldc)[o] = acc[i][j][r];
           else ((uint16_t*)C)[o] = f32_to_bf16(acc[i][j][r]);
         }
       }
@@ -233,12 +254,13 @@ hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* 
   do {                                                                                          \
     static bool attr_set = false;                                                               \
     if (!attr_set) {                                                                            \
-      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF>,                        \
+      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF, 0>,                     \
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (ea != hipSuccess) return ea;                                                          \
       attr_set = true;                                                                          \
     }                                                                                           \
-    launch((k_gemm_wide<E, AF>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m, tiles_n);   \
+    launch((k_gemm_wide<E, AF, 0>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m,        \
+           tiles_n, 1);                                                                         \
   } while (0)
   switch (epi) {
     case EPI_ACT: TPK_WIDE(EPI_ACT, 0); break;
@@ -252,6 +274,39 @@ hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* 
       return hipErrorInvalidValue;
   }
 #undef TPK_WIDE
+  return hipGetLastError();
+}
+
+// Split-K projection on 256 x 160 tiles: enough tiles times K ranges to give every CU one block,
+// for projections too narrow to fill the chip with whole-K tiles (the 70B shard's QKV: 64 tiles,
+// four K ranges). Returns 1 when the shape does not gain from it.
+int gemm_split_count(int M, int N, int K) {
+  if (M < 256 || N < 160 || K % WD_BK != 0) return 1;
+  const long tiles = (long)((M + 255) / 256) * ((N + 159) / 160);
+  if (tiles >= 128) return 1;
+  int s = (int)(256 / tiles);
+  if (s > 8) s = 8;
+  while (s > 1 && K / WD_BK < 2 * s) --s;
+  return s;
+}
+
+hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void* B, float* parts,
+                                 int ksplit, hipStream_t st) {
+  constexpr int BR = 160;
+  if (M < 256 || N < BR || K % WD_BK != 0 || ksplit < 1 || K / WD_BK < ksplit)
+    return hipErrorInvalidValue;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + BR - 1) / BR;
+  dim3 g(tiles_m * tiles_n * ksplit), blk(512);
+  const size_t lds = (size_t)2 * (256 + BR) * WD_BK * sizeof(uint16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<EPI_F32, 0, BR>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (ea != hipSuccess) return ea;
+    attr_set = true;
+  }
+  launch((k_gemm_wide<EPI_F32, 0, BR>), g, blk, lds, st, (const uint16_t*)A, (const uint16_t*)B,
+         (const uint16_t*)nullptr, M, N, K, (void*)parts, N, tiles_m, tiles_n, ksplit);
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ void make_layout(const Dims& x, tp_shard_layout* L) {
 }
 
 struct WsLayout {
-  uint64_t qkv, q, attn, part_o, part_ml, ffn, gemm, total;
+  uint64_t qkv, q, attn, part_o, part_ml, ffn, gemm, qkvp, total;
   int n_split, chunk, pos_limit;
 };
 
@@ -172,6 +172,19 @@ tp_status check_batch(const Dims& x, const tp_batch* b, bool need_attn) {
   if (need_attn && b->n_tokens > 0 && (!b->positions || !b->block_table || !b->rope_table))
     return fail(TP_ERR_INVALID_ARG, "positions, block_table and rope_table must be non-NULL");
   return TP_OK;
+}
+
+// One projection of T tokens: bf16 weights with more tokens than the GEMV holds go to the MFMA
+// GEMM; everything else streams through the GEMV (in groups of up to 4 tokens).
+bool use_gemm(const Dims& x, int T, int K) {
+  return x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K);
+}
+
+// K ranges of the split-K QKV projection (bf16 prefill shapes too narrow to fill the chip with
+// whole-K tiles); 1: the projection runs unsplit.
+int qkv_ksplit(const Dims& x, int T) {
+  if (x.at != TP_DTYPE_BF16 || T <= 64 || !use_gemm(x, T, x.d)) return 1;
+  return tpk::gemm_split_count(T, x.qkv_rows, x.d);
 }
 
 WsLayout ws_layout(const Dims& x, const tp_batch& b) {
@@ -213,14 +226,11 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
     for (uint64_t c : cand) gemm = c > gemm ? c : gemm;
   }
   put(w.gemm, gemm);
+  // fp32 partial products of the split-K QKV projection.
+  const uint64_t ks = (uint64_t)qkv_ksplit(x, (int)T);
+  put(w.qkvp, ks > 1 ? ks * T * x.qkv_rows * 4 : 0);
   w.total = off > 0 ? off : kAlign;
   return w;
-}
-
-// One projection of T tokens: bf16 weights with more tokens than the GEMV holds go to the MFMA
-// GEMM; everything else streams through the GEMV (in groups of up to 4 tokens).
-bool use_gemm(const Dims& x, int T, int K) {
-  return x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K);
 }
 
 // Kernel-execution timing of one projection (see tpk::LaunchTiming); cleared on every exit path.
@@ -482,8 +492,23 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
     re.hq = x.hq;
     re.hk = x.hk;
     re.hd = x.hd;
-    if (use_gemm(x, T, x.d) && !skw && at == tpk::ACT_BF16 &&
-        tpk::gemm_rope_supported(T, x.qkv_rows, x.d, x.hd)) {
+    const int ks = qkv_ksplit(x, T);
+    if (ks > 1) {
+      // Split-K projection on tiles that fill the chip, then the rotary embedding and the KV
+      // append from the summed partials.
+      float* parts = (float*)(ws + w.qkvp);
+      {
+        TimedScope ts(evb, eve);
+        e = tpk::launch_gemm_split_f32(T, x.qkv_rows, x.d, xn, sh + L.qkv.offset, parts, ks, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "qkv projection");
+      e = tpk::launch_rope_append_parts(parts, ks, T, x.hq, x.hk, x.hd, ws + w.q, batch->positions,
+                                        batch->mode, batch->block_table, batch->max_pages, x.ps,
+                                        kv->n_pages, w.pos_limit, kv->k_pages, kv->v_pages,
+                                        batch->rope_table, st);
+      if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
+    } else if (use_gemm(x, T, x.d) && !skw && at == tpk::ACT_BF16 &&
+               tpk::gemm_rope_supported(T, x.qkv_rows, x.d, x.hd)) {
       // Multi-token MFMA path with the rotary embedding and the KV append in the GEMM epilogue.
       {
         TimedScope ts(evb, eve);

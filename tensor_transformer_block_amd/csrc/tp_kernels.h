@@ -88,8 +88,20 @@ hipError_t launch_gemm_qkv_rope(int M, int N, int K, const void* A, const void* 
 long gemm_wide_tiles(int epi, int M, int N);
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
+// Split-K bf16 projection on 256 x 160 tiles writing ksplit fp32 partial products
+// ([ksplit][M][N]) for shapes too narrow to fill the chip with whole-K tiles;
+// gemm_split_count returns the K ranges to use (1: not worth it).
+int gemm_split_count(int M, int N, int K);
+hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void* B, float* parts,
+                                 int ksplit, hipStream_t st);
 
 // k_attn.hip
+// Rotary embedding + KV append from np (2..8) fp32 partials of the QKV projection (bf16 cache).
+hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, int hk, int hd,
+                                    void* q_out, const int* positions, int mode,
+                                    const int* block_table, int max_pages, int ps, int n_pages,
+                                    int pos_limit, void* kp, void* vp, const float* rope,
+                                    hipStream_t st);
 hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, int hd, void* q_out,
                               const int* positions, int mode, const int* block_table,
                               int max_pages, int ps, int n_pages, int pos_limit, void* kp,
