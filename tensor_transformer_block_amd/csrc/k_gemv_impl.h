@@ -8,7 +8,10 @@
 // overlap. Dot products finish with DPP row reductions.
 //
 // Weight formats: fp32, bf16, and Q8_0 split into an int8 code plane [out, in] plus an fp16 scale
-// plane [out, in/32] (dequantised in registers, exactly, by q8_dequant).
+// plane [out, in/32]. A Q8_0 chunk of 16 codes is taken as sum_k scale * c_k * x_k =
+// scale * (sum_k (c_k + 128) x_k - 128 sum_k x_k): flipping each code's sign bit gives the byte
+// c_k + 128, which converts to fp32 in one instruction, and the chunk's sum of x comes staged with
+// x, so a code costs one conversion and one FMA and the scale one multiply per chunk.
 // Epilogues:
 //   EPI_F32 / EPI_BF16   store a partial sum (row-parallel o_proj and down, TensorSharp "How
 //             tensor parallelism works", step 3);
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
                                               const uint16_t* __restrict__ S, int K, int n_out,
                                               int gate_off, const void* __restrict__ X,
                                               void* __restrict__ Y, int ldy, RopeEpi re) {
-  extern __shared__ float xs[];  // [NT][K]
+  extern __shared__ float xs[];  // [NT][K], then (Q8_0) [NT][K / 16] chunk sums of x
   constexpr int VE = WFmt<WT>::VE;
   constexpr int WB = WFmt<WT>::WB;
   constexpr int AV = Vec16<AT>::N;
@@ -134,6 +137,20 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
 
   for (int i = tid * AV; i < NT * K; i += 256 * AV)
     Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
+  float* const xq = xs + NT * K;
+  if constexpr (WT == W_Q8) {
+    __syncthreads();
+    for (int i = tid; i < NT * nch; i += 256) {
+      const float* xp = xs + (size_t)i * 16;  // chunk i % nch of token i / nch (nch = K / 16)
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 v = *(const float4*)(xp + e);
+        a += (v.x + v.y) + (v.z + v.w);
+      }
+      xq[i] = a;
+    }
+  }
   __syncthreads();
   if (!active) return;
 
@@ -151,18 +168,37 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       if (c < nch) {
 #pragma unroll
         for (int s = 0; s < R; ++s) {
-          float f[VE];
-          decode_chunk<WT>(b[s][u], sc[s][u], f);
+          if constexpr (WT == W_Q8) {
+            const uint32_t r4[4] = {b[s][u].x ^ 0x80808080u, b[s][u].y ^ 0x80808080u,
+                                    b[s][u].z ^ 0x80808080u, b[s][u].w ^ 0x80808080u};
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const float* xp = xs + t * K + c * VE;
+            for (int t = 0; t < NT; ++t) {
+              const float* xp = xs + t * K + c * VE;
+              float d = 0.f;
 #pragma unroll
-            for (int e = 0; e < VE; e += 4) {
-              const float4 xv = *(const float4*)(xp + e);
-              acc[s][t] = fmaf(f[e], xv.x, acc[s][t]);
-              acc[s][t] = fmaf(f[e + 1], xv.y, acc[s][t]);
-              acc[s][t] = fmaf(f[e + 2], xv.z, acc[s][t]);
-              acc[s][t] = fmaf(f[e + 3], xv.w, acc[s][t]);
+              for (int i = 0; i < 4; ++i) {
+                const float4 xv = *(const float4*)(xp + 4 * i);
+                d = fmaf((float)(r4[i] & 0xffu), xv.x, d);
+                d = fmaf((float)((r4[i] >> 8) & 0xffu), xv.y, d);
+                d = fmaf((float)((r4[i] >> 16) & 0xffu), xv.z, d);
+                d = fmaf((float)(r4[i] >> 24), xv.w, d);
+              }
+              acc[s][t] = fmaf(sc[s][u], fmaf(-128.f, xq[t * nch + c], d), acc[s][t]);
+            }
+          } else {
+            float f[VE];
+            decode_chunk<WT>(b[s][u], sc[s][u], f);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const float* xp = xs + t * K + c * VE;
+#pragma unroll
+              for (int e = 0; e < VE; e += 4) {
+                const float4 xv = *(const float4*)(xp + e);
+                acc[s][t] = fmaf(f[e], xv.x, acc[s][t]);
+                acc[s][t] = fmaf(f[e + 1], xv.y, acc[s][t]);
+                acc[s][t] = fmaf(f[e + 2], xv.z, acc[s][t]);
+                acc[s][t] = fmaf(f[e + 3], xv.w, acc[s][t]);
+              }
             }
           }
         }
@@ -239,10 +275,23 @@ static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n
   else if constexpr (EPI == EPI_ROPE) waves = (n_out / 2 + R / 2 - 1) / (R / 2);
   else waves = (n_out + R - 1) / R;
   dim3 g((waves + 3) / 4), b(256);
-  const size_t lds = (size_t)nt * K * sizeof(float);
+  const size_t lds = (size_t)nt * K * sizeof(float) + (WT == W_Q8 ? (size_t)nt * (K / 16) * 4 : 0);
+  // (Q8_0 with 64 KB of staged tokens goes past the default dynamic-LDS limit.)
 #define TPK_GEMV(NTV)                                                                       \
-  launch((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out,   \
-                     gate_off, X, Y, ldy, re)
+  do {                                                                                      \
+    if (lds > 65536) {                                                                      \
+      static bool attr_set = false;                                                         \
+      if (!attr_set) {                                                                      \
+        hipError_t ea = hipFuncSetAttribute((const void*)k_gemv<WT, AT, EPI, NTV, ACTF, R>, \
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                                            (int)(16384 * 4 + 4096 * 4));                    \
+        if (ea != hipSuccess) return ea;                                                    \
+        attr_set = true;                                                                    \
+      }                                                                                     \
+    }                                                                                       \
+    launch((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out, gate_off, X, \
+           Y, ldy, re);                                                                     \
+  } while (0)
   switch (nt) {
     case 1: TPK_GEMV(1); break;
     case 2: TPK_GEMV(2); break;
