@@ -22,6 +22,27 @@ __device__ __forceinline__ void load8(const void* base, size_t idx, float* v) {
   }
 }
 
+// The partials are read exactly once: streaming (non-temporal) loads keep them from displacing
+// the residual and the weights in the caches and measure faster on large reads.
+template <int T>
+__device__ __forceinline__ void load8_stream(const void* base, size_t idx, float* v) {
+  if constexpr (T == ACT_F32) {
+    const uint4 a = ld_stream16((const float*)base + idx), b = ld_stream16((const float*)base + idx + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  } else {
+    const uint4 a = ld_stream16((const uint16_t*)base + idx);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 template <int T>
 __device__ __forceinline__ void store8(void* base, size_t idx, const float* v) {
   if constexpr (T == ACT_F32) {
@@ -72,7 +93,7 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
         float p[kPre][8];
 #pragma unroll
         for (int k = 0; k < kPre; ++k)
-          if (k < n_part) load8<PT>(partials, (size_t)k * part_stride + idx, p[k]);
+          if (k < n_part) load8_stream<PT>(partials, (size_t)k * part_stride + idx, p[k]);
         float sum[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum[e] = p[0][e];
@@ -84,7 +105,7 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
           }
         for (int k = kPre; k < n_part; ++k) {
           float q[8];
-          load8<PT>(partials, (size_t)k * part_stride + idx, q);
+          load8_stream<PT>(partials, (size_t)k * part_stride + idx, q);
 #pragma unroll
           for (int e = 0; e < 8; ++e) sum[e] += q[e];
         }
