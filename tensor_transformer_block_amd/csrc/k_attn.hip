@@ -74,46 +74,62 @@ __global__ void k_rope_append_parts(const float* __restrict__ parts, int T, int 
                                     const int* __restrict__ block_table, int max_pages, int ps,
                                     int n_pages, int pos_limit, uint16_t* __restrict__ kp,
                                     uint16_t* __restrict__ vp, const float2* __restrict__ rope) {
-  const int half = hd >> 1;
+  // Thread: four consecutive rotation pairs (e .. e + 3 with e + half .. e + half + 3) of one
+  // head of one token, so every partial read and every q / k store is a 16- or 8-byte access.
+  const int half = hd >> 1, q4 = half >> 2;
   const int heads = hq + 2 * hk;
-  const int64_t total = (int64_t)T * heads * half;
+  const int64_t total = (int64_t)T * heads * q4;
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const int e = (int)(i % half);
-  const int head = (int)((i / half) % heads);
-  const int t = (int)(i / ((int64_t)half * heads));
+  const int e = (int)(i % q4) * 4;
+  const int head = (int)((i / q4) % heads);
+  const int t = (int)(i / ((int64_t)q4 * heads));
   const int pos = clampi(positions[t], 0, pos_limit - 1);
   const size_t src = (size_t)t * heads * hd + (size_t)head * hd;
   const size_t pstride = (size_t)T * heads * hd;
-  float sa = parts[src + e], sb = parts[src + e + half];
+  float4 sa = *(const float4*)(parts + src + e), sb = *(const float4*)(parts + src + e + half);
 #pragma unroll
   for (int p = 1; p < NP; ++p) {
-    sa += parts[p * pstride + src + e];
-    sb += parts[p * pstride + src + e + half];
+    const float4 xa = *(const float4*)(parts + p * pstride + src + e);
+    const float4 xb = *(const float4*)(parts + p * pstride + src + e + half);
+    sa.x += xa.x; sa.y += xa.y; sa.z += xa.z; sa.w += xa.w;
+    sb.x += xb.x; sb.y += xb.y; sb.z += xb.z; sb.w += xb.w;
   }
-  const uint16_t ua = f32_to_bf16(sa), ub = f32_to_bf16(sb);
-  const float a = bf16_to_f32(ua), b = bf16_to_f32(ub);
+  const uint16_t ua[4] = {f32_to_bf16(sa.x), f32_to_bf16(sa.y), f32_to_bf16(sa.z), f32_to_bf16(sa.w)};
+  const uint16_t ub[4] = {f32_to_bf16(sb.x), f32_to_bf16(sb.y), f32_to_bf16(sb.z), f32_to_bf16(sb.w)};
   if (head < hq + hk) {
-    const float2 cs = rope[(size_t)pos * half + e];
-    const uint16_t ra = f32_to_bf16(a * cs.x - b * cs.y), rb = f32_to_bf16(b * cs.x + a * cs.y);
-    if (head < hq) {
-      const size_t dq = (size_t)t * hq * hd + (size_t)head * hd;
-      q_out[dq + e] = ra;
-      q_out[dq + e + half] = rb;
-      return;
+    const float4 c01 = *(const float4*)(rope + (size_t)pos * half + e);      // (cos, sin) of e, e+1
+    const float4 c23 = *(const float4*)(rope + (size_t)pos * half + e + 2);  // of e+2, e+3
+    const float cs[4][2] = {{c01.x, c01.y}, {c01.z, c01.w}, {c23.x, c23.y}, {c23.z, c23.w}};
+    uint16_t ra[4], rb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_to_f32(ua[j]), b = bf16_to_f32(ub[j]);
+      ra[j] = f32_to_bf16(a * cs[j][0] - b * cs[j][1]);
+      rb[j] = f32_to_bf16(b * cs[j][0] + a * cs[j][1]);
     }
-    const int seq = (mode == 0) ? t : 0;
-    const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
-    const size_t dk = (((size_t)page * hk + (head - hq)) * ps + pos % ps) * hd;
-    kp[dk + e] = ra;
-    kp[dk + e + half] = rb;
+    const uint2 pa = make_uint2(ra[0] | ((uint32_t)ra[1] << 16), ra[2] | ((uint32_t)ra[3] << 16));
+    const uint2 pb = make_uint2(rb[0] | ((uint32_t)rb[1] << 16), rb[2] | ((uint32_t)rb[3] << 16));
+    uint16_t* d;
+    if (head < hq) {
+      d = q_out + (size_t)t * hq * hd + (size_t)head * hd;
+    } else {
+      const int seq = (mode == 0) ? t : 0;
+      const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
+      d = kp + (((size_t)page * hk + (head - hq)) * ps + pos % ps) * hd;
+    }
+    *(uint2*)(d + e) = pa;
+    *(uint2*)(d + e + half) = pb;
   } else {
     const int seq = (mode == 0) ? t : 0;
     const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
     // V pages are stored transposed: [page][kv head][hd][slot].
-    const size_t dv = ((size_t)page * hk + (head - hq - hk)) * hd;
-    vp[(dv + e) * ps + pos % ps] = ua;
-    vp[(dv + e + half) * ps + pos % ps] = ub;
+    uint16_t* dv = vp + ((size_t)page * hk + (head - hq - hk)) * hd * ps + pos % ps;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dv[(size_t)(e + j) * ps] = ua[j];
+      dv[(size_t)(e + half + j) * ps] = ub[j];
+    }
   }
 }
 
@@ -122,7 +138,8 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
                                     const int* block_table, int max_pages, int ps, int n_pages,
                                     int pos_limit, void* kp, void* vp, const float* rope,
                                     hipStream_t st) {
-  const int64_t total = (int64_t)T * (hq + 2 * hk) * (hd / 2);
+  if (hd % 8) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)T * (hq + 2 * hk) * (hd / 8);
   if (total == 0) return hipSuccess;
   dim3 g((unsigned)((total + 255) / 256)), b(256);
 #define TPK_RAP(NPV)                                                                            \
