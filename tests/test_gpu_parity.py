@@ -43,6 +43,13 @@ SHAPES = [
                n_kv_heads=2, head_dim=128, ffn_dim=2176, tp=2, w_dtype="bf16",
                act_dtype="bf16", ffn_act="silu", mode="prefill", kv_lens=(2000,),
                n_tokens=2000),
+    # QKV projection paths by token count: 128 <= T < 256 takes the 128-row tiles with the
+    # rotary embedding and KV append in the GEMM epilogue; T = 256 exactly takes the split-K
+    # projection with no shifted edge tile in M.
+    MED.with_(name="med-bf16-prefill-200", index=219, mode="prefill", kv_lens=(241,),
+              n_tokens=200),
+    MED.with_(name="med-bf16-prefill-256", index=220, mode="prefill", kv_lens=(256,),
+              n_tokens=256),
     # Prefill attention over the other GQA group sizes and head dims: one query head per KV
     # head (hd 64 and 128) and eight (hd 64), with a cached prefix and ragged token counts.
     BlockShape(name="med-bf16-prefill-g1-hd64", index=216, d_model=256, n_heads=4, n_kv_heads=4,
