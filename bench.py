@@ -228,6 +228,12 @@ def main():
             with torch.cuda.graph(g):
                 blk.step(c)
             graphs.append(g)
+        # One graph holding a step on every copy in turn (a stack of `copies` blocks, as the
+        # layers of a model would be), so a replay's fixed cost is paid once per `copies` steps.
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi):
+            for c in range(copies):
+                blk.step(c)
         torch.cuda.synchronize()
 
     def run(i):
@@ -236,22 +242,68 @@ def main():
         else:
             blk.step(i % copies)
 
+    def run_steps(k):
+        """k consecutive steps, from copy 0: whole multi-step replays, then single steps."""
+        if graphs:
+            for _ in range(k // copies):
+                multi.replay()
+            for i in range(k % copies):
+                graphs[i].replay()
+        else:
+            for i in range(k):
+                blk.step(i % copies)
+
     log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        run(i)
+    run_steps(args.steps)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
     tok_s = s.n_tokens / (ms / 1e3)
+
+    # Per-step distribution: single-step replays with an event between consecutive steps (the
+    # events cost a few microseconds each, so this loop is kept apart from the timed region).
+    n_dist = max(10, min(200, args.steps))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n_dist):
+        run(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_dist)])
+    dist = {"steps": n_dist, "p10": round(float(np.percentile(per_step, 10)), 5),
+            "median": round(float(np.median(per_step)), 5),
+            "p90": round(float(np.percentile(per_step, 90)), 5)}
+
+    # The same step launched eagerly (no graph), and one rank's share (its ATTN and FFN halves,
+    # eager) at the real shape.
+    n_extra = max(5, min(50, args.steps // 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(2):
+        blk.step(i % copies)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n_extra):
+        blk.step(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n_extra
+    e0.record()
+    for i in range(n_extra):
+        c = i % copies
+        blk.attn_half(0, c)
+        blk.ffn_half(0, c)
+    e1.record()
+    torch.cuda.synchronize()
+    rank_ms = e0.elapsed_time(e1) / n_extra
 
     # Dominant kernel: the gate/up projection. The library launches its kernels through
     # hipExtLaunchKernel with these events, so each pair spans that projection's kernel execution
@@ -303,6 +355,9 @@ def main():
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_tflops": round(step_flops(s) / (ms / 1e3) / 1e12, 3),
         "wall_s_timed": round(wall, 4),
+        "step_ms_dist": dist,
+        "eager_ms_per_step": round(eager_ms, 5),
+        "rank_share_ms": round(rank_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
