@@ -364,13 +364,8 @@ static hipError_t prefill_hg(int T, int hk, hipStream_t st, const void* q, const
   constexpr int NHW = G < 4 ? G : 4, TB = 4 / NHW;
   // Two super-tile slots; the merge at the end reuses the same bytes.
   const size_t lds = (size_t)2 * AP_KG * 2 * AP_SUB * HD * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill<HD, G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = allow_lds((const void*)k_attn_prefill<HD, G>, (int)lds);
+  if (e != hipSuccess) return e;
   dim3 grid((T + 16 * TB - 1) / (16 * TB), hk * (G / NHW));
   hipLaunchKernelGGL((k_attn_prefill<HD, G>), grid, dim3(512), lds, st, (const uint16_t*)q,
                      (const uint16_t*)kp, (const uint16_t*)vp, positions, bt, max_pages, n_pages,

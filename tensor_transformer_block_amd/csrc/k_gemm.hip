@@ -279,12 +279,8 @@ static hipError_t big_bm(int epi, int actf, int M, int N, int K, const uint16_t*
   const size_t lds = (size_t)2 * (BM + BG_N) * BG_LD * sizeof(uint16_t);
 #define TPK_BIG(E, AF)                                                                          \
   do {                                                                                          \
-    static bool attr_set = false;                                                               \
-    if (!attr_set) {                                                                            \
-      hipFuncSetAttribute((const void*)k_gemm_big<E, AF, BM>,                                   \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
-      attr_set = true;                                                                          \
-    }                                                                                           \
+    hipError_t ea = allow_lds((const void*)k_gemm_big<E, AF, BM>, (int)lds);                     \
+    if (ea != hipSuccess) return ea;                                                            \
     launch((k_gemm_big<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc,    \
                        tiles_m, tiles_n);                                                       \
   } while (0)
@@ -579,13 +575,8 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
 #define TPK_SD(MTV, DV)                                                                          \
   do {                                                                                           \
     constexpr size_t lds = (size_t)SD_ST * (MTV * 16 + 64 * (DV ? 2 : 1)) * SD_BK * 2;          \
-    static bool attr_set = false;                                                                \
-    if (!attr_set) {                                                                             \
-      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_splitk_dma<MTV, DV>,               \
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (ea != hipSuccess) return ea;                                                           \
-      attr_set = true;                                                                           \
-    }                                                                                            \
+    hipError_t ea = allow_lds((const void*)k_gemm_splitk_dma<MTV, DV>, (int)lds);                \
+    if (ea != hipSuccess) return ea;                                                             \
     launch((k_gemm_splitk_dma<MTV, DV>), g, blk, lds, st, a, b, b2, M, N, K, kc, part);         \
   } while (0)
 #define TPK_SDM(MTV) \
@@ -920,12 +911,8 @@ static hipError_t lds_bm(int epi, int actf, int M, int N, int K, const uint16_t*
   const size_t lds = (size_t)LG_ST * (BM + 128) * LG_BK * sizeof(uint16_t);
 #define TPK_LDS(E, AF)                                                                          \
   do {                                                                                          \
-    static bool attr_set = false;                                                               \
-    if (!attr_set) {                                                                            \
-      hipFuncSetAttribute((const void*)k_gemm_lds<E, AF, BM>,                                   \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
-      attr_set = true;                                                                          \
-    }                                                                                           \
+    hipError_t ea = allow_lds((const void*)k_gemm_lds<E, AF, BM>, (int)lds);                     \
+    if (ea != hipSuccess) return ea;                                                            \
     launch((k_gemm_lds<E, AF, BM>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m,        \
            tiles_n, rope_arg);                                                                  \
   } while (0)

@@ -252,13 +252,8 @@ hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* 
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
 #define TPK_WIDE(E, AF)                                                                           \
   do {                                                                                          \
-    static bool attr_set = false;                                                               \
-    if (!attr_set) {                                                                            \
-      hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<E, AF, 0>,                     \
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (ea != hipSuccess) return ea;                                                          \
-      attr_set = true;                                                                          \
-    }                                                                                           \
+    hipError_t ea = allow_lds((const void*)k_gemm_wide<E, AF, 0>, (int)lds);                     \
+    if (ea != hipSuccess) return ea;                                                            \
     launch((k_gemm_wide<E, AF, 0>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m,        \
            tiles_n, 1);                                                                         \
   } while (0)
@@ -298,13 +293,8 @@ hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void*
   const int tiles_m = (M + 255) / 256, tiles_n = (N + BR - 1) / BR;
   dim3 g(tiles_m * tiles_n * ksplit), blk(512);
   const size_t lds = (size_t)2 * (256 + BR) * WD_BK * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t ea = hipFuncSetAttribute((const void*)k_gemm_wide<EPI_F32, 0, BR>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (ea != hipSuccess) return ea;
-    attr_set = true;
-  }
+  hipError_t ea = allow_lds((const void*)k_gemm_wide<EPI_F32, 0, BR>, (int)lds);
+  if (ea != hipSuccess) return ea;
   launch((k_gemm_wide<EPI_F32, 0, BR>), g, blk, lds, st, (const uint16_t*)A, (const uint16_t*)B,
          (const uint16_t*)nullptr, M, N, K, (void*)parts, N, tiles_m, tiles_n, ksplit);
   return hipGetLastError();

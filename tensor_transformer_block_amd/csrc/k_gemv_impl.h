@@ -280,14 +280,8 @@ static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n
 #define TPK_GEMV(NTV)                                                                       \
   do {                                                                                      \
     if (lds > 65536) {                                                                      \
-      static bool attr_set = false;                                                         \
-      if (!attr_set) {                                                                      \
-        hipError_t ea = hipFuncSetAttribute((const void*)k_gemv<WT, AT, EPI, NTV, ACTF, R>, \
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,     \
-                                            (int)(16384 * 4 + 4096 * 4));                    \
-        if (ea != hipSuccess) return ea;                                                    \
-        attr_set = true;                                                                    \
-      }                                                                                     \
+      hipError_t ea = allow_lds((const void*)k_gemv<WT, AT, EPI, NTV, ACTF, R>, (int)lds);  \
+      if (ea != hipSuccess) return ea;                                                      \
     }                                                                                       \
     launch((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out, gate_off, X, \
            Y, ldy, re);                                                                     \

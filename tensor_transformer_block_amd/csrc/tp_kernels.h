@@ -44,6 +44,10 @@ struct RopeEpi {
   int mode, max_pages, ps, n_pages, pos_limit, hq, hk, hd;
 };
 
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device; done once per (kernel,
+// device) and remembered, so launchers may call it before every launch.
+hipError_t allow_lds(const void* kernel, int bytes);
+
 // k_pack.hip
 hipError_t copy2d(void* dst, size_t dst_ld, const void* src, size_t src_ld, int64_t rows,
                   size_t row_bytes, hipStream_t st);
