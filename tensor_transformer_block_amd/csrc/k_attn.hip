@@ -147,6 +147,7 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
                      (uint16_t*)q_out, positions, mode, block_table, max_pages, ps, n_pages,    \
                      pos_limit, (uint16_t*)kp, (uint16_t*)vp, (const float2*)rope)
   switch (np) {
+    case 1: TPK_RAP(1); break;
     case 2: TPK_RAP(2); break;
     case 3: TPK_RAP(3); break;
     case 4: TPK_RAP(4); break;
@@ -154,6 +155,14 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
     case 6: TPK_RAP(6); break;
     case 7: TPK_RAP(7); break;
     case 8: TPK_RAP(8); break;
+    case 9: TPK_RAP(9); break;
+    case 10: TPK_RAP(10); break;
+    case 11: TPK_RAP(11); break;
+    case 12: TPK_RAP(12); break;
+    case 13: TPK_RAP(13); break;
+    case 14: TPK_RAP(14); break;
+    case 15: TPK_RAP(15); break;
+    case 16: TPK_RAP(16); break;
     default: return hipErrorInvalidValue;
   }
 #undef TPK_RAP

@@ -561,7 +561,7 @@ size_t splitk_workspace_bytes(int M, int N, int K, bool dual) {
 
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
                               const void* B, const void* B2, void* C, int ldc, float* part,
-                              hipStream_t st) {
+                              hipStream_t st, int* parts_only) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M > 64) return hipErrorInvalidValue;
   const bool dual = (epi == EPI_GATED);
@@ -603,6 +603,10 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (parts_only) {  // the caller sums the S partial tiles itself
+    *parts_only = S;
+    return hipSuccess;
+  }
   const size_t total = (size_t)M * N;
   dim3 eg((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)), eb(256);
   switch (epi) {

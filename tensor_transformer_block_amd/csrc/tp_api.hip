@@ -509,7 +509,22 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
     re.hk = x.hk;
     re.hd = x.hd;
     const int ks = qkv_ksplit(x, T);
-    if (ks > 1) {
+    int sk_parts = 0;
+    if (use_gemm(x, T, x.d) && skw && at == tpk::ACT_BF16) {
+      // Batched decode: the split-K projection's partial tiles go straight to the rotary / KV
+      // append, which sums them (no separate epilogue launch).
+      {
+        TimedScope ts(evb, eve);
+        e = tpk::launch_gemm_splitk(tpk::EPI_ACT, x.actf, T, x.qkv_rows, x.d, xn,
+                                    sh + L.qkv.offset, nullptr, qkv, x.qkv_rows, skw, st, &sk_parts);
+      }
+      if (e != hipSuccess) return hip_fail(e, "qkv projection");
+      e = tpk::launch_rope_append_parts(skw, sk_parts, T, x.hq, x.hk, x.hd, ws + w.q,
+                                        batch->positions, batch->mode, batch->block_table,
+                                        batch->max_pages, x.ps, kv->n_pages, w.pos_limit,
+                                        kv->k_pages, kv->v_pages, batch->rope_table, st);
+      if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append");
+    } else if (ks > 1) {
       // Split-K projection on tiles that fill the chip, then the rotary embedding and the KV
       // append from the summed partials.
       float* parts = (float*)(ws + w.qkvp);

@@ -73,9 +73,11 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
 // Split-K projection of M <= 64 tokens; `part` holds the fp32 split tiles
 // (splitk_workspace_bytes), summed in split order by a small epilogue kernel.
 size_t splitk_workspace_bytes(int M, int N, int K, bool dual);
+// parts_only: launch the GEMM alone, leaving the fp32 partial tiles [S][M][N] (dual: gate then
+// up per row) in `part`, and return S there; the caller then sums them.
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
                               const void* B, const void* B2, void* C, int ldc, float* part,
-                              hipStream_t st);
+                              hipStream_t st, int* parts_only = nullptr);
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
 // The bf16 QKV projection of M tokens with the rotary embedding and the KV append in its epilogue
@@ -100,7 +102,7 @@ hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void*
                                  int ksplit, hipStream_t st);
 
 // k_attn.hip
-// Rotary embedding + KV append from np (2..8) fp32 partials of the QKV projection (bf16 cache).
+// Rotary embedding + KV append from np (1..16) fp32 partials of the QKV projection (bf16 cache).
 hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, int hk, int hd,
                                     void* q_out, const int* positions, int mode,
                                     const int* block_table, int max_pages, int ps, int n_pages,
