@@ -515,26 +515,77 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_dma(const uint16_t* __restr
     }
 }
 
-template <int EPI, int ACTF>
-__global__ void k_splitk_epilogue(const float* __restrict__ part, int S, int M, int N,
-                                  void* __restrict__ C, int ldc) {
+// Sum of the S split-K partial tiles, in split order, then the epilogue. A thread owns four
+// consecutive columns of one row (V4: N % 4 == 0, C and ldc 16-byte / 4-element aligned; else
+// one column) and issues the loads of four splits before it adds them, so the split loads
+// overlap instead of forming a chain of dependent round trips.
+template <int EPI, int ACTF, bool V4>
+__global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict__ part, int S,
+                                                         int M, int N, void* __restrict__ C,
+                                                         int ldc) {
   constexpr bool DUAL = (EPI == EPI_GATED);
+  constexpr int W = V4 ? 4 : 1;
+  typedef __attribute__((__vector_size__(W * sizeof(float)))) float vec;
   const int ncols = DUAL ? 2 * N : N;
-  const size_t total = (size_t)M * N;
+  const int nv = N / W;
+  const size_t total = (size_t)M * nv;
+  const size_t slab = (size_t)M * ncols;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
-    const int row = (int)(i / N), col = (int)(i % N);
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* p = part + ((size_t)s * M + row) * ncols;
-      g += p[col];
-      if constexpr (DUAL) u += p[N + col];
+    const int row = (int)(i / nv), col = (int)(i % nv) * W;
+    const float* p = part + (size_t)row * ncols + col;
+    vec g = {}, u = {};
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      vec a[4], b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a[k] = *(const vec*)(p + (s + k) * slab);
+        if constexpr (DUAL) b[k] = *(const vec*)(p + (s + k) * slab + N);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g += a[k];
+        if constexpr (DUAL) u += b[k];
+      }
+    }
+    for (; s < S; ++s) {
+      g += *(const vec*)(p + s * slab);
+      if constexpr (DUAL) u += *(const vec*)(p + s * slab + N);
     }
     const size_t o = (size_t)row * ldc + col;
-    if constexpr (EPI == EPI_GATED) ((uint16_t*)C)[o] = f32_to_bf16(gated<ACTF>(g, u));
-    else if constexpr (EPI == EPI_F32) ((float*)C)[o] = g;
-    else ((uint16_t*)C)[o] = f32_to_bf16(g);
+    if constexpr (EPI == EPI_F32) {
+      *(vec*)((float*)C + o) = g;
+    } else {
+      uint16_t h[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+        h[k] = f32_to_bf16(EPI == EPI_GATED ? gated<ACTF>(g[k], u[k]) : g[k]);
+      if constexpr (V4)
+        *(uint2*)((uint16_t*)C + o) = make_uint2(h[0] | ((uint32_t)h[1] << 16),
+                                                 h[2] | ((uint32_t)h[3] << 16));
+      else
+        ((uint16_t*)C)[o] = h[0];
+    }
   }
+}
+
+template <bool V4>
+static hipError_t splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
+                                  void* C, int ldc, hipStream_t st) {
+  const size_t total = (size_t)M * N / (V4 ? 4 : 1);
+  dim3 eg((unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192)), eb(256);
+  switch (epi) {
+    case EPI_ACT: launch((k_splitk_epilogue<EPI_ACT, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_F32: launch((k_splitk_epilogue<EPI_F32, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_BF16: launch((k_splitk_epilogue<EPI_BF16, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_GATED:
+      if (actf == 0) launch((k_splitk_epilogue<EPI_GATED, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      else launch((k_splitk_epilogue<EPI_GATED, 1, V4>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Split count for the split-K variants: enough workgroups to cover the chip, K ranges a multiple
@@ -607,19 +658,10 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
     *parts_only = S;
     return hipSuccess;
   }
-  const size_t total = (size_t)M * N;
-  dim3 eg((unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096)), eb(256);
-  switch (epi) {
-    case EPI_ACT: launch((k_splitk_epilogue<EPI_ACT, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_F32: launch((k_splitk_epilogue<EPI_F32, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_BF16: launch((k_splitk_epilogue<EPI_BF16, 0>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_GATED:
-      if (actf == 0) launch((k_splitk_epilogue<EPI_GATED, 0>), eg, eb, 0, st, part, S, M, N, C, ldc);
-      else launch((k_splitk_epilogue<EPI_GATED, 1>), eg, eb, 0, st, part, S, M, N, C, ldc);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const bool v4 =
+      N % 4 == 0 && ldc % 4 == 0 && (uintptr_t)C % 16 == 0 && (uintptr_t)part % 16 == 0;
+  return v4 ? splitk_epilogue<true>(epi, actf, part, S, M, N, C, ldc, st)
+            : splitk_epilogue<false>(epi, actf, part, S, M, N, C, ldc, st);
 }
 
 // Prefill GEMM with a three-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4,
