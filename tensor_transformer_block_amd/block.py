@@ -124,21 +124,30 @@ class DeviceBlock:
                                  self.partials[rank] if partial is None else partial,
                                  self.workspace, self.ws_bytes)
 
-    def ffn_half(self, rank: int, copy: int = 0, partial=None):
-        B.tp_block_shard_forward(self.desc, rank, B.TP_HALF_FFN, self.shards[copy][rank],
-                                 self.batch, self.xn2, None,
-                                 self.partials[rank] if partial is None else partial,
-                                 self.workspace, self.ws_bytes)
+    def ffn_half(self, rank: int, copy: int = 0, partial=None, events=None):
+        """``events``: optional (begin, end) raw hipEvent_t handles that bracket the gate/up
+        projection's kernel execution."""
+        out = self.partials[rank] if partial is None else partial
+        if events is None:
+            B.tp_block_shard_forward(self.desc, rank, B.TP_HALF_FFN, self.shards[copy][rank],
+                                     self.batch, self.xn2, None, out, self.workspace,
+                                     self.ws_bytes)
+        else:
+            B.tp_block_shard_forward_timed(self.desc, rank, B.TP_HALF_FFN,
+                                           self.shards[copy][rank], self.batch, self.xn2, None,
+                                           out, self.workspace, events[0], events[1],
+                                           self.ws_bytes)
 
-    def step(self, copy: int = 0):
-        """One full block step on the current stream; the result lands in ``self.out``."""
+    def step(self, copy: int = 0, ffn_events=None):
+        """One full block step on the current stream; the result lands in ``self.out``.
+        ``ffn_events``: optional per-rank (begin, end) event pairs for the gate/up projections."""
         d, T, N = self.desc, self.T, self.N
         B.tp_partial_reduce(d, T, None, 0, self.x, None, self.gamma1, self.xn)
         for r in range(N):
             self.attn_half(r, copy)
         B.tp_partial_reduce(d, T, self.partials, N, self.x, self.h1, self.gamma2, self.xn2)
         for r in range(N):
-            self.ffn_half(r, copy)
+            self.ffn_half(r, copy, events=None if ffn_events is None else ffn_events[r])
         B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, None, None)
 
     # --------------------------------------------------------------------------- readback
