@@ -14,6 +14,11 @@ from the 256 MB last-level cache. One JSON line on stdout; progress on stderr.
 Roofline: the dominant kernel is the gate/up projection (the largest weight stream of a rank).
 Its average duration is measured live with HIP events recorded by the library immediately around
 its launch, on the launch stream.
+
+``--blocks K`` (K > 1) times a stack of K distinct blocks of the workload's shape instead, chained
+as the layers of a decoder (each block's output is the next block's input, every block with its
+own shards and KV caches), captured as one HIP graph; ``value`` is then tokens/s through the whole
+stack and the stack's own K blocks are the cold rotation.
 """
 from __future__ import annotations
 
@@ -168,6 +173,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--blocks", type=int, default=1,
+                    help="time a chained stack of this many distinct blocks (one graph)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a dispatch of known "
                          "size for scaling hardware byte counters)")
@@ -191,6 +198,9 @@ def main():
         sys.exit(1)
     B.lib()  # fails loudly if the HIP library is missing
     s = CONFIGS[args.workload]
+    if args.blocks > 1:
+        bench_stack(args, s)
+        return
     log(f"workload {s.name}: generating inputs (seed {args.seed})")
     inp = make_inputs(s, seed=args.seed)
     sb = step_bytes(s)
@@ -361,6 +371,104 @@ def main():
         "rank_share_ms": round(rank_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_stack(args, s):
+    """A chained stack of ``args.blocks`` distinct blocks, one graph per stack step."""
+    import numpy as np
+    import torch
+    from tensor_transformer_block_amd.block import BlockStack
+    from tensor_transformer_block_amd.inputs import make_stack_inputs
+
+    K = args.blocks
+    log(f"workload {s.name}: generating a stack of {K} blocks (seed {args.seed})")
+    inps = make_stack_inputs(s, K, seed=args.seed)
+    st = BlockStack(inps)
+    del inps
+    resident = weight_bytes(s) + sum(s.kv_lens) * s.n_kv_heads * s.head_dim * (
+        4 if s.act_dtype == "f32" else 2) * 2
+    if K * resident < args.cold_bytes:
+        log(f"note: the stack holds {K * resident / 1e6:.0f} MB, less than --cold-bytes")
+    st.step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.step()
+        torch.cuda.synchronize()
+    run = g.replay if g is not None else st.step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} stack steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Gate/up launches timed inside eager stack steps, behind a backlog of replays.
+    n_st = max(1, (args.kernel_iters + K * s.tp - 1) // (K * s.tp))
+    hev = HipEvents(2 * n_st * K * s.tp)
+    for _ in range(min(16, args.steps)):
+        run()
+    i = 0
+    for _ in range(n_st):
+        x = st.x
+        for blk in st.blocks:
+            evs = [(hev.ev[2 * (i + r)], hev.ev[2 * (i + r) + 1]) for r in range(s.tp)]
+            blk.step(x=x, ffn_events=evs)
+            i += s.tp
+            x = blk.out
+    torch.cuda.synchronize()
+    kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(i)]))
+    hev.close()
+    ub, uf = gate_up_unit(s)
+    if s.mode == "prefill":
+        roof = {"bound": "mfma", "achieved": round(uf / kavg / 1e12, 3),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(ub / kavg / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(s.name)
+    roof["kernel"] = "gate/up projection (one rank of one block)"
+    roof["avg_us"] = round(kavg * 1e6, 2)
+    sb = K * step_bytes(s)
+    step_gbs = sb / (ms / 1e3) / 1e9
+    line = {
+        "metric": "shard decode tokens/s + achieved HBM GB/s (% of peak); prefill MFMA % peak",
+        "value": round(s.n_tokens / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.act_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{s.name} x{K} blocks", "blocks": K, "d_model": s.d_model,
+                   "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                   "ffn_dim": s.ffn_dim, "tp_degree_emulated": s.tp, "weights": s.w_dtype,
+                   "mode": s.mode, "tokens": s.n_tokens, "kv_len": max(s.kv_lens),
+                   "page_size": s.page_size, "graph": not args.no_graph},
+        "step_algorithmic_bytes": sb,
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_tflops": round(K * step_flops(s) / (ms / 1e3) / 1e12, 3),
+        "ms_per_block": round(ms / K, 5),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

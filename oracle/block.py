@@ -305,3 +305,27 @@ def run_block(inp, sharded=True, rows=None):
     res = block_sharded(s, p, x, kr, vr, inp.positions, inp.token_seq, rows)
     res["kcache_by_rank"], res["vcache_by_rank"] = kr, vr
     return res
+
+
+def run_stack(inputs, sharded=True):
+    """A stack of blocks, as the layers of a decoder: the residual stream leaves block i as its
+    ``out`` and enters block i + 1 as its x (TensorSharp, "Multi-GPU & Multi-Node", section "How
+    tensor parallelism works": every rank ends each block half holding the identical hidden state,
+    which is what the next layer consumes). ``inputs``: BlockInputs of one shape; only the first
+    one's x is used. Returns the per-block result dicts (full rows, fp64, no rounding between
+    blocks)."""
+    x = to_f64(inputs[0].x, inputs[0].shape.act_dtype)
+    results = []
+    for inp in inputs:
+        s = inp.shape
+        p = params_f64(inp)
+        kc, vc = caches_f64(inp)
+        if sharded:
+            kr, vr = rank_caches(s, kc, vc)
+            res = block_sharded(s, p, x, kr, vr, inp.positions, inp.token_seq)
+        else:
+            res = block_unsharded(s, p, x, kc, vc, inp.positions, inp.token_seq)
+        res["x"] = x
+        results.append(res)
+        x = res["out"]
+    return results

@@ -138,14 +138,16 @@ class DeviceBlock:
                                            out, self.workspace, events[0], events[1],
                                            self.ws_bytes)
 
-    def step(self, copy: int = 0, ffn_events=None):
+    def step(self, copy: int = 0, ffn_events=None, x=None):
         """One full block step on the current stream; the result lands in ``self.out``.
-        ``ffn_events``: optional per-rank (begin, end) event pairs for the gate/up projections."""
+        ``ffn_events``: optional per-rank (begin, end) event pairs for the gate/up projections.
+        ``x``: the block's input [T, d] (act dtype) in place of ``self.x``."""
         d, T, N = self.desc, self.T, self.N
-        B.tp_partial_reduce(d, T, None, 0, self.x, None, self.gamma1, self.xn)
+        x = self.x if x is None else x
+        B.tp_partial_reduce(d, T, None, 0, x, None, self.gamma1, self.xn)
         for r in range(N):
             self.attn_half(r, copy)
-        B.tp_partial_reduce(d, T, self.partials, N, self.x, self.h1, self.gamma2, self.xn2)
+        B.tp_partial_reduce(d, T, self.partials, N, x, self.h1, self.gamma2, self.xn2)
         for r in range(N):
             self.ffn_half(r, copy, events=None if ffn_events is None else ffn_events[r])
         B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, None, None)
@@ -177,3 +179,25 @@ class DeviceBlock:
             ks.append(kp[phys, :, p % s.page_size])
             vs.append(vp[phys, :, :, p % s.page_size])
         return np.stack(ks), np.stack(vs)
+
+
+class BlockStack:
+    """A stack of distinct blocks of one shape, as the layers of a decoder: block i's ``out`` is
+    block i + 1's input (the residual stream), each block with its own shards, norms and
+    per-rank KV caches. One ``step`` runs every block in order on the current stream (capturable
+    as one HIP graph); the stack's output is ``self.out``."""
+
+    def __init__(self, inputs, device="cuda", partial_dtype: str = "f32"):
+        self.blocks = [DeviceBlock(inp, device=device, partial_dtype=partial_dtype)
+                       for inp in inputs]
+        self.x = self.blocks[0].x
+
+    @property
+    def out(self):
+        return self.blocks[-1].out
+
+    def step(self):
+        x = self.x
+        for blk in self.blocks:
+            blk.step(x=x)
+            x = blk.out

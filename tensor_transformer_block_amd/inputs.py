@@ -179,8 +179,10 @@ class BlockInputs:
     extras: dict = field(default_factory=dict)
 
 
-def make_inputs(s: BlockShape, seed: int = 0) -> BlockInputs:
-    rng = np.random.default_rng([seed, s.index])
+def make_inputs(s: BlockShape, seed: int = 0, block: int = 0) -> BlockInputs:
+    """One block's inputs. ``block`` > 0 draws another block of the same shape (its own weights,
+    norms and prior caches) from the stream ``[seed, index, block]``; block 0 is the workload."""
+    rng = np.random.default_rng([seed, s.index] if block == 0 else [seed, s.index, block])
     nrm = lambda shape: rng.standard_normal(shape, dtype=np.float32)
 
     g1 = (np.float32(1.0) + np.float32(0.1) * nrm(s.d_model)).astype(np.float32)
@@ -228,6 +230,13 @@ def make_inputs(s: BlockShape, seed: int = 0) -> BlockInputs:
         weights=weights, x=_encode(x, s.act_dtype), k_prior=k_prior, v_prior=v_prior,
         positions=positions, token_seq=token_seq,
         seq_lens=np.array(s.kv_lens, dtype=np.int32), block_table=table, n_pages=n_pages)
+
+
+def make_stack_inputs(s: BlockShape, n_blocks: int, seed: int = 0) -> list:
+    """Inputs of a stack of ``n_blocks`` distinct blocks of one shape, as the layers of a decoder:
+    block 0 is ``make_inputs(s, seed)``; only its x enters the stack (each later block takes the
+    previous block's output); every block keeps its own weights, norms and KV caches."""
+    return [make_inputs(s, seed, block=i) for i in range(n_blocks)]
 
 
 def paged_prior_cache(inp: BlockInputs, rank: int):

@@ -137,6 +137,64 @@ def test_step_matches_staged_and_graph_replay():
         _ = (blk.xn.float() * 2).sum().item()  # eager work between replays
 
 
+STACKS = [(CONFIGS["tiny-llama-fp32"], 3), (MED, 2),
+          (MED.with_(name="med-bf16-prefill-stack", index=221, mode="prefill", kv_lens=(150,),
+                     n_tokens=130), 2),
+          (CONFIGS["llama3-8b-decode"], 2)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s,k", STACKS, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_block_stack_parity(s, k):
+    """A stack of k distinct blocks (each block's output is the next one's input): every block's
+    GPU output against the oracle block run on the GPU's input to that block, and the stack's
+    output against the oracle's fp64 chain; a captured graph of the whole stack replays to the
+    same bits."""
+    import copy
+    import oracle
+    from tensor_transformer_block_amd.block import BlockStack, to_host
+    from tensor_transformer_block_amd.inputs import make_stack_inputs
+    tol = {"f32": 1e-4, "bf16": 2e-2}[s.act_dtype]
+    log(f"stack {s.name} x{k}: generating inputs")
+    inps = make_stack_inputs(s, k, seed=21)
+    st = BlockStack(inps)
+    st.step()
+    torch.cuda.synchronize()
+    outs = [to_host(b.out, s.act_dtype) for b in st.blocks]
+    x = inps[0].x
+    for i, inp in enumerate(inps):
+        one = copy.copy(inp)
+        one.x = x
+        ref = oracle.run_block(one)
+        gpu = oracle.to_f64(outs[i], s.act_dtype)
+        e = nrel(gpu, ref["out"])
+        log(f"  block {i}: out err {e:.3e} (tol {tol:.0e})")
+        assert e <= tol, f"block {i}"
+        x = outs[i]
+    chain = oracle.run_stack(inps)
+    e = nrel(oracle.to_f64(outs[-1], s.act_dtype), chain[-1]["out"])
+    log(f"  stack out vs fp64 chain: err {e:.3e}")
+    assert e <= tol
+    eager = st.out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        st.step()
+    for i in range(3):
+        for b in st.blocks:
+            b.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, eager), f"replay {i}"
+        _ = (st.x.float() * 2).sum().item()  # eager work between replays
+
+
 @pytest.mark.parametrize("name", ["tiny-llama-fp32", "llama3-8b-batched", "gemma-q8-decode",
                                   "med-q8-n4"])
 def test_shard_maps_bit_exact(name):

@@ -82,14 +82,16 @@ def torch_rope(x, pos, base):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def torch_block(inp):
-    """The unsharded block written with torch library routines in float64."""
+def torch_block(inp, x=None):
+    """The unsharded block written with torch library routines in float64 (x: an fp64 input in
+    place of the stored one)."""
     s = inp.shape
     shp = weight_shapes(s)
     W = {k: torch_decode_storage(inp.weights[k], s.w_dtype, shp[k]) for k in shp}
     g1 = torch_decode_storage(inp.gamma1, s.act_dtype)
     g2 = torch_decode_storage(inp.gamma2, s.act_dtype)
-    x = torch_decode_storage(inp.x, s.act_dtype)
+    if x is None:
+        x = torch_decode_storage(inp.x, s.act_dtype)
     T, hd, Hq, Hkv = x.shape[0], s.head_dim, s.n_heads, s.n_kv_heads
     xn = F.rms_norm(x, (s.d_model,), g1, eps=s.rms_eps)
     q = F.linear(xn, W["wq"]).view(T, Hq, hd)
@@ -478,3 +480,90 @@ def test_planted_transposed_wo_is_caught():
     kc, vc = oracle.caches_f64(inp)
     res = oracle.block_unsharded(s, p, x, kc, vc, inp.positions, inp.token_seq)
     assert nrel(res["h1"], ref["h1"].numpy()) > 1e-6
+
+
+# ----------------------------------------------------------------------------- stacks of blocks
+
+STACK_SHAPES = [TINY.with_(name="tiny-stack", index=120),
+                TINY.with_(name="tiny-stack-prefill", index=121, mode="prefill", kv_lens=(6,),
+                           n_tokens=4, w_dtype="bf16", act_dtype="bf16")]
+
+
+def _identity_block(inp):
+    """The same block with zero o_proj and down weights: both residual branches add exactly 0,
+    so the block passes its input through unchanged (a closed form)."""
+    import copy
+    out = copy.copy(inp)
+    out.weights = dict(inp.weights)
+    for k in ("wo", "wd"):
+        out.weights[k] = np.zeros_like(inp.weights[k])
+    return out
+
+
+@pytest.mark.parametrize("s", STACK_SHAPES, ids=lambda s: s.name)
+def test_stack_matches_chained_library_blocks(s):
+    """A stack of three blocks against the torch-library block applied three times."""
+    from tensor_transformer_block_amd.inputs import make_stack_inputs
+    inps = make_stack_inputs(s, 3, seed=4)
+    res = oracle.run_stack(inps)
+    x = torch_decode_storage(inps[0].x, s.act_dtype)
+    for i, inp in enumerate(inps):
+        ref = torch_block(inp, x=x)
+        assert nrel(res[i]["x"], x.numpy()) <= 1e-12, i
+        assert nrel(res[i]["out"], ref["out"].numpy()) <= 1e-12, i
+        x = ref["out"]
+    # distinct blocks: the draws differ from block to block
+    assert not np.array_equal(inps[0].weights["wq"], inps[1].weights["wq"])
+
+
+@pytest.mark.parametrize("s", STACK_SHAPES, ids=lambda s: s.name)
+def test_stack_identity_blocks(s):
+    """Identity blocks (zero o_proj and down) pass the residual stream through, so a stack of a
+    block and an identity block equals that block alone, in either order; a stack of identity
+    blocks returns its input."""
+    from tensor_transformer_block_amd.inputs import make_stack_inputs
+    b0, b1 = make_stack_inputs(s, 2, seed=6)
+    i0, i1 = _identity_block(b0), _identity_block(b1)
+    x0 = oracle.to_f64(b0.x, s.act_dtype)
+    alone0 = oracle.run_block(b0)["out"]
+    assert nrel(oracle.run_stack([b0, i1])[1]["out"], alone0) <= 1e-14
+    st = oracle.run_stack([i0, b1])
+    assert np.array_equal(st[0]["out"], x0)
+    b1x = _with_x(b1, b0.x)
+    assert nrel(st[1]["out"], oracle.run_block(b1x)["out"]) <= 1e-14
+    assert np.array_equal(oracle.run_stack([i0, i1])[1]["out"], x0)
+
+
+def _with_x(inp, x):
+    import copy
+    out = copy.copy(inp)
+    out.x = x
+    return out
+
+
+@pytest.mark.parametrize("s", STACK_SHAPES, ids=lambda s: s.name)
+def test_stack_sharded_equals_unsharded(s):
+    from tensor_transformer_block_amd.inputs import make_stack_inputs
+    inps = make_stack_inputs(s, 3, seed=8)
+    a, b = oracle.run_stack(inps, sharded=True), oracle.run_stack(inps, sharded=False)
+    for i in range(3):
+        assert nrel(a[i]["out"], b[i]["out"]) <= 1e-12, i
+
+
+def test_planted_stack_chaining_is_caught(monkeypatch):
+    """A stack that feeds every block the stack input instead of the previous output trips the
+    identity-block pin."""
+    def wrong_stack(inputs, sharded=True):
+        x = ob.to_f64(inputs[0].x, inputs[0].shape.act_dtype)
+        res = []
+        for inp in inputs:
+            s = inp.shape
+            kc, vc = ob.caches_f64(inp)
+            kr, vr = ob.rank_caches(s, kc, vc)
+            r = ob.block_sharded(s, ob.params_f64(inp), x, kr, vr, inp.positions, inp.token_seq)
+            r["x"] = x
+            res.append(r)
+        return res
+    monkeypatch.setattr(oracle, "run_stack", wrong_stack)
+    with pytest.raises(AssertionError):
+        test_stack_identity_blocks(STACK_SHAPES[0])
