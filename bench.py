@@ -175,6 +175,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--blocks", type=int, default=1,
                     help="time a chained stack of this many distinct blocks (one graph)")
+    ap.add_argument("--head", action="store_true",
+                    help="with the stack, time a full token step: embedding lookup, the stack, "
+                         "final RMSNorm and LM head (replicated head of the family's vocabulary)")
+    ap.add_argument("--vocab", type=int, default=0, help="vocabulary of --head (0: the family's)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a dispatch of known "
                          "size for scaling hardware byte counters)")
@@ -198,7 +202,7 @@ def main():
         sys.exit(1)
     B.lib()  # fails loudly if the HIP library is missing
     s = CONFIGS[args.workload]
-    if args.blocks > 1:
+    if args.blocks > 1 or args.head:
         bench_stack(args, s)
         return
     log(f"workload {s.name}: generating inputs (seed {args.seed})")
@@ -385,27 +389,39 @@ def bench_stack(args, s):
     K = args.blocks
     log(f"workload {s.name}: generating a stack of {K} blocks (seed {args.seed})")
     inps = make_stack_inputs(s, K, seed=args.seed)
-    st = BlockStack(inps)
+    model = None
+    if args.head:
+        from tensor_transformer_block_amd.block import ModelStep
+        from tensor_transformer_block_amd.inputs import VOCAB, make_head_inputs
+        vocab = args.vocab or VOCAB[s.name]
+        log(f"head: vocab {vocab}")
+        head = make_head_inputs(s, vocab, seed=args.seed)
+        model = ModelStep(head, inps)
+        st = model.stack
+        del head
+    else:
+        st = BlockStack(inps)
     del inps
+    stepper = model if model is not None else st
     resident = weight_bytes(s) + sum(s.kv_lens) * s.n_kv_heads * s.head_dim * (
         4 if s.act_dtype == "f32" else 2) * 2
     if K * resident < args.cold_bytes:
         log(f"note: the stack holds {K * resident / 1e6:.0f} MB, less than --cold-bytes")
-    st.step()
+    stepper.step()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        st.step()
+        stepper.step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            st.step()
+            stepper.step()
         torch.cuda.synchronize()
-    run = g.replay if g is not None else st.step
+    run = g.replay if g is not None else stepper.step
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -449,6 +465,26 @@ def bench_stack(args, s):
     roof["kernel"] = "gate/up projection (one rank of one block)"
     roof["avg_us"] = round(kavg * 1e6, 2)
     sb = K * step_bytes(s)
+    head_info = None
+    if model is not None:
+        # The LM head alone: stream events around eager launches (one kernel per launch, so the
+        # pair spans it plus its dispatch), behind a backlog of replays.
+        hb = model.head.layout.payload_bytes + s.n_tokens * s.d_model * (
+            4 if s.act_dtype == "f32" else 2) + s.n_tokens * model.head.vocab * 4
+        sb += hb + s.n_tokens * s.d_model * (4 if s.act_dtype == "f32" else 2)
+        n_h = 50
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_h)]
+        for _ in range(min(8, args.steps)):
+            run()
+        for j in range(n_h):
+            evs[2 * j].record()
+            model.head.logits(model.xn_f, model.logits)
+            evs[2 * j + 1].record()
+        torch.cuda.synchronize()
+        h_ms = float(np.mean([evs[2 * j].elapsed_time(evs[2 * j + 1]) for j in range(n_h)]))
+        head_info = {"vocab": model.head.vocab, "lm_head_bytes": hb,
+                     "lm_head_us": round(h_ms * 1e3, 2),
+                     "lm_head_gbs": round(hb / (h_ms / 1e3) / 1e9, 1)}
     step_gbs = sb / (ms / 1e3) / 1e9
     line = {
         "metric": "shard decode tokens/s + achieved HBM GB/s (% of peak); prefill MFMA % peak",
@@ -456,7 +492,8 @@ def bench_stack(args, s):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.act_dtype,
         "data": "synthetic",
-        "config": {"workload": f"{s.name} x{K} blocks", "blocks": K, "d_model": s.d_model,
+        "config": {"workload": f"{s.name} x{K} blocks" + (" + head" if model else ""),
+                   "blocks": K, "head": head_info, "d_model": s.d_model,
                    "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "ffn_dim": s.ffn_dim, "tp_degree_emulated": s.tp, "weights": s.w_dtype,
                    "mode": s.mode, "tokens": s.n_tokens, "kv_len": max(s.kv_lens),
@@ -464,7 +501,8 @@ def bench_stack(args, s):
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "step_tflops": round(K * step_flops(s) / (ms / 1e3) / 1e12, 3),
+        "step_tflops": round((K * step_flops(s) + (2.0 * s.n_tokens * s.d_model * model.head.vocab
+                                                    if model else 0.0)) / (ms / 1e3) / 1e12, 3),
         "ms_per_block": round(ms / K, 5),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,

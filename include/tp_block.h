@@ -19,6 +19,11 @@
  *              if it is explicit, and must never give silently wrong results.
  *   [NN-CHG]   nnsight PR #677, section "Change": row-parallel layers split the input dim, the
  *              others the output dim; fused weights keep their rows grouped by rank.
+ *   [TS-REP]   TensorSharp, section "How tensor parallelism works", after its three steps: the
+ *              norms, the token embeddings and the LM head are not sharded but held whole by every
+ *              rank, so they add no collective.
+ *   [ML-OOS]   mlxcel issue #488, section "Out of scope": embeddings and LM head stay replicated
+ *              (a vocabulary-parallel split is left out).
  *
  * Conventions for every call:
  *   - All tensors are caller-owned device memory unless stated. The library allocates nothing,
@@ -184,6 +189,39 @@ tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, 
 tp_status tp_partial_reduce(const tp_block_desc* desc, int32_t n_tokens, const void* partials,
                             int32_t n_partials, const void* residual_in, void* residual_out,
                             const void* gamma, void* normed_out, void* stream);
+
+/* ---- the replicated model head around a stack of blocks [TS-REP] [ML-OOS] ----
+ * One packed table of vocab rows x d_model serves the token-embedding lookup and the LM head
+ * (tied embeddings; untied models pack two tables). Its layout, 256-byte aligned regions:
+ *   table        [vocab, d] in w_dtype; for Q8_0 the int8 codes, one byte per weight;
+ *   table_scale  Q8_0 only: the fp16 block scales [vocab, d/32] (bytes = 0 otherwise). */
+typedef struct {
+  tp_region table, table_scale;
+  uint64_t payload_bytes, alloc_bytes;
+} tp_head_layout;
+
+/* Fill `out` with the packed head layout for `vocab` rows (vocab > 0). Host only. */
+tp_status tp_head_size(const tp_block_desc* desc, int32_t vocab, tp_head_layout* out);
+
+/* Pack a full table `src` (device, [vocab, d] row-major in w_dtype; Q8_0: d/32 blocks of 34 bytes
+ * per row, fp16 scale then 32 int8) into `dst` (device, dst_bytes >= alloc_bytes). */
+tp_status tp_head_pack(const tp_block_desc* desc, int32_t vocab, const void* src, void* dst,
+                       uint64_t dst_bytes, void* stream);
+
+/* Token-embedding lookup: x_out[t] = row token_ids[t] of the packed table, in the activation
+ * dtype ([n_tokens, d], 16-byte aligned). F32 / BF16 rows are copied bit for bit; Q8_0 rows are
+ * dequantised (scale * code, exact in fp32) and rounded once to bf16 (nearest even).
+ * token_ids: device int32 [n_tokens]; ids outside [0, vocab) are clamped. n_tokens == 0 is a
+ * no-op. */
+tp_status tp_embed_lookup(const tp_block_desc* desc, int32_t vocab, const void* head,
+                          const int32_t* token_ids, int32_t n_tokens, void* x_out, void* stream);
+
+/* LM head: logits[t, v] = sum_k xn[t, k] * table[v, k] (fp32 accumulation, fp32 logits
+ * [n_tokens, vocab]). xn is the final RMSNorm of the stack's output (tp_partial_reduce with no
+ * partials), activation dtype [n_tokens, d]. Few tokens stream the table through the GEMV; BF16
+ * with more tokens runs the matrix-core GEMM. n_tokens == 0 is a no-op. */
+tp_status tp_lm_head(const tp_block_desc* desc, int32_t vocab, const void* head, const void* xn,
+                     int32_t n_tokens, float* logits, void* stream);
 
 const char* tp_status_str(tp_status status);
 /* Detail of the calling thread's last failure ("" if none). */

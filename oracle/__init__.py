@@ -10,6 +10,7 @@ unsharded, library cross-checks of every sublayer, brute force on tiny shapes, c
 """
 from .block import (  # noqa: F401
     ACTIVATIONS, attend, bf16_bits_to_f64, block_sharded, block_unsharded, caches_f64,
-    dequant_q8_0, f16_bits_to_f64, gelu_tanh, params_f64, rank_caches, rms_norm, rope,
-    rope_cos_sin, run_block, run_stack, shard_slices, shard_weights, silu, to_f64,
+    dequant_q8_0, embed_lookup, f16_bits_to_f64, gelu_tanh, head_table_f64, lm_head, params_f64,
+    rank_caches, rms_norm, rope, rope_cos_sin, round_to_bf16, run_block, run_model, run_stack,
+    shard_slices, shard_weights, silu, to_f64,
 )

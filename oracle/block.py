@@ -307,14 +307,15 @@ def run_block(inp, sharded=True, rows=None):
     return res
 
 
-def run_stack(inputs, sharded=True):
+def run_stack(inputs, sharded=True, x=None):
     """A stack of blocks, as the layers of a decoder: the residual stream leaves block i as its
     ``out`` and enters block i + 1 as its x (TensorSharp, "Multi-GPU & Multi-Node", section "How
     tensor parallelism works": every rank ends each block half holding the identical hidden state,
-    which is what the next layer consumes). ``inputs``: BlockInputs of one shape; only the first
-    one's x is used. Returns the per-block result dicts (full rows, fp64, no rounding between
-    blocks)."""
-    x = to_f64(inputs[0].x, inputs[0].shape.act_dtype)
+    which is what the next layer consumes). ``inputs``: BlockInputs of one shape; the stack input
+    is ``x`` (fp64 [T, d]) or else the first one's x. Returns the per-block result dicts (full
+    rows, fp64, no rounding between blocks)."""
+    if x is None:
+        x = to_f64(inputs[0].x, inputs[0].shape.act_dtype)
     results = []
     for inp in inputs:
         s = inp.shape
@@ -329,3 +330,52 @@ def run_stack(inputs, sharded=True):
         results.append(res)
         x = res["out"]
     return results
+
+
+# ----------------------------------------------------------------------------- the replicated head
+# TensorSharp, "Multi-GPU & Multi-Node", section "How tensor parallelism works": the norms, the
+# token embeddings and the LM head are held whole on every rank (no sharding, no collective);
+# mlxcel issue #488, section "Out of scope", keeps embeddings and LM head replicated too.
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Values exactly representable in fp32 -> nearest bfloat16 (ties to even), as float64: keep
+    the top 16 bits of the fp32 pattern after adding 0x7FFF plus the lowest kept bit."""
+    u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (r.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def head_table_f64(head) -> np.ndarray:
+    """The head's [vocab, d] table widened to fp64 (Q8_0 blocks dequantised exactly)."""
+    s = head.shape
+    if s.w_dtype == "q8_0":
+        return dequant_q8_0(head.table, head.vocab, s.d_model)
+    return to_f64(head.table, s.w_dtype)
+
+
+def embed_lookup(head, table=None) -> np.ndarray:
+    """x[t] = row token_ids[t] of the table, as the activation dtype stores it: f32 and bf16 rows
+    are taken as stored; a Q8_0 row's dequantised values (exact in fp32) are rounded to bf16."""
+    s = head.shape
+    table = head_table_f64(head) if table is None else table
+    x = table[np.asarray(head.token_ids, dtype=np.int64)]
+    if s.w_dtype == "q8_0":
+        x = round_to_bf16(x)
+    return x
+
+
+def lm_head(xn: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Logits [T, vocab] = xn [T, d] times the table transposed."""
+    return xn @ table.T
+
+
+def run_model(head, inputs, sharded=True):
+    """A synthetic full-token step: embedding lookup, the stack of blocks, the final RMSNorm with
+    the head's gamma, and the LM head. Returns dict(x, stack, xn_f, logits)."""
+    s = head.shape
+    table = head_table_f64(head)
+    x = embed_lookup(head, table)
+    stack = run_stack(inputs, sharded=sharded, x=x)
+    xn_f = rms_norm(stack[-1]["out"], to_f64(head.gamma_f, s.act_dtype), s.rms_eps)
+    return dict(x=x, stack=stack, xn_f=xn_f, logits=lm_head(xn_f, table))

@@ -28,7 +28,8 @@ EXPORTED = (
     "tp_shard_weights_size", "tp_shard_weights", "tp_workspace_size", "tp_rope_table_bytes",
     "tp_rope_table_init", "tp_block_shard_forward", "tp_partial_reduce", "tp_status_str",
     "tp_last_error", "tp_shard_unpack", "tp_dequant_q8_0", "tp_workspace_offsets",
-    "tp_block_shard_forward_timed",
+    "tp_block_shard_forward_timed", "tp_head_size", "tp_head_pack", "tp_embed_lookup",
+    "tp_lm_head",
 )
 
 
@@ -47,6 +48,11 @@ class tp_shard_layout(ctypes.Structure):
     _fields_ = [(n, tp_region) for n in (
         "qkv", "o", "gate_up", "down", "qkv_scale", "o_scale", "gate_up_scale", "down_scale")] + [
         ("payload_bytes", ctypes.c_uint64), ("alloc_bytes", ctypes.c_uint64)]
+
+
+class tp_head_layout(ctypes.Structure):
+    _fields_ = [("table", tp_region), ("table_scale", tp_region),
+                ("payload_bytes", ctypes.c_uint64), ("alloc_bytes", ctypes.c_uint64)]
 
 
 class tp_full_weights(ctypes.Structure):
@@ -97,6 +103,10 @@ def lib() -> ctypes.CDLL:
         "tp_shard_unpack": [P, I32, P, P, P],
         "tp_dequant_q8_0": [P, P, P, U64, P],
         "tp_workspace_offsets": [P, P, P, P, P],
+        "tp_head_size": [P, I32, P],
+        "tp_head_pack": [P, I32, P, P, U64, P],
+        "tp_embed_lookup": [P, I32, P, P, I32, P, P],
+        "tp_lm_head": [P, I32, P, P, I32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -234,6 +244,29 @@ def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residua
 
 def tp_dequant_q8_0(codes, scales, out, n_blocks, stream=None) -> None:
     _check(lib().tp_dequant_q8_0(ptr(codes), ptr(scales), ptr(out), n_blocks, _stream(stream)))
+
+
+def tp_head_size(desc, vocab: int) -> tp_head_layout:
+    out = tp_head_layout()
+    _check(lib().tp_head_size(ctypes.byref(desc), vocab, ctypes.byref(out)))
+    return out
+
+
+def tp_head_pack(desc, vocab, src, dst, dst_bytes=None, stream=None) -> None:
+    if dst_bytes is None:
+        dst_bytes = dst.numel() * dst.element_size()
+    _check(lib().tp_head_pack(ctypes.byref(desc), vocab, ptr(src), ptr(dst), dst_bytes,
+                              _stream(stream)))
+
+
+def tp_embed_lookup(desc, vocab, head, token_ids, n_tokens, x_out, stream=None) -> None:
+    _check(lib().tp_embed_lookup(ctypes.byref(desc), vocab, ptr(head), ptr(token_ids), n_tokens,
+                                 ptr(x_out), _stream(stream)))
+
+
+def tp_lm_head(desc, vocab, head, xn, n_tokens, logits, stream=None) -> None:
+    _check(lib().tp_lm_head(ctypes.byref(desc), vocab, ptr(head), ptr(xn), n_tokens, ptr(logits),
+                            _stream(stream)))
 
 
 def tp_status_str(status: int) -> str:

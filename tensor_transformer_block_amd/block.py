@@ -196,8 +196,54 @@ class BlockStack:
     def out(self):
         return self.blocks[-1].out
 
-    def step(self):
-        x = self.x
+    def step(self, x=None):
+        x = self.x if x is None else x
         for blk in self.blocks:
             blk.step(x=x)
             x = blk.out
+
+
+class DeviceHead:
+    """The replicated head (one packed [vocab, d] table for the token-embedding lookup and the LM
+    head, and the final norm's gamma) on the GPU."""
+
+    def __init__(self, head, desc, device="cuda"):
+        s = head.shape
+        self.vocab, self.desc, self.shape = head.vocab, desc, s
+        self.layout = B.tp_head_size(desc, head.vocab)
+        src = to_device(head.table, s.w_dtype, device)
+        self.table = torch.empty(self.layout.alloc_bytes, dtype=torch.uint8, device=device)
+        B.tp_head_pack(desc, head.vocab, src, self.table)
+        torch.cuda.synchronize()
+        del src
+        self.gamma_f = to_device(head.gamma_f, s.act_dtype, device)
+        self.token_ids = torch.from_numpy(head.token_ids).to(device)
+
+    def embed(self, x_out, token_ids=None):
+        ids = self.token_ids if token_ids is None else token_ids
+        B.tp_embed_lookup(self.desc, self.vocab, self.table, ids, int(ids.numel()), x_out)
+
+    def logits(self, xn, out):
+        B.tp_lm_head(self.desc, self.vocab, self.table, xn, int(xn.shape[0]), out)
+
+
+class ModelStep:
+    """A synthetic full-token step around a stack of blocks: embedding lookup, the stack, the
+    final RMSNorm (the reduce kernel with no partials) and the LM head. Logits in ``self.logits``
+    [T, vocab] fp32."""
+
+    def __init__(self, head, inputs, device="cuda", partial_dtype: str = "f32"):
+        self.stack = BlockStack(inputs, device=device, partial_dtype=partial_dtype)
+        b0 = self.stack.blocks[0]
+        self.head = DeviceHead(head, b0.desc, device=device)
+        self.x = torch.empty_like(b0.x)
+        self.xn_f = torch.empty_like(b0.x)
+        self.logits = torch.empty((b0.T, head.vocab), dtype=torch.float32, device=device)
+
+    def step(self):
+        b0 = self.stack.blocks[0]
+        self.head.embed(self.x)
+        self.stack.step(x=self.x)
+        B.tp_partial_reduce(b0.desc, b0.T, None, 0, self.stack.out, None, self.head.gamma_f,
+                            self.xn_f)
+        self.head.logits(self.xn_f, self.logits)

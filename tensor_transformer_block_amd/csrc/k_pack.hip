@@ -109,4 +109,59 @@ hipError_t q8_dequant_buf(const void* codes, const void* scales, float* out, int
   return hipGetLastError();
 }
 
+// Token-embedding lookup (the replicated input layer around the block stack): row ids[t] of the
+// packed table becomes x[t] in the activation dtype. F32 and BF16 rows are copied as stored; a
+// Q8_0 row is dequantised (scale * code is exact in fp32) and rounded once to bf16. A thread moves
+// one 16-byte chunk of the stored row; ids outside [0, vocab) are clamped into the table.
+template <int WT>
+__global__ void k_embed(const char* __restrict__ table, const uint16_t* __restrict__ scales,
+                        const int32_t* __restrict__ ids, int vocab, int d,
+                        char* __restrict__ x) {
+  constexpr int WB = WT == W_F32 ? 4 : (WT == W_BF16 ? 2 : 1);
+  const int t = blockIdx.x;
+  int id = ids[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const int nch = d * WB / 16;
+  const char* row = table + (size_t)id * d * WB;
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+    const uint4 v = *(const uint4*)(row + (size_t)c * 16);
+    if constexpr (WT != W_Q8) {
+      *(uint4*)(x + ((size_t)t * d * WB) + (size_t)c * 16) = v;
+    } else {
+      const float sc = f16_to_f32(scales[(size_t)id * (d / 32) + c / 2]);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t b0 = (int8_t)(w[i] & 0xffu), b1 = (int8_t)((w[i] >> 8) & 0xffu);
+        const int32_t b2 = (int8_t)((w[i] >> 16) & 0xffu), b3 = (int8_t)(w[i] >> 24);
+        o[2 * i] = f32_to_bf16(q8_dequant(sc, b0)) | ((uint32_t)f32_to_bf16(q8_dequant(sc, b1)) << 16);
+        o[2 * i + 1] =
+            f32_to_bf16(q8_dequant(sc, b2)) | ((uint32_t)f32_to_bf16(q8_dequant(sc, b3)) << 16);
+      }
+      uint4* dst = (uint4*)(x + ((size_t)t * d + (size_t)c * 16) * 2);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+hipError_t launch_embed(int wt, const void* table, const void* scales, const int32_t* ids,
+                        int T, int vocab, int d, void* x, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const dim3 g(T), b(256);
+  if (wt == W_F32)
+    hipLaunchKernelGGL(k_embed<W_F32>, g, b, 0, st, (const char*)table, nullptr, ids, vocab, d,
+                       (char*)x);
+  else if (wt == W_BF16)
+    hipLaunchKernelGGL(k_embed<W_BF16>, g, b, 0, st, (const char*)table, nullptr, ids, vocab, d,
+                       (char*)x);
+  else if (wt == W_Q8)
+    hipLaunchKernelGGL(k_embed<W_Q8>, g, b, 0, st, (const char*)table, (const uint16_t*)scales,
+                       ids, vocab, d, (char*)x);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace tpk

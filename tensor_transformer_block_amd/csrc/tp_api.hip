@@ -379,6 +379,114 @@ tp_status tp_shard_unpack(const tp_block_desc* desc, int32_t rank, const void* s
   return shard_copy(x, rank, dst, (char*)shard, false, (hipStream_t)stream);
 }
 
+// ---- replicated head: one packed [vocab, d] table for the embedding lookup and the LM head
+static tp_status check_head(const tp_block_desc* desc, int32_t vocab, Dims* x) {
+  if (tp_status s = check_desc(desc, x)) return s;
+  if (vocab <= 0) return fail(TP_ERR_INVALID_ARG, "vocab=%d must be > 0", vocab);
+  return TP_OK;
+}
+
+static void make_head_layout(const Dims& x, int32_t vocab, tp_head_layout* L) {
+  *L = tp_head_layout{};
+  L->table.offset = 0;
+  L->table.bytes = (uint64_t)vocab * x.d * x.wb;
+  uint64_t off = align_up(L->table.bytes);
+  if (x.wt == TP_DTYPE_Q8_0) {
+    L->table_scale.offset = off;
+    L->table_scale.bytes = (uint64_t)vocab * (x.d / 32) * 2;
+    off = align_up(off + L->table_scale.bytes);
+  }
+  L->payload_bytes = L->table.bytes + L->table_scale.bytes;
+  L->alloc_bytes = off;
+}
+
+tp_status tp_head_size(const tp_block_desc* desc, int32_t vocab, tp_head_layout* out) {
+  Dims x;
+  if (tp_status s = check_head(desc, vocab, &x)) return s;
+  if (!out) return fail(TP_ERR_INVALID_ARG, "out is NULL");
+  make_head_layout(x, vocab, out);
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_head_pack(const tp_block_desc* desc, int32_t vocab, const void* src, void* dst,
+                       uint64_t dst_bytes, void* stream) {
+  Dims x;
+  if (tp_status s = check_head(desc, vocab, &x)) return s;
+  if (!src || !dst) return fail(TP_ERR_INVALID_ARG, "src and dst must be non-NULL");
+  tp_head_layout L;
+  make_head_layout(x, vocab, &L);
+  if (dst_bytes < L.alloc_bytes)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "dst_bytes=%llu < alloc_bytes=%llu",
+                (unsigned long long)dst_bytes, (unsigned long long)L.alloc_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* d = (char*)dst;
+  hipError_t e;
+  if (x.wt == TP_DTYPE_Q8_0)
+    e = tpk::q8_split(src, (size_t)(x.d / 32) * 34, vocab, x.d / 32, d + L.table.offset,
+                      d + L.table_scale.offset, st);
+  else
+    e = tpk::copy2d(d + L.table.offset, (size_t)x.d * x.wb, src, (size_t)x.d * x.wb, vocab,
+                    (size_t)x.d * x.wb, st);
+  if (e != hipSuccess) return hip_fail(e, "tp_head_pack");
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_embed_lookup(const tp_block_desc* desc, int32_t vocab, const void* head,
+                          const int32_t* token_ids, int32_t n_tokens, void* x_out, void* stream) {
+  Dims x;
+  if (tp_status s = check_head(desc, vocab, &x)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (n_tokens == 0) return TP_OK;
+  if (!head || !token_ids || !x_out)
+    return fail(TP_ERR_INVALID_ARG, "head, token_ids and x_out must be non-NULL");
+  if (!aligned16(head) || !aligned16(x_out))
+    return fail(TP_ERR_INVALID_ARG, "head and x_out must be 16-byte aligned");
+  tp_head_layout L;
+  make_head_layout(x, vocab, &L);
+  const char* h = (const char*)head;
+  const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
+  hipError_t e = tpk::launch_embed(wt, h + L.table.offset, h + L.table_scale.offset, token_ids,
+                                   n_tokens, vocab, x.d, x_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tp_embed_lookup");
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_lm_head(const tp_block_desc* desc, int32_t vocab, const void* head, const void* xn,
+                     int32_t n_tokens, float* logits, void* stream) {
+  Dims x;
+  if (tp_status s = check_head(desc, vocab, &x)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (n_tokens == 0) return TP_OK;
+  if (!head || !xn || !logits)
+    return fail(TP_ERR_INVALID_ARG, "head, xn and logits must be non-NULL");
+  if (!aligned16(head) || !aligned16(xn) || !aligned16(logits))
+    return fail(TP_ERR_INVALID_ARG, "head, xn and logits must be 16-byte aligned");
+  tp_head_layout L;
+  make_head_layout(x, vocab, &L);
+  const char* h = (const char*)head;
+  hipError_t e;
+  const size_t one_split = (size_t)n_tokens * vocab * sizeof(float);
+  if (use_gemm(x, n_tokens, x.d) && n_tokens <= 64 &&
+      tpk::splitk_workspace_bytes(n_tokens, vocab, x.d, false) == one_split) {
+    // A vocabulary wide enough to fill the chip with whole-K column tiles: the batched-decode
+    // GEMM (activation tile shared through LDS) writes its single fp32 tile straight into the
+    // logits, which have the partial-tile layout [T, vocab].
+    int parts = 0;
+    e = tpk::launch_gemm_splitk(tpk::EPI_F32, 0, n_tokens, vocab, x.d, xn, h + L.table.offset,
+                                nullptr, logits, vocab, logits, (hipStream_t)stream, &parts);
+    if (e == hipSuccess && parts != 1) e = hipErrorInvalidValue;
+  } else {
+    e = project(x, tpk::EPI_F32, n_tokens, h + L.table.offset, h + L.table_scale.offset, x.d,
+                vocab, 0, xn, logits, vocab, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "tp_lm_head");
+  g_err.clear();
+  return TP_OK;
+}
+
 tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uint64_t n_blocks,
                           void* stream) {
   if (n_blocks == 0) return TP_OK;

@@ -59,6 +59,8 @@ hipError_t q8_dequant_buf(const void* codes, const void* scales, float* out, int
                           hipStream_t st);
 
 // k_reduce.hip
+hipError_t launch_embed(int wt, const void* table, const void* scales, const int32_t* ids,
+                        int T, int vocab, int d, void* x, hipStream_t st);
 hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,
                                  const void* res_in, void* res_out, const void* gamma,
                                  void* normed, float eps, hipStream_t st);

@@ -239,6 +239,39 @@ def make_stack_inputs(s: BlockShape, n_blocks: int, seed: int = 0) -> list:
     return [make_inputs(s, seed, block=i) for i in range(n_blocks)]
 
 
+# Vocabulary sizes of the model families the workloads are shaped after (the replicated head).
+VOCAB = {"tiny-llama-fp32": 512, "llama3-8b-decode": 128256, "llama3-8b-batched": 128256,
+         "llama-70b-prefill": 128256, "gemma-q8-decode": 262144}
+
+
+@dataclass
+class HeadInputs:
+    """The replicated head around a stack: one table [vocab, d] (storage form, w_dtype) used for
+    the token-embedding lookup and as the LM head, the final norm's gamma and the token ids."""
+
+    shape: BlockShape
+    vocab: int
+    table: np.ndarray                 # f32 / bf16 bits [vocab, d]; Q8_0 bytes [vocab, d/32*34]
+    gamma_f: np.ndarray               # [d], activation storage dtype
+    token_ids: np.ndarray             # int32 [T]
+
+
+def make_head_inputs(s: BlockShape, vocab: int, seed: int = 0) -> HeadInputs:
+    """Draws from ``[seed, index, 1 << 20]``: gamma_f as 1 + 0.1 N, the table as 0.02 N
+    [vocab, d] (stored like the block weights), then T token ids uniform in [0, vocab)."""
+    rng = np.random.default_rng([seed, s.index, 1 << 20])
+    gf = (np.float32(1.0) + np.float32(0.1) * rng.standard_normal(s.d_model, dtype=np.float32))
+    table = np.empty((vocab, s.d_model), dtype=np.float32)
+    step = max(1, (1 << 24) // s.d_model)
+    for r0 in range(0, vocab, step):
+        r1 = min(vocab, r0 + step)
+        table[r0:r1] = rng.standard_normal((r1 - r0, s.d_model), dtype=np.float32)
+        table[r0:r1] *= np.float32(0.02)
+    ids = rng.integers(0, vocab, s.n_tokens, dtype=np.int64).astype(np.int32)
+    return HeadInputs(shape=s, vocab=vocab, table=_encode(table, s.w_dtype),
+                      gamma_f=_encode(gf.astype(np.float32), s.act_dtype), token_ids=ids)
+
+
 def paged_prior_cache(inp: BlockInputs, rank: int):
     """Rank ``rank``'s K and V page pools holding its owned KV heads' prior keys/values.
 

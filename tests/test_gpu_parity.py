@@ -195,6 +195,108 @@ def test_block_stack_parity(s, k):
         _ = (st.x.float() * 2).sum().item()  # eager work between replays
 
 
+BY_NAME = {x.name: x for x in SHAPES}
+HEAD_SHAPES = {"f32": BY_NAME["med-fp32-g2"], "bf16": MED, "q8_0": BY_NAME["med-q8-n4"]}
+
+
+@pytest.mark.parametrize("wt", ["f32", "bf16", "q8_0"])
+def test_embedding_lookup_bit_exact(wt):
+    """Rows of the packed table as the activation dtype stores them (Q8_0: dequantised, one
+    rounding to bf16), bit for bit; ids outside [0, vocab) clamp to the first / last row."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import DeviceHead, to_host
+    from tensor_transformer_block_amd.inputs import make_head_inputs
+    s = HEAD_SHAPES[wt].with_(n_tokens=7, kv_lens=(4,) * 7)
+    head = make_head_inputs(s, vocab=1531, seed=3)
+    head.token_ids[:4] = [0, 1530, -5, 1531 + 3]
+    dh = DeviceHead(head, B.make_desc(s))
+    x = torch.empty((7, s.d_model), dtype=torch.float32 if s.act_dtype == "f32" else torch.bfloat16,
+                    device="cuda")
+    dh.embed(x)
+    torch.cuda.synchronize()
+    clamped = type(head)(**{**head.__dict__, "token_ids": np.clip(head.token_ids, 0, 1530)})
+    ref = oracle.embed_lookup(clamped)
+    got = oracle.to_f64(to_host(x, s.act_dtype), s.act_dtype)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wt,T,vocab", [("f32", 1, 1531), ("f32", 5, 1531), ("bf16", 1, 1531),
+                                        ("bf16", 3, 1531), ("bf16", 21, 1531), ("bf16", 100, 1531),
+                                        ("bf16", 21, 20011), ("bf16", 64, 20011), ("q8_0", 1, 1531),
+                                        ("q8_0", 6, 1531)])
+def test_lm_head_parity(wt, T, vocab):
+    """Logits of the GEMV (few tokens, groups of four beyond that) and of the bf16 matrix-core
+    GEMMs (more tokens; up to 64 tokens over a vocabulary wide enough to fill the chip, the
+    batched-decode GEMM writing its one tile straight into the logits) against the oracle on the
+    same normed input, with ragged vocabulary edges."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import DeviceHead, to_device
+    from tensor_transformer_block_amd.inputs import _encode, make_head_inputs
+    s = HEAD_SHAPES[wt].with_(n_tokens=T, kv_lens=(4,) * T)
+    head = make_head_inputs(s, vocab=vocab, seed=4)
+    dh = DeviceHead(head, B.make_desc(s))
+    xn32 = np.random.default_rng(T).standard_normal((T, s.d_model)).astype(np.float32)
+    xs = _encode(xn32, s.act_dtype)
+    out = torch.full((T, vocab), float("nan"), device="cuda")
+    dh.logits(to_device(xs, s.act_dtype, "cuda"), out)
+    torch.cuda.synchronize()
+    ref = oracle.lm_head(oracle.to_f64(xs, s.act_dtype), oracle.head_table_f64(head))
+    e = nrel(t2np(out), ref)
+    log(f"lm head {wt} T={T} vocab={vocab}: err {e:.3e}")
+    assert e <= {"f32": 1e-4, "bf16": 2e-2, "q8_0": 2e-2}[wt]
+
+
+MODEL_STEPS = [(CONFIGS["tiny-llama-fp32"], 2, 512), (MED, 2, 3000), (BY_NAME["med-q8-n4"], 2, 2048),
+               (CONFIGS["llama3-8b-decode"], 1, 128256)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s,k,vocab", MODEL_STEPS, ids=lambda v: getattr(v, "name", str(v)))
+def test_model_step_parity(s, k, vocab):
+    """Embedding, a stack of k blocks, final RMSNorm and LM head: the embedded input bit for bit,
+    the logits against the oracle's LM head on the GPU's own normed state (the head kernel) and
+    against the oracle's whole fp64 chain; a captured graph of the step replays to the same
+    bits."""
+    import oracle
+    from tensor_transformer_block_amd.block import ModelStep, to_host
+    from tensor_transformer_block_amd.inputs import make_head_inputs, make_stack_inputs
+    tol = {"f32": 1e-4, "bf16": 2e-2}[s.act_dtype]
+    log(f"model step {s.name} x{k} vocab {vocab}: generating inputs")
+    head = make_head_inputs(s, vocab=vocab, seed=31)
+    inps = make_stack_inputs(s, k, seed=31)
+    ms = ModelStep(head, inps)
+    ms.step()
+    torch.cuda.synchronize()
+    ref = oracle.run_model(head, inps)
+    x = oracle.to_f64(to_host(ms.x, s.act_dtype), s.act_dtype)
+    assert np.array_equal(x, ref["x"])
+    table = oracle.head_table_f64(head)
+    xn_f = oracle.to_f64(to_host(ms.xn_f, s.act_dtype), s.act_dtype)
+    e_head = nrel(t2np(ms.logits), oracle.lm_head(xn_f, table))
+    e_all = nrel(t2np(ms.logits), ref["logits"])
+    log(f"  logits: head err {e_head:.3e}, whole chain err {e_all:.3e} (tol {tol:.0e})")
+    assert e_head <= tol and e_all <= tol
+    eager = ms.logits.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ms.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        ms.step()
+    for i in range(2):
+        ms.logits.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ms.logits, eager), f"replay {i}"
+        _ = (ms.x.float() * 2).sum().item()
+
+
 @pytest.mark.parametrize("name", ["tiny-llama-fp32", "llama3-8b-batched", "gemma-q8-decode",
                                   "med-q8-n4"])
 def test_shard_maps_bit_exact(name):

@@ -567,3 +567,83 @@ def test_planted_stack_chaining_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "run_stack", wrong_stack)
     with pytest.raises(AssertionError):
         test_stack_identity_blocks(STACK_SHAPES[0])
+
+
+# ----------------------------------------------------------------------------- the replicated head
+
+HEAD_SHAPES = [TINY.with_(name="tiny-head-f32", index=130, kv_lens=(3, 2), n_tokens=2),
+               TINY.with_(name="tiny-head-bf16", index=131, w_dtype="bf16", act_dtype="bf16",
+                          mode="prefill", kv_lens=(5,), n_tokens=5),
+               BlockShape(name="small-head-q8", index=132, d_model=64, n_heads=4, n_kv_heads=2,
+                          head_dim=16, ffn_dim=128, tp=2, w_dtype="q8_0", act_dtype="bf16",
+                          ffn_act="gelu_tanh", mode="decode", kv_lens=(9, 4, 1), n_tokens=3)]
+
+
+def torch_head_table(head):
+    s = head.shape
+    return torch_decode_storage(head.table, s.w_dtype, (head.vocab, s.d_model))
+
+
+@pytest.mark.parametrize("s", HEAD_SHAPES, ids=lambda s: s.name)
+def test_embedding_lookup_against_library(s):
+    """Rows picked by torch's embedding routine from the table as torch decodes it; Q8_0 rows
+    rounded to bf16 by torch's own conversion (nearest even)."""
+    from tensor_transformer_block_amd.inputs import make_head_inputs
+    head = make_head_inputs(s, vocab=37, seed=2)
+    ref = F.embedding(torch.from_numpy(head.token_ids.astype(np.int64)), torch_head_table(head))
+    if s.w_dtype == "q8_0":
+        ref = ref.float().to(torch.bfloat16).double()
+    got = oracle.embed_lookup(head)
+    assert np.array_equal(got, ref.numpy())
+
+
+def test_bf16_rounding_closed_forms():
+    """Values halfway between two bf16 numbers go to the even one; others to the nearest."""
+    one = 1.0
+    ulp = 2.0 ** -7                       # bf16 spacing in [1, 2)
+    cases = {one + ulp / 2: one, one + 3 * ulp / 2: one + 2 * ulp, one + ulp / 4: one,
+             one + 3 * ulp / 4: one + ulp, -(one + ulp / 2): -one, 0.0: 0.0,
+             3.0 * 2.0 ** -130: 3.0 * 2.0 ** -130}   # subnormal with 2 significant bits: exact
+    for v, want in cases.items():
+        assert oracle.round_to_bf16(np.array([v]))[0] == want, v
+
+
+@pytest.mark.parametrize("s", HEAD_SHAPES, ids=lambda s: s.name)
+def test_lm_head_against_library(s):
+    from tensor_transformer_block_amd.inputs import make_head_inputs
+    head = make_head_inputs(s, vocab=41, seed=3)
+    xn = np.random.default_rng(0).standard_normal((4, s.d_model))
+    ref = F.linear(torch.from_numpy(xn), torch_head_table(head)).numpy()
+    assert nrel(oracle.lm_head(xn, oracle.head_table_f64(head)), ref) <= 1e-13
+
+
+@pytest.mark.parametrize("s", HEAD_SHAPES, ids=lambda s: s.name)
+def test_model_step_against_library_chain(s):
+    """Embedding, a stack of two blocks, final RMSNorm and LM head against torch library
+    routines chained the same way."""
+    from tensor_transformer_block_amd.inputs import make_head_inputs, make_stack_inputs
+    head = make_head_inputs(s, vocab=53, seed=5)
+    inps = make_stack_inputs(s, 2, seed=5)
+    res = oracle.run_model(head, inps)
+    W = torch_head_table(head)
+    x = F.embedding(torch.from_numpy(head.token_ids.astype(np.int64)), W)
+    if s.w_dtype == "q8_0":
+        x = x.float().to(torch.bfloat16).double()
+    for inp in inps:
+        x = torch_block(inp, x=x)["out"]
+    xn = F.rms_norm(x, (s.d_model,), torch_decode_storage(head.gamma_f, s.act_dtype),
+                    eps=s.rms_eps)
+    assert nrel(res["logits"], F.linear(xn, W).numpy()) <= 1e-12
+
+
+def test_planted_untransposed_head_is_caught(monkeypatch):
+    """An LM head that multiplies by the table's first d rows instead of its transpose trips the
+    library pin (square table so the shapes still fit)."""
+    s = HEAD_SHAPES[0]
+    monkeypatch.setattr(oracle, "lm_head", lambda xn, t: xn @ t[: t.shape[1]])
+    with pytest.raises(AssertionError):
+        from tensor_transformer_block_amd.inputs import make_head_inputs
+        head = make_head_inputs(s, vocab=s.d_model, seed=3)
+        xn = np.random.default_rng(0).standard_normal((4, s.d_model))
+        ref = F.linear(torch.from_numpy(xn), torch_head_table(head)).numpy()
+        assert nrel(oracle.lm_head(xn, oracle.head_table_f64(head)), ref) <= 1e-13
