@@ -588,6 +588,14 @@ static hipError_t splitk_epilogue(int epi, int actf, const float* part, int S, i
   return hipGetLastError();
 }
 
+hipError_t launch_splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
+                                  void* C, int ldc, hipStream_t st) {
+  const bool v4 =
+      N % 4 == 0 && ldc % 4 == 0 && (uintptr_t)C % 16 == 0 && (uintptr_t)part % 16 == 0;
+  return v4 ? splitk_epilogue<true>(epi, actf, part, S, M, N, C, ldc, st)
+            : splitk_epilogue<false>(epi, actf, part, S, M, N, C, ldc, st);
+}
+
 // Split count for the split-K variants: enough workgroups to cover the chip, K ranges a multiple
 // of the 128-wide stage and at least 256 long. The direct-to-LDS form (K % 64 == 0) holds one
 // workgroup per CU (its ring takes most of the LDS), so it stays within one round of 256.
@@ -658,10 +666,7 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
     *parts_only = S;
     return hipSuccess;
   }
-  const bool v4 =
-      N % 4 == 0 && ldc % 4 == 0 && (uintptr_t)C % 16 == 0 && (uintptr_t)part % 16 == 0;
-  return v4 ? splitk_epilogue<true>(epi, actf, part, S, M, N, C, ldc, st)
-            : splitk_epilogue<false>(epi, actf, part, S, M, N, C, ldc, st);
+  return launch_splitk_epilogue(epi, actf, part, S, M, N, C, ldc, st);
 }
 
 // Prefill GEMM with a three-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4,

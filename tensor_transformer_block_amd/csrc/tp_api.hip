@@ -163,7 +163,7 @@ void make_layout(const Dims& x, tp_shard_layout* L) {
 }
 
 struct WsLayout {
-  uint64_t qkv, q, attn, part_o, part_ml, ffn, gemm, qkvp, total;
+  uint64_t qkv, q, attn, part_o, part_ml, ffn, gemm, gemm_bytes, qkvp, total;
   int n_split, chunk, pos_limit;
 };
 
@@ -195,6 +195,10 @@ tp_status check_batch(const Dims& x, const tp_batch* b, bool need_attn) {
 bool use_gemm(const Dims& x, int T, int K) {
   return x.wt == TP_DTYPE_BF16 && T > tpk::gemv_max_tokens(K);
 }
+
+// Q8_0 projections of more than four tokens run on the matrix cores (k_gemm_q8) instead of
+// streaming the weights once per group of four tokens through the GEMV.
+bool use_q8_gemm(const Dims& x, int T) { return x.wt == TP_DTYPE_Q8_0 && T > 4; }
 
 // K ranges of the split-K QKV projection (bf16 prefill shapes too narrow to fill the chip with
 // whole-K tiles); 1: the projection runs unsplit.
@@ -231,7 +235,8 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   put(w.part_o, T * x.hq * (uint64_t)w.n_split * x.hd * 4);
   put(w.part_ml, T * x.hq * (uint64_t)w.n_split * 2 * 4);
   put(w.ffn, T * x.fr * x.ab);
-  // fp32 split-K partial tiles of the batched-decode projections (bf16 weights, 4 < T <= 64).
+  // fp32 split-K partial tiles of the batched-decode projections (bf16 weights, 4 < T <= 64)
+  // and of the Q8_0 matrix-core projections (more than four tokens, narrow shapes).
   uint64_t gemm = 0;
   if (splitk) {
     const uint64_t cand[4] = {
@@ -240,8 +245,16 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
         tpk::splitk_workspace_bytes((int)T, x.fr, x.d, true),
         tpk::splitk_workspace_bytes((int)T, x.d, x.fr, false)};
     for (uint64_t c : cand) gemm = c > gemm ? c : gemm;
+  } else if (use_q8_gemm(x, (int)T)) {
+    const uint64_t cand[4] = {
+        tpk::q8_gemm_workspace_bytes((int)T, x.qkv_rows, x.d, false),
+        tpk::q8_gemm_workspace_bytes((int)T, x.d, x.qdim, false),
+        tpk::q8_gemm_workspace_bytes((int)T, x.fr, x.d, true),
+        tpk::q8_gemm_workspace_bytes((int)T, x.d, x.fr, false)};
+    for (uint64_t c : cand) gemm = c > gemm ? c : gemm;
   }
   put(w.gemm, gemm);
+  w.gemm_bytes = gemm;
   // fp32 partial products of the split-K QKV projection.
   const uint64_t ks = (uint64_t)qkv_ksplit(x, (int)T);
   put(w.qkvp, ks > 1 ? ks * T * x.qkv_rows * 4 : 0);
@@ -258,6 +271,12 @@ struct TimedScope {
 hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, hipStream_t st,
                    const tpk::RopeEpi* rope = nullptr, float* splitk_ws = nullptr) {
+  if (use_q8_gemm(x, T) && epi != tpk::EPI_ROPE) {
+    const bool gated = epi == tpk::EPI_GATED;
+    const char* B2 = gated ? W + (size_t)gate_off * K : nullptr;
+    const char* S2 = gated ? S + (size_t)gate_off * (K / 32) * 2 : nullptr;
+    return tpk::launch_gemm_q8(epi, x.actf, T, n_out, K, X, W, S, B2, S2, Y, ldy, splitk_ws, st);
+  }
   if (use_gemm(x, T, K)) {
     const char* B2 = (epi == tpk::EPI_GATED) ? W + (size_t)gate_off * K * 2 : nullptr;
     if (T <= 64 && splitk_ws)
@@ -597,7 +616,7 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   char* ws = (char*)workspace;
   const int epi_part = x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16;
   const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
-  float* skw = w.gemm != w.total && x.wt == TP_DTYPE_BF16 && T <= 64 ? (float*)(ws + w.gemm) : nullptr;
+  float* skw = w.gemm_bytes > 0 ? (float*)(ws + w.gemm) : nullptr;
   hipError_t e;
   if (attn) {
     void* qkv = ws + w.qkv;
@@ -654,7 +673,7 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
         e = tpk::launch_gemm_qkv_rope(T, x.qkv_rows, x.d, xn, sh + L.qkv.offset, re, st);
       }
       if (e != hipSuccess) return hip_fail(e, "qkv projection");
-    } else if (use_gemm(x, T, x.d)) {
+    } else if (use_gemm(x, T, x.d) || use_q8_gemm(x, T)) {
       // Multi-token MFMA path: projection, then rotary embedding + KV append.
       {
         TimedScope ts(evb, eve);

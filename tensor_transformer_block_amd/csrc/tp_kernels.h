@@ -75,6 +75,16 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
 // Split-K projection of M <= 64 tokens; `part` holds the fp32 split tiles
 // (splitk_workspace_bytes), summed in split order by a small epilogue kernel.
 size_t splitk_workspace_bytes(int M, int N, int K, bool dual);
+// Sum of S fp32 partial tiles [S][M][N] (gated: [S][M][2N], gate then up) in split order, then the
+// epilogue into C.
+hipError_t launch_splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
+                                  void* C, int ldc, hipStream_t st);
+// Q8_0 weights (codes [N, K] int8, scales [N, K/32] fp16; gated: B2 = the up rows) for more tokens
+// than the GEMV takes; `part` (q8_gemm_workspace_bytes, may be NULL) holds split-K partial tiles.
+size_t q8_gemm_workspace_bytes(int M, int N, int K, bool dual);
+hipError_t launch_gemm_q8(int epi, int actf, int M, int N, int K, const void* A, const void* Bq,
+                          const void* Bs, const void* B2q, const void* B2s, void* C, int ldc,
+                          float* part, hipStream_t st);
 // parts_only: launch the GEMM alone, leaving the fp32 partial tiles [S][M][N] (dual: gate then
 // up per row) in `part`, and return S there; the caller then sums them.
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,

@@ -76,6 +76,23 @@ SHAPES = [
     BlockShape(name="med-bf16-g8", index=210, d_model=256, n_heads=16, n_kv_heads=2,
                head_dim=64, ffn_dim=512, tp=2, w_dtype="bf16", act_dtype="bf16",
                ffn_act="gelu_tanh", mode="decode", kv_lens=(129, 16), n_tokens=2),
+    # Q8_0 weights with more than four tokens: the matrix-core projections with per-block scales
+    # (split over K for these narrow shapes, whole-K tiles for the 300-token prefill).
+    BlockShape(name="med-q8-batched-21", index=222, d_model=512, n_heads=8, n_kv_heads=4,
+               head_dim=64, ffn_dim=1536, tp=4, w_dtype="q8_0", act_dtype="bf16",
+               ffn_act="gelu_tanh", mode="decode",
+               kv_lens=tuple(int(v) for v in np.random.default_rng(9).integers(1, 200, 21)),
+               n_tokens=21),
+    BlockShape(name="med-q8-batched-64", index=223, d_model=640, n_heads=8, n_kv_heads=2,
+               head_dim=128, ffn_dim=1280, tp=2, w_dtype="q8_0", act_dtype="bf16",
+               ffn_act="silu", mode="decode", kv_lens=tuple(range(30, 30 + 64 * 2, 2)),
+               n_tokens=64),
+    BlockShape(name="med-q8-prefill-300", index=224, d_model=512, n_heads=8, n_kv_heads=2,
+               head_dim=64, ffn_dim=1536, tp=2, w_dtype="q8_0", act_dtype="bf16",
+               ffn_act="gelu_tanh", mode="prefill", kv_lens=(333,), n_tokens=300),
+    BlockShape(name="med-q8-hd256-prefill", index=225, d_model=640, n_heads=8, n_kv_heads=2,
+               head_dim=256, ffn_dim=1280, tp=2, w_dtype="q8_0", act_dtype="bf16",
+               ffn_act="gelu_tanh", mode="prefill", kv_lens=(50,), n_tokens=40),
 ]
 
 
@@ -224,7 +241,8 @@ def test_embedding_lookup_bit_exact(wt):
 @pytest.mark.parametrize("wt,T,vocab", [("f32", 1, 1531), ("f32", 5, 1531), ("bf16", 1, 1531),
                                         ("bf16", 3, 1531), ("bf16", 21, 1531), ("bf16", 100, 1531),
                                         ("bf16", 21, 20011), ("bf16", 64, 20011), ("q8_0", 1, 1531),
-                                        ("q8_0", 6, 1531)])
+                                        ("q8_0", 6, 1531), ("q8_0", 64, 1531),
+                                        ("q8_0", 130, 1531)])
 def test_lm_head_parity(wt, T, vocab):
     """Logits of the GEMV (few tokens, groups of four beyond that) and of the bf16 matrix-core
     GEMMs (more tokens; up to 64 tokens over a vocabulary wide enough to fill the chip, the
