@@ -195,13 +195,13 @@ def main():
     import torch
     from tensor_transformer_block_amd import binding as B
     from tensor_transformer_block_amd.block import DeviceBlock
-    from tensor_transformer_block_amd.inputs import CONFIGS, make_inputs
+    from tensor_transformer_block_amd.inputs import WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()  # fails loudly if the HIP library is missing
-    s = CONFIGS[args.workload]
+    s = WORKLOADS[args.workload]
     if args.blocks > 1 or args.head:
         bench_stack(args, s)
         return

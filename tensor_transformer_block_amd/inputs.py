@@ -94,6 +94,21 @@ CONFIGS = {
         kv_lens=(8192,), n_tokens=1),
 }
 
+# Further shapes for the Q8_0 matrix-core projections (more than four tokens): the Gemma-like
+# block in batched decode, and the Llama-3-8B-shaped block quantised to Q8_0 at degree 4 in
+# prefill (its row-parallel splits fall on 32-weight block boundaries at N = 4).
+EXTRA_WORKLOADS = {
+    "gemma-q8-batched": BlockShape(
+        name="gemma-q8-batched", index=5, d_model=2560, n_heads=8, n_kv_heads=2, head_dim=256,
+        ffn_dim=10240, tp=2, w_dtype="q8_0", act_dtype="bf16", ffn_act="gelu_tanh",
+        mode="decode", kv_lens=(2048,) * 64, n_tokens=64),
+    "llama3-8b-q8-prefill": BlockShape(
+        name="llama3-8b-q8-prefill", index=6, d_model=4096, n_heads=32, n_kv_heads=8,
+        head_dim=128, ffn_dim=14336, tp=4, w_dtype="q8_0", act_dtype="bf16", ffn_act="silu",
+        mode="prefill", kv_lens=(2048,), n_tokens=2048),
+}
+WORKLOADS = {**CONFIGS, **EXTRA_WORKLOADS}
+
 WEIGHT_NAMES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
 
 
@@ -241,7 +256,8 @@ def make_stack_inputs(s: BlockShape, n_blocks: int, seed: int = 0) -> list:
 
 # Vocabulary sizes of the model families the workloads are shaped after (the replicated head).
 VOCAB = {"tiny-llama-fp32": 512, "llama3-8b-decode": 128256, "llama3-8b-batched": 128256,
-         "llama-70b-prefill": 128256, "gemma-q8-decode": 262144}
+         "llama-70b-prefill": 128256, "gemma-q8-decode": 262144, "gemma-q8-batched": 262144,
+         "llama3-8b-q8-prefill": 128256}
 
 
 @dataclass

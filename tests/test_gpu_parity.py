@@ -7,7 +7,7 @@ Q8_0 dequantised values.
 import numpy as np
 import pytest
 
-from tensor_transformer_block_amd.inputs import CONFIGS, BlockShape, make_inputs
+from tensor_transformer_block_amd.inputs import CONFIGS, WORKLOADS, BlockShape, make_inputs
 
 from parity_util import log, nrel, run_and_check, t2np
 
@@ -108,23 +108,25 @@ def test_block_parity_bf16_partials():
 
 
 @pytest.mark.parametrize("name", ["tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode",
-                                  "llama3-8b-batched"])
+                                  "llama3-8b-batched", "gemma-q8-batched"])
 def test_config_parity(name):
-    s = CONFIGS[name]
+    s = WORKLOADS[name]
     log(f"{name}: generating inputs")
     inp = make_inputs(s, seed=0)
     run_and_check(inp, label=name)
 
 
 @pytest.mark.timeout(900)
-def test_config_parity_prefill_sampled():
-    """70B-shaped prefill: every row is computed on the GPU; sampled rows (first, last, a spread
-    and the tile edges) are computed by the oracle one by one."""
-    s = CONFIGS["llama-70b-prefill"]
-    log("llama-70b-prefill: generating inputs")
+@pytest.mark.parametrize("name", ["llama-70b-prefill", "llama3-8b-q8-prefill"])
+def test_config_parity_prefill_sampled(name):
+    """2048-token prefill (70B-shaped bf16 at N=8; 8B-shaped Q8_0 at N=4): every row is computed
+    on the GPU; sampled rows (first, last, a spread and the tile edges) are computed by the
+    oracle one by one."""
+    s = WORKLOADS[name]
+    log(f"{name}: generating inputs")
     inp = make_inputs(s, seed=0)
     rows = [0, 1, 63, 64, 127, 128, 1000, 1535, 2046, 2047]
-    run_and_check(inp, rows=rows, label="llama-70b-prefill (sampled rows)")
+    run_and_check(inp, rows=rows, label=f"{name} (sampled rows)")
 
 
 def test_step_matches_staged_and_graph_replay():
