@@ -227,13 +227,35 @@ def block_sharded(s, p, x, kcaches_by_rank, vcaches_by_rank, positions, token_se
     pre-rotary qkv, post-rotary q, the new K and V, the attention output a_r, m_r and both
     partial sums.
     """
+    xn, ranks, red, h1 = attention_sharded(s, p, x, kcaches_by_rank, vcaches_by_rank, positions,
+                                           token_seq, rows)
+    N = s.tp
+    act = ACTIVATIONS[s.ffn_act]
+    xn2 = rms_norm(h1, p["gamma2"], s.rms_eps)
+    for r in range(N):
+        w = ranks[r]["w"]
+        m_r = act(xn2 @ w["wg"].T) * (xn2 @ w["wu"].T)
+        ranks[r]["m"] = m_r
+        ranks[r]["p_ffn"] = m_r @ w["wd"].T
+    red2 = ranks[0]["p_ffn"].copy()
+    for r in range(1, N):
+        red2 = red2 + ranks[r]["p_ffn"]
+    out = h1 + red2
+    for rk in ranks:
+        del rk["w"]
+    return dict(xn=xn, h1=h1, xn2=xn2, out=out, attn_sum=red, ffn_sum=red2, ranks=ranks)
+
+
+def attention_sharded(s, p, x, kcaches_by_rank, vcaches_by_rank, positions, token_seq, rows=None):
+    """The attention half of the explicit N-rank block: xn, per-rank shares (pre-rotary qkv,
+    rotated q, new K and V, a_r, its o_proj partial, and the rank's weight slices as "w"), their
+    rank-ordered sum and h1 = x + that sum (rows restricted to ``rows``)."""
     N = s.tp
     T = x.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     hd = s.head_dim
     hq, hk = s.n_heads // N, s.n_kv_heads // N
     grp = s.n_heads // s.n_kv_heads
-    act = ACTIVATIONS[s.ffn_act]
     xn = rms_norm(x, p["gamma1"], s.rms_eps)
     ranks = []
     for r in range(N):
@@ -268,19 +290,7 @@ def block_sharded(s, p, x, kcaches_by_rank, vcaches_by_rank, positions, token_se
     for r in range(1, N):
         red = red + ranks[r]["p_attn"]
     h1 = x[rows] + red
-    xn2 = rms_norm(h1, p["gamma2"], s.rms_eps)
-    for r in range(N):
-        w = ranks[r]["w"]
-        m_r = act(xn2 @ w["wg"].T) * (xn2 @ w["wu"].T)
-        ranks[r]["m"] = m_r
-        ranks[r]["p_ffn"] = m_r @ w["wd"].T
-    red2 = ranks[0]["p_ffn"].copy()
-    for r in range(1, N):
-        red2 = red2 + ranks[r]["p_ffn"]
-    out = h1 + red2
-    for rk in ranks:
-        del rk["w"]
-    return dict(xn=xn[rows], h1=h1, xn2=xn2, out=out, attn_sum=red, ffn_sum=red2, ranks=ranks)
+    return xn[rows], ranks, red, h1
 
 
 def rank_caches(s, kcache, vcache):
@@ -379,3 +389,96 @@ def run_model(head, inputs, sharded=True):
     stack = run_stack(inputs, sharded=sharded, x=x)
     xn_f = rms_norm(stack[-1]["out"], to_f64(head.gamma_f, s.act_dtype), s.rms_eps)
     return dict(x=x, stack=stack, xn_f=xn_f, logits=lm_head(xn_f, table))
+
+
+# ----------------------------------------------------------------------------- mixture of experts
+# TensorSharp, "Multi-GPU & Multi-Node", section "Supported architectures": in the expert-sliced
+# sharding the Megatron split goes inside every expert (gate/up column-parallel, down row-
+# parallel), every rank holds 1/N of every expert's weights and the router is replicated, so a
+# token's selected expert ids (distinct within the token) mean the same on every rank.
+
+
+def moe_params_f64(minp) -> dict:
+    """Router [E, d] and the experts' gate/up [E, F_e, d] and down [E, d, F_e] in float64."""
+    s, m = minp.shape, minp.moe
+    E, F, d = m.n_experts, m.expert_ffn, s.d_model
+    return dict(router=to_f64(minp.router, s.act_dtype, (E, d)),
+                wg=to_f64(minp.wg, s.w_dtype, (E * F, d)).reshape(E, F, d),
+                wu=to_f64(minp.wu, s.w_dtype, (E * F, d)).reshape(E, F, d),
+                wd=to_f64(minp.wd, s.w_dtype, (E * d, F)).reshape(E, d, F))
+
+
+def moe_select(logits: np.ndarray, top_k: int):
+    """Per token: the top_k experts by router logit, largest first (equal logits: lower expert
+    index first), and their weights, the softmax of the selected logits."""
+    T, E = logits.shape
+    ids = np.zeros((T, top_k), dtype=np.int64)
+    w = np.zeros((T, top_k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:top_k]
+        ids[t] = order
+        sel = logits[t, order]
+        ex = np.exp(sel - np.max(sel))
+        w[t] = ex / np.sum(ex)
+    return ids, w
+
+
+def moe_route(xn2: np.ndarray, router: np.ndarray, top_k: int):
+    """Router logits xn2 . router^T, then ``moe_select``."""
+    z = xn2 @ router.T
+    ids, w = moe_select(z, top_k)
+    return z, ids, w
+
+
+def moe_ffn_unsharded(act, pm, xn2, ids, w):
+    """sum_j w[t, j] * FFN_{ids[t, j]}(xn2[t]) with FFN_e(v) = (act(v Wg_e^T) * (v Wu_e^T)) Wd_e^T."""
+    out = np.zeros((xn2.shape[0], pm["wd"].shape[1]))
+    for t in range(xn2.shape[0]):
+        for j, e in enumerate(ids[t]):
+            m = act(xn2[t] @ pm["wg"][e].T) * (xn2[t] @ pm["wu"][e].T)
+            out[t] += w[t, j] * (m @ pm["wd"][e].T)
+    return out
+
+
+def moe_ffn_sharded(s, moe, pm, xn2, ids, w):
+    """Rank r's partial: its slice F_r of every selected expert's gate/up columns and down rows,
+    sum_j w[t, j] * (act(xn2 Wg_e[F_r]^T) * (xn2 Wu_e[F_r]^T)) Wd_e[:, F_r]^T. Returns the
+    per-rank partials and activations."""
+    N = s.tp
+    fr = moe.expert_ffn // N
+    act = ACTIVATIONS[s.ffn_act]
+    parts, ms = [], []
+    for r in range(N):
+        cols = slice(r * fr, (r + 1) * fr)
+        part = np.zeros((xn2.shape[0], s.d_model))
+        mr = np.zeros((xn2.shape[0], len(ids[0]), fr))
+        for t in range(xn2.shape[0]):
+            for j, e in enumerate(ids[t]):
+                m = act(xn2[t] @ pm["wg"][e][cols].T) * (xn2[t] @ pm["wu"][e][cols].T)
+                mr[t, j] = m
+                part[t] += w[t, j] * (m @ pm["wd"][e][:, cols].T)
+        parts.append(part)
+        ms.append(mr)
+    return parts, ms
+
+
+def run_moe_block(inp, minp, rows=None):
+    """The block with the MoE FFN: the explicit N-rank attention half, the reduce and RMSNorm,
+    the replicated router, every rank's MoE partial and the final reduce (rank order)."""
+    s, m = inp.shape, minp.moe
+    p = params_f64(inp)
+    pm = moe_params_f64(minp)
+    x = to_f64(inp.x, s.act_dtype)
+    kc, vc = caches_f64(inp)
+    kr, vr = rank_caches(s, kc, vc)
+    xn, ranks, red, h1 = attention_sharded(s, p, x, kr, vr, inp.positions, inp.token_seq, rows)
+    xn2 = rms_norm(h1, p["gamma2"], s.rms_eps)
+    logits, ids, w = moe_route(xn2, pm["router"], m.top_k)
+    parts, ms = moe_ffn_sharded(s, m, pm, xn2, ids, w)
+    red2 = parts[0].copy()
+    for r in range(1, s.tp):
+        red2 = red2 + parts[r]
+    for rk in ranks:
+        del rk["w"]
+    return dict(xn=xn, h1=h1, xn2=xn2, logits=logits, ids=ids, weights=w, partials=parts, m=ms,
+                ffn_sum=red2, out=h1 + red2, ranks=ranks)

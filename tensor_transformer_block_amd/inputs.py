@@ -288,6 +288,51 @@ def make_head_inputs(s: BlockShape, vocab: int, seed: int = 0) -> HeadInputs:
                       gamma_f=_encode(gf.astype(np.float32), s.act_dtype), token_ids=ids)
 
 
+@dataclass(frozen=True)
+class MoEShape:
+    """A mixture-of-experts FFN in place of the dense one: n_experts SwiGLU (or GELU-gated)
+    experts of width expert_ffn, top_k of them per token."""
+
+    n_experts: int
+    top_k: int
+    expert_ffn: int
+
+
+@dataclass
+class MoEInputs:
+    """Storage-form MoE FFN weights: the router [E, d] (activation dtype), the experts' gate and
+    up rows stacked expert-major [E * F_e, d] and their down matrices stacked [E * d, F_e]
+    (weight dtype; Q8_0 blocks along the input dim)."""
+
+    shape: BlockShape
+    moe: MoEShape
+    router: np.ndarray
+    wg: np.ndarray
+    wu: np.ndarray
+    wd: np.ndarray
+
+
+def make_moe_inputs(s: BlockShape, moe: MoEShape, seed: int = 0, block: int = 0) -> MoEInputs:
+    """Draws from ``[seed, index, 2^21, block]``: router, then every expert's gate rows, up rows
+    and down matrix, all 0.02 N."""
+    rng = np.random.default_rng([seed, s.index, 1 << 21, block])
+    E, F, d = moe.n_experts, moe.expert_ffn, s.d_model
+
+    def draw(rows, cols, dtype):
+        a = np.empty((rows, cols), dtype=np.float32)
+        step = max(1, (1 << 24) // cols)
+        for r0 in range(0, rows, step):
+            r1 = min(rows, r0 + step)
+            a[r0:r1] = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+            a[r0:r1] *= np.float32(0.02)
+        return _encode(a, dtype)
+    router = draw(E, d, s.act_dtype)
+    wg = draw(E * F, d, s.w_dtype)
+    wu = draw(E * F, d, s.w_dtype)
+    wd = draw(E * d, F, s.w_dtype)
+    return MoEInputs(shape=s, moe=moe, router=router, wg=wg, wu=wu, wd=wd)
+
+
 def paged_prior_cache(inp: BlockInputs, rank: int):
     """Rank ``rank``'s K and V page pools holding its owned KV heads' prior keys/values.
 

@@ -647,3 +647,107 @@ def test_planted_untransposed_head_is_caught(monkeypatch):
         xn = np.random.default_rng(0).standard_normal((4, s.d_model))
         ref = F.linear(torch.from_numpy(xn), torch_head_table(head)).numpy()
         assert nrel(oracle.lm_head(xn, oracle.head_table_f64(head)), ref) <= 1e-13
+
+
+# ----------------------------------------------------------------------------- mixture of experts
+
+from tensor_transformer_block_amd.inputs import MoEShape, make_moe_inputs  # noqa: E402
+
+MOE_CASES = [(TINY.with_(name="tiny-moe", index=140, kv_lens=(3, 2), n_tokens=2),
+              MoEShape(n_experts=6, top_k=2, expert_ffn=4)),
+             (TINY.with_(name="tiny-moe-bf16", index=141, w_dtype="bf16", act_dtype="bf16",
+                         ffn_act="gelu_tanh", mode="prefill", kv_lens=(5,), n_tokens=3),
+              MoEShape(n_experts=5, top_k=3, expert_ffn=6)),
+             (BlockShape(name="small-moe-q8", index=142, d_model=64, n_heads=4, n_kv_heads=2,
+                         head_dim=16, ffn_dim=128, tp=2, w_dtype="q8_0", act_dtype="bf16",
+                         ffn_act="silu", mode="decode", kv_lens=(7, 3), n_tokens=2),
+              MoEShape(n_experts=4, top_k=2, expert_ffn=64))]
+
+
+def test_moe_select_against_library_and_ties():
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((5, 9))
+    ids, w = oracle.moe_select(z, 4)
+    ref_ids = np.argsort(-z, axis=1, kind="stable")[:, :4]
+    assert np.array_equal(ids, ref_ids)
+    ref_w = torch.softmax(torch.from_numpy(np.take_along_axis(z, ref_ids, 1)), dim=1).numpy()
+    assert nrel(w, ref_w) <= 1e-15
+    # equal logits: the lower expert index first; equal weights
+    ids, w = oracle.moe_select(np.array([[1.0, 3.0, 3.0, 0.0]]), 2)
+    assert ids.tolist() == [[1, 2]] and np.allclose(w, [[0.5, 0.5]], rtol=0, atol=1e-15)
+    # every expert selected: the weights are the softmax over all logits, in logit order
+    ids, w = oracle.moe_select(z[:1], 9)
+    assert nrel(np.sort(w[0]), np.sort(torch.softmax(torch.from_numpy(z[0]), 0).numpy())) <= 1e-15
+
+
+def _torch_moe_ffn(s, minp, xn2):
+    """Routing with torch.topk / torch.softmax and every selected expert's FFN with F.linear."""
+    m = minp.moe
+    E, F_, d = m.n_experts, m.expert_ffn, s.d_model
+    R = torch_decode_storage(minp.router, s.act_dtype)
+    Wg = torch_decode_storage(minp.wg, s.w_dtype, (E * F_, d)).view(E, F_, d)
+    Wu = torch_decode_storage(minp.wu, s.w_dtype, (E * F_, d)).view(E, F_, d)
+    Wd = torch_decode_storage(minp.wd, s.w_dtype, (E * d, F_)).view(E, d, F_)
+    x = torch.from_numpy(xn2)
+    vals, idx = torch.topk(F.linear(x, R), m.top_k, dim=1)
+    w = torch.softmax(vals, dim=1)
+    act = F.silu if s.ffn_act == "silu" else (lambda z: F.gelu(z, approximate="tanh"))
+    out = torch.zeros(x.shape[0], d, dtype=torch.float64)
+    for t in range(x.shape[0]):
+        for j in range(m.top_k):
+            e = int(idx[t, j])
+            out[t] += w[t, j] * F.linear(act(F.linear(x[t], Wg[e])) * F.linear(x[t], Wu[e]), Wd[e])
+    return idx.numpy(), out.numpy()
+
+
+@pytest.mark.parametrize("s,moe", MOE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_moe_ffn_against_library(s, moe):
+    minp = make_moe_inputs(s, moe, seed=1)
+    pm = oracle.moe_params_f64(minp)
+    xn2 = np.random.default_rng(2).standard_normal((3, s.d_model))
+    _, ids, w = oracle.moe_route(xn2, pm["router"], moe.top_k)
+    ref_ids, ref = _torch_moe_ffn(s, minp, xn2)
+    assert np.array_equal(ids, ref_ids)
+    out = oracle.moe_ffn_unsharded(oracle.ACTIVATIONS[s.ffn_act], pm, xn2, ids, w)
+    assert nrel(out, ref) <= 1e-12
+
+
+@pytest.mark.parametrize("s,moe", MOE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_moe_sharded_equals_unsharded(s, moe):
+    """Expert slicing: the rank partials (each rank's slice of every selected expert) add up to
+    the unsharded expert mixture."""
+    minp = make_moe_inputs(s, moe, seed=3)
+    pm = oracle.moe_params_f64(minp)
+    xn2 = np.random.default_rng(4).standard_normal((4, s.d_model))
+    _, ids, w = oracle.moe_route(xn2, pm["router"], moe.top_k)
+    parts, _ = oracle.moe_ffn_sharded(s, moe, pm, xn2, ids, w)
+    ref = oracle.moe_ffn_unsharded(oracle.ACTIVATIONS[s.ffn_act], pm, xn2, ids, w)
+    assert nrel(sum(parts[1:], parts[0]), ref) <= 1e-12
+
+
+@pytest.mark.parametrize("s,moe", MOE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_moe_block_against_unsharded_composition(s, moe):
+    """The MoE block (sharded attention, replicated router, sliced experts) against the unsharded
+    block's h1 followed by the library MoE FFN."""
+    inp = make_inputs(s, seed=5)
+    minp = make_moe_inputs(s, moe, seed=5)
+    res = oracle.run_moe_block(inp, minp)
+    h1 = torch_block(inp)["h1"].numpy()
+    xn2 = F.rms_norm(torch.from_numpy(h1), (s.d_model,),
+                     torch_decode_storage(inp.gamma2, s.act_dtype), eps=s.rms_eps).numpy()
+    ids, ffn = _torch_moe_ffn(s, minp, xn2)
+    assert np.array_equal(res["ids"], ids)
+    assert nrel(res["out"], h1 + ffn) <= 1e-12
+
+
+def test_planted_moe_unnormalised_weights_are_caught(monkeypatch):
+    """Top-k weights taken from a softmax over all experts (not renormalised) trip the library
+    pin."""
+    def wrong(logits, top_k):
+        ids = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        return ids, np.take_along_axis(p, ids, 1)
+    monkeypatch.setattr(ob, "moe_select", wrong)
+    with pytest.raises(AssertionError):
+        test_moe_ffn_against_library(*MOE_CASES[0])
