@@ -24,6 +24,11 @@
  *              rank, so they add no collective.
  *   [ML-OOS]   mlxcel issue #488, section "Out of scope": embeddings and LM head stay replicated
  *              (a vocabulary-parallel split is left out).
+ *   [TS-MOE]   TensorSharp, section "Supported architectures": expert slicing puts the Megatron
+ *              split inside every expert (gate/up column-parallel, down row-parallel), so every
+ *              rank holds 1/N of every expert with a replicated router and a token's selected
+ *              expert ids (distinct within the token) are valid on every rank; section
+ *              "Requirements & constraints": MoE models run per sequence under tensor parallelism.
  *
  * Conventions for every call:
  *   - All tensors are caller-owned device memory unless stated. The library allocates nothing,
@@ -222,6 +227,71 @@ tp_status tp_embed_lookup(const tp_block_desc* desc, int32_t vocab, const void* 
  * with more tokens runs the matrix-core GEMM. n_tokens == 0 is a no-op. */
 tp_status tp_lm_head(const tp_block_desc* desc, int32_t vocab, const void* head, const void* xn,
                      int32_t n_tokens, float* logits, void* stream);
+
+/* ---- expert-sliced mixture-of-experts FFN half [TS-MOE] ----
+ * Replaces the dense FFN half: n_experts experts of width expert_ffn, each gated like the dense
+ * FFN (desc->ffn_act), top_k of them per token (1 <= top_k <= min(n_experts, 16),
+ * n_experts <= 1024). expert_ffn must divide by tp_degree, expert_ffn / tp_degree by 8, and for
+ * Q8_0 expert_ffn by 32 * tp_degree (the row-parallel down split on block boundaries [TS-REQ]).
+ * desc->ffn_dim is not used by these calls. */
+typedef struct {
+  int32_t n_experts, top_k, expert_ffn;
+} tp_moe_desc;
+
+/* Full expert weights, device, w_dtype as tp_full_weights: wg and wu [n_experts * expert_ffn, d]
+ * (expert-major rows), wd [n_experts * d, expert_ffn]. */
+typedef struct {
+  const void *wg, *wu, *wd;
+} tp_moe_full_weights;
+
+/* Rank r's expert shard, 256-byte aligned regions: gate and up [n_experts][expert_ffn/N][d] (the
+ * rank's gate and up rows of every expert), down [n_experts][d][expert_ffn/N] (its columns of every
+ * expert's down rows); Q8_0 code planes, with the fp16 scale planes in *_scale. payload_bytes is
+ * exactly 1/N of the experts' weight bytes (the router is replicated, not sharded). */
+typedef struct {
+  tp_region gate, up, down, gate_scale, up_scale, down_scale;
+  uint64_t payload_bytes, alloc_bytes;
+} tp_moe_layout;
+
+tp_status tp_moe_shard_size(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                            tp_moe_layout* out);
+
+/* Pack rank r's expert slices from the full expert weights into `dst` (device). */
+tp_status tp_moe_shard_weights(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                               const tp_moe_full_weights* src, void* dst, uint64_t dst_bytes,
+                               void* stream);
+
+/* The replicated router, computed once for all ranks: logits [T, n_experts] (fp32) =
+ * xn . router^T with router [n_experts, d] in the activation dtype; then per token the top_k
+ * experts by logit, largest first (equal logits: lower index first), into topk_ids [T, top_k]
+ * (int32), and their weights, the softmax of the selected logits, into topk_weights [T, top_k]
+ * (fp32). n_tokens == 0 is a no-op. */
+tp_status tp_moe_route(const tp_block_desc* desc, const tp_moe_desc* moe, const void* router,
+                       const void* xn, int32_t n_tokens, float* logits, int32_t* topk_ids,
+                       float* topk_weights, void* stream);
+
+/* Workspace bytes of tp_moe_shard_forward for n_tokens tokens. */
+tp_status tp_moe_workspace_size(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                int32_t n_tokens, uint64_t* bytes);
+
+/* Rank r's MoE FFN half: for every token t and selected expert j (e = topk_ids[t, j]),
+ * m = act(xn[t] . Wg_e[F_r]^T) * (xn[t] . Wu_e[F_r]^T) over the rank's slice F_r of the expert,
+ * partial_out[t] = sum_j topk_weights[t, j] * (m . Wd_e[:, F_r]^T) ([T, d], partial_dtype). Expert
+ * ids outside [0, n_experts) are clamped. n_tokens == 0 is a no-op. */
+tp_status tp_moe_shard_forward(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                               const void* shard, const void* xn, int32_t n_tokens,
+                               const int32_t* topk_ids, const float* topk_weights,
+                               void* partial_out, void* workspace, uint64_t workspace_bytes,
+                               void* stream);
+
+/* Measurement variant: ev_begin / ev_end span the two expert kernels, as for
+ * tp_block_shard_forward_timed. Not for graph capture. */
+tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                     int32_t rank, const void* shard, const void* xn,
+                                     int32_t n_tokens, const int32_t* topk_ids,
+                                     const float* topk_weights, void* partial_out,
+                                     void* workspace, uint64_t workspace_bytes, void* stream,
+                                     void* ev_begin, void* ev_end);
 
 const char* tp_status_str(tp_status status);
 /* Detail of the calling thread's last failure ("" if none). */

@@ -29,7 +29,8 @@ EXPORTED = (
     "tp_rope_table_init", "tp_block_shard_forward", "tp_partial_reduce", "tp_status_str",
     "tp_last_error", "tp_shard_unpack", "tp_dequant_q8_0", "tp_workspace_offsets",
     "tp_block_shard_forward_timed", "tp_head_size", "tp_head_pack", "tp_embed_lookup",
-    "tp_lm_head",
+    "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
+    "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
 )
 
 
@@ -53,6 +54,20 @@ class tp_shard_layout(ctypes.Structure):
 class tp_head_layout(ctypes.Structure):
     _fields_ = [("table", tp_region), ("table_scale", tp_region),
                 ("payload_bytes", ctypes.c_uint64), ("alloc_bytes", ctypes.c_uint64)]
+
+
+class tp_moe_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_experts", "top_k", "expert_ffn")]
+
+
+class tp_moe_full_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("wg", "wu", "wd")]
+
+
+class tp_moe_layout(ctypes.Structure):
+    _fields_ = [(n, tp_region) for n in (
+        "gate", "up", "down", "gate_scale", "up_scale", "down_scale")] + [
+        ("payload_bytes", ctypes.c_uint64), ("alloc_bytes", ctypes.c_uint64)]
 
 
 class tp_full_weights(ctypes.Structure):
@@ -107,6 +122,12 @@ def lib() -> ctypes.CDLL:
         "tp_head_pack": [P, I32, P, P, U64, P],
         "tp_embed_lookup": [P, I32, P, P, I32, P, P],
         "tp_lm_head": [P, I32, P, P, I32, P, P],
+        "tp_moe_shard_size": [P, P, I32, P],
+        "tp_moe_shard_weights": [P, P, I32, P, P, U64, P],
+        "tp_moe_route": [P, P, P, P, I32, P, P, P, P],
+        "tp_moe_workspace_size": [P, P, I32, P],
+        "tp_moe_shard_forward": [P, P, I32, P, P, I32, P, P, P, P, U64, P],
+        "tp_moe_shard_forward_timed": [P, P, I32, P, P, I32, P, P, P, P, U64, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -267,6 +288,59 @@ def tp_embed_lookup(desc, vocab, head, token_ids, n_tokens, x_out, stream=None) 
 def tp_lm_head(desc, vocab, head, xn, n_tokens, logits, stream=None) -> None:
     _check(lib().tp_lm_head(ctypes.byref(desc), vocab, ptr(head), ptr(xn), n_tokens, ptr(logits),
                             _stream(stream)))
+
+
+def make_moe_desc(moe) -> tp_moe_desc:
+    return tp_moe_desc(n_experts=moe.n_experts, top_k=moe.top_k, expert_ffn=moe.expert_ffn)
+
+
+def tp_moe_shard_size(desc, moe: tp_moe_desc, rank: int) -> tp_moe_layout:
+    out = tp_moe_layout()
+    _check(lib().tp_moe_shard_size(ctypes.byref(desc), ctypes.byref(moe), rank, ctypes.byref(out)))
+    return out
+
+
+def tp_moe_shard_weights(desc, moe, rank, src: tp_moe_full_weights, dst, dst_bytes=None,
+                         stream=None) -> None:
+    if dst_bytes is None:
+        dst_bytes = dst.numel() * dst.element_size()
+    _check(lib().tp_moe_shard_weights(ctypes.byref(desc), ctypes.byref(moe), rank,
+                                      ctypes.byref(src), ptr(dst), dst_bytes, _stream(stream)))
+
+
+def tp_moe_route(desc, moe, router, xn, n_tokens, logits, topk_ids, topk_weights,
+                 stream=None) -> None:
+    _check(lib().tp_moe_route(ctypes.byref(desc), ctypes.byref(moe), ptr(router), ptr(xn),
+                              n_tokens, ptr(logits), ptr(topk_ids), ptr(topk_weights),
+                              _stream(stream)))
+
+
+def tp_moe_workspace_size(desc, moe, n_tokens: int) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().tp_moe_workspace_size(ctypes.byref(desc), ctypes.byref(moe), n_tokens,
+                                       ctypes.byref(out)))
+    return out.value
+
+
+def tp_moe_shard_forward(desc, moe, rank, shard, xn, n_tokens, topk_ids, topk_weights,
+                         partial_out, workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().tp_moe_shard_forward(ctypes.byref(desc), ctypes.byref(moe), rank, ptr(shard),
+                                      ptr(xn), n_tokens, ptr(topk_ids), ptr(topk_weights),
+                                      ptr(partial_out), ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
+
+
+def tp_moe_shard_forward_timed(desc, moe, rank, shard, xn, n_tokens, topk_ids, topk_weights,
+                               partial_out, workspace, ev_begin, ev_end, workspace_bytes=None,
+                               stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().tp_moe_shard_forward_timed(
+        ctypes.byref(desc), ctypes.byref(moe), rank, ptr(shard), ptr(xn), n_tokens,
+        ptr(topk_ids), ptr(topk_weights), ptr(partial_out), ptr(workspace), workspace_bytes,
+        _stream(stream), ev_begin, ev_end))
 
 
 def tp_status_str(status: int) -> str:

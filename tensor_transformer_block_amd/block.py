@@ -247,3 +247,68 @@ class ModelStep:
         B.tp_partial_reduce(b0.desc, b0.T, None, 0, self.stack.out, None, self.head.gamma_f,
                             self.xn_f)
         self.head.logits(self.xn_f, self.logits)
+
+
+class MoEBlock:
+    """A block whose FFN half is the expert-sliced MoE: the dense attention half of a
+    ``DeviceBlock`` for every rank, the reduce, the replicated router (computed once), every
+    rank's MoE partial and the final reduce, all on the current stream."""
+
+    def __init__(self, inp, minp, device="cuda", partial_dtype: str = "f32", copies: int = 1):
+        s, m = inp.shape, minp.moe
+        self.attn = DeviceBlock(inp, device=device, partial_dtype=partial_dtype, copies=copies)
+        b = self.attn
+        self.moe = B.make_moe_desc(m)
+        self.m = m
+        self.router = to_device(minp.router, s.act_dtype, device)
+        full = {k: to_device(getattr(minp, k), s.w_dtype, device) for k in ("wg", "wu", "wd")}
+        src = B.tp_moe_full_weights(**{k: v.data_ptr() for k, v in full.items()})
+        self.layouts = [B.tp_moe_shard_size(b.desc, self.moe, r) for r in range(b.N)]
+        self.shards = []
+        for _ in range(copies):
+            row = []
+            for r in range(b.N):
+                buf = torch.empty(self.layouts[r].alloc_bytes, dtype=torch.uint8, device=device)
+                B.tp_moe_shard_weights(b.desc, self.moe, r, src, buf)
+                row.append(buf)
+            self.shards.append(row)
+        torch.cuda.synchronize()
+        del full
+        T = b.T
+        self.logits = torch.empty((T, m.n_experts), dtype=torch.float32, device=device)
+        self.ids = torch.empty((T, m.top_k), dtype=torch.int32, device=device)
+        self.weights = torch.empty((T, m.top_k), dtype=torch.float32, device=device)
+        self.ws_bytes = B.tp_moe_workspace_size(b.desc, self.moe, T)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    @property
+    def out(self):
+        return self.attn.out
+
+    def route(self):
+        b = self.attn
+        B.tp_moe_route(b.desc, self.moe, self.router, b.xn2, b.T, self.logits, self.ids,
+                       self.weights)
+
+    def moe_half(self, rank: int, copy: int = 0, partial=None, events=None):
+        b = self.attn
+        out = b.partials[rank] if partial is None else partial
+        if events is None:
+            B.tp_moe_shard_forward(b.desc, self.moe, rank, self.shards[copy][rank], b.xn2, b.T,
+                                   self.ids, self.weights, out, self.workspace, self.ws_bytes)
+        else:
+            B.tp_moe_shard_forward_timed(b.desc, self.moe, rank, self.shards[copy][rank], b.xn2,
+                                         b.T, self.ids, self.weights, out, self.workspace,
+                                         events[0], events[1], self.ws_bytes)
+
+    def step(self, copy: int = 0, moe_events=None):
+        b = self.attn
+        d, T, N = b.desc, b.T, b.N
+        B.tp_partial_reduce(d, T, None, 0, b.x, None, b.gamma1, b.xn)
+        for r in range(N):
+            b.attn_half(r, copy)
+        B.tp_partial_reduce(d, T, b.partials, N, b.x, b.h1, b.gamma2, b.xn2)
+        self.route()
+        for r in range(N):
+            self.moe_half(r, copy, events=None if moe_events is None else moe_events[r])
+        B.tp_partial_reduce(d, T, b.partials, N, b.h1, b.out, None, None)

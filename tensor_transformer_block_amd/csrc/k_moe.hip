@@ -1,0 +1,312 @@
+// Expert-sliced mixture-of-experts FFN for one rank (TensorSharp "Multi-GPU & Multi-Node",
+// section "Supported architectures": the Megatron split inside every expert, gate/up column-
+// parallel and down row-parallel, with a replicated router, so each rank holds 1/N of every
+// expert and a token's selected expert ids mean the same on every rank).
+//
+//   router:  logits [T, E] = xn . Wr^T (the decode GEMV), then k_moe_topk: per token the top_k
+//            experts by logit (largest first, equal logits: lower index first) and their weights,
+//            the softmax of the selected logits;
+//   gate/up: k_moe_gate_up: m[t, j*Fr + i] = act(xn[t] . Wg[e][i]) * (xn[t] . Wu[e][i]) for the
+//            token's j-th expert e, over the rank's Fr = F_e/N gate and up rows of that expert;
+//   down:    k_moe_down: partial[t, n] = sum_j w[t, j] * (m[t, j*Fr : (j+1)*Fr] . Wd[e][n]) over
+//            the rank's Fr columns of expert e's down rows.
+// The expert kernels stream only the selected experts' slices: one token's k experts are a small
+// subset of the table, so they are GEMVs over indirectly addressed rows (16-byte loads, the token
+// vector staged in LDS as fp32, dot products reduced across the wave). MoE blocks run token by
+// token (grid.y = token), as the page notes MoE models do under tensor parallelism.
+#include "k_gemv_impl.h"
+
+namespace tpk {
+
+// ---------------------------------------------------------------------------- top-k routing
+// One wave per token: each lane holds E/64 (rounded up) logits; top_k rounds of a wave-wide
+// (value, index) maximum pick the experts in order, then lane 0 takes the softmax of the
+// selected logits.
+constexpr int kMoeMaxExperts = 1024, kMoeMaxTopK = 16;
+
+__global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logits, int T, int E,
+                                                  int top_k, int32_t* __restrict__ ids,
+                                                  float* __restrict__ weights) {
+  constexpr int PER = kMoeMaxExperts / 64;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = i * 64 + lane;
+    v[i] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  bool taken[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) taken[i] = (i * 64 + lane) >= E;
+  // round r's winner is kept by lane r
+  float my_v = -INFINITY;
+  int my_i = 0;
+  for (int r = 0; r < top_k; ++r) {
+    // lane-local best untaken entry: larger value, then lower index (indices grow with i)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = i * 64 + lane;
+      if (!taken[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    // every lane now holds the winner; its owner marks it taken
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i * 64 + lane == bi) taken[i] = true;
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  // softmax of the selected logits (the first winner is their maximum)
+  const float top = __shfl(my_v, 0, 64);
+  const float ex = lane < top_k ? expf(my_v - top) : 0.f;
+  const float den = wave_sum(ex);
+  if (lane < top_k) {
+    ids[(size_t)t * top_k + lane] = my_i;
+    weights[(size_t)t * top_k + lane] = ex / den;
+  }
+}
+
+hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t* ids,
+                           float* weights, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (E < 1 || E > kMoeMaxExperts || top_k < 1 || top_k > kMoeMaxTopK || top_k > E)
+    return hipErrorInvalidValue;
+  launch(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ids, weights);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- expert GEMVs
+// Dot product of one 16-byte weight chunk with VE staged fp32 inputs.
+template <int WT>
+__device__ __forceinline__ float moe_dot(const uint4& raw, float scale, const float* xp) {
+  constexpr int VE = WFmt<WT>::VE;
+  float f[VE];
+  decode_chunk<WT>(raw, scale, f);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < VE; e += 4) {
+    const float4 xv = *(const float4*)(xp + e);
+    a = fmaf(f[e], xv.x, a);
+    a = fmaf(f[e + 1], xv.y, a);
+    a = fmaf(f[e + 2], xv.z, a);
+    a = fmaf(f[e + 3], xv.w, a);
+  }
+  return a;
+}
+
+template <int WT>
+__device__ __forceinline__ float moe_scale(const uint16_t* S, size_t row, int nblk, int chunk) {
+  if constexpr (WT == W_Q8) return f16_to_f32(S[row * nblk + (chunk >> 1)]);
+  else return 0.f;
+}
+
+// gate/up: a wave owns PW (gate, up) row pairs of the token's selected experts.
+constexpr int MOE_PW = 2;
+
+template <int WT, int AT, int ACTF>
+__global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg,
+                                                     const uint16_t* __restrict__ Sg,
+                                                     const char* __restrict__ Wu,
+                                                     const uint16_t* __restrict__ Su, int K,
+                                                     int Fr, int E, int top_k,
+                                                     const int32_t* __restrict__ ids,
+                                                     const void* __restrict__ X,
+                                                     void* __restrict__ Mout) {
+  extern __shared__ float xs[];  // [K]
+  constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.y;
+  const int nch = K / VE, nblk = K / 32;
+  const int np = top_k * Fr;
+  size_t grow[MOE_PW];
+  bool ok[MOE_PW];
+#pragma unroll
+  for (int s = 0; s < MOE_PW; ++s) {
+    const int p = (blockIdx.x * 4 + wave) * MOE_PW + s;
+    ok[s] = p < np;
+    const int pp = ok[s] ? p : 0;
+    int e = ids[(size_t)t * top_k + pp / Fr];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    grow[s] = (size_t)e * Fr + pp % Fr;
+  }
+  for (int i = tid * AV; i < K; i += 256 * AV)
+    Vec16<AT>::load((const char*)X + ((size_t)t * K + i) * (AT == ACT_F32 ? 4 : 2), xs + i);
+  __syncthreads();
+  if (!ok[0]) return;
+  float g[MOE_PW], u[MOE_PW];
+#pragma unroll
+  for (int s = 0; s < MOE_PW; ++s) g[s] = u[s] = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+    uint4 bg[MOE_PW][4], bu[MOE_PW][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * 64 + lane;
+#pragma unroll
+      for (int s = 0; s < MOE_PW; ++s) {
+        bg[s][q] = c < nch ? ld_stream16(Wg + (grow[s] * K + (size_t)c * VE) * WB)
+                           : make_uint4(0, 0, 0, 0);
+        bu[s][q] = c < nch ? ld_stream16(Wu + (grow[s] * K + (size_t)c * VE) * WB)
+                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * 64 + lane;
+      if (c >= nch) continue;
+#pragma unroll
+      for (int s = 0; s < MOE_PW; ++s) {
+        g[s] += moe_dot<WT>(bg[s][q], moe_scale<WT>(Sg, grow[s], nblk, c * VE / 16), xs + c * VE);
+        u[s] += moe_dot<WT>(bu[s][q], moe_scale<WT>(Su, grow[s], nblk, c * VE / 16), xs + c * VE);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < MOE_PW; ++s) {
+    g[s] = wave_sum(g[s]);
+    u[s] = wave_sum(u[s]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int s = 0; s < MOE_PW; ++s) {
+      const int p = (blockIdx.x * 4 + wave) * MOE_PW + s;
+      if (p < np) st_act<AT>(Mout, (size_t)t * np + p, gated<ACTF>(g[s], u[s]));
+    }
+  }
+}
+
+// down: a wave owns MOE_DR output rows; for each selected expert it streams that expert's Fr
+// columns of the rows and adds w_j times the segment's dot product with m.
+constexpr int MOE_DR = 4;
+
+template <int WT, int AT, int PT>
+__global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
+                                                  const uint16_t* __restrict__ Sd, int d, int Fr,
+                                                  int E, int top_k,
+                                                  const int32_t* __restrict__ ids,
+                                                  const float* __restrict__ wts,
+                                                  const void* __restrict__ Min,
+                                                  void* __restrict__ P) {
+  extern __shared__ float ms[];  // [top_k * Fr]
+  constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.y;
+  const int np = top_k * Fr, chF = Fr / VE, nblk = Fr / 32;
+  for (int i = tid * AV; i < np; i += 256 * AV)
+    Vec16<AT>::load((const char*)Min + ((size_t)t * np + i) * (AT == ACT_F32 ? 4 : 2), ms + i);
+  __syncthreads();
+  const int n0 = (blockIdx.x * 4 + wave) * MOE_DR;
+  if (n0 >= d) return;
+  float acc[MOE_DR];
+#pragma unroll
+  for (int s = 0; s < MOE_DR; ++s) acc[s] = 0.f;
+#pragma unroll 2
+  for (int j = 0; j < top_k; ++j) {
+    int e = ids[(size_t)t * top_k + j];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    const float wj = wts[(size_t)t * top_k + j];
+    for (int c0 = 0; c0 < chF; c0 += 64) {
+      const int c = c0 + lane;
+      uint4 b[MOE_DR];
+      size_t row[MOE_DR];
+#pragma unroll
+      for (int s = 0; s < MOE_DR; ++s) {
+        const int n = n0 + s < d ? n0 + s : d - 1;
+        row[s] = (size_t)e * d + n;
+        b[s] = c < chF ? ld_stream16(Wd + (row[s] * Fr + (size_t)c * VE) * WB)
+                       : make_uint4(0, 0, 0, 0);
+      }
+      if (c < chF) {
+#pragma unroll
+        for (int s = 0; s < MOE_DR; ++s)
+          acc[s] = fmaf(wj, moe_dot<WT>(b[s], moe_scale<WT>(Sd, row[s], nblk, c * VE / 16),
+                                        ms + j * Fr + c * VE), acc[s]);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < MOE_DR; ++s) acc[s] = wave_sum(acc[s]);
+  if (lane == 0) {
+#pragma unroll
+    for (int s = 0; s < MOE_DR; ++s) {
+      if (n0 + s >= d) continue;
+      const size_t o = (size_t)t * d + n0 + s;
+      if constexpr (PT == ACT_F32) ((float*)P)[o] = acc[s];
+      else ((uint16_t*)P)[o] = f32_to_bf16(acc[s]);
+    }
+  }
+}
+
+template <int WT, int AT>
+static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, const void* Wu,
+                              const void* Su, const void* Wd, const void* Sd, int d, int Fr, int E,
+                              int top_k, int T, const int32_t* ids, const float* wts,
+                              const void* X, void* M, void* P, hipStream_t st) {
+  const int np = top_k * Fr;
+  const dim3 gu((np + 4 * MOE_PW - 1) / (4 * MOE_PW), T), b(256);
+  const size_t lds_gu = (size_t)d * sizeof(float);
+  const char *wg = (const char*)Wg, *wu = (const char*)Wu, *wd = (const char*)Wd;
+  const uint16_t *sg = (const uint16_t*)Sg, *su = (const uint16_t*)Su, *sd = (const uint16_t*)Sd;
+  if (lds_gu > 65536) {
+    hipError_t ea = allow_lds((const void*)(actf ? k_moe_gate_up<WT, AT, 1> : k_moe_gate_up<WT, AT, 0>),
+                              (int)lds_gu);
+    if (ea != hipSuccess) return ea;
+  }
+  if (actf == 0)
+    launch((k_moe_gate_up<WT, AT, 0>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M);
+  else
+    launch((k_moe_gate_up<WT, AT, 1>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 gd((d + 4 * MOE_DR - 1) / (4 * MOE_DR), T);
+  const size_t lds_d = (size_t)np * sizeof(float);
+  if (pt == ACT_F32) {
+    if (lds_d > 65536) {
+      hipError_t ea = allow_lds((const void*)k_moe_down<WT, AT, ACT_F32>, (int)lds_d);
+      if (ea != hipSuccess) return ea;
+    }
+    launch((k_moe_down<WT, AT, ACT_F32>), gd, b, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P);
+  } else {
+    if (lds_d > 65536) {
+      hipError_t ea = allow_lds((const void*)k_moe_down<WT, AT, ACT_BF16>, (int)lds_d);
+      if (ea != hipSuccess) return ea;
+    }
+    launch((k_moe_down<WT, AT, ACT_BF16>), gd, b, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, const void* Sg,
+                          const void* Wu, const void* Su, const void* Wd, const void* Sd, int d,
+                          int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
+                          const void* X, void* M, void* P, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (wt == W_F32 && at == ACT_F32)
+    return moe_ffn_fmt<W_F32, ACT_F32>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T, ids,
+                                       wts, X, M, P, st);
+  if (wt == W_BF16 && at == ACT_BF16)
+    return moe_ffn_fmt<W_BF16, ACT_BF16>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T,
+                                         ids, wts, X, M, P, st);
+  if (wt == W_Q8 && at == ACT_BF16)
+    return moe_ffn_fmt<W_Q8, ACT_BF16>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T, ids,
+                                       wts, X, M, P, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpk

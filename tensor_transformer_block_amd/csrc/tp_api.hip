@@ -506,6 +506,217 @@ tp_status tp_lm_head(const tp_block_desc* desc, int32_t vocab, const void* head,
   return TP_OK;
 }
 
+// ---- expert-sliced MoE FFN half
+struct MoeDims {
+  int E, k, F, fr;
+};
+
+static tp_status check_moe(const tp_block_desc* desc, const tp_moe_desc* moe, Dims* x,
+                           MoeDims* m) {
+  if (tp_status s = check_desc(desc, x)) return s;
+  if (!moe) return fail(TP_ERR_INVALID_ARG, "moe is NULL");
+  if (moe->n_experts < 1 || moe->n_experts > 1024)
+    return fail(TP_ERR_INVALID_ARG, "n_experts=%d must be in [1, 1024]", moe->n_experts);
+  if (moe->top_k < 1 || moe->top_k > 16 || moe->top_k > moe->n_experts)
+    return fail(TP_ERR_INVALID_ARG, "top_k=%d must be in [1, min(n_experts, 16)]", moe->top_k);
+  if (moe->expert_ffn <= 0) return fail(TP_ERR_INVALID_ARG, "expert_ffn must be > 0");
+  if (moe->expert_ffn % x->N)
+    return fail(TP_ERR_NOT_DIVISIBLE, "expert_ffn=%d must divide by tp_degree=%d",
+                moe->expert_ffn, x->N);
+  if ((moe->expert_ffn / x->N) % 8)
+    return fail(TP_ERR_UNSUPPORTED, "expert_ffn/tp_degree=%d must be a multiple of 8",
+                moe->expert_ffn / x->N);
+  if (x->wt == TP_DTYPE_Q8_0 && moe->expert_ffn % (x->N * 32))
+    return fail(TP_ERR_QUANT_ALIGN,
+                "Q8_0 row-parallel expert down split needs expert_ffn=%d divisible by "
+                "tp_degree*32=%d",
+                moe->expert_ffn, x->N * 32);
+  *m = MoeDims{moe->n_experts, moe->top_k, moe->expert_ffn, moe->expert_ffn / x->N};
+  return TP_OK;
+}
+
+static void make_moe_layout(const Dims& x, const MoeDims& m, tp_moe_layout* L) {
+  *L = tp_moe_layout{};
+  uint64_t off = 0, payload = 0;
+  auto put = [&](tp_region& r, uint64_t rows, uint64_t cols, tp_region& sc) {
+    r.offset = off;
+    r.bytes = rows * cols * (uint64_t)x.wb;
+    off = align_up(off + r.bytes);
+    payload += r.bytes;
+    if (x.wt == TP_DTYPE_Q8_0) {
+      sc.offset = off;
+      sc.bytes = rows * (cols / 32) * 2;
+      off = align_up(off + sc.bytes);
+      payload += sc.bytes;
+    }
+  };
+  put(L->gate, (uint64_t)m.E * m.fr, x.d, L->gate_scale);
+  put(L->up, (uint64_t)m.E * m.fr, x.d, L->up_scale);
+  put(L->down, (uint64_t)m.E * x.d, m.fr, L->down_scale);
+  L->payload_bytes = payload;
+  L->alloc_bytes = off;
+}
+
+tp_status tp_moe_shard_size(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                            tp_moe_layout* out) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (!out) return fail(TP_ERR_INVALID_ARG, "out is NULL");
+  make_moe_layout(x, m, out);
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_moe_shard_weights(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                               const tp_moe_full_weights* src, void* dst, uint64_t dst_bytes,
+                               void* stream) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (!src || !src->wg || !src->wu || !src->wd || !dst)
+    return fail(TP_ERR_INVALID_ARG, "src->wg, wu, wd and dst must be non-NULL");
+  tp_moe_layout L;
+  make_moe_layout(x, m, &L);
+  if (dst_bytes < L.alloc_bytes)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "dst_bytes=%llu < alloc_bytes=%llu",
+                (unsigned long long)dst_bytes, (unsigned long long)L.alloc_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* d = (char*)dst;
+  const int64_t dm = x.d, fr = m.fr, F = m.F, E = m.E, r = rank;
+  hipError_t e = hipSuccess;
+  if (x.wt == TP_DTYPE_Q8_0) {
+    const size_t ld_in = (size_t)(dm / 32) * 34;  // one full row of d, in 34-byte blocks
+    for (int64_t ex = 0; ex < E && e == hipSuccess; ++ex) {
+      const size_t row0 = (size_t)(ex * F + r * fr);
+      e = tpk::q8_split((const char*)src->wg + row0 * ld_in, ld_in, fr, dm / 32,
+                        d + L.gate.offset + (size_t)ex * fr * dm,
+                        d + L.gate_scale.offset + (size_t)ex * fr * (dm / 32) * 2, st);
+      if (e == hipSuccess)
+        e = tpk::q8_split((const char*)src->wu + row0 * ld_in, ld_in, fr, dm / 32,
+                          d + L.up.offset + (size_t)ex * fr * dm,
+                          d + L.up_scale.offset + (size_t)ex * fr * (dm / 32) * 2, st);
+    }
+    if (e == hipSuccess)
+      e = tpk::q8_split((const char*)src->wd + (size_t)(r * fr / 32) * 34, (size_t)(F / 32) * 34,
+                        E * dm, fr / 32, d + L.down.offset, d + L.down_scale.offset, st);
+  } else {
+    const size_t wb = x.wb;
+    e = tpk::copy2d(d + L.gate.offset, fr * dm * wb, (const char*)src->wg + r * fr * dm * wb,
+                    F * dm * wb, E, fr * dm * wb, st);
+    if (e == hipSuccess)
+      e = tpk::copy2d(d + L.up.offset, fr * dm * wb, (const char*)src->wu + r * fr * dm * wb,
+                      F * dm * wb, E, fr * dm * wb, st);
+    if (e == hipSuccess)
+      e = tpk::copy2d(d + L.down.offset, fr * wb, (const char*)src->wd + r * fr * wb, F * wb,
+                      E * dm, fr * wb, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "tp_moe_shard_weights");
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_moe_route(const tp_block_desc* desc, const tp_moe_desc* moe, const void* router,
+                       const void* xn, int32_t n_tokens, float* logits, int32_t* topk_ids,
+                       float* topk_weights, void* stream) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (n_tokens == 0) return TP_OK;
+  if (!router || !xn || !logits || !topk_ids || !topk_weights)
+    return fail(TP_ERR_INVALID_ARG, "router, xn, logits, topk_ids and topk_weights must be non-NULL");
+  if (!aligned16(router) || !aligned16(xn))
+    return fail(TP_ERR_INVALID_ARG, "router and xn must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  const int wt = x.at == TP_DTYPE_F32 ? tpk::W_F32 : tpk::W_BF16;
+  hipError_t e = tpk::launch_gemv(wt, at, tpk::EPI_F32, 0, n_tokens, router, nullptr, x.d, m.E, 0,
+                                  xn, logits, m.E, nullptr, st);
+  if (e == hipSuccess) e = tpk::launch_moe_topk(logits, n_tokens, m.E, m.k, topk_ids, topk_weights, st);
+  if (e != hipSuccess) return hip_fail(e, "tp_moe_route");
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_moe_workspace_size(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                int32_t n_tokens, uint64_t* bytes) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (!bytes) return fail(TP_ERR_INVALID_ARG, "bytes is NULL");
+  const uint64_t b = (uint64_t)n_tokens * m.k * m.fr * x.ab;
+  *bytes = b > 0 ? align_up(b) : kAlign;
+  return TP_OK;
+}
+
+static tp_status moe_forward_impl(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                  int32_t rank, const void* shard, const void* xn,
+                                  int32_t n_tokens, const int32_t* topk_ids,
+                                  const float* topk_weights, void* partial_out, void* workspace,
+                                  uint64_t workspace_bytes, void* stream, hipEvent_t evb,
+                                  hipEvent_t eve) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (n_tokens == 0) {
+    g_err.clear();
+    return TP_OK;
+  }
+  if (!shard || !xn || !topk_ids || !topk_weights || !partial_out || !workspace)
+    return fail(TP_ERR_INVALID_ARG,
+                "shard, xn, topk_ids, topk_weights, partial_out and workspace must be non-NULL");
+  if (!aligned16(shard) || !aligned16(xn) || !aligned16(workspace))
+    return fail(TP_ERR_INVALID_ARG, "shard, xn and workspace must be 16-byte aligned");
+  uint64_t need = 0;
+  tp_moe_workspace_size(desc, moe, n_tokens, &need);
+  if (workspace_bytes < need)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu",
+                (unsigned long long)workspace_bytes, (unsigned long long)need);
+  tp_moe_layout L;
+  make_moe_layout(x, m, &L);
+  const char* sh = (const char*)shard;
+  const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  const int pt = x.pt == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  hipError_t e;
+  {
+    TimedScope ts(evb, eve);
+    e = tpk::launch_moe_ffn(wt, at, x.actf, pt, sh + L.gate.offset, sh + L.gate_scale.offset,
+                            sh + L.up.offset, sh + L.up_scale.offset, sh + L.down.offset,
+                            sh + L.down_scale.offset, x.d, m.fr, m.E, m.k, n_tokens, topk_ids,
+                            topk_weights, xn, workspace, partial_out, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "moe ffn");
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_moe_shard_forward(const tp_block_desc* desc, const tp_moe_desc* moe, int32_t rank,
+                               const void* shard, const void* xn, int32_t n_tokens,
+                               const int32_t* topk_ids, const float* topk_weights,
+                               void* partial_out, void* workspace, uint64_t workspace_bytes,
+                               void* stream) {
+  return moe_forward_impl(desc, moe, rank, shard, xn, n_tokens, topk_ids, topk_weights,
+                          partial_out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                     int32_t rank, const void* shard, const void* xn,
+                                     int32_t n_tokens, const int32_t* topk_ids,
+                                     const float* topk_weights, void* partial_out,
+                                     void* workspace, uint64_t workspace_bytes, void* stream,
+                                     void* ev_begin, void* ev_end) {
+  return moe_forward_impl(desc, moe, rank, shard, xn, n_tokens, topk_ids, topk_weights,
+                          partial_out, workspace, workspace_bytes, stream, (hipEvent_t)ev_begin,
+                          (hipEvent_t)ev_end);
+}
+
 tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uint64_t n_blocks,
                           void* stream) {
   if (n_blocks == 0) return TP_OK;

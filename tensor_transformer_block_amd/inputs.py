@@ -312,6 +312,17 @@ class MoEInputs:
     wd: np.ndarray
 
 
+# A mixture-of-experts block for measurement: a dense attention half (32 query / 4 KV heads of
+# 128) and 64 SwiGLU experts of width 768, 8 per token, at degree 2, decoding one token against
+# a 4096-token cache.
+MOE_WORKLOADS = {
+    "moe-decode": (BlockShape(name="moe-decode", index=7, d_model=2048, n_heads=32, n_kv_heads=4,
+                              head_dim=128, ffn_dim=768, tp=2, w_dtype="bf16", act_dtype="bf16",
+                              ffn_act="silu", mode="decode", kv_lens=(4096,), n_tokens=1),
+                   MoEShape(n_experts=64, top_k=8, expert_ffn=768)),
+}
+
+
 def make_moe_inputs(s: BlockShape, moe: MoEShape, seed: int = 0, block: int = 0) -> MoEInputs:
     """Draws from ``[seed, index, 2^21, block]``: router, then every expert's gate rows, up rows
     and down matrix, all 0.02 N."""

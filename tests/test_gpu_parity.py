@@ -317,6 +317,110 @@ def test_model_step_parity(s, k, vocab):
         _ = (ms.x.float() * 2).sum().item()
 
 
+from tensor_transformer_block_amd.inputs import MOE_WORKLOADS, MoEShape  # noqa: E402
+
+MOE_GPU = [(CONFIGS["tiny-llama-fp32"].with_(name="tiny-moe-gpu", index=230, kv_lens=(16, 5),
+                                             n_tokens=2), MoEShape(8, 2, 64)),
+           (MED.with_(name="med-moe-bf16", index=231), MoEShape(16, 4, 256)),
+           (BY_NAME["med-q8-n4"].with_(name="med-moe-q8", index=232, tp=2, n_kv_heads=2),
+            MoEShape(8, 2, 256)),
+           (MED.with_(name="med-moe-prefill", index=233, mode="prefill", kv_lens=(60,),
+                      n_tokens=40), MoEShape(16, 4, 256)),
+           MOE_WORKLOADS["moe-decode"]]
+
+
+def _moe_tol(s):
+    return {"f32": 1e-4, "bf16": 2e-2}[s.act_dtype]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s,moe", MOE_GPU, ids=lambda v: getattr(v, "name", str(v)))
+def test_moe_block_parity(s, moe):
+    """The MoE block: router logits against the oracle; the top-k selection bit for bit against
+    the oracle's rule applied to the GPU's own fp32 logits (the decision is taken in fp32 on both
+    sides) and their weights; every rank's partial against the oracle's expert slices for the
+    GPU's selection; the block output against the oracle chain; a graph replay bit-identical."""
+    import oracle
+    from tensor_transformer_block_amd.block import MoEBlock, to_host
+    from tensor_transformer_block_amd.inputs import make_moe_inputs
+    tol = _moe_tol(s)
+    log(f"moe {s.name}: generating inputs")
+    inp = make_inputs(s, seed=41)
+    minp = make_moe_inputs(s, moe, seed=41)
+    mb = MoEBlock(inp, minp)
+    mb.step()
+    torch.cuda.synchronize()
+    ref = oracle.run_moe_block(inp, minp)
+    b = mb.attn
+    xn2 = oracle.to_f64(to_host(b.xn2, s.act_dtype), s.act_dtype)
+    pm = oracle.moe_params_f64(minp)
+    z_gpu = t2np(mb.logits)
+    e_z = nrel(z_gpu, xn2 @ pm["router"].T)
+    ids_gpu = mb.ids.cpu().numpy().astype(np.int64)
+    w_gpu = t2np(mb.weights)
+    ids_ref, w_ref = oracle.moe_select(z_gpu, moe.top_k)
+    assert np.array_equal(ids_gpu, ids_ref)
+    e_w = nrel(w_gpu, w_ref)
+    parts_ref, _ = oracle.moe_ffn_sharded(s, moe, pm, xn2, ids_gpu, w_gpu)
+    chk = []
+    for r in range(s.tp):
+        chk.append(nrel(t2np(b.partials[r]), parts_ref[r]))
+    e_out = nrel(oracle.to_f64(to_host(b.out, s.act_dtype), s.act_dtype), ref["out"])
+    same = np.array_equal(ref["ids"], ids_gpu)
+    log(f"  logits {e_z:.3e}, weights {e_w:.3e}, partials {max(chk):.3e}, out {e_out:.3e} "
+        f"(tol {tol:.0e}); oracle's own selection {'matches' if same else 'differs'}")
+    assert e_z <= tol and e_w <= 1e-5 and max(chk) <= tol
+    if same:
+        assert e_out <= tol
+    eager = b.out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mb.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mb.step()
+    for i in range(2):
+        b.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.out, eager), f"replay {i}"
+
+
+def test_moe_topk_ties_and_bounds():
+    """Experts with identical router rows tie exactly; the lower index comes first. Every token
+    selects distinct experts."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import to_device
+    from tensor_transformer_block_amd.inputs import _encode
+    s = MED.with_(n_tokens=5, kv_lens=(4,) * 5)
+    moe = MoEShape(40, 6, 256)
+    rng = np.random.default_rng(5)
+    router = rng.standard_normal((40, s.d_model)).astype(np.float32) * 0.05
+    router[7] = router[3]
+    router[30] = router[3]
+    router[12] = router[21]
+    x = rng.standard_normal((5, s.d_model)).astype(np.float32)
+    x[1] = router[3] * 40  # token 1 prefers experts 3, 7 and 30 (equal logits)
+    rt = to_device(_encode(router, "bf16"), "bf16", "cuda")
+    xt = to_device(_encode(x, "bf16"), "bf16", "cuda")
+    z = torch.empty((5, 40), device="cuda")
+    ids = torch.empty((5, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((5, 6), device="cuda")
+    B.tp_moe_route(B.make_desc(s), B.make_moe_desc(moe), rt, xt, 5, z, ids, w)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.moe_select(t2np(z), 6)
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, ids_ref)
+    assert list(got[1][:3]) == [3, 7, 30]
+    assert all(len(set(row)) == 6 for row in got)
+    assert nrel(t2np(w), w_ref) <= 1e-5
+
+
 @pytest.mark.parametrize("name", ["tiny-llama-fp32", "llama3-8b-batched", "gemma-q8-decode",
                                   "med-q8-n4"])
 def test_shard_maps_bit_exact(name):
