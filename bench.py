@@ -201,6 +201,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()  # fails loudly if the HIP library is missing
+    from tensor_transformer_block_amd.inputs import MOE_WORKLOADS
+    if args.workload in MOE_WORKLOADS:
+        bench_moe(args, *MOE_WORKLOADS[args.workload])
+        return
     s = WORKLOADS[args.workload]
     if args.blocks > 1 or args.head:
         bench_stack(args, s)
@@ -507,6 +511,123 @@ def bench_stack(args, s):
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_moe(args, s, moe):
+    """A block whose FFN half is the expert-sliced MoE (dense attention half, replicated router,
+    every rank's slice of the selected experts). Cold rotation over copies of every weight and
+    cache, sized by the bytes one step touches (the selected experts, not the whole table)."""
+    import numpy as np
+    import torch
+    from tensor_transformer_block_amd.block import MoEBlock
+    from tensor_transformer_block_amd.inputs import make_inputs, make_moe_inputs
+
+    act_b = 4 if s.act_dtype == "f32" else 2
+    per = {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[s.w_dtype]
+    hd, d = s.head_dim, s.d_model
+    attn_w = ((s.n_heads + 2 * s.n_kv_heads) * hd * d + d * s.n_heads * hd) * per
+    kv = sum(s.kv_lens) * s.n_kv_heads * hd * act_b * 2
+    expert_sel = s.n_tokens * moe.top_k * 3 * moe.expert_ffn * d * per   # all ranks together
+    router = moe.n_experts * d * act_b
+    acts = 4 * s.tp * s.n_tokens * d * act_b + 4 * s.n_tokens * d * act_b
+    sb = int(attn_w + kv + expert_sel + router + acts)
+    copies = max(1, math.ceil(args.cold_bytes / sb))
+    log(f"workload {s.name} (MoE {moe.n_experts} experts, top {moe.top_k}, width "
+        f"{moe.expert_ffn}): {copies} cold copies x {sb / 1e6:.1f} MB touched per step")
+    inp = make_inputs(s, seed=args.seed)
+    minp = make_moe_inputs(s, moe, seed=args.seed)
+    mb = MoEBlock(inp, minp, copies=copies)
+    del minp
+    for c in range(copies):
+        mb.step(c)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(copies):
+            mb.step(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(multi):
+        for c in range(copies):
+            mb.step(c)
+    torch.cuda.synchronize()
+
+    def run_steps(k):
+        for _ in range(max(1, k // copies)):
+            multi.replay()
+        return max(1, k // copies) * copies
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record()
+    n = run_steps(args.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / n
+
+    # The dominant kernels: one rank's expert FFN (gate/up and down over the selected experts),
+    # timed inside eager MoE steps behind a backlog of replays.
+    n_st = max(1, (args.kernel_iters + s.tp - 1) // s.tp)
+    hev = HipEvents(2 * n_st * s.tp)
+    for _ in range(min(16, args.steps)):
+        multi.replay()
+    for i in range(n_st):
+        mb.step(i % copies, moe_events=[(hev.ev[2 * (i * s.tp + r)], hev.ev[2 * (i * s.tp + r) + 1])
+                                        for r in range(s.tp)])
+    torch.cuda.synchronize()
+    kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(n_st * s.tp)]))
+    hev.close()
+    ub = int(s.n_tokens * moe.top_k * 3 * (moe.expert_ffn // s.tp) * d * per
+             + s.n_tokens * d * act_b * 2 + s.n_tokens * moe.top_k * (moe.expert_ffn // s.tp) * act_b * 2)
+    roof = {"bound": "hbm", "achieved": round(ub / kavg / 1e9, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "expert FFN of one rank (gate/up + down over the selected experts)"
+    roof["avg_us"] = round(kavg * 1e6, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        log(f"cpu baseline: oracle MoE block for ~{args.cpu_seconds:.0f} s")
+        minp = make_moe_inputs(s, moe, seed=args.seed)
+        k, t0 = 0, time.perf_counter()
+        while True:
+            oracle.run_moe_block(inp, minp)
+            k += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        cpu = {"value": round(k * s.n_tokens / el, 4), "unit": "tokens/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{k} full MoE block steps (all {s.tp} ranks); {el:.1f} s wall, fp64 NumPy"}
+
+    step_gbs = sb / (ms / 1e3) / 1e9
+    line = {
+        "metric": "shard decode tokens/s + achieved HBM GB/s (% of peak); prefill MFMA % peak",
+        "value": round(s.n_tokens / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": n, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": s.act_dtype, "data": "synthetic",
+        "config": {"workload": s.name, "d_model": d, "n_heads": s.n_heads,
+                   "n_kv_heads": s.n_kv_heads, "head_dim": hd, "n_experts": moe.n_experts,
+                   "top_k": moe.top_k, "expert_ffn": moe.expert_ffn, "tp_degree_emulated": s.tp,
+                   "weights": s.w_dtype, "mode": s.mode, "tokens": s.n_tokens,
+                   "kv_len": max(s.kv_lens), "cold_copies": copies, "graph": True},
+        "step_algorithmic_bytes": sb,
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

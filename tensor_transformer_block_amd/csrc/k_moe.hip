@@ -191,9 +191,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
   }
 }
 
-// down: a wave owns MOE_DR output rows; for each selected expert it streams that expert's Fr
-// columns of the rows and adds w_j times the segment's dot product with m.
-constexpr int MOE_DR = 4;
+// down: a wave owns MOE_DR output rows. Its lanes walk the concatenation of the token's k
+// segments (expert j's Fr columns of the row), 16 bytes each, so every lane has a load in flight
+// whatever Fr is, and add w_j times each chunk's dot product with m.
+constexpr int MOE_DR = 2, MOE_DU = 4;  // rows per wave, chunks per lane in flight per row
 
 template <int WT, int AT, int PT>
 __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
@@ -204,39 +205,55 @@ __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
                                                   const void* __restrict__ Min,
                                                   void* __restrict__ P) {
   extern __shared__ float ms[];  // [top_k * Fr]
+  __shared__ int s_e[kMoeMaxTopK];
+  __shared__ float s_w[kMoeMaxTopK];
   constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.y;
-  const int np = top_k * Fr, chF = Fr / VE, nblk = Fr / 32;
+  const int np = top_k * Fr, chF = Fr / VE, nblk = Fr / 32, nq = top_k * chF;
   for (int i = tid * AV; i < np; i += 256 * AV)
     Vec16<AT>::load((const char*)Min + ((size_t)t * np + i) * (AT == ACT_F32 ? 4 : 2), ms + i);
+  if (tid < top_k) {
+    int e = ids[(size_t)t * top_k + tid];
+    s_e[tid] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    s_w[tid] = wts[(size_t)t * top_k + tid];
+  }
   __syncthreads();
   const int n0 = (blockIdx.x * 4 + wave) * MOE_DR;
   if (n0 >= d) return;
+  int nrow[MOE_DR];
+#pragma unroll
+  for (int s = 0; s < MOE_DR; ++s) nrow[s] = n0 + s < d ? n0 + s : d - 1;
   float acc[MOE_DR];
 #pragma unroll
   for (int s = 0; s < MOE_DR; ++s) acc[s] = 0.f;
-#pragma unroll 2
-  for (int j = 0; j < top_k; ++j) {
-    int e = ids[(size_t)t * top_k + j];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    const float wj = wts[(size_t)t * top_k + j];
-    for (int c0 = 0; c0 < chF; c0 += 64) {
-      const int c = c0 + lane;
-      uint4 b[MOE_DR];
-      size_t row[MOE_DR];
+  for (int q0 = 0; q0 < nq; q0 += 64 * MOE_DU) {
+    uint4 b[MOE_DU][MOE_DR];
+    int jj[MOE_DU], cc[MOE_DU];
+#pragma unroll
+    for (int u = 0; u < MOE_DU; ++u) {
+      const int q = q0 + u * 64 + lane;
+      const bool in = q < nq;
+      jj[u] = in ? q / chF : 0;
+      cc[u] = in ? q - jj[u] * chF : 0;
 #pragma unroll
       for (int s = 0; s < MOE_DR; ++s) {
-        const int n = n0 + s < d ? n0 + s : d - 1;
-        row[s] = (size_t)e * d + n;
-        b[s] = c < chF ? ld_stream16(Wd + (row[s] * Fr + (size_t)c * VE) * WB)
-                       : make_uint4(0, 0, 0, 0);
+        const size_t row = (size_t)s_e[jj[u]] * d + nrow[s];
+        b[u][s] = in ? ld_stream16(Wd + (row * Fr + (size_t)cc[u] * VE) * WB)
+                     : make_uint4(0, 0, 0, 0);
       }
-      if (c < chF) {
+    }
 #pragma unroll
-        for (int s = 0; s < MOE_DR; ++s)
-          acc[s] = fmaf(wj, moe_dot<WT>(b[s], moe_scale<WT>(Sd, row[s], nblk, c * VE / 16),
-                                        ms + j * Fr + c * VE), acc[s]);
+    for (int u = 0; u < MOE_DU; ++u) {
+      const int q = q0 + u * 64 + lane;
+      if (q >= nq) continue;
+      const float wj = s_w[jj[u]];
+      const float* mp = ms + jj[u] * Fr + cc[u] * VE;
+#pragma unroll
+      for (int s = 0; s < MOE_DR; ++s) {
+        const size_t row = (size_t)s_e[jj[u]] * d + nrow[s];
+        acc[s] = fmaf(wj, moe_dot<WT>(b[u][s], moe_scale<WT>(Sd, row, nblk, cc[u] * VE / 16), mp),
+                      acc[s]);
       }
     }
   }
