@@ -448,12 +448,11 @@ def bench_stack(args, s):
         run()
     i = 0
     for _ in range(n_st):
-        x = st.x
-        for blk in st.blocks:
-            evs = [(hev.ev[2 * (i + r)], hev.ev[2 * (i + r) + 1]) for r in range(s.tp)]
-            blk.step(x=x, ffn_events=evs)
+        evs = []
+        for _b in st.blocks:
+            evs.append([(hev.ev[2 * (i + r)], hev.ev[2 * (i + r) + 1]) for r in range(s.tp)])
             i += s.tp
-            x = blk.out
+        st.step(x=model.x if model is not None else None, ffn_events=evs)
     torch.cuda.synchronize()
     kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(i)]))
     hev.close()

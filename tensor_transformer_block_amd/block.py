@@ -138,19 +138,24 @@ class DeviceBlock:
                                            out, self.workspace, events[0], events[1],
                                            self.ws_bytes)
 
-    def step(self, copy: int = 0, ffn_events=None, x=None):
+    def step(self, copy: int = 0, ffn_events=None, x=None, xn_ready=False, next_norm=None):
         """One full block step on the current stream; the result lands in ``self.out``.
         ``ffn_events``: optional per-rank (begin, end) event pairs for the gate/up projections.
-        ``x``: the block's input [T, d] (act dtype) in place of ``self.x``."""
+        ``x``: the block's input [T, d] (act dtype) in place of ``self.x``; ``xn_ready``: its
+        RMSNorm is already in ``self.xn`` (the previous block's final reduce wrote it).
+        ``next_norm``: (gamma, xn_out) of the next block: the final reduce also writes the next
+        block's input RMSNorm, so that block skips its own."""
         d, T, N = self.desc, self.T, self.N
         x = self.x if x is None else x
-        B.tp_partial_reduce(d, T, None, 0, x, None, self.gamma1, self.xn)
+        if not xn_ready:
+            B.tp_partial_reduce(d, T, None, 0, x, None, self.gamma1, self.xn)
         for r in range(N):
             self.attn_half(r, copy)
         B.tp_partial_reduce(d, T, self.partials, N, x, self.h1, self.gamma2, self.xn2)
         for r in range(N):
             self.ffn_half(r, copy, events=None if ffn_events is None else ffn_events[r])
-        B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, None, None)
+        g, xo = next_norm if next_norm is not None else (None, None)
+        B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, g, xo)
 
     # --------------------------------------------------------------------------- readback
     def workspace_views(self):
@@ -196,10 +201,17 @@ class BlockStack:
     def out(self):
         return self.blocks[-1].out
 
-    def step(self, x=None):
+    def step(self, x=None, ffn_events=None):
+        """Every block in order; block i's final reduce also writes block i + 1's input RMSNorm
+        (the same rounded residual it would normalise), saving one launch per block boundary.
+        ``ffn_events``: optional per-block lists of per-rank gate/up event pairs."""
         x = self.x if x is None else x
-        for blk in self.blocks:
-            blk.step(x=x)
+        K = len(self.blocks)
+        for i, blk in enumerate(self.blocks):
+            nxt = self.blocks[i + 1] if i + 1 < K else None
+            blk.step(x=x, xn_ready=i > 0,
+                     next_norm=(nxt.gamma1, nxt.xn) if nxt is not None else None,
+                     ffn_events=None if ffn_events is None else ffn_events[i])
             x = blk.out
 
 
