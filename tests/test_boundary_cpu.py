@@ -182,3 +182,74 @@ def test_status_strings():
     assert B.tp_status_str(B.TP_OK) == "TP_OK"
     assert B.tp_status_str(B.TP_ERR_QUANT_ALIGN) == "TP_ERR_QUANT_ALIGN"
     assert B.tp_status_str(99) == "TP_ERR_UNKNOWN"
+
+
+# ----------------------------------------------------------------------------- head and MoE calls
+
+def test_head_layout_and_validation():
+    d = B.make_desc(CONFIGS["gemma-q8-decode"])
+    lay = B.tp_head_size(d, 1000)
+    assert lay.table.bytes == 1000 * 2560                     # one code byte per weight
+    assert lay.table_scale.bytes == 1000 * (2560 // 32) * 2   # one fp16 scale per block
+    assert lay.payload_bytes == 1000 * 2560 * 34 // 32
+    assert lay.table_scale.offset % 256 == 0 and lay.alloc_bytes >= lay.payload_bytes
+    lay = B.tp_head_size(B.make_desc(CONFIGS["llama3-8b-decode"]), 128256)
+    assert lay.table.bytes == 128256 * 4096 * 2 and lay.table_scale.bytes == 0
+    st, _ = _err(B.tp_head_size, d, 0)
+    assert st == B.TP_ERR_INVALID_ARG
+    st, _ = _err(B.tp_head_pack, d, 1000, 16, 16, B.tp_head_size(d, 1000).alloc_bytes - 1,
+                 stream=0)
+    assert st == B.TP_ERR_BUFFER_TOO_SMALL
+    st, _ = _err(B.tp_embed_lookup, d, 1000, 16, None, 3, 16, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG
+    st, msg = _err(B.tp_embed_lookup, d, 1000, 16, 16, 3, 8, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG and "aligned" in msg
+    st, _ = _err(B.tp_lm_head, d, 1000, 16, 16, -1, 16, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG
+    st, _ = _err(B.tp_lm_head, d, 1000, None, 16, 2, 16, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG
+    # empty token batches are no-ops, even with no buffers
+    B.tp_embed_lookup(d, 1000, None, None, 0, None, stream=0)
+    B.tp_lm_head(d, 1000, None, None, 0, None, stream=0)
+
+
+def test_moe_layout_is_one_nth_and_validates():
+    from tensor_transformer_block_amd.inputs import MoEShape
+    for name, moe in (("llama3-8b-decode", MoEShape(64, 8, 768)),
+                      ("gemma-q8-decode", MoEShape(16, 2, 1024))):
+        s = CONFIGS[name]
+        d, m = B.make_desc(s), B.make_moe_desc(moe)
+        per = {"f32": 4, "bf16": 2, "q8_0": 34 / 32}[s.w_dtype]
+        full = 3 * moe.n_experts * moe.expert_ffn * s.d_model * per
+        for r in range(s.tp):
+            lay = B.tp_moe_shard_size(d, m, r)
+            assert lay.payload_bytes * s.tp == full
+            regs = [lay.gate, lay.up, lay.down, lay.gate_scale, lay.up_scale, lay.down_scale]
+            assert sum(x.bytes for x in regs) == lay.payload_bytes
+            assert all(x.offset % 256 == 0 and x.offset + x.bytes <= lay.alloc_bytes for x in regs)
+    s = CONFIGS["llama3-8b-decode"]
+    d = B.make_desc(s)
+
+    def moe(**kw):
+        base = dict(n_experts=64, top_k=8, expert_ffn=768)
+        base.update(kw)
+        return B.tp_moe_desc(**base)
+    assert _err(B.tp_moe_shard_size, d, moe(top_k=17), 0)[0] == B.TP_ERR_INVALID_ARG
+    assert _err(B.tp_moe_shard_size, d, moe(top_k=9, n_experts=8), 0)[0] == B.TP_ERR_INVALID_ARG
+    assert _err(B.tp_moe_shard_size, d, moe(n_experts=1025), 0)[0] == B.TP_ERR_INVALID_ARG
+    assert _err(B.tp_moe_shard_size, d, moe(expert_ffn=769), 0)[0] == B.TP_ERR_NOT_DIVISIBLE
+    assert _err(B.tp_moe_shard_size, d, moe(expert_ffn=772), 0)[0] == B.TP_ERR_UNSUPPORTED
+    assert _err(B.tp_moe_shard_size, d, moe(), 2)[0] == B.TP_ERR_RANK
+    dq = B.make_desc(CONFIGS["gemma-q8-decode"])
+    assert _err(B.tp_moe_shard_size, dq, moe(expert_ffn=1040), 0)[0] == B.TP_ERR_QUANT_ALIGN
+    ws = B.tp_moe_workspace_size(d, moe(), 4)
+    assert ws >= 4 * 8 * 384 * 2
+    fwd = B.tp_moe_shard_forward
+    st, _ = _err(fwd, d, moe(), 0, 16, 16, 4, 16, 16, 16, 16, ws - 1, stream=0)
+    assert st == B.TP_ERR_BUFFER_TOO_SMALL
+    st, _ = _err(fwd, d, moe(), 0, 16, 16, 4, None, 16, 16, 16, ws, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG
+    st, _ = _err(B.tp_moe_route, d, moe(), 16, 16, 2, 16, None, 16, stream=0)
+    assert st == B.TP_ERR_INVALID_ARG
+    B.tp_moe_shard_forward(d, moe(), 0, None, None, 0, None, None, None, None, 0, stream=0)
+    B.tp_moe_route(d, moe(), None, None, 0, None, None, None, stream=0)
