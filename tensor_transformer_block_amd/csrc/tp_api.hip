@@ -912,8 +912,10 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
                                 w.pos_limit, (float*)(ws + w.part_o), (float*)(ws + w.part_ml),
                                 ws + w.attn, st);
     if (e != hipSuccess) return hip_fail(e, "attention");
+    // bf16 o_proj of a batch (short rows, K = Hq/N * hd): the skinny GEMM reduces its K split
+    // inside the workgroup, which measured faster than the split-K form and its epilogue launch.
     e = project(x, epi_part, T, sh + L.o.offset, sh + L.o_scale.offset, x.qdim, x.d, 0,
-                ws + w.attn, partial_out, x.d, st, nullptr, skw);
+                ws + w.attn, partial_out, x.d, st, nullptr, x.wt == TP_DTYPE_BF16 ? nullptr : skw);
     if (e != hipSuccess) return hip_fail(e, "o projection");
   } else {
     {
