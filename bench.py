@@ -145,19 +145,31 @@ def cpu_baseline(inp, seconds):
     if s.mode == "prefill":
         rows = np.array([s.n_tokens - 1])          # the last row attends to every key
     ntok = s.n_tokens if rows is None else len(rows)
-    n, t0 = 0, time.perf_counter()
+    n, t0, steps = 0, time.perf_counter(), []
     while True:
+        ts = time.perf_counter()
         oracle.block_sharded(s, p, x, kr, vr, inp.positions, inp.token_seq, rows)
+        steps.append(time.perf_counter() - ts)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or (s.mode == "prefill" and n >= 1):
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] or [1])
+    blas = sorted({i.get("internal_api", "?") for i in pools if i.get("user_api") == "blas"})
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     sample = (f"{n} full block steps (all {s.tp} ranks) of the same workload" if rows is None else
               f"{n} step(s) of the same workload with the oracle producing {len(rows)} output "
               f"row(s) (K/V and QKV for all {s.n_tokens} tokens)")
-    return {"value": round(n * ntok / el, 4), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "sample": sample + f"; {el:.1f} s wall, fp64 NumPy"}
+    return {"value": round(ntok / float(np.median(steps)), 4), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": sample + f"; {el:.1f} s wall, fp64 NumPy; value from the median step",
+            "host": {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}}
 
 
 def main():
