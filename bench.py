@@ -191,6 +191,8 @@ def main():
                     help="with the stack, time a full token step: embedding lookup, the stack, "
                          "final RMSNorm and LM head (replicated head of the family's vocabulary)")
     ap.add_argument("--vocab", type=int, default=0, help="vocabulary of --head (0: the family's)")
+    ap.add_argument("--partial-dtype", choices=("f32", "bf16"), default="f32",
+                    help="storage of the rank partials (f32: the default of the library)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a dispatch of known "
                          "size for scaling hardware byte counters)")
@@ -229,7 +231,7 @@ def main():
     copies = max(1, math.ceil(args.cold_bytes / resident))
     log(f"building device block: {copies} cold cop{'y' if copies == 1 else 'ies'} "
         f"x {resident / 1e6:.1f} MB")
-    blk = DeviceBlock(inp, copies=copies)
+    blk = DeviceBlock(inp, copies=copies, partial_dtype=args.partial_dtype)
     torch.cuda.synchronize()
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -380,7 +382,8 @@ def main():
                    "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim, "ffn_dim": s.ffn_dim,
                    "tp_degree_emulated": s.tp, "weights": s.w_dtype, "mode": s.mode,
                    "tokens": s.n_tokens, "kv_len": max(s.kv_lens), "page_size": s.page_size,
-                   "cold_copies": copies, "graph": not args.no_graph},
+                   "cold_copies": copies, "graph": not args.no_graph,
+                   "partial_dtype": args.partial_dtype},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
