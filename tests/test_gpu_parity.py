@@ -102,9 +102,13 @@ def test_block_parity_small(s):
     run_and_check(inp, label=s.name)
 
 
-def test_block_parity_bf16_partials():
-    inp = make_inputs(MED, seed=12)
-    run_and_check(inp, partial_dtype="bf16", label="bf16 partials")
+@pytest.mark.parametrize("name", ["med-bf16-ragged", "med-bf16-prefill-300",
+                                  "med-bf16-prefill-wide-rows", "med-bf16-batched-64"])
+def test_block_parity_bf16_partials(name):
+    """bf16 partial storage on the decode GEMV, the prefill GEMMs (narrow and 256 x 256 tiles)
+    and the batched-decode paths."""
+    inp = make_inputs({x.name: x for x in SHAPES}[name], seed=12)
+    run_and_check(inp, partial_dtype="bf16", label=f"{name}, bf16 partials")
 
 
 @pytest.mark.parametrize("name", ["tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode",
