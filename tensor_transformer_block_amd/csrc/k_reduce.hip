@@ -3,7 +3,7 @@
 // TensorSharp "How tensor parallelism works", step 3: the reduce leaves the identical hidden
 // state on every rank), fused with the residual add and the replicated RMSNorm that follows it.
 //
-// One workgroup per token row; each thread owns up to MAXC chunks of 8 features, kept in
+// One workgroup per token row; each thread owns one or two chunks of 8 features, kept in
 // registers between the sum and the normalisation, so the row is read and written once.
 // Summation order is fixed: ((P_0 + P_1) + ...) + P_{n-1} in fp32, then + residual, then a single
 // rounding to the activation dtype. The norm is computed from the stored (rounded) residual.
@@ -11,37 +11,6 @@
 #include "tp_kernels.h"
 
 namespace tpk {
-
-template <int T>
-__device__ __forceinline__ void load8(const void* base, size_t idx, float* v) {
-  if constexpr (T == ACT_F32) {
-    Vec16<ACT_F32>::load((const float*)base + idx, v);
-    Vec16<ACT_F32>::load((const float*)base + idx + 4, v + 4);
-  } else {
-    Vec16<ACT_BF16>::load((const uint16_t*)base + idx, v);
-  }
-}
-
-// The partials are read exactly once: streaming (non-temporal) loads keep them from displacing
-// the residual and the weights in the caches and measure faster on large reads.
-template <int T>
-__device__ __forceinline__ void load8_stream(const void* base, size_t idx, float* v) {
-  if constexpr (T == ACT_F32) {
-    const uint4 a = ld_stream16((const float*)base + idx), b = ld_stream16((const float*)base + idx + 4);
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
-  } else {
-    const uint4 a = ld_stream16((const uint16_t*)base + idx);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-}
 
 template <int T>
 __device__ __forceinline__ void store8(void* base, size_t idx, const float* v) {
@@ -65,70 +34,121 @@ __device__ __forceinline__ float round_to(float v) {
   else return bf16_to_f32(f32_to_bf16(v));
 }
 
-// Up to kPre partials per chunk are loaded before any is added, so their latencies overlap;
-// the sum is still taken strictly in rank order.
-constexpr int kPre = 8;
+// Register image of 8 consecutive values (two 16-byte vectors of fp32 or one of bf16), loaded
+// without conversion so that every load of a row can be in flight before the first is used.
+template <int T>
+struct Raw8 {
+  uint4 v[T == ACT_F32 ? 2 : 1];
+};
 
+template <int T>
+__device__ __forceinline__ void ld_raw8(const void* base, size_t idx, Raw8<T>& r) {
+  if constexpr (T == ACT_F32) {
+    r.v[0] = *(const uint4*)((const float*)base + idx);
+    r.v[1] = *(const uint4*)((const float*)base + idx + 4);
+  } else {
+    r.v[0] = *(const uint4*)((const uint16_t*)base + idx);
+  }
+}
+
+// The partials are read exactly once: streaming (non-temporal) loads keep them from displacing
+// the residual and the weights in the caches and measure faster on large reads.
+template <int T>
+__device__ __forceinline__ void ld_raw8_stream(const void* base, size_t idx, Raw8<T>& r) {
+  if constexpr (T == ACT_F32) {
+    r.v[0] = ld_stream16((const float*)base + idx);
+    r.v[1] = ld_stream16((const float*)base + idx + 4);
+  } else {
+    r.v[0] = ld_stream16((const uint16_t*)base + idx);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void unpack8(const Raw8<T>& r, float* v) {
+  unpack16<T>(r.v[0], v);
+  if constexpr (T == ACT_F32) unpack16<T>(r.v[1], v + 4);
+}
+
+// Partials are loaded in groups of kGroup / MAXC per chunk: a group's loads are all issued before
+// any of them is added, so their latencies overlap; the sum is still taken strictly in rank order.
+constexpr int kGroup = 8;
+constexpr int kMaxThreads = 1024;
+
+// One workgroup per token row, one chunk of 8 features per thread (two when the row has more than
+// 1024 chunks). Decode rows are a single workgroup whose time is memory latency, so the row's
+// residual, gamma and first partial group are all requested before the first wait, and the
+// stores come after the last load.
 template <int AT, int PT, int MAXC>
-__global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __restrict__ partials,
-                                                        int n_part, size_t part_stride,
-                                                        const void* res_in, void* res_out,
-                                                        const void* __restrict__ gamma,
-                                                        void* __restrict__ normed, float eps) {
-  __shared__ float red[4];
-  const int t = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(kMaxThreads) void k_partial_reduce(
+    int d, const void* __restrict__ partials, int n_part, size_t part_stride, const void* res_in,
+    void* res_out, const void* __restrict__ gamma, void* __restrict__ normed, float eps) {
+  constexpr int G = kGroup / MAXC;
+  __shared__ float red[kMaxThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int nchunk = d >> 3;
   const size_t row = (size_t)t * d;
   float v[MAXC][8], gm[MAXC][8];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int ci = tid + c * 256;
-    if (ci < nchunk) {
-      const size_t idx = row + (size_t)ci * 8;
-      float r[8];
-      load8<AT>(res_in, idx, r);
-      if (gamma != nullptr) load8<AT>(gamma, (size_t)ci * 8, gm[c]);
-      if (n_part > 0) {
-        float p[kPre][8];
+    // Threads past the row's end re-read its last chunk and store nothing.
+    const int ci = min(tid + c * nt, nchunk - 1);
+    const size_t idx = row + (size_t)ci * 8;
+    Raw8<AT> rr, gr;
+    Raw8<PT> pr[G];
+    ld_raw8<AT>(res_in, idx, rr);
+    if (gamma != nullptr) ld_raw8<AT>(gamma, (size_t)ci * 8, gr);
 #pragma unroll
-        for (int k = 0; k < kPre; ++k)
-          if (k < n_part) load8_stream<PT>(partials, (size_t)k * part_stride + idx, p[k]);
-        float sum[8];
+    for (int k = 0; k < G; ++k)
+      if (k < n_part) ld_raw8_stream<PT>(partials, (size_t)k * part_stride + idx, pr[k]);
+    unpack8<AT>(rr, v[c]);
+    if (gamma != nullptr) unpack8<AT>(gr, gm[c]);
+    if (n_part > 0) {
+      float sum[8], q[8];
+      unpack8<PT>(pr[0], sum);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum[e] = p[0][e];
-#pragma unroll
-        for (int k = 1; k < kPre; ++k)
-          if (k < n_part) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sum[e] += p[k][e];
-          }
-        for (int k = kPre; k < n_part; ++k) {
-          float q[8];
-          load8_stream<PT>(partials, (size_t)k * part_stride + idx, q);
+      for (int k = 1; k < G; ++k)
+        if (k < n_part) {
+          unpack8<PT>(pr[k], q);
 #pragma unroll
           for (int e = 0; e < 8; ++e) sum[e] += q[e];
         }
+      for (int k0 = G; k0 < n_part; k0 += G) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = round_to<AT>(r[e] + sum[e]);
-        store8<AT>(res_out, idx, r);
+        for (int k = 0; k < G; ++k)
+          if (k0 + k < n_part)
+            ld_raw8_stream<PT>(partials, (size_t)(k0 + k) * part_stride + idx, pr[k]);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+          if (k0 + k < n_part) {
+            unpack8<PT>(pr[k], q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[e] += q[e];
+          }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[c][e] = r[e];
-        ss += r[e] * r[e];
-      }
+      for (int e = 0; e < 8; ++e) v[c][e] = round_to<AT>(v[c][e] + sum[e]);
     }
+    if (tid + c * nt < nchunk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
+    }
+  }
+  if (n_part > 0) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (tid + c * nt < nchunk) store8<AT>(res_out, row + (size_t)(tid + c * nt) * 8, v[c]);
   }
   if (gamma == nullptr) return;
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float tot = 0.f;
+  for (int w = 0; w < (nt >> 6); ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int ci = tid + c * 256;
+    const int ci = tid + c * nt;
     if (ci < nchunk) {
       float o[8];
 #pragma unroll
@@ -140,27 +160,21 @@ __global__ __launch_bounds__(256) void k_partial_reduce(int d, const void* __res
 
 template <int AT, int PT>
 static hipError_t launch_reduce_t(int T, int d, const void* partials, int n, const void* res_in,
-                                  void* res_out,
-                                  const void* gamma, void* normed, float eps, hipStream_t st) {
+                                  void* res_out, const void* gamma, void* normed, float eps,
+                                  hipStream_t st) {
   const int nchunk = d / 8;
-  const int maxc = (nchunk + 255) / 256;
+  const int maxc = (nchunk + kMaxThreads - 1) / kMaxThreads;
+  const int threads = ((nchunk + maxc - 1) / maxc + 63) / 64 * 64;
   const size_t stride = (size_t)T * d;
-  dim3 g(T), b(256);
-#define TPK_RED(MC)                                                                          \
-  hipLaunchKernelGGL((k_partial_reduce<AT, PT, MC>), g, b, 0, st, d, partials, n, stride, \
-                     res_in, res_out, gamma, normed, eps)
-  switch (maxc) {
-    case 1: TPK_RED(1); break;
-    case 2: TPK_RED(2); break;
-    case 3: TPK_RED(3); break;
-    case 4: TPK_RED(4); break;
-    case 5: TPK_RED(5); break;
-    case 6: TPK_RED(6); break;
-    case 7: TPK_RED(7); break;
-    case 8: TPK_RED(8); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef TPK_RED
+  dim3 g(T), b(threads);
+  if (maxc == 1)
+    hipLaunchKernelGGL((k_partial_reduce<AT, PT, 1>), g, b, 0, st, d, partials, n, stride, res_in,
+                       res_out, gamma, normed, eps);
+  else if (maxc == 2)
+    hipLaunchKernelGGL((k_partial_reduce<AT, PT, 2>), g, b, 0, st, d, partials, n, stride, res_in,
+                       res_out, gamma, normed, eps);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@ import pytest
 
 from tensor_transformer_block_amd.inputs import CONFIGS, WORKLOADS, BlockShape, make_inputs
 
-from parity_util import log, nrel, run_and_check, t2np
+from parity_util import TOL, log, nrel, run_and_check, t2np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -28,6 +28,9 @@ SHAPES = [
               kv_lens=tuple(int(v) for v in np.random.default_rng(7).integers(1, 300, 21)),
               n_tokens=21),
     MED.with_(name="med-bf16-batched-5", index=211, kv_lens=(3, 64, 17, 250, 33), n_tokens=5),
+    # 125 key splits of 160 keys: the split merge's per-thread prefetch (16 splits per quarter)
+    # and its tail loop.
+    MED.with_(name="med-bf16-long-kv", index=234, kv_lens=(20000, 3), n_tokens=2),
     MED.with_(name="med-bf16-batched-64", index=212, tp=4, n_heads=8, n_kv_heads=4,
               ffn_dim=1408, kv_lens=tuple(range(40, 40 + 64 * 3, 3)), n_tokens=64),
     MED.with_(name="med-bf16-prefill", index=204, mode="prefill", kv_lens=(137,), n_tokens=100),
@@ -485,6 +488,45 @@ def test_empty_batch_is_noop():
     B.tp_partial_reduce(blk.desc, 0, blk.partials, 2, blk.x, blk.h1, blk.gamma2, blk.xn2)
     torch.cuda.synchronize()
     assert torch.equal(before, blk.partials)
+
+
+@pytest.mark.parametrize("d,n_part,act,part", [
+    (512, 1, "bf16", "f32"), (2560, 3, "bf16", "f32"), (4096, 11, "bf16", "bf16"),
+    (12288, 11, "bf16", "f32"), (12288, 2, "f32", "f32"), (256, 9, "f32", "f32"),
+])
+def test_reduce_groups_and_row_widths(d, n_part, act, part):
+    """The reduce with and without gamma: rows of one wave, several waves, and two chunks per
+    thread (d > 8192), more partials than one load group (tail groups), fp32 and bf16 storage.
+    The residual sum is compared bit for bit with the same fp32 order on the host; the norm with
+    the fp64 RMSNorm of the stored residual."""
+    from tensor_transformer_block_amd import binding as B
+    s = MED.with_(d_model=d, n_heads=d // 128, n_kv_heads=d // 128, ffn_dim=2 * d,
+                  act_dtype=act, w_dtype="f32" if act == "f32" else "bf16")
+    desc = B.make_desc(s, partial_dtype=part)
+    T = 3
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    g = torch.Generator().manual_seed(d + n_part)
+    P = torch.randn(n_part, T, d, generator=g).to(tdt[part])
+    x = (torch.randn(T, d, generator=g) * 3).to(tdt[act])
+    gamma = (1 + 0.1 * torch.randn(d, generator=g)).to(tdt[act])
+    acc = P[0].float().clone()
+    for r in range(1, n_part):
+        acc = acc + P[r].float()
+    ref = (x.float() + acc).to(tdt[act])
+    xd, Pd, gd = x.cuda(), P.cuda(), gamma.cuda()
+    for with_gamma in (False, True):
+        out = torch.full_like(xd, float("nan"))
+        nrm = torch.full_like(xd, float("nan"))
+        B.tp_partial_reduce(desc, T, Pd, n_part, xd, out, gd if with_gamma else None,
+                            nrm if with_gamma else None)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), ref), f"d={d} n={n_part}: residual differs"
+        if with_gamma:
+            h = ref.double().numpy()
+            want = gamma.double().numpy() * h / np.sqrt((h * h).mean(-1, keepdims=True) + s.rms_eps)
+            err = nrel(t2np(nrm), want)
+            log(f"reduce d={d} n={n_part} {act}/{part}: norm err {err:.2e}")
+            assert err < TOL[act]
 
 
 def test_reduce_order_and_rounding():
