@@ -57,10 +57,9 @@ hipError_t q8_join(void* aos, size_t aos_ld, int64_t rows, int64_t nblk, const v
                    const void* scales, hipStream_t st);
 hipError_t q8_dequant_buf(const void* codes, const void* scales, float* out, int64_t n_blocks,
                           hipStream_t st);
-
-// k_reduce.hip
 hipError_t launch_embed(int wt, const void* table, const void* scales, const int32_t* ids,
                         int T, int vocab, int d, void* x, hipStream_t st);
+
 // k_moe.hip
 hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t* ids,
                            float* weights, hipStream_t st);
@@ -68,6 +67,8 @@ hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, cons
                           const void* Wu, const void* Su, const void* Wd, const void* Sd, int d,
                           int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
                           const void* X, void* M, void* P, hipStream_t st);
+
+// k_reduce.hip
 hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,
                                  const void* res_in, void* res_out, const void* gamma,
                                  void* normed, float eps, hipStream_t st);
