@@ -60,9 +60,11 @@ __device__ __forceinline__ int clampi_g(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// Rows per wave by the number of 16-byte chunks per row.
-inline int gemv_rows_per_wave(int nch, bool paired) {
+// Rows per wave: by the number of 16-byte chunks per row, so that each wave streams a few KB, but
+// no more than leaves about 1024 waves (one per SIMD) when the matrix has few rows.
+inline int gemv_rows_per_wave(int nch, bool paired, long rows) {
   int r = nch > 512 ? 1 : (nch > 256 ? 2 : (nch > 128 ? 4 : 8));
+  while (r > 1 && rows / r < 1024) r >>= 1;
   return (paired && r < 2) ? 2 : r;
 }
 
@@ -321,7 +323,7 @@ hipError_t gemv_format(int epi, int actf, int nt, const void* W, const uint16_t*
                        hipStream_t st) {
   const int nch = K / WFmt<WT>::VE;
   const bool paired = (epi == EPI_GATED || epi == EPI_ROPE);
-  const int r = gemv_rows_per_wave(nch, paired);
+  const int r = gemv_rows_per_wave(nch, paired, epi == EPI_GATED ? 2L * n_out : (long)n_out);
   switch (epi) {
     case EPI_F32:
       return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
