@@ -137,6 +137,30 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   };
   load_batch(0);  // in flight while the token vectors are staged
 
+  // Rotary epilogue inputs (each token's position and KV page, the cos/sin of this wave's pairs)
+  // do not depend on the projection, so they are fetched here, under the weight stream, instead
+  // of as two dependent round trips after it.
+  constexpr int EN = (EPI == EPI_ROPE) ? NT : 1, EP = (EPI == EPI_ROPE) ? R / 2 : 1;
+  int e_pos[EN], e_page[EN];
+  float2 e_cs[EP][EN];
+  if constexpr (EPI == EPI_ROPE) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int tok = re.t0 + t;
+      e_pos[t] = clampi_g(re.positions[tok], 0, re.pos_limit - 1);
+      const int seq = (re.mode == 0) ? tok : 0;
+      const int pg = min(e_pos[t] / re.ps, re.max_pages - 1);
+      e_page[t] = clampi_g(re.block_table[(size_t)seq * re.max_pages + pg], 0, re.n_pages - 1);
+#pragma unroll
+      for (int s = 0; s < R; s += 2) {
+        const int p = w * (R / 2) + s / 2;
+        e_cs[s / 2][t] = make_float2(1.f, 0.f);
+        if (ok[s] && p / half < re.hq + re.hk)
+          e_cs[s / 2][t] = ((const float2*)re.rope)[(size_t)e_pos[t] * half + p % half];
+      }
+    }
+  }
+
   for (int i = tid * AV; i < NT * K; i += 256 * AV)
     Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
   float* const xq = xs + NT * K;
@@ -229,9 +253,9 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
 #pragma unroll
       for (int s = 0; s < R; ++s)
         if (ok[s]) st_act<EPI == EPI_BF16 ? ACT_BF16 : AT>(Y, yo + row[s], acc[s][t]);
-    } else {  // EPI_ROPE
+    } else if constexpr (EPI == EPI_ROPE) {
       const int tok = re.t0 + t;
-      const int pos = clampi_g(re.positions[tok], 0, re.pos_limit - 1);
+      const int pos = e_pos[t], page = e_page[t];
 #pragma unroll
       for (int s = 0; s < R; s += 2) {
         if (!ok[s]) continue;
@@ -239,25 +263,19 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
         const int head = p / half, i = p % half;
         const float a = acc[s][t], bv = acc[s + 1][t];
         if (head < re.hq + re.hk) {
-          const float2 cs = ((const float2*)re.rope)[(size_t)pos * half + i];
+          const float2 cs = e_cs[s / 2][t];
           const float ra = a * cs.x - bv * cs.y, rb = bv * cs.x + a * cs.y;
           if (head < re.hq) {
             const size_t dq = (size_t)tok * re.hq * re.hd + (size_t)head * re.hd + i;
             st_act<AT>(re.q_out, dq, ra);
             st_act<AT>(re.q_out, dq + half, rb);
           } else {
-            const int seq = (re.mode == 0) ? tok : 0;
-            const int page = clampi_g(re.block_table[(size_t)seq * re.max_pages + pos / re.ps], 0,
-                                      re.n_pages - 1);
             const size_t dk =
                 (((size_t)page * re.hk + (head - re.hq)) * re.ps + pos % re.ps) * re.hd + i;
             st_act<AT>(re.k_pages, dk, ra);
             st_act<AT>(re.k_pages, dk + half, rb);
           }
         } else {
-          const int seq = (re.mode == 0) ? tok : 0;
-          const int page = clampi_g(re.block_table[(size_t)seq * re.max_pages + pos / re.ps], 0,
-                                    re.n_pages - 1);
           // V pages are stored transposed: [page][kv head][hd][slot].
           const size_t dv = ((size_t)page * re.hk + (head - re.hq - re.hk)) * re.hd + i;
           const int slot = pos % re.ps;
