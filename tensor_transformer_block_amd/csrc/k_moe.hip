@@ -19,15 +19,15 @@
 namespace tpk {
 
 // ---------------------------------------------------------------------------- top-k routing
-// One wave per token: each lane holds E/64 (rounded up) logits; top_k rounds of a wave-wide
-// (value, index) maximum pick the experts in order, then lane 0 takes the softmax of the
-// selected logits.
+// One wave per token: each lane holds PER >= E/64 logits (PER a power of two, so a 64-expert
+// router scans one slot per lane and round); top_k rounds of a wave-wide (value, index) maximum
+// pick the experts in order, then the selected logits' softmax gives the weights.
 constexpr int kMoeMaxExperts = 1024, kMoeMaxTopK = 16;
 
+template <int PER>
 __global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logits, int T, int E,
                                                   int top_k, int32_t* __restrict__ ids,
                                                   float* __restrict__ weights) {
-  constexpr int PER = kMoeMaxExperts / 64;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -88,7 +88,13 @@ hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t
   if (T <= 0) return hipSuccess;
   if (E < 1 || E > kMoeMaxExperts || top_k < 1 || top_k > kMoeMaxTopK || top_k > E)
     return hipErrorInvalidValue;
-  launch(k_moe_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, top_k, ids, weights);
+  const dim3 g((T + 3) / 4), b(256);
+  const int per = (E + 63) / 64;
+  if (per <= 1) launch(k_moe_topk<1>, g, b, 0, st, logits, T, E, top_k, ids, weights);
+  else if (per <= 2) launch(k_moe_topk<2>, g, b, 0, st, logits, T, E, top_k, ids, weights);
+  else if (per <= 4) launch(k_moe_topk<4>, g, b, 0, st, logits, T, E, top_k, ids, weights);
+  else if (per <= 8) launch(k_moe_topk<8>, g, b, 0, st, logits, T, E, top_k, ids, weights);
+  else launch(k_moe_topk<kMoeMaxExperts / 64>, g, b, 0, st, logits, T, E, top_k, ids, weights);
   return hipGetLastError();
 }
 

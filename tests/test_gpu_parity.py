@@ -397,34 +397,38 @@ def test_moe_block_parity(s, moe):
         assert torch.equal(b.out, eager), f"replay {i}"
 
 
-def test_moe_topk_ties_and_bounds():
-    """Experts with identical router rows tie exactly; the lower index comes first. Every token
-    selects distinct experts."""
+@pytest.mark.parametrize("E,k", [(40, 6), (100, 8), (200, 16), (500, 4), (1000, 16)])
+def test_moe_topk_ties_and_bounds(E, k):
+    """Experts with identical router rows tie exactly; the lower index comes first, also between
+    experts that share a lane (64 apart). Every token selects distinct experts. The expert counts
+    give each lane 1, 2, 4, 8 and 16 logits."""
     import oracle
     from tensor_transformer_block_amd import binding as B
     from tensor_transformer_block_amd.block import to_device
     from tensor_transformer_block_amd.inputs import _encode
     s = MED.with_(n_tokens=5, kv_lens=(4,) * 5)
-    moe = MoEShape(40, 6, 256)
+    moe = MoEShape(E, k, 256)
     rng = np.random.default_rng(5)
-    router = rng.standard_normal((40, s.d_model)).astype(np.float32) * 0.05
-    router[7] = router[3]
-    router[30] = router[3]
+    router = rng.standard_normal((E, s.d_model)).astype(np.float32) * 0.05
+    tied = [e for e in (3, 7, 30, 67, 131, 515) if e < E]
+    for e in tied[1:]:
+        router[e] = router[3]
     router[12] = router[21]
     x = rng.standard_normal((5, s.d_model)).astype(np.float32)
-    x[1] = router[3] * 40  # token 1 prefers experts 3, 7 and 30 (equal logits)
+    x[1] = router[3] * 40  # token 1 prefers the tied experts (equal logits)
     rt = to_device(_encode(router, "bf16"), "bf16", "cuda")
     xt = to_device(_encode(x, "bf16"), "bf16", "cuda")
-    z = torch.empty((5, 40), device="cuda")
-    ids = torch.empty((5, 6), dtype=torch.int32, device="cuda")
-    w = torch.empty((5, 6), device="cuda")
+    z = torch.empty((5, E), device="cuda")
+    ids = torch.empty((5, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((5, k), device="cuda")
     B.tp_moe_route(B.make_desc(s), B.make_moe_desc(moe), rt, xt, 5, z, ids, w)
     torch.cuda.synchronize()
-    ids_ref, w_ref = oracle.moe_select(t2np(z), 6)
+    ids_ref, w_ref = oracle.moe_select(t2np(z), k)
     got = ids.cpu().numpy()
     assert np.array_equal(got, ids_ref)
-    assert list(got[1][:3]) == [3, 7, 30]
-    assert all(len(set(row)) == 6 for row in got)
+    n = min(k, len(tied))
+    assert list(got[1][:n]) == tied[:n]
+    assert all(len(set(row)) == k for row in got)
     assert nrel(t2np(w), w_ref) <= 1e-5
 
 
