@@ -214,13 +214,15 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   if (L > x.maxpos) L = x.maxpos;
   if (L < 1) L = 1;
   w.pos_limit = L;
-  // Key splits of the attention: about 256 workgroups in total, each at least one 32-key tile
-  // per wave (128 keys), in multiples of 32 keys.
+  // Key splits of the attention: about 256 workgroups in total, in multiples of 32 keys, each at
+  // least one 32-key tile per wave (128 keys) or, for heads of 256 and more, whose tiles carry
+  // twice the bytes, two of the four waves busy (64 keys).
   const int per_split = x.hk * (int)(T > 0 ? T : 1);
   const int want = (256 + per_split - 1) / per_split;
+  const int min_chunk = x.hd >= 256 ? 64 : 128;
   int chunk = (L + want - 1) / want;
   chunk = (chunk + 31) / 32 * 32;
-  if (chunk < 128) chunk = 128;
+  if (chunk < min_chunk) chunk = min_chunk;
   w.chunk = chunk;
   w.n_split = (L + chunk - 1) / chunk;
   uint64_t off = 0;
