@@ -19,8 +19,8 @@
 namespace tpk {
 
 // ---------------------------------------------------------------------------- top-k routing
-// One wave per token: each lane holds PER >= E/64 logits (PER a power of two, so a 64-expert
-// router scans one slot per lane and round); top_k rounds of a wave-wide (value, index) maximum
+// One wave per token: each lane holds PER >= E/64 logits (PER a power of two; routers of at most
+// 64 experts take k_moe_topk64 below instead); top_k rounds of a wave-wide (value, index) maximum
 // pick the experts in order, then the selected logits' softmax gives the weights.
 constexpr int kMoeMaxExperts = 1024, kMoeMaxTopK = 16;
 
@@ -83,6 +83,46 @@ __global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logi
   }
 }
 
+// At most 64 experts: each lane holds one logit and counts the entries ranked above it (larger,
+// or equal with a lower index), which places every selected expert directly: one pass over the
+// wave's logits in LDS instead of top_k rounds of wave-wide maxima. The winners are then moved to
+// lane = rank, the layout the softmax above uses, so ids and weights come out the same.
+__global__ __launch_bounds__(256) void k_moe_topk64(const float* __restrict__ logits, int T,
+                                                    int E, int top_k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights) {
+  __shared__ __attribute__((aligned(16))) float s_z[4][64];
+  __shared__ float s_v[4][kMoeMaxTopK];
+  __shared__ int s_i[4][kMoeMaxTopK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float v = lane < E ? logits[(size_t)t * E + lane] : -INFINITY;
+  s_z[wave][lane] = v;
+  // The wave's own LDS writes must land before its lanes read each other's entries.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const float4 z = *(const float4*)&s_z[wave][j];
+    rank += (z.x > v || (z.x == v && j < lane)) + (z.y > v || (z.y == v && j + 1 < lane)) +
+            (z.z > v || (z.z == v && j + 2 < lane)) + (z.w > v || (z.w == v && j + 3 < lane));
+  }
+  if (lane < E && rank < top_k) {  // padding lanes (-inf, highest indices) never rank this high
+    s_v[wave][rank] = v;
+    s_i[wave][rank] = lane;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  const float my_v = lane < top_k ? s_v[wave][lane] : -INFINITY;
+  const int my_i = lane < top_k ? s_i[wave][lane] : 0;
+  const float top = __shfl(my_v, 0, 64);
+  const float ex = lane < top_k ? expf(my_v - top) : 0.f;
+  const float den = wave_sum(ex);
+  if (lane < top_k) {
+    ids[(size_t)t * top_k + lane] = my_i;
+    weights[(size_t)t * top_k + lane] = ex / den;
+  }
+}
+
 hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t* ids,
                            float* weights, hipStream_t st) {
   if (T <= 0) return hipSuccess;
@@ -90,7 +130,7 @@ hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t
     return hipErrorInvalidValue;
   const dim3 g((T + 3) / 4), b(256);
   const int per = (E + 63) / 64;
-  if (per <= 1) launch(k_moe_topk<1>, g, b, 0, st, logits, T, E, top_k, ids, weights);
+  if (per <= 1) launch(k_moe_topk64, g, b, 0, st, logits, T, E, top_k, ids, weights);
   else if (per <= 2) launch(k_moe_topk<2>, g, b, 0, st, logits, T, E, top_k, ids, weights);
   else if (per <= 4) launch(k_moe_topk<4>, g, b, 0, st, logits, T, E, top_k, ids, weights);
   else if (per <= 8) launch(k_moe_topk<8>, g, b, 0, st, logits, T, E, top_k, ids, weights);
