@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
 // down: a wave owns MOE_DR output rows. Its lanes walk the concatenation of the token's k
 // segments (expert j's Fr columns of the row), 16 bytes each, so every lane has a load in flight
 // whatever Fr is, and add w_j times each chunk's dot product with m.
-constexpr int MOE_DR = 2, MOE_DU = 4;  // rows per wave, chunks per lane in flight per row
+constexpr int MOE_DR = 2, MOE_DU = 8;  // rows per wave, chunks per lane in flight per row
 
 template <int WT, int AT, int PT>
 __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
