@@ -24,11 +24,12 @@
  *              rank, so they add no collective.
  *   [ML-OOS]   mlxcel issue #488, section "Out of scope": embeddings and LM head stay replicated
  *              (a vocabulary-parallel split is left out).
- *   [TS-MOE]   TensorSharp, section "Supported architectures": expert slicing puts the Megatron
- *              split inside every expert (gate/up column-parallel, down row-parallel), so every
- *              rank holds 1/N of every expert with a replicated router and a token's selected
- *              expert ids (distinct within the token) are valid on every rank; section
- *              "Requirements & constraints": MoE models run per sequence under tensor parallelism.
+ *   [TS-MOE]   TensorSharp, section "Supported architectures": with expert slicing each expert
+ *              is itself sharded the column/row way (its gate and up projections by output
+ *              columns, its down projection by input columns), so a rank keeps 1/N of every
+ *              expert, the router is the same on every rank, and the expert ids chosen for a
+ *              token mean the same thing everywhere; section "Requirements & constraints": under
+ *              tensor parallelism MoE models take one sequence at a time.
  *
  * Conventions for every call:
  *   - All tensors are caller-owned device memory unless stated. The library allocates nothing,
@@ -125,9 +126,9 @@ typedef struct {
  * k_pages [n_pages][Hkv/N][page_size][hd] (after the rotary embedding) and v_pages stored
  * transposed, [n_pages][Hkv/N][hd][page_size], so that 8 consecutive keys of one hd column are
  * contiguous (the B operand layout of the P.V matrix-core step). Slots no key has been written to
- * yet (past a sequence's last position in its last page) are never attended, but the matrix-core
- * steps multiply them by zero weights, so they must hold finite values: allocate the pools
- * zero-filled. */
+ * (past a sequence's last position, pages a block-table entry points at beyond a sequence's own)
+ * may hold anything, NaN and Inf included: the attention kernels never let such a slot reach the
+ * output [ML-ACC], so recycled pages need no clearing. */
 typedef struct {
   void* k_pages;
   void* v_pages;
@@ -265,7 +266,9 @@ tp_status tp_moe_shard_weights(const tp_block_desc* desc, const tp_moe_desc* moe
  * xn . router^T with router [n_experts, d] in the activation dtype; then per token the top_k
  * experts by logit, largest first (equal logits: lower index first), into topk_ids [T, top_k]
  * (int32), and their weights, the softmax of the selected logits, into topk_weights [T, top_k]
- * (fp32). n_tokens == 0 is a no-op. */
+ * (fp32). A NaN logit ranks as -inf, below every number (so it is chosen only when fewer than
+ * top_k logits are numbers, with weight 0 unless every selected logit is -inf or NaN).
+ * n_tokens == 0 is a no-op. */
 tp_status tp_moe_route(const tp_block_desc* desc, const tp_moe_desc* moe, const void* router,
                        const void* xn, int32_t n_tokens, float* logits, int32_t* topk_ids,
                        float* topk_weights, void* stream);
@@ -308,6 +311,22 @@ tp_status tp_shard_unpack(const tp_block_desc* desc, int32_t rank, const void* s
  * into out [n_blocks*32] fp32: out = float(scale) * code. */
 tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uint64_t n_blocks,
                           void* stream);
+
+/* One projection of rank r's packed shard exactly as tp_block_shard_forward runs it, with the fp32
+ * output epilogue of the row-parallel partials: out[t, o] = sum_k x[t, k] W[o, k], fp32
+ * [n_tokens, rows], for W the region `which` of `shard` taken as a plain [rows, K] matrix:
+ * 0 = qkv [(Hq/N + 2 Hkv/N) hd, d], 1 = o [d, Hq/N hd], 2 = gate_up [2 F/N, d] (gate rows, then
+ * up rows), 3 = down [d, F/N]. x is [n_tokens, K] in the activation dtype. The token count picks
+ * the kernel as in the forward path (for Q8_0: the dequantising GEMV up to four tokens, the
+ * matrix-core Q8_0 GEMM beyond, split over K when its tiles do not fill the chip). With one-hot
+ * rows of x the result is the region's weights as the kernels dequantise them, which a test
+ * compares bit for bit with d * q ([TS-REQ], block-quantised weights). workspace: device, at
+ * least tp_shard_project_workspace_size bytes (may be NULL when that size is 256 or less). */
+tp_status tp_shard_project(const tp_block_desc* desc, int32_t which, const void* shard,
+                           const void* x, int32_t n_tokens, float* out, void* workspace,
+                           uint64_t workspace_bytes, void* stream);
+tp_status tp_shard_project_workspace_size(const tp_block_desc* desc, int32_t which,
+                                          int32_t n_tokens, uint64_t* bytes);
 
 /* Byte offsets, inside the workspace, of the intermediates of the last forward call with this
  * desc/batch: post-rotary q [T, Hq/N*hd], attention output a_r [T, Hq/N*hd] (activation dtype),

@@ -14,8 +14,9 @@ What it computes, and where the pages fix it:
   identical on every rank. Norms stay replicated on every rank.
 * mlxcel issue #488, section "Problem": in the one-device runtime every rank runs in sequence and
   the partials are summed locally ("reduce_sum"); this is the reduction ``block_sharded`` models.
-* nnsight PR #677, section "Change": row-parallel layers split the input dim, every other parallel
-  layer the output dim; fused weights keep their rows grouped by rank (``x @ weight.T``).
+* nnsight PR #677, section "Change": a row-parallel layer is cut along its input features and the
+  remaining parallel layers along their output features; a fused weight keeps each rank's rows
+  together (the layers compute ``x @ weight.T``).
 
 The pages do not define the block's sublayers. Their published definitions are used:
 RMSNorm (Zhang & Sennrich 2019), rotary embedding in its rotate-half form (Su et al. 2021),
@@ -392,10 +393,10 @@ def run_model(head, inputs, sharded=True):
 
 
 # ----------------------------------------------------------------------------- mixture of experts
-# TensorSharp, "Multi-GPU & Multi-Node", section "Supported architectures": in the expert-sliced
-# sharding the Megatron split goes inside every expert (gate/up column-parallel, down row-
-# parallel), every rank holds 1/N of every expert's weights and the router is replicated, so a
-# token's selected expert ids (distinct within the token) mean the same on every rank.
+# TensorSharp, "Multi-GPU & Multi-Node", section "Supported architectures": expert slicing shards
+# each expert the way the dense FFN is sharded (gate and up by output column, down by input
+# column) and keeps the router whole, so a rank owns 1/N of every expert and the distinct expert
+# ids picked for a token refer to the same experts on every rank.
 
 
 def moe_params_f64(minp) -> dict:

@@ -31,6 +31,7 @@ EXPORTED = (
     "tp_block_shard_forward_timed", "tp_head_size", "tp_head_pack", "tp_embed_lookup",
     "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
     "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
+    "tp_shard_project", "tp_shard_project_workspace_size",
 )
 
 
@@ -128,6 +129,8 @@ def lib() -> ctypes.CDLL:
         "tp_moe_workspace_size": [P, P, I32, P],
         "tp_moe_shard_forward": [P, P, I32, P, P, I32, P, P, P, P, U64, P],
         "tp_moe_shard_forward_timed": [P, P, I32, P, P, I32, P, P, P, P, U64, P, P, P],
+        "tp_shard_project": [P, I32, P, P, I32, P, P, U64, P],
+        "tp_shard_project_workspace_size": [P, I32, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -265,6 +268,21 @@ def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residua
 
 def tp_dequant_q8_0(codes, scales, out, n_blocks, stream=None) -> None:
     _check(lib().tp_dequant_q8_0(ptr(codes), ptr(scales), ptr(out), n_blocks, _stream(stream)))
+
+
+def tp_shard_project_workspace_size(desc, which: int, n_tokens: int) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().tp_shard_project_workspace_size(ctypes.byref(desc), which, n_tokens,
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def tp_shard_project(desc, which, shard, x, n_tokens, out, workspace=None, workspace_bytes=None,
+                     stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_shard_project(ctypes.byref(desc), which, ptr(shard), ptr(x), n_tokens, ptr(out),
+                                  ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def tp_head_size(desc, vocab: int) -> tp_head_layout:

@@ -580,6 +580,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     for (int n = 0; n < NO; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
+    // Keys at or past kend get P = 0, but a slot no key was written to may hold a NaN or an Inf,
+    // and 0 times either is a NaN: the last tile zeroes its V elements past kend (this lane's
+    // eight keys are kb0 + 8 fq .. kb0 + 8 fq + 7 in every hd column).
+    if (kb0 + 32 > kend) {
+      const uint4 keep = v_keep_mask(kend - (kb0 + 8 * fq));
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        vf[n].x &= keep.x;
+        vf[n].y &= keep.y;
+        vf[n].z &= keep.z;
+        vf[n].w &= keep.w;
+      }
+    }
     // The wave's own P writes must land before its lanes read them back in the A layout.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     const bf16x8_a pa = *(const bf16x8_a*)(pb + fr * kPLd + fq * 8);

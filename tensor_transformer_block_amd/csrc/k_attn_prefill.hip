@@ -88,7 +88,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   if (tid < 16 * TB && t0 + tid < T)
     atomicMax(&s_kmax, ap_clamp(positions[t0 + tid], 0, pos_limit - 1) + 1);
   __syncthreads();
-  const int nsup = (s_kmax + 4 * AP_SUB - 1) / (4 * AP_SUB);
+  const int kmax = s_kmax;  // keys below this were written (prior cache or this step)
+  const int nsup = (kmax + 4 * AP_SUB - 1) / (4 * AP_SUB);
 
   // The wave's row blocks rb = 2 wp + h (h = 0, 1): token block rb / NHW, head rb % NHW of the
   // workgroup's heads. Lane l works on row (token) l % 16 of both throughout.
@@ -227,14 +228,29 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
       lsum[h] += ps;
     }
   };
-  // V^T of the sub-tile in V slot `slot` (lane: hd row 16 n + fr, keys 8 fq .. 8 fq + 7, one
-  // 16-byte read), then O^T += V^T P^T.
-  auto accumulate = [&](int slot) {
+  // V^T of the sub-tile in V slot `slot` (lane: hd row 16 n + fr, keys kb0 + 8 fq .. kb0 + 8 fq
+  // + 7, one 16-byte read), then O^T += V^T P^T. Keys at or past kmax have P = 0, but their slots
+  // may never have been written and hold a NaN or an Inf (0 times either is a NaN), so the
+  // sub-tile that crosses kmax clears their V elements first. (`edge` is a constant at each call:
+  // the overlapped branch below only runs sub-tiles that end below every row's limit.)
+  auto accumulate = [&](int slot, int kb0, bool edge) {
     const uint16_t* vs_ = vring + (slot * AP_KG + kg) * SUBE + (fq >> 1) * HD * 16;
     bf16x8 vf[NO];
 #pragma unroll
     for (int n = 0; n < NO; ++n)
       vf[n] = *(const bf16x8*)(vs_ + (16 * n + fr) * 16 + (((fq & 1) ^ ((fr >> 2) & 1)) << 3));
+    if (edge && kb0 + AP_SUB > kmax) {
+      const uint4 keep = v_keep_mask(kmax - (kb0 + 8 * fq));
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        uint4 u = __builtin_bit_cast(uint4, vf[n]);
+        u.x &= keep.x;
+        u.y &= keep.y;
+        u.z &= keep.z;
+        u.w &= keep.w;
+        vf[n] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
 #pragma unroll
     for (int n = 0; n < NO; ++n)
 #pragma unroll
@@ -284,7 +300,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
       // Scores of the next sub-tile on the matrix cores while the exponentials run on the VALUs.
       scores((j + 1) & 1, snxt);
       exps(scur);
-      accumulate(j & 1);
+      accumulate(j & 1, kb0, false);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -301,7 +317,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NO, 0);
     } else {
       exps(scur);
-      accumulate(j & 1);
+      accumulate(j & 1, kb0, true);
     }
   }
 

@@ -1,7 +1,8 @@
 // Expert-sliced mixture-of-experts FFN for one rank (TensorSharp "Multi-GPU & Multi-Node",
-// section "Supported architectures": the Megatron split inside every expert, gate/up column-
-// parallel and down row-parallel, with a replicated router, so each rank holds 1/N of every
-// expert and a token's selected expert ids mean the same on every rank).
+// section "Supported architectures": each expert is sharded like the dense FFN, its gate and up
+// rows by output column and its down rows by input column, and the router is identical on all
+// ranks; a rank therefore keeps 1/N of every expert, and the expert ids picked for a token are
+// valid on each of them).
 //
 //   router:  logits [T, E] = xn . Wr^T (the decode GEMV), then k_moe_topk: per token the top_k
 //            experts by logit (largest first, equal logits: lower index first) and their weights,
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logi
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = i * 64 + lane;
-    v[i] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    const float z = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    v[i] = z != z ? -INFINITY : z;  // a NaN logit ranks as -inf (below every number)
   }
   bool taken[PER];
 #pragma unroll
@@ -96,7 +98,8 @@ __global__ __launch_bounds__(256) void k_moe_topk64(const float* __restrict__ lo
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const float v = lane < E ? logits[(size_t)t * E + lane] : -INFINITY;
+  const float z = lane < E ? logits[(size_t)t * E + lane] : -INFINITY;
+  const float v = z != z ? -INFINITY : z;  // a NaN logit ranks as -inf (below every number)
   s_z[wave][lane] = v;
   // The wave's own LDS writes must land before its lanes read each other's entries.
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");

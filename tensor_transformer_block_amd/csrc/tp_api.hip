@@ -729,6 +729,75 @@ tp_status tp_dequant_q8_0(const void* codes, const void* scales, float* out, uin
   return TP_OK;
 }
 
+// One region of a rank's packed shard as a plain [rows, K] matrix: the projection the forward
+// path runs on it, for the test helpers below.
+struct Region {
+  const tp_region *w, *s;
+  int K, rows;
+};
+
+static tp_status shard_region(const Dims& x, const tp_shard_layout& L, int32_t which, Region* r) {
+  switch (which) {
+    case 0: *r = Region{&L.qkv, &L.qkv_scale, x.d, x.qkv_rows}; return TP_OK;
+    case 1: *r = Region{&L.o, &L.o_scale, x.qdim, x.d}; return TP_OK;
+    case 2: *r = Region{&L.gate_up, &L.gate_up_scale, x.d, 2 * x.fr}; return TP_OK;
+    case 3: *r = Region{&L.down, &L.down_scale, x.fr, x.d}; return TP_OK;
+  }
+  return fail(TP_ERR_INVALID_ARG, "which=%d must be 0 (qkv), 1 (o), 2 (gate_up) or 3 (down)",
+              which);
+}
+
+static uint64_t project_ws_bytes(const Dims& x, int T, const Region& g) {
+  if (x.wt == TP_DTYPE_BF16 && T <= 64 && use_gemm(x, T, g.K))
+    return tpk::splitk_workspace_bytes(T, g.rows, g.K, false);
+  if (use_q8_gemm(x, T)) return tpk::q8_gemm_workspace_bytes(T, g.rows, g.K, false);
+  return 0;
+}
+
+tp_status tp_shard_project_workspace_size(const tp_block_desc* desc, int32_t which,
+                                          int32_t n_tokens, uint64_t* bytes) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  if (!bytes) return fail(TP_ERR_INVALID_ARG, "bytes is NULL");
+  tp_shard_layout L;
+  make_layout(x, &L);
+  Region g;
+  if (tp_status s = shard_region(x, L, which, &g)) return s;
+  const uint64_t b = project_ws_bytes(x, n_tokens, g);
+  *bytes = b > 0 ? align_up(b) : kAlign;
+  return TP_OK;
+}
+
+tp_status tp_shard_project(const tp_block_desc* desc, int32_t which, const void* shard,
+                           const void* x_in, int32_t n_tokens, float* out, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "n_tokens=%d must be >= 0", n_tokens);
+  tp_shard_layout L;
+  make_layout(x, &L);
+  Region g;
+  if (tp_status s = shard_region(x, L, which, &g)) return s;
+  if (n_tokens == 0) return TP_OK;
+  if (!shard || !x_in || !out) return fail(TP_ERR_INVALID_ARG, "shard, x and out must be non-NULL");
+  if (!aligned16(shard) || !aligned16(x_in) || !aligned16(out))
+    return fail(TP_ERR_INVALID_ARG, "shard, x and out must be 16-byte aligned");
+  if (tpk::gemv_max_tokens(g.K) < 1 && !use_gemm(x, n_tokens, g.K) && !use_q8_gemm(x, n_tokens))
+    return fail(TP_ERR_UNSUPPORTED, "projection with K=%d exceeds the GEMV's 16384", g.K);
+  const uint64_t need = project_ws_bytes(x, n_tokens, g);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu",
+                (unsigned long long)workspace_bytes, (unsigned long long)need);
+  const char* sh = (const char*)shard;
+  hipError_t e = project(x, tpk::EPI_F32, n_tokens, sh + g.w->offset, sh + g.s->offset, g.K,
+                         g.rows, 0, x_in, out, g.rows, (hipStream_t)stream, nullptr,
+                         need > 0 ? (float*)workspace : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "tp_shard_project");
+  g_err.clear();
+  return TP_OK;
+}
+
 tp_status tp_workspace_size(const tp_block_desc* desc, const tp_batch* batch, uint64_t* bytes) {
   Dims x;
   if (tp_status s = check_desc(desc, &x)) return s;

@@ -34,6 +34,17 @@ __device__ __forceinline__ float q8_dequant(float scale, int32_t code) {
   return scale * (float)code;
 }
 
+// Bit mask keeping the first `n` (clamped to [0, 8]) of eight bf16 values packed in 16 bytes:
+// V elements of keys no one has written to are cleared with it before a P.V product.
+__device__ __forceinline__ uint4 v_keep_mask(int n) {
+  n = n < 0 ? 0 : (n > 8 ? 8 : n);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (2 * i < n ? 0x0000ffffu : 0u) | (2 * i + 1 < n ? 0xffff0000u : 0u);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <int AT>
 __device__ __forceinline__ float ld_act(const void* p, size_t i) {
   if constexpr (AT == ACT_F32) return ((const float*)p)[i];

@@ -253,3 +253,18 @@ def test_moe_layout_is_one_nth_and_validates():
     assert st == B.TP_ERR_INVALID_ARG
     B.tp_moe_shard_forward(d, moe(), 0, None, None, 0, None, None, None, None, 0, stream=0)
     B.tp_moe_route(d, moe(), None, None, 0, None, None, None, stream=0)
+
+
+def test_shard_project_validation():
+    """The projection test helper refuses a bad region and a short workspace before any launch,
+    and sizes its workspace for the split-K Q8_0 GEMM of a 64-token batch."""
+    d = desc_of("gemma-q8-decode")
+    st, _ = _err(B.tp_shard_project_workspace_size, d, 7, 1)
+    assert st == B.TP_ERR_INVALID_ARG
+    assert B.tp_shard_project_workspace_size(d, 1, 1) == 256
+    need = B.tp_shard_project_workspace_size(d, 1, 64)
+    assert need > 256
+    st, _ = _err(B.tp_shard_project, d, 1, 256, 512, 64, 1024, 2048, need - 256)
+    assert st == B.TP_ERR_BUFFER_TOO_SMALL
+    st, _ = _err(B.tp_shard_project, d, 4, 256, 512, 1, 1024)
+    assert st == B.TP_ERR_INVALID_ARG

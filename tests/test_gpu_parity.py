@@ -459,7 +459,9 @@ def test_shard_maps_bit_exact(name):
 
 
 def test_q8_dequant_bit_exact():
-    """GPU dequant (the hot path's device function) equals fp16(d) * q computed on the host."""
+    """The library's Q8_0 dequant helper (the device function the embedding lookup and the MoE
+    expert kernels use; the projections are checked by the one-hot test below) equals
+    fp16(d) * q computed on the host."""
     from tensor_transformer_block_amd import binding as B
     from tensor_transformer_block_amd.inputs import q8_0_encode
     import oracle
@@ -477,6 +479,164 @@ def test_q8_dequant_bit_exact():
     torch.cuda.synchronize()
     ref = oracle.dequant_q8_0(aos.reshape(64, -1), 64, 512).reshape(-1)
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+# (workload, rank, tokens per call): one token and four tokens per call run the dequantising
+# GEMV of decode; 64 tokens the matrix-core Q8_0 GEMM split over K (batched decode); 0 means all
+# K one-hot rows in one call, the whole-K tiles of prefill.
+Q8_PROJ_CASES = [("gemma-q8-decode", 0, 1), ("gemma-q8-decode", 1, 1), ("gemma-q8-decode", 1, 4),
+                 ("gemma-q8-decode", 0, 64), ("gemma-q8-decode", 1, 0),
+                 ("llama3-8b-q8-prefill", 3, 1), ("llama3-8b-q8-prefill", 2, 64)]
+_Q8_CACHE = {}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,rank,T", Q8_PROJ_CASES, ids=lambda v: str(v))
+def test_q8_projection_dequant_bit_exact(name, rank, T):
+    """The Q8_0 projections as the forward path runs them (tp_shard_project: the same kernel
+    choice and main loops, with the fp32 partial epilogue of o_proj and down) on one-hot bf16
+    rows: row k of the output is column k of the region as the kernels dequantise it. Every
+    region of rank r's shard (QKV, o, gate/up, down) must equal the oracle's d * q of the same
+    blocks, bit for bit: the dequantised weights are exact in fp32 and a one-hot product adds
+    only zeros to one of them, so any error in forming them shows."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import to_device
+    s = WORKLOADS[name].with_(mode="decode", n_tokens=1, kv_lens=(1,))
+    if name not in _Q8_CACHE:
+        _Q8_CACHE.clear()
+        log(f"q8 projections {name}: generating inputs")
+        inp = make_inputs(s, seed=0)
+        _Q8_CACHE[name] = (inp, oracle.params_f64(inp))
+    inp, p = _Q8_CACHE[name]
+    desc = B.make_desc(s)
+    full = {k: to_device(v, s.w_dtype, "cuda") for k, v in inp.weights.items()}
+    lay = B.tp_shard_weights_size(desc, rank)
+    shard = torch.empty(lay.alloc_bytes, dtype=torch.uint8, device="cuda")
+    B.tp_shard_weights(desc, rank, B.full_weights(full), shard)
+    del full
+    w = oracle.shard_weights(s, p, rank)
+    regions = {0: np.concatenate([w["wq"], w["wk"], w["wv"]]), 1: w["wo"],
+               2: np.concatenate([w["wg"], w["wu"]]), 3: w["wd"]}
+    for which, ref in regions.items():
+        rows, K = ref.shape
+        per = K if T == 0 else T
+        eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+        out = torch.full((K, rows), float("nan"), device="cuda")
+        wsb = B.tp_shard_project_workspace_size(desc, which, per)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        for k0 in range(0, K, per):
+            B.tp_shard_project(desc, which, shard, eye[k0:k0 + per], per, out[k0:k0 + per], ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().T.astype(np.float64)
+        bad = int(np.count_nonzero(got != ref))
+        log(f"q8 {name} rank {rank} region {which} [{rows}x{K}] {per} token(s) per call: "
+            f"{bad} of {got.size} values differ")
+        assert bad == 0, f"region {which}: {bad} dequantised values differ"
+
+
+# Cache slots holding no key: past each sequence's last position, and a page that no sequence owns
+# which the block table's unused entries point at.
+STALE_CASES = ["med-bf16-ragged", "med-bf16-batched-64", "med-bf16-prefill", "med-q8-hd256",
+               "med-q8-hd256-prefill", "med-fp32-g2", "med-bf16-g8"]
+
+
+@pytest.mark.parametrize("name", STALE_CASES)
+def test_unwritten_cache_slots_never_reach_the_output(name):
+    """Page slots no key was written to (past each sequence's last position, and an extra page
+    that the block table's unused entries point at) filled with NaN and Inf bit patterns give the
+    same step, bit for bit, as zero-filled pools: the attention output, every rank's partials,
+    the new K and V, h1 and out (mlxcel issue #488, "Acceptance criteria": no silent wrong
+    results)."""
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import DeviceBlock
+    s = BY_NAME[name]
+    inp = make_inputs(s, seed=17)
+    extra = inp.n_pages
+    inp.n_pages += 1
+    ps = s.page_size
+    used = [-(-int(L) // ps) for L in inp.seq_lens]
+    tab = np.concatenate([inp.block_table, np.full((s.n_seqs, 2), extra, np.int32)], axis=1)
+    for b, n in enumerate(used):
+        tab[b, n:] = extra
+    inp.block_table = np.ascontiguousarray(tab)
+    blk = DeviceBlock(inp)
+    # Slots holding a prior key (the step writes each new token's slot before attending).
+    written = np.zeros((inp.n_pages, ps), dtype=bool)
+    for b in range(s.n_seqs):
+        prior = int(inp.seq_lens[b]) - (s.n_tokens if s.mode == "prefill" else 1)
+        for pos in range(prior):
+            written[tab[b, pos // ps], pos % ps] = True
+    wm = torch.from_numpy(written).cuda()
+    pristine = [(k.clone(), v.clone()) for k, v in zip(blk.k_pages[0], blk.v_pages[0])]
+
+    def run(poison: bool):
+        for r in range(blk.N):
+            kp, vp = blk.k_pages[0][r], blk.v_pages[0][r]
+            kp.copy_(pristine[r][0])
+            vp.copy_(pristine[r][1])
+            if poison:
+                kp.masked_fill_(~wm[:, None, :, None].expand_as(kp), float("nan"))
+                vp.masked_fill_(~wm[:, None, None, :].expand_as(vp), float("inf"))
+                vp[1::2].masked_fill_(~wm[1::2, None, None, :].expand_as(vp[1::2]), float("nan"))
+        d, T, N = blk.desc, blk.T, blk.N
+        res = {}
+        B.tp_partial_reduce(d, T, None, 0, blk.x, None, blk.gamma1, blk.xn)
+        for r in range(N):
+            blk.attn_half(r)
+            _, av, _ = blk.workspace_views()
+            res[f"a r{r}"] = av.clone()
+            res[f"P_attn r{r}"] = blk.partials[r].clone()
+        B.tp_partial_reduce(d, T, blk.partials, N, blk.x, blk.h1, blk.gamma2, blk.xn2)
+        for r in range(N):
+            blk.ffn_half(r)
+        B.tp_partial_reduce(d, T, blk.partials, N, blk.h1, blk.out, None, None)
+        torch.cuda.synchronize()
+        res["h1"], res["out"] = blk.h1.clone(), blk.out.clone()
+        res = {k: v.float().cpu().numpy() for k, v in res.items()}  # exact widening
+        for r in range(N):
+            kn, vn = blk.cache_new_entries(r)
+            res[f"k_new r{r}"], res[f"v_new r{r}"] = kn, vn
+        return res
+
+    clean = run(False)
+    dirty = run(True)
+    for k in clean:
+        assert np.isfinite(clean[k].astype(np.float64)).all(), k
+        a, b = np.ascontiguousarray(clean[k]), np.ascontiguousarray(dirty[k])
+        assert a.shape == b.shape and a.tobytes() == b.tobytes(), k
+    log(f"stale slots {name}: {int((~written).sum())} unwritten slots per head; outputs identical")
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 8), (40, 6), (100, 8)])
+def test_moe_route_nan_logit(E, k):
+    """A NaN router logit ranks as -inf: the selection equals the oracle's rule applied to the
+    logits with the NaN replaced by -inf, the NaN expert is picked only when every other one
+    is, with weight 0, and no weight is NaN."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import to_device
+    from tensor_transformer_block_amd.inputs import _encode
+    s = MED.with_(n_tokens=3, kv_lens=(4,) * 3)
+    moe = MoEShape(E, k, 256)
+    rng = np.random.default_rng(E + k)
+    router = _encode(rng.standard_normal((E, s.d_model)).astype(np.float32) * 0.05, "bf16")
+    router[5, 7] = 0x7FC0  # a NaN weight: expert 5's logit is NaN for every token
+    x = _encode(rng.standard_normal((3, s.d_model)).astype(np.float32), "bf16")
+    rt, xt = to_device(router, "bf16", "cuda"), to_device(x, "bf16", "cuda")
+    z = torch.empty((3, E), device="cuda")
+    ids = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((3, k), device="cuda")
+    B.tp_moe_route(B.make_desc(s), B.make_moe_desc(moe), rt, xt, 3, z, ids, w)
+    torch.cuda.synchronize()
+    zh = t2np(z)
+    assert np.isnan(zh[:, 5]).all()
+    ids_ref, w_ref = oracle.moe_select(np.where(np.isnan(zh), -np.inf, zh), k)
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, ids_ref)
+    wh = t2np(w)
+    assert np.isfinite(wh).all() and nrel(wh, w_ref) <= 1e-5
+    assert (5 in got[0]) == (k == E)
 
 
 def test_empty_batch_is_noop():
