@@ -183,6 +183,18 @@ tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, 
                                        uint64_t workspace_bytes, void* stream, void* ev_begin,
                                        void* ev_end);
 
+/* For callers that cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): tp_block_shard_forward with its workspace taken from a static
+ * device array of the library, 16 MiB per GPU (enough for every decode and 64-token batched-decode
+ * shape of the workloads here), obtained once per device on the first call there and held until
+ * the process ends. The call allocates nothing. A batch whose workspace (tp_workspace_size) is
+ * larger returns TP_ERR_BUFFER_TOO_SMALL before anything is launched. Every call on one GPU
+ * shares that array: calls that may overlap on one GPU (several streams, several threads) race
+ * and must be serialised by the caller. No part of the array needs to start at zero. */
+tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                         const void* shard, const tp_batch* batch, const void* xn,
+                                         const tp_kv_cache* kv, void* partial_out, void* stream);
+
 /* The local copy-and-reduce step [ML-PROB] that stands in for the all-reduce [TS-HOW]:
  *   residual_out[t] = residual_in[t] + (((P_0[t] + P_1[t]) + ...) + P_{n-1}[t])
  * summed in fp32 in rank order (the partials first, then the residual) and rounded once to the

@@ -31,7 +31,7 @@ EXPORTED = (
     "tp_block_shard_forward_timed", "tp_head_size", "tp_head_pack", "tp_embed_lookup",
     "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
     "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
-    "tp_shard_project", "tp_shard_project_workspace_size",
+    "tp_shard_project", "tp_shard_project_workspace_size", "tp_block_shard_forward_noalloc",
 )
 
 
@@ -131,6 +131,7 @@ def lib() -> ctypes.CDLL:
         "tp_moe_shard_forward_timed": [P, P, I32, P, P, I32, P, P, P, P, U64, P, P, P],
         "tp_shard_project": [P, I32, P, P, I32, P, P, U64, P],
         "tp_shard_project_workspace_size": [P, I32, I32, P],
+        "tp_block_shard_forward_noalloc": [P, I32, I32, P, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -257,6 +258,13 @@ def tp_block_shard_forward_timed(desc, rank, half, shard, batch: tp_batch, xn,
         ctypes.byref(desc), rank, half, ptr(shard), ctypes.byref(batch), ptr(xn),
         ctypes.byref(kv) if kv is not None else None, ptr(partial_out), ptr(workspace),
         workspace_bytes, _stream(stream), ev_begin, ev_end))
+
+
+def tp_block_shard_forward_noalloc(desc, rank, half, shard, batch: tp_batch, xn,
+                                   kv: tp_kv_cache | None, partial_out, stream=None) -> None:
+    _check(lib().tp_block_shard_forward_noalloc(
+        ctypes.byref(desc), rank, half, ptr(shard), ctypes.byref(batch), ptr(xn),
+        ctypes.byref(kv) if kv is not None else None, ptr(partial_out), _stream(stream)))
 
 
 def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residual_out, gamma,

@@ -1020,6 +1020,70 @@ tp_status tp_block_shard_forward_timed(const tp_block_desc* desc, int32_t rank, 
                       workspace_bytes, stream, (hipEvent_t)ev_begin, (hipEvent_t)ev_end);
 }
 
+}  // extern "C"
+
+// Workspace of tp_block_shard_forward_noalloc: one array per GPU, loaded with the library and held
+// until the process ends. Host code never passes `scratch` itself (its host-side name is not a
+// device address); it uses the device address hipGetSymbolAddress returns for the current device.
+static constexpr uint64_t kScratchBytes = 16ull << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+tp_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "tp_block_shard_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TP_ERR_UNSUPPORTED, "device %d: the static scratch is tracked for %d devices", dev,
+                kMaxDevices);
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "tp_block_shard_forward_noalloc: hipGetSymbolAddress(scratch)");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank, int32_t half,
+                                         const void* shard, const tp_batch* batch, const void* xn,
+                                         const tp_kv_cache* kv, void* partial_out, void* stream) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
+  if (half != TP_HALF_ATTN && half != TP_HALF_FFN)
+    return fail(TP_ERR_INVALID_ARG, "unknown half %d", half);
+  if (tp_status s = check_batch(x, batch, half == TP_HALF_ATTN)) return s;
+  const uint64_t need = ws_layout(x, *batch).total;
+  if (need > kScratchBytes)
+    return fail(TP_ERR_BUFFER_TOO_SMALL,
+                "this batch needs %llu bytes of workspace; the static scratch of "
+                "tp_block_shard_forward_noalloc holds %llu (pass a workspace to "
+                "tp_block_shard_forward instead)",
+                (unsigned long long)need, (unsigned long long)kScratchBytes);
+  if (batch->n_tokens == 0) {
+    g_err.clear();
+    return TP_OK;
+  }
+  void* ws = nullptr;
+  if (tp_status s = scratch_ptr(&ws)) return s;
+  return forward_impl(desc, rank, half, shard, batch, xn, kv, partial_out, ws, kScratchBytes,
+                      stream, nullptr, nullptr);
+}
+
 tp_status tp_partial_reduce(const tp_block_desc* desc, int32_t n_tokens, const void* partials,
                             int32_t n_partials, const void* residual_in, void* residual_out,
                             const void* gamma, void* normed_out, void* stream) {
