@@ -751,3 +751,34 @@ def test_planted_moe_unnormalised_weights_are_caught(monkeypatch):
     monkeypatch.setattr(ob, "moe_select", wrong)
     with pytest.raises(AssertionError):
         test_moe_ffn_against_library(*MOE_CASES[0])
+
+
+# (workload, sampled token rows or None for all): the sharded oracle against the unsharded one at
+# the workloads' real shapes. The 64-sequence batch and the 2048-token prefill check a few rows
+# (every token's K and V are still produced, since the sampled rows attend to them).
+P1_REAL = [("llama3-8b-decode", None), ("gemma-q8-decode", None),
+           ("llama3-8b-batched", [0, 17, 63]), ("llama-70b-prefill", [0, 1031, 2047])]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,rows", P1_REAL, ids=lambda v: str(v))
+def test_sharded_equals_unsharded_real_shapes(name, rows):
+    """Block-matrix identity at the workloads' own shapes (TensorSharp "How tensor parallelism
+    works": the reduced partials leave every rank with the hidden state the unsharded block
+    computes): every replicated tensor, both partial sums and each rank's owned columns of the
+    attention output and of m agree to 1e-12 normwise."""
+    from tensor_transformer_block_amd.inputs import WORKLOADS
+    s = WORKLOADS[name]
+    inp = make_inputs(s, seed=0)
+    a = oracle.run_block(inp, sharded=True, rows=rows)
+    b = oracle.run_block(inp, sharded=False, rows=rows)
+    for key in ("xn", "h1", "xn2", "out"):
+        assert nrel(a[key], b[key]) <= 1e-12, key
+    assert nrel(a["attn_sum"], b["attn_proj"]) <= 1e-12
+    assert nrel(a["ffn_sum"], b["ffn_proj"]) <= 1e-12
+    hq, hd, fr = s.n_heads // s.tp, s.head_dim, s.ffn_dim // s.tp
+    for r, rk in enumerate(a["ranks"]):
+        assert nrel(rk["a"], b["attn"][:, r * hq * hd:(r + 1) * hq * hd]) <= 1e-12
+        assert nrel(rk["m"], b["m"][:, r * fr:(r + 1) * fr]) <= 1e-12
+        assert nrel(rk["k_new"], b["k_new"][:, r * (s.n_kv_heads // s.tp):
+                                            (r + 1) * (s.n_kv_heads // s.tp)]) <= 1e-12
