@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--vocab", type=int, default=0, help="vocabulary of --head (0: the family's)")
     ap.add_argument("--partial-dtype", choices=("f32", "bf16"), default="f32",
                     help="storage of the rank partials (f32: the default of the library)")
+    ap.add_argument("--staged", action="store_true",
+                    help="issue the step as separate per-rank and reduce calls instead of the "
+                         "one-call step (tp_block_step)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a dispatch of known "
                          "size for scaling hardware byte counters)")
@@ -243,8 +246,15 @@ def main():
         log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
         del src, dst
 
+    if args.staged:
+        def step(c, timed=None):
+            blk.step(c, ffn_events=timed)
+    else:
+        def step(c, timed=None):
+            blk.step_fused(c, timed=timed)
+
     for c in range(copies):
-        blk.step(c)
+        step(c)
     torch.cuda.synchronize()
     graphs = []
     if not args.no_graph:
@@ -252,27 +262,27 @@ def main():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for c in range(copies):
-                blk.step(c)
+                step(c)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                blk.step(c)
+                step(c)
             graphs.append(g)
         # One graph holding a step on every copy in turn (a stack of `copies` blocks, as the
         # layers of a model would be), so a replay's fixed cost is paid once per `copies` steps.
         multi = torch.cuda.CUDAGraph()
         with torch.cuda.graph(multi):
             for c in range(copies):
-                blk.step(c)
+                step(c)
         torch.cuda.synchronize()
 
     def run(i):
         if graphs:
             graphs[i % copies].replay()
         else:
-            blk.step(i % copies)
+            step(i % copies)
 
     def run_steps(k):
         """k consecutive steps, from copy 0: whole multi-step replays, then single steps."""
@@ -283,7 +293,7 @@ def main():
                 graphs[i].replay()
         else:
             for i in range(k):
-                blk.step(i % copies)
+                step(i % copies)
 
     log(f"warmup {args.warmup} steps")
     run_steps(args.warmup)
@@ -320,11 +330,11 @@ def main():
     n_extra = max(5, min(50, args.steps // 10))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(2):
-        blk.step(i % copies)
+        step(i % copies)
     torch.cuda.synchronize()
     e0.record()
     for i in range(n_extra):
-        blk.step(i % copies)
+        step(i % copies)
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / n_extra
@@ -342,15 +352,21 @@ def main():
     # on the launch stream (what a profiler's kernel trace reports). The timed launches sit inside
     # whole block steps, launched eagerly behind a backlog of graph replays, so every one runs in
     # the same context as in the timed steps (after the attention half and the reduce).
-    n_kst = max(1, (args.kernel_iters + s.tp - 1) // s.tp)
-    n_kl = n_kst * s.tp
+    if args.staged:
+        n_kst = max(1, (args.kernel_iters + s.tp - 1) // s.tp)
+        n_kl = n_kst * s.tp
+    else:  # the one-call step times one rank's gate/up per step, the ranks in turn
+        n_kst = n_kl = max(1, args.kernel_iters)
     log(f"timing the gate/up projection ({n_kl} launches in {n_kst} steps)")
     hev = HipEvents(2 * n_kl)
     for i in range(min(64, args.steps)):
         run(i)
     for i in range(n_kst):
-        blk.step(i % copies, ffn_events=[(hev.ev[2 * (i * s.tp + r)], hev.ev[2 * (i * s.tp + r) + 1])
-                                         for r in range(s.tp)])
+        if args.staged:
+            step(i % copies, timed=[(hev.ev[2 * (i * s.tp + r)], hev.ev[2 * (i * s.tp + r) + 1])
+                                    for r in range(s.tp)])
+        else:
+            step(i % copies, timed=(i % s.tp, hev.ev[2 * i], hev.ev[2 * i + 1]))
     torch.cuda.synchronize()
     kdur = [hev.elapsed_s(2 * i, 2 * i + 1) for i in range(n_kl)]
     hev.close()
@@ -383,6 +399,7 @@ def main():
                    "tp_degree_emulated": s.tp, "weights": s.w_dtype, "mode": s.mode,
                    "tokens": s.n_tokens, "kv_len": max(s.kv_lens), "page_size": s.page_size,
                    "cold_copies": copies, "graph": not args.no_graph,
+                   "schedule": "staged" if args.staged else "one-call",
                    "partial_dtype": args.partial_dtype},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
@@ -422,25 +439,30 @@ def bench_stack(args, s):
         st = BlockStack(inps)
     del inps
     stepper = model if model is not None else st
+    fused = not args.staged
+    stepper_step = stepper.step
+    if fused:
+        def stepper_step():
+            stepper.step(fused=True)
     resident = weight_bytes(s) + sum(s.kv_lens) * s.n_kv_heads * s.head_dim * (
         4 if s.act_dtype == "f32" else 2) * 2
     if K * resident < args.cold_bytes:
         log(f"note: the stack holds {K * resident / 1e6:.0f} MB, less than --cold-bytes")
-    stepper.step()
+    stepper_step()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        stepper.step()
+        stepper_step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            stepper.step()
+            stepper_step()
         torch.cuda.synchronize()
-    run = g.replay if g is not None else stepper.step
+    run = g.replay if g is not None else stepper_step
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -457,17 +479,29 @@ def bench_stack(args, s):
     ms = ev0.elapsed_time(ev1) / args.steps
 
     # Gate/up launches timed inside eager stack steps, behind a backlog of replays.
-    n_st = max(1, (args.kernel_iters + K * s.tp - 1) // (K * s.tp))
-    hev = HipEvents(2 * n_st * K * s.tp)
+    if fused:  # one rank's gate/up per block and stack step, the ranks in turn
+        n_st = max(1, (args.kernel_iters + K - 1) // K)
+        hev = HipEvents(2 * n_st * K)
+    else:
+        n_st = max(1, (args.kernel_iters + K * s.tp - 1) // (K * s.tp))
+        hev = HipEvents(2 * n_st * K * s.tp)
     for _ in range(min(16, args.steps)):
         run()
     i = 0
-    for _ in range(n_st):
+    for j in range(n_st):
+        x_in = model.x if model is not None else None
+        if fused:
+            tm = []
+            for _b in st.blocks:
+                tm.append((j % s.tp, hev.ev[2 * i], hev.ev[2 * i + 1]))
+                i += 1
+            st.step(x=x_in, fused=True, timed=tm)
+            continue
         evs = []
         for _b in st.blocks:
             evs.append([(hev.ev[2 * (i + r)], hev.ev[2 * (i + r) + 1]) for r in range(s.tp)])
             i += s.tp
-        st.step(x=model.x if model is not None else None, ffn_events=evs)
+        st.step(x=x_in, ffn_events=evs)
     torch.cuda.synchronize()
     kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(i)]))
     hev.close()
@@ -515,7 +549,8 @@ def bench_stack(args, s):
                    "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "ffn_dim": s.ffn_dim, "tp_degree_emulated": s.tp, "weights": s.w_dtype,
                    "mode": s.mode, "tokens": s.n_tokens, "kv_len": max(s.kv_lens),
-                   "page_size": s.page_size, "graph": not args.no_graph},
+                   "page_size": s.page_size, "graph": not args.no_graph,
+                   "schedule": "staged" if args.staged else "one-call"},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -195,6 +195,37 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
                                          const void* shard, const tp_batch* batch, const void* xn,
                                          const tp_kv_cache* kv, void* partial_out, void* stream);
 
+/* One whole block step for all N ranks in one call [ML-PROB] [TS-HOW]:
+ *   xn = RMSNorm(x) gamma1;  P_r = ATTN half of rank r (r = 0..N-1);
+ *   h1 = x + (((P_0 + P_1) + ...) + P_{N-1});  xn2 = RMSNorm(h1) gamma2;
+ *   P_r = FFN half of rank r;  out = h1 + (((P_0 + P_1) + ...) + P_{N-1}),
+ * as tp_partial_reduce and tp_block_shard_forward called in that order compute it. When every
+ * projection of the step is one decode GEMV launch (at most four tokens, and no more than the
+ * GEMV takes at each row length), the call saves three launches per step: each rank's QKV and
+ * gate/up projections normalise the residual stream themselves (the projection takes
+ * gamma * x and scales its sums by 1/sqrt(mean(x^2) + eps), so the normed input is not rounded
+ * to the activation dtype first, as the separate calls round it; xn and xn2 are still stored,
+ * rounded), and the last rank's o_proj and down projections add all ranks' partials in rank
+ * order plus the residual, with the reduce's arithmetic. The ranks still run in order and every
+ * rank's partial is still stored. Otherwise the call issues exactly the separate calls above.
+ * shards, kv: host arrays of N entries (rank r's packed shard, device pointer; rank r's cache).
+ * x, gamma1, gamma2 (inputs) and xn, h1, xn2, out: activation dtype, [T, d] ([d] for the gammas);
+ * partials: [N, T, d] in partial_dtype (holds the FFN partials on return). workspace: at least
+ * tp_workspace_size bytes. n_tokens == 0 is a no-op. */
+tp_status tp_block_step(const tp_block_desc* desc, const void* const* shards, const tp_batch* batch,
+                        const tp_kv_cache* kv, const void* x, const void* gamma1,
+                        const void* gamma2, void* partials, void* xn, void* h1, void* xn2,
+                        void* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Measurement variant of tp_block_step: ev_begin / ev_end bracket the gate/up projection of rank
+ * timed_rank as in tp_block_shard_forward_timed. Not for graph capture. */
+tp_status tp_block_step_timed(const tp_block_desc* desc, const void* const* shards,
+                              const tp_batch* batch, const tp_kv_cache* kv, const void* x,
+                              const void* gamma1, const void* gamma2, void* partials, void* xn,
+                              void* h1, void* xn2, void* out, void* workspace,
+                              uint64_t workspace_bytes, void* stream, int32_t timed_rank,
+                              void* ev_begin, void* ev_end);
+
 /* The local copy-and-reduce step [ML-PROB] that stands in for the all-reduce [TS-HOW]:
  *   residual_out[t] = residual_in[t] + (((P_0[t] + P_1[t]) + ...) + P_{n-1}[t])
  * summed in fp32 in rank order (the partials first, then the residual) and rounded once to the

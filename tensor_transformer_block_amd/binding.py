@@ -32,6 +32,7 @@ EXPORTED = (
     "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
     "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
     "tp_shard_project", "tp_shard_project_workspace_size", "tp_block_shard_forward_noalloc",
+    "tp_block_step", "tp_block_step_timed",
 )
 
 
@@ -132,6 +133,8 @@ def lib() -> ctypes.CDLL:
         "tp_shard_project": [P, I32, P, P, I32, P, P, U64, P],
         "tp_shard_project_workspace_size": [P, I32, I32, P],
         "tp_block_shard_forward_noalloc": [P, I32, I32, P, P, P, P, P, P],
+        "tp_block_step": [P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P],
+        "tp_block_step_timed": [P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P, I32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -265,6 +268,36 @@ def tp_block_shard_forward_noalloc(desc, rank, half, shard, batch: tp_batch, xn,
     _check(lib().tp_block_shard_forward_noalloc(
         ctypes.byref(desc), rank, half, ptr(shard), ctypes.byref(batch), ptr(xn),
         ctypes.byref(kv) if kv is not None else None, ptr(partial_out), _stream(stream)))
+
+
+def _step_arrays(shards, kv):
+    sh = (ctypes.c_void_p * len(shards))(*[ptr(t) for t in shards])
+    kvs = (tp_kv_cache * len(kv))(*kv)
+    return sh, kvs
+
+
+def tp_block_step(desc, shards, batch: tp_batch, kv, x, gamma1, gamma2, partials, xn, h1, xn2,
+                  out, workspace, workspace_bytes=None, stream=None) -> None:
+    """shards: the N ranks' packed shards; kv: their tp_kv_cache structs (host lists)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    sh, kvs = _step_arrays(shards, kv)
+    _check(lib().tp_block_step(ctypes.byref(desc), sh, ctypes.byref(batch), kvs, ptr(x),
+                               ptr(gamma1), ptr(gamma2), ptr(partials), ptr(xn), ptr(h1),
+                               ptr(xn2), ptr(out), ptr(workspace), workspace_bytes,
+                               _stream(stream)))
+
+
+def tp_block_step_timed(desc, shards, batch: tp_batch, kv, x, gamma1, gamma2, partials, xn, h1,
+                        xn2, out, workspace, timed_rank, ev_begin, ev_end, workspace_bytes=None,
+                        stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    sh, kvs = _step_arrays(shards, kv)
+    _check(lib().tp_block_step_timed(ctypes.byref(desc), sh, ctypes.byref(batch), kvs, ptr(x),
+                                     ptr(gamma1), ptr(gamma2), ptr(partials), ptr(xn), ptr(h1),
+                                     ptr(xn2), ptr(out), ptr(workspace), workspace_bytes,
+                                     _stream(stream), timed_rank, ev_begin, ev_end))
 
 
 def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residual_out, gamma,

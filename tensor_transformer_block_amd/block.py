@@ -157,6 +157,19 @@ class DeviceBlock:
         g, xo = next_norm if next_norm is not None else (None, None)
         B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, g, xo)
 
+    def step_fused(self, copy: int = 0, x=None, timed=None):
+        """The same block step in one library call (tp_block_step): for decode batches the
+        replicated norms and the two reduces run inside the projections next to them, with the
+        same results bit for bit. ``timed``: (rank, begin, end) raw events bracketing that
+        rank's gate/up projection."""
+        x = self.x if x is None else x
+        args = (self.desc, self.shards[copy], self.batch, self.kv[copy], x, self.gamma1,
+                self.gamma2, self.partials, self.xn, self.h1, self.xn2, self.out, self.workspace)
+        if timed is None:
+            B.tp_block_step(*args, self.ws_bytes)
+        else:
+            B.tp_block_step_timed(*args, timed[0], timed[1], timed[2], self.ws_bytes)
+
     # --------------------------------------------------------------------------- readback
     def workspace_views(self):
         """Views of the last forward's intermediates: q [T, Hq/N*hd], a_r [T, Hq/N*hd], m_r."""
@@ -201,11 +214,19 @@ class BlockStack:
     def out(self):
         return self.blocks[-1].out
 
-    def step(self, x=None, ffn_events=None):
+    def step(self, x=None, ffn_events=None, fused=False, timed=None):
         """Every block in order; block i's final reduce also writes block i + 1's input RMSNorm
         (the same rounded residual it would normalise), saving one launch per block boundary.
-        ``ffn_events``: optional per-block lists of per-rank gate/up event pairs."""
+        ``ffn_events``: optional per-block lists of per-rank gate/up event pairs. ``fused``:
+        each block in one tp_block_step call instead (its projections normalise their input
+        themselves, so nothing is carried across the boundary); ``timed``: then optional
+        per-block (rank, begin, end) event triples."""
         x = self.x if x is None else x
+        if fused:
+            for i, blk in enumerate(self.blocks):
+                blk.step_fused(x=x, timed=None if timed is None else timed[i])
+                x = blk.out
+            return
         K = len(self.blocks)
         for i, blk in enumerate(self.blocks):
             nxt = self.blocks[i + 1] if i + 1 < K else None
@@ -252,10 +273,10 @@ class ModelStep:
         self.xn_f = torch.empty_like(b0.x)
         self.logits = torch.empty((b0.T, head.vocab), dtype=torch.float32, device=device)
 
-    def step(self):
+    def step(self, fused=False):
         b0 = self.stack.blocks[0]
         self.head.embed(self.x)
-        self.stack.step(x=self.x)
+        self.stack.step(x=self.x, fused=fused)
         B.tp_partial_reduce(b0.desc, b0.T, None, 0, self.stack.out, None, self.head.gamma_f,
                             self.xn_f)
         self.head.logits(self.xn_f, self.logits)

@@ -19,7 +19,14 @@
 //             and p + gate_off);
 //   EPI_ROPE  the fused QKV epilogue: slots 2k, 2k + 1 hold rows i and i + hd/2 of one head, so
 //             the rotary embedding of q and k is applied in registers, q is stored and k and v are
-//             appended to the rank's paged cache (step 2 of the same section: its own KV cache).
+//             appended to the rank's paged cache (step 2 of the same section: its own KV cache);
+//   EPI_REDUCE, EPI_REDUCE_BF  the last rank's row-parallel projection in the one-call block
+//             step: the partial (fp32, or bf16) plus the local reduce (earlier ranks' partials in
+//             rank order, then the residual).
+// With PRO (FuseArgs::gamma set) the projection's input is RMSNorm(X) * gamma of the residual rows
+// X: the workgroup stages gamma * x (exact in fp32) and the row's sum of squares from the same
+// loads, and scales the finished dot products by 1/sqrt(mean(x^2) + eps), so the norm costs no
+// extra pass, barrier or memory trip.
 #pragma once
 #include "tp_common.h"
 #include "tp_kernels.h"
@@ -68,12 +75,18 @@ inline int gemv_rows_per_wave(int nch, bool paired, long rows) {
   return (paired && r < 2) ? 2 : r;
 }
 
-template <int WT, int AT, int EPI, int NT, int ACTF, int R>
+constexpr int kMaxPrevPartials = 7;  // EPI_REDUCE: tp_degree <= 8
+
+// PRO: the norm prologue; PV: the reduce epilogues' room for earlier partials (1, 3 or 7: every
+// one is fetched ahead of the weight stream and held in registers, so it is sized to the degree).
+template <int WT, int AT, int EPI, int NT, int ACTF, int R, bool PRO, int PV>
 __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
                                               const uint16_t* __restrict__ S, int K, int n_out,
                                               int gate_off, const void* __restrict__ X,
-                                              void* __restrict__ Y, int ldy, RopeEpi re) {
+                                              void* __restrict__ Y, int ldy, RopeEpi re,
+                                              FuseArgs fa) {
   extern __shared__ float xs[];  // [NT][K], then (Q8_0) [NT][K / 16] chunk sums of x
+  __shared__ float red[PRO ? NT : 1][4];  // prologue norm: each wave's sum of squares per token
   constexpr int VE = WFmt<WT>::VE;
   constexpr int WB = WFmt<WT>::WB;
   constexpr int AV = Vec16<AT>::N;
@@ -105,6 +118,34 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   }
   const bool active = ok[0];
   const int nch = K / VE;
+
+  // EPI_REDUCE: the earlier ranks' partials and the residual of this lane's token (lane t stores
+  // token t) are requested first and kept as raw bits until the epilogue, so no wait for them
+  // sits in front of the weight stream.
+  constexpr bool RED = (EPI == EPI_REDUCE || EPI == EPI_REDUCE_BF);
+  constexpr int RV = RED ? R : 1;
+  static_assert(PV >= 1 && PV <= kMaxPrevPartials, "earlier partials held per row");
+  // The loads are unconditional (a lane past the launch's tokens reads token 0, a partial past
+  // n_prev reads partial 0, rows out of range read row 0): guarded loads would be merged with
+  // their defaults at the branch joins, and each merge waits for its load.
+  uint32_t e_prev[RV][PV], e_res[RV];
+  if constexpr (RED) {
+    const int tl = lane < NT ? lane : 0;
+    const bool any_prev = fa.n_prev > 0;
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const size_t idx = (size_t)tl * ldy + row[s];
+      if constexpr (AT == ACT_F32) e_res[s] = ((const uint32_t*)fa.res_in)[idx];
+      else e_res[s] = ((const uint16_t*)fa.res_in)[idx];
+#pragma unroll
+      for (int k = 0; k < PV; ++k) {
+        const size_t pi = any_prev ? (size_t)(k < fa.n_prev ? k : 0) * fa.part_stride + idx : 0;
+        const void* base = any_prev ? fa.prev : fa.res_in;
+        if constexpr (EPI == EPI_REDUCE_BF) e_prev[s][k] = ((const uint16_t*)base)[pi];
+        else e_prev[s][k] = ((const uint32_t*)base)[any_prev ? pi : 0];
+      }
+    }
+  }
 
   const char* wp[R];
   const uint16_t* sp[R];
@@ -161,8 +202,38 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
     }
   }
 
-  for (int i = tid * AV; i < NT * K; i += 256 * AV)
-    Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
+  if constexpr (PRO) {
+    // gamma * x and the squares of x from one load of each; per token, a wave sum per wave.
+    constexpr int EB = AT == ACT_F32 ? 4 : 2;
+    float ssq[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ssq[t] = 0.f;
+    for (int k = tid * AV; k < K; k += 256 * AV) {
+      float g[AV];
+      Vec16<AT>::load((const char*)fa.gamma + (size_t)k * EB, g);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float xv[AV];
+        Vec16<AT>::load((const char*)X + ((size_t)t * K + k) * EB, xv);
+#pragma unroll
+        for (int e = 0; e < AV; ++e) {
+          ssq[t] = fmaf(xv[e], xv[e], ssq[t]);
+          xv[e] *= g[e];
+        }
+#pragma unroll
+        for (int e = 0; e < AV; e += 4)
+          *(float4*)(xs + (size_t)t * K + k + e) = make_float4(xv[e], xv[e + 1], xv[e + 2], xv[e + 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float w = wave_sum(ssq[t]);
+      if (lane == 0) red[t][wave] = w;
+    }
+  } else {
+    for (int i = tid * AV; i < NT * K; i += 256 * AV)
+      Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
+  }
   float* const xq = xs + NT * K;
   if constexpr (WT == W_Q8) {
     __syncthreads();
@@ -178,6 +249,20 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
     }
   }
   __syncthreads();
+  float inv[PRO ? NT : 1];
+  if constexpr (PRO) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float tot = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
+      inv[t] = 1.0f / sqrtf(tot / (float)K + fa.eps);
+    }
+    if (fa.normed_out != nullptr && blockIdx.x == 0) {  // the normed rows, for the caller
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        for (int k = tid; k < K; k += 256)
+          st_act<AT>(fa.normed_out, (size_t)t * K + k, xs[(size_t)t * K + k] * inv[t]);
+    }
+  }
   if (!active) return;
 
   float acc[R][NT];
@@ -235,6 +320,12 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[s][t] = wave_sum(acc[s][t]);
+  if constexpr (PRO) {
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[s][t] *= inv[t];
+  }
 
   // Lane t stores token t's results.
 #pragma unroll
@@ -249,6 +340,34 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
 #pragma unroll
       for (int s = 0; s < R; ++s)
         if (ok[s]) ((float*)Y)[yo + row[s]] = acc[s][t];
+    } else if constexpr (RED) {
+      auto part = [&](uint32_t raw) {
+        return EPI == EPI_REDUCE_BF ? bf16_to_f32(raw) : __uint_as_float(raw);
+      };
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        if (!ok[s]) continue;
+        const size_t idx = yo + row[s];
+        float p = acc[s][t];
+        if constexpr (EPI == EPI_REDUCE_BF) {
+          const uint16_t b = f32_to_bf16(p);
+          ((uint16_t*)Y)[idx] = b;
+          p = bf16_to_f32(b);
+        } else {
+          ((float*)Y)[idx] = p;
+        }
+        // ((P_0 + P_1) + ...) + P_last, then the residual: the reduce kernel's order.
+        float sum = p;
+        if (fa.n_prev > 0) {
+          sum = part(e_prev[s][0]);
+#pragma unroll
+          for (int k = 1; k < PV; ++k)
+            if (k < fa.n_prev) sum += part(e_prev[s][k]);
+          sum += p;
+        }
+        const float res = AT == ACT_F32 ? __uint_as_float(e_res[s]) : bf16_to_f32(e_res[s]);
+        st_act<AT>(fa.res_out, idx, res + sum);
+      }
     } else if constexpr (EPI == EPI_BF16 || EPI == EPI_ACT) {
 #pragma unroll
       for (int s = 0; s < R; ++s)
@@ -287,49 +406,87 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   }
 }
 
+template <int WT, int AT, int EPI, int NT, int ACTF, int R, bool PRO, int PV>
+static hipError_t gemv_launch(dim3 g, size_t lds, const void* W, const uint16_t* S, int K,
+                              int n_out, int gate_off, const void* X, void* Y, int ldy,
+                              const RopeEpi& re, const FuseArgs& fa, hipStream_t st) {
+  // (Q8_0 with 64 KB of staged tokens goes past the default dynamic-LDS limit.)
+  if (lds > 65536) {
+    hipError_t ea = allow_lds((const void*)k_gemv<WT, AT, EPI, NT, ACTF, R, PRO, PV>, (int)lds);
+    if (ea != hipSuccess) return ea;
+  }
+  launch((k_gemv<WT, AT, EPI, NT, ACTF, R, PRO, PV>), g, dim3(256), (uint32_t)lds, st, W, S, K,
+         n_out, gate_off, X, Y, ldy, re, fa);
+  return hipGetLastError();
+}
+
+// The kernel variant for the fusion arguments: the norm prologue only for the projections that
+// consume the normed state, the reduce epilogues sized to the number of earlier partials.
+template <int WT, int AT, int EPI, int NT, int ACTF, int R>
+static hipError_t gemv_variant(dim3 g, size_t lds, const void* W, const uint16_t* S, int K,
+                               int n_out, int gate_off, const void* X, void* Y, int ldy,
+                               const RopeEpi& re, const FuseArgs& fa, hipStream_t st) {
+  constexpr bool CAN_PRO = (EPI == EPI_ROPE || EPI == EPI_GATED);
+  constexpr bool RED = (EPI == EPI_REDUCE || EPI == EPI_REDUCE_BF);
+  if constexpr (CAN_PRO) {
+    if (fa.gamma)
+      return gemv_launch<WT, AT, EPI, NT, ACTF, R, true, 1>(g, lds, W, S, K, n_out, gate_off, X,
+                                                             Y, ldy, re, fa, st);
+  } else if (fa.gamma) {
+    return hipErrorInvalidValue;
+  }
+  if constexpr (RED) {
+    if (fa.n_prev > 3)
+      return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 7>(g, lds, W, S, K, n_out, gate_off, X,
+                                                              Y, ldy, re, fa, st);
+    if (fa.n_prev > 1)
+      return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 3>(g, lds, W, S, K, n_out, gate_off, X,
+                                                              Y, ldy, re, fa, st);
+  }
+  return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 1>(g, lds, W, S, K, n_out, gate_off, X, Y,
+                                                          ldy, re, fa, st);
+}
+
 template <int WT, int AT, int EPI, int ACTF, int R>
 static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n_out, int gate_off,
-                          const void* X, void* Y, int ldy, const RopeEpi& re, hipStream_t st) {
+                          const void* X, void* Y, int ldy, const RopeEpi& re, const FuseArgs& fa,
+                          hipStream_t st) {
   int waves;
   if constexpr (EPI == EPI_GATED) waves = (n_out + R / 2 - 1) / (R / 2);
   else if constexpr (EPI == EPI_ROPE) waves = (n_out / 2 + R / 2 - 1) / (R / 2);
   else waves = (n_out + R - 1) / R;
-  dim3 g((waves + 3) / 4), b(256);
+  const dim3 g((waves + 3) / 4);
   const size_t lds = (size_t)nt * K * sizeof(float) + (WT == W_Q8 ? (size_t)nt * (K / 16) * 4 : 0);
-  // (Q8_0 with 64 KB of staged tokens goes past the default dynamic-LDS limit.)
-#define TPK_GEMV(NTV)                                                                       \
-  do {                                                                                      \
-    if (lds > 65536) {                                                                      \
-      hipError_t ea = allow_lds((const void*)k_gemv<WT, AT, EPI, NTV, ACTF, R>, (int)lds);  \
-      if (ea != hipSuccess) return ea;                                                      \
-    }                                                                                       \
-    launch((k_gemv<WT, AT, EPI, NTV, ACTF, R>), g, b, lds, st, W, S, K, n_out, gate_off, X, \
-           Y, ldy, re);                                                                     \
-  } while (0)
   switch (nt) {
-    case 1: TPK_GEMV(1); break;
-    case 2: TPK_GEMV(2); break;
-    case 3: TPK_GEMV(3); break;
-    case 4: TPK_GEMV(4); break;
-    default: return hipErrorInvalidValue;
+    case 1:
+      return gemv_variant<WT, AT, EPI, 1, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
+                                                    re, fa, st);
+    case 2:
+      return gemv_variant<WT, AT, EPI, 2, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
+                                                    re, fa, st);
+    case 3:
+      return gemv_variant<WT, AT, EPI, 3, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
+                                                    re, fa, st);
+    case 4:
+      return gemv_variant<WT, AT, EPI, 4, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
+                                                    re, fa, st);
   }
-#undef TPK_GEMV
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <int WT, int AT, int EPI, int ACTF>
 static hipError_t gemv_r(int r, int nt, const void* W, const uint16_t* S, int K, int n_out,
                          int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                         hipStream_t st) {
+                         const FuseArgs& fa, hipStream_t st) {
   constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
   switch (r) {
     case 1:
       if constexpr (!PAIRED)
-        return gemv_nt<WT, AT, EPI, ACTF, 1>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+        return gemv_nt<WT, AT, EPI, ACTF, 1>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
       return hipErrorInvalidValue;
-    case 2: return gemv_nt<WT, AT, EPI, ACTF, 2>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
-    case 4: return gemv_nt<WT, AT, EPI, ACTF, 4>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
-    case 8: return gemv_nt<WT, AT, EPI, ACTF, 8>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+    case 2: return gemv_nt<WT, AT, EPI, ACTF, 2>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+    case 4: return gemv_nt<WT, AT, EPI, ACTF, 4>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+    case 8: return gemv_nt<WT, AT, EPI, ACTF, 8>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
   }
   return hipErrorInvalidValue;
 }
@@ -338,35 +495,43 @@ static hipError_t gemv_r(int r, int nt, const void* W, const uint16_t* S, int K,
 template <int WT, int AT>
 hipError_t gemv_format(int epi, int actf, int nt, const void* W, const uint16_t* S, int K,
                        int n_out, int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                       hipStream_t st) {
+                       const FuseArgs& fa, hipStream_t st) {
   const int nch = K / WFmt<WT>::VE;
   const bool paired = (epi == EPI_GATED || epi == EPI_ROPE);
   const int r = gemv_rows_per_wave(nch, paired, epi == EPI_GATED ? 2L * n_out : (long)n_out);
   switch (epi) {
     case EPI_F32:
-      return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
     case EPI_BF16:
-      return gemv_r<WT, AT, EPI_BF16, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return gemv_r<WT, AT, EPI_BF16, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
     case EPI_ACT:
-      return gemv_r<WT, AT, EPI_ACT, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return gemv_r<WT, AT, EPI_ACT, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+    case EPI_REDUCE:
+      return gemv_r<WT, AT, EPI_REDUCE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+    case EPI_REDUCE_BF:
+      return gemv_r<WT, AT, EPI_REDUCE_BF, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa,
+                                              st);
     case EPI_ROPE:
-      return gemv_r<WT, AT, EPI_ROPE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+      return gemv_r<WT, AT, EPI_ROPE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
     case EPI_GATED:
       if (actf == 0)
-        return gemv_r<WT, AT, EPI_GATED, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
-      return gemv_r<WT, AT, EPI_GATED, 1>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, st);
+        return gemv_r<WT, AT, EPI_GATED, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_GATED, 1>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t gemv_f32(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                     int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                    const FuseArgs& fa,
                     hipStream_t st);
 hipError_t gemv_bf16(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                      int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                    const FuseArgs& fa,
                      hipStream_t st);
 hipError_t gemv_q8(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
+                    const FuseArgs& fa,
                    hipStream_t st);
 
 }  // namespace tpk

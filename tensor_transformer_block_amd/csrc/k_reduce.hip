@@ -28,12 +28,6 @@ __device__ __forceinline__ void store8(void* base, size_t idx, const float* v) {
   }
 }
 
-template <int T>
-__device__ __forceinline__ float round_to(float v) {
-  if constexpr (T == ACT_F32) return v;
-  else return bf16_to_f32(f32_to_bf16(v));
-}
-
 // Register image of 8 consecutive values (two 16-byte vectors of fp32 or one of bf16), loaded
 // without conversion so that every load of a row can be in flight before the first is used.
 template <int T>
@@ -131,7 +125,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_partial_reduce(
     }
     if (tid + c * nt < nchunk) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[c][e], v[c][e], ss);
     }
   }
   if (n_part > 0) {

@@ -272,7 +272,11 @@ struct TimedScope {
 
 hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, hipStream_t st,
-                   const tpk::RopeEpi* rope = nullptr, float* splitk_ws = nullptr) {
+                   const tpk::RopeEpi* rope = nullptr, float* splitk_ws = nullptr,
+                   const tpk::FuseArgs* fuse = nullptr) {
+  // The fused norm prologue and reduce epilogue exist on the decode GEMV only.
+  if (fuse && (use_q8_gemm(x, T) || use_gemm(x, T, K) || T > tpk::gemv_max_tokens(K)))
+    return hipErrorInvalidValue;
   if (use_q8_gemm(x, T) && epi != tpk::EPI_ROPE) {
     const bool gated = epi == tpk::EPI_GATED;
     const char* B2 = gated ? W + (size_t)gate_off * K : nullptr;
@@ -287,7 +291,17 @@ hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, 
   }
   const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
   return tpk::launch_gemv(wt, x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16, epi, x.actf, T,
-                          W, S, K, n_out, gate_off, X, Y, ldy, rope, st);
+                          W, S, K, n_out, gate_off, X, Y, ldy, rope, st, fuse);
+}
+
+// The one-call block step folds the replicated norms and the local reduces into the decode GEMVs
+// around them; that needs every projection of the step to be a single GEMV launch.
+bool fused_step_ok(const Dims& x, int T) {
+  if (T < 1 || T > 4 || x.N > 8) return false;
+  const int ks[3] = {x.d, x.qdim, x.fr};
+  for (int K : ks)
+    if (T > tpk::gemv_max_tokens(K) || use_gemm(x, T, K)) return false;
+  return !use_q8_gemm(x, T);
 }
 
 }  // namespace
@@ -855,11 +869,14 @@ tp_status tp_rope_table_init(const tp_block_desc* desc, void* dev_table, uint64_
   return TP_OK;
 }
 
+// fin: norm prologue of the half's first projection (xn is then the residual stream, not its
+// norm); fout: reduce epilogue of its row-parallel projection. Both only on the decode GEMVs.
 static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t half,
                               const void* shard, const tp_batch* batch, const void* xn,
                               const tp_kv_cache* kv, void* partial_out, void* workspace,
                               uint64_t workspace_bytes, void* stream, hipEvent_t evb,
-                              hipEvent_t eve) {
+                              hipEvent_t eve, const tpk::FuseArgs* fin = nullptr,
+                              const tpk::FuseArgs* fout = nullptr) {
   Dims x;
   if (tp_status s = check_desc(desc, &x)) return s;
   if (rank < 0 || rank >= x.N) return fail(TP_ERR_RANK, "rank %d not in [0, %d)", rank, x.N);
@@ -896,7 +913,10 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
   hipStream_t st = (hipStream_t)stream;
   const char* sh = (const char*)shard;
   char* ws = (char*)workspace;
-  const int epi_part = x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16;
+  if ((fin || fout) && !fused_step_ok(x, T))
+    return fail(TP_ERR_UNSUPPORTED, "fused norm / reduce need single-launch decode GEMVs");
+  const int epi_part = fout ? (x.pt == TP_DTYPE_F32 ? tpk::EPI_REDUCE : tpk::EPI_REDUCE_BF)
+                            : (x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16);
   const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
   float* skw = w.gemm_bytes > 0 ? (float*)(ws + w.gemm) : nullptr;
   hipError_t e;
@@ -973,7 +993,7 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
       {
         TimedScope ts(evb, eve);
         e = project(x, tpk::EPI_ROPE, T, sh + L.qkv.offset, sh + L.qkv_scale.offset, x.d,
-                    x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, &re);
+                    x.qkv_rows, 0, xn, qkv, x.qkv_rows, st, &re, nullptr, fin);
       }
       if (e != hipSuccess) return hip_fail(e, "qkv projection");
     }
@@ -986,17 +1006,18 @@ static tp_status forward_impl(const tp_block_desc* desc, int32_t rank, int32_t h
     // bf16 o_proj of a batch (short rows, K = Hq/N * hd): the skinny GEMM reduces its K split
     // inside the workgroup, which measured faster than the split-K form and its epilogue launch.
     e = project(x, epi_part, T, sh + L.o.offset, sh + L.o_scale.offset, x.qdim, x.d, 0,
-                ws + w.attn, partial_out, x.d, st, nullptr, x.wt == TP_DTYPE_BF16 ? nullptr : skw);
+                ws + w.attn, partial_out, x.d, st, nullptr, x.wt == TP_DTYPE_BF16 ? nullptr : skw,
+                fout);
     if (e != hipSuccess) return hip_fail(e, "o projection");
   } else {
     {
       TimedScope ts(evb, eve);
       e = project(x, tpk::EPI_GATED, T, sh + L.gate_up.offset, sh + L.gate_up_scale.offset, x.d,
-                  x.fr, x.fr, xn, ws + w.ffn, x.fr, st, nullptr, skw);
+                  x.fr, x.fr, xn, ws + w.ffn, x.fr, st, nullptr, skw, fin);
     }
     if (e != hipSuccess) return hip_fail(e, "gate/up projection");
     e = project(x, epi_part, T, sh + L.down.offset, sh + L.down_scale.offset, x.fr, x.d, 0,
-                ws + w.ffn, partial_out, x.d, st, nullptr, skw);
+                ws + w.ffn, partial_out, x.d, st, nullptr, skw, fout);
     if (e != hipSuccess) return hip_fail(e, "down projection");
   }
   g_err.clear();
@@ -1082,6 +1103,105 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
   if (tp_status s = scratch_ptr(&ws)) return s;
   return forward_impl(desc, rank, half, shard, batch, xn, kv, partial_out, ws, kScratchBytes,
                       stream, nullptr, nullptr);
+}
+
+static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
+                           const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                           const void* gamma1, const void* gamma2, void* partials, void* xn,
+                           void* h1, void* xn2, void* out, void* workspace,
+                           uint64_t workspace_bytes, void* stream, int32_t timed_rank,
+                           hipEvent_t evb, hipEvent_t eve) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (tp_status s = check_batch(x, batch, true)) return s;
+  const int T = batch->n_tokens, N = x.N;
+  if (T == 0) {
+    g_err.clear();
+    return TP_OK;
+  }
+  if (!shards || !kv) return fail(TP_ERR_INVALID_ARG, "shards and kv must be non-NULL arrays");
+  if (!x_in || !gamma1 || !gamma2 || !partials || !xn || !h1 || !xn2 || !out)
+    return fail(TP_ERR_INVALID_ARG,
+                "x, gamma1, gamma2, partials, xn, h1, xn2 and out must be non-NULL");
+  const void* bufs[8] = {x_in, gamma1, gamma2, partials, xn, h1, xn2, out};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return fail(TP_ERR_INVALID_ARG, "step buffers must be 16-byte aligned");
+  const size_t pstride = (size_t)T * x.d;
+  const size_t pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  char* P = (char*)partials;
+  auto part = [&](int r) { return (void*)(P + (size_t)r * pstride * pbytes); };
+  auto timing = [&](int r) -> std::pair<hipEvent_t, hipEvent_t> {
+    return r == timed_rank ? std::make_pair(evb, eve) : std::make_pair(hipEvent_t{}, hipEvent_t{});
+  };
+  if (!fused_step_ok(x, T)) {
+    // The staged sequence of the same library calls.
+    if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
+      return s;
+    for (int r = 0; r < N; ++r)
+      if (tp_status s = forward_impl(desc, r, TP_HALF_ATTN, shards[r], batch, xn, &kv[r], part(r),
+                                     workspace, workspace_bytes, stream, nullptr, nullptr))
+        return s;
+    if (tp_status s = tp_partial_reduce(desc, T, partials, N, x_in, h1, gamma2, xn2, stream))
+      return s;
+    for (int r = 0; r < N; ++r) {
+      const auto ev = timing(r);
+      if (tp_status s = forward_impl(desc, r, TP_HALF_FFN, shards[r], batch, xn2, nullptr, part(r),
+                                     workspace, workspace_bytes, stream, ev.first, ev.second))
+        return s;
+    }
+    return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
+  }
+  // Fused schedule: every rank's first projection normalises the residual stream itself, and
+  // the last rank's row-parallel projection adds all ranks' partials (rank order) and the
+  // residual. The partials are still stored per rank.
+  tpk::FuseArgs fin{};
+  fin.eps = x.eps;
+  tpk::FuseArgs fout{};
+  fout.prev = partials;
+  fout.part_stride = pstride;
+  fout.n_prev = N - 1;
+  for (int r = 0; r < N; ++r) {
+    fin.gamma = gamma1;
+    fin.normed_out = r == 0 ? xn : nullptr;
+    fout.res_in = x_in;
+    fout.res_out = h1;
+    if (tp_status s = forward_impl(desc, r, TP_HALF_ATTN, shards[r], batch, x_in, &kv[r], part(r),
+                                   workspace, workspace_bytes, stream, nullptr, nullptr, &fin,
+                                   r == N - 1 ? &fout : nullptr))
+      return s;
+  }
+  for (int r = 0; r < N; ++r) {
+    fin.gamma = gamma2;
+    fin.normed_out = r == 0 ? xn2 : nullptr;
+    fout.res_in = h1;
+    fout.res_out = out;
+    const auto ev = timing(r);
+    if (tp_status s = forward_impl(desc, r, TP_HALF_FFN, shards[r], batch, h1, nullptr, part(r),
+                                   workspace, workspace_bytes, stream, ev.first, ev.second, &fin,
+                                   r == N - 1 ? &fout : nullptr))
+      return s;
+  }
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_block_step(const tp_block_desc* desc, const void* const* shards, const tp_batch* batch,
+                        const tp_kv_cache* kv, const void* x, const void* gamma1,
+                        const void* gamma2, void* partials, void* xn, void* h1, void* xn2,
+                        void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
+  return step_impl(desc, shards, batch, kv, x, gamma1, gamma2, partials, xn, h1, xn2, out,
+                   workspace, workspace_bytes, stream, -1, nullptr, nullptr);
+}
+
+tp_status tp_block_step_timed(const tp_block_desc* desc, const void* const* shards,
+                              const tp_batch* batch, const tp_kv_cache* kv, const void* x,
+                              const void* gamma1, const void* gamma2, void* partials, void* xn,
+                              void* h1, void* xn2, void* out, void* workspace,
+                              uint64_t workspace_bytes, void* stream, int32_t timed_rank,
+                              void* ev_begin, void* ev_end) {
+  return step_impl(desc, shards, batch, kv, x, gamma1, gamma2, partials, xn, h1, xn2, out,
+                   workspace, workspace_bytes, stream, timed_rank, (hipEvent_t)ev_begin,
+                   (hipEvent_t)ev_end);
 }
 
 tp_status tp_partial_reduce(const tp_block_desc* desc, int32_t n_tokens, const void* partials,

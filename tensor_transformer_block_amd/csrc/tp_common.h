@@ -57,6 +57,12 @@ __device__ __forceinline__ void st_act(void* p, size_t i, float v) {
   else ((uint16_t*)p)[i] = f32_to_bf16(v);
 }
 
+template <int T>
+__device__ __forceinline__ float round_to(float v) {
+  if constexpr (T == ACT_F32) return v;
+  else return bf16_to_f32(f32_to_bf16(v));
+}
+
 // 16-byte vector of activations widened to fp32: 4 (fp32) or 8 (bf16) values.
 template <int AT> struct Vec16;
 template <> struct Vec16<ACT_F32> {

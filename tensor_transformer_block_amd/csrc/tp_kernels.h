@@ -9,7 +9,8 @@ namespace tpk {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
-enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3, EPI_ROPE = 4 };
+enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3, EPI_ROPE = 4,
+                EPI_REDUCE = 5, EPI_REDUCE_BF = 6 };
 
 // Optional timing of one projection by kernel execution (not by stream events): while `stop` is
 // set, every launch below goes through hipExtLaunchKernelGGL, the first one also recording
@@ -42,6 +43,24 @@ struct RopeEpi {
   void* v_pages;
   int t0;             // first token of this launch's token group
   int mode, max_pages, ps, n_pages, pos_limit, hq, hk, hd;
+};
+
+// The replicated work of the one-call block step, folded into the decode GEMVs that border it.
+//   Prologue (gamma != NULL; the QKV and gate/up projections): the token rows X are the residual
+//     stream and the projection's input is RMSNorm(X) * gamma (fp32, not rounded to the
+//     activation dtype); workgroup 0 also stores it, rounded, to normed_out when that is not NULL.
+//   EPI_REDUCE / EPI_REDUCE_BF (the o_proj and down projections of the last rank): the partial is
+//     stored as with the fp32 / bf16 partial epilogue, and res_out = res_in + (((P_0 + P_1) + ...)
+//     + P_{n_prev}) in fp32 with one rounding, P_0..P_{n_prev-1} read from `prev`.
+struct FuseArgs {
+  const void* gamma;
+  float eps;
+  void* normed_out;
+  const void* prev;
+  size_t part_stride;  // elements from one rank's partial to the next
+  int n_prev;
+  const void* res_in;
+  void* res_out;
 };
 
 // Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device; done once per (kernel,
@@ -77,7 +96,7 @@ hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* pa
 int gemv_max_tokens(int K);
 hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, const void* S,
                        int K, int n_out, int gate_off, const void* X, void* Y, int ldy,
-                       const RopeEpi* rope, hipStream_t st);
+                       const RopeEpi* rope, hipStream_t st, const FuseArgs* fuse = nullptr);
 
 // k_gemm.hip
 // Split-K projection of M <= 64 tokens; `part` holds the fp32 split tiles
