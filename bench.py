@@ -589,20 +589,21 @@ def bench_moe(args, s, moe):
     minp = make_moe_inputs(s, moe, seed=args.seed)
     mb = MoEBlock(inp, minp, copies=copies)
     del minp
+    mstep = mb.step if args.staged else mb.step_fused
     for c in range(copies):
-        mb.step(c)
+        mstep(c)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for c in range(copies):
-            mb.step(c)
+            mstep(c)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     multi = torch.cuda.CUDAGraph()
     with torch.cuda.graph(multi):
         for c in range(copies):
-            mb.step(c)
+            mstep(c)
     torch.cuda.synchronize()
 
     def run_steps(k):
@@ -622,7 +623,7 @@ def bench_moe(args, s, moe):
     ms = ev0.elapsed_time(ev1) / n
 
     # The dominant kernels: one rank's expert FFN (gate/up and down over the selected experts),
-    # timed inside eager MoE steps behind a backlog of replays.
+    # timed inside eager MoE steps (the separate calls) behind a backlog of replays.
     n_st = max(1, (args.kernel_iters + s.tp - 1) // s.tp)
     hev = HipEvents(2 * n_st * s.tp)
     for _ in range(min(16, args.steps)):
@@ -670,7 +671,8 @@ def bench_moe(args, s, moe):
                    "n_kv_heads": s.n_kv_heads, "head_dim": hd, "n_experts": moe.n_experts,
                    "top_k": moe.top_k, "expert_ffn": moe.expert_ffn, "tp_degree_emulated": s.tp,
                    "weights": s.w_dtype, "mode": s.mode, "tokens": s.n_tokens,
-                   "kv_len": max(s.kv_lens), "cold_copies": copies, "graph": True},
+                   "kv_len": max(s.kv_lens), "cold_copies": copies, "graph": True,
+                   "schedule": "staged" if args.staged else "one-call"},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

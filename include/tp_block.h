@@ -339,6 +339,24 @@ tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_des
                                      void* workspace, uint64_t workspace_bytes, void* stream,
                                      void* ev_begin, void* ev_end);
 
+/* One whole MoE block step for all N ranks in one call: the attention halves as in
+ * tp_block_step, h1 and xn2 = RMSNorm(h1) gamma2, the replicated router (tp_moe_route), every
+ * rank's expert half (tp_moe_shard_forward) and out = h1 + (((P_0 + P_1) + ...) + P_{N-1}).
+ * For decode batches whose dense projections are single GEMV launches the norms and reduces are
+ * folded into the neighbouring projections as in tp_block_step (the router's input is the
+ * unrounded norm of h1; xn2 is stored rounded for the experts), saving three launches; otherwise
+ * the separate calls run. shards (dense attention shards), moe_shards, kv: host arrays of N
+ * entries. Buffers as in tp_block_step and tp_moe_route; workspace: tp_workspace_size bytes,
+ * moe_workspace: tp_moe_workspace_size bytes. n_tokens == 0 is a no-op. */
+tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
+                            const void* const* shards, const void* const* moe_shards,
+                            const tp_batch* batch, const tp_kv_cache* kv, const void* x,
+                            const void* gamma1, const void* gamma2, const void* router,
+                            void* partials, void* xn, void* h1, void* xn2, void* out,
+                            float* logits, int32_t* topk_ids, float* topk_weights,
+                            void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                            uint64_t moe_workspace_bytes, void* stream);
+
 const char* tp_status_str(tp_status status);
 /* Detail of the calling thread's last failure ("" if none). */
 const char* tp_last_error(void);

@@ -334,6 +334,15 @@ class MoEBlock:
                                          b.T, self.ids, self.weights, out, self.workspace,
                                          events[0], events[1], self.ws_bytes)
 
+    def step_fused(self, copy: int = 0):
+        """The same MoE block step in one library call (tp_moe_block_step): for decode batches
+        the norms and the reduces run inside the neighbouring projections."""
+        b = self.attn
+        B.tp_moe_block_step(b.desc, self.moe, b.shards[copy], self.shards[copy], b.batch,
+                            b.kv[copy], b.x, b.gamma1, b.gamma2, self.router, b.partials, b.xn,
+                            b.h1, b.xn2, b.out, self.logits, self.ids, self.weights, b.workspace,
+                            self.workspace, b.ws_bytes, self.ws_bytes)
+
     def step(self, copy: int = 0, moe_events=None):
         b = self.attn
         d, T, N = b.desc, b.T, b.N

@@ -426,7 +426,8 @@ template <int WT, int AT, int EPI, int NT, int ACTF, int R>
 static hipError_t gemv_variant(dim3 g, size_t lds, const void* W, const uint16_t* S, int K,
                                int n_out, int gate_off, const void* X, void* Y, int ldy,
                                const RopeEpi& re, const FuseArgs& fa, hipStream_t st) {
-  constexpr bool CAN_PRO = (EPI == EPI_ROPE || EPI == EPI_GATED);
+  // (EPI_F32 with the prologue: the MoE router on the block's residual stream.)
+  constexpr bool CAN_PRO = (EPI == EPI_ROPE || EPI == EPI_GATED || EPI == EPI_F32);
   constexpr bool RED = (EPI == EPI_REDUCE || EPI == EPI_REDUCE_BF);
   if constexpr (CAN_PRO) {
     if (fa.gamma)

@@ -245,14 +245,17 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
 // whatever Fr is, and add w_j times each chunk's dot product with m.
 constexpr int MOE_DR = 2, MOE_DU = 8;  // rows per wave, chunks per lane in flight per row
 
-template <int WT, int AT, int PT>
+// PV > 0: the last rank of the one-call MoE block also adds the earlier ranks' partials (up to PV
+// of them, in rank order) and the residual, as the reduce kernel would (FuseArgs as for the
+// decode GEMV's reduce epilogue); their values are requested before the weight stream.
+template <int WT, int AT, int PT, int PV>
 __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
                                                   const uint16_t* __restrict__ Sd, int d, int Fr,
                                                   int E, int top_k,
                                                   const int32_t* __restrict__ ids,
                                                   const float* __restrict__ wts,
                                                   const void* __restrict__ Min,
-                                                  void* __restrict__ P) {
+                                                  void* __restrict__ P, FuseArgs fa) {
   extern __shared__ float ms[];  // [top_k * Fr]
   __shared__ int s_e[kMoeMaxTopK];
   __shared__ float s_w[kMoeMaxTopK];
@@ -273,6 +276,24 @@ __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
   int nrow[MOE_DR];
 #pragma unroll
   for (int s = 0; s < MOE_DR; ++s) nrow[s] = n0 + s < d ? n0 + s : d - 1;
+  constexpr int PR = PV > 0 ? PV : 1, RR = PV > 0 ? MOE_DR : 1;
+  uint32_t e_prev[RR][PR], e_res[RR];
+  if constexpr (PV > 0) {  // unconditional, clamped loads (no waits at branch joins)
+    const bool any_prev = fa.n_prev > 0;
+#pragma unroll
+    for (int s = 0; s < MOE_DR; ++s) {
+      const size_t o = (size_t)t * d + nrow[s];
+      if constexpr (AT == ACT_F32) e_res[s] = ((const uint32_t*)fa.res_in)[o];
+      else e_res[s] = ((const uint16_t*)fa.res_in)[o];
+#pragma unroll
+      for (int k = 0; k < PV; ++k) {
+        const size_t pi = any_prev ? (size_t)(k < fa.n_prev ? k : 0) * fa.part_stride + o : 0;
+        const void* base = any_prev ? fa.prev : fa.res_in;
+        if constexpr (PT == ACT_BF16) e_prev[s][k] = ((const uint16_t*)base)[pi];
+        else e_prev[s][k] = ((const uint32_t*)base)[any_prev ? pi : 0];
+      }
+    }
+  }
   float acc[MOE_DR];
 #pragma unroll
   for (int s = 0; s < MOE_DR; ++s) acc[s] = 0.f;
@@ -313,17 +334,69 @@ __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
     for (int s = 0; s < MOE_DR; ++s) {
       if (n0 + s >= d) continue;
       const size_t o = (size_t)t * d + n0 + s;
-      if constexpr (PT == ACT_F32) ((float*)P)[o] = acc[s];
-      else ((uint16_t*)P)[o] = f32_to_bf16(acc[s]);
+      float p = acc[s];
+      if constexpr (PT == ACT_F32) {
+        ((float*)P)[o] = p;
+      } else {
+        const uint16_t b = f32_to_bf16(p);
+        ((uint16_t*)P)[o] = b;
+        p = bf16_to_f32(b);
+      }
+      if constexpr (PV > 0) {
+        auto part = [&](uint32_t raw) {
+          return PT == ACT_BF16 ? bf16_to_f32(raw) : __uint_as_float(raw);
+        };
+        float sum = p;
+        if (fa.n_prev > 0) {
+          sum = part(e_prev[s][0]);
+#pragma unroll
+          for (int k = 1; k < PV; ++k)
+            if (k < fa.n_prev) sum += part(e_prev[s][k]);
+          sum += p;
+        }
+        const float res = AT == ACT_F32 ? __uint_as_float(e_res[s]) : bf16_to_f32(e_res[s]);
+        st_act<AT>(fa.res_out, o, res + sum);
+      }
     }
   }
+}
+
+template <int WT, int AT, int PT, int PV>
+static hipError_t moe_down_launch(dim3 g, size_t lds, hipStream_t st, const char* wd,
+                                  const uint16_t* sd, int d, int Fr, int E, int top_k,
+                                  const int32_t* ids, const float* wts, const void* M, void* P,
+                                  const FuseArgs& fa) {
+  if (lds > 65536) {
+    hipError_t ea = allow_lds((const void*)k_moe_down<WT, AT, PT, PV>, (int)lds);
+    if (ea != hipSuccess) return ea;
+  }
+  launch((k_moe_down<WT, AT, PT, PV>), g, dim3(256), (uint32_t)lds, st, wd, sd, d, Fr, E, top_k,
+         ids, wts, M, P, fa);
+  return hipGetLastError();
+}
+
+// The down kernel for the partial dtype, with the reduce epilogue when `fuse` is given.
+template <int WT, int AT, int PT>
+static hipError_t moe_down_variant(dim3 g, size_t lds, hipStream_t st, const char* wd,
+                                   const uint16_t* sd, int d, int Fr, int E, int top_k,
+                                   const int32_t* ids, const float* wts, const void* M, void* P,
+                                   const FuseArgs* fuse) {
+  const FuseArgs fa = fuse ? *fuse : FuseArgs{};
+  if (!fuse)
+    return moe_down_launch<WT, AT, PT, 0>(g, lds, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P, fa);
+  if (fa.n_prev > 3)
+    return moe_down_launch<WT, AT, PT, 7>(g, lds, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P, fa);
+  if (fa.n_prev > 1)
+    return moe_down_launch<WT, AT, PT, 3>(g, lds, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P, fa);
+  return moe_down_launch<WT, AT, PT, 1>(g, lds, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P, fa);
 }
 
 template <int WT, int AT>
 static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, const void* Wu,
                               const void* Su, const void* Wd, const void* Sd, int d, int Fr, int E,
                               int top_k, int T, const int32_t* ids, const float* wts,
-                              const void* X, void* M, void* P, hipStream_t st) {
+                              const void* X, void* M, void* P, hipStream_t st,
+                              const FuseArgs* fuse) {
   const int np = top_k * Fr;
   const dim3 gu((np + 4 * MOE_PW - 1) / (4 * MOE_PW), T), b(256);
   const size_t lds_gu = (size_t)d * sizeof(float);
@@ -342,36 +415,31 @@ static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, 
   if (e != hipSuccess) return e;
   const dim3 gd((d + 4 * MOE_DR - 1) / (4 * MOE_DR), T);
   const size_t lds_d = (size_t)np * sizeof(float);
-  if (pt == ACT_F32) {
-    if (lds_d > 65536) {
-      hipError_t ea = allow_lds((const void*)k_moe_down<WT, AT, ACT_F32>, (int)lds_d);
-      if (ea != hipSuccess) return ea;
-    }
-    launch((k_moe_down<WT, AT, ACT_F32>), gd, b, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P);
-  } else {
-    if (lds_d > 65536) {
-      hipError_t ea = allow_lds((const void*)k_moe_down<WT, AT, ACT_BF16>, (int)lds_d);
-      if (ea != hipSuccess) return ea;
-    }
-    launch((k_moe_down<WT, AT, ACT_BF16>), gd, b, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P);
-  }
-  return hipGetLastError();
+  if (pt == ACT_F32)
+    return moe_down_variant<WT, AT, ACT_F32>(gd, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M,
+                                             P, fuse);
+  return moe_down_variant<WT, AT, ACT_BF16>(gd, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P,
+                                            fuse);
 }
 
 hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, const void* Sg,
                           const void* Wu, const void* Su, const void* Wd, const void* Sd, int d,
                           int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
-                          const void* X, void* M, void* P, hipStream_t st) {
+                          const void* X, void* M, void* P, hipStream_t st,
+                          const FuseArgs* fuse) {
   if (T <= 0) return hipSuccess;
+  if (fuse && (!fuse->res_in || !fuse->res_out || fuse->n_prev < 0 ||
+               fuse->n_prev > kMaxPrevPartials || (fuse->n_prev > 0 && !fuse->prev)))
+    return hipErrorInvalidValue;
   if (wt == W_F32 && at == ACT_F32)
     return moe_ffn_fmt<W_F32, ACT_F32>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T, ids,
-                                       wts, X, M, P, st);
+                                       wts, X, M, P, st, fuse);
   if (wt == W_BF16 && at == ACT_BF16)
     return moe_ffn_fmt<W_BF16, ACT_BF16>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T,
-                                         ids, wts, X, M, P, st);
+                                         ids, wts, X, M, P, st, fuse);
   if (wt == W_Q8 && at == ACT_BF16)
     return moe_ffn_fmt<W_Q8, ACT_BF16>(actf, pt, Wg, Sg, Wu, Su, Wd, Sd, d, Fr, E, top_k, T, ids,
-                                       wts, X, M, P, st);
+                                       wts, X, M, P, st, fuse);
   return hipErrorInvalidValue;
 }
 

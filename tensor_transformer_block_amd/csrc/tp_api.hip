@@ -674,7 +674,7 @@ static tp_status moe_forward_impl(const tp_block_desc* desc, const tp_moe_desc* 
                                   int32_t n_tokens, const int32_t* topk_ids,
                                   const float* topk_weights, void* partial_out, void* workspace,
                                   uint64_t workspace_bytes, void* stream, hipEvent_t evb,
-                                  hipEvent_t eve) {
+                                  hipEvent_t eve, const tpk::FuseArgs* fout = nullptr) {
   Dims x;
   MoeDims m;
   if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
@@ -706,7 +706,7 @@ static tp_status moe_forward_impl(const tp_block_desc* desc, const tp_moe_desc* 
     e = tpk::launch_moe_ffn(wt, at, x.actf, pt, sh + L.gate.offset, sh + L.gate_scale.offset,
                             sh + L.up.offset, sh + L.up_scale.offset, sh + L.down.offset,
                             sh + L.down_scale.offset, x.d, m.fr, m.E, m.k, n_tokens, topk_ids,
-                            topk_weights, xn, workspace, partial_out, (hipStream_t)stream);
+                            topk_weights, xn, workspace, partial_out, (hipStream_t)stream, fout);
   }
   if (e != hipSuccess) return hip_fail(e, "moe ffn");
   g_err.clear();
@@ -1105,6 +1105,37 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
                       stream, nullptr, nullptr);
 }
 
+// The attention halves of every rank with the fused norm and reduce (the decode GEMV path):
+// rank r's QKV projection normalises x itself (rank 0 also stores xn) and the last rank's o_proj
+// leaves h1 = x + (((P_0 + P_1) + ...) + P_{N-1}).
+static tp_status attn_halves_fused(const tp_block_desc* desc, const Dims& x,
+                                   const void* const* shards, const tp_batch* batch,
+                                   const tp_kv_cache* kv, const void* x_in, const void* gamma1,
+                                   void* partials, void* xn, void* h1, void* workspace,
+                                   uint64_t workspace_bytes, void* stream) {
+  const int T = batch->n_tokens, N = x.N;
+  const size_t pstride = (size_t)T * x.d;
+  const size_t pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  tpk::FuseArgs fin{};
+  fin.eps = x.eps;
+  fin.gamma = gamma1;
+  tpk::FuseArgs fout{};
+  fout.prev = partials;
+  fout.part_stride = pstride;
+  fout.n_prev = N - 1;
+  fout.res_in = x_in;
+  fout.res_out = h1;
+  for (int r = 0; r < N; ++r) {
+    fin.normed_out = r == 0 ? xn : nullptr;
+    void* pr = (char*)partials + (size_t)r * pstride * pbytes;
+    if (tp_status s = forward_impl(desc, r, TP_HALF_ATTN, shards[r], batch, x_in, &kv[r], pr,
+                                   workspace, workspace_bytes, stream, nullptr, nullptr, &fin,
+                                   r == N - 1 ? &fout : nullptr))
+      return s;
+  }
+  return TP_OK;
+}
+
 static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
                            const void* gamma1, const void* gamma2, void* partials, void* xn,
@@ -1154,22 +1185,15 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
   // Fused schedule: every rank's first projection normalises the residual stream itself, and
   // the last rank's row-parallel projection adds all ranks' partials (rank order) and the
   // residual. The partials are still stored per rank.
+  if (tp_status s = attn_halves_fused(desc, x, shards, batch, kv, x_in, gamma1, partials, xn, h1,
+                                      workspace, workspace_bytes, stream))
+    return s;
   tpk::FuseArgs fin{};
   fin.eps = x.eps;
   tpk::FuseArgs fout{};
   fout.prev = partials;
   fout.part_stride = pstride;
   fout.n_prev = N - 1;
-  for (int r = 0; r < N; ++r) {
-    fin.gamma = gamma1;
-    fin.normed_out = r == 0 ? xn : nullptr;
-    fout.res_in = x_in;
-    fout.res_out = h1;
-    if (tp_status s = forward_impl(desc, r, TP_HALF_ATTN, shards[r], batch, x_in, &kv[r], part(r),
-                                   workspace, workspace_bytes, stream, nullptr, nullptr, &fin,
-                                   r == N - 1 ? &fout : nullptr))
-      return s;
-  }
   for (int r = 0; r < N; ++r) {
     fin.gamma = gamma2;
     fin.normed_out = r == 0 ? xn2 : nullptr;
@@ -1181,6 +1205,82 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
                                    r == N - 1 ? &fout : nullptr))
       return s;
   }
+  g_err.clear();
+  return TP_OK;
+}
+
+tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
+                            const void* const* shards, const void* const* moe_shards,
+                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                            const void* gamma1, const void* gamma2, const void* router,
+                            void* partials, void* xn, void* h1, void* xn2, void* out,
+                            float* logits, int32_t* topk_ids, float* topk_weights,
+                            void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                            uint64_t moe_workspace_bytes, void* stream) {
+  Dims x;
+  MoeDims m;
+  if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
+  if (tp_status s = check_batch(x, batch, true)) return s;
+  const int T = batch->n_tokens, N = x.N;
+  if (T == 0) {
+    g_err.clear();
+    return TP_OK;
+  }
+  if (!shards || !moe_shards || !kv)
+    return fail(TP_ERR_INVALID_ARG, "shards, moe_shards and kv must be non-NULL arrays");
+  if (!x_in || !gamma1 || !gamma2 || !router || !partials || !xn || !h1 || !xn2 || !out ||
+      !logits || !topk_ids || !topk_weights)
+    return fail(TP_ERR_INVALID_ARG, "every buffer of the MoE block step must be non-NULL");
+  const void* bufs[10] = {x_in, gamma1, gamma2, router, partials, xn, h1, xn2, out, logits};
+  for (const void* b : bufs)
+    if (!aligned16(b)) return fail(TP_ERR_INVALID_ARG, "step buffers must be 16-byte aligned");
+  const size_t pstride = (size_t)T * x.d;
+  const size_t pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  auto part = [&](int r) { return (void*)((char*)partials + (size_t)r * pstride * pbytes); };
+  const bool fused = fused_step_ok(x, T);
+  if (fused) {
+    if (tp_status s = attn_halves_fused(desc, x, shards, batch, kv, x_in, gamma1, partials, xn,
+                                        h1, workspace, workspace_bytes, stream))
+      return s;
+    // The router normalises h1 itself and stores xn2 for the experts.
+    tpk::FuseArgs fin{};
+    fin.eps = x.eps;
+    fin.gamma = gamma2;
+    fin.normed_out = xn2;
+    hipStream_t st = (hipStream_t)stream;
+    const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+    const int wt = x.at == TP_DTYPE_F32 ? tpk::W_F32 : tpk::W_BF16;
+    hipError_t e = tpk::launch_gemv(wt, at, tpk::EPI_F32, 0, T, router, nullptr, x.d, m.E, 0, h1,
+                                    logits, m.E, nullptr, st, &fin);
+    if (e == hipSuccess)
+      e = tpk::launch_moe_topk(logits, T, m.E, m.k, topk_ids, topk_weights, st);
+    if (e != hipSuccess) return hip_fail(e, "tp_moe_block_step: router");
+  } else {
+    if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
+      return s;
+    for (int r = 0; r < N; ++r)
+      if (tp_status s = forward_impl(desc, r, TP_HALF_ATTN, shards[r], batch, xn, &kv[r], part(r),
+                                     workspace, workspace_bytes, stream, nullptr, nullptr))
+        return s;
+    if (tp_status s = tp_partial_reduce(desc, T, partials, N, x_in, h1, gamma2, xn2, stream))
+      return s;
+    if (tp_status s = tp_moe_route(desc, moe, router, xn2, T, logits, topk_ids, topk_weights,
+                                   stream))
+      return s;
+  }
+  for (int r = 0; r < N; ++r) {
+    tpk::FuseArgs fout{};
+    fout.prev = partials;
+    fout.part_stride = pstride;
+    fout.n_prev = N - 1;
+    fout.res_in = h1;
+    fout.res_out = out;
+    if (tp_status s = moe_forward_impl(desc, moe, r, moe_shards[r], xn2, T, topk_ids, topk_weights,
+                                       part(r), moe_workspace, moe_workspace_bytes, stream,
+                                       nullptr, nullptr, fused && r == N - 1 ? &fout : nullptr))
+      return s;
+  }
+  if (!fused) return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
   g_err.clear();
   return TP_OK;
 }

@@ -82,10 +82,13 @@ hipError_t launch_embed(int wt, const void* table, const void* scales, const int
 // k_moe.hip
 hipError_t launch_moe_topk(const float* logits, int T, int E, int top_k, int32_t* ids,
                            float* weights, hipStream_t st);
+// fuse: the down kernel also adds the earlier ranks' partials and the residual (EPI_REDUCE's
+// arithmetic) into fuse->res_out.
 hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, const void* Sg,
                           const void* Wu, const void* Su, const void* Wd, const void* Sd, int d,
                           int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
-                          const void* X, void* M, void* P, hipStream_t st);
+                          const void* X, void* M, void* P, hipStream_t st,
+                          const FuseArgs* fuse = nullptr);
 
 // k_reduce.hip
 hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,

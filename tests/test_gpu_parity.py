@@ -486,6 +486,68 @@ def test_moe_block_parity(s, moe):
         assert torch.equal(b.out, eager), f"replay {i}"
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s,moe", MOE_GPU, ids=lambda v: getattr(v, "name", str(v)))
+def test_moe_one_call_step(s, moe):
+    """tp_moe_block_step against the oracle chain: the router logits on the block's own h1, the
+    selection by the oracle's rule on the GPU's logits, every rank's partial for that selection,
+    and out = h1 + (((P_0 + P_1) + ...) + P_{N-1}) bit for bit from the stored h1 and partials
+    (the reduce folded into the last rank's expert-down kernel); a graph replay bit-identical."""
+    import oracle
+    from tensor_transformer_block_amd.block import MoEBlock, to_host
+    from tensor_transformer_block_amd.inputs import make_moe_inputs
+    tol = _moe_tol(s)
+    inp = make_inputs(s, seed=43)
+    minp = make_moe_inputs(s, moe, seed=43)
+    mb = MoEBlock(inp, minp)
+    mb.step_fused()
+    torch.cuda.synchronize()
+    b = mb.attn
+    ref = oracle.run_moe_block(inp, minp)
+    h1 = oracle.to_f64(to_host(b.h1, s.act_dtype), s.act_dtype)
+    e_h1 = nrel(h1, ref["h1"])
+    xn2 = oracle.rms_norm(h1, oracle.to_f64(inp.gamma2, s.act_dtype), s.rms_eps)
+    pm = oracle.moe_params_f64(minp)
+    z_gpu = t2np(mb.logits)
+    e_z = nrel(z_gpu, xn2 @ pm["router"].T)
+    ids_gpu = mb.ids.cpu().numpy().astype(np.int64)
+    ids_ref, w_ref = oracle.moe_select(z_gpu, moe.top_k)
+    assert np.array_equal(ids_gpu, ids_ref)
+    e_w = nrel(t2np(mb.weights), w_ref)
+    xn2_s = oracle.to_f64(to_host(b.xn2, s.act_dtype), s.act_dtype)
+    parts_ref, _ = oracle.moe_ffn_sharded(s, moe, pm, xn2_s, ids_gpu, t2np(mb.weights))
+    e_p = max(nrel(t2np(b.partials[r]), parts_ref[r]) for r in range(s.tp))
+    same = np.array_equal(ref["ids"], ids_gpu)
+    e_out = nrel(oracle.to_f64(to_host(b.out, s.act_dtype), s.act_dtype), ref["out"])
+    log(f"moe one-call {s.name}: h1 {e_h1:.2e}, logits {e_z:.2e}, weights {e_w:.2e}, partials "
+        f"{e_p:.2e}, out {e_out:.2e}; oracle's own selection {'matches' if same else 'differs'}")
+    assert e_h1 <= tol and e_z <= tol and e_w <= 1e-5 and e_p <= tol
+    if same:
+        assert e_out <= tol
+    tdt = torch.float32 if s.act_dtype == "f32" else torch.bfloat16
+    acc = b.partials[0].float().cpu().clone()
+    for r in range(1, s.tp):
+        acc = acc + b.partials[r].float().cpu()
+    want = (b.h1.float().cpu() + acc).to(tdt)
+    assert torch.equal(want.view(torch.uint8), b.out.cpu().view(torch.uint8))
+    eager = b.out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mb.step_fused()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mb.step_fused()
+    for i in range(2):
+        b.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.out.view(torch.uint8), eager.view(torch.uint8)), f"replay {i}"
+
+
 @pytest.mark.parametrize("E,k", [(40, 6), (100, 8), (200, 16), (500, 4), (1000, 16)])
 def test_moe_topk_ties_and_bounds(E, k):
     """Experts with identical router rows tie exactly; the lower index comes first, also between
