@@ -218,6 +218,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     B.lib()  # fails loudly if the HIP library is missing
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
     from tensor_transformer_block_amd.inputs import MOE_WORKLOADS
     if args.workload in MOE_WORKLOADS:
         bench_moe(args, *MOE_WORKLOADS[args.workload])
@@ -236,15 +245,6 @@ def main():
         f"x {resident / 1e6:.1f} MB")
     blk = DeviceBlock(inp, copies=copies, partial_dtype=args.partial_dtype)
     torch.cuda.synchronize()
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
-        del src, dst
 
     if args.staged:
         def step(c, timed=None):
