@@ -171,9 +171,11 @@ FUSED_STEP = ["med-bf16-ragged", "med-bf16-single-key", "med-q8-n4", "med-q8-hd2
               "med-bf16-prefill"]
 
 
-@pytest.mark.parametrize("partial_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("name", FUSED_STEP + ["tiny-llama-fp32", "llama3-8b-decode",
-                                               "gemma-q8-decode"])
+ONE_CALL = ([(n, p) for n in FUSED_STEP for p in ("f32", "bf16")]
+            + [(n, "f32") for n in ("tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode")])
+
+
+@pytest.mark.parametrize("name,partial_dtype", ONE_CALL, ids=lambda v: str(v))
 def test_one_call_step(name, partial_dtype):
     """tp_block_step: xn, h1, xn2, out and every rank's new K and V against the oracle, and
     against the staged calls on the same inputs (the fused decode schedule feeds the projections
@@ -184,9 +186,6 @@ def test_one_call_step(name, partial_dtype):
     import oracle
     from tensor_transformer_block_amd.block import DeviceBlock, to_host
     s = BY_NAME.get(name) or CONFIGS.get(name)
-    if partial_dtype == "bf16" and name in ("tiny-llama-fp32", "llama3-8b-decode",
-                                            "gemma-q8-decode"):
-        pytest.skip("bf16 partials are covered on the medium shapes")
     inp = make_inputs(s, seed=23)
     blk = DeviceBlock(inp, partial_dtype=partial_dtype)
     fused = s.mode == "decode" and s.n_tokens <= 4
