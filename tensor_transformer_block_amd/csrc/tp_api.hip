@@ -285,6 +285,8 @@ hipError_t project(const Dims& x, int epi, int T, const char* W, const char* S, 
   }
   if (use_gemm(x, T, K)) {
     const char* B2 = (epi == tpk::EPI_GATED) ? W + (size_t)gate_off * K * 2 : nullptr;
+    if (T <= 64 && tpk::gemm_band_supported(epi, T, n_out, K))
+      return tpk::launch_gemm_band(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, st);
     if (T <= 64 && splitk_ws)
       return tpk::launch_gemm_splitk(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, splitk_ws, st);
     return tpk::launch_gemm_bf16(epi, x.actf, T, n_out, K, X, W, B2, Y, ldy, st);

@@ -122,6 +122,11 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
                               hipStream_t st, int* parts_only = nullptr);
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
+// k_gemm_band.hip: M <= 64 tokens, a 16-column band of the output per workgroup over the whole
+// K (no split, epilogue in the kernel); K % 128 == 0 and at least 192 bands.
+bool gemm_band_supported(int epi, int M, int N, int K);
+hipError_t launch_gemm_band(int epi, int actf, int M, int N, int K, const void* A, const void* B,
+                            const void* B2, void* C, int ldc, hipStream_t st);
 // The bf16 QKV projection of M tokens with the rotary embedding and the KV append in its epilogue
 // (the 128 or 256-row direct-to-LDS tiles; q goes to re.q_out, k and v into the pages). Supported
 // when N % 128 == 0, hd is 64 or 128, K % 64 == 0, M >= 128 and the shape is not one for the
