@@ -64,6 +64,19 @@ SHAPES = [
     BlockShape(name="med-bf16-prefill-g8-hd64", index=218, d_model=256, n_heads=16,
                n_kv_heads=2, head_dim=64, ffn_dim=512, tp=2, w_dtype="bf16", act_dtype="bf16",
                ffn_act="gelu_tanh", mode="prefill", kv_lens=(530,), n_tokens=389),
+    # Batched-decode projections on the 16-column band GEMM (at least 192 bands, K a multiple
+    # of 128): 37 tokens (a partial third token tile) with o_proj and down 3080 columns wide
+    # (a partial last band; the gate/up, whose K of 3080 is not a multiple of 128, takes the
+    # split-K GEMM), and 9 tokens with a 3208-column gated gate/up (a partial last band).
+    BlockShape(name="med-bf16-band-37", index=226, d_model=3080, n_heads=8, n_kv_heads=2,
+               head_dim=128, ffn_dim=6400, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="gelu_tanh", mode="decode",
+               kv_lens=tuple(int(v) for v in np.random.default_rng(10).integers(1, 90, 37)),
+               n_tokens=37),
+    BlockShape(name="med-bf16-band-9", index=227, d_model=3072, n_heads=8, n_kv_heads=2,
+               head_dim=128, ffn_dim=6416, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="silu", mode="decode", kv_lens=(5, 77, 1, 40, 23, 9, 60, 2, 31),
+               n_tokens=9),
     BlockShape(name="med-fp32-g2", index=206, d_model=384, n_heads=4, n_kv_heads=2, head_dim=128,
                ffn_dim=688, tp=2, w_dtype="f32", act_dtype="f32", ffn_act="silu", mode="decode",
                kv_lens=(50, 3), n_tokens=2),
@@ -106,10 +119,11 @@ def test_block_parity_small(s):
 
 
 @pytest.mark.parametrize("name", ["med-bf16-ragged", "med-bf16-prefill-300",
-                                  "med-bf16-prefill-wide-rows", "med-bf16-batched-64"])
+                                  "med-bf16-prefill-wide-rows", "med-bf16-batched-64",
+                                  "med-bf16-band-37"])
 def test_block_parity_bf16_partials(name):
     """bf16 partial storage on the decode GEMV, the prefill GEMMs (narrow and 256 x 256 tiles)
-    and the batched-decode paths."""
+    and the batched-decode paths (split-K and band GEMMs)."""
     inp = make_inputs({x.name: x for x in SHAPES}[name], seed=12)
     run_and_check(inp, partial_dtype="bf16", label=f"{name}, bf16 partials")
 
