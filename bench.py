@@ -68,15 +68,26 @@ def step_flops(s):
     return 2.0 * s.n_tokens * params + 4.0 * s.head_dim * s.n_heads * pairs
 
 
-def gate_up_unit(s):
-    """Algorithmic bytes and FLOPs of one gate/up launch (one rank): the weight slice once, the
-    normed input read and the activation output written."""
+def gate_up_unit(s, ranks=1):
+    """Algorithmic bytes and FLOPs of one gate/up launch covering `ranks` ranks (1: one rank's
+    launch; tp_degree under the all-ranks schedule): each rank's weight slice once, the input
+    rows read once and each rank's activation output written."""
     act = 4 if s.act_dtype == "f32" else 2
     per = {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[s.w_dtype]
     fr = s.ffn_dim // s.tp
     wb = 2 * fr * s.d_model * per
-    return int(wb + s.n_tokens * s.d_model * act + s.n_tokens * fr * act), \
-        2.0 * s.n_tokens * 2 * fr * s.d_model
+    return int(ranks * wb + s.n_tokens * s.d_model * act + ranks * s.n_tokens * fr * act), \
+        ranks * 2.0 * s.n_tokens * 2 * fr * s.d_model
+
+
+SCHEDULE_NAMES = {0: "staged", 1: "one-call, per rank", 2: "one-call, all ranks per launch"}
+
+
+def step_schedule(blk, staged):
+    """The schedule the library gives this block's step (the bench's --staged runs the separate
+    calls whatever the library would choose)."""
+    from tensor_transformer_block_amd import binding as B
+    return 0 if staged else B.tp_step_schedule(blk.desc, blk.batch)
 
 
 class HipEvents:
@@ -371,7 +382,9 @@ def main():
     kdur = [hev.elapsed_s(2 * i, 2 * i + 1) for i in range(n_kl)]
     hev.close()
     kavg = float(np.mean(kdur))
-    ub, uf = gate_up_unit(s)
+    sched = step_schedule(blk, args.staged)
+    all_ranks = sched == 2
+    ub, uf = gate_up_unit(s, s.tp if all_ranks else 1)
     if s.mode == "prefill":
         roof = {"bound": "mfma", "achieved": round(uf / kavg / 1e12, 3),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -380,7 +393,8 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(s.name)
-    roof["kernel"] = "gate/up projection (one rank)"
+    roof["kernel"] = ("gate/up projection (all ranks, one launch)" if all_ranks
+                      else "gate/up projection (one rank)")
     roof["avg_us"] = round(kavg * 1e6, 2)
 
     cpu = None
@@ -399,7 +413,7 @@ def main():
                    "tp_degree_emulated": s.tp, "weights": s.w_dtype, "mode": s.mode,
                    "tokens": s.n_tokens, "kv_len": max(s.kv_lens), "page_size": s.page_size,
                    "cold_copies": copies, "graph": not args.no_graph,
-                   "schedule": "staged" if args.staged else "one-call",
+                   "schedule": SCHEDULE_NAMES[sched],
                    "partial_dtype": args.partial_dtype},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
@@ -505,7 +519,9 @@ def bench_stack(args, s):
     torch.cuda.synchronize()
     kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(i)]))
     hev.close()
-    ub, uf = gate_up_unit(s)
+    sched = step_schedule(st.blocks[0], not fused)
+    all_ranks = sched == 2
+    ub, uf = gate_up_unit(s, s.tp if all_ranks else 1)
     if s.mode == "prefill":
         roof = {"bound": "mfma", "achieved": round(uf / kavg / 1e12, 3),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -514,7 +530,8 @@ def bench_stack(args, s):
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(s.name)
-    roof["kernel"] = "gate/up projection (one rank of one block)"
+    roof["kernel"] = ("gate/up projection (all ranks of one block, one launch)" if all_ranks
+                      else "gate/up projection (one rank of one block)")
     roof["avg_us"] = round(kavg * 1e6, 2)
     sb = K * step_bytes(s)
     head_info = None
@@ -550,7 +567,7 @@ def bench_stack(args, s):
                    "ffn_dim": s.ffn_dim, "tp_degree_emulated": s.tp, "weights": s.w_dtype,
                    "mode": s.mode, "tokens": s.n_tokens, "kv_len": max(s.kv_lens),
                    "page_size": s.page_size, "graph": not args.no_graph,
-                   "schedule": "staged" if args.staged else "one-call"},
+                   "schedule": SCHEDULE_NAMES[sched]},
         "step_algorithmic_bytes": sb,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -149,6 +149,19 @@ tp_status tp_shard_weights(const tp_block_desc* desc, int32_t rank, const tp_ful
 /* Bytes of workspace tp_block_shard_forward needs for this batch (either half). */
 tp_status tp_workspace_size(const tp_block_desc* desc, const tp_batch* batch, uint64_t* bytes);
 
+/* How tp_block_step (and the attention half of tp_moe_block_step) runs a batch. */
+enum {
+  TP_SCHEDULE_STAGED = 0,     /* the separate calls, rank after rank */
+  TP_SCHEDULE_PER_RANK = 1,   /* norms and reduces folded into each rank's decode GEMVs */
+  TP_SCHEDULE_ALL_RANKS = 2   /* as PER_RANK, each projection / attention one launch for all */
+};
+tp_status tp_step_schedule(const tp_block_desc* desc, const tp_batch* batch, int32_t* schedule);
+
+/* Bytes of workspace tp_block_step and tp_moe_block_step need for this batch:
+ * tp_workspace_size, times tp_degree (each copy 256-byte aligned) under TP_SCHEDULE_ALL_RANKS. */
+tp_status tp_step_workspace_size(const tp_block_desc* desc, const tp_batch* batch,
+                                 uint64_t* bytes);
+
 /* Bytes of the rotary table: max_position * head_dim/2 pairs of fp32 (cos, sin). */
 tp_status tp_rope_table_bytes(const tp_block_desc* desc, uint64_t* bytes);
 
@@ -206,19 +219,39 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * gamma * x and scales its sums by 1/sqrt(mean(x^2) + eps), so the normed input is not rounded
  * to the activation dtype first, as the separate calls round it; xn and xn2 are still stored,
  * rounded), and the last rank's o_proj and down projections add all ranks' partials in rank
- * order plus the residual, with the reduce's arithmetic. The ranks still run in order and every
- * rank's partial is still stored. Otherwise the call issues exactly the separate calls above.
+ * order plus the residual, with the reduce's arithmetic. Every rank's partial is still stored.
+ * When, in addition, every rank's inputs of a projection fit one workgroup's LDS (N > 1), each
+ * projection and the attention run as one launch for all ranks (TP_SCHEDULE_ALL_RANKS: six
+ * launches per step, seven with the attention's split merge counted): every block of a
+ * column-parallel launch works for one rank with that rank's slice and cache, and every block
+ * of a row-parallel launch computes its rows for rank 0, 1, ... in turn, each rank's sums exactly
+ * as in that rank's own launch, then adds the partials in rank order and the residual. The
+ * results equal the per-rank schedule's bit for bit. Otherwise (TP_SCHEDULE_STAGED) the call
+ * issues exactly the separate calls above. tp_step_schedule reports which schedule a batch gets.
  * shards, kv: host arrays of N entries (rank r's packed shard, device pointer; rank r's cache).
  * x, gamma1, gamma2 (inputs) and xn, h1, xn2, out: activation dtype, [T, d] ([d] for the gammas);
  * partials: [N, T, d] in partial_dtype (holds the FFN partials on return). workspace: at least
- * tp_workspace_size bytes. n_tokens == 0 is a no-op. */
+ * tp_step_workspace_size bytes (TP_ERR_BUFFER_TOO_SMALL otherwise; under the all-ranks schedule
+ * it holds one copy of the per-rank workspace per rank). n_tokens == 0 is a no-op. */
 tp_status tp_block_step(const tp_block_desc* desc, const void* const* shards, const tp_batch* batch,
                         const tp_kv_cache* kv, const void* x, const void* gamma1,
                         const void* gamma2, void* partials, void* xn, void* h1, void* xn2,
                         void* out, void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* tp_block_step with the schedule chosen by the caller (TP_SCHEDULE_*; -1: the call's own
+ * choice, as tp_block_step). A schedule the batch does not allow (any above what
+ * tp_step_schedule reports) returns TP_ERR_UNSUPPORTED before anything is launched. The staged
+ * and per-rank schedules need only tp_workspace_size bytes of workspace. */
+tp_status tp_block_step_with_schedule(const tp_block_desc* desc, int32_t schedule,
+                                      const void* const* shards, const tp_batch* batch,
+                                      const tp_kv_cache* kv, const void* x, const void* gamma1,
+                                      const void* gamma2, void* partials, void* xn, void* h1,
+                                      void* xn2, void* out, void* workspace,
+                                      uint64_t workspace_bytes, void* stream);
+
 /* Measurement variant of tp_block_step: ev_begin / ev_end bracket the gate/up projection of rank
- * timed_rank as in tp_block_shard_forward_timed. Not for graph capture. */
+ * timed_rank as in tp_block_shard_forward_timed (under TP_SCHEDULE_ALL_RANKS: the one gate/up
+ * launch of all ranks, for any timed_rank in [0, N)). Not for graph capture. */
 tp_status tp_block_step_timed(const tp_block_desc* desc, const void* const* shards,
                               const tp_batch* batch, const tp_kv_cache* kv, const void* x,
                               const void* gamma1, const void* gamma2, void* partials, void* xn,
@@ -344,10 +377,11 @@ tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_des
  * rank's expert half (tp_moe_shard_forward) and out = h1 + (((P_0 + P_1) + ...) + P_{N-1}).
  * For decode batches whose dense projections are single GEMV launches the norms and reduces are
  * folded into the neighbouring projections as in tp_block_step (the router's input is the
- * unrounded norm of h1; xn2 is stored rounded for the experts), saving three launches; otherwise
- * the separate calls run. shards (dense attention shards), moe_shards, kv: host arrays of N
- * entries. Buffers as in tp_block_step and tp_moe_route; workspace: tp_workspace_size bytes,
- * moe_workspace: tp_moe_workspace_size bytes. n_tokens == 0 is a no-op. */
+ * unrounded norm of h1; xn2 is stored rounded for the experts), saving three launches, and the
+ * attention halves run as one launch per projection for all ranks under TP_SCHEDULE_ALL_RANKS;
+ * otherwise the separate calls run. shards (dense attention shards), moe_shards, kv: host arrays
+ * of N entries. Buffers as in tp_block_step and tp_moe_route; workspace: tp_step_workspace_size
+ * bytes, moe_workspace: tp_moe_workspace_size bytes. n_tokens == 0 is a no-op. */
 tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
                             const void* const* shards, const void* const* moe_shards,
                             const tp_batch* batch, const tp_kv_cache* kv, const void* x,

@@ -32,8 +32,11 @@ EXPORTED = (
     "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
     "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
     "tp_shard_project", "tp_shard_project_workspace_size", "tp_block_shard_forward_noalloc",
-    "tp_block_step", "tp_block_step_timed", "tp_moe_block_step",
+    "tp_block_step", "tp_block_step_timed", "tp_moe_block_step", "tp_step_workspace_size",
+    "tp_step_schedule", "tp_block_step_with_schedule",
 )
+
+TP_SCHEDULE_STAGED, TP_SCHEDULE_PER_RANK, TP_SCHEDULE_ALL_RANKS = 0, 1, 2
 
 
 class tp_block_desc(ctypes.Structure):
@@ -112,6 +115,8 @@ def lib() -> ctypes.CDLL:
         "tp_shard_weights_size": [P, I32, P],
         "tp_shard_weights": [P, I32, P, P, U64, P],
         "tp_workspace_size": [P, P, P],
+        "tp_step_workspace_size": [P, P, P],
+        "tp_step_schedule": [P, P, P],
         "tp_rope_table_bytes": [P, P],
         "tp_rope_table_init": [P, P, U64, P],
         "tp_block_shard_forward": [P, I32, I32, P, P, P, P, P, P, U64, P],
@@ -134,6 +139,7 @@ def lib() -> ctypes.CDLL:
         "tp_shard_project_workspace_size": [P, I32, I32, P],
         "tp_block_shard_forward_noalloc": [P, I32, I32, P, P, P, P, P, P],
         "tp_block_step": [P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P],
+        "tp_block_step_with_schedule": [P, I32, P, P, P, P, P, P, P, P, P, P, P, P, U64, P],
         "tp_block_step_timed": [P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P, I32, P, P],
         "tp_moe_block_step": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P,
                               U64, P],
@@ -224,6 +230,19 @@ def tp_workspace_size(desc, batch: tp_batch) -> int:
     return out.value
 
 
+def tp_step_workspace_size(desc, batch: tp_batch) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().tp_step_workspace_size(ctypes.byref(desc), ctypes.byref(batch),
+                                        ctypes.byref(out)))
+    return out.value
+
+
+def tp_step_schedule(desc, batch: tp_batch) -> int:
+    out = ctypes.c_int32()
+    _check(lib().tp_step_schedule(ctypes.byref(desc), ctypes.byref(batch), ctypes.byref(out)))
+    return out.value
+
+
 def tp_workspace_offsets(desc, batch: tp_batch):
     q, a, f = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
     _check(lib().tp_workspace_offsets(ctypes.byref(desc), ctypes.byref(batch), ctypes.byref(q),
@@ -288,6 +307,19 @@ def tp_block_step(desc, shards, batch: tp_batch, kv, x, gamma1, gamma2, partials
                                ptr(gamma1), ptr(gamma2), ptr(partials), ptr(xn), ptr(h1),
                                ptr(xn2), ptr(out), ptr(workspace), workspace_bytes,
                                _stream(stream)))
+
+
+def tp_block_step_with_schedule(desc, schedule, shards, batch: tp_batch, kv, x, gamma1, gamma2,
+                                partials, xn, h1, xn2, out, workspace, workspace_bytes=None,
+                                stream=None) -> None:
+    """tp_block_step with an explicit TP_SCHEDULE_* (-1: the library's choice)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    sh, kvs = _step_arrays(shards, kv)
+    _check(lib().tp_block_step_with_schedule(ctypes.byref(desc), schedule, sh, ctypes.byref(batch),
+                                             kvs, ptr(x), ptr(gamma1), ptr(gamma2), ptr(partials),
+                                             ptr(xn), ptr(h1), ptr(xn2), ptr(out), ptr(workspace),
+                                             workspace_bytes, _stream(stream)))
 
 
 def tp_block_step_timed(desc, shards, batch: tp_batch, kv, x, gamma1, gamma2, partials, xn, h1,

@@ -113,7 +113,9 @@ class DeviceBlock:
         self.xn2 = torch.empty_like(self.xn)
         self.h1 = torch.empty_like(self.xn)
         self.out = torch.empty_like(self.xn)
-        self.ws_bytes = B.tp_workspace_size(self.desc, self.batch)
+        # tp_block_step may keep one copy per rank (the all-ranks schedule); the per-rank calls
+        # use the first copy.
+        self.ws_bytes = B.tp_step_workspace_size(self.desc, self.batch)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.copies = copies
 
@@ -157,18 +159,25 @@ class DeviceBlock:
         g, xo = next_norm if next_norm is not None else (None, None)
         B.tp_partial_reduce(d, T, self.partials, N, self.h1, self.out, g, xo)
 
-    def step_fused(self, copy: int = 0, x=None, timed=None):
+    def step_fused(self, copy: int = 0, x=None, timed=None, schedule=None):
         """The same block step in one library call (tp_block_step): for decode batches the
-        replicated norms and the two reduces run inside the projections next to them, with the
-        same results bit for bit. ``timed``: (rank, begin, end) raw events bracketing that
-        rank's gate/up projection."""
+        replicated norms and the two reduces run inside the projections next to them, and (all-
+        ranks schedule) each projection and the attention is one launch for every rank.
+        ``timed``: (rank, begin, end) raw events bracketing that rank's gate/up projection (the
+        all-ranks gate/up launch under that schedule). ``schedule``: a TP_SCHEDULE_* to force."""
         x = self.x if x is None else x
         args = (self.desc, self.shards[copy], self.batch, self.kv[copy], x, self.gamma1,
                 self.gamma2, self.partials, self.xn, self.h1, self.xn2, self.out, self.workspace)
-        if timed is None:
+        if schedule is not None:
+            B.tp_block_step_with_schedule(self.desc, schedule, *args[1:], self.ws_bytes)
+        elif timed is None:
             B.tp_block_step(*args, self.ws_bytes)
         else:
             B.tp_block_step_timed(*args, timed[0], timed[1], timed[2], self.ws_bytes)
+
+    def schedule(self) -> int:
+        """The TP_SCHEDULE_* tp_block_step takes for this block's batch."""
+        return B.tp_step_schedule(self.desc, self.batch)
 
     # --------------------------------------------------------------------------- readback
     def workspace_views(self):

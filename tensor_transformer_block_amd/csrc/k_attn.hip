@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_attn_split(
     const int* __restrict__ positions, int mode, const int* __restrict__ block_table,
     int max_pages, int ps, int n_pages, int hk, int chunk, int n_split, int pos_limit,
     float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
-    float scale_log2) {
+    float scale_log2, AttnRanks ar) {
   using TL = AttnTile<AT, HD>;
   constexpr int E = TL::E, LPK = TL::LPK, KPP = TL::KPP, NP = TL::NP;
   constexpr int EB = (AT == ACT_F32) ? 4 : 2;
@@ -219,7 +219,19 @@ __global__ __launch_bounds__(256) void k_attn_split(
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ float s_o[4][G][HD];
 
-  const int split = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int split = blockIdx.x, t = blockIdx.z;
+  int g = blockIdx.y;
+  if (ar.n > 1) {  // every rank in one launch: this block's rank and its buffers
+    const int rank = g / hk;
+    g -= rank * hk;
+    q = ar.q[rank];
+    kpages = ar.k_pages[rank];
+    vpages = ar.v_pages[rank];
+    n_pages = ar.n_pages[rank];
+    part_o = ar.part_o[rank];
+    part_ml = ar.part_ml[rank];
+    out = ar.out[rank];
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPK, e0 = (lane % LPK) * E;
   const int hq = hk * G;
@@ -416,14 +428,25 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     const uint16_t* __restrict__ vpages, const int* __restrict__ positions, int mode,
     const int* __restrict__ block_table, int max_pages, int ps, int n_pages, int hk, int G,
     int T, int chunk, int n_split, int pos_limit, float* __restrict__ part_o,
-    float* __restrict__ part_ml, uint16_t* __restrict__ out, float scale_log2) {
+    float* __restrict__ part_ml, uint16_t* __restrict__ out, float scale_log2, AttnRanks ar) {
   constexpr int KS = HD / 32;  // MFMA k-steps over hd in Q K^T
   constexpr int NO = HD / 16;  // 16-wide hd n-tiles of O
   __shared__ __attribute__((aligned(16))) uint16_t s_pb[4][16 * kPLd];
   __shared__ float s_m[4][8], s_l[4][8];
   __shared__ float s_o[PREFILL ? 1 : 4][PREFILL ? 1 : 8][HD];
 
-  const int g = blockIdx.y;
+  int g = blockIdx.y;
+  if (!PREFILL && ar.n > 1) {  // every rank in one launch: this block's rank and its buffers
+    const int rank = g / hk;
+    g -= rank * hk;
+    q = (const uint16_t*)ar.q[rank];
+    kpages = (const uint16_t*)ar.k_pages[rank];
+    vpages = (const uint16_t*)ar.v_pages[rank];
+    n_pages = ar.n_pages[rank];
+    part_o = ar.part_o[rank];
+    part_ml = ar.part_ml[rank];
+    out = (uint16_t*)ar.out[rank];
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
   const int hq = hk * G;
@@ -670,11 +693,19 @@ template <int AT>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_split, int hd, int hq,
-                                                      void* __restrict__ out) {
+                                                      void* __restrict__ out, AttnRanks ar) {
   __shared__ float s_w[kMaxSplit];
   __shared__ float s_red[2][4];
   __shared__ float s_acc[4][64];
-  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  int h = blockIdx.y;
+  if (ar.n > 1) {  // every rank in one launch (blockIdx.y = rank * hq + head)
+    const int rank = h / hq;
+    h -= rank * hq;
+    part_o = ar.part_o[rank];
+    part_ml = ar.part_ml[rank];
+    out = ar.out[rank];
+  }
   const int e = blockIdx.z * 64 + (tid & 63), part = tid >> 6;
   const size_t row0 = ((size_t)t * hq + h) * n_split;
   float mx = -INFINITY;
@@ -716,20 +747,21 @@ static hipError_t attn_mfma_g(bool prefill, int G, int T, int hk, hipStream_t st
                               const void* kp, const void* vp, const int* positions, int mode,
                               const int* bt, int max_pages, int ps, int n_pages, int chunk,
                               int n_split, int pos_limit, float* po, float* pml, void* out,
-                              float sl2) {
+                              float sl2, const AttnRanks& ar) {
   if (G > 8) return hipErrorInvalidValue;
   if (prefill) {
     const int groups = (T + 15) / 16 * G;
     dim3 grid((groups + 3) / 4, hk, 1);
     hipLaunchKernelGGL((k_attn_mfma<HD, true>), grid, dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt, max_pages,
-                       ps, n_pages, hk, G, T, chunk, 1, pos_limit, po, pml, (uint16_t*)out, sl2);
+                       ps, n_pages, hk, G, T, chunk, 1, pos_limit, po, pml, (uint16_t*)out, sl2,
+                       AttnRanks{});
   } else {
-    dim3 grid(n_split, hk, T);
+    dim3 grid(n_split, hk * (ar.n > 1 ? ar.n : 1), T);
     hipLaunchKernelGGL((k_attn_mfma<HD, false>), grid, dim3(256), 0, st, (const uint16_t*)q,
                        (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt, max_pages,
                        ps, n_pages, hk, G, T, chunk, n_split, pos_limit, po, pml, (uint16_t*)out,
-                       sl2);
+                       sl2, ar);
   }
   return hipGetLastError();
 }
@@ -738,11 +770,12 @@ template <int AT, int HD>
 static hipError_t attn_g(int G, dim3 grid, hipStream_t st, const void* q, const void* kp,
                          const void* vp, const int* positions, int mode, const int* bt,
                          int max_pages, int ps, int n_pages, int hk, int chunk, int n_split,
-                         int pos_limit, float* po, float* pml, void* out, float sl2) {
+                         int pos_limit, float* po, float* pml, void* out, float sl2,
+                         const AttnRanks& ar) {
 #define TPK_ATT(GV)                                                                           \
   hipLaunchKernelGGL((k_attn_split<AT, HD, GV>), grid, dim3(256), 0, st, q, kp, vp, positions, \
                      mode, bt, max_pages, ps, n_pages, hk, chunk, n_split, pos_limit, po, pml,   \
-                     out, sl2)
+                     out, sl2, ar)
   switch (G) {
     case 1: TPK_ATT(1); break;
     case 2: TPK_ATT(2); break;
@@ -754,19 +787,20 @@ static hipError_t attn_g(int G, dim3 grid, hipStream_t st, const void* q, const 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* q, const void* kp,
-                              const void* vp, const int* positions, int mode, const int* bt,
-                              int max_pages, int ps, int n_pages, int chunk, int n_split,
-                              int pos_limit, float* part_o, float* part_ml, void* out,
-                              hipStream_t st) {
+static hipError_t attn_decode_impl(int at, int hd, int G, int T, int hk, const void* q,
+                                   const void* kp, const void* vp, const int* positions, int mode,
+                                   const int* bt, int max_pages, int ps, int n_pages, int chunk,
+                                   int n_split, int pos_limit, float* part_o, float* part_ml,
+                                   void* out, const AttnRanks& ar, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (n_split > kMaxSplit || chunk % 16 || ps % 16) return hipErrorInvalidValue;
+  const int nr = ar.n > 1 ? ar.n : 1;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
-  dim3 grid(n_split, hk, T);
+  dim3 grid(n_split, hk * nr, T);
   hipError_t e;
 #define TPK_HD(ATV, HDV)                                                                        \
   e = attn_g<ATV, HDV>(G, grid, st, q, kp, vp, positions, mode, bt, max_pages, ps, n_pages, hk, \
-                       chunk, n_split, pos_limit, part_o, part_ml, out, sl2)
+                       chunk, n_split, pos_limit, part_o, part_ml, out, sl2, ar)
   if (at == ACT_F32) {
     if (hd == 64) TPK_HD(ACT_F32, 64);
     else if (hd == 128) TPK_HD(ACT_F32, 128);
@@ -775,12 +809,13 @@ hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* 
   } else {
     if (chunk % 32) return hipErrorInvalidValue;
     const bool prefill = (mode == 1);
+    if (prefill && nr > 1) return hipErrorInvalidValue;
     if (prefill && attn_prefill_supported(hd, G, ps))
       return launch_attn_prefill(hd, G, T, hk, q, kp, vp, positions, bt, max_pages, n_pages,
                                  pos_limit, out, st);
 #define TPK_HDM(HDV)                                                                          \
   e = attn_mfma_g<HDV>(prefill, G, T, hk, st, q, kp, vp, positions, mode, bt, max_pages, ps, \
-                       n_pages, chunk, n_split, pos_limit, part_o, part_ml, out, sl2)
+                       n_pages, chunk, n_split, pos_limit, part_o, part_ml, out, sl2, ar)
     if (hd == 64) TPK_HDM(64);
     else if (hd == 128) TPK_HDM(128);
     else if (hd == 256) TPK_HDM(256);
@@ -791,12 +826,37 @@ hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* 
 #undef TPK_HD
   if (e != hipSuccess || n_split == 1) return e;
   const int hq = hk * G;
-  dim3 cg(T, hq, (hd + 63) / 64), cb(256);
+  dim3 cg(T, hq * nr, (hd + 63) / 64), cb(256);
   if (at == ACT_F32)
-    hipLaunchKernelGGL(k_attn_combine<ACT_F32>, cg, cb, 0, st, part_o, part_ml, n_split, hd, hq, out);
+    hipLaunchKernelGGL(k_attn_combine<ACT_F32>, cg, cb, 0, st, part_o, part_ml, n_split, hd, hq,
+                       out, ar);
   else
-    hipLaunchKernelGGL(k_attn_combine<ACT_BF16>, cg, cb, 0, st, part_o, part_ml, n_split, hd, hq, out);
+    hipLaunchKernelGGL(k_attn_combine<ACT_BF16>, cg, cb, 0, st, part_o, part_ml, n_split, hd, hq,
+                       out, ar);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* q, const void* kp,
+                              const void* vp, const int* positions, int mode, const int* bt,
+                              int max_pages, int ps, int n_pages, int chunk, int n_split,
+                              int pos_limit, float* part_o, float* part_ml, void* out,
+                              hipStream_t st) {
+  return attn_decode_impl(at, hd, G, T, hk, q, kp, vp, positions, mode, bt, max_pages, ps,
+                          n_pages, chunk, n_split, pos_limit, part_o, part_ml, out, AttnRanks{},
+                          st);
+}
+
+hipError_t launch_attn_decode_ranks(int at, int hd, int G, int T, int hk, const AttnRanks& ar,
+                                    const int* positions, const int* bt, int max_pages, int ps,
+                                    int chunk, int n_split, int pos_limit, hipStream_t st) {
+  if (ar.n < 1 || ar.n > kMaxRanks) return hipErrorInvalidValue;
+  for (int r = 0; r < ar.n; ++r)
+    if (!ar.q[r] || !ar.k_pages[r] || !ar.v_pages[r] || !ar.part_o[r] || !ar.part_ml[r] ||
+        !ar.out[r] || ar.n_pages[r] < 1)
+      return hipErrorInvalidValue;
+  return attn_decode_impl(at, hd, G, T, hk, ar.q[0], ar.k_pages[0], ar.v_pages[0], positions, 0,
+                          bt, max_pages, ps, ar.n_pages[0], chunk, n_split, pos_limit,
+                          ar.part_o[0], ar.part_ml[0], ar.out[0], ar, st);
 }
 
 }  // namespace tpk

@@ -21,9 +21,11 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
     return hipErrorInvalidValue;
   // The fused prologue and reduce handle one token group (their rows must stay whole).
   if (fuse && T > ntmax) return hipErrorInvalidValue;
+  if (epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF) return hipErrorInvalidValue;
   const FuseArgs fa = fuse ? *fuse : FuseArgs{};
   RopeEpi re = rope ? *rope : RopeEpi{};
   if (!rope) re.hd = 2;  // unused by non-rotary epilogues; keeps the row mapping well defined
+  const RankPtrs rp{};  // a single rank's launch
   for (int t0 = 0; t0 < T; t0 += ntmax) {
     const int nt = (T - t0) < ntmax ? (T - t0) : ntmax;
     const void* Xt = (const char*)X + (size_t)t0 * K * xb;
@@ -32,16 +34,60 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
     hipError_t e;
     const uint16_t* s16 = (const uint16_t*)S;
     if (wt == W_F32 && at == ACT_F32)
-      e = gemv_f32(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, st);
+      e = gemv_f32(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, rp, st);
     else if (wt == W_BF16 && at == ACT_BF16)
-      e = gemv_bf16(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, st);
+      e = gemv_bf16(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, rp, st);
     else if (wt == W_Q8 && at == ACT_BF16)
-      e = gemv_q8(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, st);
+      e = gemv_q8(epi, actf, nt, W, s16, K, n_out, gate_off, Xt, Yt, ldy, re, fa, rp, st);
     else
       return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Staged bytes of a launch over all ranks: EPI_RED_ALL* stages every rank's input rows.
+static size_t ranks_lds(int wt, int epi, int n_ranks, int T, int K) {
+  const bool allr = epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF;
+  const size_t xb = (allr && wt != W_F32) ? 2 : 4;  // bf16 rows stay bf16 there
+  const size_t one = (size_t)T * K * xb + (wt == W_Q8 ? (size_t)T * (K / 16) * 4 : 0);
+  return (allr ? (size_t)n_ranks : 1) * one;
+}
+
+bool gemv_ranks_fit(int wt, int epi, int n_ranks, int T, int K) {
+  return n_ranks >= 1 && n_ranks <= kMaxRanks && T >= 1 && T <= gemv_max_tokens(K) &&
+         ranks_lds(wt, epi, n_ranks, T, K) <= 160 * 1024;
+}
+
+hipError_t launch_gemv_ranks(int wt, int at, int epi, int actf, int T, const RankPtrs& rp, int K,
+                             int n_out, int gate_off, const void* X, int ldy, const RopeEpi* rope,
+                             hipStream_t st, const FuseArgs& fuse) {
+  const bool allr = epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF;
+  if (!gemv_ranks_fit(wt, epi, rp.n, T, K)) return hipErrorInvalidValue;
+  if (!(allr || epi == EPI_ROPE || epi == EPI_GATED)) return hipErrorInvalidValue;
+  if (epi == EPI_ROPE && !rope) return hipErrorInvalidValue;
+  if (allr && (!fuse.res_in || !fuse.res_out || fuse.gamma)) return hipErrorInvalidValue;
+  for (int r = 0; r < rp.n; ++r)
+    if (!rp.w[r] || !rp.y[r] || (allr && !rp.x[r]) || (wt == W_Q8 && !rp.s[r]))
+      return hipErrorInvalidValue;
+  RopeEpi re = rope ? *rope : RopeEpi{};
+  if (!rope) re.hd = 2;
+  re.t0 = 0;
+  const uint16_t* s16 = (const uint16_t*)rp.s[0];
+  // Rank 0's pointers also go in the plain arguments (used as they are when rp.n == 1).
+  if (rope) {
+    re.q_out = rp.q_out[0];
+    re.k_pages = rp.k_pages[0];
+    re.v_pages = rp.v_pages[0];
+    re.n_pages = rp.n_pages[0];
+  }
+  if (wt == W_F32 && at == ACT_F32)
+    return gemv_f32(epi, actf, T, rp.w[0], s16, K, n_out, gate_off, X, rp.y[0], ldy, re, fuse, rp, st);
+  if (wt == W_BF16 && at == ACT_BF16)
+    return gemv_bf16(epi, actf, T, rp.w[0], s16, K, n_out, gate_off, X, rp.y[0], ldy, re, fuse, rp, st);
+  if (wt == W_Q8 && at == ACT_BF16)
+    return gemv_q8(epi, actf, T, rp.w[0], s16, K, n_out, gate_off, X, rp.y[0], ldy, re, fuse, rp, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tpk

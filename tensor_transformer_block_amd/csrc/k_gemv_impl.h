@@ -22,7 +22,14 @@
 //             appended to the rank's paged cache (step 2 of the same section: its own KV cache);
 //   EPI_REDUCE, EPI_REDUCE_BF  the last rank's row-parallel projection in the one-call block
 //             step: the partial (fp32, or bf16) plus the local reduce (earlier ranks' partials in
-//             rank order, then the residual).
+//             rank order, then the residual);
+//   EPI_RED_ALL, EPI_RED_ALL_BF  every rank's row-parallel projection in one launch: the waves of
+//             a workgroup take the same rows for different ranks (min(N, 4) waves per row group,
+//             each rank's inputs staged side by side, each rank's dot products exactly as in that
+//             rank's own launch), store each partial, and one wave per row group adds them in
+//             rank order from LDS, then the residual.
+// Column-parallel epilogues can also cover every rank in one launch (RankPtrs): each block
+// picks its rank's weight slice and outputs by its index.
 // With PRO (FuseArgs::gamma set) the projection's input is RMSNorm(X) * gamma of the residual rows
 // X: the workgroup stages gamma * x (exact in fp32) and the row's sum of squares from the same
 // loads, and scales the finished dot products by 1/sqrt(mean(x^2) + eps), so the norm costs no
@@ -84,8 +91,11 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
                                               const uint16_t* __restrict__ S, int K, int n_out,
                                               int gate_off, const void* __restrict__ X,
                                               void* __restrict__ Y, int ldy, RopeEpi re,
-                                              FuseArgs fa) {
-  extern __shared__ float xs[];  // [NT][K], then (Q8_0) [NT][K / 16] chunk sums of x
+                                              FuseArgs fa, RankPtrs rp) {
+  // [NR][NT][K] staged token rows (NR ranks' inputs under EPI_RED_ALL*, else one; fp32, or as
+  // stored when EPI_RED_ALL* takes bf16 rows, which halves the workgroup's LDS), then (Q8_0)
+  // [NR][NT][K / 16] fp32 chunk sums of x
+  extern __shared__ float xs[];
   __shared__ float red[PRO ? NT : 1][4];  // prologue norm: each wave's sum of squares per token
   constexpr int VE = WFmt<WT>::VE;
   constexpr int WB = WFmt<WT>::WB;
@@ -93,8 +103,30 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   constexpr int U = 16 / R;
   constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
   static_assert(!PAIRED || R % 2 == 0, "paired epilogues need an even number of rows");
+  constexpr bool ALLR = (EPI == EPI_RED_ALL || EPI == EPI_RED_ALL_BF);
+  constexpr bool XS16 = ALLR && AT == ACT_BF16;  // bf16 rows in LDS, widened (exactly) on use
+  uint16_t* const xs16 = (uint16_t*)xs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int w = blockIdx.x * 4 + wave;
+  // A column-parallel launch over all ranks: this block's rank and its pointers.
+  int blk = blockIdx.x;
+  if constexpr (!ALLR) {
+    if (rp.n > 1) {
+      const int rank = blockIdx.x / rp.bpr;
+      blk -= rank * rp.bpr;
+      W = rp.w[rank];
+      S = rp.s[rank];
+      Y = rp.y[rank];
+      re.q_out = rp.q_out[rank];
+      re.k_pages = rp.k_pages[rank];
+      re.v_pages = rp.v_pages[rank];
+      re.n_pages = rp.n_pages[rank];
+    }
+  }
+  const int NR = ALLR ? rp.n : 1;
+  // EPI_RED_ALL*: WPR waves per row group (wave w serves ranks w % WPR, w % WPR + WPR, ...), RW
+  // row groups per workgroup.
+  const int WPR = NR < 4 ? NR : 4, RW = 4 / WPR;
+  const int w = ALLR ? blk * RW + wave / WPR : blk * 4 + wave;
 
   // Rows of this wavefront's slots.
   int row[R];
@@ -112,7 +144,7 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       row[s] = (p / half) * re.hd + (p % half) + ((s & 1) ? half : 0);
     } else {
       row[s] = w * R + s;
-      ok[s] = row[s] < n_out;
+      ok[s] = row[s] < n_out && (!ALLR || wave / WPR < RW);
     }
     if (!ok[s]) row[s] = 0;  // loads stay in bounds; results are dropped
   }
@@ -123,13 +155,14 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   // token t) are requested first and kept as raw bits until the epilogue, so no wait for them
   // sits in front of the weight stream.
   constexpr bool RED = (EPI == EPI_REDUCE || EPI == EPI_REDUCE_BF);
-  constexpr int RV = RED ? R : 1;
+  constexpr bool RES = RED || ALLR;
+  constexpr int RV = RES ? R : 1;
   static_assert(PV >= 1 && PV <= kMaxPrevPartials, "earlier partials held per row");
   // The loads are unconditional (a lane past the launch's tokens reads token 0, a partial past
   // n_prev reads partial 0, rows out of range read row 0): guarded loads would be merged with
   // their defaults at the branch joins, and each merge waits for its load.
-  uint32_t e_prev[RV][PV], e_res[RV];
-  if constexpr (RED) {
+  uint32_t e_prev[RED ? RV : 1][PV], e_res[RV];
+  if constexpr (RES) {
     const int tl = lane < NT ? lane : 0;
     const bool any_prev = fa.n_prev > 0;
 #pragma unroll
@@ -137,6 +170,7 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       const size_t idx = (size_t)tl * ldy + row[s];
       if constexpr (AT == ACT_F32) e_res[s] = ((const uint32_t*)fa.res_in)[idx];
       else e_res[s] = ((const uint16_t*)fa.res_in)[idx];
+      if constexpr (RED) {
 #pragma unroll
       for (int k = 0; k < PV; ++k) {
         const size_t pi = any_prev ? (size_t)(k < fa.n_prev ? k : 0) * fa.part_stride + idx : 0;
@@ -144,16 +178,20 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
         if constexpr (EPI == EPI_REDUCE_BF) e_prev[s][k] = ((const uint16_t*)base)[pi];
         else e_prev[s][k] = ((const uint32_t*)base)[any_prev ? pi : 0];
       }
+      }
     }
   }
 
   const char* wp[R];
   const uint16_t* sp[R];
+  auto set_rows = [&](const void* Wr, const uint16_t* Sr) {
 #pragma unroll
-  for (int s = 0; s < R; ++s) {
-    wp[s] = (const char*)W + (size_t)row[s] * K * WB;
-    sp[s] = S + (size_t)row[s] * (K / 32);
-  }
+    for (int s = 0; s < R; ++s) {
+      wp[s] = (const char*)Wr + (size_t)row[s] * K * WB;
+      sp[s] = Sr + (size_t)row[s] * (K / 32);
+    }
+  };
+  if constexpr (!ALLR) set_rows(W, S);
   uint4 b[R][U];
   float sc[R][U];
   auto load_batch = [&](int c0) {
@@ -176,7 +214,9 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       }
     }
   };
-  load_batch(0);  // in flight while the token vectors are staged
+  // In flight while the token vectors are staged (EPI_RED_ALL*: each rank's batches all come
+  // from the loop below, which keeps one set of batch registers and address temporaries).
+  if constexpr (!ALLR) load_batch(0);
 
   // Rotary epilogue inputs (each token's position and KV page, the cos/sin of this wave's pairs)
   // do not depend on the projection, so they are fetched here, under the weight stream, instead
@@ -230,20 +270,55 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       const float w = wave_sum(ssq[t]);
       if (lane == 0) red[t][wave] = w;
     }
+  } else if constexpr (XS16) {
+    for (int r = 0; r < NR; ++r) {
+      const uint16_t* xr = (const uint16_t*)rp.x[r];
+      uint16_t* xd = xs16 + (size_t)r * NT * K;
+      for (int i = tid * 8; i < NT * K; i += 256 * 8) *(uint4*)(xd + i) = *(const uint4*)(xr + i);
+    }
   } else {
-    for (int i = tid * AV; i < NT * K; i += 256 * AV)
-      Vec16<AT>::load((const char*)X + (size_t)i * (AT == ACT_F32 ? 4 : 2), xs + i);
+    for (int r = 0; r < NR; ++r) {
+      const char* xr = (const char*)(ALLR ? rp.x[r] : X);
+      float* xd = xs + (size_t)r * NT * K;
+      for (int i = tid * AV; i < NT * K; i += 256 * AV)
+        Vec16<AT>::load(xr + (size_t)i * (AT == ACT_F32 ? 4 : 2), xd + i);
+    }
   }
-  float* const xq = xs + NT * K;
+  // Eight staged values of row `row` (rank-major) from element e0, as fp32.
+  auto xget8 = [&](size_t e0, float* v) {
+    if constexpr (XS16) {
+      const uint4 u = *(const uint4*)(xs16 + e0);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w4[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *(const float4*)(xs + e0), b = *(const float4*)(xs + e0 + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  };
+  float* const xq = XS16 ? (float*)(xs16 + (size_t)NR * NT * K) : xs + (size_t)NR * NT * K;
   if constexpr (WT == W_Q8) {
     __syncthreads();
-    for (int i = tid; i < NT * nch; i += 256) {
-      const float* xp = xs + (size_t)i * 16;  // chunk i % nch of token i / nch (nch = K / 16)
+    for (int i = tid; i < NR * NT * nch; i += 256) {
+      // chunk i % nch of row i / nch (nch = K / 16)
       float a = 0.f;
+      if constexpr (XS16) {
+        float v[16];
+        xget8((size_t)i * 16, v);
+        xget8((size_t)i * 16 + 8, v + 8);
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const float4 v = *(const float4*)(xp + e);
-        a += (v.x + v.y) + (v.z + v.w);
+        for (int e = 0; e < 16; e += 4) a += (v[e] + v[e + 1]) + (v[e + 2] + v[e + 3]);
+      } else {
+        const float* xp = xs + (size_t)i * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          const float4 v = *(const float4*)(xp + e);
+          a += (v.x + v.y) + (v.z + v.w);
+        }
       }
       xq[i] = a;
     }
@@ -263,16 +338,22 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
           st_act<AT>(fa.normed_out, (size_t)t * K + k, xs[(size_t)t * K + k] * inv[t]);
     }
   }
-  if (!active) return;
+  if (!ALLR && !active) return;
 
   float acc[R][NT];
+  // EPI_RED_ALL*: every rank's partial of this workgroup's rows, for the rank-ordered sum.
+  __shared__ float s_part[ALLR ? kMaxRanks : 1][ALLR ? 2 : 1][ALLR ? R : 1][ALLR ? NT : 1];
+  for (int rk = ALLR ? wave % WPR : 0; rk < NR && (!ALLR || active); rk += ALLR ? WPR : 1) {
+  const float* const xsr = xs + (size_t)rk * NT * K;
+  const float* const xqr = xq + (size_t)rk * NT * nch;
+  if constexpr (ALLR) set_rows(rp.w[rk], rp.s[rk]);
 #pragma unroll
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[s][t] = 0.f;
 
   for (int c0 = 0; c0 < nch; c0 += 64 * U) {
-    if (c0 > 0) load_batch(c0);
+    if (ALLR || c0 > 0) load_batch(c0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 64 + lane;
@@ -284,31 +365,49 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
                                     b[s][u].z ^ 0x80808080u, b[s][u].w ^ 0x80808080u};
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              const float* xp = xs + t * K + c * VE;
+              float xv[16];
+              if constexpr (XS16) {
+                const size_t e0 = ((size_t)rk * NT + t) * K + (size_t)c * VE;
+                xget8(e0, xv);
+                xget8(e0 + 8, xv + 8);
+              } else {
+                const float* xp = xsr + t * K + c * VE;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float4 q = *(const float4*)(xp + 4 * i);
+                  xv[4 * i] = q.x; xv[4 * i + 1] = q.y; xv[4 * i + 2] = q.z; xv[4 * i + 3] = q.w;
+                }
+              }
               float d = 0.f;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float4 xv = *(const float4*)(xp + 4 * i);
-                d = fmaf((float)(r4[i] & 0xffu), xv.x, d);
-                d = fmaf((float)((r4[i] >> 8) & 0xffu), xv.y, d);
-                d = fmaf((float)((r4[i] >> 16) & 0xffu), xv.z, d);
-                d = fmaf((float)(r4[i] >> 24), xv.w, d);
+                d = fmaf((float)(r4[i] & 0xffu), xv[4 * i], d);
+                d = fmaf((float)((r4[i] >> 8) & 0xffu), xv[4 * i + 1], d);
+                d = fmaf((float)((r4[i] >> 16) & 0xffu), xv[4 * i + 2], d);
+                d = fmaf((float)(r4[i] >> 24), xv[4 * i + 3], d);
               }
-              acc[s][t] = fmaf(sc[s][u], fmaf(-128.f, xq[t * nch + c], d), acc[s][t]);
+              acc[s][t] = fmaf(sc[s][u], fmaf(-128.f, xqr[t * nch + c], d), acc[s][t]);
             }
           } else {
             float f[VE];
             decode_chunk<WT>(b[s][u], sc[s][u], f);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              const float* xp = xs + t * K + c * VE;
+              if constexpr (XS16) {
+                float xv[8];  // VE == 8: bf16 weights
+                xget8(((size_t)rk * NT + t) * K + (size_t)c * VE, xv);
 #pragma unroll
-              for (int e = 0; e < VE; e += 4) {
-                const float4 xv = *(const float4*)(xp + e);
-                acc[s][t] = fmaf(f[e], xv.x, acc[s][t]);
-                acc[s][t] = fmaf(f[e + 1], xv.y, acc[s][t]);
-                acc[s][t] = fmaf(f[e + 2], xv.z, acc[s][t]);
-                acc[s][t] = fmaf(f[e + 3], xv.w, acc[s][t]);
+                for (int e = 0; e < VE; ++e) acc[s][t] = fmaf(f[e], xv[e], acc[s][t]);
+              } else {
+                const float* xp = xsr + t * K + c * VE;
+#pragma unroll
+                for (int e = 0; e < VE; e += 4) {
+                  const float4 xv = *(const float4*)(xp + e);
+                  acc[s][t] = fmaf(f[e], xv.x, acc[s][t]);
+                  acc[s][t] = fmaf(f[e + 1], xv.y, acc[s][t]);
+                  acc[s][t] = fmaf(f[e + 2], xv.z, acc[s][t]);
+                  acc[s][t] = fmaf(f[e + 3], xv.w, acc[s][t]);
+                }
               }
             }
           }
@@ -320,6 +419,36 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[s][t] = wave_sum(acc[s][t]);
+  if constexpr (ALLR) {
+    // Rank rk's partial at its stored precision: to memory (lane t stores token t) and to LDS.
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        float p = acc[s][t];
+        if constexpr (EPI == EPI_RED_ALL_BF) p = bf16_to_f32(f32_to_bf16(p));
+        if (lane == t && ok[s]) {
+          const size_t idx = (size_t)t * ldy + row[s];
+          if constexpr (EPI == EPI_RED_ALL_BF) ((uint16_t*)rp.y[rk])[idx] = f32_to_bf16(p);
+          else ((float*)rp.y[rk])[idx] = p;
+        }
+        if (lane == 0) s_part[rk][wave / WPR][s][t] = p;
+      }
+    }
+  }
+  }  // ranks
+  float tot[ALLR ? R : 1][ALLR ? NT : 1];  // EPI_RED_ALL*: ((P_0 + P_1) + ...) + P_{N-1}
+  if constexpr (ALLR) {
+    __syncthreads();
+    if (!active || wave % WPR != 0) return;
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        tot[s][t] = s_part[0][wave / WPR][s][t];
+        for (int r = 1; r < NR; ++r) tot[s][t] += s_part[r][wave / WPR][s][t];
+      }
+  }
   if constexpr (PRO) {
 #pragma unroll
     for (int s = 0; s < R; ++s)
@@ -368,6 +497,13 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
         const float res = AT == ACT_F32 ? __uint_as_float(e_res[s]) : bf16_to_f32(e_res[s]);
         st_act<AT>(fa.res_out, idx, res + sum);
       }
+    } else if constexpr (ALLR) {
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        if (!ok[s]) continue;
+        const float res = AT == ACT_F32 ? __uint_as_float(e_res[s]) : bf16_to_f32(e_res[s]);
+        st_act<AT>(fa.res_out, yo + row[s], res + tot[s][t]);
+      }
     } else if constexpr (EPI == EPI_BF16 || EPI == EPI_ACT) {
 #pragma unroll
       for (int s = 0; s < R; ++s)
@@ -409,14 +545,15 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
 template <int WT, int AT, int EPI, int NT, int ACTF, int R, bool PRO, int PV>
 static hipError_t gemv_launch(dim3 g, size_t lds, const void* W, const uint16_t* S, int K,
                               int n_out, int gate_off, const void* X, void* Y, int ldy,
-                              const RopeEpi& re, const FuseArgs& fa, hipStream_t st) {
+                              const RopeEpi& re, const FuseArgs& fa, const RankPtrs& rp,
+                              hipStream_t st) {
   // (Q8_0 with 64 KB of staged tokens goes past the default dynamic-LDS limit.)
   if (lds > 65536) {
     hipError_t ea = allow_lds((const void*)k_gemv<WT, AT, EPI, NT, ACTF, R, PRO, PV>, (int)lds);
     if (ea != hipSuccess) return ea;
   }
   launch((k_gemv<WT, AT, EPI, NT, ACTF, R, PRO, PV>), g, dim3(256), (uint32_t)lds, st, W, S, K,
-         n_out, gate_off, X, Y, ldy, re, fa);
+         n_out, gate_off, X, Y, ldy, re, fa, rp);
   return hipGetLastError();
 }
 
@@ -425,52 +562,64 @@ static hipError_t gemv_launch(dim3 g, size_t lds, const void* W, const uint16_t*
 template <int WT, int AT, int EPI, int NT, int ACTF, int R>
 static hipError_t gemv_variant(dim3 g, size_t lds, const void* W, const uint16_t* S, int K,
                                int n_out, int gate_off, const void* X, void* Y, int ldy,
-                               const RopeEpi& re, const FuseArgs& fa, hipStream_t st) {
+                               const RopeEpi& re, const FuseArgs& fa, const RankPtrs& rp, hipStream_t st) {
   // (EPI_F32 with the prologue: the MoE router on the block's residual stream.)
   constexpr bool CAN_PRO = (EPI == EPI_ROPE || EPI == EPI_GATED || EPI == EPI_F32);
   constexpr bool RED = (EPI == EPI_REDUCE || EPI == EPI_REDUCE_BF);
   if constexpr (CAN_PRO) {
     if (fa.gamma)
       return gemv_launch<WT, AT, EPI, NT, ACTF, R, true, 1>(g, lds, W, S, K, n_out, gate_off, X,
-                                                             Y, ldy, re, fa, st);
+                                                             Y, ldy, re, fa, rp, st);
   } else if (fa.gamma) {
     return hipErrorInvalidValue;
   }
   if constexpr (RED) {
     if (fa.n_prev > 3)
       return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 7>(g, lds, W, S, K, n_out, gate_off, X,
-                                                              Y, ldy, re, fa, st);
+                                                              Y, ldy, re, fa, rp, st);
     if (fa.n_prev > 1)
       return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 3>(g, lds, W, S, K, n_out, gate_off, X,
-                                                              Y, ldy, re, fa, st);
+                                                              Y, ldy, re, fa, rp, st);
   }
   return gemv_launch<WT, AT, EPI, NT, ACTF, R, false, 1>(g, lds, W, S, K, n_out, gate_off, X, Y,
-                                                          ldy, re, fa, st);
+                                                          ldy, re, fa, rp, st);
 }
 
 template <int WT, int AT, int EPI, int ACTF, int R>
 static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n_out, int gate_off,
                           const void* X, void* Y, int ldy, const RopeEpi& re, const FuseArgs& fa,
-                          hipStream_t st) {
+                          const RankPtrs& rp, hipStream_t st) {
   int waves;
   if constexpr (EPI == EPI_GATED) waves = (n_out + R / 2 - 1) / (R / 2);
   else if constexpr (EPI == EPI_ROPE) waves = (n_out / 2 + R / 2 - 1) / (R / 2);
   else waves = (n_out + R - 1) / R;
-  const dim3 g((waves + 3) / 4);
-  const size_t lds = (size_t)nt * K * sizeof(float) + (WT == W_Q8 ? (size_t)nt * (K / 16) * 4 : 0);
+  constexpr bool ALLR = (EPI == EPI_RED_ALL || EPI == EPI_RED_ALL_BF);
+  // Column-parallel launches over all ranks repeat the grid once per rank; the row-parallel
+  // EPI_RED_ALL* launches stage every rank's inputs.
+  const int nr = rp.n > 1 ? rp.n : 1;
+  // EPI_RED_ALL*: each row group takes min(N, 4) waves, 4 / min(N, 4) row groups per block.
+  const int rw = 4 / (nr < 4 ? nr : 4);
+  const int bpr = ALLR ? (waves + rw - 1) / rw : (waves + 3) / 4;
+  const dim3 g(ALLR ? bpr : bpr * nr);
+  // (EPI_RED_ALL* with bf16 rows keeps them as bf16.)
+  const size_t xb = (ALLR && AT == ACT_BF16) ? 2 : sizeof(float);
+  const size_t lds = (size_t)(ALLR ? nr : 1) *
+                     ((size_t)nt * K * xb + (WT == W_Q8 ? (size_t)nt * (K / 16) * 4 : 0));
+  RankPtrs rq = rp;
+  rq.bpr = bpr;
   switch (nt) {
     case 1:
       return gemv_variant<WT, AT, EPI, 1, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
-                                                    re, fa, st);
+                                                    re, fa, rq, st);
     case 2:
       return gemv_variant<WT, AT, EPI, 2, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
-                                                    re, fa, st);
+                                                    re, fa, rq, st);
     case 3:
       return gemv_variant<WT, AT, EPI, 3, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
-                                                    re, fa, st);
+                                                    re, fa, rq, st);
     case 4:
       return gemv_variant<WT, AT, EPI, 4, ACTF, R>(g, lds, W, S, K, n_out, gate_off, X, Y, ldy,
-                                                    re, fa, st);
+                                                    re, fa, rq, st);
   }
   return hipErrorInvalidValue;
 }
@@ -478,16 +627,16 @@ static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n
 template <int WT, int AT, int EPI, int ACTF>
 static hipError_t gemv_r(int r, int nt, const void* W, const uint16_t* S, int K, int n_out,
                          int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                         const FuseArgs& fa, hipStream_t st) {
+                         const FuseArgs& fa, const RankPtrs& rp, hipStream_t st) {
   constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
   switch (r) {
     case 1:
       if constexpr (!PAIRED)
-        return gemv_nt<WT, AT, EPI, ACTF, 1>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+        return gemv_nt<WT, AT, EPI, ACTF, 1>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
       return hipErrorInvalidValue;
-    case 2: return gemv_nt<WT, AT, EPI, ACTF, 2>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
-    case 4: return gemv_nt<WT, AT, EPI, ACTF, 4>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
-    case 8: return gemv_nt<WT, AT, EPI, ACTF, 8>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+    case 2: return gemv_nt<WT, AT, EPI, ACTF, 2>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
+    case 4: return gemv_nt<WT, AT, EPI, ACTF, 4>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
+    case 8: return gemv_nt<WT, AT, EPI, ACTF, 8>(nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
   }
   return hipErrorInvalidValue;
 }
@@ -496,43 +645,53 @@ static hipError_t gemv_r(int r, int nt, const void* W, const uint16_t* S, int K,
 template <int WT, int AT>
 hipError_t gemv_format(int epi, int actf, int nt, const void* W, const uint16_t* S, int K,
                        int n_out, int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                       const FuseArgs& fa, hipStream_t st) {
+                       const FuseArgs& fa, const RankPtrs& rp, hipStream_t st) {
   const int nch = K / WFmt<WT>::VE;
   const bool paired = (epi == EPI_GATED || epi == EPI_ROPE);
-  const int r = gemv_rows_per_wave(nch, paired, epi == EPI_GATED ? 2L * n_out : (long)n_out);
+  // (EPI_RED_ALL*: a row group takes one wave per rank, up to four.)
+  const long wrows = (epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF)
+                         ? (long)n_out * (rp.n < 4 ? (rp.n > 1 ? rp.n : 1) : 4)
+                         : (epi == EPI_GATED ? 2L * n_out : (long)n_out);
+  const int r = gemv_rows_per_wave(nch, paired, wrows);
   switch (epi) {
     case EPI_F32:
-      return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
     case EPI_BF16:
-      return gemv_r<WT, AT, EPI_BF16, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_BF16, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
     case EPI_ACT:
-      return gemv_r<WT, AT, EPI_ACT, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_ACT, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
     case EPI_REDUCE:
-      return gemv_r<WT, AT, EPI_REDUCE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_REDUCE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
     case EPI_REDUCE_BF:
-      return gemv_r<WT, AT, EPI_REDUCE_BF, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa,
+      return gemv_r<WT, AT, EPI_REDUCE_BF, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp,
                                               st);
+    case EPI_RED_ALL:
+      return gemv_r<WT, AT, EPI_RED_ALL, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp,
+                                            st);
+    case EPI_RED_ALL_BF:
+      return gemv_r<WT, AT, EPI_RED_ALL_BF, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa,
+                                               rp, st);
     case EPI_ROPE:
-      return gemv_r<WT, AT, EPI_ROPE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+      return gemv_r<WT, AT, EPI_ROPE, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
     case EPI_GATED:
       if (actf == 0)
-        return gemv_r<WT, AT, EPI_GATED, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
-      return gemv_r<WT, AT, EPI_GATED, 1>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, st);
+        return gemv_r<WT, AT, EPI_GATED, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
+      return gemv_r<WT, AT, EPI_GATED, 1>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t gemv_f32(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                     int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                    const FuseArgs& fa,
+                    const FuseArgs& fa, const RankPtrs& rp,
                     hipStream_t st);
 hipError_t gemv_bf16(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                      int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                    const FuseArgs& fa,
+                    const FuseArgs& fa, const RankPtrs& rp,
                      hipStream_t st);
 hipError_t gemv_q8(int epi, int actf, int nt, const void* W, const uint16_t* S, int K, int n_out,
                    int gate_off, const void* X, void* Y, int ldy, const RopeEpi& re,
-                    const FuseArgs& fa,
+                    const FuseArgs& fa, const RankPtrs& rp,
                    hipStream_t st);
 
 }  // namespace tpk

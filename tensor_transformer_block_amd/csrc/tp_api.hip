@@ -306,6 +306,26 @@ bool fused_step_ok(const Dims& x, int T) {
   return !use_q8_gemm(x, T);
 }
 
+int gemv_wt(const Dims& x) {
+  return x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
+}
+
+// ... and, when every rank's inputs fit one workgroup's LDS, each projection and the attention
+// run as one launch for all ranks (the row-parallel ones adding the partials in rank order), so
+// the decode step is six launches. Each rank then needs its own copy of the workspace.
+bool ranks_step_ok(const Dims& x, int T) {
+  if (!fused_step_ok(x, T) || x.N < 2) return false;
+  const int wt = gemv_wt(x);
+  return tpk::gemv_ranks_fit(wt, tpk::EPI_ROPE, x.N, T, x.d) &&
+         tpk::gemv_ranks_fit(wt, tpk::EPI_RED_ALL, x.N, T, x.qdim) &&
+         tpk::gemv_ranks_fit(wt, tpk::EPI_RED_ALL, x.N, T, x.fr);
+}
+
+uint64_t step_ws_bytes(const Dims& x, const tp_batch& b) {
+  const uint64_t one = ws_layout(x, b).total;
+  return ranks_step_ok(x, b.n_tokens) ? (uint64_t)x.N * align_up(one) : one;
+}
+
 }  // namespace
 
 extern "C" {
@@ -823,6 +843,27 @@ tp_status tp_workspace_size(const tp_block_desc* desc, const tp_batch* batch, ui
   return TP_OK;
 }
 
+tp_status tp_step_workspace_size(const tp_block_desc* desc, const tp_batch* batch,
+                                 uint64_t* bytes) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (tp_status s = check_batch(x, batch, false)) return s;
+  if (!bytes) return fail(TP_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = step_ws_bytes(x, *batch);
+  return TP_OK;
+}
+
+tp_status tp_step_schedule(const tp_block_desc* desc, const tp_batch* batch, int32_t* schedule) {
+  Dims x;
+  if (tp_status s = check_desc(desc, &x)) return s;
+  if (tp_status s = check_batch(x, batch, false)) return s;
+  if (!schedule) return fail(TP_ERR_INVALID_ARG, "schedule is NULL");
+  const int T = batch->n_tokens;
+  *schedule = ranks_step_ok(x, T) ? TP_SCHEDULE_ALL_RANKS
+                                  : (fused_step_ok(x, T) ? TP_SCHEDULE_PER_RANK : TP_SCHEDULE_STAGED);
+  return TP_OK;
+}
+
 tp_status tp_workspace_offsets(const tp_block_desc* desc, const tp_batch* batch,
                                uint64_t* q_offset, uint64_t* attn_offset, uint64_t* ffn_offset) {
   Dims x;
@@ -1138,16 +1179,174 @@ static tp_status attn_halves_fused(const tp_block_desc* desc, const Dims& x,
   return TP_OK;
 }
 
+// The attention halves of all ranks as three launches: every rank's QKV projection (with the norm
+// prologue; rank 0's block also stores xn), every rank's attention and split merge, and every
+// rank's o_proj with the rank-ordered reduce into h1. Rank r uses workspace copy r.
+static tp_status attn_halves_ranks(const tp_block_desc* desc, const Dims& x,
+                                   const void* const* shards, const tp_batch* batch,
+                                   const tp_kv_cache* kv, const void* x_in, const void* gamma1,
+                                   void* partials, void* xn, void* h1, void* workspace,
+                                   uint64_t workspace_bytes, void* stream) {
+  const int T = batch->n_tokens, N = x.N;
+  const WsLayout w = ws_layout(x, *batch);
+  const uint64_t wstride = align_up(w.total);
+  if (workspace_bytes < (uint64_t)N * wstride)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu (one copy per rank)",
+                (unsigned long long)workspace_bytes, (unsigned long long)N * wstride);
+  if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  for (int r = 0; r < N; ++r) {
+    if (!shards[r] || !aligned16(shards[r]))
+      return fail(TP_ERR_INVALID_ARG, "shard %d is NULL or not 16-byte aligned", r);
+    if (!kv[r].k_pages || !kv[r].v_pages || kv[r].n_pages <= 0)
+      return fail(TP_ERR_INVALID_ARG, "ATTN needs a KV cache with non-NULL pages and n_pages > 0");
+    if (!aligned16(kv[r].k_pages) || !aligned16(kv[r].v_pages))
+      return fail(TP_ERR_INVALID_ARG, "KV pages must be 16-byte aligned");
+  }
+  tp_shard_layout L;
+  make_layout(x, &L);
+  hipStream_t st = (hipStream_t)stream;
+  const int wt = gemv_wt(x);
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  const size_t pstride = (size_t)T * x.d, pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  auto wsr = [&](int r) { return (char*)workspace + (size_t)r * wstride; };
+  auto shard = [&](int r) { return (const char*)shards[r]; };
+
+  tpk::RankPtrs rq{};
+  rq.n = N;
+  for (int r = 0; r < N; ++r) {
+    rq.w[r] = shard(r) + L.qkv.offset;
+    rq.s[r] = (const uint16_t*)(shard(r) + L.qkv_scale.offset);
+    rq.y[r] = wsr(r) + w.qkv;
+    rq.q_out[r] = wsr(r) + w.q;
+    rq.k_pages[r] = kv[r].k_pages;
+    rq.v_pages[r] = kv[r].v_pages;
+    rq.n_pages[r] = kv[r].n_pages;
+  }
+  tpk::RopeEpi re{};
+  re.positions = batch->positions;
+  re.block_table = batch->block_table;
+  re.rope = batch->rope_table;
+  re.mode = batch->mode;
+  re.max_pages = batch->max_pages;
+  re.ps = x.ps;
+  re.pos_limit = w.pos_limit;
+  re.hq = x.hq;
+  re.hk = x.hk;
+  re.hd = x.hd;
+  tpk::FuseArgs fin{};
+  fin.gamma = gamma1;
+  fin.eps = x.eps;
+  fin.normed_out = xn;
+  hipError_t e = tpk::launch_gemv_ranks(wt, at, tpk::EPI_ROPE, x.actf, T, rq, x.d, x.qkv_rows, 0,
+                                        x_in, x.qkv_rows, &re, st, fin);
+  if (e != hipSuccess) return hip_fail(e, "qkv projection (all ranks)");
+
+  tpk::AttnRanks ar{};
+  ar.n = N;
+  for (int r = 0; r < N; ++r) {
+    ar.q[r] = wsr(r) + w.q;
+    ar.k_pages[r] = kv[r].k_pages;
+    ar.v_pages[r] = kv[r].v_pages;
+    ar.n_pages[r] = kv[r].n_pages;
+    ar.part_o[r] = (float*)(wsr(r) + w.part_o);
+    ar.part_ml[r] = (float*)(wsr(r) + w.part_ml);
+    ar.out[r] = wsr(r) + w.attn;
+  }
+  e = tpk::launch_attn_decode_ranks(at, x.hd, x.Hq / x.Hkv, T, x.hk, ar, batch->positions,
+                                    batch->block_table, batch->max_pages, x.ps, w.chunk, w.n_split,
+                                    w.pos_limit, st);
+  if (e != hipSuccess) return hip_fail(e, "attention (all ranks)");
+
+  tpk::RankPtrs ro{};
+  ro.n = N;
+  for (int r = 0; r < N; ++r) {
+    ro.w[r] = shard(r) + L.o.offset;
+    ro.s[r] = (const uint16_t*)(shard(r) + L.o_scale.offset);
+    ro.x[r] = wsr(r) + w.attn;
+    ro.y[r] = (char*)partials + (size_t)r * pstride * pbytes;
+  }
+  tpk::FuseArgs fo{};
+  fo.res_in = x_in;
+  fo.res_out = h1;
+  e = tpk::launch_gemv_ranks(wt, at, x.pt == TP_DTYPE_F32 ? tpk::EPI_RED_ALL : tpk::EPI_RED_ALL_BF,
+                             0, T, ro, x.qdim, x.d, 0, nullptr, x.d, nullptr, st, fo);
+  if (e != hipSuccess) return hip_fail(e, "o projection and reduce (all ranks)");
+  return TP_OK;
+}
+
+// The FFN half of all ranks as two launches: every rank's gate/up (norm prologue; rank 0's block
+// stores xn2) and every rank's down projection with the rank-ordered reduce into out.
+static tp_status ffn_halves_ranks(const tp_block_desc* desc, const Dims& x,
+                                  const void* const* shards, const tp_batch* batch,
+                                  const void* h1, const void* gamma2, void* partials, void* xn2,
+                                  void* out, void* workspace, void* stream, hipEvent_t evb,
+                                  hipEvent_t eve) {
+  (void)desc;
+  const int T = batch->n_tokens, N = x.N;
+  const WsLayout w = ws_layout(x, *batch);
+  const uint64_t wstride = align_up(w.total);
+  tp_shard_layout L;
+  make_layout(x, &L);
+  hipStream_t st = (hipStream_t)stream;
+  const int wt = gemv_wt(x);
+  const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+  const size_t pstride = (size_t)T * x.d, pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  auto wsr = [&](int r) { return (char*)workspace + (size_t)r * wstride; };
+  auto shard = [&](int r) { return (const char*)shards[r]; };
+  tpk::RankPtrs rg{};
+  rg.n = N;
+  for (int r = 0; r < N; ++r) {
+    rg.w[r] = shard(r) + L.gate_up.offset;
+    rg.s[r] = (const uint16_t*)(shard(r) + L.gate_up_scale.offset);
+    rg.y[r] = wsr(r) + w.ffn;
+  }
+  tpk::FuseArgs fin{};
+  fin.gamma = gamma2;
+  fin.eps = x.eps;
+  fin.normed_out = xn2;
+  hipError_t e;
+  {
+    TimedScope ts(evb, eve);
+    e = tpk::launch_gemv_ranks(wt, at, tpk::EPI_GATED, x.actf, T, rg, x.d, x.fr, x.fr, h1, x.fr,
+                               nullptr, st, fin);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gate/up projection (all ranks)");
+  tpk::RankPtrs rd{};
+  rd.n = N;
+  for (int r = 0; r < N; ++r) {
+    rd.w[r] = shard(r) + L.down.offset;
+    rd.s[r] = (const uint16_t*)(shard(r) + L.down_scale.offset);
+    rd.x[r] = wsr(r) + w.ffn;
+    rd.y[r] = (char*)partials + (size_t)r * pstride * pbytes;
+  }
+  tpk::FuseArgs fo{};
+  fo.res_in = h1;
+  fo.res_out = out;
+  e = tpk::launch_gemv_ranks(wt, at, x.pt == TP_DTYPE_F32 ? tpk::EPI_RED_ALL : tpk::EPI_RED_ALL_BF,
+                             0, T, rd, x.fr, x.d, 0, nullptr, x.d, nullptr, st, fo);
+  if (e != hipSuccess) return hip_fail(e, "down projection and reduce (all ranks)");
+  return TP_OK;
+}
+
 static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
                            const void* gamma1, const void* gamma2, void* partials, void* xn,
                            void* h1, void* xn2, void* out, void* workspace,
                            uint64_t workspace_bytes, void* stream, int32_t timed_rank,
-                           hipEvent_t evb, hipEvent_t eve) {
+                           hipEvent_t evb, hipEvent_t eve, int32_t schedule = -1) {
   Dims x;
   if (tp_status s = check_desc(desc, &x)) return s;
   if (tp_status s = check_batch(x, batch, true)) return s;
   const int T = batch->n_tokens, N = x.N;
+  if (schedule < -1 || schedule > TP_SCHEDULE_ALL_RANKS)
+    return fail(TP_ERR_INVALID_ARG, "unknown schedule %d", schedule);
+  const int best = ranks_step_ok(x, T) ? TP_SCHEDULE_ALL_RANKS
+                                       : (fused_step_ok(x, T) ? TP_SCHEDULE_PER_RANK
+                                                              : TP_SCHEDULE_STAGED);
+  if (schedule > best)
+    return fail(TP_ERR_UNSUPPORTED, "schedule %d is not available for this batch (at most %d)",
+                schedule, best);
+  const int sched = schedule < 0 ? best : schedule;
   if (T == 0) {
     g_err.clear();
     return TP_OK;
@@ -1166,7 +1365,7 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
   auto timing = [&](int r) -> std::pair<hipEvent_t, hipEvent_t> {
     return r == timed_rank ? std::make_pair(evb, eve) : std::make_pair(hipEvent_t{}, hipEvent_t{});
   };
-  if (!fused_step_ok(x, T)) {
+  if (sched == TP_SCHEDULE_STAGED) {
     // The staged sequence of the same library calls.
     if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
       return s;
@@ -1183,6 +1382,19 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
         return s;
     }
     return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
+  }
+  if (sched == TP_SCHEDULE_ALL_RANKS) {
+    // One launch per projection and for the attention, covering every rank.
+    if (tp_status s = attn_halves_ranks(desc, x, shards, batch, kv, x_in, gamma1, partials, xn,
+                                        h1, workspace, workspace_bytes, stream))
+      return s;
+    const bool timed = timed_rank >= 0 && timed_rank < N;
+    if (tp_status s = ffn_halves_ranks(desc, x, shards, batch, h1, gamma2, partials, xn2, out,
+                                       workspace, stream, timed ? evb : nullptr,
+                                       timed ? eve : nullptr))
+      return s;
+    g_err.clear();
+    return TP_OK;
   }
   // Fused schedule: every rank's first projection normalises the residual stream itself, and
   // the last rank's row-parallel projection adds all ranks' partials (rank order) and the
@@ -1241,9 +1453,14 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
   auto part = [&](int r) { return (void*)((char*)partials + (size_t)r * pstride * pbytes); };
   const bool fused = fused_step_ok(x, T);
   if (fused) {
-    if (tp_status s = attn_halves_fused(desc, x, shards, batch, kv, x_in, gamma1, partials, xn,
-                                        h1, workspace, workspace_bytes, stream))
+    if (ranks_step_ok(x, T)) {
+      if (tp_status s = attn_halves_ranks(desc, x, shards, batch, kv, x_in, gamma1, partials, xn,
+                                          h1, workspace, workspace_bytes, stream))
+        return s;
+    } else if (tp_status s = attn_halves_fused(desc, x, shards, batch, kv, x_in, gamma1, partials,
+                                               xn, h1, workspace, workspace_bytes, stream)) {
       return s;
+    }
     // The router normalises h1 itself and stores xn2 for the experts.
     tpk::FuseArgs fin{};
     fin.eps = x.eps;
@@ -1293,6 +1510,16 @@ tp_status tp_block_step(const tp_block_desc* desc, const void* const* shards, co
                         void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
   return step_impl(desc, shards, batch, kv, x, gamma1, gamma2, partials, xn, h1, xn2, out,
                    workspace, workspace_bytes, stream, -1, nullptr, nullptr);
+}
+
+tp_status tp_block_step_with_schedule(const tp_block_desc* desc, int32_t schedule,
+                                      const void* const* shards, const tp_batch* batch,
+                                      const tp_kv_cache* kv, const void* x, const void* gamma1,
+                                      const void* gamma2, void* partials, void* xn, void* h1,
+                                      void* xn2, void* out, void* workspace,
+                                      uint64_t workspace_bytes, void* stream) {
+  return step_impl(desc, shards, batch, kv, x, gamma1, gamma2, partials, xn, h1, xn2, out,
+                   workspace, workspace_bytes, stream, -1, nullptr, nullptr, schedule);
 }
 
 tp_status tp_block_step_timed(const tp_block_desc* desc, const void* const* shards,

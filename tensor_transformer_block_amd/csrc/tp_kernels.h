@@ -10,7 +10,7 @@ namespace tpk {
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 enum WType { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
 enum Epilogue { EPI_ACT = 0, EPI_F32 = 1, EPI_BF16 = 2, EPI_GATED = 3, EPI_ROPE = 4,
-                EPI_REDUCE = 5, EPI_REDUCE_BF = 6 };
+                EPI_REDUCE = 5, EPI_REDUCE_BF = 6, EPI_RED_ALL = 7, EPI_RED_ALL_BF = 8 };
 
 // Optional timing of one projection by kernel execution (not by stream events): while `stop` is
 // set, every launch below goes through hipExtLaunchKernelGGL, the first one also recording
@@ -63,6 +63,40 @@ struct FuseArgs {
   void* res_out;
 };
 
+// One launch that covers every rank's share of a step (the one-call decode step), with each
+// rank's own pointers. Column-parallel projections (and the decode attention): blocks
+// [r * bpr, (r + 1) * bpr) work for rank r with w[r], s[r], y[r] and, under the rotary epilogue,
+// the rank's q buffer and KV pool. Row-parallel projections with EPI_RED_ALL / EPI_RED_ALL_BF:
+// every block computes its output rows for all ranks, rank r from its input rows x[r] and weight
+// slice w[r]; each rank's partial is stored at y[r] and the partials are added in rank order
+// (then the residual, FuseArgs::res_in / res_out), the arithmetic of the reduce kernel.
+constexpr int kMaxRanks = 8;
+struct RankPtrs {
+  int n;    // ranks in the launch; 0: a single rank's launch (the plain pointer arguments)
+  int bpr;  // blocks per rank of a column-parallel launch
+  const void* w[kMaxRanks];
+  const uint16_t* s[kMaxRanks];
+  const void* x[kMaxRanks];
+  void* y[kMaxRanks];
+  void* q_out[kMaxRanks];
+  void* k_pages[kMaxRanks];
+  void* v_pages[kMaxRanks];
+  int n_pages[kMaxRanks];
+};
+
+// Per-rank pointers of a decode attention launch over all ranks (blockIdx.y = rank * hk + kv
+// head); n = 0: a single rank's launch (the plain pointer arguments).
+struct AttnRanks {
+  int n;
+  const void* q[kMaxRanks];
+  const void* k_pages[kMaxRanks];
+  const void* v_pages[kMaxRanks];
+  int n_pages[kMaxRanks];
+  float* part_o[kMaxRanks];
+  float* part_ml[kMaxRanks];
+  void* out[kMaxRanks];
+};
+
 // Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device; done once per (kernel,
 // device) and remembered, so launchers may call it before every launch.
 hipError_t allow_lds(const void* kernel, int bytes);
@@ -100,6 +134,13 @@ int gemv_max_tokens(int K);
 hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, const void* S,
                        int K, int n_out, int gate_off, const void* X, void* Y, int ldy,
                        const RopeEpi* rope, hipStream_t st, const FuseArgs* fuse = nullptr);
+// The same projection for every rank in one launch (RankPtrs; T within one token group):
+// column-parallel epilogues (EPI_ROPE, EPI_GATED) with the norm prologue, or the row-parallel
+// EPI_RED_ALL / EPI_RED_ALL_BF. gemv_ranks_fit: whether the launch's staged inputs fit the LDS.
+bool gemv_ranks_fit(int wt, int epi, int n_ranks, int T, int K);
+hipError_t launch_gemv_ranks(int wt, int at, int epi, int actf, int T, const RankPtrs& rp, int K,
+                             int n_out, int gate_off, const void* X, int ldy, const RopeEpi* rope,
+                             hipStream_t st, const FuseArgs& fuse);
 
 // k_gemm.hip
 // Split-K projection of M <= 64 tokens; `part` holds the fp32 split tiles
@@ -170,5 +211,9 @@ hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* 
                               int max_pages, int ps, int n_pages, int chunk, int n_split,
                               int pos_limit, float* part_o, float* part_ml, void* out,
                               hipStream_t st);
+// Decode attention (mode 0) of every rank in one launch, and one merge launch for all ranks.
+hipError_t launch_attn_decode_ranks(int at, int hd, int G, int T, int hk, const AttnRanks& ar,
+                                    const int* positions, const int* bt, int max_pages, int ps,
+                                    int chunk, int n_split, int pos_limit, hipStream_t st);
 
 }  // namespace tpk

@@ -238,6 +238,27 @@ def test_one_call_step(name, partial_dtype):
         assert b <= tol, (k, b)
         if not fused:
             assert b == 0.0, (k, b)
+    # The all-ranks schedule (one launch per projection for every rank) against the per-rank
+    # fused schedule: the same bits everywhere, partials and new cache entries included.
+    from tensor_transformer_block_amd import binding as B
+    if blk.schedule() == B.TP_SCHEDULE_ALL_RANKS:
+        def bits(t):
+            return t.contiguous().view(torch.uint8).cpu()
+        outs = ("xn", "h1", "xn2", "out", "partials")
+        all_ranks = {k: bits(getattr(blk, k)) for k in outs}
+        def nbits(a):
+            return np.ascontiguousarray(a).view(np.uint8).copy()
+        kv_all = [tuple(nbits(a) for a in blk.cache_new_entries(rk)) for rk in range(blk.N)]
+        for k in outs:
+            getattr(blk, k).fill_(float("nan"))
+        blk.step_fused(schedule=B.TP_SCHEDULE_PER_RANK)
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(bits(getattr(blk, k)), all_ranks[k]), f"all-ranks vs per-rank {k}"
+        for rk in range(blk.N):
+            for a, b in zip(kv_all[rk], blk.cache_new_entries(rk)):
+                assert np.array_equal(a, nbits(b)), f"all-ranks vs per-rank cache r{rk}"
+        log(f"one-call step {name}: all-ranks schedule == per-rank schedule, bit for bit")
     # The folded reduce, bit for bit: out from h1 and the stored FFN partials.
     tdt = torch.float32 if s.act_dtype == "f32" else torch.bfloat16
     acc = blk.partials[0].float().cpu().clone()
