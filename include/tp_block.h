@@ -220,7 +220,7 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * to the activation dtype first, as the separate calls round it; xn and xn2 are still stored,
  * rounded), and the last rank's o_proj and down projections add all ranks' partials in rank
  * order plus the residual, with the reduce's arithmetic. Every rank's partial is still stored.
- * When, in addition, every rank's inputs of a projection fit one workgroup's LDS (N > 1), each
+ * When, in addition, every rank's inputs of a projection fit one workgroup's LDS (1 < N <= 4), each
  * projection and the attention run as one launch for all ranks (TP_SCHEDULE_ALL_RANKS: six
  * launches per step, seven with the attention's split merge counted): every block of a
  * column-parallel launch works for one rank with that rank's slice and cache, and every block

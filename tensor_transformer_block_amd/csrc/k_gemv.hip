@@ -55,8 +55,9 @@ static size_t ranks_lds(int wt, int epi, int n_ranks, int T, int K) {
 }
 
 bool gemv_ranks_fit(int wt, int epi, int n_ranks, int T, int K) {
-  return n_ranks >= 1 && n_ranks <= kMaxRanks && T >= 1 && T <= gemv_max_tokens(K) &&
-         ranks_lds(wt, epi, n_ranks, T, K) <= 160 * 1024;
+  const bool allr = epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF;
+  return n_ranks >= 1 && n_ranks <= (allr ? 4 : kMaxRanks) && T >= 1 &&
+         T <= gemv_max_tokens(K) && ranks_lds(wt, epi, n_ranks, T, K) <= 160 * 1024;
 }
 
 hipError_t launch_gemv_ranks(int wt, int at, int epi, int actf, int T, const RankPtrs& rp, int K,

@@ -23,8 +23,8 @@
 //   EPI_REDUCE, EPI_REDUCE_BF  the last rank's row-parallel projection in the one-call block
 //             step: the partial (fp32, or bf16) plus the local reduce (earlier ranks' partials in
 //             rank order, then the residual);
-//   EPI_RED_ALL, EPI_RED_ALL_BF  every rank's row-parallel projection in one launch: the waves of
-//             a workgroup take the same rows for different ranks (min(N, 4) waves per row group,
+//   EPI_RED_ALL, EPI_RED_ALL_BF  every rank's row-parallel projection in one launch (N <= 4): the
+//             waves of a workgroup take the same rows for different ranks (N waves per row group,
 //             each rank's inputs staged side by side, each rank's dot products exactly as in that
 //             rank's own launch), store each partial, and one wave per row group adds them in
 //             rank order from LDS, then the residual.
@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
     }
   }
   const int NR = ALLR ? rp.n : 1;
-  // EPI_RED_ALL*: WPR waves per row group (wave w serves ranks w % WPR, w % WPR + WPR, ...), RW
-  // row groups per workgroup.
+  // EPI_RED_ALL* (N <= 4): WPR = N waves per row group (wave w serves rank w % N), RW row
+  // groups per workgroup.
   const int WPR = NR < 4 ? NR : 4, RW = 4 / WPR;
   const int w = ALLR ? blk * RW + wave / WPR : blk * 4 + wave;
 
@@ -214,9 +214,11 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       }
     }
   };
-  // In flight while the token vectors are staged (EPI_RED_ALL*: each rank's batches all come
-  // from the loop below, which keeps one set of batch registers and address temporaries).
-  if constexpr (!ALLR) load_batch(0);
+  // In flight while the token vectors are staged (EPI_RED_ALL*: the first batch of the wave's
+  // first rank).
+  const int rk0 = ALLR ? wave % WPR : 0;
+  if constexpr (ALLR) set_rows(rp.w[rk0], rp.s[rk0]);  // rk0 < NR; idle waves read row 0
+  load_batch(0);
 
   // Rotary epilogue inputs (each token's position and KV page, the cos/sin of this wave's pairs)
   // do not depend on the projection, so they are fetched here, under the weight stream, instead
@@ -343,17 +345,18 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   float acc[R][NT];
   // EPI_RED_ALL*: every rank's partial of this workgroup's rows, for the rank-ordered sum.
   __shared__ float s_part[ALLR ? kMaxRanks : 1][ALLR ? 2 : 1][ALLR ? R : 1][ALLR ? NT : 1];
-  for (int rk = ALLR ? wave % WPR : 0; rk < NR && (!ALLR || active); rk += ALLR ? WPR : 1) {
+  // EPI_RED_ALL* (at most four ranks): each wave serves exactly one rank, rk0.
+  if (!ALLR || active) {
+  const int rk = rk0;
   const float* const xsr = xs + (size_t)rk * NT * K;
   const float* const xqr = xq + (size_t)rk * NT * nch;
-  if constexpr (ALLR) set_rows(rp.w[rk], rp.s[rk]);
 #pragma unroll
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[s][t] = 0.f;
 
   for (int c0 = 0; c0 < nch; c0 += 64 * U) {
-    if (ALLR || c0 > 0) load_batch(c0);
+    if (c0 > 0) load_batch(c0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 64 + lane;
@@ -436,7 +439,7 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       }
     }
   }
-  }  // ranks
+  }  // the wave's rank
   float tot[ALLR ? R : 1][ALLR ? NT : 1];  // EPI_RED_ALL*: ((P_0 + P_1) + ...) + P_{N-1}
   if constexpr (ALLR) {
     __syncthreads();

@@ -310,7 +310,7 @@ int gemv_wt(const Dims& x) {
   return x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
 }
 
-// ... and, when every rank's inputs fit one workgroup's LDS, each projection and the attention
+// ... and, with at most four ranks whose inputs fit one workgroup's LDS, each projection and the attention
 // run as one launch for all ranks (the row-parallel ones adding the partials in rank order), so
 // the decode step is six launches. Each rank then needs its own copy of the workspace.
 bool ranks_step_ok(const Dims& x, int T) {

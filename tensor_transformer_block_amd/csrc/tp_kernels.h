@@ -66,10 +66,11 @@ struct FuseArgs {
 // One launch that covers every rank's share of a step (the one-call decode step), with each
 // rank's own pointers. Column-parallel projections (and the decode attention): blocks
 // [r * bpr, (r + 1) * bpr) work for rank r with w[r], s[r], y[r] and, under the rotary epilogue,
-// the rank's q buffer and KV pool. Row-parallel projections with EPI_RED_ALL / EPI_RED_ALL_BF:
-// every block computes its output rows for all ranks, rank r from its input rows x[r] and weight
-// slice w[r]; each rank's partial is stored at y[r] and the partials are added in rank order
-// (then the residual, FuseArgs::res_in / res_out), the arithmetic of the reduce kernel.
+// the rank's q buffer and KV pool. Row-parallel projections with EPI_RED_ALL / EPI_RED_ALL_BF
+// (at most four ranks): every block computes its output rows for all ranks, rank r from its
+// input rows x[r] and weight slice w[r]; each rank's partial is stored at y[r] and the partials
+// are added in rank order (then the residual, FuseArgs::res_in / res_out), the arithmetic of the
+// reduce kernel.
 constexpr int kMaxRanks = 8;
 struct RankPtrs {
   int n;    // ranks in the launch; 0: a single rank's launch (the plain pointer arguments)
