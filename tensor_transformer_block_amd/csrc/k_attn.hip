@@ -73,7 +73,16 @@ __global__ void k_rope_append_parts(const float* __restrict__ parts, int T, int 
                                     const int* __restrict__ positions, int mode,
                                     const int* __restrict__ block_table, int max_pages, int ps,
                                     int n_pages, int pos_limit, uint16_t* __restrict__ kp,
-                                    uint16_t* __restrict__ vp, const float2* __restrict__ rope) {
+                                    uint16_t* __restrict__ vp, const float2* __restrict__ rope,
+                                    RopeRanks rr) {
+  if (rr.n > 1) {  // every rank in one launch (blockIdx.y = rank)
+    const int r = blockIdx.y;
+    parts = rr.parts[r];
+    q_out = (uint16_t*)rr.q_out[r];
+    kp = (uint16_t*)rr.k_pages[r];
+    vp = (uint16_t*)rr.v_pages[r];
+    n_pages = rr.n_pages[r];
+  }
   // Thread: four consecutive rotation pairs (e .. e + 3 with e + half .. e + half + 3) of one
   // head of one token, so every partial read and every q / k store is a 16- or 8-byte access.
   const int half = hd >> 1, q4 = half >> 2;
@@ -137,15 +146,25 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
                                     void* q_out, const int* positions, int mode,
                                     const int* block_table, int max_pages, int ps, int n_pages,
                                     int pos_limit, void* kp, void* vp, const float* rope,
-                                    hipStream_t st) {
+                                    hipStream_t st, const RopeRanks* rr) {
   if (hd % 8) return hipErrorInvalidValue;
   const int64_t total = (int64_t)T * (hq + 2 * hk) * (hd / 8);
   if (total == 0) return hipSuccess;
-  dim3 g((unsigned)((total + 255) / 256)), b(256);
+  const RopeRanks one{};
+  const RopeRanks& rk = rr ? *rr : one;
+  if (rr && (rr->n < 1 || rr->n > kMaxRanks)) return hipErrorInvalidValue;
+  if (rr) {
+    parts = rr->parts[0];
+    q_out = rr->q_out[0];
+    kp = rr->k_pages[0];
+    vp = rr->v_pages[0];
+    n_pages = rr->n_pages[0];
+  }
+  dim3 g((unsigned)((total + 255) / 256), rr && rr->n > 1 ? rr->n : 1), b(256);
 #define TPK_RAP(NPV)                                                                            \
   hipLaunchKernelGGL(k_rope_append_parts<NPV>, g, b, 0, st, parts, T, hq, hk, hd,               \
                      (uint16_t*)q_out, positions, mode, block_table, max_pages, ps, n_pages,    \
-                     pos_limit, (uint16_t*)kp, (uint16_t*)vp, (const float2*)rope)
+                     pos_limit, (uint16_t*)kp, (uint16_t*)vp, (const float2*)rope, rk)
   switch (np) {
     case 1: TPK_RAP(1); break;
     case 2: TPK_RAP(2); break;

@@ -414,7 +414,14 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_dma(const uint16_t* __restr
                                                          const uint16_t* __restrict__ B,
                                                          const uint16_t* __restrict__ B2, int M,
                                                          int N, int K, int kchunk,
-                                                         float* __restrict__ part) {
+                                                         float* __restrict__ part, GemmRanks gr) {
+  if (gr.n > 1) {  // every rank in one launch (blockIdx.z = rank)
+    const int r = blockIdx.z;
+    A = (const uint16_t*)gr.a[r];
+    B = (const uint16_t*)gr.b[r];
+    B2 = (const uint16_t*)gr.b2[r];
+    part = (float*)gr.c[r];
+  }
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int AR = MT * 16;                       // activation rows staged
   constexpr int BR = 64 * NB;                       // weight rows staged
@@ -618,15 +625,15 @@ size_t splitk_workspace_bytes(int M, int N, int K, bool dual) {
   return (size_t)S * M * (dual ? 2 * N : N) * sizeof(float);
 }
 
-hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
+static hipError_t splitk_impl(int epi, int actf, int M, int N, int K, const void* A,
                               const void* B, const void* B2, void* C, int ldc, float* part,
-                              hipStream_t st, int* parts_only) {
+                              hipStream_t st, int* parts_only, const GemmRanks& gr) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M > 64) return hipErrorInvalidValue;
   const bool dual = (epi == EPI_GATED);
   int S, kc;
   splitk_plan(N, K, dual, &S, &kc);
-  dim3 g((N + 63) / 64, S), blk(256);
+  dim3 g((N + 63) / 64, S, gr.n > 1 ? gr.n : 1), blk(256);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   const int mt = (M + 15) / 16;
   if (K % SD_BK == 0) {
@@ -636,7 +643,7 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
     constexpr size_t lds = (size_t)SD_ST * (MTV * 16 + 64 * (DV ? 2 : 1)) * SD_BK * 2;          \
     hipError_t ea = allow_lds((const void*)k_gemm_splitk_dma<MTV, DV>, (int)lds);                \
     if (ea != hipSuccess) return ea;                                                             \
-    launch((k_gemm_splitk_dma<MTV, DV>), g, blk, lds, st, a, b, b2, M, N, K, kc, part);         \
+    launch((k_gemm_splitk_dma<MTV, DV>), g, blk, lds, st, a, b, b2, M, N, K, kc, part, gr);     \
   } while (0)
 #define TPK_SDM(MTV) \
   if (dual) TPK_SD(MTV, true); else TPK_SD(MTV, false)
@@ -667,6 +674,22 @@ hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void
     return hipSuccess;
   }
   return launch_splitk_epilogue(epi, actf, part, S, M, N, C, ldc, st);
+}
+
+hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
+                              const void* B, const void* B2, void* C, int ldc, float* part,
+                              hipStream_t st, int* parts_only) {
+  return splitk_impl(epi, actf, M, N, K, A, B, B2, C, ldc, part, st, parts_only, GemmRanks{});
+}
+
+hipError_t launch_gemm_splitk_ranks(int epi, int M, int N, int K, const GemmRanks& gr,
+                                    hipStream_t st, int* parts) {
+  if (gr.n < 1 || gr.n > kMaxRanks || K % SD_BK != 0 || !parts) return hipErrorInvalidValue;
+  for (int r = 0; r < gr.n; ++r)
+    if (!gr.a[r] || !gr.b[r] || !gr.c[r] || (epi == EPI_GATED && !gr.b2[r]))
+      return hipErrorInvalidValue;
+  return splitk_impl(epi, 0, M, N, K, gr.a[0], gr.b[0], gr.b2[0], nullptr, 0, (float*)gr.c[0],
+                     st, parts, gr);
 }
 
 // Prefill GEMM with a three-stage LDS ring filled by direct-to-LDS loads (global_load_lds_dwordx4,

@@ -24,7 +24,8 @@ template <int MT, int EPI, int ACTF, int BK, int RS>
 __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ A,
                                                    const uint16_t* __restrict__ B,
                                                    const uint16_t* __restrict__ B2, int M, int N,
-                                                   int K, void* __restrict__ C, int ldc) {
+                                                   int K, void* __restrict__ C, int ldc,
+                                                   GemmRanks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
   constexpr int NB = DUAL ? 2 : 1;
   constexpr int AR = MT * 16, BR = 16 * NB;  // staged activation and weight rows
@@ -39,6 +40,13 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
   static_assert((RS - 2) * LPW <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
+  if (gr.n > 1) {  // every rank in one launch (blockIdx.z = rank)
+    const int r = blockIdx.z;
+    A = (const uint16_t*)gr.a[r];
+    B = (const uint16_t*)gr.b[r];
+    B2 = (const uint16_t*)gr.b2[r];
+    C = gr.c[r];
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 16;
@@ -138,7 +146,7 @@ constexpr int band_slots() {
 
 template <int MT, int EPI, int ACTF>
 hipError_t band_launch(int M, int N, int K, const uint16_t* a, const uint16_t* b,
-                       const uint16_t* b2, void* C, int ldc, hipStream_t st) {
+                       const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr) {
   constexpr bool DUAL = EPI == EPI_GATED;
   constexpr int BK = BD_BK;
   constexpr int RS = band_slots<MT, DUAL>();
@@ -147,20 +155,21 @@ hipError_t band_launch(int M, int N, int K, const uint16_t* a, const uint16_t* b
   auto kern = k_gemm_band<MT, EPI, ACTF, BK, RS>;
   hipError_t e = allow_lds((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
-  launch(kern, dim3((N + 15) / 16), dim3(256), lds, st, a, b, b2, M, N, K, C, ldc);
+  launch(kern, dim3((N + 15) / 16, 1, gr.n > 1 ? gr.n : 1), dim3(256), lds, st, a, b, b2, M, N, K,
+         C, ldc, gr);
   return hipGetLastError();
 }
 
 template <int MT>
 hipError_t band_mt(int epi, int actf, int M, int N, int K, const uint16_t* a, const uint16_t* b,
-                   const uint16_t* b2, void* C, int ldc, hipStream_t st) {
+                   const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr) {
   switch (epi) {
-    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st);
-    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st);
-    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st);
+    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
+    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
+    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
     case EPI_GATED:
-      return actf == 0 ? band_launch<MT, EPI_GATED, 0>(M, N, K, a, b, b2, C, ldc, st)
-                       : band_launch<MT, EPI_GATED, 1>(M, N, K, a, b, b2, C, ldc, st);
+      return actf == 0 ? band_launch<MT, EPI_GATED, 0>(M, N, K, a, b, b2, C, ldc, st, gr)
+                       : band_launch<MT, EPI_GATED, 1>(M, N, K, a, b, b2, C, ldc, st, gr);
     default: return hipErrorInvalidValue;
   }
 }
@@ -173,15 +182,28 @@ bool gemm_band_supported(int epi, int M, int N, int K) {
 }
 
 hipError_t launch_gemm_band(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                            const void* B2, void* C, int ldc, hipStream_t st) {
+                            const void* B2, void* C, int ldc, hipStream_t st,
+                            const GemmRanks* gr) {
   if (M == 0 || N == 0) return hipSuccess;
   if (!gemm_band_supported(epi, M, N, K)) return hipErrorInvalidValue;
+  const GemmRanks one{};
+  if (gr) {
+    if (gr->n < 1 || gr->n > kMaxRanks) return hipErrorInvalidValue;
+    for (int r = 0; r < gr->n; ++r)
+      if (!gr->a[r] || !gr->b[r] || !gr->c[r] || (epi == EPI_GATED && !gr->b2[r]))
+        return hipErrorInvalidValue;
+    A = gr->a[0];
+    B = gr->b[0];
+    B2 = gr->b2[0];
+    C = gr->c[0];
+  }
+  const GemmRanks& g = gr ? *gr : one;
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   switch ((M + 15) / 16) {
-    case 1: return band_mt<1>(epi, actf, M, N, K, a, b, b2, C, ldc, st);
-    case 2: return band_mt<2>(epi, actf, M, N, K, a, b, b2, C, ldc, st);
-    case 3: return band_mt<3>(epi, actf, M, N, K, a, b, b2, C, ldc, st);
-    default: return band_mt<4>(epi, actf, M, N, K, a, b, b2, C, ldc, st);
+    case 1: return band_mt<1>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
+    case 2: return band_mt<2>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
+    case 3: return band_mt<3>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
+    default: return band_mt<4>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
   }
 }
 

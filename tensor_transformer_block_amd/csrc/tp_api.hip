@@ -321,9 +321,27 @@ bool ranks_step_ok(const Dims& x, int T) {
          tpk::gemv_ranks_fit(wt, tpk::EPI_RED_ALL, x.N, T, x.fr);
 }
 
+// Batched decode (5 to 64 tokens, bf16) whose projections all take the split-K QKV and the band
+// GEMMs: the staged sequence with each projection, the rotary / KV append and the attention as
+// one launch for all ranks (the reduces are one launch for all ranks already).
+bool ranks_staged_ok(const Dims& x, const tp_batch& b) {
+  const int T = b.n_tokens;
+  if (x.N < 2 || x.N > tpk::kMaxRanks || T < 1 || T > 64 || b.mode != TP_MODE_DECODE) return false;
+  if (x.wt != TP_DTYPE_BF16 || x.at != TP_DTYPE_BF16) return false;
+  if (!use_gemm(x, T, x.d) || !use_gemm(x, T, x.qdim) || !use_gemm(x, T, x.fr)) return false;
+  if (x.d % 64 != 0) return false;  // the direct-to-LDS split-K QKV
+  return tpk::gemm_band_supported(tpk::EPI_F32, T, x.d, x.qdim) &&
+         tpk::gemm_band_supported(tpk::EPI_GATED, T, x.fr, x.d) &&
+         tpk::gemm_band_supported(tpk::EPI_F32, T, x.d, x.fr);
+}
+
+bool all_ranks_ok(const Dims& x, const tp_batch& b) {
+  return ranks_step_ok(x, b.n_tokens) || ranks_staged_ok(x, b);
+}
+
 uint64_t step_ws_bytes(const Dims& x, const tp_batch& b) {
   const uint64_t one = ws_layout(x, b).total;
-  return ranks_step_ok(x, b.n_tokens) ? (uint64_t)x.N * align_up(one) : one;
+  return all_ranks_ok(x, b) ? (uint64_t)x.N * align_up(one) : one;
 }
 
 }  // namespace
@@ -859,8 +877,9 @@ tp_status tp_step_schedule(const tp_block_desc* desc, const tp_batch* batch, int
   if (tp_status s = check_batch(x, batch, false)) return s;
   if (!schedule) return fail(TP_ERR_INVALID_ARG, "schedule is NULL");
   const int T = batch->n_tokens;
-  *schedule = ranks_step_ok(x, T) ? TP_SCHEDULE_ALL_RANKS
-                                  : (fused_step_ok(x, T) ? TP_SCHEDULE_PER_RANK : TP_SCHEDULE_STAGED);
+  *schedule = all_ranks_ok(x, *batch) ? TP_SCHEDULE_ALL_RANKS
+                                      : (fused_step_ok(x, T) ? TP_SCHEDULE_PER_RANK
+                                                             : TP_SCHEDULE_STAGED);
   return TP_OK;
 }
 
@@ -1328,6 +1347,121 @@ static tp_status ffn_halves_ranks(const tp_block_desc* desc, const Dims& x,
   return TP_OK;
 }
 
+// The batched-decode block step with one launch per stage for all ranks (ranks_staged_ok):
+// xn = norm(x); every rank's split-K QKV, then its sum + rotary + KV append; every rank's
+// attention and split merge; every rank's o_proj partial; h1, xn2 = reduce; every rank's gate/up;
+// every rank's down partial; out = reduce. Each rank's work is exactly that of its own launches.
+static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const void* const* shards,
+                              const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                              const void* gamma1, const void* gamma2, void* partials, void* xn,
+                              void* h1, void* xn2, void* out, void* workspace,
+                              uint64_t workspace_bytes, void* stream, hipEvent_t evb,
+                              hipEvent_t eve) {
+  const int T = batch->n_tokens, N = x.N;
+  const WsLayout w = ws_layout(x, *batch);
+  const uint64_t wstride = align_up(w.total);
+  if (workspace_bytes < (uint64_t)N * wstride)
+    return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu (one copy per rank)",
+                (unsigned long long)workspace_bytes, (unsigned long long)N * wstride);
+  if (!aligned16(workspace)) return fail(TP_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  for (int r = 0; r < N; ++r) {
+    if (!shards[r] || !aligned16(shards[r]))
+      return fail(TP_ERR_INVALID_ARG, "shard %d is NULL or not 16-byte aligned", r);
+    if (!kv[r].k_pages || !kv[r].v_pages || kv[r].n_pages <= 0)
+      return fail(TP_ERR_INVALID_ARG, "ATTN needs a KV cache with non-NULL pages and n_pages > 0");
+    if (!aligned16(kv[r].k_pages) || !aligned16(kv[r].v_pages))
+      return fail(TP_ERR_INVALID_ARG, "KV pages must be 16-byte aligned");
+  }
+  if (w.gemm_bytes == 0) return fail(TP_ERR_UNSUPPORTED, "no split-K workspace for this batch");
+  tp_shard_layout L;
+  make_layout(x, &L);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t pstride = (size_t)T * x.d, pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
+  const int epi_part = x.pt == TP_DTYPE_F32 ? tpk::EPI_F32 : tpk::EPI_BF16;
+  auto wsr = [&](int r) { return (char*)workspace + (size_t)r * wstride; };
+  auto shard = [&](int r) { return (const char*)shards[r]; };
+  auto part = [&](int r) { return (void*)((char*)partials + (size_t)r * pstride * pbytes); };
+
+  if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
+    return s;
+  tpk::GemmRanks gq{};
+  gq.n = N;
+  for (int r = 0; r < N; ++r) {
+    gq.a[r] = xn;
+    gq.b[r] = shard(r) + L.qkv.offset;
+    gq.c[r] = wsr(r) + w.gemm;
+  }
+  int S = 0;
+  hipError_t e = tpk::launch_gemm_splitk_ranks(tpk::EPI_ACT, T, x.qkv_rows, x.d, gq, st, &S);
+  if (e != hipSuccess) return hip_fail(e, "qkv projection (all ranks)");
+  tpk::RopeRanks rr{};
+  rr.n = N;
+  for (int r = 0; r < N; ++r) {
+    rr.parts[r] = (const float*)(wsr(r) + w.gemm);
+    rr.q_out[r] = wsr(r) + w.q;
+    rr.k_pages[r] = kv[r].k_pages;
+    rr.v_pages[r] = kv[r].v_pages;
+    rr.n_pages[r] = kv[r].n_pages;
+  }
+  e = tpk::launch_rope_append_parts(rr.parts[0], S, T, x.hq, x.hk, x.hd, rr.q_out[0],
+                                    batch->positions, batch->mode, batch->block_table,
+                                    batch->max_pages, x.ps, rr.n_pages[0], w.pos_limit,
+                                    rr.k_pages[0], rr.v_pages[0], batch->rope_table, st, &rr);
+  if (e != hipSuccess) return hip_fail(e, "rotary embedding / KV append (all ranks)");
+  tpk::AttnRanks ar{};
+  ar.n = N;
+  for (int r = 0; r < N; ++r) {
+    ar.q[r] = wsr(r) + w.q;
+    ar.k_pages[r] = kv[r].k_pages;
+    ar.v_pages[r] = kv[r].v_pages;
+    ar.n_pages[r] = kv[r].n_pages;
+    ar.part_o[r] = (float*)(wsr(r) + w.part_o);
+    ar.part_ml[r] = (float*)(wsr(r) + w.part_ml);
+    ar.out[r] = wsr(r) + w.attn;
+  }
+  e = tpk::launch_attn_decode_ranks(tpk::ACT_BF16, x.hd, x.Hq / x.Hkv, T, x.hk, ar,
+                                    batch->positions, batch->block_table, batch->max_pages, x.ps,
+                                    w.chunk, w.n_split, w.pos_limit, st);
+  if (e != hipSuccess) return hip_fail(e, "attention (all ranks)");
+  tpk::GemmRanks go{};
+  go.n = N;
+  for (int r = 0; r < N; ++r) {
+    go.a[r] = wsr(r) + w.attn;
+    go.b[r] = shard(r) + L.o.offset;
+    go.c[r] = part(r);
+  }
+  e = tpk::launch_gemm_band(epi_part, 0, T, x.d, x.qdim, nullptr, nullptr, nullptr, nullptr, x.d,
+                            st, &go);
+  if (e != hipSuccess) return hip_fail(e, "o projection (all ranks)");
+  if (tp_status s = tp_partial_reduce(desc, T, partials, N, x_in, h1, gamma2, xn2, stream))
+    return s;
+  tpk::GemmRanks gg{};
+  gg.n = N;
+  for (int r = 0; r < N; ++r) {
+    gg.a[r] = xn2;
+    gg.b[r] = shard(r) + L.gate_up.offset;
+    gg.b2[r] = shard(r) + L.gate_up.offset + (size_t)x.fr * x.d * 2;
+    gg.c[r] = wsr(r) + w.ffn;
+  }
+  {
+    TimedScope ts(evb, eve);
+    e = tpk::launch_gemm_band(tpk::EPI_GATED, x.actf, T, x.fr, x.d, nullptr, nullptr, nullptr,
+                              nullptr, x.fr, st, &gg);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gate/up projection (all ranks)");
+  tpk::GemmRanks gd{};
+  gd.n = N;
+  for (int r = 0; r < N; ++r) {
+    gd.a[r] = wsr(r) + w.ffn;
+    gd.b[r] = shard(r) + L.down.offset;
+    gd.c[r] = part(r);
+  }
+  e = tpk::launch_gemm_band(epi_part, 0, T, x.d, x.fr, nullptr, nullptr, nullptr, nullptr, x.d, st,
+                            &gd);
+  if (e != hipSuccess) return hip_fail(e, "down projection (all ranks)");
+  return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
+}
+
 static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
                            const void* gamma1, const void* gamma2, void* partials, void* xn,
@@ -1340,12 +1474,12 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
   const int T = batch->n_tokens, N = x.N;
   if (schedule < -1 || schedule > TP_SCHEDULE_ALL_RANKS)
     return fail(TP_ERR_INVALID_ARG, "unknown schedule %d", schedule);
-  const int best = ranks_step_ok(x, T) ? TP_SCHEDULE_ALL_RANKS
-                                       : (fused_step_ok(x, T) ? TP_SCHEDULE_PER_RANK
-                                                              : TP_SCHEDULE_STAGED);
-  if (schedule > best)
-    return fail(TP_ERR_UNSUPPORTED, "schedule %d is not available for this batch (at most %d)",
-                schedule, best);
+  const bool can_fuse = fused_step_ok(x, T), can_all = all_ranks_ok(x, *batch);
+  const int best = can_all ? TP_SCHEDULE_ALL_RANKS
+                           : (can_fuse ? TP_SCHEDULE_PER_RANK : TP_SCHEDULE_STAGED);
+  if ((schedule == TP_SCHEDULE_PER_RANK && !can_fuse) ||
+      (schedule == TP_SCHEDULE_ALL_RANKS && !can_all))
+    return fail(TP_ERR_UNSUPPORTED, "schedule %d is not available for this batch", schedule);
   const int sched = schedule < 0 ? best : schedule;
   if (T == 0) {
     g_err.clear();
@@ -1365,6 +1499,15 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
   auto timing = [&](int r) -> std::pair<hipEvent_t, hipEvent_t> {
     return r == timed_rank ? std::make_pair(evb, eve) : std::make_pair(hipEvent_t{}, hipEvent_t{});
   };
+  if (sched == TP_SCHEDULE_ALL_RANKS && !can_fuse) {
+    const bool timed = timed_rank >= 0 && timed_rank < N;
+    if (tp_status s = staged_ranks(desc, x, shards, batch, kv, x_in, gamma1, gamma2, partials, xn,
+                                   h1, xn2, out, workspace, workspace_bytes, stream,
+                                   timed ? evb : nullptr, timed ? eve : nullptr))
+      return s;
+    g_err.clear();
+    return TP_OK;
+  }
   if (sched == TP_SCHEDULE_STAGED) {
     // The staged sequence of the same library calls.
     if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))

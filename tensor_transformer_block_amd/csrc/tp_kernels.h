@@ -85,6 +85,26 @@ struct RankPtrs {
   int n_pages[kMaxRanks];
 };
 
+// Per-rank operands of a matrix-core GEMM launch over all ranks (grid.z = rank): activations a,
+// weights b (gated: b2 the up rows), output c. n = 0: a single rank's launch.
+struct GemmRanks {
+  int n;
+  const void* a[kMaxRanks];
+  const void* b[kMaxRanks];
+  const void* b2[kMaxRanks];
+  void* c[kMaxRanks];
+};
+
+// Per-rank buffers of the rotary / KV-append kernel over all ranks (grid.y = rank).
+struct RopeRanks {
+  int n;
+  const float* parts[kMaxRanks];
+  void* q_out[kMaxRanks];
+  void* k_pages[kMaxRanks];
+  void* v_pages[kMaxRanks];
+  int n_pages[kMaxRanks];
+};
+
 // Per-rank pointers of a decode attention launch over all ranks (blockIdx.y = rank * hk + kv
 // head); n = 0: a single rank's launch (the plain pointer arguments).
 struct AttnRanks {
@@ -162,13 +182,18 @@ hipError_t launch_gemm_q8(int epi, int actf, int M, int N, int K, const void* A,
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,
                               const void* B, const void* B2, void* C, int ldc, float* part,
                               hipStream_t st, int* parts_only = nullptr);
+// The direct-to-LDS split-K GEMM of every rank in one launch, partial tiles only (K % 64 == 0):
+// rank r reads gr.a[r], gr.b[r] (gr.b2[r]) and writes its S tiles to (float*)gr.c[r]; returns S.
+hipError_t launch_gemm_splitk_ranks(int epi, int M, int N, int K, const GemmRanks& gr,
+                                    hipStream_t st, int* parts);
 hipError_t launch_gemm_bf16(int epi, int actf, int M, int N, int K, const void* A, const void* B,
                             const void* B2, void* C, int ldc, hipStream_t st);
 // k_gemm_band.hip: M <= 64 tokens, a 16-column band of the output per workgroup over the whole
 // K (no split, epilogue in the kernel); K % 128 == 0 and at least 192 bands.
 bool gemm_band_supported(int epi, int M, int N, int K);
 hipError_t launch_gemm_band(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                            const void* B2, void* C, int ldc, hipStream_t st);
+                            const void* B2, void* C, int ldc, hipStream_t st,
+                            const GemmRanks* gr = nullptr);
 // The bf16 QKV projection of M tokens with the rotary embedding and the KV append in its epilogue
 // (the 128 or 256-row direct-to-LDS tiles; q goes to re.q_out, k and v into the pages). Supported
 // when N % 128 == 0, hd is 64 or 128, K % 64 == 0, M >= 128 and the shape is not one for the
@@ -196,7 +221,7 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
                                     void* q_out, const int* positions, int mode,
                                     const int* block_table, int max_pages, int ps, int n_pages,
                                     int pos_limit, void* kp, void* vp, const float* rope,
-                                    hipStream_t st);
+                                    hipStream_t st, const RopeRanks* rr = nullptr);
 hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, int hd, void* q_out,
                               const int* positions, int mode, const int* block_table,
                               int max_pages, int ps, int n_pages, int pos_limit, void* kp,

@@ -77,6 +77,13 @@ SHAPES = [
                head_dim=128, ffn_dim=6416, tp=2, w_dtype="bf16", act_dtype="bf16",
                ffn_act="silu", mode="decode", kv_lens=(5, 77, 1, 40, 23, 9, 60, 2, 31),
                n_tokens=9),
+    # Batched decode whose every projection takes the split-K QKV or a band GEMM, so the block
+    # step runs each stage as one launch for both ranks.
+    BlockShape(name="med-bf16-band-all", index=228, d_model=3072, n_heads=8, n_kv_heads=2,
+               head_dim=128, ffn_dim=6400, tp=2, w_dtype="bf16", act_dtype="bf16",
+               ffn_act="silu", mode="decode",
+               kv_lens=tuple(int(v) for v in np.random.default_rng(11).integers(1, 120, 21)),
+               n_tokens=21),
     BlockShape(name="med-fp32-g2", index=206, d_model=384, n_heads=4, n_kv_heads=2, head_dim=128,
                ffn_dim=688, tp=2, w_dtype="f32", act_dtype="f32", ffn_act="silu", mode="decode",
                kv_lens=(50, 3), n_tokens=2),
@@ -178,15 +185,17 @@ def test_step_matches_staged_and_graph_replay():
 
 
 # The one-call step: decode shapes take the fused schedule (norms in the QKV and gate/up
-# projections, reduces in the last rank's o_proj and down); the batched and prefill shapes take the
-# staged sequence of the same calls.
+# projections, reduces in the last rank's o_proj and down, at most four ranks: one launch per
+# projection for all ranks); the batched and prefill shapes take the staged sequence of the same
+# calls, batched ones on the split-K and band GEMMs as one launch per stage for all ranks.
 FUSED_STEP = ["med-bf16-ragged", "med-bf16-single-key", "med-q8-n4", "med-q8-hd256",
               "med-fp32-g2", "med-bf16-g8", "med-bf16-long-kv", "med-bf16-batched-64",
-              "med-bf16-prefill"]
+              "med-bf16-prefill", "med-bf16-band-all"]
 
 
 ONE_CALL = ([(n, p) for n in FUSED_STEP for p in ("f32", "bf16")]
-            + [(n, "f32") for n in ("tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode")])
+            + [(n, "f32") for n in ("tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode",
+                                    "llama3-8b-batched")])
 
 
 @pytest.mark.parametrize("name,partial_dtype", ONE_CALL, ids=lambda v: str(v))
@@ -231,7 +240,9 @@ def test_one_call_step(name, partial_dtype):
                                 nrel(got[f"k{rk}"], staged[f"k{rk}"]))
         errs[f"v_new r{rk}"] = (nrel(got[f"v{rk}"], ref["ranks"][rk]["v_new"]),
                                 nrel(got[f"v{rk}"], staged[f"v{rk}"]))
-    log(f"one-call step {name} ({partial_dtype} partials, {'fused' if fused else 'staged'}): "
+    sched = {0: "staged", 1: "per rank", 2: "all ranks"}[blk.schedule()]
+    log(f"one-call step {name} ({partial_dtype} partials, {'fused' if fused else 'staged'}, "
+        f"{sched}): "
         + ", ".join(f"{k} {a:.1e}/{b:.1e}" for k, (a, b) in errs.items()))
     for k, (a, b) in errs.items():
         assert a <= tol, (k, a)
@@ -239,9 +250,10 @@ def test_one_call_step(name, partial_dtype):
         if not fused:
             assert b == 0.0, (k, b)
     # The all-ranks schedule (one launch per projection for every rank) against the per-rank
-    # fused schedule: the same bits everywhere, partials and new cache entries included.
+    # fused schedule: the same bits everywhere, partials and new cache entries included. (For
+    # batched shapes the all-ranks schedule is the staged sequence's, compared above: b == 0.)
     from tensor_transformer_block_amd import binding as B
-    if blk.schedule() == B.TP_SCHEDULE_ALL_RANKS:
+    if blk.schedule() == B.TP_SCHEDULE_ALL_RANKS and fused:
         def bits(t):
             return t.contiguous().view(torch.uint8).cpu()
         outs = ("xn", "h1", "xn2", "out", "partials")
