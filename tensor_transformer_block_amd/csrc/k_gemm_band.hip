@@ -20,7 +20,7 @@
 
 namespace tpk {
 
-template <int MT, int EPI, int ACTF, int BK, int RS>
+template <int MT, int EPI, int ACTF, int BK, int RS, int NRK>
 __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ A,
                                                    const uint16_t* __restrict__ B,
                                                    const uint16_t* __restrict__ B2, int M, int N,
@@ -28,25 +28,28 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
                                                    GemmRanks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int AR = MT * 16, BR = 16 * NB;  // staged activation and weight rows
+  constexpr int AR = MT * 16, BR = 16 * NB;  // staged activation rows, weight rows per rank
+  constexpr int BRA = NRK * BR;              // weight rows of the NRK ranks sharing A
   constexpr int CPR = BK / 8;                // 16-byte chunks per staged row
   constexpr int RPL = 64 / CPR;              // rows per wave-load
   constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
-  constexpr int STAGE = (AR + BR) * BK;      // bf16 elements per ring slot
-  constexpr int A_WL = AR / RPL, B_WL = BR / RPL;
+  constexpr int STAGE = (AR + BRA) * BK;     // bf16 elements per ring slot
+  constexpr int A_WL = AR / RPL, B_WL = BRA / RPL;
   constexpr int A_PW = (A_WL + 3) / 4, B_PW = (B_WL + 3) / 4;  // per wave; surplus ones repeat
   constexpr int LPW = A_PW + B_PW;
   static_assert(BK % 32 == 0 && 64 % CPR == 0 && AR % RPL == 0 && BR % RPL == 0, "stage shape");
   static_assert((RS - 2) * LPW <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  if (gr.n > 1) {  // every rank in one launch (blockIdx.z = rank)
-    const int r = blockIdx.z;
-    A = (const uint16_t*)gr.a[r];
-    B = (const uint16_t*)gr.b[r];
-    B2 = (const uint16_t*)gr.b2[r];
-    C = gr.c[r];
-  }
+  // Every rank in one launch: blockIdx.z picks rank (NRK = 1) or the group of NRK ranks that
+  // share the activations A (column-parallel projections of one input), rank r0 + i's weights
+  // in staged rows [i * BR, (i + 1) * BR).
+  const int r0 = gr.n > 1 ? (int)blockIdx.z * NRK : 0;
+  if (gr.n > 1) A = (const uint16_t*)gr.a[r0];
+  auto wsrc = [&](int i, bool up) -> const uint16_t* {
+    if (gr.n > 1) return (const uint16_t*)(up ? gr.b2[r0 + i] : gr.b[r0 + i]);
+    return up ? B2 : B;
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 16;
@@ -70,18 +73,21 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < B_PW; ++i) {
       const int g = (wave * B_PW + i) % B_WL;
-      const int row = g * RPL + lrow;  // 0 .. BR - 1: gate rows, then (gated) the up rows
-      const uint16_t* base = (DUAL && row >= 16) ? B2 : B;
-      const int col = min(n0 + (row & 15), N - 1);
+      const int row = g * RPL + lrow;  // rank row / BR: gate rows, then (gated) the up rows
+      const int lr = row % BR;
+      const uint16_t* base = wsrc(row / BR, DUAL && lr >= 16);
+      const int col = min(n0 + (lr & 15), N - 1);
       const uint16_t* src = base + (size_t)col * K + kb + ((lpc ^ (row & SWZ)) << 3);
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
                                        (lds_void_t*)(st + (AR + g * RPL) * BK), 16, 0, 0);
     }
   };
 
-  floatx4 acc[NB];
+  floatx4 acc[NRK][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NRK; ++i)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[i][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fq = lane >> 4;
   const bool mma_wave = MT == 4 || wave < MT;  // wave-uniform
 
@@ -101,10 +107,12 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
         const int sw = ((kk * 4 + fq) ^ (fr & SWZ)) << 3;
         const bf16x8 af = *(const bf16x8*)(a_s + sw);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x8 bf = *(const bf16x8*)(b_s + b * 16 * BK + sw);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[b], 0, 0, 0);
-        }
+        for (int i = 0; i < NRK; ++i)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const bf16x8 bf = *(const bf16x8*)(b_s + (i * BR + b * 16) * BK + sw);
+            acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i][b], 0, 0, 0);
+          }
       }
     }
   }
@@ -113,16 +121,20 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
   const int col = n0 + fr;
   if (!mma_wave || col >= N) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 16 + fq * 4 + r;
-    if (row >= M) continue;
-    const size_t o = (size_t)row * ldc + col;
-    if constexpr (EPI == EPI_GATED) {
-      ((uint16_t*)C)[o] = f32_to_bf16(gated<ACTF>(acc[0][r], acc[NB - 1][r]));
-    } else if constexpr (EPI == EPI_F32) {
-      ((float*)C)[o] = acc[0][r];
-    } else {
-      ((uint16_t*)C)[o] = f32_to_bf16(acc[0][r]);
+  for (int i = 0; i < NRK; ++i) {
+    void* Ci = gr.n > 1 ? gr.c[r0 + i] : C;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wave * 16 + fq * 4 + r;
+      if (row >= M) continue;
+      const size_t o = (size_t)row * ldc + col;
+      if constexpr (EPI == EPI_GATED) {
+        ((uint16_t*)Ci)[o] = f32_to_bf16(gated<ACTF>(acc[i][0][r], acc[i][NB - 1][r]));
+      } else if constexpr (EPI == EPI_F32) {
+        ((float*)Ci)[o] = acc[i][0][r];
+      } else {
+        ((uint16_t*)Ci)[o] = f32_to_bf16(acc[i][0][r]);
+      }
     }
   }
 }
@@ -133,43 +145,56 @@ namespace {
 // 160 KB of LDS and the wait counter's range. (512-byte segments, or non-temporal weight loads,
 // measured no faster inside the block step.)
 constexpr int BD_BK = 128;
-template <int MT, bool DUAL>
+template <int MT, bool DUAL, int BK, int NRK>
 constexpr int band_slots() {
-  constexpr int stage = (MT * 16 + 16 * (DUAL ? 2 : 1)) * BD_BK * 2;
-  constexpr int rpl = 64 / (BD_BK / 8);
-  constexpr int lpw = (MT * 16 / rpl + 3) / 4 + (16 * (DUAL ? 2 : 1) / rpl + 3) / 4;
+  constexpr int stage = (MT * 16 + NRK * 16 * (DUAL ? 2 : 1)) * BK * 2;
+  constexpr int rpl = 64 / (BK / 8);
+  constexpr int lpw = (MT * 16 / rpl + 3) / 4 + (NRK * 16 * (DUAL ? 2 : 1) / rpl + 3) / 4;
   constexpr int s = (160 * 1024) / stage;
   constexpr int smax = 63 / lpw + 2;
   constexpr int r = s < smax ? s : smax;
   return r > 8 ? 8 : r;
 }
 
-template <int MT, int EPI, int ACTF>
-hipError_t band_launch(int M, int N, int K, const uint16_t* a, const uint16_t* b,
-                       const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr) {
+template <int MT, int EPI, int ACTF, int NRK>
+hipError_t band_launch_n(int M, int N, int K, const uint16_t* a, const uint16_t* b,
+                         const uint16_t* b2, void* C, int ldc, hipStream_t st,
+                         const GemmRanks& gr) {
   constexpr bool DUAL = EPI == EPI_GATED;
-  constexpr int BK = BD_BK;
-  constexpr int RS = band_slots<MT, DUAL>();
-  constexpr size_t lds = (size_t)RS * (MT * 16 + 16 * (DUAL ? 2 : 1)) * BK * 2;
+  // Groups of ranks sharing A stage more weight rows per slot: 128-byte row segments keep the
+  // ring deep enough there.
+  constexpr int BK = NRK > 1 ? 64 : BD_BK;
+  constexpr int RS = band_slots<MT, DUAL, BK, NRK>();
+  constexpr size_t lds = (size_t)RS * (MT * 16 + NRK * 16 * (DUAL ? 2 : 1)) * BK * 2;
   if (K % BK != 0) return hipErrorInvalidValue;
-  auto kern = k_gemm_band<MT, EPI, ACTF, BK, RS>;
+  auto kern = k_gemm_band<MT, EPI, ACTF, BK, RS, NRK>;
   hipError_t e = allow_lds((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
-  launch(kern, dim3((N + 15) / 16, 1, gr.n > 1 ? gr.n : 1), dim3(256), lds, st, a, b, b2, M, N, K,
-         C, ldc, gr);
+  const int nz = gr.n > 1 ? gr.n / NRK : 1;
+  launch(kern, dim3((N + 15) / 16, 1, nz), dim3(256), lds, st, a, b, b2, M, N, K, C, ldc, gr);
   return hipGetLastError();
+}
+
+template <int MT, int EPI, int ACTF>
+hipError_t band_launch(int M, int N, int K, const uint16_t* a, const uint16_t* b,
+                       const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr,
+                       int share) {
+  if (share == 4) return band_launch_n<MT, EPI, ACTF, 4>(M, N, K, a, b, b2, C, ldc, st, gr);
+  if (share == 2) return band_launch_n<MT, EPI, ACTF, 2>(M, N, K, a, b, b2, C, ldc, st, gr);
+  return band_launch_n<MT, EPI, ACTF, 1>(M, N, K, a, b, b2, C, ldc, st, gr);
 }
 
 template <int MT>
 hipError_t band_mt(int epi, int actf, int M, int N, int K, const uint16_t* a, const uint16_t* b,
-                   const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr) {
+                   const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr,
+                   int share) {
   switch (epi) {
-    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
-    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
-    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st, gr);
+    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
+    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
+    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
     case EPI_GATED:
-      return actf == 0 ? band_launch<MT, EPI_GATED, 0>(M, N, K, a, b, b2, C, ldc, st, gr)
-                       : band_launch<MT, EPI_GATED, 1>(M, N, K, a, b, b2, C, ldc, st, gr);
+      return actf == 0 ? band_launch<MT, EPI_GATED, 0>(M, N, K, a, b, b2, C, ldc, st, gr, share)
+                       : band_launch<MT, EPI_GATED, 1>(M, N, K, a, b, b2, C, ldc, st, gr, share);
     default: return hipErrorInvalidValue;
   }
 }
@@ -198,12 +223,22 @@ hipError_t launch_gemm_band(int epi, int actf, int M, int N, int K, const void* 
     C = gr->c[0];
   }
   const GemmRanks& g = gr ? *gr : one;
+  // Gated projections of one input for several ranks: groups of four (or two) ranks share each
+  // workgroup's activation stages.
+  int share = 1;
+  if (gr && epi == EPI_GATED && gr->n > 1) {
+    const int n = gr->n;
+    share = n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+    for (int r = 1; r < n; ++r)
+      if (gr->a[r] != gr->a[0]) share = 1;
+    if (K % 64 != 0) share = 1;
+  }
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   switch ((M + 15) / 16) {
-    case 1: return band_mt<1>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
-    case 2: return band_mt<2>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
-    case 3: return band_mt<3>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
-    default: return band_mt<4>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g);
+    case 1: return band_mt<1>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g, share);
+    case 2: return band_mt<2>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g, share);
+    case 3: return band_mt<3>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g, share);
+    default: return band_mt<4>(epi, actf, M, N, K, a, b, b2, C, ldc, st, g, share);
   }
 }
 
