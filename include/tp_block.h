@@ -227,9 +227,12 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * of a row-parallel launch computes its rows for rank 0, 1, ... in turn, each rank's sums exactly
  * as in that rank's own launch, then adds the partials in rank order and the residual. The
  * results equal the per-rank schedule's bit for bit. Batched decode (5 to 64 tokens, bf16) whose
- * projections all take the split-K QKV and the band GEMMs also gets TP_SCHEDULE_ALL_RANKS: the
- * separate calls' sequence with each projection, the rotary / KV append and the attention as one
- * launch for all ranks, equal to the separate calls bit for bit. Otherwise (TP_SCHEDULE_STAGED)
+ * projections all take the split-K QKV and the band GEMMs, and bf16 prefill whose QKV takes the
+ * split-K wide tiles and whose other projections take the 256 x 256 wide tiles, also get
+ * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection, the rotary / KV
+ * append and the attention as one launch for all ranks, equal to the separate calls bit for bit
+ * (under one launch the causal prefill's long and short row blocks of all ranks share the chip).
+ * Otherwise (TP_SCHEDULE_STAGED)
  * the call issues exactly the separate calls above. tp_step_schedule reports which schedule a
  * batch gets.
  * shards, kv: host arrays of N entries (rank r's packed shard, device pointer; rank r's cache).

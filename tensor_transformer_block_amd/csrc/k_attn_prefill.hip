@@ -59,7 +59,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpages,
     const uint16_t* __restrict__ vpages, const int* __restrict__ positions,
     const int* __restrict__ block_table, int max_pages, int n_pages, int hk, int T, int pos_limit,
-    uint16_t* __restrict__ out, float scale_log2) {
+    uint16_t* __restrict__ out, float scale_log2, AttnRanks ar) {
   constexpr int KS = HD / 32;               // k-steps over hd in Q K^T
   constexpr int NO = HD / 16;               // hd blocks of O
   constexpr int NHW = G < 4 ? G : 4;        // query heads per workgroup
@@ -73,6 +73,14 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   __shared__ float2 s_ml[AP_KG][2][2][64];  // merge: (m, l) per key group, wave, row block, lane
   __shared__ int s_kmax;
+  if (ar.n > 1) {  // every rank in one launch (blockIdx.z = rank)
+    const int r = blockIdx.z;
+    q = (const uint16_t*)ar.q[r];
+    kpages = (const uint16_t*)ar.k_pages[r];
+    vpages = (const uint16_t*)ar.v_pages[r];
+    n_pages = ar.n_pages[r];
+    out = (uint16_t*)ar.out[r];
+  }
 
   const int g = blockIdx.y / (G / NHW), hgrp = blockIdx.y % (G / NHW);
   const int t0 = (gridDim.x - 1 - blockIdx.x) * (16 * TB);  // latest tokens first
@@ -376,16 +384,17 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
 template <int HD, int G>
 static hipError_t prefill_hg(int T, int hk, hipStream_t st, const void* q, const void* kp,
                              const void* vp, const int* positions, const int* bt, int max_pages,
-                             int n_pages, int pos_limit, void* out, float sl2) {
+                             int n_pages, int pos_limit, void* out, float sl2,
+                             const AttnRanks& ar) {
   constexpr int NHW = G < 4 ? G : 4, TB = 4 / NHW;
   // Two super-tile slots; the merge at the end reuses the same bytes.
   const size_t lds = (size_t)2 * AP_KG * 2 * AP_SUB * HD * sizeof(uint16_t);
   hipError_t e = allow_lds((const void*)k_attn_prefill<HD, G>, (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid((T + 16 * TB - 1) / (16 * TB), hk * (G / NHW));
+  dim3 grid((T + 16 * TB - 1) / (16 * TB), hk * (G / NHW), ar.n > 1 ? ar.n : 1);
   hipLaunchKernelGGL((k_attn_prefill<HD, G>), grid, dim3(512), lds, st, (const uint16_t*)q,
                      (const uint16_t*)kp, (const uint16_t*)vp, positions, bt, max_pages, n_pages,
-                     hk, T, pos_limit, (uint16_t*)out, sl2);
+                     hk, T, pos_limit, (uint16_t*)out, sl2, ar);
   return hipGetLastError();
 }
 
@@ -396,11 +405,24 @@ bool attn_prefill_supported(int hd, int G, int ps) {
 hipError_t launch_attn_prefill(int hd, int G, int T, int hk, const void* q, const void* kp,
                                const void* vp, const int* positions, const int* bt,
                                int max_pages, int n_pages, int pos_limit, void* out,
-                               hipStream_t st) {
+                               hipStream_t st, const AttnRanks* ar) {
   if (T <= 0) return hipSuccess;
+  const AttnRanks one{};
+  if (ar) {
+    if (ar->n < 1 || ar->n > kMaxRanks) return hipErrorInvalidValue;
+    for (int r = 0; r < ar->n; ++r)
+      if (!ar->q[r] || !ar->k_pages[r] || !ar->v_pages[r] || !ar->out[r] || ar->n_pages[r] < 1)
+        return hipErrorInvalidValue;
+    q = ar->q[0];
+    kp = ar->k_pages[0];
+    vp = ar->v_pages[0];
+    n_pages = ar->n_pages[0];
+    out = ar->out[0];
+  }
+  const AttnRanks& arr = ar ? *ar : one;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
 #define TPK_AP(HDV, GV) \
-  return prefill_hg<HDV, GV>(T, hk, st, q, kp, vp, positions, bt, max_pages, n_pages, pos_limit, out, sl2)
+  return prefill_hg<HDV, GV>(T, hk, st, q, kp, vp, positions, bt, max_pages, n_pages, pos_limit, out, sl2, arr)
   if (hd == 128) {
     switch (G) {
       case 1: TPK_AP(128, 1);

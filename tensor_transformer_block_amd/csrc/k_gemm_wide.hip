@@ -37,7 +37,7 @@ template <int EPI, int ACTF, int BR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_wide(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int M, int N, int K, void* __restrict__ C, int ldc,
-    int tiles_m, int tiles_n, int ksplit) {
+    int tiles_m, int tiles_n, int ksplit, GemmRanks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
   constexpr int NBR = wd_brows(EPI, BR);      // staged B rows
   constexpr int NW = wd_ncols(EPI, BR);       // output columns per tile
@@ -47,6 +47,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NGB = NBR / 8;                // 8-row groups of B per slot
   constexpr int LB = (NGB + 7) / 8;           // B wave-loads per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  if (gr.n > 1) {  // every rank in one launch (blockIdx.z = rank)
+    const int r = blockIdx.z;
+    A = (const uint16_t*)gr.a[r];
+    B = (const uint16_t*)gr.b[r];
+    B2 = (const uint16_t*)gr.b2[r];
+    C = gr.c[r];
+  }
 
   int tm, tn, split;
   {
@@ -242,12 +249,30 @@ long gemm_wide_tiles(int epi, int M, int N) {
   return (long)((M + 255) / 256) * ((N + nw - 1) / nw);
 }
 
+static bool ranks_ok(const GemmRanks* gr, bool dual) {
+  if (!gr) return true;
+  if (gr->n < 1 || gr->n > kMaxRanks) return false;
+  for (int r = 0; r < gr->n; ++r)
+    if (!gr->a[r] || !gr->b[r] || !gr->c[r] || (dual && !gr->b2[r])) return false;
+  return true;
+}
+
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                          const void* B2, void* C, int ldc, hipStream_t st) {
+                          const void* B2, void* C, int ldc, hipStream_t st,
+                          const GemmRanks* gr) {
   const int nw = wd_ncols(epi);
   if (M < 256 || N < nw || K % WD_BK != 0) return hipErrorInvalidValue;
+  if (!ranks_ok(gr, epi == EPI_GATED)) return hipErrorInvalidValue;
+  const GemmRanks one{};
+  const GemmRanks& grr = gr ? *gr : one;
+  if (gr) {
+    A = gr->a[0];
+    B = gr->b[0];
+    B2 = gr->b2[0];
+    C = gr->c[0];
+  }
   const int tiles_m = (M + 255) / 256, tiles_n = (N + nw - 1) / nw;
-  dim3 g(tiles_m * tiles_n), blk(512);
+  dim3 g(tiles_m * tiles_n, 1, grr.n > 1 ? grr.n : 1), blk(512);
   const size_t lds = (size_t)2 * (256 + wd_brows(epi)) * WD_BK * sizeof(uint16_t);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
 #define TPK_WIDE(E, AF)                                                                           \
@@ -255,7 +280,7 @@ hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* 
     hipError_t ea = allow_lds((const void*)k_gemm_wide<E, AF, 0>, (int)lds);                     \
     if (ea != hipSuccess) return ea;                                                            \
     launch((k_gemm_wide<E, AF, 0>), g, blk, lds, st, a, b, b2, M, N, K, C, ldc, tiles_m,        \
-           tiles_n, 1);                                                                         \
+           tiles_n, 1, grr);                                                                    \
   } while (0)
   switch (epi) {
     case EPI_ACT: TPK_WIDE(EPI_ACT, 0); break;
@@ -286,17 +311,25 @@ int gemm_split_count(int M, int N, int K) {
 }
 
 hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void* B, float* parts,
-                                 int ksplit, hipStream_t st) {
+                                 int ksplit, hipStream_t st, const GemmRanks* gr) {
   constexpr int BR = 160;
   if (M < 256 || N < BR || K % WD_BK != 0 || ksplit < 1 || K / WD_BK < ksplit)
     return hipErrorInvalidValue;
+  if (!ranks_ok(gr, false)) return hipErrorInvalidValue;
+  const GemmRanks one{};
+  const GemmRanks& grr = gr ? *gr : one;
+  if (gr) {
+    A = gr->a[0];
+    B = gr->b[0];
+    parts = (float*)gr->c[0];
+  }
   const int tiles_m = (M + 255) / 256, tiles_n = (N + BR - 1) / BR;
-  dim3 g(tiles_m * tiles_n * ksplit), blk(512);
+  dim3 g(tiles_m * tiles_n * ksplit, 1, grr.n > 1 ? grr.n : 1), blk(512);
   const size_t lds = (size_t)2 * (256 + BR) * WD_BK * sizeof(uint16_t);
   hipError_t ea = allow_lds((const void*)k_gemm_wide<EPI_F32, 0, BR>, (int)lds);
   if (ea != hipSuccess) return ea;
   launch((k_gemm_wide<EPI_F32, 0, BR>), g, blk, lds, st, (const uint16_t*)A, (const uint16_t*)B,
-         (const uint16_t*)nullptr, M, N, K, (void*)parts, N, tiles_m, tiles_n, ksplit);
+         (const uint16_t*)nullptr, M, N, K, (void*)parts, N, tiles_m, tiles_n, ksplit, grr);
   return hipGetLastError();
 }
 

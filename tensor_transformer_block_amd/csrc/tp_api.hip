@@ -335,8 +335,23 @@ bool ranks_staged_ok(const Dims& x, const tp_batch& b) {
          tpk::gemm_band_supported(tpk::EPI_F32, T, x.d, x.fr);
 }
 
+// Prefill (bf16) whose QKV takes the split-K wide tiles and whose o_proj, gate/up and down take
+// the 256 x 256 wide tiles: the staged sequence with one launch per stage for all ranks.
+bool ranks_prefill_ok(const Dims& x, const tp_batch& b) {
+  const int T = b.n_tokens;
+  if (x.N < 2 || x.N > tpk::kMaxRanks || T < 256 || b.mode != TP_MODE_PREFILL) return false;
+  if (x.wt != TP_DTYPE_BF16 || x.at != TP_DTYPE_BF16) return false;
+  if (qkv_ksplit(x, T) <= 1 || !tpk::attn_prefill_supported(x.hd, x.Hq / x.Hkv, x.ps))
+    return false;
+  auto wide = [&](int epi, int n_out, int K) {
+    return K % 64 == 0 && tpk::gemm_wide_tiles(epi, T, n_out) >= 192;
+  };
+  return wide(tpk::EPI_F32, x.d, x.qdim) && wide(tpk::EPI_GATED, x.fr, x.d) &&
+         wide(tpk::EPI_F32, x.d, x.fr);
+}
+
 bool all_ranks_ok(const Dims& x, const tp_batch& b) {
-  return ranks_step_ok(x, b.n_tokens) || ranks_staged_ok(x, b);
+  return ranks_step_ok(x, b.n_tokens) || ranks_staged_ok(x, b) || ranks_prefill_ok(x, b);
 }
 
 uint64_t step_ws_bytes(const Dims& x, const tp_batch& b) {
@@ -1347,10 +1362,11 @@ static tp_status ffn_halves_ranks(const tp_block_desc* desc, const Dims& x,
   return TP_OK;
 }
 
-// The batched-decode block step with one launch per stage for all ranks (ranks_staged_ok):
-// xn = norm(x); every rank's split-K QKV, then its sum + rotary + KV append; every rank's
-// attention and split merge; every rank's o_proj partial; h1, xn2 = reduce; every rank's gate/up;
-// every rank's down partial; out = reduce. Each rank's work is exactly that of its own launches.
+// The batched-decode or prefill block step with one launch per stage for all ranks
+// (ranks_staged_ok, ranks_prefill_ok): xn = norm(x); every rank's split-K QKV, then its sum +
+// rotary + KV append; every rank's attention (decode: and split merge); every rank's o_proj
+// partial; h1, xn2 = reduce; every rank's gate/up; every rank's down partial; out = reduce. Each
+// rank's work is exactly that of its own launches.
 static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const void* const* shards,
                               const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
                               const void* gamma1, const void* gamma2, void* partials, void* xn,
@@ -1372,7 +1388,9 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     if (!aligned16(kv[r].k_pages) || !aligned16(kv[r].v_pages))
       return fail(TP_ERR_INVALID_ARG, "KV pages must be 16-byte aligned");
   }
-  if (w.gemm_bytes == 0) return fail(TP_ERR_UNSUPPORTED, "no split-K workspace for this batch");
+  const bool prefill = batch->mode == TP_MODE_PREFILL;
+  if (!prefill && w.gemm_bytes == 0)
+    return fail(TP_ERR_UNSUPPORTED, "no split-K workspace for this batch");
   tp_shard_layout L;
   make_layout(x, &L);
   hipStream_t st = (hipStream_t)stream;
@@ -1384,20 +1402,28 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
 
   if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
     return s;
+  // QKV partial products: split-K tiles (batched) or the wide split-K tiles (prefill).
+  const uint64_t pofs = prefill ? w.qkvp : w.gemm;
   tpk::GemmRanks gq{};
   gq.n = N;
   for (int r = 0; r < N; ++r) {
     gq.a[r] = xn;
     gq.b[r] = shard(r) + L.qkv.offset;
-    gq.c[r] = wsr(r) + w.gemm;
+    gq.c[r] = wsr(r) + pofs;
   }
   int S = 0;
-  hipError_t e = tpk::launch_gemm_splitk_ranks(tpk::EPI_ACT, T, x.qkv_rows, x.d, gq, st, &S);
+  hipError_t e;
+  if (prefill) {
+    S = qkv_ksplit(x, T);
+    e = tpk::launch_gemm_split_f32(T, x.qkv_rows, x.d, nullptr, nullptr, nullptr, S, st, &gq);
+  } else {
+    e = tpk::launch_gemm_splitk_ranks(tpk::EPI_ACT, T, x.qkv_rows, x.d, gq, st, &S);
+  }
   if (e != hipSuccess) return hip_fail(e, "qkv projection (all ranks)");
   tpk::RopeRanks rr{};
   rr.n = N;
   for (int r = 0; r < N; ++r) {
-    rr.parts[r] = (const float*)(wsr(r) + w.gemm);
+    rr.parts[r] = (const float*)(wsr(r) + pofs);
     rr.q_out[r] = wsr(r) + w.q;
     rr.k_pages[r] = kv[r].k_pages;
     rr.v_pages[r] = kv[r].v_pages;
@@ -1419,10 +1445,22 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     ar.part_ml[r] = (float*)(wsr(r) + w.part_ml);
     ar.out[r] = wsr(r) + w.attn;
   }
-  e = tpk::launch_attn_decode_ranks(tpk::ACT_BF16, x.hd, x.Hq / x.Hkv, T, x.hk, ar,
-                                    batch->positions, batch->block_table, batch->max_pages, x.ps,
-                                    w.chunk, w.n_split, w.pos_limit, st);
+  if (prefill)
+    e = tpk::launch_attn_prefill(x.hd, x.Hq / x.Hkv, T, x.hk, nullptr, nullptr, nullptr,
+                                 batch->positions, batch->block_table, batch->max_pages, 1,
+                                 w.pos_limit, nullptr, st, &ar);
+  else
+    e = tpk::launch_attn_decode_ranks(tpk::ACT_BF16, x.hd, x.Hq / x.Hkv, T, x.hk, ar,
+                                      batch->positions, batch->block_table, batch->max_pages,
+                                      x.ps, w.chunk, w.n_split, w.pos_limit, st);
   if (e != hipSuccess) return hip_fail(e, "attention (all ranks)");
+  // The projections: band GEMMs (batched) or wide tiles (prefill), as the separate calls pick.
+  auto gemm = [&](int epi, int actf, int n_out, int K, int ldc, const tpk::GemmRanks* g) {
+    return prefill ? tpk::launch_gemm_wide(epi, actf, T, n_out, K, nullptr, nullptr, nullptr,
+                                           nullptr, ldc, st, g)
+                   : tpk::launch_gemm_band(epi, actf, T, n_out, K, nullptr, nullptr, nullptr,
+                                           nullptr, ldc, st, g);
+  };
   tpk::GemmRanks go{};
   go.n = N;
   for (int r = 0; r < N; ++r) {
@@ -1430,8 +1468,7 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     go.b[r] = shard(r) + L.o.offset;
     go.c[r] = part(r);
   }
-  e = tpk::launch_gemm_band(epi_part, 0, T, x.d, x.qdim, nullptr, nullptr, nullptr, nullptr, x.d,
-                            st, &go);
+  e = gemm(epi_part, 0, x.d, x.qdim, x.d, &go);
   if (e != hipSuccess) return hip_fail(e, "o projection (all ranks)");
   if (tp_status s = tp_partial_reduce(desc, T, partials, N, x_in, h1, gamma2, xn2, stream))
     return s;
@@ -1445,8 +1482,7 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
   }
   {
     TimedScope ts(evb, eve);
-    e = tpk::launch_gemm_band(tpk::EPI_GATED, x.actf, T, x.fr, x.d, nullptr, nullptr, nullptr,
-                              nullptr, x.fr, st, &gg);
+    e = gemm(tpk::EPI_GATED, x.actf, x.fr, x.d, x.fr, &gg);
   }
   if (e != hipSuccess) return hip_fail(e, "gate/up projection (all ranks)");
   tpk::GemmRanks gd{};
@@ -1456,8 +1492,7 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     gd.b[r] = shard(r) + L.down.offset;
     gd.c[r] = part(r);
   }
-  e = tpk::launch_gemm_band(epi_part, 0, T, x.d, x.fr, nullptr, nullptr, nullptr, nullptr, x.d, st,
-                            &gd);
+  e = gemm(epi_part, 0, x.d, x.fr, x.d, &gd);
   if (e != hipSuccess) return hip_fail(e, "down projection (all ranks)");
   return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
 }

@@ -207,13 +207,14 @@ hipError_t launch_gemm_qkv_rope(int M, int N, int K, const void* A, const void* 
 // does not fit.
 long gemm_wide_tiles(int epi, int M, int N);
 hipError_t launch_gemm_wide(int epi, int actf, int M, int N, int K, const void* A, const void* B,
-                            const void* B2, void* C, int ldc, hipStream_t st);
+                            const void* B2, void* C, int ldc, hipStream_t st,
+                            const GemmRanks* gr = nullptr);
 // Split-K bf16 projection on 256 x 160 tiles writing ksplit fp32 partial products
 // ([ksplit][M][N]) for shapes too narrow to fill the chip with whole-K tiles;
 // gemm_split_count returns the K ranges to use (1: not worth it).
 int gemm_split_count(int M, int N, int K);
 hipError_t launch_gemm_split_f32(int M, int N, int K, const void* A, const void* B, float* parts,
-                                 int ksplit, hipStream_t st);
+                                 int ksplit, hipStream_t st, const GemmRanks* gr = nullptr);
 
 // k_attn.hip
 // Rotary embedding + KV append from np (1..16) fp32 partials of the QKV projection (bf16 cache).
@@ -228,10 +229,11 @@ hipError_t launch_rope_append(int at, const void* qkv, int T, int hq, int hk, in
                               void* vp, const float* rope, hipStream_t st);
 // k_attn_prefill.hip: bf16 causal prefill of one sequence, KV tiles shared by a GQA group.
 bool attn_prefill_supported(int hd, int G, int ps);
+// ar: every rank in one launch (grid.z = rank; q, pages, n_pages, out per rank).
 hipError_t launch_attn_prefill(int hd, int G, int T, int hk, const void* q, const void* kp,
                                const void* vp, const int* positions, const int* bt,
                                int max_pages, int n_pages, int pos_limit, void* out,
-                               hipStream_t st);
+                               hipStream_t st, const AttnRanks* ar = nullptr);
 hipError_t launch_attn_decode(int at, int hd, int G, int T, int hk, const void* q, const void* kp,
                               const void* vp, const int* positions, int mode, const int* bt,
                               int max_pages, int ps, int n_pages, int chunk, int n_split,

@@ -157,6 +157,42 @@ def test_config_parity_prefill_sampled(name):
     run_and_check(inp, rows=rows, label=f"{name} (sampled rows)")
 
 
+@pytest.mark.timeout(900)
+def test_all_ranks_prefill_matches_staged():
+    """70B-shaped prefill at N = 8: the block step with one launch per stage for all ranks
+    (split-K QKV, rotary / KV append, attention, o_proj, gate/up, down) equals the separate
+    per-rank calls bit for bit: xn, h1, xn2, out, the FFN partials and every rank's new K, V."""
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import DeviceBlock
+    s = WORKLOADS["llama-70b-prefill"]
+    log("llama-70b-prefill: generating inputs")
+    blk = DeviceBlock(make_inputs(s, seed=3))
+    assert blk.schedule() == B.TP_SCHEDULE_ALL_RANKS
+
+    def snap():
+        torch.cuda.synchronize()
+        r = {k: getattr(blk, k).contiguous().view(torch.uint8).cpu()
+             for k in ("xn", "h1", "xn2", "out", "partials")}
+        for rk in range(blk.N):
+            kn, vn = blk.cache_new_entries(rk)
+            r[f"kv{rk}"] = (np.ascontiguousarray(kn).view(np.uint8).copy(),
+                            np.ascontiguousarray(vn).view(np.uint8).copy())
+        return r
+
+    blk.step()
+    staged = snap()
+    for k in ("xn", "h1", "xn2", "out"):
+        getattr(blk, k).fill_(float("nan"))
+    blk.step_fused(schedule=B.TP_SCHEDULE_ALL_RANKS)
+    got = snap()
+    for k in ("xn", "h1", "xn2", "out", "partials"):
+        assert torch.equal(got[k], staged[k]), k
+    for rk in range(blk.N):
+        for a, b in zip(got[f"kv{rk}"], staged[f"kv{rk}"]):
+            assert np.array_equal(a, b), f"cache r{rk}"
+    log("llama-70b-prefill: all-ranks step == separate calls, bit for bit")
+
+
 def test_step_matches_staged_and_graph_replay():
     """The one-call step equals the staged run bit for bit, and a captured HIP graph of the step
     replays to the same bits, with eager work between replays."""
