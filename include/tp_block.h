@@ -230,8 +230,10 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * projections all take the split-K QKV and the band GEMMs, and bf16 prefill whose QKV takes the
  * split-K wide tiles and whose other projections take the 256 x 256 wide tiles, also get
  * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection, the rotary / KV
- * append and the attention as one launch for all ranks, equal to the separate calls bit for bit
- * (under one launch the causal prefill's long and short row blocks of all ranks share the chip).
+ * append and the attention as one launch for all ranks (under one launch the causal prefill's
+ * long and short row blocks of all ranks share the chip), equal to the separate calls bit for
+ * bit, except that a prefill QKV whose tiles of all ranks fill the chip is not split over K: its
+ * q, k, v (and so the rest of the step) equal the separate calls' to rounding.
  * Otherwise (TP_SCHEDULE_STAGED)
  * the call issues exactly the separate calls above. tp_step_schedule reports which schedule a
  * batch gets.

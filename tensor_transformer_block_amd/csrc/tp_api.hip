@@ -1414,7 +1414,11 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
   int S = 0;
   hipError_t e;
   if (prefill) {
-    S = qkv_ksplit(x, T);
+    // One rank's QKV tiles are too few to fill the chip, which is why the separate calls split K;
+    // all ranks' tiles together usually are enough, and then each tile takes the whole K (one
+    // fp32 sum per output, rounded once: the separate calls' q, k, v to rounding).
+    const long tiles = (long)((T + 255) / 256) * ((x.qkv_rows + 159) / 160);
+    S = tiles * N >= 192 ? 1 : qkv_ksplit(x, T);
     e = tpk::launch_gemm_split_f32(T, x.qkv_rows, x.d, nullptr, nullptr, nullptr, S, st, &gq);
   } else {
     e = tpk::launch_gemm_splitk_ranks(tpk::EPI_ACT, T, x.qkv_rows, x.d, gq, st, &S);

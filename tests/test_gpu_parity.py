@@ -159,9 +159,11 @@ def test_config_parity_prefill_sampled(name):
 
 @pytest.mark.timeout(900)
 def test_all_ranks_prefill_matches_staged():
-    """70B-shaped prefill at N = 8: the block step with one launch per stage for all ranks
-    (split-K QKV, rotary / KV append, attention, o_proj, gate/up, down) equals the separate
-    per-rank calls bit for bit: xn, h1, xn2, out, the FFN partials and every rank's new K, V."""
+    """70B-shaped prefill at N = 8: the block step with one launch per stage for all ranks (QKV
+    over the whole K, rotary / KV append, attention, o_proj, gate/up, down) against the separate
+    per-rank calls (whose QKV splits K four ways): xn bit for bit (the same reduce), and h1, xn2,
+    out, the FFN partials and every rank's new K, V to the bf16 tolerance (they differ only by
+    the QKV's fp32 summation order before its bf16 rounding)."""
     from tensor_transformer_block_amd import binding as B
     from tensor_transformer_block_amd.block import DeviceBlock
     s = WORKLOADS["llama-70b-prefill"]
@@ -185,12 +187,24 @@ def test_all_ranks_prefill_matches_staged():
         getattr(blk, k).fill_(float("nan"))
     blk.step_fused(schedule=B.TP_SCHEDULE_ALL_RANKS)
     got = snap()
-    for k in ("xn", "h1", "xn2", "out", "partials"):
-        assert torch.equal(got[k], staged[k]), k
+    assert torch.equal(got["xn"], staged["xn"])
+    errs = {}
+    for k in ("h1", "xn2", "out"):
+        a = got[k].view(torch.bfloat16).float().numpy()
+        b = staged[k].view(torch.bfloat16).float().numpy()
+        errs[k] = nrel(a, b)
+    pa = got["partials"].view(torch.float32).numpy()
+    pb = staged["partials"].view(torch.float32).numpy()
+    errs["partials"] = nrel(pa, pb)
     for rk in range(blk.N):
-        for a, b in zip(got[f"kv{rk}"], staged[f"kv{rk}"]):
-            assert np.array_equal(a, b), f"cache r{rk}"
-    log("llama-70b-prefill: all-ranks step == separate calls, bit for bit")
+        for nm, a, b in zip(("k", "v"), got[f"kv{rk}"], staged[f"kv{rk}"]):
+            fa = (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+            fb = (b.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+            errs[f"{nm}_new r{rk}"] = nrel(fa, fb)
+    log("llama-70b-prefill: all-ranks step vs separate calls: "
+        + ", ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= 2e-2, (k, v)
 
 
 def test_step_matches_staged_and_graph_replay():
