@@ -20,7 +20,7 @@
 
 namespace tpk {
 
-template <int MT, int EPI, int ACTF, int BK, int RS, int NRK>
+template <int MT, int EPI, int ACTF, int BK, int RS, int NRK, bool XR>
 __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ A,
                                                    const uint16_t* __restrict__ B,
                                                    const uint16_t* __restrict__ B2, int M, int N,
@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
                                                    GemmRanks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int AR = MT * 16, BR = 16 * NB;  // staged activation rows, weight rows per rank
-  constexpr int BRA = NRK * BR;              // weight rows of the NRK ranks sharing A
+  constexpr int AR = MT * 16, BR = 16 * NB;  // staged activation rows, weight rows per group
+  constexpr int BRA = NRK * BR;              // weight rows of the NRK groups sharing A
   constexpr int CPR = BK / 8;                // 16-byte chunks per staged row
   constexpr int RPL = 64 / CPR;              // rows per wave-load
   constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
@@ -41,18 +41,22 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
   static_assert((RS - 2) * LPW <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  // Every rank in one launch: blockIdx.z picks rank (NRK = 1) or the group of NRK ranks that
-  // share the activations A (column-parallel projections of one input), rank r0 + i's weights
-  // in staged rows [i * BR, (i + 1) * BR).
-  const int r0 = gr.n > 1 ? (int)blockIdx.z * NRK : 0;
+  // The workgroup's NRK groups of 16 columns share its activation stages, group i in staged rows
+  // [i * BR, (i + 1) * BR). XR: the groups are NRK ranks' same 16 columns (a column-parallel
+  // projection of one input, every rank in one launch; blockIdx.z picks the ranks r0 ..
+  // r0 + NRK - 1). Otherwise: NRK adjacent 16-column bands of one rank (blockIdx.z = rank when
+  // every rank is in the launch), so each activation stage serves 16 NRK columns.
+  const int r0 = gr.n > 1 ? (int)blockIdx.z * (XR ? NRK : 1) : 0;
   if (gr.n > 1) A = (const uint16_t*)gr.a[r0];
   auto wsrc = [&](int i, bool up) -> const uint16_t* {
-    if (gr.n > 1) return (const uint16_t*)(up ? gr.b2[r0 + i] : gr.b[r0 + i]);
+    const int r = XR ? r0 + i : r0;
+    if (gr.n > 1) return (const uint16_t*)(up ? gr.b2[r] : gr.b[r]);
     return up ? B2 : B;
   };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * (XR ? 1 : NRK);
+  auto cbase = [&](int i) { return XR ? n0 : n0 + 16 * i; };
   const int nst = K / BK;  // K % BK == 0 (checked by the launcher)
 
   // Lane l of a wave-load stores its 16 bytes at chunk l % CPR of row l / CPR of the wave-load's
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
       const int row = g * RPL + lrow;  // rank row / BR: gate rows, then (gated) the up rows
       const int lr = row % BR;
       const uint16_t* base = wsrc(row / BR, DUAL && lr >= 16);
-      const int col = min(n0 + (lr & 15), N - 1);
+      const int col = min(cbase(row / BR) + (lr & 15), N - 1);
       const uint16_t* src = base + (size_t)col * K + kb + ((lpc ^ (row & SWZ)) << 3);
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
                                        (lds_void_t*)(st + (AR + g * RPL) * BK), 16, 0, 0);
@@ -118,11 +122,12 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
   }
   // The clamped loads past the last stage may still be in flight.
   wait_vmcnt<0>();
-  const int col = n0 + fr;
-  if (!mma_wave || col >= N) return;
+  if (!mma_wave) return;
 #pragma unroll
   for (int i = 0; i < NRK; ++i) {
-    void* Ci = gr.n > 1 ? gr.c[r0 + i] : C;
+    void* Ci = gr.n > 1 ? gr.c[XR ? r0 + i : r0] : C;
+    const int col = cbase(i) + fr;
+    if (col >= N) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = wave * 16 + fq * 4 + r;
@@ -156,7 +161,7 @@ constexpr int band_slots() {
   return r > 8 ? 8 : r;
 }
 
-template <int MT, int EPI, int ACTF, int NRK>
+template <int MT, int EPI, int ACTF, int NRK, bool XR>
 hipError_t band_launch_n(int M, int N, int K, const uint16_t* a, const uint16_t* b,
                          const uint16_t* b2, void* C, int ldc, hipStream_t st,
                          const GemmRanks& gr) {
@@ -167,21 +172,26 @@ hipError_t band_launch_n(int M, int N, int K, const uint16_t* a, const uint16_t*
   constexpr int RS = band_slots<MT, DUAL, BK, NRK>();
   constexpr size_t lds = (size_t)RS * (MT * 16 + NRK * 16 * (DUAL ? 2 : 1)) * BK * 2;
   if (K % BK != 0) return hipErrorInvalidValue;
-  auto kern = k_gemm_band<MT, EPI, ACTF, BK, RS, NRK>;
+  auto kern = k_gemm_band<MT, EPI, ACTF, BK, RS, NRK, XR>;
   hipError_t e = allow_lds((const void*)kern, (int)lds);
   if (e != hipSuccess) return e;
-  const int nz = gr.n > 1 ? gr.n / NRK : 1;
-  launch(kern, dim3((N + 15) / 16, 1, nz), dim3(256), lds, st, a, b, b2, M, N, K, C, ldc, gr);
+  const int nz = gr.n > 1 ? (XR ? gr.n / NRK : gr.n) : 1;
+  const int cols = 16 * (XR ? 1 : NRK);
+  launch(kern, dim3((N + cols - 1) / cols, 1, nz), dim3(256), lds, st, a, b, b2, M, N, K, C, ldc,
+         gr);
   return hipGetLastError();
 }
 
+// share > 0: groups of `share` ranks of one input; share < 0: -share adjacent bands of one rank.
 template <int MT, int EPI, int ACTF>
 hipError_t band_launch(int M, int N, int K, const uint16_t* a, const uint16_t* b,
                        const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr,
                        int share) {
-  if (share == 4) return band_launch_n<MT, EPI, ACTF, 4>(M, N, K, a, b, b2, C, ldc, st, gr);
-  if (share == 2) return band_launch_n<MT, EPI, ACTF, 2>(M, N, K, a, b, b2, C, ldc, st, gr);
-  return band_launch_n<MT, EPI, ACTF, 1>(M, N, K, a, b, b2, C, ldc, st, gr);
+  if (share == 4) return band_launch_n<MT, EPI, ACTF, 4, true>(M, N, K, a, b, b2, C, ldc, st, gr);
+  if (share == 2) return band_launch_n<MT, EPI, ACTF, 2, true>(M, N, K, a, b, b2, C, ldc, st, gr);
+  if (share == -4) return band_launch_n<MT, EPI, ACTF, 4, false>(M, N, K, a, b, b2, C, ldc, st, gr);
+  if (share == -2) return band_launch_n<MT, EPI, ACTF, 2, false>(M, N, K, a, b, b2, C, ldc, st, gr);
+  return band_launch_n<MT, EPI, ACTF, 1, true>(M, N, K, a, b, b2, C, ldc, st, gr);
 }
 
 template <int MT>
@@ -189,9 +199,9 @@ hipError_t band_mt(int epi, int actf, int M, int N, int K, const uint16_t* a, co
                    const uint16_t* b2, void* C, int ldc, hipStream_t st, const GemmRanks& gr,
                    int share) {
   switch (epi) {
-    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
-    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
-    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st, gr, 1);
+    case EPI_ACT: return band_launch<MT, EPI_ACT, 0>(M, N, K, a, b, b2, C, ldc, st, gr, share);
+    case EPI_F32: return band_launch<MT, EPI_F32, 0>(M, N, K, a, b, b2, C, ldc, st, gr, share);
+    case EPI_BF16: return band_launch<MT, EPI_BF16, 0>(M, N, K, a, b, b2, C, ldc, st, gr, share);
     case EPI_GATED:
       return actf == 0 ? band_launch<MT, EPI_GATED, 0>(M, N, K, a, b, b2, C, ldc, st, gr, share)
                        : band_launch<MT, EPI_GATED, 1>(M, N, K, a, b, b2, C, ldc, st, gr, share);
@@ -223,15 +233,22 @@ hipError_t launch_gemm_band(int epi, int actf, int M, int N, int K, const void* 
     C = gr->c[0];
   }
   const GemmRanks& g = gr ? *gr : one;
-  // Gated projections of one input for several ranks: groups of four (or two) ranks share each
-  // workgroup's activation stages.
+  // Every rank in one launch: a gated projection of one input shares each workgroup's
+  // activation stages among groups of four (or two) ranks; other projections (each rank its own
+  // input) give a workgroup four (or two) adjacent bands of one rank while the launch still has
+  // 256 workgroups, so each activation stage serves more weight rows.
   int share = 1;
-  if (gr && epi == EPI_GATED && gr->n > 1) {
+  if (gr && gr->n > 1 && K % 64 == 0) {
     const int n = gr->n;
-    share = n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+    bool same_a = true;
     for (int r = 1; r < n; ++r)
-      if (gr->a[r] != gr->a[0]) share = 1;
-    if (K % 64 != 0) share = 1;
+      if (gr->a[r] != gr->a[0]) same_a = false;
+    if (epi == EPI_GATED && same_a) {
+      share = n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+    } else if (epi != EPI_GATED) {
+      const long bands = (N + 15) / 16;
+      share = (bands / 4) * n >= 256 ? -4 : ((bands / 2) * n >= 256 ? -2 : 1);
+    }
   }
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   switch ((M + 15) / 16) {

@@ -245,7 +245,8 @@ FUSED_STEP = ["med-bf16-ragged", "med-bf16-single-key", "med-q8-n4", "med-q8-hd2
 
 ONE_CALL = ([(n, p) for n in FUSED_STEP for p in ("f32", "bf16")]
             + [(n, "f32") for n in ("tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode",
-                                    "llama3-8b-batched")])
+                                    "llama3-8b-batched")]
+            + [("llama3-8b-batched", "bf16")])
 
 
 @pytest.mark.parametrize("name,partial_dtype", ONE_CALL, ids=lambda v: str(v))
