@@ -207,7 +207,9 @@ int qkv_ksplit(const Dims& x, int T) {
   return tpk::gemm_split_count(T, x.qkv_rows, x.d);
 }
 
-WsLayout ws_layout(const Dims& x, const tp_batch& b) {
+// ranks: how many ranks' attention shares one launch (the all-ranks batched schedule: the key
+// range is split only as far as all ranks' workgroups together need).
+WsLayout ws_layout(const Dims& x, const tp_batch& b, int ranks = 1) {
   WsLayout w{};
   const uint64_t T = (uint64_t)b.n_tokens;
   int L = b.max_seq_len > 0 ? b.max_seq_len : b.max_pages * x.ps;
@@ -217,7 +219,7 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b) {
   // Key splits of the attention: about 256 workgroups in total, in multiples of 32 keys, each at
   // least one 32-key tile per wave (128 keys) or, for heads of 256 and more, whose tiles carry
   // twice the bytes, two of the four waves busy (64 keys).
-  const int per_split = x.hk * (int)(T > 0 ? T : 1);
+  const int per_split = x.hk * (int)(T > 0 ? T : 1) * ranks;
   const int want = (256 + per_split - 1) / per_split;
   const int min_chunk = x.hd >= 256 ? 64 : 128;
   int chunk = (L + want - 1) / want;
@@ -354,9 +356,17 @@ bool all_ranks_ok(const Dims& x, const tp_batch& b) {
   return ranks_step_ok(x, b.n_tokens) || ranks_staged_ok(x, b) || ranks_prefill_ok(x, b);
 }
 
+// Workspace layout of one rank under the step's schedule (the all-ranks staged schedule plans
+// the attention's key splits for all ranks' workgroups together).
+WsLayout step_ws_layout(const Dims& x, const tp_batch& b) {
+  const bool staged_all = !ranks_step_ok(x, b.n_tokens) &&
+                          (ranks_staged_ok(x, b) || ranks_prefill_ok(x, b));
+  return ws_layout(x, b, staged_all ? x.N : 1);
+}
+
 uint64_t step_ws_bytes(const Dims& x, const tp_batch& b) {
-  const uint64_t one = ws_layout(x, b).total;
-  return all_ranks_ok(x, b) ? (uint64_t)x.N * align_up(one) : one;
+  if (!all_ranks_ok(x, b)) return ws_layout(x, b).total;
+  return (uint64_t)x.N * align_up(step_ws_layout(x, b).total);
 }
 
 }  // namespace
@@ -1374,7 +1384,7 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
                               uint64_t workspace_bytes, void* stream, hipEvent_t evb,
                               hipEvent_t eve) {
   const int T = batch->n_tokens, N = x.N;
-  const WsLayout w = ws_layout(x, *batch);
+  const WsLayout w = step_ws_layout(x, *batch);
   const uint64_t wstride = align_up(w.total);
   if (workspace_bytes < (uint64_t)N * wstride)
     return fail(TP_ERR_BUFFER_TOO_SMALL, "workspace_bytes=%llu < %llu (one copy per rank)",

@@ -298,7 +298,9 @@ def test_one_call_step(name, partial_dtype):
     for k, (a, b) in errs.items():
         assert a <= tol, (k, a)
         assert b <= tol, (k, b)
-        if not fused:
+        # The staged schedule is the separate calls themselves; the all-ranks batched schedule
+        # plans the attention's key splits for all ranks together (to rounding).
+        if not fused and sched == "staged":
             assert b == 0.0, (k, b)
     # The all-ranks schedule (one launch per projection for every rank) against the per-rank
     # fused schedule: the same bits everywhere, partials and new cache entries included. (For
