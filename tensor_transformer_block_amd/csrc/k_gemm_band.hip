@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
       const int col = min(cbase(row / BR) + (lr & 15), N - 1);
       const uint16_t* src = base + (size_t)col * K + kb + ((lpc ^ (row & SWZ)) << 3);
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
-                                       (lds_void_t*)(st + (AR + g * RPL) * BK), 16, 0, 0);
+                                       (lds_void_t*)(st + (AR + g * RPL) * BK), 16, 0,
+                                       kStreamAux);
     }
   };
 

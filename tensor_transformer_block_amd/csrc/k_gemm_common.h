@@ -9,6 +9,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// Cache-policy bits of a direct-to-LDS load: 0 for data other tiles read again, kStreamAux (the
+// non-temporal bit) for weights that a skinny batch reads exactly once.
+constexpr int kStreamAux = 2;
+
 template <int N_OUT>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt with vmcnt = N_OUT (6-bit, split field), expcnt and lgkmcnt left at "no wait".
