@@ -655,7 +655,12 @@ hipError_t gemv_format(int epi, int actf, int nt, const void* W, const uint16_t*
   const long wrows = (epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF)
                          ? (long)n_out * (rp.n < 4 ? (rp.n > 1 ? rp.n : 1) : 4)
                          : (epi == EPI_GATED ? 2L * n_out : (long)n_out);
-  const int r = gemv_rows_per_wave(nch, paired, wrows);
+  int r = gemv_rows_per_wave(nch, paired, wrows);
+  // Two ranks' row-parallel launch of 16-bit or Q8_0 weights: two rows per wave. Every workgroup
+  // stages both ranks' input rows, so fewer, larger workgroups stage less; two rows measured best
+  // or level on the 8B-shaped down (K 7168: 22.9 -> 20.5 us with one row) and o_proj and the
+  // Gemma-like Q8_0 down and o_proj.
+  if ((epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF) && rp.n == 2 && WT != W_F32) r = 2;
   switch (epi) {
     case EPI_F32:
       return gemv_r<WT, AT, EPI_F32, 0>(r, nt, W, S, K, n_out, gate_off, X, Y, ldy, re, fa, rp, st);
