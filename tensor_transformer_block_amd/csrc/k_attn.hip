@@ -449,8 +449,10 @@ __device__ __forceinline__ uint4 kv_ld(const uint16_t* p) {
   else return ld_stream16(p);
 }
 
+// Decode with heads of up to 128 fits three waves per SIMD (168 registers) without spilling; more
+// waves keep more key tiles in flight (64 sequences of 2048 keys, 4 ranks: 84.9 -> 83.4 us).
 template <int HD, bool PREFILL>
-__global__ __launch_bounds__(256) void k_attn_mfma(
+__global__ __launch_bounds__(256, (HD <= 128 && !PREFILL) ? 3 : 1) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpages,
     const uint16_t* __restrict__ vpages, const int* __restrict__ positions, int mode,
     const int* __restrict__ block_table, int max_pages, int ps, int n_pages, int hk, int G,

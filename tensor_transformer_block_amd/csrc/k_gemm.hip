@@ -633,8 +633,10 @@ static hipError_t splitk_impl(int epi, int actf, int M, int N, int K, const void
   if (M > 64) return hipErrorInvalidValue;
   const bool dual = (epi == EPI_GATED);
   int S, kc;
-  splitk_plan(N, K, dual, &S, &kc);
-  dim3 g((N + 63) / 64, S, gr.n > 1 ? gr.n : 1), blk(256);
+  // A launch over all ranks counts every rank's tiles toward filling the chip.
+  const int nr = gr.n > 1 ? gr.n : 1;
+  splitk_plan(N * nr, K, dual, &S, &kc);
+  dim3 g((N + 63) / 64, S, nr), blk(256);
   const uint16_t *a = (const uint16_t*)A, *b = (const uint16_t*)B, *b2 = (const uint16_t*)B2;
   const int mt = (M + 15) / 16;
   if (K % SD_BK == 0) {
