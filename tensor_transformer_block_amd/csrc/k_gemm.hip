@@ -468,8 +468,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_dma(const uint16_t* __restr
       }
       const char* src = (const char*)(base + (size_t)min(col, N - 1) * K) + kb + lchunk;
       __builtin_amdgcn_global_load_lds((glb_void_t*)src,
-                                       (lds_void_t*)(st + (AR + g * 8) * SD_BK), 16, 0,
-                                       kStreamAux);
+                                       (lds_void_t*)(st + (AR + g * 8) * SD_BK), 16, 0, 0);
     }
   };
 

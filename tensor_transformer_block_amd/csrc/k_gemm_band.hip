@@ -147,9 +147,12 @@ __global__ __launch_bounds__(256) void k_gemm_band(const uint16_t* __restrict__ 
 
 namespace {
 
-// Stage depth and ring size: 256-byte weight row segments and the deepest ring that fits the
-// 160 KB of LDS and the wait counter's range. (512-byte segments, or non-temporal weight loads,
-// measured no faster inside the block step.)
+// Stage depth and ring size: 256-byte weight row segments and a ring of at most five slots (four
+// stages in flight) that fits the 160 KB of LDS and the wait counter's range. Deeper rings, or
+// separate rings that keep more weight stages than activation stages in flight, measured slower
+// inside the batched step (64 sequences, 4 ranks: 201.1 us with five slots, 202.2 with six,
+// 203.3 with up to eight, 205.9 with four, 216.6 with 23 weight stages in flight); so did
+// 512-byte segments.
 constexpr int BD_BK = 128;
 template <int MT, bool DUAL, int BK, int NRK>
 constexpr int band_slots() {
@@ -159,7 +162,7 @@ constexpr int band_slots() {
   constexpr int s = (160 * 1024) / stage;
   constexpr int smax = 63 / lpw + 2;
   constexpr int r = s < smax ? s : smax;
-  return r > 8 ? 8 : r;
+  return r > 5 ? 5 : r;
 }
 
 template <int MT, int EPI, int ACTF, int NRK, bool XR>
