@@ -73,8 +73,15 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   __shared__ float2 s_ml[AP_KG][2][2][64];  // merge: (m, l) per key group, wave, row block, lane
   __shared__ int s_kmax;
-  if (ar.n > 1) {  // every rank in one launch (blockIdx.z = rank)
-    const int r = blockIdx.z;
+  // Every rank in one launch: consecutive workgroups, which the dispatcher deals round-robin to
+  // the XCDs, take consecutive ranks, so each XCD's L2 holds the KV of few ranks; the longest
+  // token tiles of every rank still go first.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (ar.n > 1) {
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int r = lin % ar.n, rest = lin / ar.n;
+    by = rest % gridDim.y;
+    bx = rest / gridDim.y;
     q = (const uint16_t*)ar.q[r];
     kpages = (const uint16_t*)ar.k_pages[r];
     vpages = (const uint16_t*)ar.v_pages[r];
@@ -82,8 +89,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(
     out = (uint16_t*)ar.out[r];
   }
 
-  const int g = blockIdx.y / (G / NHW), hgrp = blockIdx.y % (G / NHW);
-  const int t0 = (gridDim.x - 1 - blockIdx.x) * (16 * TB);  // latest tokens first
+  const int g = by / (G / NHW), hgrp = by % (G / NHW);
+  const int t0 = (gridDim.x - 1 - bx) * (16 * TB);  // latest tokens first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave >> 1, wp = wave & 1;  // key group, wave within the group
