@@ -231,9 +231,12 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * split-K wide tiles and whose other projections take the 256 x 256 wide tiles, also get
  * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection, the rotary / KV
  * append and the attention as one launch for all ranks (under one launch the causal prefill's
- * long and short row blocks of all ranks share the chip), equal to the separate calls bit for
- * bit, except that a prefill QKV whose tiles of all ranks fill the chip is not split over K: its
- * q, k, v (and so the rest of the step) equal the separate calls' to rounding.
+ * long and short row blocks of all ranks share the chip). The launches are sized for all ranks'
+ * work together, so three choices differ from the separate calls': a prefill QKV whose tiles of
+ * all ranks fill the chip is not split over K; the batched QKV splits K into fewer ranges; the
+ * batched attention splits each sequence's keys into fewer ranges (often none). Each changes
+ * only the order of fp32 additions before a rounding: q, k, v, the attention output and so the
+ * rest of the step equal the separate calls' to rounding, not bit for bit.
  * Otherwise (TP_SCHEDULE_STAGED)
  * the call issues exactly the separate calls above. tp_step_schedule reports which schedule a
  * batch gets.

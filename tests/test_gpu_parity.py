@@ -299,12 +299,13 @@ def test_one_call_step(name, partial_dtype):
         assert a <= tol, (k, a)
         assert b <= tol, (k, b)
         # The staged schedule is the separate calls themselves; the all-ranks batched schedule
-        # plans the attention's key splits for all ranks together (to rounding).
+        # plans the QKV's K ranges and the attention's key splits for all ranks together, which
+        # changes only the order of fp32 additions (to rounding).
         if not fused and sched == "staged":
             assert b == 0.0, (k, b)
     # The all-ranks schedule (one launch per projection for every rank) against the per-rank
-    # fused schedule: the same bits everywhere, partials and new cache entries included. (For
-    # batched shapes the all-ranks schedule is the staged sequence's, compared above: b == 0.)
+    # fused schedule: the same bits everywhere, partials and new cache entries included. (Batched
+    # shapes have no per-rank fused schedule; they are compared with the staged calls above.)
     from tensor_transformer_block_amd import binding as B
     if blk.schedule() == B.TP_SCHEDULE_ALL_RANKS and fused:
         def bits(t):
