@@ -67,6 +67,8 @@ __global__ void k_rope_append(const void* __restrict__ qkv, int T, int hq, int h
 // The same rotary embedding + KV append from NP fp32 partial products of the QKV projection
 // (a split-K GEMM's K ranges, [NP][T][heads * hd]): the partials are summed in range order and
 // rounded once to bf16, the value the unsplit projection would have stored, then rotated.
+// Workgroup: one token (blockIdx.x) of one rank (blockIdx.y); its position and KV page are read
+// once, and the threads walk the token's heads in groups of four rotation pairs.
 template <int NP>
 __global__ void k_rope_append_parts(const float* __restrict__ parts, int T, int hq, int hk, int hd,
                                     uint16_t* __restrict__ q_out,
@@ -83,61 +85,53 @@ __global__ void k_rope_append_parts(const float* __restrict__ parts, int T, int 
     vp = (uint16_t*)rr.v_pages[r];
     n_pages = rr.n_pages[r];
   }
-  // Thread: four consecutive rotation pairs (e .. e + 3 with e + half .. e + half + 3) of one
-  // head of one token, so every partial read and every q / k store is a 16- or 8-byte access.
+  const int t = blockIdx.x;
   const int half = hd >> 1, q4 = half >> 2;
   const int heads = hq + 2 * hk;
-  const int64_t total = (int64_t)T * heads * q4;
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int e = (int)(i % q4) * 4;
-  const int head = (int)((i / q4) % heads);
-  const int t = (int)(i / ((int64_t)q4 * heads));
   const int pos = clampi(positions[t], 0, pos_limit - 1);
-  const size_t src = (size_t)t * heads * hd + (size_t)head * hd;
+  const int seq = (mode == 0) ? t : 0;
+  const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
   const size_t pstride = (size_t)T * heads * hd;
-  float4 sa = *(const float4*)(parts + src + e), sb = *(const float4*)(parts + src + e + half);
+  // Thread j: four consecutive rotation pairs (e .. e + 3 with e + half .. e + half + 3) of one
+  // head, so every partial read and every q / k store is a 16- or 8-byte access.
+  for (int j = threadIdx.x; j < heads * q4; j += blockDim.x) {
+    const int head = j / q4, e = (j - head * q4) * 4;
+    const size_t src = ((size_t)t * heads + head) * hd;
+    float4 sa = *(const float4*)(parts + src + e), sb = *(const float4*)(parts + src + e + half);
 #pragma unroll
-  for (int p = 1; p < NP; ++p) {
-    const float4 xa = *(const float4*)(parts + p * pstride + src + e);
-    const float4 xb = *(const float4*)(parts + p * pstride + src + e + half);
-    sa.x += xa.x; sa.y += xa.y; sa.z += xa.z; sa.w += xa.w;
-    sb.x += xb.x; sb.y += xb.y; sb.z += xb.z; sb.w += xb.w;
-  }
-  const uint16_t ua[4] = {f32_to_bf16(sa.x), f32_to_bf16(sa.y), f32_to_bf16(sa.z), f32_to_bf16(sa.w)};
-  const uint16_t ub[4] = {f32_to_bf16(sb.x), f32_to_bf16(sb.y), f32_to_bf16(sb.z), f32_to_bf16(sb.w)};
-  if (head < hq + hk) {
-    const float4 c01 = *(const float4*)(rope + (size_t)pos * half + e);      // (cos, sin) of e, e+1
-    const float4 c23 = *(const float4*)(rope + (size_t)pos * half + e + 2);  // of e+2, e+3
-    const float cs[4][2] = {{c01.x, c01.y}, {c01.z, c01.w}, {c23.x, c23.y}, {c23.z, c23.w}};
-    uint16_t ra[4], rb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = bf16_to_f32(ua[j]), b = bf16_to_f32(ub[j]);
-      ra[j] = f32_to_bf16(a * cs[j][0] - b * cs[j][1]);
-      rb[j] = f32_to_bf16(b * cs[j][0] + a * cs[j][1]);
+    for (int p = 1; p < NP; ++p) {
+      const float4 xa = *(const float4*)(parts + p * pstride + src + e);
+      const float4 xb = *(const float4*)(parts + p * pstride + src + e + half);
+      sa.x += xa.x; sa.y += xa.y; sa.z += xa.z; sa.w += xa.w;
+      sb.x += xb.x; sb.y += xb.y; sb.z += xb.z; sb.w += xb.w;
     }
-    const uint2 pa = make_uint2(ra[0] | ((uint32_t)ra[1] << 16), ra[2] | ((uint32_t)ra[3] << 16));
-    const uint2 pb = make_uint2(rb[0] | ((uint32_t)rb[1] << 16), rb[2] | ((uint32_t)rb[3] << 16));
-    uint16_t* d;
-    if (head < hq) {
-      d = q_out + (size_t)t * hq * hd + (size_t)head * hd;
+    const uint16_t ua[4] = {f32_to_bf16(sa.x), f32_to_bf16(sa.y), f32_to_bf16(sa.z), f32_to_bf16(sa.w)};
+    const uint16_t ub[4] = {f32_to_bf16(sb.x), f32_to_bf16(sb.y), f32_to_bf16(sb.z), f32_to_bf16(sb.w)};
+    if (head < hq + hk) {
+      const float4 c01 = *(const float4*)(rope + (size_t)pos * half + e);      // (cos, sin) of e, e+1
+      const float4 c23 = *(const float4*)(rope + (size_t)pos * half + e + 2);  // of e+2, e+3
+      const float cs[4][2] = {{c01.x, c01.y}, {c01.z, c01.w}, {c23.x, c23.y}, {c23.z, c23.w}};
+      uint16_t ra[4], rb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_to_f32(ua[i]), b = bf16_to_f32(ub[i]);
+        ra[i] = f32_to_bf16(a * cs[i][0] - b * cs[i][1]);
+        rb[i] = f32_to_bf16(b * cs[i][0] + a * cs[i][1]);
+      }
+      const uint2 pa = make_uint2(ra[0] | ((uint32_t)ra[1] << 16), ra[2] | ((uint32_t)ra[3] << 16));
+      const uint2 pb = make_uint2(rb[0] | ((uint32_t)rb[1] << 16), rb[2] | ((uint32_t)rb[3] << 16));
+      uint16_t* d = head < hq ? q_out + ((size_t)t * hq + head) * hd
+                              : kp + (((size_t)page * hk + (head - hq)) * ps + pos % ps) * hd;
+      *(uint2*)(d + e) = pa;
+      *(uint2*)(d + e + half) = pb;
     } else {
-      const int seq = (mode == 0) ? t : 0;
-      const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
-      d = kp + (((size_t)page * hk + (head - hq)) * ps + pos % ps) * hd;
-    }
-    *(uint2*)(d + e) = pa;
-    *(uint2*)(d + e + half) = pb;
-  } else {
-    const int seq = (mode == 0) ? t : 0;
-    const int page = clampi(block_table[(size_t)seq * max_pages + pos / ps], 0, n_pages - 1);
-    // V pages are stored transposed: [page][kv head][hd][slot].
-    uint16_t* dv = vp + ((size_t)page * hk + (head - hq - hk)) * hd * ps + pos % ps;
+      // V pages are stored transposed: [page][kv head][hd][slot].
+      uint16_t* dv = vp + ((size_t)page * hk + (head - hq - hk)) * hd * ps + pos % ps;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dv[(size_t)(e + j) * ps] = ua[j];
-      dv[(size_t)(e + half + j) * ps] = ub[j];
+      for (int i = 0; i < 4; ++i) {
+        dv[(size_t)(e + i) * ps] = ua[i];
+        dv[(size_t)(e + half + i) * ps] = ub[i];
+      }
     }
   }
 }
@@ -148,8 +142,8 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
                                     int pos_limit, void* kp, void* vp, const float* rope,
                                     hipStream_t st, const RopeRanks* rr) {
   if (hd % 8) return hipErrorInvalidValue;
-  const int64_t total = (int64_t)T * (hq + 2 * hk) * (hd / 8);
-  if (total == 0) return hipSuccess;
+  const int per_token = (hq + 2 * hk) * (hd / 8);  // threads' work items per token
+  if (T == 0 || per_token == 0) return hipSuccess;
   const RopeRanks one{};
   const RopeRanks& rk = rr ? *rr : one;
   if (rr && (rr->n < 1 || rr->n > kMaxRanks)) return hipErrorInvalidValue;
@@ -160,7 +154,8 @@ hipError_t launch_rope_append_parts(const float* parts, int np, int T, int hq, i
     vp = rr->v_pages[0];
     n_pages = rr->n_pages[0];
   }
-  dim3 g((unsigned)((total + 255) / 256), rr && rr->n > 1 ? rr->n : 1), b(256);
+  const int threads = per_token > 1024 - 63 ? 1024 : (per_token + 63) / 64 * 64;
+  dim3 g((unsigned)T, rr && rr->n > 1 ? rr->n : 1), b(threads);
 #define TPK_RAP(NPV)                                                                            \
   hipLaunchKernelGGL(k_rope_append_parts<NPV>, g, b, 0, st, parts, T, hq, hk, hd,               \
                      (uint16_t*)q_out, positions, mode, block_table, max_pages, ps, n_pages,    \
