@@ -321,7 +321,10 @@ class MoEBlock:
         self.ids = torch.empty((T, m.top_k), dtype=torch.int32, device=device)
         self.weights = torch.empty((T, m.top_k), dtype=torch.float32, device=device)
         self.ws_bytes = B.tp_moe_workspace_size(b.desc, self.moe, T)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        # One rank's share per rank: the block step then runs every rank's expert gate/up as
+        # one launch (the per-rank calls use the first share).
+        self.step_ws_bytes = self.ws_bytes * b.N
+        self.workspace = torch.empty(self.step_ws_bytes, dtype=torch.uint8, device=device)
 
     @property
     def out(self):
@@ -343,14 +346,16 @@ class MoEBlock:
                                          b.T, self.ids, self.weights, out, self.workspace,
                                          events[0], events[1], self.ws_bytes)
 
-    def step_fused(self, copy: int = 0):
+    def step_fused(self, copy: int = 0, moe_ws_bytes: int | None = None):
         """The same MoE block step in one library call (tp_moe_block_step): for decode batches
-        the norms and the reduces run inside the neighbouring projections."""
+        the norms and the reduces run inside the neighbouring projections. moe_ws_bytes: the
+        expert workspace handed to the call (default: every rank's share)."""
         b = self.attn
         B.tp_moe_block_step(b.desc, self.moe, b.shards[copy], self.shards[copy], b.batch,
                             b.kv[copy], b.x, b.gamma1, b.gamma2, self.router, b.partials, b.xn,
                             b.h1, b.xn2, b.out, self.logits, self.ids, self.weights, b.workspace,
-                            self.workspace, b.ws_bytes, self.ws_bytes)
+                            self.workspace, b.ws_bytes,
+                            self.step_ws_bytes if moe_ws_bytes is None else moe_ws_bytes)
 
     def step(self, copy: int = 0, moe_events=None):
         b = self.attn

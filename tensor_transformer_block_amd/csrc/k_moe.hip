@@ -177,9 +177,17 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
                                                      int Fr, int E, int top_k,
                                                      const int32_t* __restrict__ ids,
                                                      const void* __restrict__ X,
-                                                     void* __restrict__ Mout) {
+                                                     void* __restrict__ Mout, MoeRanks mr) {
   extern __shared__ float xs[];  // [K]
   constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
+  if (mr.n > 1) {  // every rank in one launch (blockIdx.z = rank): that rank's slices and output
+    const int r = blockIdx.z;
+    Wg = (const char*)mr.wg[r];
+    Sg = (const uint16_t*)mr.sg[r];
+    Wu = (const char*)mr.wu[r];
+    Su = (const uint16_t*)mr.su[r];
+    Mout = mr.m[r];
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.y;
   const int nch = K / VE, nblk = K / 32;
@@ -391,35 +399,94 @@ static hipError_t moe_down_variant(dim3 g, size_t lds, hipStream_t st, const cha
   return moe_down_launch<WT, AT, PT, 1>(g, lds, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P, fa);
 }
 
+// The gate/up kernel of one rank (mr.n == 0) or of every rank (grid.z = rank).
 template <int WT, int AT>
-static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, const void* Wu,
-                              const void* Su, const void* Wd, const void* Sd, int d, int Fr, int E,
-                              int top_k, int T, const int32_t* ids, const float* wts,
-                              const void* X, void* M, void* P, hipStream_t st,
-                              const FuseArgs* fuse) {
+static hipError_t moe_gate_up_fmt(int actf, const void* Wg, const void* Sg, const void* Wu,
+                                  const void* Su, int d, int Fr, int E, int top_k, int T,
+                                  const int32_t* ids, const void* X, void* M, const MoeRanks& mr,
+                                  hipStream_t st) {
   const int np = top_k * Fr;
-  const dim3 gu((np + 4 * MOE_PW - 1) / (4 * MOE_PW), T), b(256);
+  const dim3 gu((np + 4 * MOE_PW - 1) / (4 * MOE_PW), T, mr.n > 1 ? mr.n : 1), b(256);
   const size_t lds_gu = (size_t)d * sizeof(float);
-  const char *wg = (const char*)Wg, *wu = (const char*)Wu, *wd = (const char*)Wd;
-  const uint16_t *sg = (const uint16_t*)Sg, *su = (const uint16_t*)Su, *sd = (const uint16_t*)Sd;
+  const char *wg = (const char*)Wg, *wu = (const char*)Wu;
+  const uint16_t *sg = (const uint16_t*)Sg, *su = (const uint16_t*)Su;
   if (lds_gu > 65536) {
     hipError_t ea = allow_lds((const void*)(actf ? k_moe_gate_up<WT, AT, 1> : k_moe_gate_up<WT, AT, 0>),
                               (int)lds_gu);
     if (ea != hipSuccess) return ea;
   }
   if (actf == 0)
-    launch((k_moe_gate_up<WT, AT, 0>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M);
+    launch((k_moe_gate_up<WT, AT, 0>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M,
+           mr);
   else
-    launch((k_moe_gate_up<WT, AT, 1>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    launch((k_moe_gate_up<WT, AT, 1>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M,
+           mr);
+  return hipGetLastError();
+}
+
+template <int WT, int AT>
+static hipError_t moe_down_fmt(int pt, const void* Wd, const void* Sd, int d, int Fr, int E,
+                               int top_k, int T, const int32_t* ids, const float* wts,
+                               const void* M, void* P, hipStream_t st, const FuseArgs* fuse) {
+  const int np = top_k * Fr;
   const dim3 gd((d + 4 * MOE_DR - 1) / (4 * MOE_DR), T);
   const size_t lds_d = (size_t)np * sizeof(float);
+  const char* wd = (const char*)Wd;
+  const uint16_t* sd = (const uint16_t*)Sd;
   if (pt == ACT_F32)
     return moe_down_variant<WT, AT, ACT_F32>(gd, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M,
                                              P, fuse);
   return moe_down_variant<WT, AT, ACT_BF16>(gd, lds_d, st, wd, sd, d, Fr, E, top_k, ids, wts, M, P,
                                             fuse);
+}
+
+template <int WT, int AT>
+static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, const void* Wu,
+                              const void* Su, const void* Wd, const void* Sd, int d, int Fr, int E,
+                              int top_k, int T, const int32_t* ids, const float* wts,
+                              const void* X, void* M, void* P, hipStream_t st,
+                              const FuseArgs* fuse) {
+  hipError_t e = moe_gate_up_fmt<WT, AT>(actf, Wg, Sg, Wu, Su, d, Fr, E, top_k, T, ids, X, M,
+                                         MoeRanks{}, st);
+  if (e != hipSuccess) return e;
+  return moe_down_fmt<WT, AT>(pt, Wd, Sd, d, Fr, E, top_k, T, ids, wts, M, P, st, fuse);
+}
+
+hipError_t launch_moe_gate_up_ranks(int wt, int at, int actf, int d, int Fr, int E, int top_k,
+                                    int T, const int32_t* ids, const void* X, const MoeRanks& mr,
+                                    hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (mr.n < 1 || mr.n > kMaxRanks) return hipErrorInvalidValue;
+  for (int r = 0; r < mr.n; ++r)
+    if (!mr.wg[r] || !mr.wu[r] || !mr.m[r] || (wt == W_Q8 && (!mr.sg[r] || !mr.su[r])))
+      return hipErrorInvalidValue;
+  if (wt == W_F32 && at == ACT_F32)
+    return moe_gate_up_fmt<W_F32, ACT_F32>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr, E,
+                                           top_k, T, ids, X, mr.m[0], mr, st);
+  if (wt == W_BF16 && at == ACT_BF16)
+    return moe_gate_up_fmt<W_BF16, ACT_BF16>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr,
+                                             E, top_k, T, ids, X, mr.m[0], mr, st);
+  if (wt == W_Q8 && at == ACT_BF16)
+    return moe_gate_up_fmt<W_Q8, ACT_BF16>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr, E,
+                                           top_k, T, ids, X, mr.m[0], mr, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_moe_down(int wt, int at, int pt, const void* Wd, const void* Sd, int d, int Fr,
+                           int E, int top_k, int T, const int32_t* ids, const float* wts,
+                           const void* M, void* P, hipStream_t st, const FuseArgs* fuse) {
+  if (T <= 0) return hipSuccess;
+  if (fuse && (!fuse->res_in || !fuse->res_out || fuse->n_prev < 0 ||
+               fuse->n_prev > kMaxPrevPartials || (fuse->n_prev > 0 && !fuse->prev)))
+    return hipErrorInvalidValue;
+  if (wt == W_F32 && at == ACT_F32)
+    return moe_down_fmt<W_F32, ACT_F32>(pt, Wd, Sd, d, Fr, E, top_k, T, ids, wts, M, P, st, fuse);
+  if (wt == W_BF16 && at == ACT_BF16)
+    return moe_down_fmt<W_BF16, ACT_BF16>(pt, Wd, Sd, d, Fr, E, top_k, T, ids, wts, M, P, st,
+                                          fuse);
+  if (wt == W_Q8 && at == ACT_BF16)
+    return moe_down_fmt<W_Q8, ACT_BF16>(pt, Wd, Sd, d, Fr, E, top_k, T, ids, wts, M, P, st, fuse);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, const void* Sg,

@@ -1679,13 +1679,52 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
                                    stream))
       return s;
   }
+  tpk::FuseArgs fout{};
+  fout.prev = partials;
+  fout.part_stride = pstride;
+  fout.n_prev = N - 1;
+  fout.res_in = h1;
+  fout.res_out = out;
+  // With room for every rank's expert activations in moe_workspace, a decode step runs the
+  // ranks' expert gate/up projections as one launch (each block's work that of its rank's own
+  // launch), then each rank's down; the last one adds the partials and the residual.
+  uint64_t mws = 0;
+  tp_moe_workspace_size(desc, moe, T, &mws);
+  if (fused && N > 1 && moe_workspace && aligned16(moe_workspace) &&
+      moe_workspace_bytes >= (uint64_t)N * mws) {
+    for (int r = 0; r < N; ++r)
+      if (!moe_shards[r] || !aligned16(moe_shards[r]))
+        return fail(TP_ERR_INVALID_ARG, "moe shard %d is NULL or not 16-byte aligned", r);
+    tp_moe_layout L;
+    make_moe_layout(x, m, &L);
+    const int wt = x.wt == TP_DTYPE_F32 ? tpk::W_F32 : (x.wt == TP_DTYPE_BF16 ? tpk::W_BF16 : tpk::W_Q8);
+    const int at = x.at == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+    const int pt = x.pt == TP_DTYPE_F32 ? tpk::ACT_F32 : tpk::ACT_BF16;
+    hipStream_t st = (hipStream_t)stream;
+    tpk::MoeRanks mr{};
+    mr.n = N;
+    for (int r = 0; r < N; ++r) {
+      const char* sh = (const char*)moe_shards[r];
+      mr.wg[r] = sh + L.gate.offset;
+      mr.sg[r] = sh + L.gate_scale.offset;
+      mr.wu[r] = sh + L.up.offset;
+      mr.su[r] = sh + L.up_scale.offset;
+      mr.m[r] = (char*)moe_workspace + (size_t)r * mws;
+    }
+    hipError_t e = tpk::launch_moe_gate_up_ranks(wt, at, x.actf, x.d, m.fr, m.E, m.k, T,
+                                                 topk_ids, xn2, mr, st);
+    if (e != hipSuccess) return hip_fail(e, "moe gate/up (all ranks)");
+    for (int r = 0; r < N; ++r) {
+      const char* sh = (const char*)moe_shards[r];
+      e = tpk::launch_moe_down(wt, at, pt, sh + L.down.offset, sh + L.down_scale.offset, x.d,
+                               m.fr, m.E, m.k, T, topk_ids, topk_weights, mr.m[r], part(r), st,
+                               r == N - 1 ? &fout : nullptr);
+      if (e != hipSuccess) return hip_fail(e, "moe down");
+    }
+    g_err.clear();
+    return TP_OK;
+  }
   for (int r = 0; r < N; ++r) {
-    tpk::FuseArgs fout{};
-    fout.prev = partials;
-    fout.part_stride = pstride;
-    fout.n_prev = N - 1;
-    fout.res_in = h1;
-    fout.res_out = out;
     if (tp_status s = moe_forward_impl(desc, moe, r, moe_shards[r], xn2, T, topk_ids, topk_weights,
                                        part(r), moe_workspace, moe_workspace_bytes, stream,
                                        nullptr, nullptr, fused && r == N - 1 ? &fout : nullptr))

@@ -144,6 +144,25 @@ hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, cons
                           int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
                           const void* X, void* M, void* P, hipStream_t st,
                           const FuseArgs* fuse = nullptr);
+// Per-rank operands of the MoE expert gate/up of every rank in one launch (blockIdx.z = rank):
+// the rank's gate and up slices (wg, wu; Q8_0 scales sg, su) and its output m [T][top_k * Fr].
+struct MoeRanks {
+  int n;
+  const void* wg[kMaxRanks];
+  const void* sg[kMaxRanks];
+  const void* wu[kMaxRanks];
+  const void* su[kMaxRanks];
+  void* m[kMaxRanks];
+};
+// The two halves of launch_moe_ffn on their own: the gate/up of every rank in mr (each block's
+// work exactly that of the rank's own launch) and one rank's down (with the reduce epilogue when
+// `fuse` is given).
+hipError_t launch_moe_gate_up_ranks(int wt, int at, int actf, int d, int Fr, int E, int top_k,
+                                    int T, const int32_t* ids, const void* X, const MoeRanks& mr,
+                                    hipStream_t st);
+hipError_t launch_moe_down(int wt, int at, int pt, const void* Wd, const void* Sd, int d, int Fr,
+                           int E, int top_k, int T, const int32_t* ids, const float* wts,
+                           const void* M, void* P, hipStream_t st, const FuseArgs* fuse);
 
 // k_reduce.hip
 hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,
