@@ -395,8 +395,11 @@ tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_des
  * of N entries. Buffers as in tp_block_step and tp_moe_route; workspace: tp_step_workspace_size
  * bytes, moe_workspace: at least tp_moe_workspace_size bytes (16-byte aligned); with N times
  * that, a decode step whose norms and reduces are folded runs every rank's expert gate/up
- * projection as one launch (rank r's activations in the r-th share; each block's work exactly
- * that of the rank's own launch, so the results are the same bits). n_tokens == 0 is a no-op. */
+ * projection as one launch (rank r's activations in the r-th share), and, for at most four
+ * ranks whose activations fit one workgroup's LDS, every rank's expert down as one launch whose
+ * workgroups add the ranks' partials in rank order and the residual; each rank's sums are those
+ * of its own launch and every partial is still stored, so the results are the same bits.
+ * n_tokens == 0 is a no-op. */
 tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
                             const void* const* shards, const void* const* moe_shards,
                             const tp_batch* batch, const tp_kv_cache* kv, const void* x,

@@ -369,6 +369,116 @@ __global__ __launch_bounds__(256) void k_moe_down(const char* __restrict__ Wd,
   }
 }
 
+// The down of every rank in one launch (at most four ranks, NR dividing four): wave w serves
+// rank w % NR for the MOE_DR rows of row group w / NR, with the rank's activations staged in LDS
+// beside the other ranks'; the partials go to memory at their stored precision and to LDS, and
+// the rank-0 wave of each row group adds them in rank order, then the residual.
+template <int WT, int AT, int PT>
+__global__ __launch_bounds__(256) void k_moe_down_ranks(int d, int Fr, int E, int top_k,
+                                                        const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ wts,
+                                                        MoeRanks mr,
+                                                        const void* __restrict__ res,
+                                                        void* __restrict__ out) {
+  extern __shared__ float ms[];  // [NR][top_k * Fr]
+  __shared__ int s_e[kMoeMaxTopK];
+  __shared__ float s_w[kMoeMaxTopK];
+  __shared__ float s_part[4][MOE_DR];  // [wave][row]
+  constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.y;
+  const int NR = mr.n, RG = 4 / NR;
+  const int np = top_k * Fr, chF = Fr / VE, nblk = Fr / 32, nq = top_k * chF;
+  for (int r = 0; r < NR; ++r)
+    for (int i = tid * AV; i < np; i += 256 * AV)
+      Vec16<AT>::load((const char*)mr.m[r] + ((size_t)t * np + i) * (AT == ACT_F32 ? 4 : 2),
+                      ms + (size_t)r * np + i);
+  if (tid < top_k) {
+    int e = ids[(size_t)t * top_k + tid];
+    s_e[tid] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    s_w[tid] = wts[(size_t)t * top_k + tid];
+  }
+  __syncthreads();
+  const int rk = wave % NR, g = wave / NR;
+  const bool active = g < RG;  // NR = 3 leaves the fourth wave idle
+  const int n0 = (blockIdx.x * RG + (active ? g : 0)) * MOE_DR;
+  const char* Wd = (const char*)mr.wd[rk];
+  const uint16_t* Sd = (const uint16_t*)mr.sd[rk];
+  const float* msr = ms + (size_t)rk * np;
+  int nrow[MOE_DR];
+#pragma unroll
+  for (int s = 0; s < MOE_DR; ++s) nrow[s] = n0 + s < d ? n0 + s : d - 1;
+  float acc[MOE_DR];
+#pragma unroll
+  for (int s = 0; s < MOE_DR; ++s) acc[s] = 0.f;
+  if (active && n0 < d) {
+    for (int q0 = 0; q0 < nq; q0 += 64 * MOE_DU) {
+      uint4 b[MOE_DU][MOE_DR];
+      int jj[MOE_DU], cc[MOE_DU];
+#pragma unroll
+      for (int u = 0; u < MOE_DU; ++u) {
+        const int q = q0 + u * 64 + lane;
+        const bool in = q < nq;
+        jj[u] = in ? q / chF : 0;
+        cc[u] = in ? q - jj[u] * chF : 0;
+#pragma unroll
+        for (int s = 0; s < MOE_DR; ++s) {
+          const size_t row = (size_t)s_e[jj[u]] * d + nrow[s];
+          b[u][s] = in ? ld_stream16(Wd + (row * Fr + (size_t)cc[u] * VE) * WB)
+                       : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MOE_DU; ++u) {
+        const int q = q0 + u * 64 + lane;
+        if (q >= nq) continue;
+        const float wj = s_w[jj[u]];
+        const float* mp = msr + jj[u] * Fr + cc[u] * VE;
+#pragma unroll
+        for (int s = 0; s < MOE_DR; ++s) {
+          const size_t row = (size_t)s_e[jj[u]] * d + nrow[s];
+          acc[s] = fmaf(wj, moe_dot<WT>(b[u][s], moe_scale<WT>(Sd, row, nblk, cc[u] * VE / 16), mp),
+                        acc[s]);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < MOE_DR; ++s) acc[s] = wave_sum(acc[s]);
+    if (lane == 0) {
+#pragma unroll
+      for (int s = 0; s < MOE_DR; ++s) {
+        float p = acc[s];
+        if (n0 + s < d) {
+          const size_t o = (size_t)t * d + n0 + s;
+          if constexpr (PT == ACT_F32) {
+            ((float*)mr.p[rk])[o] = p;
+          } else {
+            const uint16_t bb = f32_to_bf16(p);
+            ((uint16_t*)mr.p[rk])[o] = bb;
+            p = bf16_to_f32(bb);
+          }
+        }
+        s_part[wave][s] = p;
+      }
+    }
+  }
+  __syncthreads();
+  if (active && rk == 0 && lane == 0 && n0 < d) {
+#pragma unroll
+    for (int s = 0; s < MOE_DR; ++s) {
+      if (n0 + s >= d) continue;
+      const size_t o = (size_t)t * d + n0 + s;
+      float sum = s_part[wave][s];
+      for (int r = 1; r < NR; ++r) sum += s_part[wave + r][s];
+      st_act<AT>(out, o, ld_act<AT>(res, o) + sum);
+    }
+  }
+}
+
+bool moe_down_ranks_fit(int n_ranks, int top_k, int Fr) {
+  return n_ranks >= 1 && n_ranks <= 4 && (size_t)n_ranks * top_k * Fr * sizeof(float) <= 160 * 1024;
+}
+
 template <int WT, int AT, int PT, int PV>
 static hipError_t moe_down_launch(dim3 g, size_t lds, hipStream_t st, const char* wd,
                                   const uint16_t* sd, int d, int Fr, int E, int top_k,
@@ -486,6 +596,44 @@ hipError_t launch_moe_down(int wt, int at, int pt, const void* Wd, const void* S
                                           fuse);
   if (wt == W_Q8 && at == ACT_BF16)
     return moe_down_fmt<W_Q8, ACT_BF16>(pt, Wd, Sd, d, Fr, E, top_k, T, ids, wts, M, P, st, fuse);
+  return hipErrorInvalidValue;
+}
+
+template <int WT, int AT>
+static hipError_t moe_down_ranks_fmt(int pt, int d, int Fr, int E, int top_k, int T,
+                                     const int32_t* ids, const float* wts, const MoeRanks& mr,
+                                     const void* res, void* out, hipStream_t st) {
+  const int rg = 4 / mr.n;
+  const dim3 g((d + rg * MOE_DR - 1) / (rg * MOE_DR), T), b(256);
+  const size_t lds = (size_t)mr.n * top_k * Fr * sizeof(float);
+  const void* kern = pt == ACT_F32 ? (const void*)k_moe_down_ranks<WT, AT, ACT_F32>
+                                   : (const void*)k_moe_down_ranks<WT, AT, ACT_BF16>;
+  if (lds > 65536) {
+    hipError_t ea = allow_lds(kern, (int)lds);
+    if (ea != hipSuccess) return ea;
+  }
+  if (pt == ACT_F32)
+    launch((k_moe_down_ranks<WT, AT, ACT_F32>), g, b, (uint32_t)lds, st, d, Fr, E, top_k, ids,
+           wts, mr, res, out);
+  else
+    launch((k_moe_down_ranks<WT, AT, ACT_BF16>), g, b, (uint32_t)lds, st, d, Fr, E, top_k, ids,
+           wts, mr, res, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_down_ranks(int wt, int at, int pt, int d, int Fr, int E, int top_k, int T,
+                                 const int32_t* ids, const float* wts, const MoeRanks& mr,
+                                 const void* res, void* out, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (!moe_down_ranks_fit(mr.n, top_k, Fr) || !res || !out) return hipErrorInvalidValue;
+  for (int r = 0; r < mr.n; ++r)
+    if (!mr.wd[r] || !mr.m[r] || !mr.p[r] || (wt == W_Q8 && !mr.sd[r])) return hipErrorInvalidValue;
+  if (wt == W_F32 && at == ACT_F32)
+    return moe_down_ranks_fmt<W_F32, ACT_F32>(pt, d, Fr, E, top_k, T, ids, wts, mr, res, out, st);
+  if (wt == W_BF16 && at == ACT_BF16)
+    return moe_down_ranks_fmt<W_BF16, ACT_BF16>(pt, d, Fr, E, top_k, T, ids, wts, mr, res, out, st);
+  if (wt == W_Q8 && at == ACT_BF16)
+    return moe_down_ranks_fmt<W_Q8, ACT_BF16>(pt, d, Fr, E, top_k, T, ids, wts, mr, res, out, st);
   return hipErrorInvalidValue;
 }
 

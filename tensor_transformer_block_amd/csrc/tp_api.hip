@@ -1714,6 +1714,20 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
     hipError_t e = tpk::launch_moe_gate_up_ranks(wt, at, x.actf, x.d, m.fr, m.E, m.k, T,
                                                  topk_ids, xn2, mr, st);
     if (e != hipSuccess) return hip_fail(e, "moe gate/up (all ranks)");
+    if (tpk::moe_down_ranks_fit(N, m.k, m.fr)) {
+      // Every rank's down in one launch, the reduce in it (as the last rank's down adds it).
+      for (int r = 0; r < N; ++r) {
+        const char* sh = (const char*)moe_shards[r];
+        mr.wd[r] = sh + L.down.offset;
+        mr.sd[r] = sh + L.down_scale.offset;
+        mr.p[r] = part(r);
+      }
+      e = tpk::launch_moe_down_ranks(wt, at, pt, x.d, m.fr, m.E, m.k, T, topk_ids, topk_weights,
+                                     mr, h1, out, st);
+      if (e != hipSuccess) return hip_fail(e, "moe down (all ranks)");
+      g_err.clear();
+      return TP_OK;
+    }
     for (int r = 0; r < N; ++r) {
       const char* sh = (const char*)moe_shards[r];
       e = tpk::launch_moe_down(wt, at, pt, sh + L.down.offset, sh + L.down_scale.offset, x.d,

@@ -144,25 +144,38 @@ hipError_t launch_moe_ffn(int wt, int at, int actf, int pt, const void* Wg, cons
                           int Fr, int E, int top_k, int T, const int32_t* ids, const float* wts,
                           const void* X, void* M, void* P, hipStream_t st,
                           const FuseArgs* fuse = nullptr);
-// Per-rank operands of the MoE expert gate/up of every rank in one launch (blockIdx.z = rank):
-// the rank's gate and up slices (wg, wu; Q8_0 scales sg, su) and its output m [T][top_k * Fr].
+// Per-rank operands of the MoE expert projections of every rank in one launch: the rank's gate,
+// up and down slices (wg, wu, wd; Q8_0 scales sg, su, sd), its expert activations m
+// [T][top_k * Fr] and its partial p [T][d].
 struct MoeRanks {
   int n;
   const void* wg[kMaxRanks];
   const void* sg[kMaxRanks];
   const void* wu[kMaxRanks];
   const void* su[kMaxRanks];
+  const void* wd[kMaxRanks];
+  const void* sd[kMaxRanks];
   void* m[kMaxRanks];
+  void* p[kMaxRanks];
 };
-// The two halves of launch_moe_ffn on their own: the gate/up of every rank in mr (each block's
-// work exactly that of the rank's own launch) and one rank's down (with the reduce epilogue when
-// `fuse` is given).
+// The two halves of launch_moe_ffn on their own: the gate/up of every rank in mr (blockIdx.z =
+// rank; each block's work exactly that of the rank's own launch) and one rank's down (with the
+// reduce epilogue when `fuse` is given).
 hipError_t launch_moe_gate_up_ranks(int wt, int at, int actf, int d, int Fr, int E, int top_k,
                                     int T, const int32_t* ids, const void* X, const MoeRanks& mr,
                                     hipStream_t st);
 hipError_t launch_moe_down(int wt, int at, int pt, const void* Wd, const void* Sd, int d, int Fr,
                            int E, int top_k, int T, const int32_t* ids, const float* wts,
                            const void* M, void* P, hipStream_t st, const FuseArgs* fuse);
+// The down of every rank in mr (at most four, dividing four) in one launch with the reduce in
+// it: a workgroup's waves take the same output rows for different ranks, each wave's sums
+// exactly as in its rank's own launch; every partial is stored at mr.p[r], and out = res +
+// (((P_0 + P_1) + ...) + P_{n-1}) with the partials at their stored precision, the reduce
+// kernel's arithmetic. moe_down_ranks_fit: whether every rank's activations fit the LDS.
+bool moe_down_ranks_fit(int n_ranks, int top_k, int Fr);
+hipError_t launch_moe_down_ranks(int wt, int at, int pt, int d, int Fr, int E, int top_k, int T,
+                                 const int32_t* ids, const float* wts, const MoeRanks& mr,
+                                 const void* res, void* out, hipStream_t st);
 
 // k_reduce.hip
 hipError_t launch_partial_reduce(int act, int part, int T, int d, const void* partials, int n,

@@ -630,8 +630,9 @@ def test_moe_one_call_step(s, moe):
         acc = acc + b.partials[r].float().cpu()
     want = (b.h1.float().cpu() + acc).to(tdt)
     assert torch.equal(want.view(torch.uint8), b.out.cpu().view(torch.uint8))
-    # With one rank's expert workspace the step runs each rank's gate/up on its own; with every
-    # rank's share (above) a decode step runs them as one launch: the same bits.
+    # With one rank's expert workspace the step runs each rank's expert gate/up and down on its
+    # own; with every rank's share (above) a decode step runs the gate/up of every rank as one
+    # launch and the down of every rank, reduce included, as another: the same bits.
     if s.mode == "decode" and s.tp > 1:
         snap = {k: getattr(b, k).clone() for k in ("out", "partials")}
         b.out.fill_(float("nan"))
