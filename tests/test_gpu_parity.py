@@ -522,6 +522,10 @@ MOE_GPU = [(CONFIGS["tiny-llama-fp32"].with_(name="tiny-moe-gpu", index=230, kv_
             MoEShape(8, 2, 256)),
            (MED.with_(name="med-moe-prefill", index=233, mode="prefill", kv_lens=(60,),
                       n_tokens=40), MoEShape(16, 4, 256)),
+           # Four ranks: the one-call step's expert down of every rank in one launch, one wave
+           # per rank for each row pair.
+           (MED.with_(name="med-moe-n4", index=235, tp=4, n_kv_heads=4, ffn_dim=1408),
+            MoEShape(16, 4, 256)),
            MOE_WORKLOADS["moe-decode"]]
 
 
