@@ -526,6 +526,9 @@ MOE_GPU = [(CONFIGS["tiny-llama-fp32"].with_(name="tiny-moe-gpu", index=230, kv_
            # per rank for each row pair.
            (MED.with_(name="med-moe-n4", index=235, tp=4, n_kv_heads=4, ffn_dim=1408),
             MoEShape(16, 4, 256)),
+           (BY_NAME["med-q8-n4"].with_(name="med-moe-q8-n4", index=236), MoEShape(8, 2, 256)),
+           (CONFIGS["tiny-llama-fp32"].with_(name="tiny-moe-n4", index=237, tp=4, ffn_dim=704,
+                                             kv_lens=(16, 5), n_tokens=2), MoEShape(8, 2, 64)),
            MOE_WORKLOADS["moe-decode"]]
 
 
