@@ -50,7 +50,8 @@ hipError_t launch_gemv(int wt, int at, int epi, int actf, int T, const void* W, 
 static size_t ranks_lds(int wt, int epi, int n_ranks, int T, int K) {
   const bool allr = epi == EPI_RED_ALL || epi == EPI_RED_ALL_BF;
   const size_t xb = (allr && wt != W_F32) ? 2 : 4;  // bf16 rows stay bf16 there
-  const size_t one = (size_t)T * K * xb + (wt == W_Q8 ? (size_t)T * (K / 16) * 4 : 0);
+  // Q8_0: fp16 rows and an (offset, 1 / scale) pair per 16 values.
+  const size_t one = wt == W_Q8 ? (size_t)T * K * 2 + (size_t)T * (K / 16) * 8 : (size_t)T * K * xb;
   return (allr ? (size_t)n_ranks : 1) * one;
 }
 

@@ -2,16 +2,21 @@
 //
 // Decode reads every byte of a rank's 1/N weight slice once per step and does ~1 FLOP per byte,
 // so these kernels are HBM-streaming GEMVs, not GEMMs. A wavefront owns R weight rows and streams
-// them with 16-byte loads, U per row and lane in flight (R * U = 16 loads per lane), R chosen by
-// row length so short rows (o_proj, Q8_0) still keep enough bytes in flight. The first batch of
-// loads is issued before the token vectors are staged in LDS (as fp32), so the two latencies
+// them with 16-byte loads, U per row and lane in flight (R * U = 16 loads per lane, 12 for Q8_0),
+// R chosen by row length so short rows (o_proj, Q8_0) still keep enough bytes in flight. The first
+// batch of loads is issued before the token vectors are staged in LDS, so the two latencies
 // overlap. Dot products finish with DPP row reductions.
 //
 // Weight formats: fp32, bf16, and Q8_0 split into an int8 code plane [out, in] plus an fp16 scale
-// plane [out, in/32]. A Q8_0 chunk of 16 codes is taken as sum_k scale * c_k * x_k =
-// scale * (sum_k (c_k + 128) x_k - 128 sum_k x_k): flipping each code's sign bit gives the byte
-// c_k + 128, which converts to fp32 in one instruction, and the chunk's sum of x comes staged with
-// x, so a code costs one conversion and one FMA and the scale one multiply per chunk.
+// plane [out, in/32]. For Q8_0 the token rows are staged as fp16, each chunk of 16 values scaled
+// by its own power of two (largest magnitude in [2^14, 2^15)): bf16 values fit fp16's 11-bit
+// significand exactly, and the prologue's gamma * x is rounded once to it. A code c becomes the
+// fp16 number 1152 + c with one byte permute per two codes (its sign bit flipped gives the byte
+// c + 128, placed under the exponent of 1024), and the chunk is
+// sum_k c_k x_k = sum_k (1152 + c_k) x_k - 1152 sum_k x_k, eight two-term fp16 dot products with
+// fp32 accumulation (the products are exact in fp32) and the staged offset. A code costs one
+// instruction instead of a conversion and an FMA, which matters here: the weight bytes are a
+// quarter of fp32's per value, so the arithmetic per byte is four times the fp32 path's.
 // Epilogues:
 //   EPI_F32 / EPI_BF16   store a partial sum (row-parallel o_proj and down, TensorSharp "How
 //             tensor parallelism works", step 3);
@@ -70,6 +75,33 @@ __device__ __forceinline__ void decode_chunk(const uint4& raw, float scale, floa
   }
 }
 
+typedef _Float16 q8h2 __attribute__((ext_vector_type(2)));
+
+// Stage one chunk of 16 activations for the Q8_0 inner product: the values times a power of two
+// that puts the largest magnitude in [2^14, 2^15) (2^127 for an all-zero or subnormal chunk, so
+// the scale stays a finite float), rounded to fp16, and the pair (1152 * sum of the fp16 values,
+// 1 / scale) that turns a chunk's dot product with the codes' 1152 + c back into sum c x.
+__device__ __forceinline__ void q8_stage_chunk(const float* v, uint16_t* dst, float2* meta) {
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  const int eb = (int)((__float_as_uint(amax) >> 23) & 0xffu);  // amax in [2^(eb-127), 2^(eb-126))
+  const int sb = 268 - eb > 254 ? 254 : 268 - eb;                // scale 2^(141 - eb)
+  const float sc = __uint_as_float((uint32_t)sb << 23), inv = 1.0f / sc;
+  uint32_t h[8];
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    const _Float16 a = (_Float16)(v[e] * sc), b = (_Float16)(v[e + 1] * sc);
+    sum += (float)a + (float)b;
+    h[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  *(uint4*)dst = make_uint4(h[0], h[1], h[2], h[3]);
+  *(uint4*)(dst + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+  *meta = make_float2(1152.f * sum * inv, inv);
+}
+
 __device__ __forceinline__ int clampi_g(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
@@ -92,21 +124,26 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
                                               int gate_off, const void* __restrict__ X,
                                               void* __restrict__ Y, int ldy, RopeEpi re,
                                               FuseArgs fa, RankPtrs rp) {
-  // [NR][NT][K] staged token rows (NR ranks' inputs under EPI_RED_ALL*, else one; fp32, or as
-  // stored when EPI_RED_ALL* takes bf16 rows, which halves the workgroup's LDS), then (Q8_0)
-  // [NR][NT][K / 16] fp32 chunk sums of x
+  // [NR][NT][K] staged token rows (NR ranks' inputs under EPI_RED_ALL*, else one): fp32, or as
+  // stored when EPI_RED_ALL* takes bf16 rows (which halves the workgroup's LDS); Q8_0 weights
+  // take fp16 rows and then [NR][NT][K / 16] (offset, 1 / scale) pairs
   extern __shared__ float xs[];
   __shared__ float red[PRO ? NT : 1][4];  // prologue norm: each wave's sum of squares per token
   constexpr int VE = WFmt<WT>::VE;
   constexpr int WB = WFmt<WT>::WB;
   constexpr int AV = Vec16<AT>::N;
-  constexpr int U = 16 / R;
+  // Q8_0: 12 chunks per lane in flight (three per row at four rows, enough for 3072-wide rows
+  // in one batch), which keeps four waves per SIMD.
+  constexpr int U = WT == W_Q8 ? (R >= 8 ? 2 : 12 / R) : 16 / R;
+  static_assert(WT != W_Q8 || AT == ACT_BF16, "Q8_0 weights take bf16 activations");
   constexpr bool PAIRED = (EPI == EPI_GATED || EPI == EPI_ROPE);
   static_assert(!PAIRED || R % 2 == 0, "paired epilogues need an even number of rows");
   constexpr bool ALLR = (EPI == EPI_RED_ALL || EPI == EPI_RED_ALL_BF);
   constexpr bool XS16 = ALLR && AT == ACT_BF16;  // bf16 rows in LDS, widened (exactly) on use
   uint16_t* const xs16 = (uint16_t*)xs;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: with it in a scalar register, each weight row's base address is
+  // too, and the loads take a 32-bit lane offset instead of a 64-bit address per lane.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // A column-parallel launch over all ranks: this block's rank and its pointers.
   int blk = blockIdx.x;
   if constexpr (!ALLR) {
@@ -244,7 +281,44 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
     }
   }
 
-  if constexpr (PRO) {
+  // Q8_0: [NR][NT][K] fp16 token rows, then [NR][NT][K / 16] (offset, 1 / scale) per chunk.
+  uint16_t* const xh = (uint16_t*)xs;
+  float2* const xc = (float2*)(xh + (size_t)NR * NT * K);
+  if constexpr (WT == W_Q8) {
+    float ssq[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ssq[t] = 0.f;
+    for (int i = tid; i < NR * NT * nch; i += 256) {
+      const int rt = i / nch, c = i - rt * nch;  // chunk c of token row rt = r * NT + t
+      const int r = rt / NT, t = rt - r * NT;
+      const uint16_t* xr = (const uint16_t*)(ALLR ? rp.x[r] : X) + (size_t)t * K + (size_t)c * 16;
+      float v[16];
+      Vec16<ACT_BF16>::load(xr, v);
+      Vec16<ACT_BF16>::load(xr + 8, v + 8);
+      if constexpr (PRO) {
+        float g[16];
+        Vec16<ACT_BF16>::load((const uint16_t*)fa.gamma + (size_t)c * 16, g);
+        Vec16<ACT_BF16>::load((const uint16_t*)fa.gamma + (size_t)c * 16 + 8, g + 8);
+        float q = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          q = fmaf(v[e], v[e], q);
+          v[e] *= g[e];
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          if (tt == t) ssq[tt] += q;
+      }
+      q8_stage_chunk(v, xh + (size_t)i * 16, xc + i);
+    }
+    if constexpr (PRO) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float w = wave_sum(ssq[t]);
+        if (lane == 0) red[t][wave] = w;
+      }
+    }
+  } else if constexpr (PRO) {
     // gamma * x and the squares of x from one load of each; per token, a wave sum per wave.
     constexpr int EB = AT == ACT_F32 ? 4 : 2;
     float ssq[NT];
@@ -302,29 +376,6 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
   };
-  float* const xq = XS16 ? (float*)(xs16 + (size_t)NR * NT * K) : xs + (size_t)NR * NT * K;
-  if constexpr (WT == W_Q8) {
-    __syncthreads();
-    for (int i = tid; i < NR * NT * nch; i += 256) {
-      // chunk i % nch of row i / nch (nch = K / 16)
-      float a = 0.f;
-      if constexpr (XS16) {
-        float v[16];
-        xget8((size_t)i * 16, v);
-        xget8((size_t)i * 16 + 8, v + 8);
-#pragma unroll
-        for (int e = 0; e < 16; e += 4) a += (v[e] + v[e + 1]) + (v[e + 2] + v[e + 3]);
-      } else {
-        const float* xp = xs + (size_t)i * 16;
-#pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-          const float4 v = *(const float4*)(xp + e);
-          a += (v.x + v.y) + (v.z + v.w);
-        }
-      }
-      xq[i] = a;
-    }
-  }
   __syncthreads();
   float inv[PRO ? NT : 1];
   if constexpr (PRO) {
@@ -336,8 +387,12 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
     if (fa.normed_out != nullptr && blockIdx.x == 0) {  // the normed rows, for the caller
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        for (int k = tid; k < K; k += 256)
-          st_act<AT>(fa.normed_out, (size_t)t * K + k, xs[(size_t)t * K + k] * inv[t]);
+        for (int k = tid; k < K; k += 256) {
+          // (Q8_0 staged fp16: gamma * x again from its inputs, in the same fp32 product.)
+          const float v = WT == W_Q8 ? ld_act<AT>(X, (size_t)t * K + k) * ld_act<AT>(fa.gamma, k)
+                                     : xs[(size_t)t * K + k];
+          st_act<AT>(fa.normed_out, (size_t)t * K + k, v * inv[t]);
+        }
     }
   }
   if (!ALLR && !active) return;
@@ -349,7 +404,6 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
   if (!ALLR || active) {
   const int rk = rk0;
   const float* const xsr = xs + (size_t)rk * NT * K;
-  const float* const xqr = xq + (size_t)rk * NT * nch;
 #pragma unroll
   for (int s = 0; s < R; ++s)
 #pragma unroll
@@ -364,32 +418,27 @@ __global__ __launch_bounds__(256) void k_gemv(const void* __restrict__ W,
 #pragma unroll
         for (int s = 0; s < R; ++s) {
           if constexpr (WT == W_Q8) {
+            // Codes as fp16 1152 + c, two per word: sign bits flipped, then each byte under 0x64.
             const uint32_t r4[4] = {b[s][u].x ^ 0x80808080u, b[s][u].y ^ 0x80808080u,
                                     b[s][u].z ^ 0x80808080u, b[s][u].w ^ 0x80808080u};
+            q8h2 wh[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              wh[2 * i] = __builtin_bit_cast(q8h2, __builtin_amdgcn_perm(0x64646464u, r4[i], 0x04010400u));
+              wh[2 * i + 1] =
+                  __builtin_bit_cast(q8h2, __builtin_amdgcn_perm(0x64646464u, r4[i], 0x04030402u));
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              float xv[16];
-              if constexpr (XS16) {
-                const size_t e0 = ((size_t)rk * NT + t) * K + (size_t)c * VE;
-                xget8(e0, xv);
-                xget8(e0 + 8, xv + 8);
-              } else {
-                const float* xp = xsr + t * K + c * VE;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const float4 q = *(const float4*)(xp + 4 * i);
-                  xv[4 * i] = q.x; xv[4 * i + 1] = q.y; xv[4 * i + 2] = q.z; xv[4 * i + 3] = q.w;
-                }
-              }
+              const size_t e0 = ((size_t)rk * NT + t) * K + (size_t)c * 16;
+              const uint4 xa = *(const uint4*)(xh + e0), xb = *(const uint4*)(xh + e0 + 8);
+              const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
               float d = 0.f;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                d = fmaf((float)(r4[i] & 0xffu), xv[4 * i], d);
-                d = fmaf((float)((r4[i] >> 8) & 0xffu), xv[4 * i + 1], d);
-                d = fmaf((float)((r4[i] >> 16) & 0xffu), xv[4 * i + 2], d);
-                d = fmaf((float)(r4[i] >> 24), xv[4 * i + 3], d);
-              }
-              acc[s][t] = fmaf(sc[s][u], fmaf(-128.f, xqr[t * nch + c], d), acc[s][t]);
+              for (int i = 0; i < 8; ++i)
+                d = __builtin_amdgcn_fdot2(wh[i], __builtin_bit_cast(q8h2, xw[i]), d, false);
+              const float2 m = xc[((size_t)rk * NT + t) * nch + c];
+              acc[s][t] = fmaf(sc[s][u], fmaf(d, m.y, -m.x), acc[s][t]);
             }
           } else {
             float f[VE];
@@ -604,10 +653,12 @@ static hipError_t gemv_nt(int nt, const void* W, const uint16_t* S, int K, int n
   const int rw = 4 / (nr < 4 ? nr : 4);
   const int bpr = ALLR ? (waves + rw - 1) / rw : (waves + 3) / 4;
   const dim3 g(ALLR ? bpr : bpr * nr);
-  // (EPI_RED_ALL* with bf16 rows keeps them as bf16.)
+  // (EPI_RED_ALL* with bf16 rows keeps them as bf16; Q8_0 stages fp16 rows and a pair of floats
+  // per 16 values.)
   const size_t xb = (ALLR && AT == ACT_BF16) ? 2 : sizeof(float);
   const size_t lds = (size_t)(ALLR ? nr : 1) *
-                     ((size_t)nt * K * xb + (WT == W_Q8 ? (size_t)nt * (K / 16) * 4 : 0));
+                     (WT == W_Q8 ? (size_t)nt * K * 2 + (size_t)nt * (K / 16) * 8
+                                 : (size_t)nt * K * xb);
   RankPtrs rq = rp;
   rq.bpr = bpr;
   switch (nt) {
