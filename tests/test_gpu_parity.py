@@ -803,6 +803,59 @@ def test_q8_projection_dequant_bit_exact(name, rank, T):
         assert bad == 0, f"region {which}: {bad} dequantised values differ"
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_q8_gemv_activation_range(T):
+    """The Q8_0 decode GEMV stages each 16-value chunk of the activations as fp16 times a power of
+    two of its own. Rows whose chunks span magnitudes 2^-100 to 2^100, with all-zero chunks among
+    them, through the forward path's projection kernels (tp_shard_project, T tokens per call, every
+    region of the Gemma-like shard's rank 0): the products must equal the oracle's fp64 products of
+    the dequantised weights to 1e-4 of each token's largest output. bf16 values fit fp16's
+    significand, so a chunk's dot product with the codes is exact up to fp32 accumulation, and no
+    chunk is lost to the range of the others (a shared fp16 scale would flush the small ones)."""
+    import oracle
+    from tensor_transformer_block_amd import binding as B
+    from tensor_transformer_block_amd.block import to_device
+    from tensor_transformer_block_amd.inputs import f32_to_bf16_bits
+    s = WORKLOADS["gemma-q8-decode"].with_(mode="decode", n_tokens=1, kv_lens=(1,))
+    if "gemma-q8-decode" not in _Q8_CACHE:
+        _Q8_CACHE.clear()
+        inp = make_inputs(s, seed=0)
+        _Q8_CACHE["gemma-q8-decode"] = (inp, oracle.params_f64(inp))
+    inp, p = _Q8_CACHE["gemma-q8-decode"]
+    desc = B.make_desc(s)
+    full = {k: to_device(v, s.w_dtype, "cuda") for k, v in inp.weights.items()}
+    lay = B.tp_shard_weights_size(desc, 0)
+    shard = torch.empty(lay.alloc_bytes, dtype=torch.uint8, device="cuda")
+    B.tp_shard_weights(desc, 0, B.full_weights(full), shard)
+    del full
+    w = oracle.shard_weights(s, p, 0)
+    regions = {0: np.concatenate([w["wq"], w["wk"], w["wv"]]), 1: w["wo"],
+               2: np.concatenate([w["wg"], w["wu"]]), 3: w["wd"]}
+    rng = np.random.default_rng(31)
+    for which, ref_w in regions.items():
+        rows, K = ref_w.shape
+        nch = K // 16
+        expo = rng.integers(-100, 101, size=(T, nch)).astype(np.float64)
+        expo[:, ::7] = np.nan  # every seventh chunk all zero
+        scale = np.where(np.isnan(expo), 0.0, np.exp2(np.nan_to_num(expo)))
+        x = rng.standard_normal((T, nch, 16)) * scale[:, :, None]
+        xb = f32_to_bf16_bits(x.reshape(T, K).astype(np.float32))
+        x64 = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xt = to_device(xb, "bf16", "cuda")
+        out = torch.full((T, rows), float("nan"), device="cuda")
+        ws = torch.empty(B.tp_shard_project_workspace_size(desc, which, T), dtype=torch.uint8,
+                         device="cuda")
+        B.tp_shard_project(desc, which, shard, xt, T, out, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        ref = x64 @ ref_w.T
+        err = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
+        log(f"q8 activation range region {which} [{rows}x{K}] T={T}: max-abs-rel per token "
+            f"{np.array2string(err, precision=2)}")
+        assert np.isfinite(got).all(), f"region {which}: non-finite outputs"
+        assert err.max() <= 1e-4, f"region {which}: {err.max():.3g}"
+
+
 # Cache slots holding no key: past each sequence's last position, and a page that no sequence owns
 # which the block table's unused entries point at.
 STALE_CASES = ["med-bf16-ragged", "med-bf16-batched-64", "med-bf16-prefill", "med-q8-hd256",
