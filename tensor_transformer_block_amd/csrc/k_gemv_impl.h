@@ -50,7 +50,8 @@ template <> struct WFmt<W_F32> { static constexpr int VE = 4, WB = 4; };
 template <> struct WFmt<W_BF16> { static constexpr int VE = 8, WB = 2; };
 template <> struct WFmt<W_Q8> { static constexpr int VE = 16, WB = 1; };
 
-// Decode one 16-byte weight chunk into VE fp32 values.
+// Decode one 16-byte weight chunk into VE fp32 values (Q8_0: for the MoE expert kernels; the
+// decode GEMV's main loop takes fp16 dot products of Q8_0 chunks instead).
 template <int WT>
 __device__ __forceinline__ void decode_chunk(const uint4& raw, float scale, float* w) {
   const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
