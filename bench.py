@@ -119,10 +119,44 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+def code_text(src):
+    """C++ source without its comments, whitespace runs collapsed: what the compiler sees of it,
+    so that a comment edit does not count as a kernel change."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # string or character literal, kept whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def code_digest(paths, root):
+    """sha256 over the code text of the given sources (repository-relative paths), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(code_text(open(os.path.join(root, p), encoding="utf-8").read()).encode())
+        h.update(b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per gate/up launch from the committed counter summary, or None when there is no
-    summary for this workload or the kernel source changed since the counters were taken."""
-    import hashlib
+    summary for this workload or the kernel's code changed since the counters were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"traffic_gate_up_{workload}.md")
     if not os.path.exists(path):
@@ -133,9 +167,7 @@ def measured_traffic(workload):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     try:
-        srcs = fields["sources"].split()
-        h = hashlib.sha256(b"".join(open(os.path.join(root, p), "rb").read() for p in srcs))
-        if h.hexdigest() != fields["source_sha256"]:
+        if code_digest(fields["sources"].split(), root) != fields["code_sha256"]:
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
