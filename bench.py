@@ -215,6 +215,43 @@ def cpu_baseline(inp, seconds):
             "host": {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}}
 
 
+def bench_vendor_gemm(args, s):
+    """The vendor GEMM library (torch.matmul / torch.bmm in bf16 -> hipBLASLt) on the workload's
+    four projections with every rank in one call: the column-parallel QKV and gate/up as one GEMM
+    over the ranks' stacked weight slices (they share their input), the row-parallel o_proj and
+    down as a batch of N GEMMs (each rank its own input). Random operands; bf16 outputs (the
+    block's own row-parallel launches store fp32 partials, twice the output bytes). One JSON line
+    with the mean time of 20 calls after 3 warm-ups, and the rate against the bf16 dense peak."""
+    import torch
+    T, d, N, hd = s.n_tokens, s.d_model, s.tp, s.head_dim
+    qkv = (s.n_heads + 2 * s.n_kv_heads) * hd // N
+    shapes = [("qkv", 1, T, N * qkv, d), ("o_proj", N, T, d, s.n_heads * hd // N),
+              ("gate_up", 1, T, 2 * s.ffn_dim, d), ("down", N, T, d, s.ffn_dim // N)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    out = []
+    for name, batch, M, Nc, K in shapes:
+        g = torch.Generator(device="cuda").manual_seed(args.seed)
+        a = torch.randn(batch, M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(batch, K, Nc, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+        fn = (lambda: torch.matmul(a[0], b[0])) if batch == 1 else (lambda: torch.bmm(a, b))
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(20):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / 20
+        fl = 2.0 * batch * M * Nc * K
+        out.append({"projection": name, "batch": batch, "m": M, "n": Nc, "k": K, "us": round(us, 1),
+                    "tflops": round(fl / us / 1e6, 1), "frac": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 3)})
+        log(f"vendor GEMM {name}: {us:.1f} us")
+        del a, b
+    print(json.dumps({"vendor_gemm": out, "workload": s.name, "library": "torch.matmul / torch.bmm (hipBLASLt)",
+                      "dtype": "bf16", "peak_tflops": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +276,10 @@ def main():
     ap.add_argument("--staged", action="store_true",
                     help="issue the step as separate per-rank and reduce calls instead of the "
                          "one-call step (tp_block_step)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the step: time the vendor GEMM library (torch.matmul / bmm, "
+                         "bf16, random operands) on the workload's projections with every rank "
+                         "in one call, as a reference rate for the chip")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a dispatch of known "
                          "size for scaling hardware byte counters)")
@@ -275,6 +316,9 @@ def main():
         bench_moe(args, *MOE_WORKLOADS[args.workload])
         return
     s = WORKLOADS[args.workload]
+    if args.vendor_gemm:
+        bench_vendor_gemm(args, s)
+        return
     if args.blocks > 1 or args.head:
         bench_stack(args, s)
         return
