@@ -715,25 +715,27 @@ def bench_moe(args, s, moe):
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / n
 
-    # The dominant kernels: one rank's expert FFN (gate/up and down over the selected experts),
-    # timed inside eager MoE steps (the separate calls) behind a backlog of replays.
-    n_st = max(1, (args.kernel_iters + s.tp - 1) // s.tp)
-    hev = HipEvents(2 * n_st * s.tp)
+    # The dominant kernel: the expert gate/up projection of every rank in one launch (the
+    # selected experts' gate and up slices of all ranks), timed with HIP events the library
+    # records around that launch inside eager one-call steps, behind a backlog of replays.
+    n_st = max(1, args.kernel_iters)
+    hev = HipEvents(2 * n_st)
     for _ in range(min(16, args.steps)):
         multi.replay()
     for i in range(n_st):
-        mb.step(i % copies, moe_events=[(hev.ev[2 * (i * s.tp + r)], hev.ev[2 * (i * s.tp + r) + 1])
-                                        for r in range(s.tp)])
+        mb.step_fused(i % copies, timed=(hev.ev[2 * i], hev.ev[2 * i + 1]))
     torch.cuda.synchronize()
-    kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(n_st * s.tp)]))
+    kavg = float(np.mean([hev.elapsed_s(2 * j, 2 * j + 1) for j in range(n_st)]))
     hev.close()
-    ub = int(s.n_tokens * moe.top_k * 3 * (moe.expert_ffn // s.tp) * d * per
-             + s.n_tokens * d * act_b * 2 + s.n_tokens * moe.top_k * (moe.expert_ffn // s.tp) * act_b * 2)
+    # weights of every rank's gate and up slices of the selected experts, each rank's read of the
+    # normed input, the activations written
+    ub = int(s.n_tokens * moe.top_k * 2 * moe.expert_ffn * d * per + s.tp * s.n_tokens * d * act_b
+             + s.n_tokens * moe.top_k * moe.expert_ffn * act_b)
     roof = {"bound": "hbm", "achieved": round(ub / kavg / 1e9, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    roof["kernel"] = "expert FFN of one rank (gate/up + down over the selected experts)"
+    roof["kernel"] = "expert gate/up projection (all ranks, one launch)"
     roof["avg_us"] = round(kavg * 1e6, 2)
 
     cpu = None

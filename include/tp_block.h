@@ -409,6 +409,20 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
                             void* workspace, uint64_t workspace_bytes, void* moe_workspace,
                             uint64_t moe_workspace_bytes, void* stream);
 
+/* Measurement variant of tp_moe_block_step (the same launches and results): ev_begin / ev_end
+ * (hipEvent_t, non-NULL, else TP_ERR_INVALID_ARG) bracket the expert gate/up launch of every
+ * rank when the step takes the all-ranks expert launches described above, and otherwise rank 0's
+ * expert half as in tp_moe_shard_forward_timed. Not for graph capture. */
+tp_status tp_moe_block_step_timed(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                  const void* const* shards, const void* const* moe_shards,
+                                  const tp_batch* batch, const tp_kv_cache* kv, const void* x,
+                                  const void* gamma1, const void* gamma2, const void* router,
+                                  void* partials, void* xn, void* h1, void* xn2, void* out,
+                                  float* logits, int32_t* topk_ids, float* topk_weights,
+                                  void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                                  uint64_t moe_workspace_bytes, void* stream, void* ev_begin,
+                                  void* ev_end);
+
 const char* tp_status_str(tp_status status);
 /* Detail of the calling thread's last failure ("" if none). */
 const char* tp_last_error(void);

@@ -32,7 +32,8 @@ EXPORTED = (
     "tp_lm_head", "tp_moe_shard_size", "tp_moe_shard_weights", "tp_moe_route",
     "tp_moe_workspace_size", "tp_moe_shard_forward", "tp_moe_shard_forward_timed",
     "tp_shard_project", "tp_shard_project_workspace_size", "tp_block_shard_forward_noalloc",
-    "tp_block_step", "tp_block_step_timed", "tp_moe_block_step", "tp_step_workspace_size",
+    "tp_block_step", "tp_block_step_timed", "tp_moe_block_step", "tp_moe_block_step_timed",
+    "tp_step_workspace_size",
     "tp_step_schedule", "tp_block_step_with_schedule",
 )
 
@@ -143,6 +144,8 @@ def lib() -> ctypes.CDLL:
         "tp_block_step_timed": [P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P, I32, P, P],
         "tp_moe_block_step": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U64, P,
                               U64, P],
+        "tp_moe_block_step_timed": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U64,
+                                    P, U64, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -349,6 +352,23 @@ def tp_moe_block_step(desc, moe, shards, moe_shards, batch: tp_batch, kv, x, gam
         ptr(gamma1), ptr(gamma2), ptr(router), ptr(partials), ptr(xn), ptr(h1), ptr(xn2),
         ptr(out), ptr(logits), ptr(topk_ids), ptr(topk_weights), ptr(workspace), workspace_bytes,
         ptr(moe_workspace), moe_workspace_bytes, _stream(stream)))
+
+
+def tp_moe_block_step_timed(desc, moe, shards, moe_shards, batch: tp_batch, kv, x, gamma1, gamma2,
+                            router, partials, xn, h1, xn2, out, logits, topk_ids, topk_weights,
+                            workspace, moe_workspace, ev_begin, ev_end, workspace_bytes=None,
+                            moe_workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    if moe_workspace_bytes is None:
+        moe_workspace_bytes = moe_workspace.numel() * moe_workspace.element_size()
+    sh, kvs = _step_arrays(shards, kv)
+    msh = (ctypes.c_void_p * len(moe_shards))(*[ptr(t) for t in moe_shards])
+    _check(lib().tp_moe_block_step_timed(
+        ctypes.byref(desc), ctypes.byref(moe), sh, msh, ctypes.byref(batch), kvs, ptr(x),
+        ptr(gamma1), ptr(gamma2), ptr(router), ptr(partials), ptr(xn), ptr(h1), ptr(xn2),
+        ptr(out), ptr(logits), ptr(topk_ids), ptr(topk_weights), ptr(workspace), workspace_bytes,
+        ptr(moe_workspace), moe_workspace_bytes, _stream(stream), ev_begin, ev_end))
 
 
 def tp_partial_reduce(desc, n_tokens, partials, n_partials, residual_in, residual_out, gamma,

@@ -346,16 +346,21 @@ class MoEBlock:
                                          b.T, self.ids, self.weights, out, self.workspace,
                                          events[0], events[1], self.ws_bytes)
 
-    def step_fused(self, copy: int = 0, moe_ws_bytes: int | None = None):
+    def step_fused(self, copy: int = 0, moe_ws_bytes: int | None = None, timed=None):
         """The same MoE block step in one library call (tp_moe_block_step): for decode batches
         the norms and the reduces run inside the neighbouring projections. moe_ws_bytes: the
-        expert workspace handed to the call (default: every rank's share)."""
+        expert workspace handed to the call (default: every rank's share). ``timed``: (begin,
+        end) raw events bracketing the expert gate/up launch of every rank
+        (tp_moe_block_step_timed)."""
         b = self.attn
-        B.tp_moe_block_step(b.desc, self.moe, b.shards[copy], self.shards[copy], b.batch,
-                            b.kv[copy], b.x, b.gamma1, b.gamma2, self.router, b.partials, b.xn,
-                            b.h1, b.xn2, b.out, self.logits, self.ids, self.weights, b.workspace,
-                            self.workspace, b.ws_bytes,
-                            self.step_ws_bytes if moe_ws_bytes is None else moe_ws_bytes)
+        args = (b.desc, self.moe, b.shards[copy], self.shards[copy], b.batch, b.kv[copy], b.x,
+                b.gamma1, b.gamma2, self.router, b.partials, b.xn, b.h1, b.xn2, b.out,
+                self.logits, self.ids, self.weights, b.workspace, self.workspace)
+        ws = self.step_ws_bytes if moe_ws_bytes is None else moe_ws_bytes
+        if timed is None:
+            B.tp_moe_block_step(*args, b.ws_bytes, ws)
+        else:
+            B.tp_moe_block_step_timed(*args, timed[0], timed[1], b.ws_bytes, ws)
 
     def step(self, copy: int = 0, moe_events=None):
         b = self.attn

@@ -1615,14 +1615,17 @@ static tp_status step_impl(const tp_block_desc* desc, const void* const* shards,
   return TP_OK;
 }
 
-tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
-                            const void* const* shards, const void* const* moe_shards,
-                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
-                            const void* gamma1, const void* gamma2, const void* router,
-                            void* partials, void* xn, void* h1, void* xn2, void* out,
-                            float* logits, int32_t* topk_ids, float* topk_weights,
-                            void* workspace, uint64_t workspace_bytes, void* moe_workspace,
-                            uint64_t moe_workspace_bytes, void* stream) {
+// evb / eve (optional): bracket the expert gate/up launch of every rank when the step takes the
+// all-ranks expert launches, else rank 0's expert half.
+static tp_status moe_step_impl(const tp_block_desc* desc, const tp_moe_desc* moe,
+                               const void* const* shards, const void* const* moe_shards,
+                               const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                               const void* gamma1, const void* gamma2, const void* router,
+                               void* partials, void* xn, void* h1, void* xn2, void* out,
+                               float* logits, int32_t* topk_ids, float* topk_weights,
+                               void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                               uint64_t moe_workspace_bytes, void* stream, hipEvent_t evb,
+                               hipEvent_t eve) {
   Dims x;
   MoeDims m;
   if (tp_status s = check_moe(desc, moe, &x, &m)) return s;
@@ -1711,8 +1714,12 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
       mr.su[r] = sh + L.up_scale.offset;
       mr.m[r] = (char*)moe_workspace + (size_t)r * mws;
     }
-    hipError_t e = tpk::launch_moe_gate_up_ranks(wt, at, x.actf, x.d, m.fr, m.E, m.k, T,
-                                                 topk_ids, xn2, mr, st);
+    hipError_t e;
+    {
+      TimedScope ts(evb, eve);
+      e = tpk::launch_moe_gate_up_ranks(wt, at, x.actf, x.d, m.fr, m.E, m.k, T, topk_ids, xn2, mr,
+                                        st);
+    }
     if (e != hipSuccess) return hip_fail(e, "moe gate/up (all ranks)");
     if (tpk::moe_down_ranks_fit(N, m.k, m.fr)) {
       // Every rank's down in one launch, the reduce in it (as the last rank's down adds it).
@@ -1741,12 +1748,43 @@ tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
   for (int r = 0; r < N; ++r) {
     if (tp_status s = moe_forward_impl(desc, moe, r, moe_shards[r], xn2, T, topk_ids, topk_weights,
                                        part(r), moe_workspace, moe_workspace_bytes, stream,
-                                       nullptr, nullptr, fused && r == N - 1 ? &fout : nullptr))
+                                       r == 0 ? evb : nullptr, r == 0 ? eve : nullptr,
+                                       fused && r == N - 1 ? &fout : nullptr))
       return s;
   }
   if (!fused) return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
   g_err.clear();
   return TP_OK;
+}
+
+tp_status tp_moe_block_step(const tp_block_desc* desc, const tp_moe_desc* moe,
+                            const void* const* shards, const void* const* moe_shards,
+                            const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                            const void* gamma1, const void* gamma2, const void* router,
+                            void* partials, void* xn, void* h1, void* xn2, void* out,
+                            float* logits, int32_t* topk_ids, float* topk_weights,
+                            void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                            uint64_t moe_workspace_bytes, void* stream) {
+  return moe_step_impl(desc, moe, shards, moe_shards, batch, kv, x_in, gamma1, gamma2, router,
+                       partials, xn, h1, xn2, out, logits, topk_ids, topk_weights, workspace,
+                       workspace_bytes, moe_workspace, moe_workspace_bytes, stream, nullptr,
+                       nullptr);
+}
+
+tp_status tp_moe_block_step_timed(const tp_block_desc* desc, const tp_moe_desc* moe,
+                                  const void* const* shards, const void* const* moe_shards,
+                                  const tp_batch* batch, const tp_kv_cache* kv, const void* x_in,
+                                  const void* gamma1, const void* gamma2, const void* router,
+                                  void* partials, void* xn, void* h1, void* xn2, void* out,
+                                  float* logits, int32_t* topk_ids, float* topk_weights,
+                                  void* workspace, uint64_t workspace_bytes, void* moe_workspace,
+                                  uint64_t moe_workspace_bytes, void* stream, void* ev_begin,
+                                  void* ev_end) {
+  if (!ev_begin || !ev_end) return fail(TP_ERR_INVALID_ARG, "ev_begin and ev_end must be non-NULL");
+  return moe_step_impl(desc, moe, shards, moe_shards, batch, kv, x_in, gamma1, gamma2, router,
+                       partials, xn, h1, xn2, out, logits, topk_ids, topk_weights, workspace,
+                       workspace_bytes, moe_workspace, moe_workspace_bytes, stream,
+                       (hipEvent_t)ev_begin, (hipEvent_t)ev_end);
 }
 
 tp_status tp_block_step(const tp_block_desc* desc, const void* const* shards, const tp_batch* batch,

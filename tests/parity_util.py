@@ -15,6 +15,35 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+class HipEventPair:
+    """Two hipEvent_t handles (created through the HIP runtime) for the library's *_timed calls,
+    which record them around a launch."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        hs = []
+        for _ in range(2):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0, "hipEventCreate failed"
+            hs.append(h.value)
+        self.begin, self.end = hs
+
+    def elapsed_us(self) -> float:
+        ms = self.ct.c_float()
+        assert self.hip.hipEventElapsedTime(self.ct.byref(ms), self.begin, self.end) == 0
+        return ms.value * 1e3
+
+    def close(self) -> None:
+        self.hip.hipEventDestroy(self.begin)
+        self.hip.hipEventDestroy(self.end)
+
+
 def nrel(a, b) -> float:
     """Normwise max-abs-relative error: max|a - b| / max|b|."""
     a = np.asarray(a, dtype=np.float64)

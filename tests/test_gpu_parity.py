@@ -647,6 +647,16 @@ def test_moe_one_call_step(s, moe):
         torch.cuda.synchronize()
         for k, v in snap.items():
             assert torch.equal(getattr(b, k).view(torch.uint8), v.view(torch.uint8)), k
+        # The measurement variant (events around the all-ranks expert gate/up): the same bits.
+        from parity_util import HipEventPair
+        ev = HipEventPair()
+        b.out.fill_(float("nan"))
+        mb.step_fused(timed=(ev.begin, ev.end))
+        torch.cuda.synchronize()
+        for k, v in snap.items():
+            assert torch.equal(getattr(b, k).view(torch.uint8), v.view(torch.uint8)), k
+        assert ev.elapsed_us() > 0
+        ev.close()
     eager = b.out.clone()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
