@@ -469,8 +469,11 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(s.name)
-    roof["kernel"] = ("gate/up projection (all ranks, one launch)" if all_ranks
-                      else "gate/up projection (one rank)")
+    if all_ranks and s.w_dtype == "q8_0" and s.n_tokens > 4:
+        roof["kernel"] = "gate/up projection (all ranks: Q8_0 GEMM and its split-K epilogue)"
+    else:
+        roof["kernel"] = ("gate/up projection (all ranks, one launch)" if all_ranks
+                          else "gate/up projection (one rank)")
     roof["avg_us"] = round(kavg * 1e6, 2)
 
     cpu = None

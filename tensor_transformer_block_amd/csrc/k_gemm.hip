@@ -525,12 +525,17 @@ __global__ __launch_bounds__(256) void k_gemm_splitk_dma(const uint16_t* __restr
 // Sum of the S split-K partial tiles, in split order, then the epilogue. A thread owns four
 // consecutive columns of one row (V4: N % 4 == 0, C and ldc 16-byte / 4-element aligned; else
 // one column) and issues the loads of four splits before it adds them, so the split loads
-// overlap instead of forming a chain of dependent round trips.
+// overlap instead of forming a chain of dependent round trips. Every rank in one launch
+// (gr.n > 1): blockIdx.y = rank, its partial tiles at gr.a[rank] and its output at gr.c[rank].
 template <int EPI, int ACTF, bool V4>
 __global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict__ part, int S,
                                                          int M, int N, void* __restrict__ C,
-                                                         int ldc) {
+                                                         int ldc, GemmRanks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
+  if (gr.n > 1) {
+    part = (const float*)gr.a[blockIdx.y];
+    C = gr.c[blockIdx.y];
+  }
   constexpr int W = V4 ? 4 : 1;
   typedef __attribute__((__vector_size__(W * sizeof(float)))) float vec;
   const int ncols = DUAL ? 2 * N : N;
@@ -579,28 +584,36 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict
 
 template <bool V4>
 static hipError_t splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
-                                  void* C, int ldc, hipStream_t st) {
+                                  void* C, int ldc, hipStream_t st, const GemmRanks& gr) {
   const size_t total = (size_t)M * N / (V4 ? 4 : 1);
-  dim3 eg((unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192)), eb(256);
+  dim3 eg((unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192),
+          gr.n > 1 ? gr.n : 1),
+      eb(256);
+#define TPK_EPI(E, A) launch((k_splitk_epilogue<E, A, V4>), eg, eb, 0, st, part, S, M, N, C, ldc, gr)
   switch (epi) {
-    case EPI_ACT: launch((k_splitk_epilogue<EPI_ACT, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_F32: launch((k_splitk_epilogue<EPI_F32, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
-    case EPI_BF16: launch((k_splitk_epilogue<EPI_BF16, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc); break;
+    case EPI_ACT: TPK_EPI(EPI_ACT, 0); break;
+    case EPI_F32: TPK_EPI(EPI_F32, 0); break;
+    case EPI_BF16: TPK_EPI(EPI_BF16, 0); break;
     case EPI_GATED:
-      if (actf == 0) launch((k_splitk_epilogue<EPI_GATED, 0, V4>), eg, eb, 0, st, part, S, M, N, C, ldc);
-      else launch((k_splitk_epilogue<EPI_GATED, 1, V4>), eg, eb, 0, st, part, S, M, N, C, ldc);
+      if (actf == 0) TPK_EPI(EPI_GATED, 0);
+      else TPK_EPI(EPI_GATED, 1);
       break;
     default: return hipErrorInvalidValue;
   }
+#undef TPK_EPI
   return hipGetLastError();
 }
 
 hipError_t launch_splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
-                                  void* C, int ldc, hipStream_t st) {
-  const bool v4 =
-      N % 4 == 0 && ldc % 4 == 0 && (uintptr_t)C % 16 == 0 && (uintptr_t)part % 16 == 0;
-  return v4 ? splitk_epilogue<true>(epi, actf, part, S, M, N, C, ldc, st)
-            : splitk_epilogue<false>(epi, actf, part, S, M, N, C, ldc, st);
+                                  void* C, int ldc, hipStream_t st, const GemmRanks* gr) {
+  const GemmRanks one{};
+  const GemmRanks& g = gr ? *gr : one;
+  if (gr && (gr->n < 1 || gr->n > kMaxRanks)) return hipErrorInvalidValue;
+  bool v4 = N % 4 == 0 && ldc % 4 == 0 && (uintptr_t)C % 16 == 0 && (uintptr_t)part % 16 == 0;
+  for (int r = 0; gr && r < gr->n; ++r)
+    v4 = v4 && (uintptr_t)gr->c[r] % 16 == 0 && (uintptr_t)gr->a[r] % 16 == 0;
+  return v4 ? splitk_epilogue<true>(epi, actf, part, S, M, N, C, ldc, st, g)
+            : splitk_epilogue<false>(epi, actf, part, S, M, N, C, ldc, st, g);
 }
 
 // Split count for the split-K variants: enough workgroups to cover the chip, K ranges a multiple

@@ -37,8 +37,21 @@ __global__ __launch_bounds__(256) void k_gemm_q8(const uint16_t* __restrict__ A,
                                                  const int8_t* __restrict__ B2q,
                                                  const uint16_t* __restrict__ B2s, int M, int N,
                                                  int K, int kt_per, void* __restrict__ C, int ldc,
-                                                 float* __restrict__ part) {
+                                                 float* __restrict__ part, int nsplit, Q8Ranks gr) {
   constexpr bool DUAL = (EPI == EPI_GATED);
+  // Every rank in one launch: blockIdx.z = rank * nsplit + K range.
+  int split = blockIdx.z;
+  if (gr.n > 1) {
+    const int r = blockIdx.z / nsplit;
+    split = blockIdx.z - r * nsplit;
+    A = (const uint16_t*)gr.a[r];
+    Bq = (const int8_t*)gr.q[r];
+    Bs = (const uint16_t*)gr.s[r];
+    B2q = (const int8_t*)gr.q2[r];
+    B2s = (const uint16_t*)gr.s2[r];
+    C = gr.c[r];
+    part = gr.part[r];
+  }
   constexpr int NB = DUAL ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][Q8_BM * Q8_LD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][NB][Q8_BN * Q8_LD];
@@ -48,7 +61,7 @@ __global__ __launch_bounds__(256) void k_gemm_q8(const uint16_t* __restrict__ A,
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * Q8_BM, n0 = blockIdx.x * Q8_BN;
   const int nkt = (K + Q8_BK - 1) / Q8_BK;
-  const int kt0 = blockIdx.z * kt_per, kt1 = min(nkt, kt0 + kt_per);
+  const int kt0 = split * kt_per, kt1 = min(nkt, kt0 + kt_per);
   const int nblk = K / 32;
 
   // Staging assignment: A as two rows of 8 bf16 per thread; the codes as 16 bytes of one weight
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(256) void k_gemm_q8(const uint16_t* __restrict__ A,
 
   // Lane holds C[row0 + r][col] for r = 0..3 (the MFMA output layout).
   const int ncols = DUAL ? 2 * N : N;
-  float* pbase = part ? part + (size_t)blockIdx.z * M * ncols : nullptr;
+  float* pbase = part ? part + (size_t)split * M * ncols : nullptr;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -195,6 +208,12 @@ static void q8_plan(int M, int N, int K, int* S, int* kt_per) {
   *S = (nkt + per - 1) / per;
 }
 
+int q8_gemm_splits(int M, int N, int K) {
+  int S, per;
+  q8_plan(M, N, K, &S, &per);
+  return S;
+}
+
 size_t q8_gemm_workspace_bytes(int M, int N, int K, bool dual) {
   int S, per;
   q8_plan(M, N, K, &S, &per);
@@ -214,25 +233,26 @@ hipError_t launch_gemm_q8(int epi, int actf, int M, int N, int K, const void* A,
     per = (K + Q8_BK - 1) / Q8_BK;
   }
   float* p = S > 1 ? part : nullptr;
+  const Q8Ranks nr{};
   const dim3 g((N + Q8_BN - 1) / Q8_BN, (M + Q8_BM - 1) / Q8_BM, S), b(256);
   const uint16_t* a = (const uint16_t*)A;
   const int8_t *q = (const int8_t*)Bq, *q2 = (const int8_t*)B2q;
   const uint16_t *s = (const uint16_t*)Bs, *s2 = (const uint16_t*)B2s;
   switch (epi) {
     case EPI_ACT:
-      launch((k_gemm_q8<EPI_ACT, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p);
+      launch((k_gemm_q8<EPI_ACT, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, nr);
       break;
     case EPI_F32:
-      launch((k_gemm_q8<EPI_F32, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p);
+      launch((k_gemm_q8<EPI_F32, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, nr);
       break;
     case EPI_BF16:
-      launch((k_gemm_q8<EPI_BF16, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p);
+      launch((k_gemm_q8<EPI_BF16, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, nr);
       break;
     case EPI_GATED:
       if (actf == 0)
-        launch((k_gemm_q8<EPI_GATED, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p);
+        launch((k_gemm_q8<EPI_GATED, 0>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, nr);
       else
-        launch((k_gemm_q8<EPI_GATED, 1>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p);
+        launch((k_gemm_q8<EPI_GATED, 1>), g, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, nr);
       break;
     default:
       return hipErrorInvalidValue;
@@ -240,6 +260,60 @@ hipError_t launch_gemm_q8(int epi, int actf, int M, int N, int K, const void* A,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_splitk_epilogue(epi, actf, part, S, M, N, C, ldc, st);
+}
+
+hipError_t launch_gemm_q8_ranks(int epi, int actf, int M, int N, int K, const Q8Ranks& gr, int ldc,
+                                hipStream_t st, bool parts_only, int* S_out) {
+  if (gr.n < 1 || gr.n > kMaxRanks || K % 32 || !S_out) return hipErrorInvalidValue;
+  const bool dual = epi == EPI_GATED;
+  int S, per;
+  q8_plan(M, N, K, &S, &per);
+  *S_out = S;
+  for (int r = 0; r < gr.n; ++r)
+    if (!gr.a[r] || !gr.q[r] || !gr.s[r] || !gr.c[r] || (dual && (!gr.q2[r] || !gr.s2[r])) ||
+        ((S > 1 || parts_only) && !gr.part[r]))
+      return hipErrorInvalidValue;
+  if (M == 0 || N == 0) return hipSuccess;
+  if (parts_only && dual) return hipErrorInvalidValue;
+  Q8Ranks g = gr;
+  if (S == 1 && !parts_only)
+    for (int r = 0; r < gr.n; ++r) g.part[r] = nullptr;  // one K range: the epilogue in the tiles
+  const dim3 grid((N + Q8_BN - 1) / Q8_BN, (M + Q8_BM - 1) / Q8_BM, S * gr.n), b(256);
+  const uint16_t* a = (const uint16_t*)g.a[0];
+  const int8_t *q = (const int8_t*)g.q[0], *q2 = (const int8_t*)g.q2[0];
+  const uint16_t *s = (const uint16_t*)g.s[0], *s2 = (const uint16_t*)g.s2[0];
+  float* p = g.part[0];
+  void* C = g.c[0];
+  if (gr.n == 1) g.n = 0;  // a single rank takes the plain arguments
+  switch (epi) {
+    case EPI_ACT:
+      launch((k_gemm_q8<EPI_ACT, 0>), grid, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, g);
+      break;
+    case EPI_F32:
+      launch((k_gemm_q8<EPI_F32, 0>), grid, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, g);
+      break;
+    case EPI_BF16:
+      launch((k_gemm_q8<EPI_BF16, 0>), grid, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, g);
+      break;
+    case EPI_GATED:
+      if (actf == 0)
+        launch((k_gemm_q8<EPI_GATED, 0>), grid, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, g);
+      else
+        launch((k_gemm_q8<EPI_GATED, 1>), grid, b, 0, st, a, q, s, q2, s2, M, N, K, per, C, ldc, p, S, g);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || parts_only || S == 1) return e;
+  GemmRanks ge{};
+  ge.n = gr.n;
+  for (int r = 0; r < gr.n; ++r) {
+    ge.a[r] = gr.part[r];
+    ge.c[r] = gr.c[r];
+  }
+  return launch_splitk_epilogue(epi, actf, gr.part[0], S, M, N, gr.c[0], ldc, st,
+                                gr.n > 1 ? &ge : nullptr);
 }
 
 }  // namespace tpk

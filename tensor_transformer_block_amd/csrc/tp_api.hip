@@ -250,8 +250,10 @@ WsLayout ws_layout(const Dims& x, const tp_batch& b, int ranks = 1) {
         tpk::splitk_workspace_bytes((int)T, x.d, x.fr, false)};
     for (uint64_t c : cand) gemm = c > gemm ? c : gemm;
   } else if (use_q8_gemm(x, (int)T)) {
+    // (The QKV's: its K ranges' tiles, which the all-ranks batched step leaves for the rotary
+    // kernel to sum, even when there is one range.)
     const uint64_t cand[4] = {
-        tpk::q8_gemm_workspace_bytes((int)T, x.qkv_rows, x.d, false),
+        (uint64_t)tpk::q8_gemm_splits((int)T, x.qkv_rows, x.d) * T * x.qkv_rows * 4,
         tpk::q8_gemm_workspace_bytes((int)T, x.d, x.qdim, false),
         tpk::q8_gemm_workspace_bytes((int)T, x.fr, x.d, true),
         tpk::q8_gemm_workspace_bytes((int)T, x.d, x.fr, false)};
@@ -323,13 +325,18 @@ bool ranks_step_ok(const Dims& x, int T) {
          tpk::gemv_ranks_fit(wt, tpk::EPI_RED_ALL, x.N, T, x.fr);
 }
 
-// Batched decode (5 to 64 tokens, bf16) whose projections all take the split-K QKV and the band
-// GEMMs: the staged sequence with each projection, the rotary / KV append and the attention as
-// one launch for all ranks (the reduces are one launch for all ranks already).
+// Batched decode (5 to 64 tokens) whose projections all take the split-K QKV and the band GEMMs
+// (bf16) or the Q8_0 matrix-core GEMM: the staged sequence with each projection, the rotary / KV
+// append and the attention as one launch for all ranks (the reduces are one launch for all ranks
+// already).
 bool ranks_staged_ok(const Dims& x, const tp_batch& b) {
   const int T = b.n_tokens;
   if (x.N < 2 || x.N > tpk::kMaxRanks || T < 1 || T > 64 || b.mode != TP_MODE_DECODE) return false;
-  if (x.wt != TP_DTYPE_BF16 || x.at != TP_DTYPE_BF16) return false;
+  if (x.at != TP_DTYPE_BF16) return false;
+  // Q8_0: the rotary kernel sums the QKV's K ranges (at most 16).
+  if (x.wt == TP_DTYPE_Q8_0)
+    return use_q8_gemm(x, T) && tpk::q8_gemm_splits(T, x.qkv_rows, x.d) <= 16;
+  if (x.wt != TP_DTYPE_BF16) return false;
   if (!use_gemm(x, T, x.d) || !use_gemm(x, T, x.qdim) || !use_gemm(x, T, x.fr)) return false;
   if (x.d % 64 != 0) return false;  // the direct-to-LDS split-K QKV
   return tpk::gemm_band_supported(tpk::EPI_F32, T, x.d, x.qdim) &&
@@ -1423,7 +1430,36 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
   }
   int S = 0;
   hipError_t e;
-  if (prefill) {
+  const bool q8 = x.wt == TP_DTYPE_Q8_0;
+  // Q8_0 projections: rank r's codes and block scales of one region (gated: gate rows, then the up
+  // rows at row gate_off).
+  auto q8ranks = [&](const tp_region& codes, const tp_region& scales, int K, int gate_off,
+                     const void* const* in, void* const* outp, bool with_part) {
+    tpk::Q8Ranks g{};
+    g.n = N;
+    for (int r = 0; r < N; ++r) {
+      g.a[r] = in[r];
+      g.q[r] = shard(r) + codes.offset;
+      g.s[r] = shard(r) + scales.offset;
+      if (gate_off > 0) {
+        g.q2[r] = shard(r) + codes.offset + (size_t)gate_off * K;
+        g.s2[r] = shard(r) + scales.offset + (size_t)gate_off * (K / 32) * 2;
+      }
+      g.c[r] = outp[r];
+      g.part[r] = with_part ? (float*)(wsr(r) + w.gemm) : nullptr;
+    }
+    return g;
+  };
+  if (q8) {
+    const void* in[tpk::kMaxRanks];
+    void* outp[tpk::kMaxRanks];
+    for (int r = 0; r < N; ++r) {
+      in[r] = xn;
+      outp[r] = wsr(r) + w.qkv;  // (unused: the tiles stay in the workspace)
+    }
+    const tpk::Q8Ranks g = q8ranks(L.qkv, L.qkv_scale, x.d, 0, in, outp, true);
+    e = tpk::launch_gemm_q8_ranks(tpk::EPI_ACT, 0, T, x.qkv_rows, x.d, g, x.qkv_rows, st, true, &S);
+  } else if (prefill) {
     // One rank's QKV tiles are too few to fill the chip, which is why the separate calls split K;
     // all ranks' tiles together usually are enough, and then each tile takes the whole K (one
     // fp32 sum per output, rounded once: the separate calls' q, k, v to rounding).
@@ -1475,6 +1511,19 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
                    : tpk::launch_gemm_band(epi, actf, T, n_out, K, nullptr, nullptr, nullptr,
                                            nullptr, ldc, st, g);
   };
+  int S8 = 0;
+  auto q8gemm = [&](int epi, int actf, int n_out, int K, int ldc, const tp_region& codes,
+                    const tp_region& scales, int gate_off, const void* const* in,
+                    void* const* outp) {
+    const tpk::Q8Ranks g = q8ranks(codes, scales, K, gate_off, in, outp, true);
+    return tpk::launch_gemm_q8_ranks(epi, actf, T, n_out, K, g, ldc, st, false, &S8);
+  };
+  const void* in_o[tpk::kMaxRanks];
+  void* out_p[tpk::kMaxRanks];
+  for (int r = 0; r < N; ++r) {
+    in_o[r] = wsr(r) + w.attn;
+    out_p[r] = part(r);
+  }
   tpk::GemmRanks go{};
   go.n = N;
   for (int r = 0; r < N; ++r) {
@@ -1482,7 +1531,8 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     go.b[r] = shard(r) + L.o.offset;
     go.c[r] = part(r);
   }
-  e = gemm(epi_part, 0, x.d, x.qdim, x.d, &go);
+  e = q8 ? q8gemm(epi_part, 0, x.d, x.qdim, x.d, L.o, L.o_scale, 0, in_o, out_p)
+         : gemm(epi_part, 0, x.d, x.qdim, x.d, &go);
   if (e != hipSuccess) return hip_fail(e, "o projection (all ranks)");
   if (tp_status s = tp_partial_reduce(desc, T, partials, N, x_in, h1, gamma2, xn2, stream))
     return s;
@@ -1496,7 +1546,18 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
   }
   {
     TimedScope ts(evb, eve);
-    e = gemm(tpk::EPI_GATED, x.actf, x.fr, x.d, x.fr, &gg);
+    if (q8) {
+      const void* in[tpk::kMaxRanks];
+      void* outp[tpk::kMaxRanks];
+      for (int r = 0; r < N; ++r) {
+        in[r] = xn2;
+        outp[r] = wsr(r) + w.ffn;
+      }
+      e = q8gemm(tpk::EPI_GATED, x.actf, x.fr, x.d, x.fr, L.gate_up, L.gate_up_scale, x.fr, in,
+                 outp);
+    } else {
+      e = gemm(tpk::EPI_GATED, x.actf, x.fr, x.d, x.fr, &gg);
+    }
   }
   if (e != hipSuccess) return hip_fail(e, "gate/up projection (all ranks)");
   tpk::GemmRanks gd{};
@@ -1506,7 +1567,13 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
     gd.b[r] = shard(r) + L.down.offset;
     gd.c[r] = part(r);
   }
-  e = gemm(epi_part, 0, x.d, x.fr, x.d, &gd);
+  if (q8) {
+    const void* in[tpk::kMaxRanks];
+    for (int r = 0; r < N; ++r) in[r] = wsr(r) + w.ffn;
+    e = q8gemm(epi_part, 0, x.d, x.fr, x.d, L.down, L.down_scale, 0, in, out_p);
+  } else {
+    e = gemm(epi_part, 0, x.d, x.fr, x.d, &gd);
+  }
   if (e != hipSuccess) return hip_fail(e, "down projection (all ranks)");
   return tp_partial_reduce(desc, T, partials, N, h1, out, nullptr, nullptr, stream);
 }

@@ -200,15 +200,35 @@ hipError_t launch_gemv_ranks(int wt, int at, int epi, int actf, int T, const Ran
 // (splitk_workspace_bytes), summed in split order by a small epilogue kernel.
 size_t splitk_workspace_bytes(int M, int N, int K, bool dual);
 // Sum of S fp32 partial tiles [S][M][N] (gated: [S][M][2N], gate then up) in split order, then the
-// epilogue into C.
+// epilogue into C. gr (optional): every rank in one launch, rank r's tiles at gr->a[r] and its
+// output at gr->c[r].
 hipError_t launch_splitk_epilogue(int epi, int actf, const float* part, int S, int M, int N,
-                                  void* C, int ldc, hipStream_t st);
+                                  void* C, int ldc, hipStream_t st, const GemmRanks* gr = nullptr);
 // Q8_0 weights (codes [N, K] int8, scales [N, K/32] fp16; gated: B2 = the up rows) for more tokens
 // than the GEMV takes; `part` (q8_gemm_workspace_bytes, may be NULL) holds split-K partial tiles.
 size_t q8_gemm_workspace_bytes(int M, int N, int K, bool dual);
 hipError_t launch_gemm_q8(int epi, int actf, int M, int N, int K, const void* A, const void* Bq,
                           const void* Bs, const void* B2q, const void* B2s, void* C, int ldc,
                           float* part, hipStream_t st);
+// The Q8_0 projection of every rank in one launch (grid.z = rank * S + K range): rank r's
+// activations a[r], codes and scales q[r], s[r] (gated: the up rows' q2[r], s2[r]), output c[r]
+// and partial-tile workspace part[r] (q8_gemm_workspace_bytes; with parts_only at least
+// S * M * N floats). Each rank's K ranges are those of its own launch_gemm_q8, so its results are
+// the same bits. parts_only: leave the fp32 partial tiles [S][M][N] in part[r] (even for S == 1)
+// and return S in *S_out, for the caller to sum; else the all-ranks epilogue runs when S > 1.
+struct Q8Ranks {
+  int n;
+  const void* a[kMaxRanks];
+  const void* q[kMaxRanks];
+  const void* s[kMaxRanks];
+  const void* q2[kMaxRanks];
+  const void* s2[kMaxRanks];
+  void* c[kMaxRanks];
+  float* part[kMaxRanks];
+};
+int q8_gemm_splits(int M, int N, int K);
+hipError_t launch_gemm_q8_ranks(int epi, int actf, int M, int N, int K, const Q8Ranks& gr, int ldc,
+                                hipStream_t st, bool parts_only, int* S_out);
 // parts_only: launch the GEMM alone, leaving the fp32 partial tiles [S][M][N] (dual: gate then
 // up per row) in `part`, and return S there; the caller then sums them.
 hipError_t launch_gemm_splitk(int epi, int actf, int M, int N, int K, const void* A,

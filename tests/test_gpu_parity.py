@@ -237,7 +237,8 @@ def test_step_matches_staged_and_graph_replay():
 # The one-call step: decode shapes take the fused schedule (norms in the QKV and gate/up
 # projections, reduces in the last rank's o_proj and down, at most four ranks: one launch per
 # projection for all ranks); the batched and prefill shapes take the staged sequence of the same
-# calls, batched ones on the split-K and band GEMMs as one launch per stage for all ranks.
+# calls, batched ones (on the split-K and band GEMMs, or the Q8_0 matrix-core GEMM) as one launch
+# per stage for all ranks.
 FUSED_STEP = ["med-bf16-ragged", "med-bf16-single-key", "med-q8-n4", "med-q8-hd256",
               "med-fp32-g2", "med-bf16-g8", "med-bf16-long-kv", "med-bf16-batched-64",
               "med-bf16-prefill", "med-bf16-band-all"]
@@ -246,7 +247,10 @@ FUSED_STEP = ["med-bf16-ragged", "med-bf16-single-key", "med-q8-n4", "med-q8-hd2
 ONE_CALL = ([(n, p) for n in FUSED_STEP for p in ("f32", "bf16")]
             + [(n, "f32") for n in ("tiny-llama-fp32", "llama3-8b-decode", "gemma-q8-decode",
                                     "llama3-8b-batched")]
-            + [("llama3-8b-batched", "bf16")])
+            + [("llama3-8b-batched", "bf16")]
+            # Q8_0 batches: each projection one matrix-core launch for all ranks
+            + [(n, p) for n in ("med-q8-batched-21", "med-q8-batched-64") for p in ("f32", "bf16")]
+            + [("gemma-q8-batched", "f32")])
 
 
 @pytest.mark.parametrize("name,partial_dtype", ONE_CALL, ids=lambda v: str(v))
@@ -259,7 +263,7 @@ def test_one_call_step(name, partial_dtype):
     the step replays to the same bits."""
     import oracle
     from tensor_transformer_block_amd.block import DeviceBlock, to_host
-    s = BY_NAME.get(name) or CONFIGS.get(name)
+    s = BY_NAME.get(name) or WORKLOADS.get(name)
     inp = make_inputs(s, seed=23)
     blk = DeviceBlock(inp, partial_dtype=partial_dtype)
     fused = s.mode == "decode" and s.n_tokens <= 4
