@@ -226,17 +226,20 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * column-parallel launch works for one rank with that rank's slice and cache, and every block
  * of a row-parallel launch computes its rows for rank 0, 1, ... in turn, each rank's sums exactly
  * as in that rank's own launch, then adds the partials in rank order and the residual. The
- * results equal the per-rank schedule's bit for bit. Batched decode (5 to 64 tokens, bf16) whose
- * projections all take the split-K QKV and the band GEMMs, and bf16 prefill whose QKV takes the
- * split-K wide tiles and whose other projections take the 256 x 256 wide tiles, also get
- * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection, the rotary / KV
- * append and the attention as one launch for all ranks (under one launch the causal prefill's
- * long and short row blocks of all ranks share the chip). The launches are sized for all ranks'
- * work together, so three choices differ from the separate calls': a prefill QKV whose tiles of
- * all ranks fill the chip is not split over K; the batched QKV splits K into fewer ranges; the
- * batched attention splits each sequence's keys into fewer ranges (often none). Each changes
- * only the order of fp32 additions before a rounding: q, k, v, the attention output and so the
- * rest of the step equal the separate calls' to rounding, not bit for bit.
+ * results equal the per-rank schedule's bit for bit. Batched decode (5 to 64 tokens) whose
+ * projections all take the split-K QKV and the band GEMMs (bf16) or the Q8_0 matrix-core GEMM
+ * (Q8_0, whose QKV has at most 16 K ranges), and bf16 prefill whose QKV takes the split-K wide
+ * tiles and whose other projections take the 256 x 256 wide tiles, also get
+ * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection (with its split-K
+ * epilogue), the rotary / KV append and the attention as one launch for all ranks (under one
+ * launch the causal prefill's long and short row blocks of all ranks share the chip). The
+ * launches are sized for all ranks' work together, so three choices differ from the separate
+ * calls': a prefill QKV whose tiles of all ranks fill the chip is not split over K; the bf16
+ * batched QKV splits K into fewer ranges; the batched attention splits each sequence's keys into
+ * fewer ranges (often none). (The Q8_0 projections keep each rank's K ranges; their QKV tiles are
+ * summed in the same order by the rotary kernel.) Each changes only the order of fp32 additions
+ * before a rounding: q, k, v, the attention output and so the rest of the step equal the separate
+ * calls' to rounding, not bit for bit.
  * Otherwise (TP_SCHEDULE_STAGED)
  * the call issues exactly the separate calls above. tp_step_schedule reports which schedule a
  * batch gets.
