@@ -470,7 +470,8 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(s.name)
     if all_ranks and s.w_dtype == "q8_0" and s.n_tokens > 4:
-        roof["kernel"] = "gate/up projection (all ranks: Q8_0 GEMM and its split-K epilogue)"
+        roof["kernel"] = ("gate/up projection (all ranks: the Q8_0 GEMM, with its split-K "
+                          "epilogue when K is split)")
     else:
         roof["kernel"] = ("gate/up projection (all ranks, one launch)" if all_ranks
                           else "gate/up projection (one rank)")

@@ -228,8 +228,9 @@ tp_status tp_block_shard_forward_noalloc(const tp_block_desc* desc, int32_t rank
  * as in that rank's own launch, then adds the partials in rank order and the residual. The
  * results equal the per-rank schedule's bit for bit. Batched decode (5 to 64 tokens) whose
  * projections all take the split-K QKV and the band GEMMs (bf16) or the Q8_0 matrix-core GEMM
- * (Q8_0, whose QKV has at most 16 K ranges), and bf16 prefill whose QKV takes the split-K wide
- * tiles and whose other projections take the 256 x 256 wide tiles, also get
+ * (Q8_0, whose QKV has at most 16 K ranges), bf16 prefill whose QKV takes the split-K wide
+ * tiles and whose other projections take the 256 x 256 wide tiles, and Q8_0 prefill on the
+ * matrix-core GEMM (head dims the prefill attention takes), also get
  * TP_SCHEDULE_ALL_RANKS: the separate calls' sequence with each projection (with its split-K
  * epilogue), the rotary / KV append and the attention as one launch for all ranks (under one
  * launch the causal prefill's long and short row blocks of all ranks share the chip). The

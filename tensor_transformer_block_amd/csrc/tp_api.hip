@@ -344,12 +344,17 @@ bool ranks_staged_ok(const Dims& x, const tp_batch& b) {
          tpk::gemm_band_supported(tpk::EPI_F32, T, x.d, x.fr);
 }
 
-// Prefill (bf16) whose QKV takes the split-K wide tiles and whose o_proj, gate/up and down take
-// the 256 x 256 wide tiles: the staged sequence with one launch per stage for all ranks.
+// Prefill whose QKV takes the split-K wide tiles and whose o_proj, gate/up and down take the
+// 256 x 256 wide tiles (bf16), or whose projections take the Q8_0 matrix-core GEMM (Q8_0, at
+// most 16 K ranges for the QKV): the staged sequence with one launch per stage for all ranks.
 bool ranks_prefill_ok(const Dims& x, const tp_batch& b) {
   const int T = b.n_tokens;
   if (x.N < 2 || x.N > tpk::kMaxRanks || T < 256 || b.mode != TP_MODE_PREFILL) return false;
-  if (x.wt != TP_DTYPE_BF16 || x.at != TP_DTYPE_BF16) return false;
+  if (x.at != TP_DTYPE_BF16) return false;
+  if (x.wt == TP_DTYPE_Q8_0)
+    return use_q8_gemm(x, T) && tpk::attn_prefill_supported(x.hd, x.Hq / x.Hkv, x.ps) &&
+           tpk::q8_gemm_splits(T, x.qkv_rows, x.d) <= 16;
+  if (x.wt != TP_DTYPE_BF16) return false;
   if (qkv_ksplit(x, T) <= 1 || !tpk::attn_prefill_supported(x.hd, x.Hq / x.Hkv, x.ps))
     return false;
   auto wide = [&](int epi, int n_out, int K) {
@@ -1406,7 +1411,8 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
       return fail(TP_ERR_INVALID_ARG, "KV pages must be 16-byte aligned");
   }
   const bool prefill = batch->mode == TP_MODE_PREFILL;
-  if (!prefill && w.gemm_bytes == 0)
+  const bool q8 = x.wt == TP_DTYPE_Q8_0;
+  if ((!prefill || q8) && w.gemm_bytes == 0)
     return fail(TP_ERR_UNSUPPORTED, "no split-K workspace for this batch");
   tp_shard_layout L;
   make_layout(x, &L);
@@ -1419,8 +1425,8 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
 
   if (tp_status s = tp_partial_reduce(desc, T, nullptr, 0, x_in, nullptr, gamma1, xn, stream))
     return s;
-  // QKV partial products: split-K tiles (batched) or the wide split-K tiles (prefill).
-  const uint64_t pofs = prefill ? w.qkvp : w.gemm;
+  // QKV partial products: split-K tiles (batched, and Q8_0) or the wide split-K tiles (prefill).
+  const uint64_t pofs = prefill && !q8 ? w.qkvp : w.gemm;
   tpk::GemmRanks gq{};
   gq.n = N;
   for (int r = 0; r < N; ++r) {
@@ -1430,7 +1436,6 @@ static tp_status staged_ranks(const tp_block_desc* desc, const Dims& x, const vo
   }
   int S = 0;
   hipError_t e;
-  const bool q8 = x.wt == TP_DTYPE_Q8_0;
   // Q8_0 projections: rank r's codes and block scales of one region (gated: gate rows, then the up
   // rows at row gate_off).
   auto q8ranks = [&](const tp_region& codes, const tp_region& scales, int K, int gate_off,

@@ -249,7 +249,8 @@ ONE_CALL = ([(n, p) for n in FUSED_STEP for p in ("f32", "bf16")]
                                     "llama3-8b-batched")]
             + [("llama3-8b-batched", "bf16")]
             # Q8_0 batches: each projection one matrix-core launch for all ranks
-            + [(n, p) for n in ("med-q8-batched-21", "med-q8-batched-64") for p in ("f32", "bf16")]
+            + [(n, p) for n in ("med-q8-batched-21", "med-q8-batched-64", "med-q8-prefill-300")
+               for p in ("f32", "bf16")]
             + [("gemma-q8-batched", "f32")])
 
 
