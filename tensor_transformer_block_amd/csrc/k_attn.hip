@@ -439,7 +439,8 @@ constexpr int kPLd = 40;  // bf16 per LDS row of P (32 keys + padding)
 // A decode launch reads each key and value once: streaming (non-temporal) loads, which keep the
 // caches from filling with lines nothing reads again (64 sequences of 2048 keys, 4 ranks: 95.2 ->
 // 83.2 us; one 4096-key sequence, 2 ranks: 2.3 us less per step). Heads of 256 measured 0.45 us
-// faster per step with plain loads, and prefill tiles re-read K and V from cache.
+// faster per step with plain loads for one sequence but not for batches (the launcher picks), and
+// prefill tiles re-read K and V from cache.
 template <bool PLAIN>
 __device__ __forceinline__ uint4 kv_ld(const uint16_t* p) {
   if constexpr (PLAIN) return *(const uint4*)p;
@@ -448,7 +449,8 @@ __device__ __forceinline__ uint4 kv_ld(const uint16_t* p) {
 
 // Decode with heads of up to 128 fits three waves per SIMD (168 registers) without spilling; more
 // waves keep more key tiles in flight (64 sequences of 2048 keys, 4 ranks: 84.9 -> 83.4 us).
-template <int HD, bool PREFILL>
+// NTW: streaming loads for heads wider than 128 too (the batched launches; see the launcher).
+template <int HD, bool PREFILL, bool NTW = false>
 __global__ __launch_bounds__(256, (HD <= 128 && !PREFILL) ? 3 : 1) void k_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpages,
     const uint16_t* __restrict__ vpages, const int* __restrict__ positions, int mode,
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256, (HD <= 128 && !PREFILL) ? 3 : 1) void k_attn_m
       const int key = tile_key(j) + 16 * h + fr;
       const uint16_t* base = kpages + (((size_t)pid * hk + g) * ps + (key % ps)) * HD + fq * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[h][ks] = kv_ld<PREFILL || (HD > 128)>(base + ks * 32);
+      for (int ks = 0; ks < KS; ++ks) kf[h][ks] = kv_ld<PREFILL || (HD > 128 && !NTW)>(base + ks * 32);
     }
   };
   auto load_v = [&](int j) {
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(256, (HD <= 128 && !PREFILL) ? 3 : 1) void k_attn_m
     const int slot = (tile_key(j) + 16 * (fq >> 1)) % ps + 8 * (fq & 1);
     const uint16_t* base = vpages + (((size_t)pid * hk + g) * HD + fr) * ps + slot;
 #pragma unroll
-    for (int n = 0; n < NO; ++n) vf[n] = kv_ld<PREFILL || (HD > 128)>(base + (size_t)n * 16 * ps);
+    for (int n = 0; n < NO; ++n) vf[n] = kv_ld<PREFILL || (HD > 128 && !NTW)>(base + (size_t)n * 16 * ps);
   };
   auto refresh_pages = [&](int j) {
     if ((j & 31) == 0) {
@@ -784,10 +786,19 @@ static hipError_t attn_mfma_g(bool prefill, int G, int T, int hk, hipStream_t st
                        AttnRanks{});
   } else {
     dim3 grid(n_split, hk * (ar.n > 1 ? ar.n : 1), T);
-    hipLaunchKernelGGL((k_attn_mfma<HD, false>), grid, dim3(256), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt, max_pages,
-                       ps, n_pages, hk, G, T, chunk, n_split, pos_limit, po, pml, (uint16_t*)out,
-                       sl2, ar);
+    // Heads wider than 128: plain loads for a few sequences (the Gemma-like decode, 0.5 us per
+    // step faster than streaming loads), streaming loads for batches (the Gemma-like 64-sequence
+    // batch streams 255 MB of K and V: 153.1 -> 146.8 us per step).
+    if (HD > 128 && T > 4)
+      hipLaunchKernelGGL((k_attn_mfma<HD, false, true>), grid, dim3(256), 0, st,
+                         (const uint16_t*)q, (const uint16_t*)kp, (const uint16_t*)vp, positions,
+                         mode, bt, max_pages, ps, n_pages, hk, G, T, chunk, n_split, pos_limit,
+                         po, pml, (uint16_t*)out, sl2, ar);
+    else
+      hipLaunchKernelGGL((k_attn_mfma<HD, false>), grid, dim3(256), 0, st, (const uint16_t*)q,
+                         (const uint16_t*)kp, (const uint16_t*)vp, positions, mode, bt,
+                         max_pages, ps, n_pages, hk, G, T, chunk, n_split, pos_limit, po, pml,
+                         (uint16_t*)out, sl2, ar);
   }
   return hipGetLastError();
 }
