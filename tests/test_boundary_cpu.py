@@ -268,3 +268,32 @@ def test_shard_project_validation():
     assert st == B.TP_ERR_BUFFER_TOO_SMALL
     st, _ = _err(B.tp_shard_project, d, 4, 256, 512, 1, 1024)
     assert st == B.TP_ERR_INVALID_ARG
+
+
+def test_traffic_record_hash_ignores_comments_only(tmp_path):
+    """The gate/up traffic records carry a hash of their kernels' code: an edit of comments or
+    whitespace keeps it, a change of code (or of a string literal holding comment markers) does
+    not, and every committed record still matches the current sources."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char* s = "x // y";\n'
+    variants = {
+        "comments": 'int f(int a) {  // add two\n\n  return a + 1;   /* done,\n twice */ }\n'
+                    'const char* s = "x // y";\n',
+        "code": 'int f(int a) { // add one\n  return a + 2; /* done */ }\nconst char* s = "x // y";\n',
+        "string": 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char* s = "x / y";\n',
+    }
+    base = tmp_path / "a.hip"
+    base.write_text(src)
+    d0 = bench.code_digest(["a.hip"], str(tmp_path))
+    got = {}
+    for k, v in variants.items():
+        (tmp_path / f"{k}.hip").write_text(v)
+        got[k] = bench.code_digest([f"{k}.hip"], str(tmp_path))
+    assert got["comments"] == d0
+    assert got["code"] != d0 and got["string"] != d0
+    assert bench.code_text(src) == 'int f(int a) { return a + 1; } const char* s = "x // y";'
+    for w in ("llama3-8b-decode", "gemma-q8-decode", "llama3-8b-batched", "llama-70b-prefill"):
+        assert bench.measured_traffic(w) is not None, w
