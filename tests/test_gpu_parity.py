@@ -158,16 +158,19 @@ def test_config_parity_prefill_sampled(name):
 
 
 @pytest.mark.timeout(900)
-def test_all_ranks_prefill_matches_staged():
-    """70B-shaped prefill at N = 8: the block step with one launch per stage for all ranks (QKV
-    over the whole K, rotary / KV append, attention, o_proj, gate/up, down) against the separate
-    per-rank calls (whose QKV splits K four ways): xn bit for bit (the same reduce), and h1, xn2,
-    out, the FFN partials and every rank's new K, V to the bf16 tolerance (they differ only by
-    the QKV's fp32 summation order before its bf16 rounding)."""
+@pytest.mark.parametrize("name", ["llama-70b-prefill", "llama3-8b-q8-prefill"])
+def test_all_ranks_prefill_matches_staged(name):
+    """2048-token prefill (70B-shaped bf16 at N = 8, 8B-shaped Q8_0 at N = 4): the block step with
+    one launch per stage for all ranks (QKV, rotary / KV append, attention, o_proj, gate/up,
+    down) against the separate per-rank calls: xn bit for bit (the same reduce), and h1, xn2, out,
+    the FFN partials and every rank's new K, V to the bf16 tolerance (bf16: the all-ranks QKV
+    takes the whole K where the separate calls split it four ways, which changes only the fp32
+    summation order before its bf16 rounding); Q8_0 bit for bit (every projection keeps each
+    rank's K ranges)."""
     from tensor_transformer_block_amd import binding as B
     from tensor_transformer_block_amd.block import DeviceBlock
-    s = WORKLOADS["llama-70b-prefill"]
-    log("llama-70b-prefill: generating inputs")
+    s = WORKLOADS[name]
+    log(f"{name}: generating inputs")
     blk = DeviceBlock(make_inputs(s, seed=3))
     assert blk.schedule() == B.TP_SCHEDULE_ALL_RANKS
 
@@ -201,10 +204,14 @@ def test_all_ranks_prefill_matches_staged():
             fa = (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
             fb = (b.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
             errs[f"{nm}_new r{rk}"] = nrel(fa, fb)
-    log("llama-70b-prefill: all-ranks step vs separate calls: "
+    log(f"{name}: all-ranks step vs separate calls: "
         + ", ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= 2e-2, (k, v)
+        # Q8_0: the same K ranges, the QKV's fp32 tiles rounded once by the rotary kernel as the
+        # separate calls' epilogue rounds them, and the same attention: the same bits.
+        if s.w_dtype == "q8_0":
+            assert v == 0.0, (k, v)
 
 
 def test_step_matches_staged_and_graph_replay():
