@@ -399,7 +399,9 @@ tp_status tp_moe_shard_forward_timed(const tp_block_desc* desc, const tp_moe_des
  * of N entries. Buffers as in tp_block_step and tp_moe_route; workspace: tp_step_workspace_size
  * bytes, moe_workspace: at least tp_moe_workspace_size bytes (16-byte aligned); with N times
  * that, a decode step whose norms and reduces are folded runs every rank's expert gate/up
- * projection as one launch (rank r's activations in the r-th share), and, for at most four
+ * projection as one launch (rank r's activations in the r-th share; with at most 64 experts
+ * that launch also selects the experts from the logits, by tp_moe_route's rule and with the same
+ * ids and weights, so no separate top-k launch runs), and, for at most four
  * ranks whose activations fit one workgroup's LDS, every rank's expert down as one launch whose
  * workgroups add the ranks' partials in rank order and the residual; each rank's sums are those
  * of its own launch and every partial is still stored, so the results are the same bits.

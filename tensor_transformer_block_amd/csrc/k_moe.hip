@@ -89,6 +89,38 @@ __global__ __launch_bounds__(256) void k_moe_topk(const float* __restrict__ logi
 // or equal with a lower index), which places every selected expert directly: one pass over the
 // wave's logits in LDS instead of top_k rounds of wave-wide maxima. The winners are then moved to
 // lane = rank, the layout the softmax above uses, so ids and weights come out the same.
+// One wave selects token t's top_k of E <= 64 logits (as above) into s_i / s_v (the wave's own
+// LDS rows, kMoeMaxTopK entries each) and returns, in lanes < top_k, the selection's id and
+// softmax weight.
+__device__ __forceinline__ void moe_topk64_wave(const float* __restrict__ zt, int E, int top_k,
+                                                float* s_z, float* s_v, int* s_i, int lane,
+                                                int* id_out, float* w_out) {
+  const float z = lane < E ? zt[lane] : -INFINITY;
+  const float v = z != z ? -INFINITY : z;  // a NaN logit ranks as -inf (below every number)
+  s_z[lane] = v;
+  // The wave's own LDS writes must land before its lanes read each other's entries.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const float4 z = *(const float4*)&s_z[j];
+    rank += (z.x > v || (z.x == v && j < lane)) + (z.y > v || (z.y == v && j + 1 < lane)) +
+            (z.z > v || (z.z == v && j + 2 < lane)) + (z.w > v || (z.w == v && j + 3 < lane));
+  }
+  if (lane < E && rank < top_k) {  // padding lanes (-inf, highest indices) never rank this high
+    s_v[rank] = v;
+    s_i[rank] = lane;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  const float my_v = lane < top_k ? s_v[lane] : -INFINITY;
+  const int my_i = lane < top_k ? s_i[lane] : 0;
+  const float top = __shfl(my_v, 0, 64);
+  const float ex = lane < top_k ? expf(my_v - top) : 0.f;
+  const float den = wave_sum(ex);
+  *id_out = my_i;
+  *w_out = ex / den;
+}
+
 __global__ __launch_bounds__(256) void k_moe_topk64(const float* __restrict__ logits, int T,
                                                     int E, int top_k, int32_t* __restrict__ ids,
                                                     float* __restrict__ weights) {
@@ -98,31 +130,13 @@ __global__ __launch_bounds__(256) void k_moe_topk64(const float* __restrict__ lo
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const float z = lane < E ? logits[(size_t)t * E + lane] : -INFINITY;
-  const float v = z != z ? -INFINITY : z;  // a NaN logit ranks as -inf (below every number)
-  s_z[wave][lane] = v;
-  // The wave's own LDS writes must land before its lanes read each other's entries.
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  int rank = 0;
-#pragma unroll
-  for (int j = 0; j < 64; j += 4) {
-    const float4 z = *(const float4*)&s_z[wave][j];
-    rank += (z.x > v || (z.x == v && j < lane)) + (z.y > v || (z.y == v && j + 1 < lane)) +
-            (z.z > v || (z.z == v && j + 2 < lane)) + (z.w > v || (z.w == v && j + 3 < lane));
-  }
-  if (lane < E && rank < top_k) {  // padding lanes (-inf, highest indices) never rank this high
-    s_v[wave][rank] = v;
-    s_i[wave][rank] = lane;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  const float my_v = lane < top_k ? s_v[wave][lane] : -INFINITY;
-  const int my_i = lane < top_k ? s_i[wave][lane] : 0;
-  const float top = __shfl(my_v, 0, 64);
-  const float ex = lane < top_k ? expf(my_v - top) : 0.f;
-  const float den = wave_sum(ex);
+  int id;
+  float w;
+  moe_topk64_wave(logits + (size_t)t * E, E, top_k, s_z[wave], s_v[wave], s_i[wave], lane, &id,
+                  &w);
   if (lane < top_k) {
-    ids[(size_t)t * top_k + lane] = my_i;
-    weights[(size_t)t * top_k + lane] = ex / den;
+    ids[(size_t)t * top_k + lane] = id;
+    weights[(size_t)t * top_k + lane] = w;
   }
 }
 
@@ -177,8 +191,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
                                                      int Fr, int E, int top_k,
                                                      const int32_t* __restrict__ ids,
                                                      const void* __restrict__ X,
-                                                     void* __restrict__ Mout, MoeRanks mr) {
+                                                     void* __restrict__ Mout, MoeRanks mr,
+                                                     const float* __restrict__ logits,
+                                                     int32_t* __restrict__ ids_out,
+                                                     float* __restrict__ w_out) {
   extern __shared__ float xs[];  // [K]
+  // logits (E <= 64): the workgroup selects the token's experts itself (wave 0, the router's
+  // top-k rule) instead of reading ids; the first workgroup of rank 0 stores the selection and
+  // its weights for the down projection and the caller.
+  __shared__ __attribute__((aligned(16))) float s_z[64];
+  __shared__ float s_v[kMoeMaxTopK];
+  __shared__ int s_i[kMoeMaxTopK], s_ids[kMoeMaxTopK];
+  const bool sel = logits != nullptr;
   constexpr int VE = WFmt<WT>::VE, WB = WFmt<WT>::WB, AV = Vec16<AT>::N;
   if (mr.n > 1) {  // every rank in one launch (blockIdx.z = rank): that rank's slices and output
     const int r = blockIdx.z;
@@ -194,18 +218,35 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const char* __restrict__ Wg
   const int np = top_k * Fr;
   size_t grow[MOE_PW];
   bool ok[MOE_PW];
+  auto rows = [&](const int32_t* id_src) {
 #pragma unroll
-  for (int s = 0; s < MOE_PW; ++s) {
-    const int p = (blockIdx.x * 4 + wave) * MOE_PW + s;
-    ok[s] = p < np;
-    const int pp = ok[s] ? p : 0;
-    int e = ids[(size_t)t * top_k + pp / Fr];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    grow[s] = (size_t)e * Fr + pp % Fr;
+    for (int s = 0; s < MOE_PW; ++s) {
+      const int p = (blockIdx.x * 4 + wave) * MOE_PW + s;
+      ok[s] = p < np;
+      const int pp = ok[s] ? p : 0;
+      int e = id_src[pp / Fr];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      grow[s] = (size_t)e * Fr + pp % Fr;
+    }
+  };
+  if (!sel) {
+    rows(ids + (size_t)t * top_k);
+  } else if (wave == 0) {
+    int id;
+    float w;
+    moe_topk64_wave(logits + (size_t)t * E, E, top_k, s_z, s_v, s_i, lane, &id, &w);
+    if (lane < top_k) {
+      s_ids[lane] = id;
+      if (blockIdx.x == 0 && blockIdx.z == 0) {
+        ids_out[(size_t)t * top_k + lane] = id;
+        w_out[(size_t)t * top_k + lane] = w;
+      }
+    }
   }
   for (int i = tid * AV; i < K; i += 256 * AV)
     Vec16<AT>::load((const char*)X + ((size_t)t * K + i) * (AT == ACT_F32 ? 4 : 2), xs + i);
   __syncthreads();
+  if (sel) rows(s_ids);
   if (!ok[0]) return;
   float g[MOE_PW], u[MOE_PW];
 #pragma unroll
@@ -514,7 +555,8 @@ template <int WT, int AT>
 static hipError_t moe_gate_up_fmt(int actf, const void* Wg, const void* Sg, const void* Wu,
                                   const void* Su, int d, int Fr, int E, int top_k, int T,
                                   const int32_t* ids, const void* X, void* M, const MoeRanks& mr,
-                                  hipStream_t st) {
+                                  hipStream_t st, const float* logits = nullptr,
+                                  int32_t* ids_out = nullptr, float* w_out = nullptr) {
   const int np = top_k * Fr;
   const dim3 gu((np + 4 * MOE_PW - 1) / (4 * MOE_PW), T, mr.n > 1 ? mr.n : 1), b(256);
   const size_t lds_gu = (size_t)d * sizeof(float);
@@ -527,10 +569,10 @@ static hipError_t moe_gate_up_fmt(int actf, const void* Wg, const void* Sg, cons
   }
   if (actf == 0)
     launch((k_moe_gate_up<WT, AT, 0>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M,
-           mr);
+           mr, logits, ids_out, w_out);
   else
     launch((k_moe_gate_up<WT, AT, 1>), gu, b, lds_gu, st, wg, sg, wu, su, d, Fr, E, top_k, ids, X, M,
-           mr);
+           mr, logits, ids_out, w_out);
   return hipGetLastError();
 }
 
@@ -564,21 +606,24 @@ static hipError_t moe_ffn_fmt(int actf, int pt, const void* Wg, const void* Sg, 
 
 hipError_t launch_moe_gate_up_ranks(int wt, int at, int actf, int d, int Fr, int E, int top_k,
                                     int T, const int32_t* ids, const void* X, const MoeRanks& mr,
-                                    hipStream_t st) {
+                                    hipStream_t st, const float* logits, float* weights) {
   if (T <= 0) return hipSuccess;
   if (mr.n < 1 || mr.n > kMaxRanks) return hipErrorInvalidValue;
+  if (logits && (E > 64 || top_k < 1 || top_k > kMoeMaxTopK || top_k > E || !weights || !ids))
+    return hipErrorInvalidValue;
+  int32_t* ids_out = logits ? const_cast<int32_t*>(ids) : nullptr;
   for (int r = 0; r < mr.n; ++r)
     if (!mr.wg[r] || !mr.wu[r] || !mr.m[r] || (wt == W_Q8 && (!mr.sg[r] || !mr.su[r])))
       return hipErrorInvalidValue;
   if (wt == W_F32 && at == ACT_F32)
     return moe_gate_up_fmt<W_F32, ACT_F32>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr, E,
-                                           top_k, T, ids, X, mr.m[0], mr, st);
+                                           top_k, T, ids, X, mr.m[0], mr, st, logits, ids_out, weights);
   if (wt == W_BF16 && at == ACT_BF16)
     return moe_gate_up_fmt<W_BF16, ACT_BF16>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr,
-                                             E, top_k, T, ids, X, mr.m[0], mr, st);
+                                             E, top_k, T, ids, X, mr.m[0], mr, st, logits, ids_out, weights);
   if (wt == W_Q8 && at == ACT_BF16)
     return moe_gate_up_fmt<W_Q8, ACT_BF16>(actf, mr.wg[0], mr.sg[0], mr.wu[0], mr.su[0], d, Fr, E,
-                                           top_k, T, ids, X, mr.m[0], mr, st);
+                                           top_k, T, ids, X, mr.m[0], mr, st, logits, ids_out, weights);
   return hipErrorInvalidValue;
 }
 

@@ -1719,6 +1719,14 @@ static tp_status moe_step_impl(const tp_block_desc* desc, const tp_moe_desc* moe
   const size_t pbytes = x.pt == TP_DTYPE_F32 ? 4 : 2;
   auto part = [&](int r) { return (void*)((char*)partials + (size_t)r * pstride * pbytes); };
   const bool fused = fused_step_ok(x, T);
+  // With room for every rank's expert activations in moe_workspace, a decode step runs the
+  // ranks' expert gate/up projections as one launch (each block's work that of its rank's own
+  // launch), and with at most 64 experts that launch also selects the experts (no top-k launch).
+  uint64_t mws = 0;
+  tp_moe_workspace_size(desc, moe, T, &mws);
+  const bool ranks_experts = fused && N > 1 && moe_workspace && aligned16(moe_workspace) &&
+                             moe_workspace_bytes >= (uint64_t)N * mws;
+  const bool fold_topk = ranks_experts && m.E <= 64;
   if (fused) {
     if (ranks_step_ok(x, T)) {
       if (tp_status s = attn_halves_ranks(desc, x, shards, batch, kv, x_in, gamma1, partials, xn,
@@ -1738,7 +1746,7 @@ static tp_status moe_step_impl(const tp_block_desc* desc, const tp_moe_desc* moe
     const int wt = x.at == TP_DTYPE_F32 ? tpk::W_F32 : tpk::W_BF16;
     hipError_t e = tpk::launch_gemv(wt, at, tpk::EPI_F32, 0, T, router, nullptr, x.d, m.E, 0, h1,
                                     logits, m.E, nullptr, st, &fin);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !fold_topk)
       e = tpk::launch_moe_topk(logits, T, m.E, m.k, topk_ids, topk_weights, st);
     if (e != hipSuccess) return hip_fail(e, "tp_moe_block_step: router");
   } else {
@@ -1760,13 +1768,10 @@ static tp_status moe_step_impl(const tp_block_desc* desc, const tp_moe_desc* moe
   fout.n_prev = N - 1;
   fout.res_in = h1;
   fout.res_out = out;
-  // With room for every rank's expert activations in moe_workspace, a decode step runs the
-  // ranks' expert gate/up projections as one launch (each block's work that of its rank's own
-  // launch), then each rank's down; the last one adds the partials and the residual.
-  uint64_t mws = 0;
-  tp_moe_workspace_size(desc, moe, T, &mws);
-  if (fused && N > 1 && moe_workspace && aligned16(moe_workspace) &&
-      moe_workspace_bytes >= (uint64_t)N * mws) {
+  // The all-ranks expert launches: the gate/up of every rank (selecting the experts when the
+  // top-k launch was skipped), then the down of every rank or each rank's down, the last one
+  // adding the partials and the residual.
+  if (ranks_experts) {
     for (int r = 0; r < N; ++r)
       if (!moe_shards[r] || !aligned16(moe_shards[r]))
         return fail(TP_ERR_INVALID_ARG, "moe shard %d is NULL or not 16-byte aligned", r);
@@ -1790,7 +1795,7 @@ static tp_status moe_step_impl(const tp_block_desc* desc, const tp_moe_desc* moe
     {
       TimedScope ts(evb, eve);
       e = tpk::launch_moe_gate_up_ranks(wt, at, x.actf, x.d, m.fr, m.E, m.k, T, topk_ids, xn2, mr,
-                                        st);
+                                        st, fold_topk ? logits : nullptr, topk_weights);
     }
     if (e != hipSuccess) return hip_fail(e, "moe gate/up (all ranks)");
     if (tpk::moe_down_ranks_fit(N, m.k, m.fr)) {

@@ -160,10 +160,13 @@ struct MoeRanks {
 };
 // The two halves of launch_moe_ffn on their own: the gate/up of every rank in mr (blockIdx.z =
 // rank; each block's work exactly that of the rank's own launch) and one rank's down (with the
-// reduce epilogue when `fuse` is given).
+// reduce epilogue when `fuse` is given). logits (optional, E <= 64): the gate/up selects each
+// token's experts from the router logits itself (launch_moe_topk's rule and results) and stores
+// the selection in ids and its weights in weights.
 hipError_t launch_moe_gate_up_ranks(int wt, int at, int actf, int d, int Fr, int E, int top_k,
                                     int T, const int32_t* ids, const void* X, const MoeRanks& mr,
-                                    hipStream_t st);
+                                    hipStream_t st, const float* logits = nullptr,
+                                    float* weights = nullptr);
 hipError_t launch_moe_down(int wt, int at, int pt, const void* Wd, const void* Sd, int d, int Fr,
                            int E, int top_k, int T, const int32_t* ids, const float* wts,
                            const void* M, void* P, hipStream_t st, const FuseArgs* fuse);
